@@ -1,0 +1,238 @@
+"""Seeded synthetic workloads for the MLA + DSA path.
+
+This module draws inputs only: random numbers from ``numpy.random.default_rng(seed)`` in a
+fixed order, bf16 rounding of those draws (round to nearest even on the bit pattern),
+and the paged-pool layout (a seeded random block permutation).  It computes nothing of
+the method itself, so the GPU tests, the benchmark and the CPU oracle can all consume the
+same arrays.  No trained weights, prompts or datasets exist here: every value is synthetic,
+shaped like a GLM-5.2-class MLA layer (64 heads, qk_nope 192, qk_rope 64, v_head 256,
+kv_lora 512; a 32-head, 128-wide DSA indexer keeping 2048 keys).
+
+Draw order (per workload, one generator each):
+  tiny  (seed 1): x[T, hidden], q_a, q_b, kv_a, kv_b, o_w   -- all fp32
+  decode(seed s): Lc[T, L], Rc[T, rope], q_nope[B, H, nope], q_rope[B, H, rope],
+                  kv_b[H*(nope+v), L], then (DSA) Ic[T, hd], q_idx[B, n_ih, hd], w_idx[B, n_ih]
+  prefill       : q[S, H, nope+rope], Lc, Rc, kv_b
+  paged batch   : seq_len[B], block permutation, Lc pool, Rc pool, Ic pool, q_nope, q_rope,
+                  kv_b, q_idx, w_idx
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# GLM-5.2-like dims
+H, QK_NOPE, QK_ROPE, V_HEAD, KV_LORA = 64, 192, 64, 256, 512
+N_IH, INDEX_HD, TOPK = 32, 128, 2048
+BLOCK = 64
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bf16 bit pattern (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit pattern -> float32 value (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng, shape, std=1.0, chunk=1 << 26) -> np.ndarray:
+    """N(0, std^2) float32 draws, generated in chunks to bound peak memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        rng.standard_normal(e - s, dtype=np.float32, out=out[s:e])
+    if std != 1.0:
+        out *= np.float32(std)
+    return out.reshape(shape)
+
+
+def _normal_bf16(rng, shape, std=1.0, chunk=1 << 26) -> np.ndarray:
+    """N(0, std^2) draws rounded to bf16, returned as uint16 bit patterns."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    buf = np.empty(min(n, chunk), dtype=np.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        b = buf[: e - s]
+        rng.standard_normal(e - s, dtype=np.float32, out=b)
+        if std != 1.0:
+            b *= np.float32(std)
+        out[s:e] = to_bf16_bits(b)
+    return out.reshape(shape)
+
+
+@dataclass
+class TinyLayer:
+    """A tiny fp32 MLA layer: H=4, qk_nope=16, qk_rope=8, v_head=16, kv_lora=32, hidden=64,
+    q_lora=32, T=64 cached tokens.  Activations N(0,1), weights N(0, 0.02^2)."""
+    H: int = 4
+    nope: int = 16
+    rope: int = 8
+    v: int = 16
+    L: int = 32
+    hidden: int = 64
+    q_lora: int = 32
+    T: int = 64
+    x: np.ndarray = field(default=None, repr=False)
+    q_a: np.ndarray = field(default=None, repr=False)
+    q_b: np.ndarray = field(default=None, repr=False)
+    kv_a: np.ndarray = field(default=None, repr=False)
+    kv_b: np.ndarray = field(default=None, repr=False)
+    o_w: np.ndarray = field(default=None, repr=False)
+
+
+def tiny_layer(seed: int = 1) -> TinyLayer:
+    t = TinyLayer()
+    rng = np.random.default_rng(seed)
+    t.x = _normal(rng, (t.T, t.hidden))
+    t.q_a = _normal(rng, (t.q_lora, t.hidden), 0.02)
+    t.q_b = _normal(rng, (t.H * (t.nope + t.rope), t.q_lora), 0.02)
+    t.kv_a = _normal(rng, (t.L + t.rope, t.hidden), 0.02)
+    t.kv_b = _normal(rng, (t.H * (t.nope + t.v), t.L), 0.02)
+    t.o_w = _normal(rng, (t.hidden, t.H * t.v), 0.02)
+    return t
+
+
+@dataclass
+class Decode:
+    """One decode step over contiguous caches (B sequences of equal length T).
+    Arrays are bf16 bit patterns (uint16) when ``bf16`` else float32; Ic/q_idx/w_idx are
+    always float32.  Rc rows are the cached (already rotated) keys; q_rope is the query's
+    tail before rotation.  The query sits at position T-1 and sees keys 0..T-1."""
+    B: int
+    T: int
+    H: int
+    nope: int
+    rope: int
+    v: int
+    L: int
+    bf16: bool
+    lc: np.ndarray = field(repr=False)
+    rc: np.ndarray = field(repr=False)
+    q_nope: np.ndarray = field(repr=False)
+    q_rope: np.ndarray = field(repr=False)
+    kv_b: np.ndarray = field(repr=False)
+    n_ih: int = 0
+    hd: int = 0
+    ic: np.ndarray = field(default=None, repr=False)
+    q_idx: np.ndarray = field(default=None, repr=False)
+    w_idx: np.ndarray = field(default=None, repr=False)
+
+
+def decode(seed: int, T: int, B: int = 1, *, H_=H, nope=QK_NOPE, rope=QK_ROPE, v=V_HEAD,
+           L=KV_LORA, bf16=True, dsa=False, n_ih=N_IH, hd=INDEX_HD, w_std=0.02) -> Decode:
+    """Contiguous decode workload.  Lc/Rc: [B*T, *] (sequence b occupies rows b*T..b*T+T-1).
+    Values: Lc, Rc, q ~ N(0,1); kv_b ~ N(0, w_std^2); Ic, q_idx, w_idx ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    g = _normal_bf16 if bf16 else _normal
+    lc = g(rng, (B * T, L))
+    rc = g(rng, (B * T, rope))
+    q_nope = g(rng, (B, H_, nope))
+    q_rope = g(rng, (B, H_, rope))
+    kv_b = g(rng, (H_ * (nope + v), L), w_std)
+    d = Decode(B, T, H_, nope, rope, v, L, bf16, lc, rc, q_nope, q_rope, kv_b)
+    if dsa:
+        d.n_ih, d.hd = n_ih, hd
+        d.ic = _normal(rng, (B * T, hd))
+        d.q_idx = _normal(rng, (B, n_ih, hd))
+        d.w_idx = _normal(rng, (B, n_ih))
+    return d
+
+
+@dataclass
+class Prefill:
+    S: int
+    pos_base: int
+    H: int
+    nope: int
+    rope: int
+    v: int
+    L: int
+    bf16: bool
+    q: np.ndarray = field(repr=False)      # [S, H, nope+rope], tail already rotated
+    lc: np.ndarray = field(repr=False)     # [pos_base+S, L]
+    rc: np.ndarray = field(repr=False)     # [pos_base+S, rope]
+    kv_b: np.ndarray = field(repr=False)
+
+
+def prefill(seed: int, S: int, pos_base: int = 0, *, H_=H, nope=QK_NOPE, rope=QK_ROPE,
+            v=V_HEAD, L=KV_LORA, bf16=True, w_std=0.02) -> Prefill:
+    rng = np.random.default_rng(seed)
+    g = _normal_bf16 if bf16 else _normal
+    T = pos_base + S
+    q = g(rng, (S, H_, nope + rope))
+    lc = g(rng, (T, L))
+    rc = g(rng, (T, rope))
+    kv_b = g(rng, (H_ * (nope + v), L), w_std)
+    return Prefill(S, pos_base, H_, nope, rope, v, L, bf16, q, lc, rc, kv_b)
+
+
+@dataclass
+class PagedBatch:
+    """Batched decode over paged caches: 64-token blocks, one shared block table.
+    Physical block p of the pools holds tokens [64*j, 64*j+64) of sequence b when
+    block_table[b, j] == p.  Unused table entries are -1."""
+    B: int
+    seq_len: np.ndarray                    # int32 [B], tokens cached including the query's own
+    block_size: int
+    max_blocks: int
+    block_table: np.ndarray = field(repr=False)   # int32 [B, max_blocks]
+    n_blocks: int = 0
+    lc: np.ndarray = field(default=None, repr=False)      # bf16 bits [n_blocks*bs, L]
+    rc: np.ndarray = field(default=None, repr=False)      # bf16 bits [n_blocks*bs, rope]
+    ic: np.ndarray = field(default=None, repr=False)      # f32 [n_blocks*bs, hd]
+    q_nope: np.ndarray = field(default=None, repr=False)
+    q_rope: np.ndarray = field(default=None, repr=False)
+    kv_b: np.ndarray = field(default=None, repr=False)
+    q_idx: np.ndarray = field(default=None, repr=False)
+    w_idx: np.ndarray = field(default=None, repr=False)
+    H: int = H
+    nope: int = QK_NOPE
+    rope: int = QK_ROPE
+    v: int = V_HEAD
+    L: int = KV_LORA
+    n_ih: int = N_IH
+    hd: int = INDEX_HD
+
+    def rows(self, b: int, t) -> np.ndarray:
+        """Pool row index of logical token(s) t of sequence b (layout bookkeeping only)."""
+        t = np.asarray(t, dtype=np.int64)
+        return self.block_table[b, t // self.block_size].astype(np.int64) * self.block_size + t % self.block_size
+
+
+def paged_batch(seed: int, B: int = 32, t_lo: int = 8192, t_hi: int = 131072, *,
+                block_size: int = BLOCK, max_ctx: int = 131072, H_=H, nope=QK_NOPE,
+                rope=QK_ROPE, v=V_HEAD, L=KV_LORA, n_ih=N_IH, hd=INDEX_HD,
+                w_std=0.02) -> PagedBatch:
+    """seq_len ~ U{t_lo..t_hi} (inclusive); pools filled in physical order after a seeded
+    random permutation of the blocks; values distributed as in ``decode``."""
+    rng = np.random.default_rng(seed)
+    seq_len = rng.integers(t_lo, t_hi + 1, size=B).astype(np.int32)
+    max_blocks = (max_ctx + block_size - 1) // block_size
+    nb = [(int(s) + block_size - 1) // block_size for s in seq_len]
+    n_blocks = int(sum(nb))
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    bt = np.full((B, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(B):
+        bt[b, : nb[b]] = perm[o: o + nb[b]]
+        o += nb[b]
+    pb = PagedBatch(B, seq_len, block_size, max_blocks, bt, n_blocks, H=H_, nope=nope, rope=rope,
+                    v=v, L=L, n_ih=n_ih, hd=hd)
+    rows = n_blocks * block_size
+    pb.lc = _normal_bf16(rng, (rows, L))
+    pb.rc = _normal_bf16(rng, (rows, rope))
+    pb.ic = _normal(rng, (rows, hd))
+    pb.q_nope = _normal_bf16(rng, (B, H_, nope))
+    pb.q_rope = _normal_bf16(rng, (B, H_, rope))
+    pb.kv_b = _normal_bf16(rng, (H_ * (nope + v), L), w_std)
+    pb.q_idx = _normal(rng, (B, n_ih, hd))
+    pb.w_idx = _normal(rng, (B, n_ih))
+    return pb

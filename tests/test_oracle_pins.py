@@ -1,0 +1,370 @@
+"""Pins for the CPU oracle: each oracle function is checked against something other than
+itself -- worked examples fixed by hand (tests/golden), closed forms, invariants the pages
+state (absorbed == non-absorbed, keep-all selection == dense), brute force on tiny inputs,
+error bounds, and library routines (numpy sort, torch's scaled-dot-product attention).
+
+Pages: chen3feng, "colibri-analysis 06: MLA attention and KV cache" (sec. 1, 2, 2.1, 2.2,
+2.3); aiknowledge.cn, "Ch.7 sec. 03: token-exact forward validation and faithful DSA".
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _closed(v):
+    if isinstance(v, str):
+        return float(eval(v, {"__builtins__": {}}, {"cos": math.cos, "sin": math.sin}))
+    return float(v)
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ----------------------------------------------------------------------------- sizes
+def test_state_size_arithmetic_matches_pages():
+    g = _golden("mla_state_sizes.json")
+    naive = g["n_heads"] * (g["k_head"] + g["v_head"])
+    mla = g["kv_lora"] + g["qk_rope"]
+    assert naive == g["naive_floats_per_token"]
+    assert mla == g["mla_floats_per_token"]
+    assert round(naive / mla) == g["ratio_rounded"]
+
+
+# ----------------------------------------------------------------------------- RoPE
+def test_rope_worked_examples(oracle):
+    g = _golden("rope_worked_examples.json")
+    for c in g["cases"]:
+        x = np.array(c["x"], np.float64).reshape(1, 1, -1)
+        y = oracle.rope_interleave(x, [c["pos"]], 0, c["rope_dim"], c["theta"]).reshape(-1)
+        exp = np.array([_closed(v) for v in c["expected"]])
+        assert np.max(np.abs(y - exp)) <= 1e-15, c["name"]
+
+
+def test_rope_position_zero_is_exact_deinterleave_and_nope_untouched(oracle):
+    rng = np.random.default_rng(10)
+    nope, rope = 16, 8
+    x = rng.standard_normal((5, 3, nope + rope))
+    y = oracle.rope_interleave(x, np.zeros(5, np.int32), nope, rope)
+    assert np.array_equal(y[..., :nope], x[..., :nope])
+    assert np.array_equal(y[..., nope: nope + rope // 2], x[..., nope::2])
+    assert np.array_equal(y[..., nope + rope // 2:], x[..., nope + 1::2])
+    # at other positions the nope dims are still bit-identical
+    y2 = oracle.rope_interleave(x, rng.integers(0, 1 << 17, 5).astype(np.int32), nope, rope)
+    assert np.array_equal(y2[..., :nope], x[..., :nope])
+
+
+def test_rope_preserves_pair_norms(oracle):
+    rng = np.random.default_rng(11)
+    rope = 64
+    x = rng.standard_normal((7, 2, rope))
+    pos = rng.integers(0, 131072, 7).astype(np.int32)
+    y = oracle.rope_interleave(x, pos, 0, rope)
+    h = rope // 2
+    n_in = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n_out = y[..., :h] ** 2 + y[..., h:] ** 2
+    assert np.max(np.abs(n_in - n_out)) <= 1e-12 * np.max(n_in)
+
+
+def test_rope_dot_depends_only_on_relative_position(oracle):
+    rng = np.random.default_rng(12)
+    rope = 64
+    q = rng.standard_normal((1, 1, rope))
+    k = rng.standard_normal((1, 1, rope))
+    for m, n in [(5, 3), (1000, 17), (131071, 129000), (40, 40)]:
+        a = np.dot(oracle.rope_interleave(q, [m], 0, rope).ravel(), oracle.rope_interleave(k, [n], 0, rope).ravel())
+        b = np.dot(oracle.rope_interleave(q, [m - n], 0, rope).ravel(), oracle.rope_interleave(k, [0], 0, rope).ravel())
+        assert abs(a - b) <= 1e-9 * (np.linalg.norm(q) * np.linalg.norm(k))
+
+
+# ----------------------------------------------------------------------------- indexer
+def test_indexer_fixed_order_worked_examples(oracle):
+    g = _golden("indexer_fixed_order.json")
+    for c in g["cases"]:
+        s = oracle.index_scores(np.array(c["q"]), np.array(c["w"]), np.array(c["ic"]))
+        assert s.astype(np.float64).tolist() == c["expected"], c["name"]
+
+
+def test_indexer_integer_inputs_are_exact(oracle):
+    # small integers: every partial sum is exact in fp32, so any correct evaluation
+    # equals exact integer arithmetic
+    rng = np.random.default_rng(20)
+    n_ih, hd, T = 5, 7, 300
+    q = rng.integers(-3, 4, (n_ih, hd))
+    w = rng.integers(-2, 3, n_ih)
+    ic = rng.integers(-3, 4, (T, hd))
+    dots = ic @ q.T                                   # [T, n_ih] exact int64
+    exact = (np.maximum(dots, 0) * w).sum(axis=1)
+    got = oracle.index_scores(q, w, ic)
+    assert np.array_equal(got.astype(np.int64), exact)
+
+
+def test_indexer_one_hot_keys_closed_form(oracle):
+    rng = np.random.default_rng(21)
+    n_ih, hd, T = 32, 128, 256
+    q = rng.standard_normal((n_ih, hd)).astype(np.float32)
+    w = rng.standard_normal(n_ih).astype(np.float32)
+    d_of_t = rng.integers(0, hd, T)
+    ic = np.zeros((T, hd), np.float32)
+    ic[np.arange(T), d_of_t] = 1.0
+    got = oracle.index_scores(q, w, ic).astype(np.float64)
+    ref = (w.astype(np.float64)[None, :] * np.maximum(q.T[d_of_t].astype(np.float64), 0)).sum(1)
+    bound = n_ih * 2.0 ** -24 * (np.abs(w)[None, :] * np.abs(q.T[d_of_t])).sum(1) * 1.01
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+
+
+def test_indexer_one_hot_weight_is_relu_dot(oracle):
+    rng = np.random.default_rng(22)
+    n_ih, hd, T = 8, 128, 200
+    q = rng.standard_normal((n_ih, hd)).astype(np.float32)
+    ic = rng.standard_normal((T, hd)).astype(np.float32)
+    for h in (0, 5):
+        w = np.zeros(n_ih, np.float32)
+        w[h] = 1.0
+        got = oracle.index_scores(q, w, ic).astype(np.float64)
+        ref = np.maximum(ic.astype(np.float64) @ q[h].astype(np.float64), 0)
+        gam = hd * 2.0 ** -24 / (1 - hd * 2.0 ** -24)
+        bound = gam * (np.abs(ic) @ np.abs(q[h])).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_indexer_fp32_within_forward_error_bound(oracle):
+    rng = np.random.default_rng(23)
+    n_ih, hd, T = 32, 128, 1024
+    q = rng.standard_normal((n_ih, hd)).astype(np.float32)
+    w = rng.standard_normal(n_ih).astype(np.float32)
+    ic = rng.standard_normal((T, hd)).astype(np.float32)
+    s32 = oracle.index_scores(q, w, ic).astype(np.float64)
+    s64 = oracle.index_scores_f64(q, w, ic)
+    # the fp64 path itself agrees with a library product
+    lib = (np.maximum(ic.astype(np.float64) @ q.T.astype(np.float64), 0) @ w.astype(np.float64))
+    assert _rel(s64, lib) <= 1e-12
+    n = hd + n_ih
+    u = 2.0 ** -24
+    gam = n * u / (1 - n * u)
+    mag = (np.abs(ic).astype(np.float64) @ np.abs(q.T).astype(np.float64)) @ np.abs(w).astype(np.float64)
+    assert np.all(np.abs(s32 - s64) <= gam * mag)
+
+
+def test_indexer_power_of_two_homogeneity_is_bit_exact(oracle):
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((32, 128)).astype(np.float32)
+    w = rng.standard_normal(32).astype(np.float32)
+    ic = rng.standard_normal((300, 128)).astype(np.float32)
+    base = oracle.index_scores(q, w, ic)
+    assert np.array_equal(oracle.index_scores(q, 2 * w, ic), 2 * base)
+    assert np.array_equal(oracle.index_scores(4 * q, w / 4, ic), base)
+
+
+# ----------------------------------------------------------------------------- top-k
+def test_topk_worked_examples(oracle):
+    g = _golden("topk_worked_examples.json")
+    for c in g["cases"]:
+        sel, nsel = oracle.topk(np.array(c["scores"], np.float32), c["n_valid"], c["k"])
+        assert nsel == c["nsel"], c["name"]
+        assert sel[:nsel].tolist() == c["sel"], c["name"]
+        assert np.all(sel[nsel:] == -1)
+
+
+def _rank_select(s, n_valid, k):
+    """Brute force by counting: key t is kept iff fewer than k keys precede it in the
+    order (higher score, or equal score at a lower position)."""
+    out = []
+    for t in range(n_valid):
+        better = sum(1 for u in range(n_valid) if s[u] > s[t] or (s[u] == s[t] and u < t))
+        if better < k:
+            out.append(t)
+    return out
+
+
+def test_topk_exhaustive_brute_force(oracle):
+    for T in range(1, 8):
+        pats = np.array(list(itertools.product([0.0, 1.0, 2.0], repeat=T)), np.float32)
+        for n_valid in {T, max(T - 2, 0)}:
+            for k in range(1, T + 2):
+                sel, nsel = oracle.topk_batch(pats, np.full(len(pats), n_valid, np.int32), k)
+                for i, s in enumerate(pats):
+                    ref = _rank_select(s, n_valid, k)
+                    assert nsel[i] == len(ref)
+                    assert sel[i, : nsel[i]].tolist() == ref
+
+
+def test_topk_large_random_matches_library_sort(oracle):
+    rng = np.random.default_rng(30)
+    T, k = 131072, 2048
+    s = np.round(rng.standard_normal(T) * 8).astype(np.float32) / 8   # many ties
+    s[rng.integers(0, T, 50)] = -0.0
+    for n_valid in (T, 100000, 2048, 1500):
+        sel, nsel = oracle.topk(s, n_valid, k)
+        order = np.lexsort((np.arange(n_valid), -s[:n_valid].astype(np.float64)))
+        ref = np.sort(order[: min(k, n_valid)])
+        assert nsel == ref.size
+        assert np.array_equal(sel[:nsel], ref)
+
+
+# ----------------------------------------------------------------------------- decode
+def _rand_decode(seed, H=4, nope=16, rope=8, v=16, L=32, T=50, wstd=0.3):
+    rng = np.random.default_rng(seed)
+    return dict(
+        q_nope=rng.standard_normal((H, nope)).astype(np.float32),
+        q_rope=rng.standard_normal((H, rope)).astype(np.float32),
+        kv_b=(rng.standard_normal((H * (nope + v), L)) * wstd).astype(np.float32),
+        lc=rng.standard_normal((T, L)).astype(np.float32),
+        rc=rng.standard_normal((T, rope)).astype(np.float32),
+    ), (H, nope, rope, v, L, T)
+
+
+@pytest.mark.parametrize("dims", [(4, 16, 8, 16, 32, 50), (8, 24, 16, 20, 40, 130)])
+def test_absorbed_equals_nonabsorbed(oracle, dims):
+    H, nope, rope, v, L, T = dims
+    a, _ = _rand_decode(40, H, nope, rope, v, L, T)
+    keys = np.arange(T)
+    sc = 1 / math.sqrt(nope + rope)
+    o1 = oracle.absorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], keys, v, sc)
+    o2 = oracle.nonabsorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], keys, v, sc)
+    assert _rel(o1, o2) <= 1e-10
+
+
+def test_decode_matches_torch_sdpa(oracle):
+    import torch
+    a, (H, nope, rope, v, L, T) = _rand_decode(41, 6, 12, 8, 10, 24, 77)
+    keys = np.random.default_rng(1).permutation(T)[:40]
+    sc = 0.37
+    got = oracle.absorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], keys, v, sc)
+    kvb = torch.from_numpy(a["kv_b"].astype(np.float64)).view(H, nope + v, L)
+    lc = torch.from_numpy(a["lc"].astype(np.float64))[keys]
+    rc = torch.from_numpy(a["rc"].astype(np.float64))[keys]
+    k_nope = torch.einsum("hic,tc->hti", kvb[:, :nope], lc)
+    vv = torch.einsum("hjc,tc->htj", kvb[:, nope:], lc)
+    k = torch.cat([k_nope, rc.unsqueeze(0).expand(H, -1, -1)], dim=-1)
+    q = torch.cat([torch.from_numpy(a["q_nope"]).double(), torch.from_numpy(a["q_rope"]).double()], -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q[:, None, :], k, vv, scale=sc)[:, 0]
+    assert _rel(got, ref.numpy()) <= 1e-10
+
+
+def test_decode_single_key_closed_form(oracle):
+    a, (H, nope, rope, v, L, T) = _rand_decode(42)
+    got = oracle.absorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], [17], v, 0.2)
+    W = a["kv_b"].astype(np.float64).reshape(H, nope + v, L)
+    ref = W[:, nope:] @ a["lc"][17].astype(np.float64)
+    assert _rel(got, ref) <= 1e-12
+
+
+def test_decode_zero_query_is_uniform_average(oracle):
+    a, (H, nope, rope, v, L, T) = _rand_decode(43)
+    z1 = np.zeros_like(a["q_nope"])
+    z2 = np.zeros_like(a["q_rope"])
+    keys = np.arange(3, 41)
+    got = oracle.absorbed_decode(z1, z2, a["kv_b"], a["lc"], a["rc"], keys, v, 0.5)
+    W = a["kv_b"].astype(np.float64).reshape(H, nope + v, L)
+    ref = W[:, nope:] @ a["lc"][keys].astype(np.float64).mean(0)
+    assert _rel(got, ref) <= 1e-12
+
+
+def test_decode_dominant_key(oracle):
+    a, (H, nope, rope, v, L, T) = _rand_decode(44)
+    star = 29
+    rc = a["rc"].astype(np.float64)
+    gap = rc[star] @ rc[star] - np.max(np.delete(rc @ rc[star], star))
+    assert gap > 0
+    qr = np.tile(rc[star] * (80.0 / gap), (H, 1)).astype(np.float32)   # score margin >= ~80
+    got = oracle.absorbed_decode(np.zeros_like(a["q_nope"]), qr, a["kv_b"], a["lc"], a["rc"], np.arange(T), v, 1.0)
+    W = a["kv_b"].astype(np.float64).reshape(H, nope + v, L)
+    ref = W[:, nope:] @ a["lc"][star].astype(np.float64)
+    assert _rel(got, ref) <= 1e-9
+
+
+def test_decode_key_order_and_keep_all(oracle):
+    a, (H, nope, rope, v, L, T) = _rand_decode(45, T=90)
+    dense = np.arange(T)
+    perm = np.random.default_rng(2).permutation(T)
+    o1 = oracle.absorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], dense, v, 0.25)
+    o2 = oracle.absorbed_decode(a["q_nope"], a["q_rope"], a["kv_b"], a["lc"], a["rc"], perm, v, 0.25)
+    assert _rel(o1, o2) <= 1e-13
+    # a top-k that keeps every key selects exactly the dense key set
+    sel, nsel = oracle.topk(np.random.default_rng(3).standard_normal(T).astype(np.float32), T, 4 * T)
+    assert nsel == T and np.array_equal(sel[:nsel], dense)
+
+
+# ----------------------------------------------------------------------------- prefill
+def _rand_prefill(seed, S, pos_base, H=4, nope=16, rope=8, v=16, L=32):
+    rng = np.random.default_rng(seed)
+    T = pos_base + S
+    return dict(q=rng.standard_normal((S, H, nope + rope)).astype(np.float32),
+                kv_b=(rng.standard_normal((H * (nope + v), L)) * 0.3).astype(np.float32),
+                lc=rng.standard_normal((T, L)).astype(np.float32),
+                rc=rng.standard_normal((T, rope)).astype(np.float32)), (H, nope, rope, v, L, T)
+
+
+def test_prefill_first_row_is_first_value(oracle):
+    p, (H, nope, rope, v, L, T) = _rand_prefill(50, 9, 0)
+    got = oracle.prefill_rows(p["q"], p["kv_b"], p["lc"], p["rc"], 0, nope, v, 0.3, [0])[0]
+    W = p["kv_b"].astype(np.float64).reshape(H, nope + v, L)
+    assert _rel(got, W[:, nope:] @ p["lc"][0].astype(np.float64)) <= 1e-12
+
+
+def test_prefill_last_row_equals_decode(oracle):
+    p, (H, nope, rope, v, L, T) = _rand_prefill(51, 1, 63)
+    sc = 1 / math.sqrt(nope + rope)
+    got = oracle.prefill_rows(p["q"], p["kv_b"], p["lc"], p["rc"], 63, nope, v, sc, [0])[0]
+    ref = oracle.absorbed_decode(p["q"][0, :, :nope], p["q"][0, :, nope:], p["kv_b"], p["lc"], p["rc"],
+                                 np.arange(T), v, sc)
+    assert _rel(got, ref) <= 1e-10
+
+
+def test_prefill_matches_torch_causal_sdpa(oracle):
+    import torch
+    S, pb = 20, 7
+    p, (H, nope, rope, v, L, T) = _rand_prefill(52, S, pb, H=3, nope=10, rope=6, v=12, L=20)
+    sc = 0.29
+    got = oracle.prefill_rows(p["q"], p["kv_b"], p["lc"], p["rc"], pb, nope, v, sc, np.arange(S))
+    kvb = torch.from_numpy(p["kv_b"].astype(np.float64)).view(H, nope + v, L)
+    lc = torch.from_numpy(p["lc"].astype(np.float64))
+    rc = torch.from_numpy(p["rc"].astype(np.float64))
+    k = torch.cat([torch.einsum("hic,tc->hti", kvb[:, :nope], lc), rc.expand(H, -1, -1)], -1)
+    vv = torch.einsum("hjc,tc->htj", kvb[:, nope:], lc)
+    q = torch.from_numpy(p["q"].astype(np.float64)).permute(1, 0, 2)
+    mask = torch.arange(T)[None, :] <= (pb + torch.arange(S))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, vv, attn_mask=mask, scale=sc)
+    assert _rel(got, ref.permute(1, 0, 2).numpy()) <= 1e-10
+
+
+# ----------------------------------------------------------------------------- tiny layer
+def test_tiny_layer_pins(oracle):
+    from mla_latent_kv_dsa_amd import synth
+    t = synth.tiny_layer(1)
+    lc, rc, q = oracle.tiny_layer(t.x, t.q_a, t.q_b, t.kv_a, t.H, t.nope, t.rope, t.L)
+    # latent rows are RMS-normalised with unit gain: mean square = ms / (ms + eps)
+    comp = t.x.astype(np.float64) @ t.kv_a.astype(np.float64).T
+    ms = (comp[:, : t.L] ** 2).mean(1)
+    assert np.max(np.abs((lc ** 2).mean(1) - ms / (ms + 1e-6))) <= 1e-12
+    # the shared rope key is the rotated tail of the kv_a projection (pair norms kept)
+    tail = comp[:, t.L:]
+    n_in = tail[:, 0::2] ** 2 + tail[:, 1::2] ** 2
+    n_out = rc[:, : t.rope // 2] ** 2 + rc[:, t.rope // 2:] ** 2
+    assert np.max(np.abs(n_in - n_out)) <= 1e-12 * n_in.max()
+    # the query's nope dims are untouched by RoPE: q_b . RMSNorm(q_a x)
+    qa = t.q_a.astype(np.float64) @ t.x[-1].astype(np.float64)
+    qa = qa / np.sqrt((qa ** 2).mean() + 1e-6)
+    qf = (t.q_b.astype(np.float64) @ qa).reshape(t.H, t.nope + t.rope)
+    assert np.max(np.abs(q[:, : t.nope] - qf[:, : t.nope])) <= 1e-12 * np.abs(qf).max()
+    sc = 1 / math.sqrt(t.nope + t.rope)
+    keys = np.arange(t.T)
+    o1 = oracle.absorbed_decode(q[:, : t.nope], q[:, t.nope:], t.kv_b, lc, rc, keys, t.v, sc)
+    o2 = oracle.nonabsorbed_decode(q[:, : t.nope], q[:, t.nope:], t.kv_b, lc, rc, keys, t.v, sc)
+    assert _rel(o1, o2) <= 1e-10
+    y = oracle.o_proj(t.o_w, o1)
+    assert _rel(y, t.o_w.astype(np.float64) @ o1.reshape(-1)) <= 1e-12
