@@ -1,0 +1,184 @@
+/*
+ * mla_dsa.h -- C ABI of libmla_dsa.so: Multi-head Latent Attention over a compressed KV
+ * cache, with a DSA lightning indexer, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two public pages:
+ *   chen3feng, "colibri-analysis 06: MLA attention and KV cache"  (cited below as [MLA])
+ *   aiknowledge.cn, "Ch.7 sec. 03: token-exact forward validation and faithful DSA" ([FDSA])
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers allocated and owned by the caller.  The library
+ *     never allocates, frees or synchronizes; scratch space is a caller-provided workspace
+ *     whose size the matching *_workspace_bytes() query returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is queued
+ *     asynchronously on it; results are ready when the stream reaches that point.
+ *   - Arguments that live on the host are validated before any HIP call.  A failed check
+ *     returns a negative status with nothing launched; mla_last_error() then holds a
+ *     message (thread-local).  Launch failures return MLA_ERR_HIP.
+ *   - Device-resident sizes (seq_len, n_valid, nsel, block tables) are read by the kernels.
+ *     They are clamped to the host-declared capacities, so contract violations give
+ *     unspecified values but never an out-of-bounds access.
+ *   - Row-major layouts; all strides are in elements.
+ *   - Shapes outside what the library implements return MLA_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_DSA_H
+#define MLA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_ARG = -1,         /* invalid pointer, size or stride                       */
+    MLA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype this library does not build  */
+    MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query returned  */
+    MLA_ERR_HIP = -4          /* a HIP launch or runtime call failed                   */
+} mla_status;
+
+typedef enum { MLA_FP32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Head geometry of one MLA layer ([MLA] sec. 2: qh = qk_nope + qk_rope,
+ * kvb_dim = n_heads * (qk_nope + v_head)). */
+typedef struct {
+    int32_t n_heads;
+    int32_t qk_nope;
+    int32_t qk_rope;
+    int32_t v_head;
+    int32_t kv_lora;
+} mla_dims;
+
+/* Compressed KV cache of a batch of sequences ([MLA] sec. 1; [FDSA] sec. 2).
+ * Each cached token is one row in three pools:
+ *   lc: latent row   [kv_lora]   (kv_dtype)   -- the RMS-normed latent Lc
+ *   rc: rope-key row [qk_rope]   (kv_dtype)   -- the rotated key Rc shared by all heads
+ *   ic: indexer row  [index_hd]  (fp32)       -- the DSA indexer key Ic (may be NULL
+ *                                                when no indexer call uses this view)
+ * Row of token t of sequence b:
+ *   paged      (block_table != NULL): block_table[b*max_blocks + t/block_size]*block_size
+ *                                     + t % block_size
+ *   contiguous (block_table == NULL): b*seq_stride + t
+ * seq_len[b] (device int32) counts the cached tokens of sequence b INCLUDING the current
+ * query's own token: a decode query sits at position seq_len[b]-1 and sees keys
+ * 0..seq_len[b]-1.  Rows outside [0, rows) are never touched. */
+typedef struct {
+    const void *lc;
+    const void *rc;
+    const float *ic;
+    int64_t rows;             /* rows in each pool                                      */
+    mla_dtype kv_dtype;       /* dtype of lc and rc                                     */
+    int32_t index_hd;         /* width of an ic row (0 if ic is NULL)                   */
+    const int32_t *block_table; /* device [B][max_blocks], or NULL for contiguous       */
+    int32_t block_size;       /* tokens per block (paged)                               */
+    int32_t max_blocks;       /* block-table row length (paged)                         */
+    int64_t seq_stride;       /* rows between consecutive sequences (contiguous)        */
+    const int32_t *seq_len;   /* device [B]                                             */
+    int64_t max_seq_len;      /* host bound: every seq_len[b] <= max_seq_len            */
+} mla_kv_view;
+
+/* ---------------------------------------------------------------------------------
+ * Interleaved partial RoPE, in place.  [MLA] sec. 2.1 (rope_interleave): only the
+ * qk_rope tail of each head rotates; the even/odd input pair (a, b) = (x[2j], x[2j+1])
+ * of the tail becomes out[j] = a*cos - b*sin, out[half+j] = b*cos + a*sin, half =
+ * rope_dim/2, angle = pos * theta^(-2j/rope_dim) (angle formed in double).  Used on each
+ * query head's tail (rope_off = qk_nope) and on the shared key Rc (n_heads = 1).
+ *   x          device, dtype dt; element (n, h, e) at n*tok_stride + h*head_stride + e
+ *   pos        device int32 [n_tok], the token positions
+ *   rope_dim   even, 2..512; dims outside [rope_off, rope_off+rope_dim) are untouched
+ * --------------------------------------------------------------------------------- */
+mla_status mla_rope_interleave(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads,
+                               int64_t tok_stride, int64_t head_stride, int32_t rope_off,
+                               int32_t rope_dim, const int32_t *pos, double theta,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * DSA lightning-indexer scores.  [MLA] sec. 2.2: per query and causal key t, a
+ * ReLU-gated, per-head-weighted score; [FDSA] sec. 2: the key cache Ic is fp32.
+ *   scores[b][t] = sum_h w_idx[b][h] * ReLU( sum_d q_idx[b][h][d] * Ic(b,t)[d] )
+ * evaluated in fp32 in a FIXED order (heads ascending; dims ascending; one fused
+ * multiply-add per product; ReLU; one fused multiply-add per head weight), so that the
+ * result is reproducible bit for bit and the selected key set is exact.
+ *   q_idx   device fp32 [B][n_ih][kv->index_hd]
+ *   w_idx   device fp32 [B][n_ih]
+ *   kv      host struct; kv->ic, kv->index_hd, layout and seq_len are used
+ *   scores  device fp32 [B][t_max]; t < min(seq_len[b], t_max) get the score, the rest of
+ *           the row is set to -INFINITY
+ * Supported: 1 <= n_ih <= 64, index_hd a multiple of 4 in [4, 256].
+ * --------------------------------------------------------------------------------- */
+mla_status dsa_index_scores(const float *q_idx, const float *w_idx, int32_t B, int32_t n_ih,
+                            const mla_kv_view *kv, int64_t t_max, float *scores, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Top-k causal key selection.  [MLA] sec. 2.2 (sort + threshold scan into
+ * dsa_sel / dsa_nsel; the top-2048 causal keys).  For each row b, among
+ * t < n = min(n_valid[b], t_max): order by score descending, then position ascending
+ * (-0.0 equals +0.0); keep the first nsel[b] = min(k, n); write them to sel[b][0..nsel)
+ * sorted by position ascending; sel[b][nsel..k) = -1.  No full sort is performed.
+ *   scores   device fp32 [B][t_max] (NaN is outside the contract)
+ *   n_valid  device int32 [B] (for decode: seq_len)
+ *   sel      device int32 [B][k];  nsel: device int32 [B]
+ *   ws       device workspace of at least dsa_topk_workspace_bytes(B, t_max, k) bytes
+ * Supported: 1 <= k <= 65536, t_max < 2^31.
+ * --------------------------------------------------------------------------------- */
+size_t dsa_topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
+mla_status dsa_topk_select(const float *scores, int32_t B, int64_t t_max,
+                           const int32_t *n_valid, int32_t k, int32_t *sel, int32_t *nsel,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Absorbed MLA decode, one query per sequence.  [MLA] sec. 2.3 (absorbed path):
+ *   q_abs[b][h]   = W_UK[h]^T q_nope[b][h]                    (fold W_UK into the query)
+ *   s[b][h][t]    = sm_scale * (q_abs[b][h] . Lc(b,t) + q_rope[b][h] . Rc(b,t))
+ *   p             = softmax over the attended keys t
+ *   clat[b][h]    = sum_t p[b][h][t] Lc(b,t)                   (softmax-weighted latent)
+ *   out[b][h]     = W_UV[h] clat[b][h]                         (apply W_UV)
+ * with W_UK[h] = kv_b rows [h*(qk_nope+v_head), +qk_nope) and W_UV[h] = the following
+ * v_head rows ([MLA] sec. 2: kvb_dim = H*(qk_nope+v_head)).
+ * Attended keys: sel == NULL -> every t < seq_len[b] (dense causal);
+ *                sel != NULL -> the positions sel[b*sel_stride + j], j < nsel[b]
+ *                (logical positions; entries >= seq_len[b] or < 0 are skipped).
+ *   q_nope  device [B][H][qk_nope], q_rope device [B][H][qk_rope] (already rotated), q_dt
+ *   kv_b    device [H*(qk_nope+v_head)][kv_lora], w_dt
+ *   out     device fp32 [B][H][v_head]
+ *   ws      workspace of at least mla_decode_workspace_bytes(d, B, max_keys) bytes, where
+ *           max_keys bounds the keys one sequence attends (sel_stride, or max_seq_len)
+ * A sequence with no attended key produces zeros.  q_dt, w_dt and kv->kv_dtype must match.
+ * --------------------------------------------------------------------------------- */
+size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t max_keys);
+mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt,
+                               const void *kv_b, mla_dtype w_dt, const mla_dims *d, int32_t B,
+                               const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel,
+                               int32_t sel_stride, float sm_scale, float *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Non-absorbed causal prefill of S queries of one sequence.  [MLA] sec. 2.3
+ * (non-absorbed path): one kv_b matmul rebuilds k_nope and v for every token,
+ *   [k_nope | v](t, h) = kv_b[h*(qk_nope+v_head) .. +qk_nope+v_head) . Lc(t),
+ * then causal attention: query i sits at position pos_base + i ([MLA] sec. 2:
+ * Tk = pos_base + S) and attends keys t <= pos_base + i with
+ *   s = sm_scale * (q[i][h][:qk_nope] . k_nope(t,h) + q[i][h][qk_nope:] . Rc(t)),
+ * softmax, out[i][h] = sum_t p v(t,h).
+ *   q     device [S][H][qk_nope+qk_rope] (tail already rotated), q_dt
+ *   kv    host struct for sequence 0 (seq_len is not read); rows 0..pos_base+S-1 used
+ *   out   device [S][H][v_head], out_dt
+ *   ws    workspace of at least mla_prefill_workspace_bytes(d, S, pos_base+S) bytes
+ * q_dt, w_dt and kv->kv_dtype must match.
+ * --------------------------------------------------------------------------------- */
+size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T);
+mla_status mla_prefill_nonabsorbed(const void *q, mla_dtype q_dt, const void *kv_b,
+                                   mla_dtype w_dt, const mla_dims *d, const mla_kv_view *kv,
+                                   int32_t S, int32_t pos_base, float sm_scale, void *out,
+                                   mla_dtype out_dt, void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status, and the detail of the last failure on this thread. */
+const char *mla_status_string(mla_status s);
+const char *mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DSA_H */

@@ -1,1 +1,307 @@
-"""MI355X-native MLA latent-KV decode with a DSA lightning indexer (binding loaded lazily)."""
+"""MI355X-native MLA latent-KV attention with a DSA lightning indexer.
+
+Thin binding over ``libmla_dsa.so`` (HIP for gfx950, built by ``mla_latent_kv_dsa_amd.build``).
+Each function has the name of the C entry point it calls and only marshals arguments:
+torch tensors become device pointers, torch's current stream becomes the HIP stream,
+and a non-OK status becomes an :class:`MlaError`.  Every step of the computation runs in
+the library's kernels; there is no other implementation behind these names.  If the
+library has not been built, every call raises.
+
+Pages the operations follow: chen3feng, "colibri-analysis 06: MLA attention and KV cache"
+(sec. 1, 2, 2.1, 2.2, 2.3) and aiknowledge.cn, "Ch.7 sec. 03: token-exact forward
+validation and faithful DSA" (sec. 2).  The header ``include/mla_dsa.h`` states the exact
+contract of each call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_dsa.so")
+
+MLA_OK, MLA_ERR_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
+MLA_FP32, MLA_BF16 = 0, 1
+
+EXPORTED = (
+    "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
+    "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_prefill_workspace_bytes",
+    "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("qk_nope", ctypes.c_int32), ("qk_rope", ctypes.c_int32),
+                ("v_head", ctypes.c_int32), ("kv_lora", ctypes.c_int32)]
+
+
+class mla_kv_view(ctypes.Structure):
+    _fields_ = [("lc", ctypes.c_void_p), ("rc", ctypes.c_void_p), ("ic", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("kv_dtype", ctypes.c_int), ("index_hd", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("seq_stride", ctypes.c_int64),
+                ("seq_len", ctypes.c_void_p), ("max_seq_len", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla_dsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_dsa_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    st = ctypes.c_int
+    L.mla_rope_interleave.argtypes = [P, ctypes.c_int, i64, i32, i64, i64, i32, i32, P, ctypes.c_double, P]
+    L.mla_rope_interleave.restype = st
+    L.dsa_index_scores.argtypes = [P, P, i32, i32, ctypes.POINTER(mla_kv_view), i64, P, P]
+    L.dsa_index_scores.restype = st
+    L.dsa_topk_workspace_bytes.argtypes = [i32, i64, i32]
+    L.dsa_topk_workspace_bytes.restype = ctypes.c_size_t
+    L.dsa_topk_select.argtypes = [P, i32, i64, P, i32, P, P, P, ctypes.c_size_t, P]
+    L.dsa_topk_select.restype = st
+    L.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
+    L.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_absorbed_decode.argtypes = [P, P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), i32,
+                                      ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P,
+                                      ctypes.c_size_t, P]
+    L.mla_absorbed_decode.restype = st
+    L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
+    L.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_prefill_nonabsorbed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims),
+                                          ctypes.POINTER(mla_kv_view), i32, i32, ctypes.c_float, P,
+                                          ctypes.c_int, P, ctypes.c_size_t, P]
+    L.mla_prefill_nonabsorbed.restype = st
+    L.mla_status_string.argtypes = [ctypes.c_int]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def mla_last_error() -> str:
+    return lib().mla_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MLA_OK:
+        raise MlaError(status, f"{mla_status_string(status)}: {mla_last_error()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_FP32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+class KvCache:
+    """Caller-owned compressed KV pools plus their layout (maps to ``mla_kv_view``).
+
+    lc: [rows, kv_lora] and rc: [rows, qk_rope] (float32 or bfloat16); ic: [rows, index_hd]
+    float32 or None.  Contiguous layout: token t of sequence b is row b*seq_stride + t.
+    Paged layout: block_table int32 [B, max_blocks], row = block_table[b, t//bs]*bs + t%bs.
+    seq_len: int32 [B] on the GPU (tokens cached including the query's own)."""
+
+    def __init__(self, lc, rc, ic=None, *, seq_len=None, max_seq_len: int, block_table=None,
+                 block_size: int = 0, seq_stride: int = 0):
+        _dev(lc, rc, ic, seq_len, block_table)
+        _contig(lc, rc, ic, seq_len, block_table)
+        if seq_len is not None and seq_len.dtype != torch.int32:
+            raise TypeError("seq_len must be int32")
+        if block_table is not None and block_table.dtype != torch.int32:
+            raise TypeError("block_table must be int32")
+        if ic is not None and ic.dtype != torch.float32:
+            raise TypeError("ic must be float32")
+        self.lc, self.rc, self.ic = lc, rc, ic
+        self.seq_len, self.block_table = seq_len, block_table
+        v = mla_kv_view()
+        v.lc, v.rc, v.ic = lc.data_ptr(), rc.data_ptr(), (ic.data_ptr() if ic is not None else None)
+        v.rows = lc.shape[0]
+        v.kv_dtype = _dt(lc)
+        v.index_hd = ic.shape[1] if ic is not None else 0
+        v.block_table = block_table.data_ptr() if block_table is not None else None
+        v.block_size = block_size
+        v.max_blocks = block_table.shape[1] if block_table is not None else 0
+        v.seq_stride = seq_stride
+        v.seq_len = seq_len.data_ptr() if seq_len is not None else None
+        v.max_seq_len = max_seq_len
+        for t in (rc, ic):
+            if t is not None and t.shape[0] != lc.shape[0]:
+                raise ValueError("lc, rc and ic must have the same number of rows")
+        self.view = v
+
+
+def mla_rope_interleave(x: torch.Tensor, pos: torch.Tensor, rope_off: int, rope_dim: int,
+                        theta: float = 10000.0) -> torch.Tensor:
+    """In-place interleaved partial RoPE on x [n_tok, n_heads, head_dim] (last dim unit
+    stride); pos int32 [n_tok].  Returns x."""
+    _dev(x, pos)
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [n_tok, n_heads, head_dim] with a unit-stride last dim")
+    if pos.dtype != torch.int32 or pos.shape != (x.shape[0],) or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32 [n_tok]")
+    if rope_off + rope_dim > x.shape[2]:
+        raise ValueError("rope_off + rope_dim exceeds head_dim")
+    _check(lib().mla_rope_interleave(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0), x.stride(1),
+                                     rope_off, rope_dim, _ptr(pos), float(theta), _stream(x.device)))
+    return x
+
+
+def dsa_index_scores(q_idx: torch.Tensor, w_idx: torch.Tensor, kv: KvCache, t_max: int,
+                     scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexer scores [B, t_max] float32 (fixed-order fp32; -inf beyond seq_len)."""
+    _dev(q_idx, w_idx, scores)
+    _contig(q_idx, w_idx, scores)
+    B, n_ih, hd = q_idx.shape
+    if w_idx.shape != (B, n_ih) or q_idx.dtype != torch.float32 or w_idx.dtype != torch.float32:
+        raise ValueError("q_idx [B, n_ih, hd] and w_idx [B, n_ih] must be float32")
+    if kv.ic is None or kv.ic.shape[1] != hd:
+        raise ValueError("kv.ic width must equal q_idx's last dim")
+    if scores is None:
+        scores = torch.empty((B, t_max), dtype=torch.float32, device=q_idx.device)
+    elif scores.shape != (B, t_max) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [B, t_max]")
+    _check(lib().dsa_index_scores(_ptr(q_idx), _ptr(w_idx), B, n_ih, ctypes.byref(kv.view), t_max,
+                                  _ptr(scores), _stream(q_idx.device)))
+    return scores
+
+
+def dsa_topk_workspace_bytes(B: int, t_max: int, k: int) -> int:
+    return int(lib().dsa_topk_workspace_bytes(B, t_max, k))
+
+
+def dsa_topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int, sel: Optional[torch.Tensor] = None,
+                    nsel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Top-k positions per row (score desc, position asc), ascending; returns (sel [B, k]
+    int32 with -1 padding, nsel [B] int32)."""
+    _dev(scores, n_valid, sel, nsel, ws)
+    _contig(scores, n_valid, sel, nsel, ws)
+    B, t_max = scores.shape
+    if scores.dtype != torch.float32 or n_valid.dtype != torch.int32 or n_valid.shape != (B,):
+        raise ValueError("scores float32 [B, t_max], n_valid int32 [B]")
+    dev = scores.device
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev) if nsel is None else nsel
+    need = dsa_topk_workspace_bytes(B, t_max, k)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().dsa_topk_select(_ptr(scores), B, t_max, _ptr(n_valid), k, _ptr(sel), _ptr(nsel), _ptr(ws),
+                                 ws.numel() * ws.element_size() if ws is not None else 0, _stream(dev)))
+    return sel, nsel
+
+
+def _dims(H: int, nope: int, rope: int, v: int, L: int) -> mla_dims:
+    d = mla_dims()
+    d.n_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora = H, nope, rope, v, L
+    return d
+
+
+def mla_decode_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, B: int, max_keys: int) -> int:
+    return int(lib().mla_decode_workspace_bytes(ctypes.byref(_dims(H, nope, rope, v, L)), B, max_keys))
+
+
+def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache,
+                        sm_scale: float, sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Absorbed MLA decode: q_nope [B, H, nope], q_rope [B, H, rope] (rotated),
+    kv_b [H*(nope+v), L]; sel int32 [B, k] / nsel int32 [B] or None for dense causal.
+    Returns out [B, H, v] float32."""
+    _dev(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    B, H, nope = q_nope.shape
+    rope = q_rope.shape[2]
+    L = kv_b.shape[1]
+    if q_rope.shape[:2] != (B, H) or kv_b.shape[0] % H:
+        raise ValueError("shape mismatch between q_nope, q_rope and kv_b")
+    v = kv_b.shape[0] // H - nope
+    if kv.lc.shape[1] != L or kv.rc.shape[1] != rope:
+        raise ValueError("cache widths must match kv_lora and qk_rope")
+    d = _dims(H, nope, rope, v, L)
+    sel_stride = 0
+    if sel is not None:
+        if sel.dtype != torch.int32 or sel.dim() != 2 or sel.shape[0] != B or nsel is None:
+            raise ValueError("sel must be int32 [B, k] with nsel int32 [B]")
+        if nsel.dtype != torch.int32 or nsel.shape != (B,):
+            raise ValueError("nsel must be int32 [B]")
+        sel_stride = sel.shape[1]
+    max_keys = sel_stride if sel is not None else kv.view.max_seq_len
+    if out is None:
+        out = torch.empty((B, H, v), dtype=torch.float32, device=q_nope.device)
+    need = int(lib().mla_decode_workspace_bytes(ctypes.byref(d), B, max_keys))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_absorbed_decode(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), _ptr(kv_b), _dt(kv_b),
+                                     ctypes.byref(d), B, ctypes.byref(kv.view), _ptr(sel), _ptr(nsel),
+                                     sel_stride, float(sm_scale), _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(q_nope.device)))
+    return out
+
+
+def mla_prefill_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, S: int, T: int) -> int:
+    return int(lib().mla_prefill_workspace_bytes(ctypes.byref(_dims(H, nope, rope, v, L)), S, T))
+
+
+def mla_prefill_nonabsorbed(q: torch.Tensor, kv_b: torch.Tensor, kv: KvCache, qk_nope: int, pos_base: int,
+                            sm_scale: float, out_dtype: torch.dtype = torch.float32,
+                            out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Non-absorbed causal prefill: q [S, H, nope+rope] (rotated tail), kv_b
+    [H*(nope+v), L]; query i at position pos_base+i.  Returns out [S, H, v]."""
+    _dev(q, kv_b, out, ws)
+    _contig(q, kv_b, out, ws)
+    S, H, qh = q.shape
+    rope = qh - qk_nope
+    L = kv_b.shape[1]
+    if kv_b.shape[0] % H:
+        raise ValueError("kv_b rows must be a multiple of the head count")
+    v = kv_b.shape[0] // H - qk_nope
+    d = _dims(H, qk_nope, rope, v, L)
+    if out is None:
+        out = torch.empty((S, H, v), dtype=out_dtype, device=q.device)
+    need = int(lib().mla_prefill_workspace_bytes(ctypes.byref(d), S, pos_base + S))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mla_prefill_nonabsorbed(_ptr(q), _dt(q), _ptr(kv_b), _dt(kv_b), ctypes.byref(d),
+                                         ctypes.byref(kv.view), S, pos_base, float(sm_scale), _ptr(out),
+                                         _dt(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(q.device)))
+    return out

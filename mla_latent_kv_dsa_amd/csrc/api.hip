@@ -1,0 +1,243 @@
+// api.hip -- the extern "C" entry points of libmla_dsa.so: argument validation (before any
+// HIP call), workspace queries, and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace mla {
+
+static thread_local char g_err[512];
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+mla_status fail(mla_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mla_status check_launch(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MLA_OK;
+}
+
+static bool valid_dtype(mla_dtype d) { return d == MLA_FP32 || d == MLA_BF16; }
+
+// Host-side checks of a KV view.  need_lc_rc / need_ic select which pools must exist.
+static mla_status check_view(const mla_kv_view *kv, int32_t B, bool need_lc_rc, bool need_ic,
+                             bool need_seq_len)
+{
+    if (!kv) return fail(MLA_ERR_ARG, "kv view is NULL");
+    if (need_lc_rc && (!kv->lc || !kv->rc)) return fail(MLA_ERR_ARG, "kv->lc / kv->rc is NULL");
+    if (need_ic && !kv->ic) return fail(MLA_ERR_ARG, "kv->ic is NULL");
+    if (!valid_dtype(kv->kv_dtype)) return fail(MLA_ERR_ARG, "kv->kv_dtype invalid");
+    if (kv->rows <= 0) return fail(MLA_ERR_ARG, "kv->rows must be positive");
+    if (need_seq_len && !kv->seq_len) return fail(MLA_ERR_ARG, "kv->seq_len is NULL");
+    if (kv->max_seq_len < 0) return fail(MLA_ERR_ARG, "kv->max_seq_len negative");
+    if (kv->max_seq_len >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "kv->max_seq_len >= 2^31");
+    if (kv->block_table) {
+        if (kv->block_size <= 0 || kv->max_blocks <= 0)
+            return fail(MLA_ERR_ARG, "paged view needs block_size > 0 and max_blocks > 0");
+        if ((int64_t)kv->max_blocks * kv->block_size < kv->max_seq_len)
+            return fail(MLA_ERR_ARG, "max_blocks * block_size (%lld) < max_seq_len (%lld)",
+                        (long long)kv->max_blocks * kv->block_size, (long long)kv->max_seq_len);
+        if (kv->rows % kv->block_size != 0)
+            return fail(MLA_ERR_ARG, "paged pools must hold whole blocks (rows %% block_size != 0)");
+    } else {
+        if (kv->seq_stride < 0) return fail(MLA_ERR_ARG, "kv->seq_stride negative");
+        if (B > 1 && kv->seq_stride < kv->max_seq_len)
+            return fail(MLA_ERR_ARG, "contiguous view: seq_stride < max_seq_len overlaps sequences");
+        if ((int64_t)(B > 0 ? B - 1 : 0) * kv->seq_stride + kv->max_seq_len > kv->rows)
+            return fail(MLA_ERR_ARG, "contiguous view: (B-1)*seq_stride + max_seq_len > rows");
+    }
+    return MLA_OK;
+}
+
+static mla_status check_dims(const mla_dims *d)
+{
+    if (!d) return fail(MLA_ERR_ARG, "dims is NULL");
+    if (d->n_heads <= 0 || d->qk_nope <= 0 || d->qk_rope <= 0 || d->v_head <= 0 || d->kv_lora <= 0)
+        return fail(MLA_ERR_ARG, "dims must be positive");
+    if (d->n_heads > 256 || d->qk_nope > 1024 || d->qk_rope > 512 || d->v_head > 1024 || d->kv_lora > 2048)
+        return fail(MLA_ERR_UNSUPPORTED, "dims beyond the supported range "
+                    "(n_heads<=256, qk_nope<=1024, qk_rope<=512, v_head<=1024, kv_lora<=2048)");
+    return MLA_OK;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char *mla_status_string(mla_status s)
+{
+    switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_ARG: return "MLA_ERR_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    }
+    return "MLA_ERR_UNKNOWN";
+}
+
+const char *mla_last_error(void) { return g_err; }
+
+mla_status mla_rope_interleave(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads,
+                               int64_t tok_stride, int64_t head_stride, int32_t rope_off,
+                               int32_t rope_dim, const int32_t *pos, double theta, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_dtype(dt)) return fail(MLA_ERR_ARG, "rope: dtype invalid");
+    if (n_tok < 0 || n_heads <= 0) return fail(MLA_ERR_ARG, "rope: n_tok < 0 or n_heads <= 0");
+    if (rope_dim <= 0 || (rope_dim & 1)) return fail(MLA_ERR_ARG, "rope: rope_dim must be even and positive");
+    if (rope_dim > 512) return fail(MLA_ERR_UNSUPPORTED, "rope: rope_dim > 512");
+    if (rope_off < 0 || tok_stride < 0 || head_stride < 0) return fail(MLA_ERR_ARG, "rope: negative offset or stride");
+    if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ARG, "rope: theta must be positive and finite");
+    if (n_tok == 0) return MLA_OK;
+    if (!x || !pos) return fail(MLA_ERR_ARG, "rope: x or pos is NULL");
+    if (n_heads > 1 && head_stride < rope_off + rope_dim)
+        return fail(MLA_ERR_ARG, "rope: head_stride smaller than rope_off + rope_dim");
+    if (n_tok > 1 && tok_stride < (int64_t)(n_heads - 1) * head_stride + rope_off + rope_dim)
+        return fail(MLA_ERR_ARG, "rope: tok_stride overlaps tokens");
+    return launch_rope(x, dt, n_tok, n_heads, tok_stride, head_stride, rope_off, rope_dim, pos, theta,
+                       (hipStream_t)stream);
+}
+
+mla_status dsa_index_scores(const float *q_idx, const float *w_idx, int32_t B, int32_t n_ih,
+                            const mla_kv_view *kv, int64_t t_max, float *scores, void *stream)
+{
+    g_err[0] = 0;
+    if (B < 0 || t_max < 0) return fail(MLA_ERR_ARG, "index: B or t_max negative");
+    if (n_ih <= 0) return fail(MLA_ERR_ARG, "index: n_ih must be positive");
+    if (n_ih > 64) return fail(MLA_ERR_UNSUPPORTED, "index: n_ih > 64");
+    mla_status st = check_view(kv, B, false, true, true);
+    if (st) return st;
+    if (kv->index_hd <= 0 || kv->index_hd % 4 != 0) return fail(MLA_ERR_ARG, "index: index_hd must be a positive multiple of 4");
+    if (kv->index_hd > 256) return fail(MLA_ERR_UNSUPPORTED, "index: index_hd > 256");
+    if (t_max >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "index: t_max >= 2^31");
+    if (B == 0 || t_max == 0) return MLA_OK;
+    if (!q_idx || !w_idx || !scores) return fail(MLA_ERR_ARG, "index: NULL tensor");
+    KvView v = to_view(*kv);
+    if (v.max_seq_len > t_max) v.max_seq_len = t_max;
+    return launch_index_scores(q_idx, w_idx, B, n_ih, kv->index_hd, v, t_max, scores, (hipStream_t)stream);
+}
+
+size_t dsa_topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k)
+{
+    if (B <= 0 || t_max <= 0 || k <= 0) return 0;
+    return topk_workspace_bytes(B, t_max, k);
+}
+
+mla_status dsa_topk_select(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid,
+                           int32_t k, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    g_err[0] = 0;
+    if (B < 0 || t_max < 0) return fail(MLA_ERR_ARG, "topk: B or t_max negative");
+    if (k <= 0) return fail(MLA_ERR_ARG, "topk: k must be positive");
+    if (k > 65536) return fail(MLA_ERR_UNSUPPORTED, "topk: k > 65536");
+    if (t_max >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "topk: t_max >= 2^31");
+    if (B == 0) return MLA_OK;
+    if (!scores && t_max > 0) return fail(MLA_ERR_ARG, "topk: scores is NULL");
+    if (!n_valid || !sel || !nsel) return fail(MLA_ERR_ARG, "topk: NULL tensor");
+    size_t need = dsa_topk_workspace_bytes(B, t_max, k);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MLA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    return launch_topk(scores, B, t_max, n_valid, k, sel, nsel, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t max_keys)
+{
+    if (!d || B <= 0 || max_keys < 0) return 0;
+    if (check_dims(d) != MLA_OK) return 0;
+    return decode_workspace_bytes(*d, B, max_keys, MLA_BF16) > decode_workspace_bytes(*d, B, max_keys, MLA_FP32)
+               ? decode_workspace_bytes(*d, B, max_keys, MLA_BF16)
+               : decode_workspace_bytes(*d, B, max_keys, MLA_FP32);
+}
+
+mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt,
+                               const void *kv_b, mla_dtype w_dt, const mla_dims *d, int32_t B,
+                               const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel,
+                               int32_t sel_stride, float sm_scale, float *out, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_dims(d);
+    if (st) return st;
+    if (B < 0) return fail(MLA_ERR_ARG, "decode: B negative");
+    if (!valid_dtype(q_dt) || !valid_dtype(w_dt)) return fail(MLA_ERR_ARG, "decode: dtype invalid");
+    st = check_view(kv, B, true, false, true);
+    if (st) return st;
+    if (q_dt != w_dt || q_dt != kv->kv_dtype)
+        return fail(MLA_ERR_UNSUPPORTED, "decode: q, kv_b and cache dtypes must match");
+    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "decode: sm_scale not finite");
+    if (sel) {
+        if (!nsel) return fail(MLA_ERR_ARG, "decode: sel given without nsel");
+        if (sel_stride <= 0) return fail(MLA_ERR_ARG, "decode: sel_stride must be positive");
+    }
+    if (B == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !kv_b || !out) return fail(MLA_ERR_ARG, "decode: NULL tensor");
+    int64_t max_keys = sel ? (int64_t)sel_stride : kv->max_seq_len;
+    size_t need = decode_workspace_bytes(*d, B, max_keys, q_dt);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MLA_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    return launch_decode(q_nope, q_rope, kv_b, q_dt, *d, B, to_view(*kv), sel, nsel, sel_stride, max_keys,
+                         sm_scale, out, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T)
+{
+    if (!d || S <= 0 || T <= 0) return 0;
+    if (check_dims(d) != MLA_OK) return 0;
+    size_t a = prefill_workspace_bytes(*d, S, T, MLA_BF16), b = prefill_workspace_bytes(*d, S, T, MLA_FP32);
+    return a > b ? a : b;
+}
+
+mla_status mla_prefill_nonabsorbed(const void *q, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
+                                   const mla_dims *d, const mla_kv_view *kv, int32_t S,
+                                   int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt,
+                                   void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_dims(d);
+    if (st) return st;
+    if (S < 0 || pos_base < 0) return fail(MLA_ERR_ARG, "prefill: S or pos_base negative");
+    if (!valid_dtype(q_dt) || !valid_dtype(w_dt) || !valid_dtype(out_dt)) return fail(MLA_ERR_ARG, "prefill: dtype invalid");
+    if (!kv) return fail(MLA_ERR_ARG, "prefill: kv view is NULL");
+    int64_t T = (int64_t)pos_base + S;
+    if (T >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "prefill: pos_base + S >= 2^31");
+    mla_kv_view v1 = *kv;
+    if (v1.max_seq_len < T) v1.max_seq_len = T;   // the prefill covers rows 0..T-1 of sequence 0
+    st = check_view(&v1, 1, true, false, false);
+    if (st) return st;
+    if (q_dt != w_dt || q_dt != kv->kv_dtype)
+        return fail(MLA_ERR_UNSUPPORTED, "prefill: q, kv_b and cache dtypes must match");
+    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "prefill: sm_scale not finite");
+    if (S == 0) return MLA_OK;
+    if (!q || !kv_b || !out) return fail(MLA_ERR_ARG, "prefill: NULL tensor");
+    size_t need = prefill_workspace_bytes(*d, S, T, q_dt);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MLA_ERR_WORKSPACE, "prefill: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    KvView v = to_view(v1);
+    v.seq_len = nullptr;   // sequence 0 spans rows for t < T
+    v.max_seq_len = T;
+    return launch_prefill(q, kv_b, q_dt, *d, v, S, pos_base, sm_scale, out, out_dt, ws, ws_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"

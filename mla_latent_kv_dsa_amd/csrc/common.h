@@ -1,0 +1,132 @@
+// common.h -- internal helpers shared by the HIP kernels of libmla_dsa (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla_dsa.h"
+
+namespace mla {
+
+// ------------------------------------------------------------------ error reporting
+void set_error(const char *fmt, ...);
+mla_status fail(mla_status s, const char *fmt, ...);
+// Check the last launch; returns MLA_ERR_HIP (with the HIP message) on failure.
+mla_status check_launch(const char *what);
+
+// ------------------------------------------------------------------ bf16 as raw bits
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to nearest even (inputs here are finite)
+__device__ __forceinline__ bf16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float ld(const T *p);
+template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t *p) { return bf2f(*p); }
+
+template <typename T> __device__ __forceinline__ void st(T *p, float v);
+template <> __device__ __forceinline__ void st<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<bf16_t>(bf16_t *p, float v) { *p = f2bf(v); }
+
+// ------------------------------------------------------------------ KV cache addressing
+// Device-side copy of mla_kv_view (passed by value to kernels).
+struct KvView {
+    const void *lc;
+    const void *rc;
+    const float *ic;
+    int64_t rows;
+    const int32_t *bt;
+    int32_t bs;
+    int32_t max_blocks;
+    int64_t seq_stride;
+    const int32_t *seq_len;
+    int64_t max_seq_len;
+};
+
+inline KvView to_view(const mla_kv_view &v)
+{
+    KvView k;
+    k.lc = v.lc;
+    k.rc = v.rc;
+    k.ic = v.ic;
+    k.rows = v.rows;
+    k.bt = v.block_table;
+    k.bs = v.block_size > 0 ? v.block_size : 1;
+    k.max_blocks = v.max_blocks;
+    k.seq_stride = v.seq_stride;
+    k.seq_len = v.seq_len;
+    k.max_seq_len = v.max_seq_len;
+    return k;
+}
+
+// Pool row of logical token t of sequence b, or -1 if it falls outside the pools.
+// t must satisfy 0 <= t < max_seq_len (callers clamp), so the table index is in range.
+__device__ __forceinline__ int64_t kv_row(const KvView &v, int b, int64_t t)
+{
+    int64_t r;
+    if (v.bt) {
+        int32_t blk = v.bt[(int64_t)b * v.max_blocks + t / v.bs];
+        r = (int64_t)blk * v.bs + t % v.bs;
+    } else {
+        r = (int64_t)b * v.seq_stride + t;
+    }
+    return (r >= 0 && r < v.rows) ? r : -1;
+}
+
+// seq_len[b] clamped to [0, max_seq_len].
+__device__ __forceinline__ int64_t seq_len_of(const KvView &v, int b)
+{
+    int64_t s = v.seq_len ? (int64_t)v.seq_len[b] : v.max_seq_len;
+    if (s < 0) s = 0;
+    if (s > v.max_seq_len) s = v.max_seq_len;
+    return s;
+}
+
+// ------------------------------------------------------------------ wave helpers (wave64)
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// ------------------------------------------------------------------ internal launchers
+mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, int64_t tok_stride,
+                       int64_t head_stride, int32_t rope_off, int32_t rope_dim, const int32_t *pos,
+                       double theta, hipStream_t s);
+
+mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih,
+                               int32_t hd, const KvView &kv, int64_t t_max, float *scores,
+                               hipStream_t s);
+
+size_t topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
+mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid,
+                       int32_t k, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes,
+                       hipStream_t s);
+
+size_t decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t max_keys, mla_dtype dt);
+mla_status launch_decode(const void *q_nope, const void *q_rope, const void *kv_b, mla_dtype dt,
+                         const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
+                         const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
+                         float sm_scale, float *out, void *ws, size_t ws_bytes, hipStream_t s);
+
+size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt);
+mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d,
+                          const KvView &kv, int32_t S, int32_t pos_base, float sm_scale,
+                          void *out, mla_dtype out_dt, void *ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,23 @@
+// decode_plan.h -- split-K planning and internal launchers of the absorbed decode.
+#pragma once
+#include "common.h"
+
+namespace mla {
+
+// Splits of the attended keys for the generic decode: enough (b, h, split) blocks to fill
+// the chip at batch 1, at most 64 so the partial buffers stay small.
+inline int generic_splits(int64_t max_keys)
+{
+    int64_t ns = (max_keys + 127) / 128;
+    if (ns < 1) ns = 1;
+    if (ns > 64) ns = 64;
+    return (int)ns;
+}
+
+size_t decode_generic_ws(const mla_dims &d, int32_t B, int64_t max_keys);
+mla_status launch_decode_generic(const void *q_nope, const void *q_rope, const void *kv_b, mla_dtype dt,
+                                 const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
+                                 const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale,
+                                 float *out, void *ws, hipStream_t s);
+
+}  // namespace mla

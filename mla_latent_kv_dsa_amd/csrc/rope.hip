@@ -1,0 +1,66 @@
+// rope.hip -- interleaved partial RoPE, in place.
+// colibri-analysis 06 "MLA attention and KV cache", sec. 2.1: only the qk_rope tail of a
+// head rotates; input pair (a, b) = (x[2j], x[2j+1]) of the tail becomes
+// out[j] = a cos - b sin and out[half + j] = b cos + a sin.  The angle pos * theta^(-2j/rope)
+// is formed and reduced in double (an fp32 angle at position ~1e5 is off by ~1e-2 rad); the
+// rotation itself runs in fp32.
+#include "common.h"
+
+namespace mla {
+
+// One (token, head) tail is a "unit"; a block of 256 threads handles 256/half units, one
+// thread per rotation pair.  Every thread reads its pair before any thread writes, because
+// the half-split output slots of one unit overlap the interleaved input slots of others.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T *__restrict__ x, int64_t n_units, int32_t n_heads,
+                                                   int64_t tok_stride, int64_t head_stride,
+                                                   int32_t rope_off, int32_t half,
+                                                   const int32_t *__restrict__ pos, double theta,
+                                                   int32_t units_per_block)
+{
+    const int tid = threadIdx.x;
+    const int u_local = tid / half;
+    const int j = tid - u_local * half;
+    const int64_t unit = (int64_t)blockIdx.x * units_per_block + u_local;
+    const bool active = u_local < units_per_block && unit < n_units;
+    T *tail = nullptr;
+    float a = 0.f, b = 0.f, c = 1.f, s = 0.f;
+    if (active) {
+        const int64_t n = unit / n_heads;
+        const int32_t h = (int32_t)(unit - n * n_heads);
+        tail = x + n * tok_stride + (int64_t)h * head_stride + rope_off;
+        a = ld(tail + 2 * j);
+        b = ld(tail + 2 * j + 1);
+        const double inv = pow(theta, -2.0 * (double)j / (double)(2 * half));
+        const double phi = (double)pos[n] * inv;
+        double sd, cd;
+        sincos(phi, &sd, &cd);
+        c = (float)cd;
+        s = (float)sd;
+    }
+    __syncthreads();
+    if (active) {
+        st(tail + j, a * c - b * s);
+        st(tail + half + j, b * c + a * s);
+    }
+}
+
+mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, int64_t tok_stride,
+                       int64_t head_stride, int32_t rope_off, int32_t rope_dim, const int32_t *pos,
+                       double theta, hipStream_t s)
+{
+    const int32_t half = rope_dim / 2;
+    const int32_t upb = 256 / half;
+    const int64_t n_units = n_tok * n_heads;
+    const int64_t blocks = (n_units + upb - 1) / upb;
+    if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "rope: too many units");
+    if (dt == MLA_FP32)
+        hipLaunchKernelGGL(rope_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (float *)x, n_units,
+                           n_heads, tok_stride, head_stride, rope_off, half, pos, theta, upb);
+    else
+        hipLaunchKernelGGL(rope_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (bf16_t *)x, n_units,
+                           n_heads, tok_stride, head_stride, rope_off, half, pos, theta, upb);
+    return check_launch("rope_kernel");
+}
+
+}  // namespace mla

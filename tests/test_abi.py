@@ -1,0 +1,183 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/mla_dsa.h declares, and its host-side validation returns the documented status
+before any HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_latent_kv_dsa_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_dsa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.fail("libmla_dsa.so is not built (python -m mla_latent_kv_dsa_amd.build)")
+    return mla.lib()
+
+
+def test_header_declares_the_five_calls():
+    fns = _declared_functions()
+    for name in ("mla_rope_interleave", "dsa_index_scores", "dsa_topk_select", "mla_absorbed_decode",
+                 "mla_prefill_nonabsorbed"):
+        assert name in fns
+    assert set(fns) == set(mla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for fn in _declared_functions():
+        assert fn in exported, fn
+        assert hasattr(L, fn)
+
+
+def test_status_strings(L):
+    assert mla.mla_status_string(0) == "MLA_OK"
+    assert mla.mla_status_string(-3) == "MLA_ERR_WORKSPACE"
+    assert mla.mla_status_string(-99) == "MLA_ERR_UNKNOWN"
+
+
+# Fake (never dereferenced) device addresses: every call below fails host validation first.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _no_gpu():
+    # On a GPU machine an unexpected pass of validation would launch on fake pointers;
+    # these checks are host logic and run where no GPU is visible.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation tests run without a GPU")
+
+
+def _view(**kw):
+    v = mla.mla_kv_view()
+    v.lc, v.rc, v.ic = 0x1000, 0x2000, 0x3000
+    v.rows, v.kv_dtype, v.index_hd = 4096, mla.MLA_BF16, 128
+    v.block_table, v.block_size, v.max_blocks = None, 0, 0
+    v.seq_stride, v.seq_len, v.max_seq_len = 4096, 0x4000, 4096
+    for k, val in kw.items():
+        setattr(v, k, val)
+    return v
+
+
+def _dims(**kw):
+    d = mla.mla_dims()
+    d.n_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora = 64, 192, 64, 256, 512
+    for k, val in kw.items():
+        setattr(d, k, val)
+    return d
+
+
+def test_rope_validation(L):
+    _no_gpu()
+    r = lambda **kw: L.mla_rope_interleave(FAKE, kw.get("dt", 0), kw.get("n", 4), kw.get("h", 2),
+                                            kw.get("ts", 512), kw.get("hs", 256), kw.get("off", 192),
+                                            kw.get("rd", 64), FAKE, kw.get("theta", 1e4), None)
+    assert r(rd=63) == mla.MLA_ERR_ARG
+    assert r(rd=0) == mla.MLA_ERR_ARG
+    assert r(rd=1024) == mla.MLA_ERR_UNSUPPORTED
+    assert r(dt=7) == mla.MLA_ERR_ARG
+    assert r(theta=-1.0) == mla.MLA_ERR_ARG
+    assert r(hs=100) == mla.MLA_ERR_ARG          # heads overlap
+    assert r(ts=300) == mla.MLA_ERR_ARG          # tokens overlap
+    assert r(n=0) == mla.MLA_OK                  # nothing to do, nothing launched
+    assert "rope" in mla.mla_last_error() or mla.mla_last_error() == ""
+
+
+def test_index_validation(L):
+    _no_gpu()
+    f = lambda B=1, n_ih=32, v=None, t_max=4096: L.dsa_index_scores(FAKE, FAKE, B, n_ih, ctypes.byref(v or _view()), t_max, FAKE, None)
+    assert f(n_ih=0) == mla.MLA_ERR_ARG
+    assert f(n_ih=65) == mla.MLA_ERR_UNSUPPORTED
+    assert f(v=_view(ic=None)) == mla.MLA_ERR_ARG
+    assert f(v=_view(index_hd=130)) == mla.MLA_ERR_ARG
+    assert f(v=_view(index_hd=512)) == mla.MLA_ERR_UNSUPPORTED
+    assert f(v=_view(seq_len=None)) == mla.MLA_ERR_ARG
+    assert f(B=2, v=_view(seq_stride=100)) == mla.MLA_ERR_ARG          # sequences overlap
+    assert f(B=2, v=_view(rows=5000)) == mla.MLA_ERR_ARG               # second sequence past the pool
+    assert f(v=_view(block_table=0x5000, block_size=64, max_blocks=10)) == mla.MLA_ERR_ARG  # table too short
+    assert f(v=_view(block_table=0x5000, block_size=64, max_blocks=64, rows=4000)) == mla.MLA_ERR_ARG
+    assert f(t_max=1 << 31) == mla.MLA_ERR_UNSUPPORTED
+    assert f(B=0) == mla.MLA_OK
+
+
+def test_topk_validation(L):
+    _no_gpu()
+    f = lambda B=1, t=4096, k=2048, ws=None, wsb=0: L.dsa_topk_select(FAKE, B, t, FAKE, k, FAKE, FAKE, ws, wsb, None)
+    assert f(k=0) == mla.MLA_ERR_ARG
+    assert f(k=70000) == mla.MLA_ERR_UNSUPPORTED
+    assert f(B=-1) == mla.MLA_ERR_ARG
+    assert f(t=1 << 31) == mla.MLA_ERR_UNSUPPORTED
+    assert L.dsa_topk_select(FAKE, 1, 4096, None, 8, FAKE, FAKE, None, 0, None) == mla.MLA_ERR_ARG
+    need = L.dsa_topk_workspace_bytes(1, 4096, 2048)
+    if need:
+        assert f(ws=None) == mla.MLA_ERR_WORKSPACE
+        assert f(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert f(B=0) == mla.MLA_OK
+
+
+def test_decode_validation(L):
+    _no_gpu()
+    d = _dims()
+
+    def f(d=d, B=1, v=None, q_dt=1, w_dt=1, sel=None, nsel=None, sel_stride=0, ws=None, wsb=0, scale=0.0625):
+        return L.mla_absorbed_decode(FAKE, FAKE, q_dt, FAKE, w_dt, ctypes.byref(d), B, ctypes.byref(v or _view()),
+                                     sel, nsel, sel_stride, scale, FAKE, ws, wsb, None)
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 4096)
+    assert need > 0
+    assert f() == mla.MLA_ERR_WORKSPACE
+    assert f(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert f(d=_dims(n_heads=0)) == mla.MLA_ERR_ARG
+    assert f(d=_dims(kv_lora=4096)) == mla.MLA_ERR_UNSUPPORTED
+    assert f(q_dt=0) == mla.MLA_ERR_UNSUPPORTED         # mixed dtypes
+    assert f(q_dt=5) == mla.MLA_ERR_ARG
+    assert f(sel=FAKE, nsel=None, sel_stride=2048) == mla.MLA_ERR_ARG
+    assert f(sel=FAKE, nsel=FAKE, sel_stride=0) == mla.MLA_ERR_ARG
+    assert f(v=_view(lc=None)) == mla.MLA_ERR_ARG
+    assert f(scale=float("inf")) == mla.MLA_ERR_ARG
+    assert f(B=0) == mla.MLA_OK
+
+
+def test_prefill_validation(L):
+    _no_gpu()
+    d = _dims()
+
+    def f(S=4096, pb=0, v=None, ws=None, wsb=0, out_dt=0):
+        return L.mla_prefill_nonabsorbed(FAKE, 1, FAKE, 1, ctypes.byref(d), ctypes.byref(v or _view(seq_len=None)),
+                                         S, pb, 0.0625, FAKE, out_dt, ws, wsb, None)
+    need = L.mla_prefill_workspace_bytes(ctypes.byref(d), 4096, 4096)
+    assert need > 0
+    assert f() == mla.MLA_ERR_WORKSPACE
+    assert f(S=-1) == mla.MLA_ERR_ARG
+    assert f(out_dt=9) == mla.MLA_ERR_ARG
+    assert f(S=4000, pb=200) == mla.MLA_ERR_ARG          # rows 0..4199 exceed the 4096-row pool
+    assert f(S=0) == mla.MLA_OK
+
+
+def test_workspace_queries_are_host_only(L):
+    d = _dims()
+    assert L.mla_decode_workspace_bytes(ctypes.byref(d), 32, 2048) >= L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 2048)
+    assert L.mla_decode_workspace_bytes(None, 1, 2048) == 0
+    assert L.mla_prefill_workspace_bytes(ctypes.byref(d), 4096, 4096) >= 4096 * 64 * (192 + 256) * 2
+    assert L.dsa_topk_workspace_bytes(0, 10, 10) == 0
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(mla, "_lib", None)
+    monkeypatch.setattr(mla, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        mla.lib()

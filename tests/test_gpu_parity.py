@@ -1,0 +1,332 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: selected index sets and nsel bit-exact; indexer scores bit-exact (fixed fp32
+order); attention outputs within rel = max|g-r|/max|r| <= 2e-3 for fp32 inputs and 1e-2
+for bf16 inputs; RoPE within a few fp32 ulps (fp32) or one bf16 ulp (bf16), untouched dims
+bit-exact.  Pages: chen3feng, "colibri-analysis 06: MLA attention and KV cache" (sec. 2.1,
+2.2, 2.3); aiknowledge.cn, "Ch.7 sec. 03 ... faithful DSA" (sec. 2).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_latent_kv_dsa_amd import synth
+from tests.helpers import dev, dev_bf16, host, log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mla_latent_kv_dsa_amd as mla  # noqa: E402
+
+TOL_F32, TOL_BF16 = 2e-3, 1e-2
+
+
+def _kv(lc, rc, ic=None, seq_len=None, max_seq_len=0, block_table=None, block_size=0, seq_stride=0, bf16=True):
+    to = dev_bf16 if bf16 else dev
+    return mla.KvCache(to(lc), to(rc), dev(ic) if ic is not None else None,
+                       seq_len=dev(np.asarray(seq_len, np.int32)) if seq_len is not None else None,
+                       max_seq_len=max_seq_len,
+                       block_table=dev(block_table) if block_table is not None else None,
+                       block_size=block_size, seq_stride=seq_stride)
+
+
+# ------------------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("bf16", [False, True])
+def test_rope_query_tails_and_shared_key(bf16):
+    rng = np.random.default_rng(100)
+    n, H, nope, rope = 37, 64, 192, 64
+    x = rng.standard_normal((n, H, nope + rope)).astype(np.float32)
+    pos = rng.integers(0, 131072, n).astype(np.int32)
+    pos[0] = 0
+    pos[1] = 131071
+    xin = synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) if bf16 else x
+    log(f"rope q tails bf16={bf16} n={n}")
+    t = dev_bf16(synth.to_bf16_bits(x)) if bf16 else dev(x)
+    mla.mla_rope_interleave(t, dev(pos), nope, rope)
+    got = host(t)
+    ref = oracle.rope_interleave(xin, pos, nope, rope)
+    assert np.array_equal(got[..., :nope], xin[..., :nope])
+    err = np.abs(got - ref)
+    if bf16:
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-6 * np.abs(xin).max())
+    else:
+        assert err.max() <= 2e-6 * np.abs(xin).max()
+    # the shared key Rc: one head, offset 0, rows of a cache
+    rc = rng.standard_normal((300, 1, rope)).astype(np.float32)
+    pr = np.arange(300, dtype=np.int32) * 400
+    rin = synth.bf16_bits_to_f32(synth.to_bf16_bits(rc)) if bf16 else rc
+    t = dev_bf16(synth.to_bf16_bits(rc)) if bf16 else dev(rc)
+    mla.mla_rope_interleave(t, dev(pr), 0, rope)
+    ref = oracle.rope_interleave(rin, pr, 0, rope)
+    err = np.abs(host(t) - ref)
+    if bf16:
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-6 * np.abs(rin).max())
+    else:
+        assert err.max() <= 2e-6 * np.abs(rin).max()
+
+
+def test_rope_strided_view_and_odd_geometry():
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((9, 3, 40)).astype(np.float32)
+    pos = rng.integers(0, 5000, 9).astype(np.int32)
+    full = dev(x)
+    view = full[:, :, :]                     # strides (120, 40, 1)
+    mla.mla_rope_interleave(view, dev(pos), 10, 22)
+    ref = oracle.rope_interleave(x, pos, 10, 22)
+    got = host(full)
+    assert np.array_equal(got[..., :10], x[..., :10]) and np.array_equal(got[..., 32:], x[..., 32:])
+    assert np.abs(got - ref).max() <= 2e-6 * np.abs(x).max()
+
+
+# ------------------------------------------------------------------------------ indexer
+def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed):
+    rng = np.random.default_rng(seed)
+    if paged:
+        bs = 64
+        nb = [(s + bs - 1) // bs for s in seq_len]
+        perm = rng.permutation(sum(nb)).astype(np.int32)
+        max_blocks = (t_max + bs - 1) // bs
+        bt = np.full((B, max_blocks), -1, np.int32)
+        o = 0
+        for b in range(B):
+            bt[b, : nb[b]] = perm[o: o + nb[b]]
+            o += nb[b]
+        rows = sum(nb) * bs
+        ic = rng.standard_normal((rows, hd)).astype(np.float32)
+        logical = [ic[(bt[b, np.arange(seq_len[b]) // bs].astype(np.int64) * bs + np.arange(seq_len[b]) % bs)]
+                   for b in range(B)]
+        kvd = dict(block_table=bt, block_size=bs)
+    else:
+        stride = t_max
+        ic = rng.standard_normal((B * stride, hd)).astype(np.float32)
+        logical = [ic[b * stride: b * stride + seq_len[b]] for b in range(B)]
+        kvd = dict(seq_stride=stride)
+    q = rng.standard_normal((B, n_ih, hd)).astype(np.float32)
+    w = rng.standard_normal((B, n_ih)).astype(np.float32)
+    lc = np.zeros((ic.shape[0], 8), np.uint16)
+    rc = np.zeros((ic.shape[0], 8), np.uint16)
+    kv = _kv(lc, rc, ic, seq_len, t_max, **kvd)
+    return q, w, kv, logical
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("n_ih,hd", [(32, 128), (5, 64), (1, 4)])
+def test_index_scores_bit_exact(paged, n_ih, hd):
+    B, t_max = 3, 1100
+    seq_len = [1100, 777, 1]
+    log(f"index paged={paged} n_ih={n_ih} hd={hd}")
+    q, w, kv, logical = _index_case(B, seq_len, t_max, n_ih, hd, paged, 200 + n_ih + paged)
+    s = host(mla.dsa_index_scores(dev(q), dev(w), kv, t_max))
+    for b in range(B):
+        ref = oracle.index_scores(q[b], w[b], logical[b])
+        assert np.array_equal(s[b, : seq_len[b]].view(np.uint32), ref.view(np.uint32)), b
+        assert np.all(np.isneginf(s[b, seq_len[b]:]))
+
+
+def test_index_scores_full_context_131072():
+    d = synth.decode(3, 131072, dsa=True, bf16=True)
+    log("index full T=131072")
+    kv = _kv(d.lc, d.rc, d.ic, [d.T], d.T, seq_stride=d.T)
+    s = host(mla.dsa_index_scores(dev(d.q_idx), dev(d.w_idx), kv, d.T))[0]
+    ref = oracle.index_scores(d.q_idx[0], d.w_idx[0], d.ic)
+    assert np.array_equal(s.view(np.uint32), ref.view(np.uint32))
+
+
+def test_index_empty_and_zero_length():
+    q, w, kv, logical = _index_case(2, [0, 5], 64, 32, 128, False, 250)
+    s = host(mla.dsa_index_scores(dev(q), dev(w), kv, 64))
+    assert np.all(np.isneginf(s[0])) and np.all(np.isneginf(s[1, 5:]))
+    assert np.array_equal(s[1, :5], oracle.index_scores(q[1], w[1], logical[1]))
+
+
+# ------------------------------------------------------------------------------ top-k
+def _topk_check(scores, n_valid, k):
+    sel, nsel = mla.dsa_topk_select(dev(scores), dev(np.asarray(n_valid, np.int32)), k)
+    rs, rn = oracle.topk_batch(scores, np.asarray(n_valid, np.int32), k)
+    assert np.array_equal(host(nsel), rn)
+    assert np.array_equal(host(sel), rs)
+
+
+@pytest.mark.parametrize("seed", [300, 301])
+def test_topk_bit_exact_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    B, T = 5, 9000
+    s = (np.round(rng.standard_normal((B, T)) * 4) / 4).astype(np.float32)   # heavy ties
+    s[0, ::7] = -0.0
+    s[1, ::5] = 0.0
+    s[2] = 1.5                                                                # all equal
+    n_valid = [9000, 8191, 4000, 2048, 0]
+    log(f"topk ties seed={seed}")
+    for k in (1, 7, 2048, 3000):
+        _topk_check(s, n_valid, k)
+
+
+def test_topk_random_full_context():
+    rng = np.random.default_rng(302)
+    T = 131072
+    s = rng.standard_normal((2, T)).astype(np.float32)
+    log("topk T=131072")
+    _topk_check(s, [T, 100001], 2048)
+
+
+def test_topk_special_values():
+    s = np.array([[np.inf, -np.inf, 3.0, -0.0, 0.0, 1e-38, -1e-38, 3.0, 2.0, -5.0]], np.float32)
+    for k in range(1, 11):
+        _topk_check(s, [10], k)
+
+
+# ------------------------------------------------------------------------------ decode
+def _decode_ref(d, b, keys, sm, absorbed=True):
+    f = oracle.absorbed_decode if absorbed else oracle.nonabsorbed_decode
+    cv = synth.bf16_bits_to_f32 if d.bf16 else (lambda a: a)
+    lc = cv(d.lc[b * d.T:(b + 1) * d.T])
+    rc = cv(d.rc[b * d.T:(b + 1) * d.T])
+    return f(cv(d.q_nope[b]), cv(d.q_rope[b]), cv(d.kv_b), lc, rc, keys, d.v, sm)
+
+
+def _run_decode(d, seq_len, sel=None, nsel=None, paged=None):
+    to = dev_bf16 if d.bf16 else dev
+    kv = _kv(d.lc, d.rc, None, seq_len, d.T, seq_stride=d.T, bf16=d.bf16)
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    out = mla.mla_absorbed_decode(to(d.q_nope), to(d.q_rope), to(d.kv_b), kv, sm,
+                                  sel=dev(sel) if sel is not None else None,
+                                  nsel=dev(nsel) if nsel is not None else None)
+    return host(out), sm
+
+
+def test_decode_tiny_fp32_layer_absorbed_equals_nonabsorbed():
+    t = synth.tiny_layer(1)
+    lc, rc, q = oracle.tiny_layer(t.x, t.q_a, t.q_b, t.kv_a, t.H, t.nope, t.rope, t.L)
+    lc32, rc32, q32 = lc.astype(np.float32), rc.astype(np.float32), q.astype(np.float32)
+    sm = 1.0 / math.sqrt(t.nope + t.rope)
+    log("decode tiny fp32")
+    kv = mla.KvCache(dev(lc32), dev(rc32), seq_len=dev(np.array([t.T], np.int32)), max_seq_len=t.T, seq_stride=t.T)
+    out = host(mla.mla_absorbed_decode(dev(q32[None, :, : t.nope].copy()), dev(q32[None, :, t.nope:].copy()),
+                                       dev(t.kv_b), kv, sm))[0]
+    keys = np.arange(t.T)
+    ref_a = oracle.absorbed_decode(q32[:, : t.nope], q32[:, t.nope:], t.kv_b, lc32, rc32, keys, t.v, sm)
+    ref_n = oracle.nonabsorbed_decode(q32[:, : t.nope], q32[:, t.nope:], t.kv_b, lc32, rc32, keys, t.v, sm)
+    assert rel_err(out, ref_a) <= TOL_F32
+    assert rel_err(out, ref_n) <= TOL_F32
+    # the layer output after o_proj, from the GPU attention and from the oracle
+    assert rel_err(oracle.o_proj(t.o_w, out), oracle.o_proj(t.o_w, ref_a)) <= TOL_F32
+
+
+@pytest.mark.parametrize("T,B", [(300, 1), (1000, 2)])
+def test_decode_dense_glm_bf16(T, B):
+    d = synth.decode(2 + T, T, B=B)
+    seq_len = [T] + [T - 333 * i for i in range(1, B)]
+    log(f"decode dense bf16 T={T} B={B}")
+    out, sm = _run_decode(d, seq_len)
+    for b in range(B):
+        ref = _decode_ref(d, b, np.arange(seq_len[b]), sm)
+        assert rel_err(out[b], ref) <= TOL_BF16, b
+
+
+def test_decode_selected_keys_and_keep_all_equals_dense():
+    T, k = 700, 256
+    d = synth.decode(20, T, B=2)
+    rng = np.random.default_rng(21)
+    sel = np.full((2, k), -1, np.int32)
+    s0 = np.sort(rng.choice(T, k, replace=False)).astype(np.int32)
+    s1 = np.sort(rng.choice(400, 100, replace=False)).astype(np.int32)
+    sel[0], sel[1, :100] = s0, s1
+    nsel = np.array([k, 100], np.int32)
+    log("decode selected keys")
+    out, sm = _run_decode(d, [T, 400], sel, nsel)
+    assert rel_err(out[0], _decode_ref(d, 0, s0, sm)) <= TOL_BF16
+    assert rel_err(out[1], _decode_ref(d, 1, s1, sm)) <= TOL_BF16
+    # keeping every causal key reproduces the dense path bit for bit
+    all_sel = np.tile(np.arange(T, dtype=np.int32), (2, 1))
+    dense, _ = _run_decode(d, [T, T])
+    kept, _ = _run_decode(d, [T, T], all_sel, np.array([T, T], np.int32))
+    assert np.array_equal(dense, kept)
+
+
+def test_decode_paged_equals_contiguous():
+    T = 640
+    d = synth.decode(30, T, B=2)
+    bs = 64
+    rng = np.random.default_rng(31)
+    nb = T // bs
+    perm = rng.permutation(2 * nb).astype(np.int32)
+    bt = perm.reshape(2, nb)
+    rows = 2 * nb * bs
+    lc_p = np.zeros((rows, d.L), np.uint16)
+    rc_p = np.zeros((rows, d.rope), np.uint16)
+    for b in range(2):
+        for j in range(nb):
+            lc_p[bt[b, j] * bs:(bt[b, j] + 1) * bs] = d.lc[b * T + j * bs: b * T + (j + 1) * bs]
+            rc_p[bt[b, j] * bs:(bt[b, j] + 1) * bs] = d.rc[b * T + j * bs: b * T + (j + 1) * bs]
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    log("decode paged vs contiguous")
+    kvp = _kv(lc_p, rc_p, None, [T, 500], T, block_table=bt, block_size=bs)
+    outp = host(mla.mla_absorbed_decode(dev_bf16(d.q_nope), dev_bf16(d.q_rope), dev_bf16(d.kv_b), kvp, sm))
+    outc, _ = _run_decode(d, [T, 500])
+    assert np.array_equal(outp, outc)
+    assert rel_err(outc[1], _decode_ref(d, 1, np.arange(500), sm)) <= TOL_BF16
+
+
+def test_decode_empty_sequence_gives_zeros():
+    d = synth.decode(40, 64, B=2)
+    out, _ = _run_decode(d, [64, 0])
+    assert np.all(out[1] == 0) and np.all(np.isfinite(out[0]))
+
+
+def test_decode_repeat_runs_bit_identical():
+    d = synth.decode(41, 2048)
+    a, _ = _run_decode(d, [2048])
+    b, _ = _run_decode(d, [2048])
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------------------ prefill
+def test_prefill_tiny_fp32_last_row_equals_decode():
+    t = synth.tiny_layer(1)
+    lc, rc, q = oracle.tiny_layer(t.x, t.q_a, t.q_b, t.kv_a, t.H, t.nope, t.rope, t.L)
+    lc32, rc32, q32 = lc.astype(np.float32), rc.astype(np.float32), q.astype(np.float32)
+    sm = 1.0 / math.sqrt(t.nope + t.rope)
+    log("prefill tiny fp32 S=1")
+    kv = mla.KvCache(dev(lc32), dev(rc32), max_seq_len=t.T, seq_stride=t.T)
+    out = host(mla.mla_prefill_nonabsorbed(dev(q32[None]), dev(t.kv_b), kv, t.nope, t.T - 1, sm))[0]
+    ref = oracle.absorbed_decode(q32[:, : t.nope], q32[:, t.nope:], t.kv_b, lc32, rc32, np.arange(t.T), t.v, sm)
+    assert rel_err(out, ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("S,pos_base,out_bf16", [(130, 0, False), (77, 50, True)])
+def test_prefill_small_glm_heads(S, pos_base, out_bf16):
+    p = synth.prefill(60 + S, S, pos_base, H_=4)
+    sm = 1.0 / math.sqrt(p.nope + p.rope)
+    log(f"prefill S={S} pos_base={pos_base}")
+    kv = _kv(p.lc, p.rc, None, None, pos_base + S, seq_stride=pos_base + S)
+    out = mla.mla_prefill_nonabsorbed(dev_bf16(p.q), dev_bf16(p.kv_b), kv, p.nope, pos_base, sm,
+                                      out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    out = host(out)
+    cv = synth.bf16_bits_to_f32
+    rows = np.unique(np.r_[0, S - 1, np.linspace(0, S - 1, 9).astype(int)])
+    ref = oracle.prefill_rows(cv(p.q), cv(p.kv_b), cv(p.lc), cv(p.rc), pos_base, p.nope, p.v, sm, rows)
+    assert rel_err(out[rows], ref) <= TOL_BF16
+
+
+# ------------------------------------------------------------------------------ end to end
+def test_dsa_decode_step_end_to_end_small():
+    """index -> top-k -> absorbed decode over the selected keys, at a size with T > k."""
+    T, k = 5000, 512
+    d = synth.decode(70, T, dsa=True)
+    log("end-to-end DSA decode T=5000 k=512")
+    kv = _kv(d.lc, d.rc, d.ic, [T], T, seq_stride=T)
+    scores = mla.dsa_index_scores(dev(d.q_idx), dev(d.w_idx), kv, T)
+    sel, nsel = mla.dsa_topk_select(scores, dev(np.array([T], np.int32)), k)
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    out = host(mla.mla_absorbed_decode(dev_bf16(d.q_nope), dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm,
+                                       sel=sel, nsel=nsel))
+    ref_s = oracle.index_scores(d.q_idx[0], d.w_idx[0], d.ic)
+    ref_sel, ref_n = oracle.topk(ref_s, T, k)
+    assert int(host(nsel)[0]) == ref_n == k
+    assert np.array_equal(host(sel)[0], ref_sel)
+    assert rel_err(out[0], _decode_ref(d, 0, ref_sel, sm)) <= TOL_BF16
