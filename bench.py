@@ -1,0 +1,330 @@
+"""Benchmark of the MLA + DSA decode hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsa_decode|paged_decode|prefill]
+
+One step of the default workload is a full DSA decode step at T = 131072 cached tokens,
+batch 1, GLM-5.2-like heads (64 heads, kv_lora 512, qk_rope 64, qk_nope 192, v_head 256,
+32 indexer heads of width 128, top-2048): RoPE on the query tail, lightning-indexer scores
+over every cached key, top-k selection, absorbed decode over the selected keys.  Inputs are
+seeded synthetic data already resident in HBM; they rotate over several copies so that no
+step finds its data in the 256 MB Infinity Cache.  Steps are replayed from HIP graphs
+(one per input copy) so host launch overhead stays out of the timed region.
+
+Output: one JSON line (metric, value, roofline of the dominant kernel, CPU-oracle baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MLA+DSA decode keys·heads/sec at T=128k; achieved HBM GB/s vs peak"
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_key: str, src: str, per_launch_algo_bytes: float):
+    """HBM traffic per launch from the committed counter summary, if it was taken on the
+    current source of the kernel; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_key}.counters.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        m = re.match(r"^(\w+)\s*=\s*(\S+)", line.strip())
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256_16") != _src_hash(src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+# ----------------------------------------------------------------------------- decode
+def bench_dsa_decode(args):
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_dsa_amd as mla
+    from mla_latent_kv_dsa_amd import synth
+
+    dev = torch.device("cuda:0")
+    T, B, H, NOPE, ROPE, V, L = 131072, 1, synth.H, synth.QK_NOPE, synth.QK_ROPE, synth.V_HEAD, synth.KV_LORA
+    N_IH, HD, K = synth.N_IH, synth.INDEX_HD, synth.TOPK
+    sm = 1.0 / math.sqrt(NOPE + ROPE)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = synth.decode(3, T, B=B, dsa=True)
+    copies = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(1003)
+    for c in range(args.copies):
+        if c == 0:
+            lc, rc, ic = bf(d.lc), bf(d.rc), torch.from_numpy(d.ic).to(dev)
+            qn, qr, kvb = bf(d.q_nope), bf(d.q_rope), bf(d.kv_b)
+            qi, wi = torch.from_numpy(d.q_idx).to(dev), torch.from_numpy(d.w_idx).to(dev)
+        else:
+            rn = lambda *s, std=1.0: torch.randn(*s, generator=g, device=dev) * std
+            lc, rc, ic = rn(T, L).bfloat16(), rn(T, ROPE).bfloat16(), rn(T, HD)
+            qn, qr, kvb = rn(B, H, NOPE).bfloat16(), rn(B, H, ROPE).bfloat16(), rn(H * (NOPE + V), L, std=0.02).bfloat16()
+            qi, wi = rn(B, N_IH, HD), rn(B, N_IH)
+        seq_len = torch.full((B,), T, dtype=torch.int32, device=dev)
+        kv = mla.KvCache(lc, rc, ic, seq_len=seq_len, max_seq_len=T, seq_stride=T)
+        copies.append(dict(kv=kv, qn=qn, qr=qr, kvb=kvb, qi=qi, wi=wi, seq_len=seq_len,
+                           pos=torch.full((B,), T - 1, dtype=torch.int32, device=dev),
+                           scores=torch.empty((B, T), dtype=torch.float32, device=dev),
+                           sel=torch.empty((B, K), dtype=torch.int32, device=dev),
+                           nsel=torch.empty((B,), dtype=torch.int32, device=dev),
+                           out=torch.empty((B, H, V), dtype=torch.float32, device=dev)))
+    tk_need = mla.dsa_topk_workspace_bytes(B, T, K)
+    dec_need = mla.mla_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, K)
+    for c in copies:
+        c["tk_ws"] = torch.empty(max(tk_need, 1), dtype=torch.uint8, device=dev)
+        c["dec_ws"] = torch.empty(max(dec_need, 1), dtype=torch.uint8, device=dev)
+
+    def rope(c):
+        mla.mla_rope_interleave(c["qr"], c["pos"], 0, ROPE)
+
+    def index(c):
+        mla.dsa_index_scores(c["qi"], c["wi"], c["kv"], T, scores=c["scores"])
+
+    def topk(c):
+        mla.dsa_topk_select(c["scores"], c["seq_len"], K, sel=c["sel"], nsel=c["nsel"], ws=c["tk_ws"])
+
+    def decode(c):
+        mla.mla_absorbed_decode(c["qn"], c["qr"], c["kvb"], c["kv"], sm, sel=c["sel"], nsel=c["nsel"],
+                                out=c["out"], ws=c["dec_ws"])
+
+    def step(c):
+        rope(c)
+        index(c)
+        topk(c)
+        decode(c)
+
+    # eager reference of one step on copy 0 (q_rope is rotated in place, so keep a copy)
+    qr0 = copies[0]["qr"].clone()
+    step(copies[0])
+    torch.cuda.synchronize()
+    ref_sel, ref_out = copies[0]["sel"].clone(), copies[0]["out"].clone()
+    copies[0]["qr"].copy_(qr0)
+
+    graphs = []
+    if not args.no_graph:
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(s):
+            for c in copies:
+                step(c)                       # warm the allocator-free path on this stream
+        torch.cuda.current_stream(dev).wait_stream(s)
+        torch.cuda.synchronize()
+        copies[0]["qr"].copy_(qr0)
+        for c in copies:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(c)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        copies[0]["qr"].copy_(qr0)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(copies[0]["sel"], ref_sel), "graph replay selection differs from eager"
+        assert torch.equal(copies[0]["out"], ref_out), "graph replay output differs from eager"
+
+    def run(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(copies[i % len(copies)])
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations (eager launches, events around each call, same rotation)
+    parts = {"rope": rope, "index": index, "topk": topk, "decode": decode}
+    dur = {k: [] for k in parts}
+    n_k = max(args.steps, 20)
+    for i in range(n_k):
+        c = copies[i % len(copies)]
+        ev = _events(torch, 5)
+        ev[0].record()
+        for j, (k, f) in enumerate(parts.items()):
+            f(c)
+            ev[j + 1].record()
+        dur_i = ev
+        torch.cuda.synchronize()
+        for j, k in enumerate(parts):
+            dur[k].append(dur_i[j].elapsed_time(dur_i[j + 1]) * 1e3)   # us
+    us = {k: statistics.mean(v) for k, v in dur.items()}
+
+    keys_heads = T * H * B
+    value = keys_heads / (ms_step * 1e-3)
+    ic_bytes = T * HD * 4
+    score_bytes = T * 4
+    q_bytes = N_IH * HD * 4 + N_IH * 4
+    idx_bytes = ic_bytes + score_bytes + q_bytes
+    idx_gbs = idx_bytes / (us["index"] * 1e-6) / 1e9
+    sel_kv_bytes = K * (L + ROPE) * 2
+    kvb_bytes = H * (NOPE + V) * L * 2
+    step_bytes = ic_bytes + sel_kv_bytes + kvb_bytes + score_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
+    stream_bytes = ic_bytes + sel_kv_bytes
+    stream_us = us["index"] + us["topk"] + us["decode"]
+    src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", "dsa_index.hip")
+    traffic = _traffic("dsa_index_scores_T131072", src, idx_bytes)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_decode(d, T, K, sm)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "keys·heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dsa_decode_T131072_B1", "T": T, "B": B, "heads": H, "qk_nope": NOPE,
+                   "qk_rope": ROPE, "v_head": V, "kv_lora": L, "index_heads": N_IH, "index_hd": HD,
+                   "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "input_copies": args.copies,
+                   "hip_graphs": bool(graphs)},
+        "roofline": {"kernel": "dsa_index_scores", "bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": idx_bytes, "avg_us": us["index"]},
+        "cpu_baseline": cpu,
+        "breakdown_us": us,
+        "stream": {"bytes": stream_bytes, "us_index_topk_decode": stream_us,
+                   "GBs": stream_bytes / (stream_us * 1e-6) / 1e9,
+                   "frac": stream_bytes / (stream_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "whole_step": {"bytes": step_bytes, "GBs": step_bytes / (ms_step * 1e-3) / 1e9,
+                       "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "wall_s_timed": t_wall,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_decode(d, T, K, sm):
+    """The oracle (as it stands) on one full decode step of the same workload: indexer over
+    all T keys, top-k, absorbed decode over the selected keys, on the host's cores."""
+    import numpy as np
+
+    import oracle
+    from mla_latent_kv_dsa_amd import synth
+
+    cv = synth.bf16_bits_to_f32
+    lc, rc, kvb = cv(d.lc), cv(d.rc), cv(d.kv_b)
+    qn, qr = cv(d.q_nope[0]), cv(d.q_rope[0])
+    qr = oracle.rope_interleave(qr[None], np.array([T - 1], np.int32), 0, d.rope)[0]
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        s = oracle.index_scores(d.q_idx[0], d.w_idx[0], d.ic)
+        sel, n = oracle.topk(s, T, K)
+        oracle.absorbed_decode(qn, qr, kvb, lc, rc, sel[:n], d.v, sm)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": T * d.H / t, "unit": "keys·heads/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one full decode step at T={T} (RoPE of the query, fixed-order fp32 indexer over all keys, "
+                      f"sort-based top-{K}, fp64 absorbed decode over the selected keys), median of 3 runs",
+            "seconds_per_step": t}
+
+
+# ----------------------------------------------------------------------------- prefill
+def bench_prefill(args):
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_dsa_amd as mla
+    from mla_latent_kv_dsa_amd import synth
+
+    dev = torch.device("cuda:0")
+    S = 4096
+    p = synth.prefill(4, S, 0)
+    sm = 1.0 / math.sqrt(p.nope + p.rope)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, lc, rc, kvb = bf(p.q), bf(p.lc), bf(p.rc), bf(p.kv_b)
+    kv = mla.KvCache(lc, rc, max_seq_len=S, seq_stride=S)
+    out = torch.empty((S, p.H, p.v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_prefill_workspace_bytes(p.H, p.nope, p.rope, p.v, p.L, S, S), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: mla.mla_prefill_nonabsorbed(q, kvb, kv, p.nope, 0, sm, out=out, ws=ws)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(args.steps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2 * S * (p.H * (p.nope + p.v)) * p.L + 2 * p.H * (S * (S + 1) // 2) * (p.nope + p.rope) \
+        + 2 * p.H * (S * (S + 1) // 2) * p.v
+    tf = flops / (ms * 1e-3) / 1e12
+    line = {"metric": "MLA prefill (non-absorbed) TFLOP/s at S=T=4096", "value": tf, "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "prefill_S4096", "S": S, "heads": p.H, "qk_nope": p.nope, "qk_rope": p.rope,
+                       "v_head": p.v, "kv_lora": p.L},
+            "roofline": {"kernel": "mla_prefill_nonabsorbed", "bound": "mfma", "achieved": tf,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "algorithmic_flops": flops}}
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "prefill"])
+    ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "dsa_decode":
+        bench_dsa_decode(args)
+    else:
+        bench_prefill(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,4 +20,10 @@ mla_status launch_decode_generic(const void *q_nope, const void *q_rope, const v
                                  const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale,
                                  float *out, void *ws, hipStream_t s);
 
+bool decode_mfma_supported(const mla_dims &d, mla_dtype dt);
+size_t decode_mfma_ws(const mla_dims &d, int32_t B, int64_t max_keys);
+mla_status launch_decode_mfma(const void *q_nope, const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B,
+                              const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                              int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s);
+
 }  // namespace mla

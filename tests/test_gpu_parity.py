@@ -330,3 +330,51 @@ def test_dsa_decode_step_end_to_end_small():
     assert int(host(nsel)[0]) == ref_n == k
     assert np.array_equal(host(sel)[0], ref_sel)
     assert rel_err(out[0], _decode_ref(d, 0, ref_sel, sm)) <= TOL_BF16
+
+
+def test_topk_all_equal_full_context():
+    # every score in one threshold bin: all 131072 positions become candidates
+    T = 131072
+    s = np.full((1, T), 0.75, np.float32)
+    log("topk all equal T=131072")
+    _topk_check(s, [T], 2048)
+    s[0, 5000:5100] = 0.7500001
+    _topk_check(s, [T], 2048)
+
+
+def test_decode_generic_and_matrix_core_paths_agree():
+    """A 2-byte offset makes the query pointer misaligned, which routes the same GLM-shape
+    inputs to the generic kernels; both paths must meet the oracle bar."""
+    T = 900
+    d = synth.decode(80, T, B=2)
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    kv = _kv(d.lc, d.rc, None, [T, 611], T, seq_stride=T)
+    qn = dev_bf16(d.q_nope)
+    buf = torch.empty(qn.numel() + 1, dtype=torch.bfloat16, device=qn.device)
+    qn_mis = buf[1:].view(qn.shape)
+    qn_mis.copy_(qn)
+    log("decode generic vs matrix-core")
+    fast = host(mla.mla_absorbed_decode(qn, dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm))
+    slow = host(mla.mla_absorbed_decode(qn_mis, dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm))
+    for b, n in enumerate([T, 611]):
+        ref = _decode_ref(d, b, np.arange(n), sm)
+        assert rel_err(fast[b], ref) <= TOL_BF16
+        assert rel_err(slow[b], ref) <= TOL_BF16
+
+
+def test_decode_batched_selected_large():
+    """Many sequences with selections of different sizes (covers multi-tile splits)."""
+    B, T, k = 6, 3000, 2048
+    d = synth.decode(81, T, B=B)
+    rng = np.random.default_rng(82)
+    sel = np.full((B, k), -1, np.int32)
+    nsel = np.array([2048, 1, 0, 777, 2048, 33], np.int32)
+    for b in range(B):
+        sel[b, : nsel[b]] = np.sort(rng.choice(T, nsel[b], replace=False))
+    log("decode batched selected")
+    out, sm = _run_decode(d, [T] * B, sel, nsel)
+    for b in range(B):
+        if nsel[b] == 0:
+            assert np.all(out[b] == 0)
+            continue
+        assert rel_err(out[b], _decode_ref(d, b, sel[b, : nsel[b]], sm)) <= TOL_BF16, b
