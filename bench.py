@@ -171,22 +171,35 @@ def bench_dsa_decode(args):
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel durations (eager launches, events around each call, same rotation)
+    # per-kernel durations: each part alone, captured back to back over every input copy
+    # (REPS passes) in one HIP graph, replayed between two events on the launch stream
     parts = {"rope": rope, "index": index, "topk": topk, "decode": decode}
-    dur = {k: [] for k in parts}
-    n_k = max(args.steps, 20)
-    for i in range(n_k):
-        c = copies[i % len(copies)]
-        ev = _events(torch, 5)
-        ev[0].record()
-        for j, (k, f) in enumerate(parts.items()):
-            f(c)
-            ev[j + 1].record()
-        dur_i = ev
+    us = {}
+    REPS = 4
+    for k, f in parts.items():
+        if graphs:
+            gk = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gk):
+                for _ in range(REPS):
+                    for c in copies:
+                        f(c)
+            launch = gk.replay
+            per = REPS * len(copies)
+        else:
+            def launch(f=f):
+                for c in copies:
+                    f(c)
+            per = len(copies)
+        launch()
         torch.cuda.synchronize()
-        for j, k in enumerate(parts):
-            dur[k].append(dur_i[j].elapsed_time(dur_i[j + 1]) * 1e3)   # us
-    us = {k: statistics.mean(v) for k, v in dur.items()}
+        n_rep = max(3, args.steps // per)
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        for _ in range(n_rep):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        us[k] = e0.elapsed_time(e1) * 1e3 / (n_rep * per)
 
     keys_heads = T * H * B
     value = keys_heads / (ms_step * 1e-3)

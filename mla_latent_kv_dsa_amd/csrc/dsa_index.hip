@@ -109,96 +109,132 @@ __global__ __launch_bounds__(256) void index_scores_generic(const float *__restr
 //   lane L supplies a = q[L % 32][d] (head) and b = Ic[key L][d]; block 0 covers keys
 //   0..31 of the tile, block 1 keys 32..63.  Accumulator register r (0..15) of lane L holds
 //   block 0, key L % 32, head 8*(r/4) + 4*(L/32) + r%4; registers 16..31 hold block 1.
-// A wave owns a 64-key tile; the key rows are staged through LDS in 32-wide d slices so
-// that each lane can read its own key's row (rows padded to avoid bank conflicts), with
-// the next slice prefetched into registers while the current one is consumed.
+// A wave owns 64-key tiles.  Lane L loads key L's row straight into registers, 32 dims
+// (one slice, 8 x 16 B) at a time, through a ring of two slices: while slice s feeds the
+// 32 MFMAs of one step, slice s + 2 is already in flight.  No LDS staging is needed because
+// the B operand of this MFMA is exactly "key L's value at dim d" in lane L.  The query
+// (32 x 128) is staged in LDS once per block, before any key load is issued, so that the
+// block barrier does not wait on the key stream.
 typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int IXM_WAVES = 4;
-constexpr int IXM_ROW = 32 + 4;      // floats per staged key row (32 d + pad)
-constexpr int IXM_QROW = 128 + 4;    // floats per query row in LDS
+constexpr int IXM_QROW = 128 + 4;    // floats per query row in LDS (pad against bank conflicts)
 
-__device__ __forceinline__ void wave_lds_sync()
+// Row pointer of key (tile * 64 + lane) for lane-private loads.  A key with no score (past
+// the sequence or outside the pools) reads the query block instead (any readable 512 B will
+// do), so that every load is unconditional; its lane's result is replaced by -inf.
+//   MODE 0: contiguous rows (no block table);
+//   MODE 1: block table with block_size % 64 == 0 -- the whole tile sits in one block, so the
+//           table entry is wave-uniform and is fetched with a scalar load, which leaves the
+//           vector-memory counter (and the key stream waiting on it) alone;
+//   MODE 2: any block size, one table lookup per lane.
+template <int MODE>
+__device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int64_t tile, int lane, int64_t n,
+                                                   const float *dummy, bool &valid)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t t = tile * 64 + lane;
+    int64_t row;
+    if (MODE == 0) {
+        row = (int64_t)b * kv.seq_stride + t;
+    } else if (MODE == 1) {
+        const int64_t t0 = tile * 64;
+        const int64_t blk = kv.bt[(int64_t)b * kv.max_blocks + t0 / kv.bs];
+        row = blk < 0 ? -1 : blk * kv.bs + t0 % kv.bs + lane;
+    } else {
+        row = t < n ? kv_row(kv, b, t) : -1;
+    }
+    valid = t < n && row >= 0 && row < kv.rows;
+    return valid ? kv.ic + row * 128 : dummy;
 }
 
+__device__ __forceinline__ void ix_load_slice(v32f &dst, const float *p, int sl)
+{
+    const float4 *src = reinterpret_cast<const float4 *>(p + sl * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 x = src[i];
+        dst[4 * i + 0] = x.x;
+        dst[4 * i + 1] = x.y;
+        dst[4 * i + 2] = x.z;
+        dst[4 * i + 3] = x.w;
+    }
+}
+
+// acc += q[:, 32 sl .. 32 sl + 31] x K[:, same dims]^T, one MFMA per dim, d ascending.
+__device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *qrow, int sl)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        // keeps the LDS reads of q next to their MFMAs instead of all hoisted (VGPR pressure)
+        if ((j & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+        const float4 qq = *reinterpret_cast<const float4 *>(&qrow[sl * 32 + 4 * j]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, K[4 * j + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, K[4 * j + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, K[4 * j + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, K[4 * j + 3], acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
                                                                      const float *__restrict__ w, KvView kv,
-                                                                     int64_t t_max, int tiles_per_wave,
-                                                                     float *__restrict__ scores)
+                                                                     int64_t t_max, float *__restrict__ scores)
 {
     __shared__ float sq[32 * IXM_QROW];
-    __shared__ float sw[32];
-    __shared__ float sk[IXM_WAVES][64 * IXM_ROW];
-    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile math stays scalar
     const int64_t n = seq_len_of(kv, b) < t_max ? seq_len_of(kv, b) : t_max;
-    const int64_t ntiles = (t_max + 63) / 64;
+    const int64_t ntv = (n + 63) / 64;   // tiles holding at least one scored key
     const int64_t waves_total = (int64_t)gridDim.x * IXM_WAVES;
     float *out = scores + (int64_t)b * t_max;
+    const float *wb = w + (int64_t)b * 32;
 
+    // whole tiles past the last scored key
+    for (int64_t t = ntv * 64 + (int64_t)blockIdx.x * 64 * IXM_WAVES + tid; t < t_max; t += waves_total * 64)
+        out[t] = -INFINITY;
+
+    // query to LDS: all four loads in flight before the first store
     const float4 *qb = reinterpret_cast<const float4 *>(q + (int64_t)b * 32 * 128);
-    for (int i = tid; i < 32 * 32; i += 64 * IXM_WAVES) {
-        const float4 v = qb[i];
-        *reinterpret_cast<float4 *>(&sq[(i >> 5) * IXM_QROW + (i & 31) * 4]) = v;
+    float4 qv[32 * 32 / (64 * IXM_WAVES)];
+#pragma unroll
+    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) qv[k] = qb[tid + k * 64 * IXM_WAVES];
+#pragma unroll
+    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) {
+        const int i = tid + k * 64 * IXM_WAVES;
+        *reinterpret_cast<float4 *>(&sq[(i >> 5) * IXM_QROW + (i & 31) * 4]) = qv[k];
     }
-    if (tid < 32) sw[tid] = w[(int64_t)b * 32 + tid];
     __syncthreads();
 
-    float *skw = sk[wave];
-    const int lrow = lane >> 3;          // rows lrow + 8*i of the tile are loaded by this lane
-    const int lcol = (lane & 7) * 4;     // float offset inside the 32-wide slice
+    int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
+    if (tile >= ntv) return;
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
     const bool lo_half = lane < 32;
 
-    for (int it = 0; it < tiles_per_wave; ++it) {
-        const int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave + (int64_t)it * waves_total;
-        if (tile >= ntiles) break;
-        const int64_t t0 = tile * 64;
-        if (t0 >= n) {
-            const int64_t t = t0 + lane;
-            if (t < t_max) out[t] = -INFINITY;
-            continue;
-        }
-        const float *src[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t t = t0 + lrow + 8 * i;
-            const int64_t row = t < n ? kv_row(kv, b, t) : -1;
-            src[i] = row >= 0 ? kv.ic + row * 128 + lcol : nullptr;
-        }
-        float4 stg[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            stg[i] = src[i] ? *reinterpret_cast<const float4 *>(src[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
-        v32f acc;
+    const float *qraw = q + (int64_t)b * 32 * 128;
+    bool valid, valid_n = false;
+    const float *p = ix_key_ptr<MODE>(kv, b, tile, lane, n, qraw, valid);
+    v32f KA, KB, acc;
+    ix_load_slice(KA, p, 0);
+    __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
+    ix_load_slice(KB, p, 1);
+    for (; tile < ntv; tile += waves_total) {
+        // the next tile's first two slices are loaded unconditionally (from the query block
+        // when there is no next tile) so every iteration leaves the same loads in flight
+        const int64_t nxt = tile + waves_total;
+        const float *pn = qraw;
+        valid_n = false;
+        if (nxt < ntv) pn = ix_key_ptr<MODE>(kv, b, nxt, lane, n, qraw, valid_n);
 #pragma unroll
         for (int r = 0; r < 32; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int st_ = 0; st_ < 4; ++st_) {
-            wave_lds_sync();   // every lane is done reading the previous slice
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<float4 *>(&skw[(lrow + 8 * i) * IXM_ROW + lcol]) = stg[i];
-            wave_lds_sync();
-            if (st_ < 3) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    stg[i] = src[i] ? *reinterpret_cast<const float4 *>(src[i] + (st_ + 1) * 32)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float4 kk = *reinterpret_cast<const float4 *>(&skw[lane * IXM_ROW + 4 * j]);
-                const float4 qq = *reinterpret_cast<const float4 *>(&qrow[st_ * 32 + 4 * j]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, kk.x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, kk.y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, kk.z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, kk.w, acc, 0, 0, 0);
-            }
-        }
+        ix_slice(acc, KA, qrow, 0);
+        ix_load_slice(KA, p, 2);
+        ix_slice(acc, KB, qrow, 1);
+        ix_load_slice(KB, p, 3);
+        ix_slice(acc, KA, qrow, 2);
+        ix_load_slice(KA, pn, 0);
+        ix_slice(acc, KB, qrow, 3);
+        ix_load_slice(KB, pn, 1);
         // lanes L and L^32 hold complementary head groups of the same two keys: swap so that
         // lane L holds all 32 heads of key L, then fold them in ascending head order
         float y[16];
@@ -210,16 +246,18 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const float a = lo_half ? acc[4 * g + r4] : y[4 * g + r4];
-                s = __builtin_fmaf(sw[8 * g + r4], a > 0.f ? a : 0.f, s);
+                s = __builtin_fmaf(wb[8 * g + r4], a > 0.f ? a : 0.f, s);
             }
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const float a = lo_half ? y[4 * g + r4] : acc[16 + 4 * g + r4];
-                s = __builtin_fmaf(sw[8 * g + 4 + r4], a > 0.f ? a : 0.f, s);
+                s = __builtin_fmaf(wb[8 * g + 4 + r4], a > 0.f ? a : 0.f, s);
             }
         }
-        const int64_t t = t0 + lane;
-        if (t < t_max) out[t] = t < n ? s : -INFINITY;
+        const int64_t t = tile * 64 + lane;
+        if (t < t_max) out[t] = valid ? s : -INFINITY;
+        p = pn;
+        valid = valid_n;
     }
 }
 
@@ -231,14 +269,20 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
     dim3 grid((unsigned)gx, (unsigned)B);
     const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv.ic)) & 15u) == 0;
     if (hd == 128 && n_ih == 32 && aligned) {
-        // enough waves for two resident blocks per CU (256 CUs); each wave loops over tiles
+        // about 3 resident waves per SIMD over the chip; each wave strides over the tiles
         const int64_t ntiles = (t_max + 63) / 64;
-        const int64_t want_waves = 2 * 256 * IXM_WAVES;
-        int64_t tpw = (ntiles * B + want_waves - 1) / want_waves;
-        if (tpw < 1) tpw = 1;
-        const int64_t bx = (ntiles + IXM_WAVES * tpw - 1) / (IXM_WAVES * tpw);
-        hipLaunchKernelGGL(index_scores_mfma, dim3((unsigned)bx, (unsigned)B), dim3(64 * IXM_WAVES), 0, s, q, w, kv,
-                           t_max, (int)tpw, scores);
+        int64_t bx = 768 / B;
+        if (bx < 1) bx = 1;
+        const int64_t need = (ntiles + IXM_WAVES - 1) / IXM_WAVES;
+        if (bx > need) bx = need;
+        if (bx < 1) bx = 1;
+        const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
+        if (!kv.bt)
+            hipLaunchKernelGGL(index_scores_mfma<0>, g, blk, 0, s, q, w, kv, t_max, scores);
+        else if (kv.bs % 64 == 0)
+            hipLaunchKernelGGL(index_scores_mfma<1>, g, blk, 0, s, q, w, kv, t_max, scores);
+        else
+            hipLaunchKernelGGL(index_scores_mfma<2>, g, blk, 0, s, q, w, kv, t_max, scores);
     } else if (hd == 128 && aligned)
         hipLaunchKernelGGL(index_scores_lane_per_key<128>, grid, dim3(256), 0, s, q, w, n_ih, kv, t_max, scores);
     else

@@ -84,10 +84,11 @@ def test_rope_strided_view_and_odd_geometry():
 
 
 # ------------------------------------------------------------------------------ indexer
-def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed):
+def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed, bs=64, hole=False):
+    """Random indexer problem.  Returns q, w, the view, and per sequence the logical key rows
+    plus a mask of keys that have a row (a block-table hole leaves a gap of -1 entries)."""
     rng = np.random.default_rng(seed)
     if paged:
-        bs = 64
         nb = [(s + bs - 1) // bs for s in seq_len]
         perm = rng.permutation(sum(nb)).astype(np.int32)
         max_blocks = (t_max + bs - 1) // bs
@@ -96,22 +97,40 @@ def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed):
         for b in range(B):
             bt[b, : nb[b]] = perm[o: o + nb[b]]
             o += nb[b]
+        if hole and nb[0] > 2:
+            bt[0, nb[0] // 2] = -1
         rows = sum(nb) * bs
         ic = rng.standard_normal((rows, hd)).astype(np.float32)
-        logical = [ic[(bt[b, np.arange(seq_len[b]) // bs].astype(np.int64) * bs + np.arange(seq_len[b]) % bs)]
-                   for b in range(B)]
+        logical, masks = [], []
+        for b in range(B):
+            t = np.arange(seq_len[b])
+            blk = bt[b, t // bs].astype(np.int64)
+            m = blk >= 0
+            r = np.where(m, blk * bs + t % bs, 0)
+            logical.append(ic[r])
+            masks.append(m)
         kvd = dict(block_table=bt, block_size=bs)
     else:
         stride = t_max
         ic = rng.standard_normal((B * stride, hd)).astype(np.float32)
         logical = [ic[b * stride: b * stride + seq_len[b]] for b in range(B)]
+        masks = [np.ones(seq_len[b], bool) for b in range(B)]
         kvd = dict(seq_stride=stride)
     q = rng.standard_normal((B, n_ih, hd)).astype(np.float32)
     w = rng.standard_normal((B, n_ih)).astype(np.float32)
     lc = np.zeros((ic.shape[0], 8), np.uint16)
     rc = np.zeros((ic.shape[0], 8), np.uint16)
     kv = _kv(lc, rc, ic, seq_len, t_max, **kvd)
-    return q, w, kv, logical
+    return q, w, kv, logical, masks
+
+
+def _index_check(q, w, kv, logical, masks, seq_len, t_max):
+    s = host(mla.dsa_index_scores(dev(q), dev(w), kv, t_max))
+    for b in range(len(seq_len)):
+        ref = oracle.index_scores(q[b], w[b], logical[b])
+        ref = np.where(masks[b], ref, np.float32(-np.inf)).astype(np.float32)
+        assert np.array_equal(s[b, : seq_len[b]].view(np.uint32), ref.view(np.uint32)), b
+        assert np.all(np.isneginf(s[b, seq_len[b]:]))
 
 
 @pytest.mark.parametrize("paged", [False, True])
@@ -120,12 +139,20 @@ def test_index_scores_bit_exact(paged, n_ih, hd):
     B, t_max = 3, 1100
     seq_len = [1100, 777, 1]
     log(f"index paged={paged} n_ih={n_ih} hd={hd}")
-    q, w, kv, logical = _index_case(B, seq_len, t_max, n_ih, hd, paged, 200 + n_ih + paged)
-    s = host(mla.dsa_index_scores(dev(q), dev(w), kv, t_max))
-    for b in range(B):
-        ref = oracle.index_scores(q[b], w[b], logical[b])
-        assert np.array_equal(s[b, : seq_len[b]].view(np.uint32), ref.view(np.uint32)), b
-        assert np.all(np.isneginf(s[b, seq_len[b]:]))
+    q, w, kv, logical, masks = _index_case(B, seq_len, t_max, n_ih, hd, paged, 200 + n_ih + paged)
+    _index_check(q, w, kv, logical, masks, seq_len, t_max)
+
+
+@pytest.mark.parametrize("bs,hole", [(16, False), (16, True), (128, True), (64, True), (1, False)])
+def test_index_scores_block_sizes(bs, hole):
+    """Every addressing mode of the matrix-core indexer: block sizes that keep a 64-key tile
+    in one block (one table entry per tile) and ones that do not (one per key), with a -1
+    hole inside a sequence, a ragged tail and several tiles per wave."""
+    B, t_max = 2, 70000
+    seq_len = [70000, 4097]
+    log(f"index bs={bs} hole={hole}")
+    q, w, kv, logical, masks = _index_case(B, seq_len, t_max, 32, 128, True, 260 + bs, bs=bs, hole=hole)
+    _index_check(q, w, kv, logical, masks, seq_len, t_max)
 
 
 def test_index_scores_full_context_131072():
@@ -138,7 +165,7 @@ def test_index_scores_full_context_131072():
 
 
 def test_index_empty_and_zero_length():
-    q, w, kv, logical = _index_case(2, [0, 5], 64, 32, 128, False, 250)
+    q, w, kv, logical, _ = _index_case(2, [0, 5], 64, 32, 128, False, 250)
     s = host(mla.dsa_index_scores(dev(q), dev(w), kv, 64))
     assert np.all(np.isneginf(s[0])) and np.all(np.isneginf(s[1, 5:]))
     assert np.array_equal(s[1, :5], oracle.index_scores(q[1], w[1], logical[1]))
