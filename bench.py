@@ -113,15 +113,21 @@ def bench_dsa_decode(args):
     def topk(c):
         mla.dsa_topk_select(c["scores"], c["seq_len"], K, sel=c["sel"], nsel=c["nsel"], ws=c["tk_ws"])
 
-    def decode(c):
-        mla.mla_absorbed_decode(c["qn"], c["qr"], c["kvb"], c["kv"], sm, sel=c["sel"], nsel=c["nsel"],
-                                out=c["out"], ws=c["dec_ws"])
+    def absorb(c):
+        mla.mla_decode_absorb(c["qn"], c["kvb"], c["dec_ws"], qk_rope=ROPE)
+
+    def attend(c):
+        mla.mla_decode_attend(c["qr"], c["kvb"], c["kv"], NOPE, sm, c["dec_ws"], sel=c["sel"], nsel=c["nsel"],
+                              out=c["out"])
 
     def step(c):
+        # one stream: a fork/join across two streams inside the captured graph cost more per
+        # step than running the query absorption beside the top-k saved
         rope(c)
         index(c)
         topk(c)
-        decode(c)
+        absorb(c)
+        attend(c)
 
     # eager reference of one step on copy 0 (q_rope is rotated in place, so keep a copy)
     qr0 = copies[0]["qr"].clone()
@@ -173,7 +179,7 @@ def bench_dsa_decode(args):
 
     # per-kernel durations: each part alone, captured back to back over every input copy
     # (REPS passes) in one HIP graph, replayed between two events on the launch stream
-    parts = {"rope": rope, "index": index, "topk": topk, "decode": decode}
+    parts = {"rope": rope, "index": index, "topk": topk, "absorb": absorb, "attend": attend}
     us = {}
     REPS = 4
     for k, f in parts.items():
@@ -212,7 +218,7 @@ def bench_dsa_decode(args):
     kvb_bytes = H * (NOPE + V) * L * 2
     step_bytes = ic_bytes + sel_kv_bytes + kvb_bytes + score_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
     stream_bytes = ic_bytes + sel_kv_bytes
-    stream_us = us["index"] + us["topk"] + us["decode"]
+    stream_us = us["index"] + us["topk"] + us["attend"]
     src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", "dsa_index.hip")
     traffic = _traffic("dsa_index_scores_T131072", src, idx_bytes)
 
@@ -233,7 +239,7 @@ def bench_dsa_decode(args):
                      "algorithmic_bytes": idx_bytes, "avg_us": us["index"]},
         "cpu_baseline": cpu,
         "breakdown_us": us,
-        "stream": {"bytes": stream_bytes, "us_index_topk_decode": stream_us,
+        "stream": {"bytes": stream_bytes, "us_index_topk_attend": stream_us,
                    "GBs": stream_bytes / (stream_us * 1e-6) / 1e9,
                    "frac": stream_bytes / (stream_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "whole_step": {"bytes": step_bytes, "GBs": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -315,18 +321,126 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+# ----------------------------------------------------------------------------- counters
+COPY_MIB = 256
+
+
+def bench_copy(args):
+    """Plain device-to-device copy of COPY_MIB MiB: the known-size kernel whose FETCH_SIZE and
+    WRITE_SIZE readings calibrate the HBM byte counters."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = COPY_MIB * 2**20 // 4
+    a = torch.randn(n, device=dev)
+    b = torch.empty_like(a)
+    res = {}
+    # the runtime's blit kernel (copy_) and a one-pass elementwise kernel (mul by 1)
+    for name, f in (("copyBuffer", lambda: b.copy_(a)), ("elementwise", lambda: torch.mul(a, 1.0, out=b))):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": ms, "GBs": 2 * n * 4 / (ms * 1e-3) / 1e9}
+    print(json.dumps({"workload": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "kernels": res}), flush=True)
+
+
+def _counter_means(csv_path, kernel_substr):
+    """Mean value per dispatch of every counter in a rocprofv3 counter_collection.csv, over
+    the dispatches whose kernel name contains kernel_substr."""
+    import csv
+    from collections import defaultdict
+
+    acc = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(csv_path)):
+        if kernel_substr in r["Kernel_Name"]:
+            acc[r["Counter_Name"]][r.get("Dispatch_Id") or r.get("Correlation_Id")] += float(r["Counter_Value"])
+    return {k: (statistics.mean(v.values()), len(v)) for k, v in acc.items()}
+
+
+def summarize_counters(args):
+    """Write profiles/<name>.counters.txt from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, each for the kernel's workload and for the calibration copy)."""
+    d = args.counters_dir
+    find = lambda sub: next(os.path.join(r, f) for r, _, fs in os.walk(os.path.join(d, sub)) for f in fs
+                            if f.endswith("counter_collection.csv"))
+    copy_bytes = COPY_MIB * 2**20
+    cf, _ = _counter_means(find("copy_fetch"), "copyBuffer")["FETCH_SIZE"]
+    cw, _ = _counter_means(find("copy_write"), "copyBuffer")["WRITE_SIZE"]
+    ef, _ = _counter_means(find("copy_fetch"), "elementwise")["FETCH_SIZE"]
+    ew, _ = _counter_means(find("copy_write"), "elementwise")["WRITE_SIZE"]
+    kf, nf = _counter_means(find("kernel_fetch"), args.kernel)["FETCH_SIZE"]
+    kw, nw = _counter_means(find("kernel_write"), args.kernel)["WRITE_SIZE"]
+    f_fetch, f_write = copy_bytes / cf, copy_bytes / cw          # bytes per counter unit
+    hbm = kf * f_fetch + kw * f_write
+    src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", args.kernel_src)
+    out = os.path.join(ROOT, "profiles", f"{args.counters_name}.counters.txt")
+    with open(out, "w") as fo:
+        fo.write(f"# HBM traffic of {args.kernel} per launch, from rocprofv3 --pmc counters\n")
+        fo.write(f"# kernel runs : rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                 f"python3 bench.py {args.counters_cmd}\n")
+        fo.write(f"# calibration : rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                 f"python3 bench.py --workload copy --steps 5 --warmup 1   ({COPY_MIB} MiB read + written)\n")
+        fo.write(f"copy_FETCH_SIZE_per_dispatch = {cf:.1f}\ncopy_WRITE_SIZE_per_dispatch = {cw:.1f}\n")
+        fo.write(f"# cross-check, elementwise kernel over the same buffers: FETCH_SIZE {ef:.1f}, WRITE_SIZE {ew:.1f}\n")
+        fo.write(f"fetch_bytes_per_unit = {f_fetch:.4f}\nwrite_bytes_per_unit = {f_write:.4f}\n")
+        fo.write(f"kernel_dispatches = {nf}/{nw}\n")
+        fo.write(f"kernel_FETCH_SIZE_per_dispatch = {kf:.1f}\nkernel_WRITE_SIZE_per_dispatch = {kw:.1f}\n")
+        fo.write(f"fetch_bytes_per_launch = {kf * f_fetch:.0f}\nwrite_bytes_per_launch = {kw * f_write:.0f}\n")
+        fo.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        fo.write(f"source = {os.path.relpath(src, ROOT)}\nsource_sha256_16 = {_src_hash(src)}\n")
+    print(open(out).read())
+
+
+def summarize_trace(args):
+    """Write profiles/<name>.kernel_stats.txt from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+
+    rows = list(csv.DictReader(open(args.stats_csv)))
+    out = os.path.join(ROOT, "profiles", f"{args.stats_name}.kernel_stats.txt")
+    with open(out, "w") as fo:
+        fo.write(f"# per-kernel durations (rocprofv3 kernel trace)\n")
+        fo.write(f"# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                 f"python3 <repo>/bench.py {args.stats_cmd}\n")
+        fo.write(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total%':>7}  kernel\n")
+        for r in rows:
+            fo.write(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}  {r['Name'][:110]}\n")
+    print(open(out).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "prefill"])
+    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "prefill", "copy"])
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--counters-dir", help="summarize rocprofv3 --pmc runs found in this directory and exit")
+    ap.add_argument("--kernel", default="index_scores_mfma")
+    ap.add_argument("--kernel-src", default="dsa_index.hip")
+    ap.add_argument("--counters-name", default="dsa_index_scores_T131072")
+    ap.add_argument("--counters-cmd", default="--steps 5 --warmup 1 --no-cpu")
+    ap.add_argument("--stats-csv", help="summarize a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--stats-name", default="dsa_decode_T131072_B1")
+    ap.add_argument("--stats-cmd", default="")
     args = ap.parse_args()
+    if args.stats_csv:
+        summarize_trace(args)
+        return
+    if args.counters_dir:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -335,6 +449,8 @@ def main():
         sys.exit(1)
     if args.workload == "dsa_decode":
         bench_dsa_decode(args)
+    elif args.workload == "copy":
+        bench_copy(args)
     else:
         bench_prefill(args)
 

@@ -153,6 +153,24 @@ mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype
                                const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel,
                                int32_t sel_stride, float sm_scale, float *out, void *ws,
                                size_t ws_bytes, void *stream);
+/* The same decode in its two steps, for callers that overlap the query absorption with other
+ * work (it needs neither the cache nor the selection, e.g. it can run on a second stream
+ * while dsa_index_scores and dsa_topk_select run):
+ *   mla_decode_absorb   q_abs = W_UK^T q_nope into the workspace       ([MLA] sec. 2.3, first step)
+ *   mla_decode_attend   everything after it, reading q_abs from the same workspace
+ * Arguments mean what they mean for mla_absorbed_decode.  The two calls must see the same
+ * d, B, dtypes and kv_b, and the same ws (of at least mla_decode_workspace_bytes(d, B,
+ * max_keys) bytes; the absorb step alone uses only its first part), in stream order, and
+ * with no other decode on that workspace in between.  Unlike the fused call, attend on the
+ * matrix-core path (bf16, 64 heads, kv_lora 512, qk_rope 64, 16-byte aligned kv_b) returns
+ * MLA_ERR_UNSUPPORTED for q_rope, Lc or Rc that are not 16-byte aligned. */
+mla_status mla_decode_absorb(const void *q_nope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
+                             const mla_dims *d, int32_t B, void *ws, size_t ws_bytes, void *stream);
+mla_status mla_decode_attend(const void *q_rope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
+                             const mla_dims *d, int32_t B, const mla_kv_view *kv, const int32_t *sel,
+                             const int32_t *nsel, int32_t sel_stride, float sm_scale, float *out, void *ws,
+                             size_t ws_bytes, void *stream);
+
 
 /* ---------------------------------------------------------------------------------
  * Non-absorbed causal prefill of S queries of one sequence.  [MLA] sec. 2.3

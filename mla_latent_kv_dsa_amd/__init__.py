@@ -28,7 +28,8 @@ MLA_FP32, MLA_BF16 = 0, 1
 
 EXPORTED = (
     "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
-    "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_prefill_workspace_bytes",
+    "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
+    "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
 
@@ -79,6 +80,12 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P,
                                       ctypes.c_size_t, P]
     L.mla_absorbed_decode.restype = st
+    L.mla_decode_absorb.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), i32, P,
+                                    ctypes.c_size_t, P]
+    L.mla_decode_absorb.restype = st
+    L.mla_decode_attend.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), i32,
+                                    ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    L.mla_decode_attend.restype = st
     L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
     L.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.mla_prefill_nonabsorbed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims),
@@ -240,14 +247,7 @@ def mla_decode_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, B: 
     return int(lib().mla_decode_workspace_bytes(ctypes.byref(_dims(H, nope, rope, v, L)), B, max_keys))
 
 
-def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache,
-                        sm_scale: float, sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
-                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Absorbed MLA decode: q_nope [B, H, nope], q_rope [B, H, rope] (rotated),
-    kv_b [H*(nope+v), L]; sel int32 [B, k] / nsel int32 [B] or None for dense causal.
-    Returns out [B, H, v] float32."""
-    _dev(q_nope, q_rope, kv_b, sel, nsel, out, ws)
-    _contig(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+def _decode_args(q_nope, q_rope, kv_b, kv, sel, nsel):
     B, H, nope = q_nope.shape
     rope = q_rope.shape[2]
     L = kv_b.shape[1]
@@ -256,7 +256,6 @@ def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.
     v = kv_b.shape[0] // H - nope
     if kv.lc.shape[1] != L or kv.rc.shape[1] != rope:
         raise ValueError("cache widths must match kv_lora and qk_rope")
-    d = _dims(H, nope, rope, v, L)
     sel_stride = 0
     if sel is not None:
         if sel.dtype != torch.int32 or sel.dim() != 2 or sel.shape[0] != B or nsel is None:
@@ -265,6 +264,18 @@ def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.
             raise ValueError("nsel must be int32 [B]")
         sel_stride = sel.shape[1]
     max_keys = sel_stride if sel is not None else kv.view.max_seq_len
+    return B, H, nope, rope, v, L, _dims(H, nope, rope, v, L), sel_stride, max_keys
+
+
+def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache,
+                        sm_scale: float, sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Absorbed MLA decode: q_nope [B, H, nope], q_rope [B, H, rope] (rotated),
+    kv_b [H*(nope+v), L]; sel int32 [B, k] / nsel int32 [B] or None for dense causal.
+    Returns out [B, H, v] float32."""
+    _dev(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    B, H, nope, rope, v, L, d, sel_stride, max_keys = _decode_args(q_nope, q_rope, kv_b, kv, sel, nsel)
     if out is None:
         out = torch.empty((B, H, v), dtype=torch.float32, device=q_nope.device)
     need = int(lib().mla_decode_workspace_bytes(ctypes.byref(d), B, max_keys))
@@ -274,6 +285,38 @@ def mla_absorbed_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.
                                      ctypes.byref(d), B, ctypes.byref(kv.view), _ptr(sel), _ptr(nsel),
                                      sel_stride, float(sm_scale), _ptr(out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(q_nope.device)))
+    return out
+
+
+def mla_decode_absorb(q_nope: torch.Tensor, kv_b: torch.Tensor, ws: torch.Tensor, qk_rope: int = 64) -> None:
+    """First step of the absorbed decode, q_abs = W_UK^T q_nope, written into ws for a later
+    mla_decode_attend on the same ws (uint8 device tensor of at least
+    mla_decode_workspace_bytes(...) bytes).  q_nope [B, H, nope], kv_b [H*(nope+v), L]."""
+    _dev(q_nope, kv_b, ws)
+    _contig(q_nope, kv_b, ws)
+    B, H, nope = q_nope.shape
+    if kv_b.shape[0] % H:
+        raise ValueError("kv_b rows must be a multiple of the head count")
+    d = _dims(H, nope, qk_rope, kv_b.shape[0] // H - nope, kv_b.shape[1])
+    _check(lib().mla_decode_absorb(_ptr(q_nope), _dt(q_nope), _ptr(kv_b), _dt(kv_b), ctypes.byref(d), B, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(q_nope.device)))
+
+
+def mla_decode_attend(q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache, qk_nope: int, sm_scale: float,
+                      ws: torch.Tensor, sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Second step of the absorbed decode: scores, softmax, latent accumulation and W_UV,
+    reading q_abs from ws (written by mla_decode_absorb).  Returns out [B, H, v] float32."""
+    _dev(q_rope, kv_b, sel, nsel, out, ws)
+    _contig(q_rope, kv_b, sel, nsel, out, ws)
+    B, H, _ = q_rope.shape
+    shape_only = torch.empty((B, H, qk_nope), dtype=q_rope.dtype, device="meta")
+    B, H, nope, rope, v, L, d, sel_stride, max_keys = _decode_args(shape_only, q_rope, kv_b, kv, sel, nsel)
+    if out is None:
+        out = torch.empty((B, H, v), dtype=torch.float32, device=q_rope.device)
+    _check(lib().mla_decode_attend(_ptr(q_rope), _dt(q_rope), _ptr(kv_b), _dt(kv_b), ctypes.byref(d), B,
+                                   ctypes.byref(kv.view), _ptr(sel), _ptr(nsel), sel_stride, float(sm_scale),
+                                   _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(q_rope.device)))
     return out
 
 

@@ -171,6 +171,42 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t max_keys
                : decode_workspace_bytes(*d, B, max_keys, MLA_FP32);
 }
 
+// Checks shared by the decode entry points (everything but the tensors each step reads).
+static mla_status check_decode_common(const mla_dims *d, int32_t B, mla_dtype q_dt, mla_dtype w_dt)
+{
+    mla_status st = check_dims(d);
+    if (st) return st;
+    if (B < 0) return fail(MLA_ERR_ARG, "decode: B negative");
+    if (!valid_dtype(q_dt) || !valid_dtype(w_dt)) return fail(MLA_ERR_ARG, "decode: dtype invalid");
+    if (q_dt != w_dt) return fail(MLA_ERR_UNSUPPORTED, "decode: q and kv_b dtypes must match");
+    return MLA_OK;
+}
+
+static mla_status check_decode_attend(const mla_dims *d, int32_t B, mla_dtype q_dt, mla_dtype w_dt,
+                                      const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel,
+                                      int32_t sel_stride, float sm_scale)
+{
+    mla_status st = check_decode_common(d, B, q_dt, w_dt);
+    if (st) return st;
+    st = check_view(kv, B, true, false, true);
+    if (st) return st;
+    if (q_dt != kv->kv_dtype) return fail(MLA_ERR_UNSUPPORTED, "decode: q, kv_b and cache dtypes must match");
+    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "decode: sm_scale not finite");
+    if (sel) {
+        if (!nsel) return fail(MLA_ERR_ARG, "decode: sel given without nsel");
+        if (sel_stride <= 0) return fail(MLA_ERR_ARG, "decode: sel_stride must be positive");
+    }
+    return MLA_OK;
+}
+
+static mla_status check_ws(const char *what, size_t need, const void *ws, size_t ws_bytes)
+{
+    if (need && (!ws || ws_bytes < need))
+        return fail(MLA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", what, need,
+                    ws ? ws_bytes : (size_t)0);
+    return MLA_OK;
+}
+
 mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt,
                                const void *kv_b, mla_dtype w_dt, const mla_dims *d, int32_t B,
                                const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel,
@@ -178,27 +214,45 @@ mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype
                                size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
-    mla_status st = check_dims(d);
+    mla_status st = check_decode_attend(d, B, q_dt, w_dt, kv, sel, nsel, sel_stride, sm_scale);
     if (st) return st;
-    if (B < 0) return fail(MLA_ERR_ARG, "decode: B negative");
-    if (!valid_dtype(q_dt) || !valid_dtype(w_dt)) return fail(MLA_ERR_ARG, "decode: dtype invalid");
-    st = check_view(kv, B, true, false, true);
-    if (st) return st;
-    if (q_dt != w_dt || q_dt != kv->kv_dtype)
-        return fail(MLA_ERR_UNSUPPORTED, "decode: q, kv_b and cache dtypes must match");
-    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "decode: sm_scale not finite");
-    if (sel) {
-        if (!nsel) return fail(MLA_ERR_ARG, "decode: sel given without nsel");
-        if (sel_stride <= 0) return fail(MLA_ERR_ARG, "decode: sel_stride must be positive");
-    }
     if (B == 0) return MLA_OK;
     if (!q_nope || !q_rope || !kv_b || !out) return fail(MLA_ERR_ARG, "decode: NULL tensor");
-    int64_t max_keys = sel ? (int64_t)sel_stride : kv->max_seq_len;
-    size_t need = decode_workspace_bytes(*d, B, max_keys, q_dt);
-    if (need && (!ws || ws_bytes < need))
-        return fail(MLA_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    const int64_t max_keys = sel ? (int64_t)sel_stride : kv->max_seq_len;
+    st = check_ws("decode", decode_workspace_bytes(*d, B, max_keys, q_dt), ws, ws_bytes);
+    if (st) return st;
     return launch_decode(q_nope, q_rope, kv_b, q_dt, *d, B, to_view(*kv), sel, nsel, sel_stride, max_keys,
                          sm_scale, out, ws, ws_bytes, (hipStream_t)stream);
+}
+
+mla_status mla_decode_absorb(const void *q_nope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
+                             const mla_dims *d, int32_t B, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_decode_common(d, B, q_dt, w_dt);
+    if (st) return st;
+    if (B == 0) return MLA_OK;
+    if (!q_nope || !kv_b) return fail(MLA_ERR_ARG, "decode absorb: NULL tensor");
+    st = check_ws("decode absorb", decode_absorb_workspace_bytes(*d, B, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return launch_decode_absorb(q_nope, kv_b, q_dt, *d, B, ws, (hipStream_t)stream);
+}
+
+mla_status mla_decode_attend(const void *q_rope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
+                             const mla_dims *d, int32_t B, const mla_kv_view *kv, const int32_t *sel,
+                             const int32_t *nsel, int32_t sel_stride, float sm_scale, float *out, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_decode_attend(d, B, q_dt, w_dt, kv, sel, nsel, sel_stride, sm_scale);
+    if (st) return st;
+    if (B == 0) return MLA_OK;
+    if (!q_rope || !kv_b || !out) return fail(MLA_ERR_ARG, "decode attend: NULL tensor");
+    const int64_t max_keys = sel ? (int64_t)sel_stride : kv->max_seq_len;
+    st = check_ws("decode attend", decode_workspace_bytes(*d, B, max_keys, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return launch_decode_attend(q_rope, kv_b, q_dt, *d, B, to_view(*kv), sel, nsel, sel_stride, max_keys, sm_scale,
+                                out, ws, (hipStream_t)stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T)

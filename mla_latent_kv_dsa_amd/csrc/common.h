@@ -119,6 +119,12 @@ mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int3
                        hipStream_t s);
 
 size_t decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t max_keys, mla_dtype dt);
+size_t decode_absorb_workspace_bytes(const mla_dims &d, int32_t B, mla_dtype dt);
+mla_status launch_decode_absorb(const void *q_nope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                void *ws, hipStream_t s);
+mla_status launch_decode_attend(const void *q_rope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                                int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s);
 mla_status launch_decode(const void *q_nope, const void *q_rope, const void *kv_b, mla_dtype dt,
                          const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
                          const int32_t *nsel, int32_t sel_stride, int64_t max_keys,

@@ -178,42 +178,56 @@ size_t decode_generic_ws(const mla_dims &d, int32_t B, int64_t max_keys)
     return BH * d.kv_lora * 4 + BH * NS * 8 + BH * NS * (size_t)d.kv_lora * 4 + 256;
 }
 
+size_t decode_generic_absorb_ws(const mla_dims &d, int32_t B) { return (size_t)B * d.n_heads * d.kv_lora * 4; }
+
+// Workspace layout: q_abs (fp32, depends on B only) | split maxima | split sums | split latents
+mla_status launch_absorb_generic(const void *q_nope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                 void *ws, hipStream_t s)
+{
+    const int H = d.n_heads, nope = d.qk_nope, v = d.v_head, L = d.kv_lora;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: B*H too large");
+    float *q_abs = reinterpret_cast<float *>(ws);
+    const dim3 g((unsigned)BH, (L + 255) / 256);
+    if (dt == MLA_FP32)
+        hipLaunchKernelGGL(absorb_generic<float>, g, dim3(256), 0, s, (const float *)q_nope, (const float *)kv_b, H,
+                           nope, v, L, q_abs);
+    else
+        hipLaunchKernelGGL(absorb_generic<bf16_t>, g, dim3(256), 0, s, (const bf16_t *)q_nope, (const bf16_t *)kv_b,
+                           H, nope, v, L, q_abs);
+    return check_launch("absorb_generic");
+}
+
 template <typename T>
-static mla_status run_generic(const void *q_nope, const void *q_rope, const void *kv_b, const mla_dims &d,
-                              int32_t B, const KvView &kv, const int32_t *sel, const int32_t *nsel,
-                              int32_t sel_stride, int64_t max_keys, float sm_scale, float *out, void *ws,
-                              hipStream_t s)
+static mla_status attend_generic(const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B, const KvView &kv,
+                                 const int32_t *sel, const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
+                                 float sm_scale, float *out, void *ws, hipStream_t s)
 {
     const int H = d.n_heads, nope = d.qk_nope, rope = d.qk_rope, v = d.v_head, L = d.kv_lora;
     const int NS = generic_splits(max_keys);
     const int64_t BH = (int64_t)B * H;
+    if (BH > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: B*H too large");
     float *q_abs = reinterpret_cast<float *>(ws);
     float *pm = q_abs + BH * L;
     float *pl = pm + BH * NS;
     float *pc = pl + BH * NS;
-    if (BH > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: B*H too large");
-    hipLaunchKernelGGL(absorb_generic<T>, dim3((unsigned)BH, (L + 255) / 256), dim3(256), 0, s,
-                       (const T *)q_nope, (const T *)kv_b, H, nope, v, L, q_abs);
-    mla_status st = check_launch("absorb_generic");
-    if (st) return st;
     const size_t shm = (size_t)(L + rope + kChunk) * 4 + (size_t)kChunk * 8;
     hipLaunchKernelGGL(decode_core_generic<T>, dim3(NS, (unsigned)BH), dim3(256), shm, s, q_abs,
                        (const T *)q_rope, H, rope, L, kv, sel, nsel, sel_stride, sm_scale, NS, pm, pl, pc);
-    st = check_launch("decode_core_generic");
+    mla_status st = check_launch("decode_core_generic");
     if (st) return st;
     hipLaunchKernelGGL(combine_unabsorb_generic<T>, dim3((unsigned)BH, (v + 63) / 64), dim3(256), (size_t)L * 4, s,
                        pm, pl, pc, NS, (const T *)kv_b, H, nope, v, L, out);
     return check_launch("combine_unabsorb_generic");
 }
 
-mla_status launch_decode_generic(const void *q_nope, const void *q_rope, const void *kv_b, mla_dtype dt,
-                                 const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
-                                 const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale,
-                                 float *out, void *ws, hipStream_t s)
+mla_status launch_attend_generic(const void *q_rope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                 const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                                 int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s)
 {
     if (dt == MLA_FP32)
-        return run_generic<float>(q_nope, q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
-    return run_generic<bf16_t>(q_nope, q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
+        return attend_generic<float>(q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
+    return attend_generic<bf16_t>(q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
 }
 
 }  // namespace mla

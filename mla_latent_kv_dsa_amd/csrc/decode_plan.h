@@ -15,15 +15,20 @@ inline int generic_splits(int64_t max_keys)
 }
 
 size_t decode_generic_ws(const mla_dims &d, int32_t B, int64_t max_keys);
-mla_status launch_decode_generic(const void *q_nope, const void *q_rope, const void *kv_b, mla_dtype dt,
-                                 const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
-                                 const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale,
-                                 float *out, void *ws, hipStream_t s);
+size_t decode_generic_absorb_ws(const mla_dims &d, int32_t B);
+mla_status launch_absorb_generic(const void *q_nope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                 void *ws, hipStream_t s);
+mla_status launch_attend_generic(const void *q_rope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
+                                 const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                                 int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s);
 
 bool decode_mfma_supported(const mla_dims &d, mla_dtype dt);
 size_t decode_mfma_ws(const mla_dims &d, int32_t B, int64_t max_keys);
-mla_status launch_decode_mfma(const void *q_nope, const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B,
-                              const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
-                              int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s);
+size_t decode_mfma_absorb_ws(int32_t B);
+mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_dims &d, int32_t B, void *ws,
+                              hipStream_t s);
+mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B, const KvView &kv,
+                              const int32_t *sel, const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
+                              float sm_scale, float *out, void *ws, hipStream_t s);
 
 }  // namespace mla

@@ -151,6 +151,32 @@ def test_decode_validation(L):
     assert f(B=0) == mla.MLA_OK
 
 
+def test_decode_split_validation(L):
+    _no_gpu()
+    d = _dims()
+
+    def a(d=d, B=1, q_dt=1, w_dt=1, q=FAKE, w=FAKE, ws=None, wsb=0):
+        return L.mla_decode_absorb(q, q_dt, w, w_dt, ctypes.byref(d), B, ws, wsb, None)
+
+    def t(d=d, B=1, v=None, q_dt=1, w_dt=1, sel=None, nsel=None, sel_stride=0, ws=None, wsb=0, scale=0.0625):
+        return L.mla_decode_attend(FAKE, q_dt, FAKE, w_dt, ctypes.byref(d), B, ctypes.byref(v or _view()), sel, nsel,
+                                   sel_stride, scale, FAKE, ws, wsb, None)
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 4096)
+    assert a() == mla.MLA_ERR_WORKSPACE                  # the absorb step still needs its part
+    assert a(ws=FAKE, wsb=1) == mla.MLA_ERR_WORKSPACE
+    assert a(q_dt=0) == mla.MLA_ERR_UNSUPPORTED
+    assert a(q=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
+    assert a(d=_dims(n_heads=0)) == mla.MLA_ERR_ARG
+    assert a(B=-1) == mla.MLA_ERR_ARG
+    assert a(B=0) == mla.MLA_OK
+    assert t() == mla.MLA_ERR_WORKSPACE
+    assert t(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert t(sel=FAKE, nsel=None, sel_stride=2048) == mla.MLA_ERR_ARG
+    assert t(v=_view(lc=None)) == mla.MLA_ERR_ARG
+    assert t(scale=float("nan")) == mla.MLA_ERR_ARG
+    assert t(B=0) == mla.MLA_OK
+
+
 def test_prefill_validation(L):
     _no_gpu()
     d = _dims()

@@ -275,6 +275,32 @@ def test_decode_selected_keys_and_keep_all_equals_dense():
     assert np.array_equal(dense, kept)
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+def test_decode_split_steps_equal_fused(bf16):
+    """mla_decode_absorb followed by mla_decode_attend on one workspace gives the fused call's
+    output bit for bit (matrix-core path for bf16 GLM shapes, generic kernels for fp32)."""
+    T, k = 900, 300
+    d = synth.decode(40, T, B=2, bf16=bf16)
+    rng = np.random.default_rng(41)
+    sel = np.full((2, k), -1, np.int32)
+    sel[0] = np.sort(rng.choice(T, k, replace=False))
+    sel[1, :77] = np.sort(rng.choice(600, 77, replace=False))
+    nsel = np.array([k, 77], np.int32)
+    to = dev_bf16 if bf16 else dev
+    kv = _kv(d.lc, d.rc, None, [T, 600], T, seq_stride=T, bf16=bf16)
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    qn, qr, kvb = to(d.q_nope), to(d.q_rope), to(d.kv_b)
+    sl, ns = dev(sel), dev(nsel)
+    log(f"decode split steps bf16={bf16}")
+    fused = host(mla.mla_absorbed_decode(qn, qr, kvb, kv, sm, sel=sl, nsel=ns))
+    need = mla.mla_decode_workspace_bytes(d.H, d.nope, d.rope, d.v, d.L, 2, k)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    mla.mla_decode_absorb(qn, kvb, ws, qk_rope=d.rope)
+    split = host(mla.mla_decode_attend(qr, kvb, kv, d.nope, sm, ws, sel=sl, nsel=ns))
+    assert np.array_equal(fused, split)
+    assert rel_err(split[1], _decode_ref(d, 1, sel[1, :77], sm)) <= (TOL_BF16 if bf16 else TOL_F32)
+
+
 def test_decode_paged_equals_contiguous():
     T = 640
     d = synth.decode(30, T, B=2)
