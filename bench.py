@@ -99,9 +99,11 @@ def bench_dsa_decode(args):
                            nsel=torch.empty((B,), dtype=torch.int32, device=dev),
                            out=torch.empty((B, H, V), dtype=torch.float32, device=dev)))
     tk_need = mla.dsa_topk_workspace_bytes(B, T, K)
+    sel_need = mla.dsa_index_select_workspace_bytes(B, T, K)
     dec_need = mla.mla_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, K)
     for c in copies:
         c["tk_ws"] = torch.empty(max(tk_need, 1), dtype=torch.uint8, device=dev)
+        c["sel_ws"] = torch.empty(max(sel_need, 1), dtype=torch.uint8, device=dev)
         c["dec_ws"] = torch.empty(max(dec_need, 1), dtype=torch.uint8, device=dev)
 
     def rope(c):
@@ -112,6 +114,10 @@ def bench_dsa_decode(args):
 
     def topk(c):
         mla.dsa_topk_select(c["scores"], c["seq_len"], K, sel=c["sel"], nsel=c["nsel"], ws=c["tk_ws"])
+
+    def select(c):
+        mla.dsa_index_select(c["qi"], c["wi"], c["kv"], T, K, scores=c["scores"], sel=c["sel"], nsel=c["nsel"],
+                             ws=c["sel_ws"])
 
     def absorb(c):
         mla.mla_decode_absorb(c["qn"], c["kvb"], c["dec_ws"], qk_rope=ROPE)
@@ -124,8 +130,7 @@ def bench_dsa_decode(args):
         # one stream: a fork/join across two streams inside the captured graph cost more per
         # step than running the query absorption beside the top-k saved
         rope(c)
-        index(c)
-        topk(c)
+        select(c)      # indexer scores + top-k in one call
         absorb(c)
         attend(c)
 
@@ -179,7 +184,7 @@ def bench_dsa_decode(args):
 
     # per-kernel durations: each part alone, captured back to back over every input copy
     # (REPS passes) in one HIP graph, replayed between two events on the launch stream
-    parts = {"rope": rope, "index": index, "topk": topk, "absorb": absorb, "attend": attend}
+    parts = {"rope": rope, "select": select, "absorb": absorb, "attend": attend, "index": index, "topk": topk}
     us = {}
     REPS = 4
     for k, f in parts.items():
@@ -218,7 +223,7 @@ def bench_dsa_decode(args):
     kvb_bytes = H * (NOPE + V) * L * 2
     step_bytes = ic_bytes + sel_kv_bytes + kvb_bytes + score_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
     stream_bytes = ic_bytes + sel_kv_bytes
-    stream_us = us["index"] + us["topk"] + us["attend"]
+    stream_us = us["select"] + us["attend"]
     src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", "dsa_index.hip")
     traffic = _traffic("dsa_index_scores_T131072", src, idx_bytes)
 
@@ -234,12 +239,14 @@ def bench_dsa_decode(args):
                    "qk_rope": ROPE, "v_head": V, "kv_lora": L, "index_heads": N_IH, "index_hd": HD,
                    "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "input_copies": args.copies,
                    "hip_graphs": bool(graphs)},
-        "roofline": {"kernel": "dsa_index_scores", "bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "index_scores_mfma (dsa_index_scores; the step runs the same kernel with the "
+                               "selection histogram added, inside dsa_index_select)",
+                     "bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": idx_bytes, "avg_us": us["index"]},
         "cpu_baseline": cpu,
         "breakdown_us": us,
-        "stream": {"bytes": stream_bytes, "us_index_topk_attend": stream_us,
+        "stream": {"bytes": stream_bytes, "us_select_attend": stream_us,
                    "GBs": stream_bytes / (stream_us * 1e-6) / 1e9,
                    "frac": stream_bytes / (stream_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "whole_step": {"bytes": step_bytes, "GBs": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -129,6 +129,25 @@ mla_status dsa_topk_select(const float *scores, int32_t B, int64_t t_max,
                            void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * The indexer and the top-k of every row in one call ([MLA] sec. 2.2: score every causal key,
+ * keep the top-k).  The result equals dsa_index_scores(...) followed by dsa_topk_select(...)
+ * with n_valid[b] = the row's causal length (seq_len[b], or max_seq_len without seq_len,
+ * clamped to [0, t_max]): the same scores, the same sel and nsel, bit for bit.  Fewer passes
+ * over the scores: the first histogram of the selection is taken while the scores are
+ * produced.
+ *   q_idx, w_idx, kv, t_max, scores   as for dsa_index_scores (scores is written too)
+ *   k, sel, nsel                      as for dsa_topk_select
+ *   ws   device workspace of at least dsa_index_select_workspace_bytes(B, t_max, k) bytes
+ *        (its content on entry does not matter; it is scratch)
+ * Supported: 1 <= k <= 65536, t_max < 2^31 (rows up to 262144 keys take the single-pass
+ * selection, longer ones the general top-k).
+ * --------------------------------------------------------------------------------- */
+size_t dsa_index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
+mla_status dsa_index_select(const float *q_idx, const float *w_idx, int32_t B, int32_t n_ih,
+                            const mla_kv_view *kv, int64_t t_max, int32_t k, float *scores,
+                            int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Absorbed MLA decode, one query per sequence.  [MLA] sec. 2.3 (absorbed path):
  *   q_abs[b][h]   = W_UK[h]^T q_nope[b][h]                    (fold W_UK into the query)
  *   s[b][h][t]    = sm_scale * (q_abs[b][h] . Lc(b,t) + q_rope[b][h] . Rc(b,t))

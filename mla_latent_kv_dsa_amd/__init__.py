@@ -28,6 +28,7 @@ MLA_FP32, MLA_BF16 = 0, 1
 
 EXPORTED = (
     "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
+    "dsa_index_select_workspace_bytes", "dsa_index_select",
     "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
     L.dsa_topk_workspace_bytes.restype = ctypes.c_size_t
     L.dsa_topk_select.argtypes = [P, i32, i64, P, i32, P, P, P, ctypes.c_size_t, P]
     L.dsa_topk_select.restype = st
+    L.dsa_index_select_workspace_bytes.argtypes = [i32, i64, i32]
+    L.dsa_index_select_workspace_bytes.restype = ctypes.c_size_t
+    L.dsa_index_select.argtypes = [P, P, i32, i32, ctypes.POINTER(mla_kv_view), i64, i32, P, P, P, P,
+                                   ctypes.c_size_t, P]
+    L.dsa_index_select.restype = st
     L.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
     L.mla_decode_workspace_bytes.restype = ctypes.c_size_t
     L.mla_absorbed_decode.argtypes = [P, P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), i32,
@@ -235,6 +241,39 @@ def dsa_topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int, sel: Op
     _check(lib().dsa_topk_select(_ptr(scores), B, t_max, _ptr(n_valid), k, _ptr(sel), _ptr(nsel), _ptr(ws),
                                  ws.numel() * ws.element_size() if ws is not None else 0, _stream(dev)))
     return sel, nsel
+
+
+def dsa_index_select_workspace_bytes(B: int, t_max: int, k: int) -> int:
+    return int(lib().dsa_index_select_workspace_bytes(B, t_max, k))
+
+
+def dsa_index_select(q_idx: torch.Tensor, w_idx: torch.Tensor, kv: KvCache, t_max: int, k: int,
+                     scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                     nsel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Indexer scores and the top-k of every row in one call; returns (scores [B, t_max],
+    sel [B, k] int32 with -1 padding, nsel [B] int32), equal to dsa_index_scores followed
+    by dsa_topk_select with n_valid = the rows' causal lengths."""
+    _dev(q_idx, w_idx, scores, sel, nsel, ws)
+    _contig(q_idx, w_idx, scores, sel, nsel, ws)
+    B, n_ih, hd = q_idx.shape
+    if w_idx.shape != (B, n_ih) or q_idx.dtype != torch.float32 or w_idx.dtype != torch.float32:
+        raise ValueError("q_idx [B, n_ih, hd] and w_idx [B, n_ih] must be float32")
+    if kv.ic is None or kv.ic.shape[1] != hd:
+        raise ValueError("kv.ic width must equal q_idx's last dim")
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((B, t_max), dtype=torch.float32, device=dev)
+    elif scores.shape != (B, t_max) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [B, t_max]")
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev) if nsel is None else nsel
+    need = dsa_index_select_workspace_bytes(B, t_max, k)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().dsa_index_select(_ptr(q_idx), _ptr(w_idx), B, n_ih, ctypes.byref(kv.view), t_max, k, _ptr(scores),
+                                  _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                  _stream(dev)))
+    return scores, sel, nsel
 
 
 def _dims(H: int, nope: int, rope: int, v: int, L: int) -> mla_dims:

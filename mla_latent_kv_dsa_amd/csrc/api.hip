@@ -135,7 +135,7 @@ mla_status dsa_index_scores(const float *q_idx, const float *w_idx, int32_t B, i
     if (!q_idx || !w_idx || !scores) return fail(MLA_ERR_ARG, "index: NULL tensor");
     KvView v = to_view(*kv);
     if (v.max_seq_len > t_max) v.max_seq_len = t_max;
-    return launch_index_scores(q_idx, w_idx, B, n_ih, kv->index_hd, v, t_max, scores, (hipStream_t)stream);
+    return launch_index_scores(q_idx, w_idx, B, n_ih, kv->index_hd, v, t_max, scores, nullptr, (hipStream_t)stream);
 }
 
 size_t dsa_topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k)
@@ -159,7 +159,41 @@ mla_status dsa_topk_select(const float *scores, int32_t B, int64_t t_max, const 
     size_t need = dsa_topk_workspace_bytes(B, t_max, k);
     if (need && (!ws || ws_bytes < need))
         return fail(MLA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-    return launch_topk(scores, B, t_max, n_valid, k, sel, nsel, ws, ws_bytes, (hipStream_t)stream);
+    return launch_topk(scores, B, t_max, n_valid, t_max, k, sel, nsel, ws, ws_bytes, (hipStream_t)stream);
+}
+
+size_t dsa_index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k)
+{
+    if (B <= 0 || t_max <= 0 || k <= 0) return 0;
+    return index_select_workspace_bytes(B, t_max, k);
+}
+
+mla_status dsa_index_select(const float *q_idx, const float *w_idx, int32_t B, int32_t n_ih, const mla_kv_view *kv,
+                            int64_t t_max, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
+                            size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (B < 0 || t_max < 0) return fail(MLA_ERR_ARG, "select: B or t_max negative");
+    if (n_ih <= 0) return fail(MLA_ERR_ARG, "select: n_ih must be positive");
+    if (n_ih > 64) return fail(MLA_ERR_UNSUPPORTED, "select: n_ih > 64");
+    if (k <= 0) return fail(MLA_ERR_ARG, "select: k must be positive");
+    if (k > 65536) return fail(MLA_ERR_UNSUPPORTED, "select: k > 65536");
+    mla_status st = check_view(kv, B, false, true, true);
+    if (st) return st;
+    if (kv->index_hd <= 0 || kv->index_hd % 4 != 0)
+        return fail(MLA_ERR_ARG, "select: index_hd must be a positive multiple of 4");
+    if (kv->index_hd > 256) return fail(MLA_ERR_UNSUPPORTED, "select: index_hd > 256");
+    if (t_max >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "select: t_max >= 2^31");
+    if (B == 0) return MLA_OK;
+    if (!q_idx || !w_idx || !sel || !nsel || (!scores && t_max > 0)) return fail(MLA_ERR_ARG, "select: NULL tensor");
+    size_t need = dsa_index_select_workspace_bytes(B, t_max, k);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MLA_ERR_WORKSPACE, "select: workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    KvView v = to_view(*kv);
+    if (v.max_seq_len > t_max) v.max_seq_len = t_max;
+    return launch_index_select(q_idx, w_idx, B, n_ih, kv->index_hd, v, t_max, k, scores, sel, nsel, ws, ws_bytes,
+                               (hipStream_t)stream);
 }
 
 size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t max_keys)

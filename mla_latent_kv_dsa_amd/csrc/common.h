@@ -89,6 +89,15 @@ __device__ __forceinline__ int64_t seq_len_of(const KvView &v, int b)
     return s;
 }
 
+// ------------------------------------------------------------------ selection keys
+// Order-preserving map fp32 -> uint32 (larger score -> larger key); -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ------------------------------------------------------------------ wave helpers (wave64)
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -109,14 +118,21 @@ mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, in
                        int64_t head_stride, int32_t rope_off, int32_t rope_dim, const int32_t *pos,
                        double theta, hipStream_t s);
 
-mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih,
-                               int32_t hd, const KvView &kv, int64_t t_max, float *scores,
-                               hipStream_t s);
+// ghist (optional): [B][2048] histogram of the top 11 order-key bits of the scores of keys
+// t < seq_len, accumulated with atomics (the caller zeroes it first)
+mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd,
+                               const KvView &kv, int64_t t_max, float *scores, uint32_t *ghist, hipStream_t s);
 
+mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, uint32_t *ghist,
+                             hipStream_t s);
+size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
+mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
+                               int64_t t_max, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
+                               size_t ws_bytes, hipStream_t s);
 size_t topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
-mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid,
-                       int32_t k, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes,
-                       hipStream_t s);
+// n_valid (optional): row lengths, clamped to [0, max_len]; without it every row has max_len
+mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid, int64_t max_len,
+                       int32_t k, int32_t *sel, int32_t *nsel, void *ws, size_t ws_bytes, hipStream_t s);
 
 size_t decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t max_keys, mla_dtype dt);
 size_t decode_absorb_workspace_bytes(const mla_dims &d, int32_t B, mla_dtype dt);

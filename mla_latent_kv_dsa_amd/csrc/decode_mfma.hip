@@ -385,15 +385,19 @@ __global__ __launch_bounds__(256) void combine_unabsorb(const float *__restrict_
     }
 
     float2 x[CU_QB][CU_SB];
+    // unconditional loads (query and split clamped into range), zeroed after: conditional loads
+    // would each wait for the previous ones
     auto load_batch = [&](int q0, int s0) {
 #pragma unroll
         for (int qq = 0; qq < CU_QB; ++qq)
 #pragma unroll
-            for (int u = 0; u < CU_SB; ++u)
-                x[qq][u] = (q0 + qq < nb && s0 + u < NS)
-                               ? *reinterpret_cast<const float2 *>(
-                                     o_part + (((int64_t)(b0 + q0 + qq) * NS + s0 + u) * DM_H + h) * DM_L + 2 * tid)
-                               : make_float2(0.f, 0.f);
+            for (int u = 0; u < CU_SB; ++u) {
+                const int qc = q0 + qq < nb ? q0 + qq : nb - 1;
+                const int sc = s0 + u < NS ? s0 + u : NS - 1;
+                const float2 v = *reinterpret_cast<const float2 *>(
+                    o_part + (((int64_t)(b0 + qc) * NS + sc) * DM_H + h) * DM_L + 2 * tid);
+                x[qq][u] = (q0 + qq < nb && s0 + u < NS) ? v : make_float2(0.f, 0.f);
+            }
     };
     load_batch(0, 0);
     if (tid < nb) {

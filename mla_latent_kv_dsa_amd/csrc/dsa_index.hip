@@ -176,12 +176,18 @@ __device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE>
+// HIST: also count the top 11 order-key bits of every score with t < n (LDS histogram per
+// block, added into ghist[b] with atomics at the end) -- the first pass of the top-k selection.
+constexpr int IX_BINS = 2048;
+
+template <int MODE, bool HIST>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
                                                                      const float *__restrict__ w, KvView kv,
-                                                                     int64_t t_max, float *__restrict__ scores)
+                                                                     int64_t t_max, float *__restrict__ scores,
+                                                                     uint32_t *__restrict__ ghist)
 {
     __shared__ float sq[32 * IXM_QROW];
+    __shared__ uint32_t hs[HIST ? IX_BINS : 1];
     const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile math stays scalar
     const int64_t n = seq_len_of(kv, b) < t_max ? seq_len_of(kv, b) : t_max;
@@ -194,6 +200,8 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     for (int64_t t = ntv * 64 + (int64_t)blockIdx.x * 64 * IXM_WAVES + tid; t < t_max; t += waves_total * 64)
         out[t] = -INFINITY;
 
+    if (HIST)
+        for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) hs[i] = 0u;
     // query to LDS: all four loads in flight before the first store
     const float4 *qb = reinterpret_cast<const float4 *>(q + (int64_t)b * 32 * 128);
     float4 qv[32 * 32 / (64 * IXM_WAVES)];
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     __syncthreads();
 
     int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
-    if (tile >= ntv) return;
+    if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
     const bool lo_half = lane < 32;
 
@@ -255,14 +263,25 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
             }
         }
         const int64_t t = tile * 64 + lane;
-        if (t < t_max) out[t] = valid ? s : -INFINITY;
+        const float sc = valid ? s : -INFINITY;
+        if (t < t_max) out[t] = sc;
+        if (HIST && t < n) atomicAdd(&hs[order_key(sc) >> 21], 1u);
         p = pn;
         valid = valid_n;
+    }
+    }
+    if (HIST) {
+        __syncthreads();
+        uint32_t *gh = ghist + (int64_t)b * IX_BINS;
+        for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) {
+            const uint32_t c = hs[i];
+            if (c) atomicAdd(&gh[i], c);
+        }
     }
 }
 
 mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd,
-                               const KvView &kv, int64_t t_max, float *scores, hipStream_t s)
+                               const KvView &kv, int64_t t_max, float *scores, uint32_t *ghist, hipStream_t s)
 {
     const int64_t gx = (t_max + 255) / 256;
     if (gx > 0x7fffffff || B > 65535) return fail(MLA_ERR_UNSUPPORTED, "index: grid too large");
@@ -277,17 +296,23 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
         if (bx > need) bx = need;
         if (bx < 1) bx = 1;
         const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
-        if (!kv.bt)
-            hipLaunchKernelGGL(index_scores_mfma<0>, g, blk, 0, s, q, w, kv, t_max, scores);
-        else if (kv.bs % 64 == 0)
-            hipLaunchKernelGGL(index_scores_mfma<1>, g, blk, 0, s, q, w, kv, t_max, scores);
-        else
-            hipLaunchKernelGGL(index_scores_mfma<2>, g, blk, 0, s, q, w, kv, t_max, scores);
+        const int mode = !kv.bt ? 0 : (kv.bs % 64 == 0 ? 1 : 2);
+        if (ghist) {
+            if (mode == 0) hipLaunchKernelGGL((index_scores_mfma<0, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
+            else if (mode == 1) hipLaunchKernelGGL((index_scores_mfma<1, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
+            else hipLaunchKernelGGL((index_scores_mfma<2, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
+            return check_launch("index_scores");
+        }
+        if (mode == 0) hipLaunchKernelGGL((index_scores_mfma<0, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
+        else if (mode == 1) hipLaunchKernelGGL((index_scores_mfma<1, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
+        else hipLaunchKernelGGL((index_scores_mfma<2, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
     } else if (hd == 128 && aligned)
         hipLaunchKernelGGL(index_scores_lane_per_key<128>, grid, dim3(256), 0, s, q, w, n_ih, kv, t_max, scores);
     else
         hipLaunchKernelGGL(index_scores_generic, grid, dim3(256), 0, s, q, w, n_ih, hd, kv, t_max, scores);
-    return check_launch("index_scores");
+    mla_status st = check_launch("index_scores");
+    if (st || !ghist) return st;
+    return launch_score_hist(scores, B, t_max, kv, ghist, s);   // kernels without a built-in histogram
 }
 
 }  // namespace mla

@@ -26,14 +26,6 @@ constexpr int TK_BINS = 2048;      // top 11 bits of the key
 constexpr int TK_FINAL_THREADS = 1024;
 static_assert(TK_PER == 32, "one bitmap word per thread");
 
-// Order-preserving map fp32 -> uint32 (larger score -> larger key).  -0.0 maps like +0.0.
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Block-wide exclusive scan of one uint32 per thread (NW waves of 64).  sh needs 2*NW+1 words.
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t *total = nullptr)
@@ -65,11 +57,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, ui
     return r;
 }
 
-__device__ __forceinline__ int64_t row_len(const int32_t *n_valid, int b, int64_t t_max)
+// Row length: n_valid[b] clamped to [0, max_len], or max_len when there is no n_valid.
+__device__ __forceinline__ int64_t row_len(const int32_t *n_valid, int b, int64_t max_len)
 {
-    int64_t n = n_valid[b];
+    int64_t n = n_valid ? (int64_t)n_valid[b] : max_len;
     if (n < 0) n = 0;
-    if (n > t_max) n = t_max;
+    if (n > max_len) n = max_len;
     return n;
 }
 
@@ -100,12 +93,13 @@ __device__ __forceinline__ uint32_t load_keys32(const float *s, int64_t t0, int6
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_hist(const float *__restrict__ scores, int64_t t_max,
-                                                        const int32_t *__restrict__ n_valid, int k, int nch,
+                                                        const int32_t *__restrict__ n_valid, int64_t max_len, int k,
+                                                        int nch,
                                                         uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t h[TK_BINS];
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-    const int64_t n = row_len(n_valid, b, t_max);
+    const int64_t n = row_len(n_valid, b, max_len);
     if (n <= k) return;
     for (int i = tid; i < TK_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
@@ -123,7 +117,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist(const float *__restrict_
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_filter(const float *__restrict__ scores, int64_t t_max,
-                                                          const int32_t *__restrict__ n_valid, int k, int nch,
+                                                          const int32_t *__restrict__ n_valid, int64_t max_len, int k,
+                                                          int nch,
                                                           const uint32_t *__restrict__ hist,
                                                           uint32_t *__restrict__ bitmap, int64_t nwords,
                                                           uint2 *__restrict__ cand, uint32_t *__restrict__ meta)
@@ -132,7 +127,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter(const float *__restric
     __shared__ uint32_t sh[2 * (TK_THREADS / 64) + 1];
     __shared__ uint32_t s_tb, s_above;
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-    const int64_t n = row_len(n_valid, b, t_max);
+    const int64_t n = row_len(n_valid, b, max_len);
     if (n <= k) return;
     // 1. row histogram: thread t owns the 8 bins [2040-8t, 2048-8t) (so thread order is
     //    descending bin order) and sums them over the chunks, several chunks in flight
@@ -202,7 +197,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter(const float *__restric
 
 constexpr int TK_LDS_CAND = 6144;   // candidates staged in LDS (48 KB); more are read from memory
 
-__global__ __launch_bounds__(TK_FINAL_THREADS) void topk_final(const int32_t *__restrict__ n_valid, int64_t t_max,
+__global__ __launch_bounds__(TK_FINAL_THREADS) void topk_final(const int32_t *__restrict__ n_valid, int64_t max_len,
                                                               int k, int nch, const uint32_t *__restrict__ hist,
                                                               uint32_t *__restrict__ bitmap, int64_t nwords,
                                                               const uint2 *__restrict__ cand,
@@ -216,7 +211,7 @@ __global__ __launch_bounds__(TK_FINAL_THREADS) void topk_final(const int32_t *__
     __shared__ uint2 sc[TK_LDS_CAND];
     extern __shared__ uint32_t cc[];   // [nch + 1]: exclusive prefix of candidates per chunk
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int64_t n = row_len(n_valid, b, t_max);
+    const int64_t n = row_len(n_valid, b, max_len);
     int32_t *out = sel + (int64_t)b * k;
     if (n <= k) {
         for (int64_t i = tid; i < k; i += TK_FINAL_THREADS) out[i] = i < n ? (int32_t)i : -1;
@@ -363,8 +358,8 @@ size_t topk_workspace_bytes(int32_t B, int64_t t_max, int32_t)
     return bytes + 256;
 }
 
-mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid, int32_t k,
-                       int32_t *sel, int32_t *nsel, void *ws, size_t, hipStream_t s)
+mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid, int64_t max_len,
+                       int32_t k, int32_t *sel, int32_t *nsel, void *ws, size_t, hipStream_t s)
 {
     const int nch = tk_chunks(t_max);
     const int64_t nwords = (t_max + 31) / 32;
@@ -380,15 +375,16 @@ mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int3
     p += (size_t)B * nch * TK_CH * 8;
     uint32_t *meta = reinterpret_cast<uint32_t *>(p);
     if (nch > 0) {
-        hipLaunchKernelGGL(topk_hist, dim3(nch, B), dim3(TK_THREADS), 0, s, scores, t_max, n_valid, k, nch, hist);
+        hipLaunchKernelGGL(topk_hist, dim3(nch, B), dim3(TK_THREADS), 0, s, scores, t_max, n_valid, max_len, k, nch,
+                           hist);
         mla_status st = check_launch("topk_hist");
         if (st) return st;
-        hipLaunchKernelGGL(topk_filter, dim3(nch, B), dim3(TK_THREADS), 0, s, scores, t_max, n_valid, k, nch, hist,
+        hipLaunchKernelGGL(topk_filter, dim3(nch, B), dim3(TK_THREADS), 0, s, scores, t_max, n_valid, max_len, k, nch, hist,
                            bitmap, nwords, cand, meta);
         st = check_launch("topk_filter");
         if (st) return st;
     }
-    hipLaunchKernelGGL(topk_final, dim3(B), dim3(TK_FINAL_THREADS), (size_t)(nch + 1) * 4, s, n_valid, t_max, k, nch,
+    hipLaunchKernelGGL(topk_final, dim3(B), dim3(TK_FINAL_THREADS), (size_t)(nch + 1) * 4, s, n_valid, max_len, k, nch,
                        hist, bitmap, nwords, cand, meta, sel, nsel);
     return check_launch("topk_final");
 }

@@ -129,6 +129,27 @@ def test_topk_validation(L):
     assert f(B=0) == mla.MLA_OK
 
 
+def test_index_select_validation(L):
+    _no_gpu()
+
+    def f(B=1, n_ih=32, t=4096, k=2048, v=None, ws=None, wsb=0, scores=FAKE):
+        return L.dsa_index_select(FAKE, FAKE, B, n_ih, ctypes.byref(v or _view()), t, k, scores, FAKE, FAKE, ws, wsb,
+                                  None)
+    need = L.dsa_index_select_workspace_bytes(1, 4096, 2048)
+    assert need > 0
+    assert f() == mla.MLA_ERR_WORKSPACE
+    assert f(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert f(k=0) == mla.MLA_ERR_ARG
+    assert f(k=70000) == mla.MLA_ERR_UNSUPPORTED
+    assert f(n_ih=0) == mla.MLA_ERR_ARG
+    assert f(B=-1) == mla.MLA_ERR_ARG
+    assert f(t=1 << 31) == mla.MLA_ERR_UNSUPPORTED
+    assert f(scores=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
+    assert f(v=_view(ic=None)) == mla.MLA_ERR_ARG
+    assert f(B=0) == mla.MLA_OK
+    assert L.dsa_index_select_workspace_bytes(1, 300000, 2048) >= L.dsa_topk_workspace_bytes(1, 300000, 2048)
+
+
 def test_decode_validation(L):
     _no_gpu()
     d = _dims()

@@ -171,6 +171,77 @@ def test_index_empty_and_zero_length():
     assert np.array_equal(s[1, :5], oracle.index_scores(q[1], w[1], logical[1]))
 
 
+# ------------------------------------------------------------------------------ fused index + select
+def _select_check(q, w, kv, t_max, k, seq_len, logical=None, masks=None):
+    """dsa_index_select == dsa_index_scores + dsa_topk_select (bit for bit), and the oracle."""
+    qd, wd = dev(q), dev(w)
+    sc, sel, nsel = mla.dsa_index_select(qd, wd, kv, t_max, k)
+    ref_sc = mla.dsa_index_scores(qd, wd, kv, t_max)
+    n_valid = dev(np.minimum(np.asarray(seq_len, np.int32), t_max))
+    ref_sel, ref_nsel = mla.dsa_topk_select(ref_sc, n_valid, k)
+    assert np.array_equal(host(sc).view(np.uint32), host(ref_sc).view(np.uint32))
+    assert np.array_equal(host(nsel), host(ref_nsel))
+    assert np.array_equal(host(sel), host(ref_sel))
+    rs, rn = oracle.topk_batch(host(ref_sc), np.minimum(np.asarray(seq_len, np.int32), t_max), k)
+    assert np.array_equal(host(sel), rs) and np.array_equal(host(nsel), rn)
+    return host(sel), host(nsel)
+
+
+def test_index_select_full_context_131072():
+    d = synth.decode(3, 131072, dsa=True, bf16=True)
+    log("index+select T=131072 k=2048")
+    kv = _kv(d.lc, d.rc, d.ic, [d.T], d.T, seq_stride=d.T)
+    _select_check(d.q_idx, d.w_idx, kv, d.T, 2048, [d.T])
+
+
+@pytest.mark.parametrize("paged,bs", [(False, 0), (True, 64), (True, 16)])
+def test_index_select_batched_rows(paged, bs):
+    """Rows longer and shorter than k, an empty row, a ragged tail, block-table holes."""
+    B, t_max, k = 5, 9000, 777
+    seq_len = [9000, 8191, 700, 0, 777]
+    log(f"index+select batched paged={paged} bs={bs}")
+    q, w, kv, logical, masks = _index_case(B, seq_len, t_max, 32, 128, paged, 270 + bs, bs=bs or 64, hole=paged)
+    _select_check(q, w, kv, t_max, k, seq_len)
+
+
+def test_index_select_generic_indexer_shape():
+    B, t_max, k = 2, 5000, 300
+    seq_len = [5000, 4321]
+    log("index+select n_ih=5 hd=64")
+    q, w, kv, logical, masks = _index_case(B, seq_len, t_max, 5, 64, False, 280)
+    _select_check(q, w, kv, t_max, k, seq_len)
+
+
+def test_index_select_ties_and_all_equal():
+    """Duplicated key rows tie exactly (lower position wins); all-zero keys tie everywhere
+    (the candidate list overflows the LDS-resident path)."""
+    rng = np.random.default_rng(290)
+    T, k = 20000, 2048
+    base = rng.standard_normal((T // 8, 128)).astype(np.float32)
+    ic = np.repeat(base, 8, axis=0)
+    q = rng.standard_normal((1, 32, 128)).astype(np.float32)
+    w = rng.standard_normal((1, 32)).astype(np.float32)
+    z = np.zeros((T, 8), np.uint16)
+    log("index+select ties")
+    kv = _kv(z, z, ic, [T], T, seq_stride=T)
+    _select_check(q, w, kv, T, k, [T])
+    kv0 = _kv(z, z, np.zeros_like(ic), [T], T, seq_stride=T)
+    sel, nsel = _select_check(q, w, kv0, T, k, [T])
+    assert np.array_equal(sel[0], np.arange(k))
+
+
+def test_index_select_long_row_general_path():
+    T, k = 300000, 2048
+    rng = np.random.default_rng(291)
+    ic = rng.standard_normal((T, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 32, 128)).astype(np.float32)
+    w = rng.standard_normal((1, 32)).astype(np.float32)
+    z = np.zeros((T, 8), np.uint16)
+    log("index+select T=300000 (general top-k)")
+    kv = _kv(z, z, ic, [T - 5], T, seq_stride=T)
+    _select_check(q, w, kv, T, k, [T - 5])
+
+
 # ------------------------------------------------------------------------------ top-k
 def _topk_check(scores, n_valid, k):
     sel, nsel = mla.dsa_topk_select(dev(scores), dev(np.asarray(n_valid, np.int32)), k)
