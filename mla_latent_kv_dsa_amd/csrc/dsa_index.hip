@@ -176,6 +176,33 @@ __device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Score of key L in lane L from the accumulator: lanes L and L^32 hold complementary head
+// groups of the same two keys, so one v_permlane32_swap per register pair leaves every lane
+// with heads 8g..8g+3 of its key in lo[] and heads 8g+4..8g+7 in hi[]; the heads are then folded
+// in ascending order.  (Selecting acc[r] or acc[16 + r] by lane half would index the register
+// array per lane, which compiles to long chains of selects.)
+__device__ __forceinline__ float ix_fold(const v32f &acc, const float *__restrict__ w)
+{
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float lo[4], hi[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int r = 4 * g + r4;
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[16 + r]),
+                                                            false, false);
+            lo[r4] = __uint_as_float(p[0]);
+            hi[r4] = __uint_as_float(p[1]);
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) s = __builtin_fmaf(w[8 * g + r4], lo[r4] > 0.f ? lo[r4] : 0.f, s);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) s = __builtin_fmaf(w[8 * g + 4 + r4], hi[r4] > 0.f ? hi[r4] : 0.f, s);
+    }
+    return s;
+}
+
 // HIST: also count the top 11 order-key bits of every score with t < n (LDS histogram per
 // block, added into ghist[b] with atomics at the end) -- the first pass of the top-k selection.
 constexpr int IX_BINS = 2048;
@@ -217,7 +244,6 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
     if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
-    const bool lo_half = lane < 32;
 
     const float *qraw = q + (int64_t)b * 32 * 128;
     bool valid, valid_n = false;
@@ -243,25 +269,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
         ix_load_slice(KA, pn, 0);
         ix_slice(acc, KB, qrow, 3);
         ix_load_slice(KB, pn, 1);
-        // lanes L and L^32 hold complementary head groups of the same two keys: swap so that
-        // lane L holds all 32 heads of key L, then fold them in ascending head order
-        float y[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = __shfl_xor(lo_half ? acc[16 + r] : acc[r], 32, 64);
-        float s = 0.f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float a = lo_half ? acc[4 * g + r4] : y[4 * g + r4];
-                s = __builtin_fmaf(wb[8 * g + r4], a > 0.f ? a : 0.f, s);
-            }
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float a = lo_half ? y[4 * g + r4] : acc[16 + 4 * g + r4];
-                s = __builtin_fmaf(wb[8 * g + 4 + r4], a > 0.f ? a : 0.f, s);
-            }
-        }
+        const float s = ix_fold(acc, wb);
         const int64_t t = tile * 64 + lane;
         const float sc = valid ? s : -INFINITY;
         if (t < t_max) out[t] = sc;

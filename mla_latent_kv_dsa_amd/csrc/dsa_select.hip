@@ -113,7 +113,7 @@ mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, cons
 // Every workgroup finds the threshold bin tb from the row histogram, counts its keys above the
 // bin and appends its keys inside the bin to the row's candidate list.
 constexpr int SEL_MAXCH = SEL_TMAX / SEL_CH;   // workgroups per row (256)
-constexpr int SEL_CPT = 8;                     // candidates per thread held in registers
+constexpr int SEL_CPT = 16;                    // candidates per thread held in registers
 
 struct SelRow {           // per-row results of the filter (uint32 words)
     uint32_t tb, kth, remaining, pad;
@@ -135,25 +135,36 @@ __global__ __launch_bounds__(256) void sel_resolve(int64_t t_max, KvView kv, int
     const int tid = threadIdx.x, b = blockIdx.x;
     if (seq_len_of(kv, b) <= k) return;
     const SelRow rin = row_out[b];   // tb and the count above its bin, from the filter
-    const uint32_t tb = rin.tb, above_total = rin.kth;
     uint32_t E = cnt[b];
-    if (E > cap) E = (uint32_t)cap;
+    // issued before anything waits: the filter workgroups' counts above the bin, and the first
+    // 256 * SEL_CPT candidates (thread t holds t + 256 i), as unconditional loads clamped into
+    // the buffers and masked on use
+    const uint32_t above_blk = blkabove[(int64_t)b * SEL_MAXCH + (tid < nch ? tid : 0)];
     const uint2 *cb = cand + (int64_t)b * cap;
-    // candidates: up to 2048 in registers (thread t holds t + 256 i), beyond that from memory
     uint2 cr[SEL_CPT];
 #pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i) {   // unconditional loads (clamped into the list), masked on use
+    for (int i = 0; i < SEL_CPT; ++i) {
         const int64_t j = tid + 256 * i;
         cr[i] = cb[j < cap ? j : cap - 1];
     }
-    const bool in_reg = E <= 256u * SEL_CPT;
+    const uint32_t tb = rin.tb, above_total = rin.kth;
+    if (E > cap) E = (uint32_t)cap;
+    // every candidate once: those held in registers, then the rest from memory in batches of
+    // eight independent loads per thread
     auto for_each = [&](auto f) {
-        if (in_reg) {
 #pragma unroll
-            for (int i = 0; i < SEL_CPT; ++i)
-                if (tid + 256u * i < E) f(cr[i]);
-        } else {
-            for (uint32_t j = tid; j < E; j += 256) f(cb[j]);
+        for (int i = 0; i < SEL_CPT; ++i)
+            if (tid + 256u * i < E) f(cr[i]);
+        for (uint32_t base = 256u * SEL_CPT; base < E; base += 2048u) {
+            uint2 t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t j = base + tid + 256u * i;
+                t[i] = cb[j < E ? j : E - 1u];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (base + tid + 256u * i < E) f(t[i]);
         }
     };
     // radix select of the need-th largest key: digits of bits 20..10, then 9..0
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(256) void sel_resolve(int64_t t_max, KvView kv, int
     const uint32_t epf = block_excl_scan_dpp<NW>(ec, sh);
     uint32_t take = remaining > epf ? remaining - epf : 0u;
     if (take > ec) take = ec;
-    const uint32_t kept = tid < nch ? blkabove[(int64_t)b * SEL_MAXCH + tid] + gtc[tid] + take : 0u;
+    const uint32_t kept = tid < nch ? above_blk + gtc[tid] + take : 0u;
     const uint32_t opf = block_excl_scan_dpp<NW>(kept, sh);
     if (tid < nch) {
         outpfx[(int64_t)b * SEL_MAXCH + tid] = opf;
@@ -341,7 +352,6 @@ __global__ __launch_bounds__(256) void sel_emit(const float *__restrict__ scores
                                                 const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
                                                 int32_t *__restrict__ nsel)
 {
-    constexpr int NW = 4;
     __shared__ uint32_t s_eq[SEL_CH / 64], s_kp[SEL_CH / 64];   // per (step, wave), position order
     const int b = blockIdx.y, c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
