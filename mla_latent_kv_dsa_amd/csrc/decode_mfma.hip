@@ -3,24 +3,17 @@
 // sec. 2.3, absorbed path: fold W_UK into the query, score against Lc/Rc directly, weight the
 // latent rows by the softmax, apply W_UV per head.
 //
-// Four launches, asynchronous on the caller's stream, each spread over the whole chip even
+// Three launches, asynchronous on the caller's stream, each spread over the whole chip even
 // at batch 1:
-//   absorb_q         q_abs[b][h][:] = W_UK[h]^T q_nope[b][h]       (fp32 FMA, bf16 out); also
-//                    resets the per-head running maxima used below
-//   dec_scores       S[b][h][j] = scale * log2(e) * (q_abs . Lc[t_j] + q_rope . Rc[t_j]) for
-//                    16-key tiles x all 64 heads on v_mfma_f32_16x16x32_bf16; the per-head
-//                    maximum over all keys is kept with an integer atomicMax on an
-//                    order-preserving encoding (max is order independent, so the result is
-//                    deterministic)
-//   dec_pv           P = exp2(S - max) (bf16) and O_part[b][split][h][c] = sum_j P V[j][c] for
-//                    (64-column chunk, key split) blocks on v_mfma_f32_32x32x16_bf16; V is
-//                    staged row-major in LDS and read transposed with ds_read_b64_tr_b16;
-//                    l_part = sum_j P
-//   combine_unabsorb clat = sum_split O_part / sum_split l_part (bf16), then
+//   absorb_q         q_abs[b][h][:] = W_UK[h]^T q_nope[b][h]       (fp32 FMA, bf16 out)
+//   dec_core         per (key split, group of 16 heads): scores S = q_abs . Lc + q_rope . Rc on
+//                    v_mfma_f32_16x16x32_bf16, an online softmax over the split's keys in 64-key
+//                    chunks, and O = sum_j P_j Lc[t_j] on the same instruction; the split's O,
+//                    running maximum and sum are written as partials
+//   combine_unabsorb clat = sum_s f_s O_s / sum_s f_s l_s with f_s = exp2(m_s - max m), then
 //                    out[b][h][:] = W_UV[h] clat on v_mfma_f32_16x16x32_bf16
-// The softmax needs no rescaling between splits because every split subtracts the same
-// global maximum, so the split partials are plain sums.
-//
+// Each split keeps its own maximum, so the splits need no common pass before the values.
+
 // MFMA operand layouts used (gfx950, checked on the device):
 //   32x32x16: lane l supplies A[l%32][8*(l/32)+e] and B[8*(l/32)+e][l%32], e = 0..7;
 //             result register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
@@ -42,14 +35,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int DM_H = 64, DM_L = 512, DM_R = 64;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Integer encoding of a float whose signed-integer order is the float order (for atomicMax).
-__device__ __forceinline__ int f2ord(float f)
-{
-    const int i = __float_as_int(f);
-    return i >= 0 ? i : i ^ 0x7fffffff;
-}
-__device__ __forceinline__ float ord2f(int i) { return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff); }
 
 // Keys attended by sequence b: the selected ones, or every cached token.
 __device__ __forceinline__ int64_t dec_nkeys(const KvView &kv, int b, const int32_t *sel, const int32_t *nsel,
@@ -83,7 +68,7 @@ constexpr int AB_QB = 8;
 
 template <int NR>   // qk_nope / 16
 __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nope, const bf16_t *__restrict__ kv_b,
-                                                int B, int v, bf16_t *__restrict__ q_abs, int *__restrict__ m2)
+                                                int B, int v, bf16_t *__restrict__ q_abs)
 {
     constexpr int nope = 16 * NR;
     extern __shared__ float sh_abs[];   // q [B][nope] fp32, then partials [4][AB_QB][128]
@@ -93,8 +78,6 @@ __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nop
     uint4 w[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) w[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)k * 16 * DM_L);
-    if (blockIdx.x == 0)
-        for (int b = tid; b < B; b += 256) m2[(int64_t)b * DM_H + h] = f2ord(-INFINITY);
     float *sq = sh_abs;
     float *red = sh_abs + B * nope;
     for (int i = tid; i < B * nope; i += 256) {
@@ -159,76 +142,25 @@ __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nop
     }
 }
 
-// ------------------------------------------------------------------------------ scores
-// grid (ceil(max_keys / 16), B), 256 threads; wave w scores heads 16w..16w+15 against the
-// block's 16 keys over the 576 dims (16 MFMA steps over Lc, 2 over Rc).  Operands come straight
-// from memory: lane l reads 16 B of key l%16 and of head 16w + l%16 at dims 32ks + 8(l/16).
-// Keys without a cache row read the query row instead and score -inf.
-__global__ __launch_bounds__(256) void dec_scores(const bf16_t *__restrict__ q_abs, const bf16_t *__restrict__ q_rope,
-                                                  KvView kv, const int32_t *__restrict__ sel,
-                                                  const int32_t *__restrict__ nsel, int sel_stride, float scale_log2,
-                                                  int nkp, float *__restrict__ S2, int *__restrict__ m2,
-                                                  int64_t *__restrict__ rows)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.y, jj = lane & 15, quad = lane >> 4;
-    const int64_t j0 = (int64_t)blockIdx.x * 16;
-    const int h = 16 * wave + jj;
-    const bf16_t *qa = q_abs + ((int64_t)b * DM_H + h) * DM_L + 8 * quad;
-    const bf16_t *qr = q_rope + ((int64_t)b * DM_H + h) * DM_R + 8 * quad;
-    // query operands first: they depend on nothing, so they are in flight during the key lookups
-    uint4 A[18], Bq[18];
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) Bq[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Bq[16 + ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
-    // the selection entry is read before the key count is known (clamped into the row of sel)
-    const int64_t jq = j0 + jj;
-    int64_t t = jq;
-    if (sel) t = sel[(int64_t)b * sel_stride + (jq < sel_stride ? jq : sel_stride - 1)];
-    const int64_t sl = seq_len_of(kv, b);
-    const int64_t nk = dec_nkeys(kv, b, sel, nsel, sel_stride);
-    if (j0 >= nk) return;
-    const int64_t row = (jq < nk && t >= 0 && t < sl) ? kv_row(kv, b, t) : -1;
-    const bool valid = row >= 0;
-    const uint64_t vmask = __ballot(valid);   // bit k (k < 16): key j0 + k has a row
-    if (tid < 16) rows[(int64_t)b * nkp + j0 + jj] = row;   // for the P V step
-    const bf16_t *ka = valid ? reinterpret_cast<const bf16_t *>(kv.lc) + row * DM_L + 8 * quad : qa;
-    const bf16_t *kr = valid ? reinterpret_cast<const bf16_t *>(kv.rc) + row * DM_R + 8 * quad : qr;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) A[ks] = *reinterpret_cast<const uint4 *>(ka + 32 * ks);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) A[16 + ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
-    __builtin_amdgcn_sched_barrier(0);   // every operand load in flight before the first MFMA
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[ks]), as_bf16x8(Bq[ks]), d, 0, 0, 0);
-    // register r holds key 4*quad + r of head h
-    float s[4], mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        s[r] = ((vmask >> (4 * quad + r)) & 1) ? d[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[r]);
-    }
-    *reinterpret_cast<float4 *>(S2 + ((int64_t)b * DM_H + h) * nkp + j0 + 4 * quad) = make_float4(s[0], s[1], s[2], s[3]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (quad == 0 && mx > -INFINITY) atomicMax(&m2[(int64_t)b * DM_H + h], f2ord(mx));
-}
-
-// ------------------------------------------------------------------------------ P V
-// grid (DM_L / 64, NS, B), 256 threads; wave w: heads 32(w&1) .. +32, columns
-// 64 bx + 32 (w>>1) .. +32.  Keys of split s: [s*kps, min((s+1)*kps, nk)), in chunks of four
-// 32-key tiles.  The chunk's cache rows (resolved by dec_scores) and scores are requested
-// before the key count is known (it only masks).  P = exp2(S - max) is computed once per
-// block (thread t: head t/4, keys 8(t%4) .. +8 of each tile) and staged in LDS with the
-// latent tile; then each wave runs
-//   A = P[32 heads][16 keys] (one 16-byte LDS read per lane)
-//   B = V[16 keys][32 columns] (two transposed LDS reads)
-constexpr int PV_KT = 32, PV_CH = 4;
-constexpr int PV_VROW = 80;   // bf16 per staged V row: 64 columns + pad (160 B: the 4 rows of a
-                              // transposed read fall in distinct banks)
-constexpr int PV_PROW = 40;   // bf16 per staged P row: 32 keys + pad (80 B: conflict-free reads)
+// ------------------------------------------------------------------------------ attention core
+// grid (NS, DM_H / 16, B), 256 threads: split s of sequence b (keys [s*kps, min((s+1)*kps, nk)))
+// against heads 16g .. 16g+15.  Up to 128 keys at a time are staged in LDS: every wave copies
+// the latent rows of 16 of them straight from memory (one 1 KB row per global_load_lds_dwordx4,
+// rows padded to 1072 B so that both the row reads of the score product and the transposed
+// reads of the value product fall in distinct banks); the query operands (B of the score
+// product) and the rope rows (A, read straight into registers) are requested before that.
+// Per 64-key chunk:
+//   S[key][head] = q_abs . Lc + q_rope . Rc   wave w: keys 16w..16w+15, v_mfma_f32_16x16x32_bf16
+//   chunk max per head across the waves (LDS); m_new = max(m_run, chunk max);
+//   P = exp2(S * scale_log2 - m_new) rounded to bf16, staged in LDS as [head][key];
+//   O = O * exp2(m_run - m_new) + P Lc        wave w: columns 128w .. 128w+127, transposed reads
+// The split's O, running maximum m (log2 units) and sum l (of the rounded P) go to the partials;
+// the combine step rescales the splits to their common maximum.
+constexpr int DC_KC = 64;                        // keys per chunk (four waves x 16)
+constexpr int DC_SUP = 2;                        // chunks staged at a time
+constexpr int DC_ROWB = 1072;                    // bytes per staged latent row
+constexpr int DC_PROW = 72;                      // bf16 per P row (64 keys + pad: 144 B)
+constexpr size_t DC_LDS = (size_t)DC_SUP * DC_KC * DC_ROWB + 16 * DC_PROW * 2 + (64 + 64 + 16) * 4;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -239,130 +171,209 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b, float &sum)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(256) void dec_pv(const float *__restrict__ S2, const int *__restrict__ m2, KvView kv,
-                                              const int64_t *__restrict__ rows, const int32_t *__restrict__ sel,
-                                              const int32_t *__restrict__ nsel, int sel_stride, int nkp, int kps,
-                                              float *__restrict__ o_part, float *__restrict__ l_part)
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
-    __shared__ __attribute__((aligned(16))) bf16_t sV[PV_CH][PV_KT * PV_VROW];
-    __shared__ __attribute__((aligned(16))) bf16_t sP[PV_CH][DM_H * PV_PROW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hb = wave & 1, cb = wave >> 1;
-    const int cc = blockIdx.x, s = blockIdx.y, b = blockIdx.z, NS = gridDim.y;
-    const int64_t k0 = (int64_t)s * kps;
-    // keys of the split as far as the buffers go; the true bound only masks
-    const int64_t ks1 = k0 + kps < nkp ? k0 + kps : nkp;
-    const int ph = tid >> 2, pk = tid & 3;     // P role
-    const float *srow = S2 + ((int64_t)b * DM_H + ph) * nkp + 8 * pk;
-    const int64_t *rrow = rows + (int64_t)b * nkp;
-    const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc) + 64 * cc;
-    const int lk = tid >> 3, lch = tid & 7;    // V loader role: key lk, 16-byte chunk lch
-    const int G = lane >> 4, i16 = lane & 15;  // transposed-read address inside a 16-key step
-    const int tr_off = (8 * (G >> 1) + (i16 >> 2)) * PV_VROW + 32 * cb + 16 * (G & 1) + 4 * (i16 & 3);
-    const int pa_off = (32 * hb + (lane & 31)) * PV_PROW + 8 * (lane >> 5);
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 
-    int64_t rw[PV_CH];
-    float4 sp[PV_CH][2];
-    auto prefetch = [&](int64_t c0) {
+// One 64-lane global_load_lds_dwordx4 (16 B per lane from g, lane i's to LDS byte lds + 16 i;
+// lds must be wave-uniform), issued from inline assembly: the compiler's wait-count pass would
+// otherwise treat every later LDS access as dependent on it and wait for all outstanding memory
+// traffic.  Completion is awaited explicitly (s_waitcnt vmcnt) before the staged data is read.
+// M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(g), "s"(lds)
+                 : "memory");
+}
+
+__global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs, const bf16_t *__restrict__ q_rope,
+                                                KvView kv, const int32_t *__restrict__ sel,
+                                                const int32_t *__restrict__ nsel, int sel_stride, float scale_log2,
+                                                int kps, float *__restrict__ o_part, float *__restrict__ m_part,
+                                                float *__restrict__ l_part)
+{
+    extern __shared__ __attribute__((aligned(16))) char dc_smem[];
+    char *sL = dc_smem;
+    bf16_t *sP = reinterpret_cast<bf16_t *>(dc_smem + DC_SUP * DC_KC * DC_ROWB);
+    float *sMx = reinterpret_cast<float *>(sP + 16 * DC_PROW);   // [wave][head] chunk maxima
+    float *sSum = sMx + 64;                                      // [wave][head] sums of P
+    float *sAl = sSum + 64;                                      // [head] rescale factor
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = blockIdx.x, NS = gridDim.x, h0 = 16 * blockIdx.y, b = blockIdx.z;
+    const int jj = lane & 15, quad = lane >> 4;
+    const int h = h0 + jj;
+    const bf16_t *qa = q_abs + ((int64_t)b * DM_H + h) * DM_L + 8 * quad;
+    const bf16_t *qr = q_rope + ((int64_t)b * DM_H + h) * DM_R + 8 * quad;
+    const bf16_t *dummy = q_abs + ((int64_t)b * DM_H + h0) * DM_L + 8 * lane;   // any readable 1 KB
+    uint4 Bq[18];
 #pragma unroll
-        for (int m = 0; m < PV_CH; ++m) {
-            const int64_t j = c0 + PV_KT * m + lk;
-            rw[m] = j < ks1 ? rrow[j] : -1;
+    for (int ks = 0; ks < 16; ++ks) Bq[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                sp[m][u] = c0 + PV_KT * m < ks1 ? *reinterpret_cast<const float4 *>(srow + c0 + PV_KT * m + 4 * u)
-                                                : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    if (k0 < ks1) prefetch(k0);
+    for (int ks = 0; ks < 2; ++ks) Bq[16 + ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
+    const int64_t sl = seq_len_of(kv, b);
     const int64_t nk = dec_nkeys(kv, b, sel, nsel, sel_stride);
+    const int64_t k0 = (int64_t)s * kps;
     const int64_t k1 = k0 + kps < nk ? k0 + kps : nk;
-    const float mh = ord2f(m2[(int64_t)b * DM_H + ph]);
-    const bool live = mh > -INFINITY;
+    const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc);
+    const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
 
-    f32x16 acc;
+    float m_run = -INFINITY, l_run = 0.f;   // head h (the same in every lane with this jj)
+    f32x4 acc[8];                            // column tile ct: heads 4 quad + r, column 128 wave + 16 ct + jj
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    float psum = 0.f;
-    for (int64_t c0 = k0; c0 < k1; c0 += PV_KT * PV_CH) {
-        uint4 vv[PV_CH];
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t c0 = k0; c0 < k1; c0 += DC_SUP * DC_KC) {
+        // cache rows: lane jj of wave w resolves key c0 + 64 u + 16 w + jj (the selection entry
+        // is read unconditionally, clamped into its row)
+        int64_t row[DC_SUP];
+        uint4 Arc[DC_SUP][2];
 #pragma unroll
-        for (int m = 0; m < PV_CH; ++m)
-            vv[m] = (rw[m] >= 0 && c0 + PV_KT * m + lk < k1)
-                        ? *reinterpret_cast<const uint4 *>(lc + rw[m] * DM_L + 8 * lch)
-                        : make_uint4(0u, 0u, 0u, 0u);
-        // P of this thread's 8 keys in each tile
-        uint4 pv[PV_CH];
+        for (int u = 0; u < DC_SUP; ++u) {
+            const int64_t j = c0 + 64 * u + 16 * wave + jj;
+            int64_t t = j;
+            if (sel) t = sel[(int64_t)b * sel_stride + (j < sel_stride ? j : sel_stride - 1)];
+            row[u] = (j < k1 && t >= 0 && t < sl) ? kv_row(kv, b, t) : -1;
+            const bf16_t *kr = row[u] >= 0 ? rc + row[u] * DM_R + 8 * quad : qr;
 #pragma unroll
-        for (int m = 0; m < PV_CH; ++m) {
-            const int64_t kb = c0 + PV_KT * m + 8 * pk;
-            const float sv[8] = {sp[m][0].x, sp[m][0].y, sp[m][0].z, sp[m][0].w,
-                                 sp[m][1].x, sp[m][1].y, sp[m][1].z, sp[m][1].w};
-            float p[8];
-            if (live && kb + 8 <= k1) {
+            for (int ks = 0; ks < 2; ++ks) Arc[u][ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+        }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - mh);
-            } else {
+        for (int u = 0; u < DC_SUP; ++u) {
+            if (c0 + 64 * u >= k1) break;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = (live && kb + e < k1) ? __builtin_amdgcn_exp2f(sv[e] - mh) : 0.f;
+            for (int i = 0; i < 16; ++i) {
+                const int64_t r = ((int64_t)__builtin_amdgcn_readlane((int)(row[u] >> 32), i) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readlane((int)row[u], i);
+                const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * lane : dummy;
+                lds_dma16(src, lds_addr(sL + (64 * u + 16 * wave + i) * DC_ROWB));
             }
-            pv[m].x = pack_bf16(p[0], p[1], psum);
-            pv[m].y = pack_bf16(p[2], p[3], psum);
-            pv[m].z = pack_bf16(p[4], p[5], psum);
-            pv[m].w = pack_bf16(p[6], p[7], psum);
         }
-        if (c0 + PV_KT * PV_CH < k1) prefetch(c0 + PV_KT * PV_CH);
-        __syncthreads();   // the previous chunk's tiles are no longer read
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int m = 0; m < PV_CH; ++m) {
-            *reinterpret_cast<uint4 *>(&sV[m][lk * PV_VROW + 8 * lch]) = vv[m];
-            *reinterpret_cast<uint4 *>(&sP[m][ph * PV_PROW + 8 * pk]) = pv[m];
-        }
-        __syncthreads();
+        for (int u = 0; u < DC_SUP; ++u) {
+            if (c0 + 64 * u >= k1) break;
+            // scores: register r is key 16 wave + 4 quad + r of the chunk, head h
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            const char *ka = sL + (64 * u + 16 * wave + jj) * DC_ROWB + 16 * quad;
 #pragma unroll
-        for (int m = 0; m < PV_CH; ++m) {
-            if (c0 + PV_KT * m >= k1) break;
+            for (int ks = 0; ks < 16; ++ks)
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const uint4 *>(ka + 64 * ks)),
+                                                            as_bf16x8(Bq[ks]), d, 0, 0, 0);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Arc[u][ks]), as_bf16x8(Bq[16 + ks]), d, 0, 0, 0);
+            const uint64_t vmask = __ballot(row[u] >= 0);   // bit k < 16: key 16 wave + k has a row
+            float sv[4], mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sv[r] = ((vmask >> (4 * quad + r)) & 1) ? d[r] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sv[r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (quad == 0) sMx[16 * wave + jj] = mx;
+            __syncthreads();
+            const float cm = fmaxf(fmaxf(sMx[jj], sMx[16 + jj]), fmaxf(sMx[32 + jj], sMx[48 + jj]));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            float p[4], psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_new);
+            uint2 pw;
+            pw.x = pack_bf16(p[0], p[1], psum);
+            pw.y = pack_bf16(p[2], p[3], psum);
+            *reinterpret_cast<uint2 *>(&sP[jj * DC_PROW + 16 * wave + 4 * quad]) = pw;
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            if (quad == 0) sSum[16 * wave + jj] = psum;
+            if (wave == 0 && quad == 0) sAl[jj] = alpha;
+            __syncthreads();
+            l_run = l_run * alpha + ((sSum[jj] + sSum[16 + jj]) + sSum[32 + jj]) + sSum[48 + jj];
+            m_run = m_new;
+            // values: rescale, then two 32-key steps over eight column tiles
+            float al[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) al[r] = sAl[4 * quad + r];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[ct][r] *= al[r];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const uint4 pa = *reinterpret_cast<const uint4 *>(&sP[m][pa_off + 16 * kk]);
-                const bf16_t *vb = &sV[m][16 * kk * PV_VROW + tr_off];
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)vb);
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s *)(vb + 4 * PV_VROW));
-                const v8s vt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa), __builtin_bit_cast(bf16x8, vt), acc, 0,
-                                                              0, 0);
+                const uint4 pa = *reinterpret_cast<const uint4 *>(&sP[jj * DC_PROW + 32 * kk + 8 * quad]);
+                const char *vb = sL + (64 * u + 32 * kk + 8 * quad + (jj >> 2)) * DC_ROWB + 2 * (128 * wave + 4 * (jj & 3));
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(vb + 32 * ct));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(vb + 4 * DC_ROWB + 32 * ct));
+                    const v8s vt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), __builtin_bit_cast(bf16x8, vt),
+                                                                      acc[ct], 0, 0, 0);
+                }
             }
         }
+        __syncthreads();   // the staged rows are no longer read
     }
-    // register r: head 32hb + 8(r/4) + 4(l/32) + r%4, column 64cc + 32cb + l%32
-    float *po = o_part + ((int64_t)b * NS + s) * DM_H * DM_L + 64 * cc + 32 * cb + (lane & 31);
+    float *po = o_part + (((int64_t)b * NS + s) * DM_H + h0 + 4 * quad) * DM_L + 128 * wave + jj;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int hr = 32 * hb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        po[(int64_t)hr * DM_L] = acc[r];
-    }
-    if (cc == 0) {
-        psum += __shfl_xor(psum, 1, 64);
-        psum += __shfl_xor(psum, 2, 64);
-        if (pk == 0) l_part[((int64_t)b * NS + s) * DM_H + ph] = psum;
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = acc[ct][r];
+    if (wave == 0 && quad == 0) {
+        m_part[((int64_t)b * NS + s) * DM_H + h] = m_run;
+        l_part[((int64_t)b * NS + s) * DM_H + h] = l_run;
     }
 }
 
 // ------------------------------------------------------------------------------ combine + W_UV
-// grid (v / 64, H, ceil(B / 16)), 256 threads.  Wave w owns rows 64 bx + 16 w .. +16 of W_UV[h].
-// They are requested first, one whole 1 KB row per instruction straight into LDS
-// (global_load_lds_dwordx4; rows padded to 1040 B so the later operand reads are
-// conflict-free).  The softmax denominators of the block's queries and the first batch of
-// split partials follow; the latent rows (sum of the partials over the splits, in split
-// order, divided by the denominator) are staged in LDS as bf16, then the 512 latent columns
-// are contracted in 16 MFMA steps.
+// Maximum and sum over the 64 lanes of a wave with DPP moves (row shifts inside rows of 16 lanes,
+// then row broadcasts), read back from the last lane: no LDS traffic.
+__device__ __forceinline__ float wave_max_dpp(float x)
+{
+    const int ninf = __float_as_int(-INFINITY);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x111, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x112, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x114, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x118, 0xf, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x142, 0xa, 0xf, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// grid (v / 64, H, ceil(B / 16)), 256 threads; QB queries and SB splits per batch of partials
+// (QB = 1, SB >= NS when the launch holds one query: a single batch).  Wave w owns rows
+// 64 bx + 16 w .. +16 of W_UV[h]; they are requested first, one whole 1 KB row per DMA straight
+// into LDS (rows padded to 1040 B so the operand reads are conflict-free), then the first batch
+// of split partials and the splits' maxima and sums.  Wave w reduces queries w, w+4, .. over
+// the splits (one split per lane) into the factors
+//   f_s = exp2(m_s - max_s m_s) / sum_s exp2(m_s - max_s m_s) l_s,
+// the latent rows clat = sum_s f_s O_s (in split order) are staged in LDS as bf16, and the 512
+// latent columns are contracted in 16 MFMA steps.
 constexpr int CU_ROW = DM_L + 8;
 constexpr int CU_WROW = DM_L + 8;          // bf16 per staged W_UV row (1040 B)
-constexpr int CU_QB = 4, CU_SB = 16;
-constexpr size_t CU_LDS = (size_t)(64 * CU_WROW + 16 * CU_ROW) * 2 + 16 * 4;
+constexpr int CU_MAXNS = 64;
+constexpr size_t CU_LDS = (size_t)(64 * CU_WROW + 16 * CU_ROW) * 2 + (size_t)16 * CU_MAXNS * 4;
 
+template <int QB, int SB>
 __global__ __launch_bounds__(256) void combine_unabsorb(const float *__restrict__ o_part,
+                                                        const float *__restrict__ m_part,
                                                         const float *__restrict__ l_part, int NS,
                                                         const bf16_t *__restrict__ kv_b, int B, int nope, int v,
                                                         float *__restrict__ out)
@@ -370,67 +381,82 @@ __global__ __launch_bounds__(256) void combine_unabsorb(const float *__restrict_
     extern __shared__ __attribute__((aligned(16))) char cu_smem[];
     bf16_t *sW = reinterpret_cast<bf16_t *>(cu_smem);
     bf16_t *sC = sW + 64 * CU_WROW;
-    float *sInv = reinterpret_cast<float *>(sC + 16 * CU_ROW);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float *sF = reinterpret_cast<float *>(sC + 16 * CU_ROW);   // [query][split] factors
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = blockIdx.y, j0 = 64 * blockIdx.x + 16 * wave, b0 = 16 * blockIdx.z;
     const int nb = B - b0 < 16 ? B - b0 : 16;
     const int r16 = lane & 15, q4 = lane >> 4;
     {
         const bf16_t *wsrc = kv_b + ((int64_t)h * (nope + v) + nope + j0) * DM_L + 8 * lane;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(wsrc + (int64_t)i * DM_L),
-                                             (__attribute__((address_space(3))) void *)(sW + (16 * wave + i) * CU_WROW),
-                                             16, 0, 0);
+        for (int i = 0; i < 16; ++i) lds_dma16(wsrc + (int64_t)i * DM_L, lds_addr(sW + (16 * wave + i) * CU_WROW));
     }
 
-    float2 x[CU_QB][CU_SB];
+    float2 x[QB][SB];
     // unconditional loads (query and split clamped into range), zeroed after: conditional loads
     // would each wait for the previous ones
     auto load_batch = [&](int q0, int s0) {
 #pragma unroll
-        for (int qq = 0; qq < CU_QB; ++qq)
+        for (int qq = 0; qq < QB; ++qq)
 #pragma unroll
-            for (int u = 0; u < CU_SB; ++u) {
+            for (int u = 0; u < SB; ++u) {
                 const int qc = q0 + qq < nb ? q0 + qq : nb - 1;
                 const int sc = s0 + u < NS ? s0 + u : NS - 1;
-                const float2 v = *reinterpret_cast<const float2 *>(
+                const float2 val = *reinterpret_cast<const float2 *>(
                     o_part + (((int64_t)(b0 + qc) * NS + sc) * DM_H + h) * DM_L + 2 * tid);
-                x[qq][u] = (q0 + qq < nb && s0 + u < NS) ? v : make_float2(0.f, 0.f);
+                x[qq][u] = (q0 + qq < nb && s0 + u < NS) ? val : make_float2(0.f, 0.f);
             }
     };
     load_batch(0, 0);
-    if (tid < nb) {
-        float l = 0.f;
+    // maxima and sums: wave w, lane = split, queries w + 4k
+    float mv[4], lv[4];
 #pragma unroll
-        for (int s = 0; s < 64; ++s)
-            if (s < NS) l += l_part[((int64_t)(b0 + tid) * NS + s) * DM_H + h];
-        sInv[tid] = l > 0.f ? 1.f / l : 0.f;
+    for (int k = 0; k < 4; ++k) {
+        const int q = wave + 4 * k;
+        const int qc = q < nb ? q : nb - 1, sc = lane < NS ? lane : NS - 1;
+        const int64_t o = ((int64_t)(b0 + qc) * NS + sc) * DM_H + h;
+        mv[k] = m_part[o];
+        lv[k] = l_part[o];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int q = wave + 4 * k;
+        if (q < nb) {
+            const float m = lane < NS ? mv[k] : -INFINITY;
+            const float M = wave_max_dpp(m);
+            const float e = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            const float L = wave_sum_dpp(e * (lane < NS ? lv[k] : 0.f));
+            sF[q * CU_MAXNS + lane] = L > 0.f ? e / L : 0.f;
+        }
     }
     __syncthreads();
-    for (int q0 = 0; q0 < nb; q0 += CU_QB) {
-        float o[CU_QB][2];
+    for (int q0 = 0; q0 < nb; q0 += QB) {
+        float o[QB][2];
 #pragma unroll
-        for (int qq = 0; qq < CU_QB; ++qq) o[qq][0] = o[qq][1] = 0.f;
-        for (int s0 = 0; s0 < NS; s0 += CU_SB) {
+        for (int qq = 0; qq < QB; ++qq) o[qq][0] = o[qq][1] = 0.f;
+        for (int s0 = 0; s0 < NS; s0 += SB) {
             if (q0 + s0 > 0) load_batch(q0, s0);
 #pragma unroll
-            for (int qq = 0; qq < CU_QB; ++qq)
+            for (int qq = 0; qq < QB; ++qq) {
+                const int qc = q0 + qq < nb ? q0 + qq : 0;
 #pragma unroll
-                for (int u = 0; u < CU_SB; ++u) {
-                    o[qq][0] += x[qq][u].x;
-                    o[qq][1] += x[qq][u].y;
+                for (int u = 0; u < SB; ++u) {
+                    // factors past the last split are zero; the index only stays inside the row
+                    const float f = sF[qc * CU_MAXNS + (s0 + u < CU_MAXNS ? s0 + u : CU_MAXNS - 1)];
+                    o[qq][0] = fmaf(f, x[qq][u].x, o[qq][0]);
+                    o[qq][1] = fmaf(f, x[qq][u].y, o[qq][1]);
                 }
+            }
         }
 #pragma unroll
-        for (int qq = 0; qq < CU_QB; ++qq) {
+        for (int qq = 0; qq < QB; ++qq) {
             if (q0 + qq < nb) {
-                const float inv = sInv[q0 + qq];
-                const bf16x2 c = {(__bf16)(o[qq][0] * inv), (__bf16)(o[qq][1] * inv)};
+                const bf16x2 c = {(__bf16)o[qq][0], (__bf16)o[qq][1]};
                 *reinterpret_cast<uint32_t *>(&sC[(q0 + qq) * CU_ROW + 2 * tid]) = __builtin_bit_cast(uint32_t, c);
             }
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the W_UV rows have landed
     __syncthreads();
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     const bf16_t *wl = sW + (16 * wave + r16) * CU_WROW + 8 * q4;
@@ -455,35 +481,42 @@ bool decode_mfma_supported(const mla_dims &d, mla_dtype dt)
 }
 
 struct DecPlan {
-    int ns;        // key splits of the P V step
-    int64_t kps;   // keys per split (multiple of 32)
-    int64_t nkp;   // row stride of the score buffer (multiple of 32)
+    int ns;        // key splits
+    int64_t kps;   // keys per split (multiple of 64)
 };
 
+// Splits: at most 256 keys per split, enough splits for ~256 blocks (4 head groups each), at
+// least 64 keys per split and at most CU_MAXNS splits.
 static DecPlan dec_plan(int32_t B, int64_t max_keys)
 {
     DecPlan p;
-    const int64_t by_keys = (max_keys + 127) / 128;                 // >= 128 keys per split
-    const int64_t by_fill = ((1024 / 8) + B - 1) / (int64_t)B;     // ~1024 (chunk, split, b) blocks
-    int64_t ns = by_keys < by_fill ? by_keys : by_fill;
-    if (ns > 64) ns = 64;
+    const int64_t by_len = (max_keys + 255) / 256;
+    const int64_t by_fill = (64 + B - 1) / (int64_t)B;
+    const int64_t most = (max_keys + DC_KC - 1) / DC_KC;
+    int64_t ns = by_len > by_fill ? by_len : by_fill;
+    if (ns > most) ns = most;
+    if (ns > CU_MAXNS) ns = CU_MAXNS;
     if (ns < 1) ns = 1;
     p.ns = (int)ns;
     int64_t kps = (max_keys + ns - 1) / ns;
-    p.kps = (kps + PV_KT - 1) / PV_KT * PV_KT;
-    if (p.kps < PV_KT) p.kps = PV_KT;
-    p.nkp = (max_keys + 31) / 32 * 32;
-    if (p.nkp < 32) p.nkp = 32;
+    p.kps = (kps + DC_KC - 1) / DC_KC * DC_KC;
+    if (p.kps < DC_KC) p.kps = DC_KC;
     return p;
 }
 
-// combine_unabsorb stages 64 rows of W_UV (65 KB) besides the latent rows
+// dec_core stages 128 latent rows (134 KB), combine_unabsorb 64 rows of W_UV (65 KB)
 static mla_status enable_big_lds()
 {
     static bool done = false;
     if (!done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&combine_unabsorb),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)CU_LDS);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
+        const void *cu[4] = {reinterpret_cast<const void *>(&combine_unabsorb<1, 16>),
+                             reinterpret_cast<const void *>(&combine_unabsorb<1, 32>),
+                             reinterpret_cast<const void *>(&combine_unabsorb<1, 64>),
+                             reinterpret_cast<const void *>(&combine_unabsorb<4, 16>)};
+        for (int i = 0; i < 4 && e == hipSuccess; ++i)
+            e = hipFuncSetAttribute(cu[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)CU_LDS);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
     }
@@ -497,24 +530,20 @@ size_t decode_mfma_ws(const mla_dims &d, int32_t B, int64_t max_keys)
     const DecPlan p = dec_plan(B, max_keys);
     size_t bytes = 256;
     bytes += al256((size_t)B * DM_H * DM_L * 2);                // q_abs
-    bytes += al256((size_t)B * DM_H * 4);                       // running maxima
-    bytes += al256((size_t)B * DM_H * p.nkp * 4);               // scores
-    bytes += al256((size_t)B * p.nkp * 8);                      // cache rows of the attended keys
-    bytes += al256((size_t)B * p.ns * DM_H * DM_L * 4);         // P V partials
-    bytes += al256((size_t)B * p.ns * DM_H * 4);                // softmax denominators
+    bytes += al256((size_t)B * p.ns * DM_H * 4);                // split maxima
+    bytes += al256((size_t)B * p.ns * DM_H * 4);                // split sums
+    bytes += al256((size_t)B * p.ns * DM_H * DM_L * 4);         // split outputs
     (void)d;
     return bytes;
 }
 
-// Workspace layout (the first two parts depend on B only, so the absorb step can run without
-// knowing the key count): q_abs | running maxima | scores | key rows | P V partials | denominators
+// Workspace layout (the first part depends on B only, so the absorb step can run without
+// knowing the key count): q_abs | split maxima | split sums | split outputs
 struct DecWs {
     bf16_t *q_abs;
-    int *m2;
-    float *S2;
-    int64_t *rows;
-    float *o_part;
+    float *m_part;
     float *l_part;
+    float *o_part;
 };
 
 static DecWs dec_ws(void *ws, int32_t B, const DecPlan &p)
@@ -523,19 +552,15 @@ static DecWs dec_ws(void *ws, int32_t B, const DecPlan &p)
     char *c = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
     w.q_abs = reinterpret_cast<bf16_t *>(c);
     c += al256((size_t)B * DM_H * DM_L * 2);
-    w.m2 = reinterpret_cast<int *>(c);
-    c += al256((size_t)B * DM_H * 4);
-    w.S2 = reinterpret_cast<float *>(c);
-    c += al256((size_t)B * DM_H * p.nkp * 4);
-    w.rows = reinterpret_cast<int64_t *>(c);
-    c += al256((size_t)B * p.nkp * 8);
-    w.o_part = reinterpret_cast<float *>(c);
-    c += al256((size_t)B * p.ns * DM_H * DM_L * 4);
+    w.m_part = reinterpret_cast<float *>(c);
+    c += al256((size_t)B * p.ns * DM_H * 4);
     w.l_part = reinterpret_cast<float *>(c);
+    c += al256((size_t)B * p.ns * DM_H * 4);
+    w.o_part = reinterpret_cast<float *>(c);
     return w;
 }
 
-size_t decode_mfma_absorb_ws(int32_t B) { return 256 + al256((size_t)B * DM_H * DM_L * 2) + al256((size_t)B * DM_H * 4); }
+size_t decode_mfma_absorb_ws(int32_t B) { return 256 + al256((size_t)B * DM_H * DM_L * 2); }
 
 mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_dims &d, int32_t B, void *ws,
                               hipStream_t s)
@@ -549,13 +574,12 @@ mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_di
         const dim3 g(DM_L / 128, DM_H), blk(256);
         const bf16_t *qn = (const bf16_t *)q_nope + (int64_t)b0 * DM_H * d.qk_nope;
         bf16_t *qa = w.q_abs + (int64_t)b0 * DM_H * DM_L;
-        int *mm = w.m2 + (int64_t)b0 * DM_H;
         if (d.qk_nope == 128)
-            hipLaunchKernelGGL(absorb_q<8>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa, mm);
+            hipLaunchKernelGGL(absorb_q<8>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa);
         else if (d.qk_nope == 192)
-            hipLaunchKernelGGL(absorb_q<12>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa, mm);
+            hipLaunchKernelGGL(absorb_q<12>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa);
         else
-            hipLaunchKernelGGL(absorb_q<16>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa, mm);
+            hipLaunchKernelGGL(absorb_q<16>, g, blk, shm, s, qn, (const bf16_t *)kv_b, nb, d.v_head, qa);
         mla_status st = check_launch("absorb_q");
         if (st) return st;
     }
@@ -567,25 +591,30 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
                               float sm_scale, float *out, void *ws, hipStream_t s)
 {
     if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: B > 65535");
+    if (max_keys > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: too many keys");
     const DecPlan p = dec_plan(B, max_keys);
-    if (p.nkp > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: too many keys");
     const DecWs w = dec_ws(ws, B, p);
-    const int64_t gk = (max_keys + 15) / 16;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    if (gk > 0) {
-        hipLaunchKernelGGL(dec_scores, dim3((unsigned)gk, B), dim3(256), 0, s, w.q_abs, (const bf16_t *)q_rope, kv,
-                           sel, nsel, sel_stride, scale_log2, (int)p.nkp, w.S2, w.m2, w.rows);
-        mla_status st = check_launch("dec_scores");
-        if (st) return st;
-    }
-    hipLaunchKernelGGL(dec_pv, dim3(DM_L / 64, p.ns, B), dim3(256), 0, s, w.S2, w.m2, kv, w.rows, sel, nsel,
-                       sel_stride, (int)p.nkp, (int)p.kps, w.o_part, w.l_part);
-    mla_status st = check_launch("dec_pv");
+    mla_status st = enable_big_lds();
     if (st) return st;
-    st = enable_big_lds();
+    hipLaunchKernelGGL(dec_core, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv,
+                       sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
+    st = check_launch("dec_core");
     if (st) return st;
-    hipLaunchKernelGGL(combine_unabsorb, dim3(d.v_head / 64, DM_H, (B + 15) / 16), dim3(256), CU_LDS, s, w.o_part,
-                       w.l_part, p.ns, (const bf16_t *)kv_b, B, d.qk_nope, d.v_head, out);
+    const dim3 gc(d.v_head / 64, DM_H, (B + 15) / 16);
+    const bf16_t *kb = (const bf16_t *)kv_b;
+    if (B == 1 && p.ns <= 16)
+        hipLaunchKernelGGL((combine_unabsorb<1, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                           kb, B, d.qk_nope, d.v_head, out);
+    else if (B == 1 && p.ns <= 32)
+        hipLaunchKernelGGL((combine_unabsorb<1, 32>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                           kb, B, d.qk_nope, d.v_head, out);
+    else if (B == 1)
+        hipLaunchKernelGGL((combine_unabsorb<1, 64>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                           kb, B, d.qk_nope, d.v_head, out);
+    else
+        hipLaunchKernelGGL((combine_unabsorb<4, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                           kb, B, d.qk_nope, d.v_head, out);
     return check_launch("combine_unabsorb");
 }
 
