@@ -98,6 +98,7 @@ def bench_dsa_decode(args):
                            sel=torch.empty((B, K), dtype=torch.int32, device=dev),
                            nsel=torch.empty((B,), dtype=torch.int32, device=dev),
                            out=torch.empty((B, H, V), dtype=torch.float32, device=dev)))
+    step_need = mla.mla_dsa_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, T, K)
     tk_need = mla.dsa_topk_workspace_bytes(B, T, K)
     sel_need = mla.dsa_index_select_workspace_bytes(B, T, K)
     dec_need = mla.mla_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, K)
@@ -105,6 +106,7 @@ def bench_dsa_decode(args):
         c["tk_ws"] = torch.empty(max(tk_need, 1), dtype=torch.uint8, device=dev)
         c["sel_ws"] = torch.empty(max(sel_need, 1), dtype=torch.uint8, device=dev)
         c["dec_ws"] = torch.empty(max(dec_need, 1), dtype=torch.uint8, device=dev)
+        c["step_ws"] = torch.empty(max(step_need, 1), dtype=torch.uint8, device=dev)
 
     def rope(c):
         mla.mla_rope_interleave(c["qr"], c["pos"], 0, ROPE)
@@ -127,10 +129,16 @@ def bench_dsa_decode(args):
                               out=c["out"])
 
     def step(c):
-        # one stream: a fork/join across two streams inside the captured graph cost more per
-        # step than running the query absorption beside the top-k saved
+        # the whole hot path in one call: RoPE of the query tail at T-1, indexer + top-k,
+        # absorbed attention over the selected keys (the query absorption and the rotation
+        # run beside the selection's final pass)
+        mla.mla_dsa_decode(c["qn"], c["qr"], c["qi"], c["wi"], c["kvb"], c["kv"], T, K, sm, scores=c["scores"],
+                           sel=c["sel"], nsel=c["nsel"], out=c["out"], ws=c["step_ws"])
+
+    def separate(c):
+        # the same step as four calls (RoPE in place, so only for the per-part timing)
         rope(c)
-        select(c)      # indexer scores + top-k in one call
+        select(c)
         absorb(c)
         attend(c)
 
@@ -156,35 +164,57 @@ def bench_dsa_decode(args):
             with torch.cuda.graph(gr):
                 step(c)
             graphs.append(gr)
+        # one graph with a step on every input copy, so that the per-replay launch cost is
+        # shared by len(copies) steps (as it is when a decode graph holds many layers)
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for c in copies:
+                step(c)
         torch.cuda.synchronize()
         copies[0]["qr"].copy_(qr0)
         graphs[0].replay()
         torch.cuda.synchronize()
         assert torch.equal(copies[0]["sel"], ref_sel), "graph replay selection differs from eager"
         assert torch.equal(copies[0]["out"], ref_out), "graph replay output differs from eager"
+        g_all.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(copies[0]["sel"], ref_sel), "graph replay selection differs from eager"
+        assert torch.equal(copies[0]["out"], ref_out), "graph replay output differs from eager"
 
-    def run(i):
-        if graphs:
-            graphs[i % len(graphs)].replay()
+    def run_steps(n, i0=0):
+        """Exactly n steps: whole replays of the all-copies graph, then single-step graphs."""
+        if not graphs:
+            for i in range(n):
+                step(copies[(i0 + i) % len(copies)])
+            return
+        full, rest = divmod(n, len(copies))
+        for _ in range(full):
+            g_all.replay()
+        for i in range(rest):
+            graphs[i].replay()
+
+    def time_steps(n, single):
+        e0, e1 = _events(torch, 2)
+        t = time.perf_counter()
+        e0.record()
+        if single:
+            for i in range(n):
+                graphs[i % len(graphs)].replay()
         else:
-            step(copies[i % len(copies)])
+            run_steps(n)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, time.perf_counter() - t
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
-    e0, e1 = _events(torch, 2)
-    t_wall = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        run(i)
-    e1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step, t_wall = time_steps(args.steps, False)
+    ms_step_single = time_steps(args.steps, True)[0] if graphs else None
 
     # per-kernel durations: each part alone, captured back to back over every input copy
     # (REPS passes) in one HIP graph, replayed between two events on the launch stream
-    parts = {"rope": rope, "select": select, "absorb": absorb, "attend": attend, "index": index, "topk": topk}
+    parts = {"rope": rope, "select": select, "absorb": absorb, "attend": attend, "index": index, "topk": topk,
+             "separate_calls": separate, "fused_step": step}
     us = {}
     REPS = 4
     for k, f in parts.items():
@@ -223,7 +253,7 @@ def bench_dsa_decode(args):
     kvb_bytes = H * (NOPE + V) * L * 2
     step_bytes = ic_bytes + sel_kv_bytes + kvb_bytes + score_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
     stream_bytes = ic_bytes + sel_kv_bytes
-    stream_us = us["select"] + us["attend"]
+    stream_us = ms_step * 1e3   # the fused step: indexer, selection and attention (RoPE and absorb hidden)
     src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", "dsa_index.hip")
     traffic = _traffic("dsa_index_scores_T131072", src, idx_bytes)
 
@@ -238,7 +268,7 @@ def bench_dsa_decode(args):
         "config": {"workload": "dsa_decode_T131072_B1", "T": T, "B": B, "heads": H, "qk_nope": NOPE,
                    "qk_rope": ROPE, "v_head": V, "kv_lora": L, "index_heads": N_IH, "index_hd": HD,
                    "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "input_copies": args.copies,
-                   "hip_graphs": bool(graphs)},
+                   "hip_graphs": bool(graphs), "steps_per_graph_replay": len(copies) if graphs else 0},
         "roofline": {"kernel": "index_scores_mfma (dsa_index_scores; the step runs the same kernel with the "
                                "selection histogram added, inside dsa_index_select)",
                      "bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS,
@@ -246,12 +276,13 @@ def bench_dsa_decode(args):
                      "algorithmic_bytes": idx_bytes, "avg_us": us["index"]},
         "cpu_baseline": cpu,
         "breakdown_us": us,
-        "stream": {"bytes": stream_bytes, "us_select_attend": stream_us,
+        "stream": {"bytes": stream_bytes, "us_step": stream_us,
                    "GBs": stream_bytes / (stream_us * 1e-6) / 1e9,
                    "frac": stream_bytes / (stream_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "whole_step": {"bytes": step_bytes, "GBs": step_bytes / (ms_step * 1e-3) / 1e9,
                        "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "wall_s_timed": t_wall,
+        "ms_per_step_one_graph_per_step": ms_step_single,
     }
     print(json.dumps(line), flush=True)
 

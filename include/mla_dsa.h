@@ -192,6 +192,34 @@ mla_status mla_decode_attend(const void *q_rope, mla_dtype q_dt, const void *kv_
 
 
 /* ---------------------------------------------------------------------------------
+ * The whole DSA decode step in one call, for one query per sequence at its position
+ * seq_len[b] - 1 ([MLA] sec. 2.1 RoPE, sec. 2.2 indexer and top-k, sec. 2.3 absorbed path):
+ *   1. q_rope' = RoPE(q_rope) at position seq_len[b] - 1 (as mla_rope_interleave, written
+ *      to the workspace: q_rope itself is not modified)
+ *   2. scores, sel, nsel = dsa_index_select(q_idx, w_idx, kv, t_max, k)
+ *   3. out = mla_absorbed_decode(q_nope, q_rope', sel, nsel) over the selected keys
+ * Rows with seq_len[b] <= k keep every key (sel = 0..seq_len-1), which is the dense decode.
+ * The results equal those of the separate calls bit for bit; the call only schedules
+ * them together (on the matrix-core decode path the query absorption and the rotation run
+ * beside the selection's final pass instead of as launches of their own).
+ *   q_nope, q_rope, q_dt, kv_b, w_dt, d, B, sm_scale   as for mla_absorbed_decode (q_rope
+ *                                                     before rotation), rope_theta as the
+ *                                                     theta of mla_rope_interleave
+ *   q_idx, w_idx, n_ih, kv, t_max, k, scores, sel, nsel as for dsa_index_select (kv must
+ *                                                     carry Lc, Rc, Ic and seq_len; sel is
+ *                                                     [B][k]); t_max >= every seq_len[b]
+ *   out   device fp32 [B][H][v_head]
+ *   ws    device workspace of at least mla_dsa_decode_workspace_bytes(d, B, t_max, k)
+ *         bytes (scratch; its content on entry does not matter)
+ * --------------------------------------------------------------------------------- */
+size_t mla_dsa_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t t_max, int32_t k);
+mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                          const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b,
+                          mla_dtype w_dt, const mla_dims *d, int32_t B, const mla_kv_view *kv,
+                          int64_t t_max, int32_t k, float sm_scale, float *scores, int32_t *sel,
+                          int32_t *nsel, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Non-absorbed causal prefill of S queries of one sequence.  [MLA] sec. 2.3
  * (non-absorbed path): one kv_b matmul rebuilds k_nope and v for every token,
  *   [k_nope | v](t, h) = kv_b[h*(qk_nope+v_head) .. +qk_nope+v_head) . Lc(t),

@@ -30,6 +30,7 @@ EXPORTED = (
     "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
     "dsa_index_select_workspace_bytes", "dsa_index_select",
     "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
+    "mla_dsa_decode_workspace_bytes", "mla_dsa_decode",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
@@ -92,6 +93,12 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_attend.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), i32,
                                     ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P, ctypes.c_size_t, P]
     L.mla_decode_attend.restype = st
+    L.mla_dsa_decode_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64, i32]
+    L.mla_dsa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_dsa_decode.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P, P, i32, P, ctypes.c_int,
+                                 ctypes.POINTER(mla_dims), i32, ctypes.POINTER(mla_kv_view), i64, i32, ctypes.c_float,
+                                 P, P, P, P, P, ctypes.c_size_t, P]
+    L.mla_dsa_decode.restype = st
     L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
     L.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.mla_prefill_nonabsorbed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims),
@@ -357,6 +364,55 @@ def mla_decode_attend(q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache, qk_
                                    ctypes.byref(kv.view), _ptr(sel), _ptr(nsel), sel_stride, float(sm_scale),
                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(q_rope.device)))
     return out
+
+
+def mla_dsa_decode_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, B: int, t_max: int, k: int) -> int:
+    return int(lib().mla_dsa_decode_workspace_bytes(ctypes.byref(_dims(H, nope, rope, v, L)), B, t_max, k))
+
+
+def mla_dsa_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
+                   kv_b: torch.Tensor, kv: KvCache, t_max: int, k: int, sm_scale: float, theta: float = 10000.0,
+                   scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                   nsel: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None):
+    """The whole decode step: RoPE of q_rope [B, H, rope] (before rotation; not modified) at
+    position seq_len - 1, indexer scores and top-k selection, absorbed attention over the
+    selected keys.  Returns (out [B, H, v] float32, scores [B, t_max], sel [B, k], nsel [B])."""
+    _dev(q_nope, q_rope, q_idx, w_idx, kv_b, scores, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, q_idx, w_idx, kv_b, scores, sel, nsel, out, ws)
+    B, H, nope = q_nope.shape
+    rope = q_rope.shape[2]
+    L = kv_b.shape[1]
+    if q_rope.shape[:2] != (B, H) or kv_b.shape[0] % H:
+        raise ValueError("shape mismatch between q_nope, q_rope and kv_b")
+    v = kv_b.shape[0] // H - nope
+    Bi, n_ih, hd = q_idx.shape
+    if Bi != B or w_idx.shape != (B, n_ih) or q_idx.dtype != torch.float32 or w_idx.dtype != torch.float32:
+        raise ValueError("q_idx [B, n_ih, hd] and w_idx [B, n_ih] must be float32")
+    if kv.ic is None or kv.ic.shape[1] != hd:
+        raise ValueError("kv.ic width must equal q_idx's last dim")
+    if kv.lc.shape[1] != L or kv.rc.shape[1] != rope:
+        raise ValueError("cache widths must match kv_lora and qk_rope")
+    dev = q_nope.device
+    if scores is None:
+        scores = torch.empty((B, t_max), dtype=torch.float32, device=dev)
+    elif scores.shape != (B, t_max) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [B, t_max]")
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev) if nsel is None else nsel
+    if sel.shape != (B, k) or sel.dtype != torch.int32 or nsel.shape != (B,) or nsel.dtype != torch.int32:
+        raise ValueError("sel must be int32 [B, k] and nsel int32 [B]")
+    if out is None:
+        out = torch.empty((B, H, v), dtype=torch.float32, device=dev)
+    d = _dims(H, nope, rope, v, L)
+    need = int(lib().mla_dsa_decode_workspace_bytes(ctypes.byref(d), B, t_max, k))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().mla_dsa_decode(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), float(theta), _ptr(q_idx), _ptr(w_idx), n_ih,
+                                _ptr(kv_b), _dt(kv_b), ctypes.byref(d), B, ctypes.byref(kv.view), t_max, k,
+                                float(sm_scale), _ptr(scores), _ptr(sel), _ptr(nsel), _ptr(out), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(dev)))
+    return out, scores, sel, nsel
 
 
 def mla_prefill_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, S: int, T: int) -> int:

@@ -289,6 +289,51 @@ mla_status mla_decode_attend(const void *q_rope, mla_dtype q_dt, const void *kv_
                                 out, ws, (hipStream_t)stream);
 }
 
+size_t mla_dsa_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t t_max, int32_t k)
+{
+    if (!d || B <= 0 || t_max < 0 || k <= 0) return 0;
+    if (check_dims(d) != MLA_OK) return 0;
+    const size_t a = dsa_decode_workspace_bytes(*d, B, t_max, k, MLA_BF16);
+    const size_t b = dsa_decode_workspace_bytes(*d, B, t_max, k, MLA_FP32);
+    return a > b ? a : b;
+}
+
+mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                          const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b, mla_dtype w_dt,
+                          const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
+                          float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_decode_common(d, B, q_dt, w_dt);
+    if (st) return st;
+    st = check_view(kv, B, true, true, true);
+    if (st) return st;
+    if (q_dt != kv->kv_dtype) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: q, kv_b and cache dtypes must match");
+    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "dsa decode: sm_scale not finite");
+    if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return fail(MLA_ERR_ARG, "dsa decode: rope_theta must be positive and finite");
+    if (d->qk_rope > 512) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: qk_rope > 512");
+    if (t_max < 0) return fail(MLA_ERR_ARG, "dsa decode: t_max negative");
+    if (t_max >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: t_max >= 2^31");
+    if (n_ih <= 0) return fail(MLA_ERR_ARG, "dsa decode: n_ih must be positive");
+    if (n_ih > 64) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: n_ih > 64");
+    if (k <= 0) return fail(MLA_ERR_ARG, "dsa decode: k must be positive");
+    if (k > 65536) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: k > 65536");
+    if (kv->index_hd <= 0 || kv->index_hd % 4 != 0)
+        return fail(MLA_ERR_ARG, "dsa decode: index_hd must be a positive multiple of 4");
+    if (kv->index_hd > 256) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: index_hd > 256");
+    if (B == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !q_idx || !w_idx || !kv_b || !sel || !nsel || !out || (!scores && t_max > 0))
+        return fail(MLA_ERR_ARG, "dsa decode: NULL tensor");
+    st = check_ws("dsa decode", dsa_decode_workspace_bytes(*d, B, t_max, k, q_dt), ws, ws_bytes);
+    if (st) return st;
+    const KvView v = to_view(*kv);
+    KvView vs = v;
+    if (vs.max_seq_len > t_max) vs.max_seq_len = t_max;
+    return launch_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv->index_hd, kv_b, *d, B, vs, v,
+                             t_max, k, sm_scale, scores, sel, nsel, out, ws, (hipStream_t)stream);
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T)
 {
     if (!d || S <= 0 || T <= 0) return 0;

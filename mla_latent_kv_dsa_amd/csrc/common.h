@@ -89,6 +89,21 @@ __device__ __forceinline__ int64_t seq_len_of(const KvView &v, int b)
     return s;
 }
 
+// ------------------------------------------------------------------ RoPE
+// Pair j of a rope_dim-wide interleaved tail at position pos: (a, b) -> (a cos - b sin,
+// b cos + a sin) with angle pos * theta^(-2j/rope_dim) formed in double.  The rotation uses
+// explicit fused multiply-adds so that every kernel that rotates produces the same bits.
+__device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim, double pos, double theta,
+                                          float &lo, float &hi)
+{
+    const double inv = pow(theta, -2.0 * (double)j / (double)rope_dim);
+    double sd, cd;
+    sincos(pos * inv, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    lo = __builtin_fmaf(a, c, -(b * sn));
+    hi = __builtin_fmaf(b, c, a * sn);
+}
+
 // ------------------------------------------------------------------ selection keys
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0.0 maps like +0.0.
 __device__ __forceinline__ uint32_t order_key(float f)
@@ -117,6 +132,8 @@ __device__ __forceinline__ float wave_max(float x)
 mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, int64_t tok_stride,
                        int64_t head_stride, int32_t rope_off, int32_t rope_dim, const int32_t *pos,
                        double theta, hipStream_t s);
+mla_status launch_rope_decode(const void *x, void *y, mla_dtype dt, int32_t B, int32_t n_heads, int32_t rope_dim,
+                              const KvView &kv, double theta, hipStream_t s);
 
 // ghist (optional): [B][2048] histogram of the top 11 order-key bits of the scores of keys
 // t < seq_len, accumulated with atomics (the caller zeroes it first)
@@ -126,9 +143,23 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
 mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, uint32_t *ghist,
                              hipStream_t s);
 size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
+// Work that the fused decode step runs beside the select's resolve step (matrix-core decode
+// geometry: 64 heads, kv_lora 512, bf16): q_abs = W_UK^T q_nope, and the query tails rotated
+// by RoPE at position seq_len - 1 into q_rope_out.
+constexpr int SIDE_MAXB = 32;
+struct SideAbsorb {
+    const bf16_t *q_nope;   // [B][64][nope]
+    const bf16_t *kv_b;     // [64 (nope + v)][512]
+    bf16_t *q_abs;          // [B][64][512]
+    const bf16_t *q_rope;   // [B][64][rope], before rotation
+    bf16_t *q_rope_out;     // [B][64][rope]
+    int B, nope, v, rope;
+    double theta;
+};
 mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
                                int64_t t_max, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
-                               size_t ws_bytes, hipStream_t s);
+                               size_t ws_bytes, hipStream_t s,
+                               const SideAbsorb *side = nullptr, bool *side_done = nullptr);
 size_t topk_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
 // n_valid (optional): row lengths, clamped to [0, max_len]; without it every row has max_len
 mla_status launch_topk(const float *scores, int32_t B, int64_t t_max, const int32_t *n_valid, int64_t max_len,
@@ -145,6 +176,12 @@ mla_status launch_decode(const void *q_nope, const void *q_rope, const void *kv_
                          const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
                          const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
                          float sm_scale, float *out, void *ws, size_t ws_bytes, hipStream_t s);
+size_t dsa_decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t t_max, int32_t k, mla_dtype dt);
+mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const float *q_idx,
+                             const float *w_idx, int32_t n_ih, int32_t hd, const void *kv_b, const mla_dims &d,
+                             int32_t B, const KvView &kv_sel, const KvView &kv, int64_t t_max, int32_t k,
+                             float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                             hipStream_t s);
 
 size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt);
 mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d,

@@ -73,4 +73,66 @@ mla_status launch_decode(const void *q_nope, const void *q_rope, const void *kv_
     return launch_attend_generic(q_rope, kv_b, dt, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
 }
 
+// ------------------------------------------------------------------------------ decode step
+// The whole decode hot path in one call: RoPE of the query tails (at seq_len - 1, out of place),
+// indexer scores and top-k selection, absorbed attention over the selected keys.
+// Workspace: select part | decode part | rotated query tails.
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t dsa_decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t t_max, int32_t k, mla_dtype dt)
+{
+    const size_t esz = dt == MLA_FP32 ? 4 : 2;
+    return 256 + al256(index_select_workspace_bytes(B, t_max, k)) + al256(decode_workspace_bytes(d, B, k, dt)) +
+           al256((size_t)B * d.n_heads * d.qk_rope * esz);
+}
+
+mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const float *q_idx,
+                             const float *w_idx, int32_t n_ih, int32_t hd, const void *kv_b, const mla_dims &d,
+                             int32_t B, const KvView &kv_sel, const KvView &kv, int64_t t_max, int32_t k,
+                             float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                             hipStream_t s)
+{
+    char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    const size_t sel_bytes = index_select_workspace_bytes(B, t_max, k);
+    void *sel_ws = p;
+    p += al256(sel_bytes);
+    void *dec_ws = p;
+    p += al256(decode_workspace_bytes(d, B, k, dt));
+    void *qr = p;
+    mla_status st;
+    const bool mfma = use_mfma(d, dt, kv_b) && aligned16(q_nope) && aligned16(q_rope) && aligned16(kv.lc) &&
+                      aligned16(kv.rc) && B <= SIDE_MAXB;
+    if (mfma) {
+        // the query absorption and the rotation run as extra workgroups of the selection's
+        // resolve step, which occupies only B workgroups
+        SideAbsorb sa;
+        sa.q_nope = (const bf16_t *)q_nope;
+        sa.kv_b = (const bf16_t *)kv_b;
+        sa.q_abs = decode_mfma_qabs(dec_ws);
+        sa.q_rope = (const bf16_t *)q_rope;
+        sa.q_rope_out = (bf16_t *)qr;
+        sa.B = B;
+        sa.nope = d.qk_nope;
+        sa.v = d.v_head;
+        sa.rope = d.qk_rope;
+        sa.theta = theta;
+        bool done = false;
+        st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s,
+                                 &sa, &done);
+        if (st) return st;
+        if (!done) {
+            st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
+            if (st) return st;
+            st = launch_absorb_mfma(q_nope, kv_b, d, B, dec_ws, s);
+            if (st) return st;
+        }
+        return launch_attend_mfma(qr, kv_b, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s);
+    }
+    st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
+    if (st) return st;
+    st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s);
+    if (st) return st;
+    return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
+}
+
 }  // namespace mla

@@ -23,6 +23,7 @@
 //             8-byte word addressed by lane 4e + j/4.
 #include "common.h"
 #include "decode_plan.h"
+#include "absorb_body.h"
 
 namespace mla {
 
@@ -59,87 +60,13 @@ __device__ __forceinline__ int64_t dec_row(const KvView &kv, int b, int64_t j, i
 }
 
 // ------------------------------------------------------------------------------ absorb
-// grid (DM_L / 128, H), 256 threads.  Thread t: row group rg = t/16 (rows rg, rg+16, ...) and
-// column group cg = t%16 (8 of the block's 128 columns).  The W_UK rows go out first, then the
-// queries of head h are staged in LDS, so both latencies overlap.  Queries are handled eight at
-// a time; row-group partial sums are reduced with lane shuffles inside a wave, then across
-// the four waves through LDS in a fixed order.
-constexpr int AB_QB = 8;
-
+// grid (DM_L / 128, H): one absorb_block per workgroup (absorb_body.h).
 template <int NR>   // qk_nope / 16
 __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nope, const bf16_t *__restrict__ kv_b,
                                                 int B, int v, bf16_t *__restrict__ q_abs)
 {
-    constexpr int nope = 16 * NR;
     extern __shared__ float sh_abs[];   // q [B][nope] fp32, then partials [4][AB_QB][128]
-    const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.y, cbase = blockIdx.x * 128;
-    const bf16_t *W = kv_b + ((int64_t)h * (nope + v) + rg) * DM_L + cbase + cg * 8;
-    uint4 w[NR];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) w[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)k * 16 * DM_L);
-    float *sq = sh_abs;
-    float *red = sh_abs + B * nope;
-    for (int i = tid; i < B * nope; i += 256) {
-        const int b = i / nope, r = i - b * nope;
-        sq[i] = bf2f(q_nope[((int64_t)b * DM_H + h) * nope + r]);
-    }
-    __syncthreads();
-    for (int b0 = 0; b0 < B; b0 += AB_QB) {
-        const int nb = B - b0 < AB_QB ? B - b0 : AB_QB;
-        float acc[AB_QB][8];
-#pragma unroll
-        for (int q = 0; q < AB_QB; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            float wf[8];
-            wf[0] = __uint_as_float(w[k].x << 16); wf[1] = __uint_as_float(w[k].x & 0xffff0000u);
-            wf[2] = __uint_as_float(w[k].y << 16); wf[3] = __uint_as_float(w[k].y & 0xffff0000u);
-            wf[4] = __uint_as_float(w[k].z << 16); wf[5] = __uint_as_float(w[k].z & 0xffff0000u);
-            wf[6] = __uint_as_float(w[k].w << 16); wf[7] = __uint_as_float(w[k].w & 0xffff0000u);
-#pragma unroll
-            for (int q = 0; q < AB_QB; ++q) {
-                if (q < nb) {
-                    const float qv = sq[(b0 + q) * nope + rg + 16 * k];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(qv, wf[e], acc[q][e]);
-                }
-            }
-        }
-        // the four row groups of a wave sit 16 lanes apart
-#pragma unroll
-        for (int q = 0; q < AB_QB; ++q) {
-            if (q < nb) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = acc[q][e];
-                    x += __shfl_xor(x, 16, 64);
-                    x += __shfl_xor(x, 32, 64);
-                    acc[q][e] = x;
-                }
-            }
-        }
-        if (lane < 16) {
-#pragma unroll
-            for (int q = 0; q < AB_QB; ++q) {
-                if (q < nb) {
-                    float *dst = &red[(wave * AB_QB + q) * 128 + cg * 8];
-                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-                    *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
-                }
-            }
-        }
-        __syncthreads();
-        for (int i = tid; i < nb * 128; i += 256) {
-            const int q = i >> 7, c = i & 127;
-            const float s = ((red[(0 * AB_QB + q) * 128 + c] + red[(1 * AB_QB + q) * 128 + c]) +
-                             red[(2 * AB_QB + q) * 128 + c]) + red[(3 * AB_QB + q) * 128 + c];
-            q_abs[((int64_t)(b0 + q) * DM_H + h) * DM_L + cbase + c] = f2bf(s);
-        }
-        __syncthreads();
-    }
+    absorb_block<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs);
 }
 
 // ------------------------------------------------------------------------------ attention core
@@ -561,6 +488,8 @@ static DecWs dec_ws(void *ws, int32_t B, const DecPlan &p)
 }
 
 size_t decode_mfma_absorb_ws(int32_t B) { return 256 + al256((size_t)B * DM_H * DM_L * 2); }
+
+bf16_t *decode_mfma_qabs(void *ws) { return dec_ws(ws, 1, DecPlan{1, DC_KC}).q_abs; }
 
 mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_dims &d, int32_t B, void *ws,
                               hipStream_t s)

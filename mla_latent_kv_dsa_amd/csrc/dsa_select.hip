@@ -19,6 +19,7 @@
 //                   and writes their positions at its offset -- ascending across the row
 // Rows longer than SEL_TMAX positions take the general top-k (three launches, any length).
 #include "common.h"
+#include "absorb_body.h"
 
 namespace mla {
 
@@ -119,20 +120,19 @@ struct SelRow {           // per-row results of the filter (uint32 words)
     uint32_t tb, kth, remaining, pad;
 };
 
-// grid (B), 256 threads: resolves the exact k-th key of a row among its candidates and the output
-// offset of every filter workgroup.
-__global__ __launch_bounds__(256) void sel_resolve(int64_t t_max, KvView kv, int nch, int k,
-                                                   const uint2 *__restrict__ cand, int64_t cap,
-                                                   const uint32_t *__restrict__ cnt, const uint32_t *__restrict__ blkabove,
-                                                   uint32_t *__restrict__ outpfx, uint32_t *__restrict__ eqpfx,
-                                                   SelRow *__restrict__ row_out)
+// One workgroup of 256 threads per row b: resolves the exact k-th key of the row among its
+// candidates and the output offset of every filter workgroup.
+__device__ __forceinline__ void resolve_row(int b, KvView kv, int nch, int k, const uint2 *__restrict__ cand,
+                                            int64_t cap, const uint32_t *__restrict__ cnt,
+                                            const uint32_t *__restrict__ blkabove, uint32_t *__restrict__ outpfx,
+                                            uint32_t *__restrict__ eqpfx, SelRow *__restrict__ row_out)
 {
     constexpr int NW = 4;
     __shared__ uint32_t h[SEL_BINS];
     __shared__ uint32_t gtc[SEL_MAXCH], eqc[SEL_MAXCH];
     __shared__ uint32_t sh[NW];
     __shared__ uint32_t s_bc[2];
-    const int tid = threadIdx.x, b = blockIdx.x;
+    const int tid = threadIdx.x;
     if (seq_len_of(kv, b) <= k) return;
     const SelRow rin = row_out[b];   // tb and the count above its bin, from the filter
     uint32_t E = cnt[b];
@@ -239,6 +239,48 @@ __global__ __launch_bounds__(256) void sel_resolve(int64_t t_max, KvView kv, int
         r.remaining = remaining;
         r.pad = 0u;
         row_out[b] = r;
+    }
+}
+
+// grid (B), 256 threads
+__global__ __launch_bounds__(256) void sel_resolve(KvView kv, int nch, int k, const uint2 *__restrict__ cand,
+                                                   int64_t cap, const uint32_t *__restrict__ cnt,
+                                                   const uint32_t *__restrict__ blkabove, uint32_t *__restrict__ outpfx,
+                                                   uint32_t *__restrict__ eqpfx, SelRow *__restrict__ row_out)
+{
+    resolve_row(blockIdx.x, kv, nch, k, cand, cap, cnt, blkabove, outpfx, eqpfx, row_out);
+}
+
+// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
+// work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
+// rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
+// grid (nres + 4 * 64): workgroups nres.. are absorb workgroup (cb, h) = (a % 4, a / 4); the
+// cb == 0 one of head h also rotates that head's query tails.
+template <int NR>
+__global__ __launch_bounds__(256) void sel_resolve_absorb(KvView kv, int nch, int k, const uint2 *__restrict__ cand,
+                                                          int64_t cap, const uint32_t *__restrict__ cnt,
+                                                          const uint32_t *__restrict__ blkabove,
+                                                          uint32_t *__restrict__ outpfx, uint32_t *__restrict__ eqpfx,
+                                                          SelRow *__restrict__ row_out, int nres, SideAbsorb sa)
+{
+    extern __shared__ float sh_abs[];
+    if ((int)blockIdx.x < nres) {
+        resolve_row(blockIdx.x, kv, nch, k, cand, cap, cnt, blkabove, outpfx, eqpfx, row_out);
+        return;
+    }
+    const int a = blockIdx.x - nres, cb = a & 3, h = a >> 2;
+    absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, sh_abs);
+    if (cb != 0) return;
+    const int half = sa.rope / 2;
+    for (int p = threadIdx.x; p < sa.B * half; p += 256) {
+        const int b = p / half, j = p - b * half;
+        const bf16_t *x = sa.q_rope + ((int64_t)b * AB_H + h) * sa.rope;
+        bf16_t *y = sa.q_rope_out + ((int64_t)b * AB_H + h) * sa.rope;
+        const int64_t sl = seq_len_of(kv, b);
+        float lo, hi;
+        rope_pair(bf2f(x[2 * j]), bf2f(x[2 * j + 1]), j, sa.rope, (double)(sl > 0 ? sl - 1 : 0), sa.theta, lo, hi);
+        y[j] = f2bf(lo);
+        y[half + j] = f2bf(hi);
     }
 }
 
@@ -463,8 +505,9 @@ size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k)
 
 mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
                                int64_t t_max, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
-                               size_t ws_bytes, hipStream_t s)
+                               size_t ws_bytes, hipStream_t s, const SideAbsorb *side, bool *side_done)
 {
+    if (side_done) *side_done = false;
     if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "select: B > 65535");
     mla_status st;
     if (t_max > SEL_TMAX) {
@@ -477,6 +520,9 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     hipLaunchKernelGGL(sel_zero, dim3(B), dim3(256), 0, s, sw.ghist, sw.cnt);
     st = check_launch("sel_zero");
     if (st) return st;
+    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
+                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
+    const int nres = t_max > 0 ? B : 0;
     if (t_max > 0) {
         st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, sw.ghist, s);
         if (st) return st;
@@ -484,10 +530,29 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
                            sw.cand, sw.cap, sw.cnt, sw.blkabove, sw.rows);
         st = check_launch("sel_filter");
         if (st) return st;
-        hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(256), 0, s, t_max, kv, (int)sw.nch, k, sw.cand, sw.cap, sw.cnt,
-                           sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows);
-        st = check_launch("sel_resolve");
+        if (!with_side) {
+            hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(256), 0, s, kv, (int)sw.nch, k, sw.cand, sw.cap, sw.cnt,
+                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows);
+            st = check_launch("sel_resolve");
+            if (st) return st;
+        }
+    }
+    if (with_side) {
+        const dim3 g((unsigned)(nres + 4 * AB_H));
+        const size_t shm = (size_t)B * side->nope * 4 + 4 * AB_QB * 128 * 4;
+        const int nch = (int)sw.nch;
+        if (side->nope == 128)
+            hipLaunchKernelGGL(sel_resolve_absorb<8>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
+                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
+        else if (side->nope == 192)
+            hipLaunchKernelGGL(sel_resolve_absorb<12>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
+                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
+        else
+            hipLaunchKernelGGL(sel_resolve_absorb<16>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
+                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
+        st = check_launch("sel_resolve_absorb");
         if (st) return st;
+        if (side_done) *side_done = true;
     }
     const unsigned ge = sw.nch > 0 ? (unsigned)sw.nch : 1u;
     hipLaunchKernelGGL(sel_emit, dim3(ge, B), dim3(256), 0, s, scores, t_max, kv, k, sw.outpfx, sw.eqpfx, sw.rows, sel,

@@ -24,24 +24,17 @@ __global__ __launch_bounds__(256) void rope_kernel(T *__restrict__ x, int64_t n_
     const int64_t unit = (int64_t)blockIdx.x * units_per_block + u_local;
     const bool active = u_local < units_per_block && unit < n_units;
     T *tail = nullptr;
-    float a = 0.f, b = 0.f, c = 1.f, s = 0.f;
+    float lo = 0.f, hi = 0.f;
     if (active) {
         const int64_t n = unit / n_heads;
         const int32_t h = (int32_t)(unit - n * n_heads);
         tail = x + n * tok_stride + (int64_t)h * head_stride + rope_off;
-        a = ld(tail + 2 * j);
-        b = ld(tail + 2 * j + 1);
-        const double inv = pow(theta, -2.0 * (double)j / (double)(2 * half));
-        const double phi = (double)pos[n] * inv;
-        double sd, cd;
-        sincos(phi, &sd, &cd);
-        c = (float)cd;
-        s = (float)sd;
+        rope_pair(ld(tail + 2 * j), ld(tail + 2 * j + 1), j, 2 * half, (double)pos[n], theta, lo, hi);
     }
     __syncthreads();
     if (active) {
-        st(tail + j, a * c - b * s);
-        st(tail + half + j, b * c + a * s);
+        st(tail + j, lo);
+        st(tail + half + j, hi);
     }
 }
 
@@ -61,6 +54,42 @@ mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, in
         hipLaunchKernelGGL(rope_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (bf16_t *)x, n_units,
                            n_heads, tok_stride, head_stride, rope_off, half, pos, theta, upb);
     return check_launch("rope_kernel");
+}
+
+// Decode queries: y[b][h] = RoPE of the tail x[b][h][0..rope) at position seq_len[b] - 1 (the
+// query's own position, the last cached token), out of place.  grid (ceil(B * H * half / 256)).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_decode_kernel(const T *__restrict__ x, T *__restrict__ y, int32_t B,
+                                                          int32_t n_heads, int32_t half, KvView kv, double theta)
+{
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= (int64_t)B * n_heads * half) return;
+    const int64_t unit = p / half;
+    const int j = (int)(p - unit * half);
+    const int b = (int)(unit / n_heads);
+    const int64_t sl = seq_len_of(kv, b);
+    float lo, hi;
+    rope_pair(ld(x + unit * 2 * half + 2 * j), ld(x + unit * 2 * half + 2 * j + 1), j, 2 * half,
+              (double)(sl > 0 ? sl - 1 : 0), theta, lo, hi);
+    st(y + unit * 2 * half + j, lo);
+    st(y + unit * 2 * half + half + j, hi);
+}
+
+mla_status launch_rope_decode(const void *x, void *y, mla_dtype dt, int32_t B, int32_t n_heads, int32_t rope_dim,
+                              const KvView &kv, double theta, hipStream_t s)
+{
+    const int32_t half = rope_dim / 2;
+    const int64_t n = (int64_t)B * n_heads * half;
+    if (n == 0) return MLA_OK;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "rope: too many units");
+    if (dt == MLA_FP32)
+        hipLaunchKernelGGL(rope_decode_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, (const float *)x,
+                           (float *)y, B, n_heads, half, kv, theta);
+    else
+        hipLaunchKernelGGL(rope_decode_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t *)x,
+                           (bf16_t *)y, B, n_heads, half, kv, theta);
+    return check_launch("rope_decode_kernel");
 }
 
 }  // namespace mla

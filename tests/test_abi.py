@@ -228,3 +228,35 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(mla, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mla.lib()
+
+
+def test_dsa_decode_validation(L):
+    _no_gpu()
+    d = _dims()
+
+    def f(d=d, B=1, v=None, q_dt=1, w_dt=1, theta=1e4, n_ih=32, t=4096, k=2048, scale=0.0625, ws=None, wsb=0,
+          scores=FAKE, out=FAKE):
+        return L.mla_dsa_decode(FAKE, FAKE, q_dt, theta, FAKE, FAKE, n_ih, FAKE, w_dt, ctypes.byref(d), B,
+                                ctypes.byref(v or _view()), t, k, scale, scores, FAKE, FAKE, out, ws, wsb, None)
+    need = L.mla_dsa_decode_workspace_bytes(ctypes.byref(d), 1, 4096, 2048)
+    assert need >= L.dsa_index_select_workspace_bytes(1, 4096, 2048) + L.mla_decode_workspace_bytes(
+        ctypes.byref(d), 1, 2048)
+    assert f() == mla.MLA_ERR_WORKSPACE
+    assert f(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert f(d=_dims(n_heads=0)) == mla.MLA_ERR_ARG
+    assert f(q_dt=0) == mla.MLA_ERR_UNSUPPORTED          # mixed dtypes
+    assert f(theta=0.0) == mla.MLA_ERR_ARG
+    assert f(theta=float("nan")) == mla.MLA_ERR_ARG
+    assert f(scale=float("inf")) == mla.MLA_ERR_ARG
+    assert f(n_ih=0) == mla.MLA_ERR_ARG
+    assert f(k=0) == mla.MLA_ERR_ARG
+    assert f(k=70000) == mla.MLA_ERR_UNSUPPORTED
+    assert f(t=-1) == mla.MLA_ERR_ARG
+    assert f(t=1 << 31) == mla.MLA_ERR_UNSUPPORTED
+    assert f(v=_view(ic=None)) == mla.MLA_ERR_ARG
+    assert f(v=_view(lc=None)) == mla.MLA_ERR_ARG
+    assert f(v=_view(seq_len=None)) == mla.MLA_ERR_ARG
+    assert f(v=_view(index_hd=6)) == mla.MLA_ERR_ARG
+    assert f(out=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
+    assert f(scores=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
+    assert f(B=0) == mla.MLA_OK

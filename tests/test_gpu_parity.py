@@ -456,6 +456,96 @@ def test_dsa_decode_step_end_to_end_small():
     assert rel_err(out[0], _decode_ref(d, 0, ref_sel, sm)) <= TOL_BF16
 
 
+def _paged_copy(rows_by_seq, bs, rng):
+    """Scatter per-sequence row arrays [B][T, w] into a pool of bs-row blocks in a random
+    physical order; returns (pool, block_table [B, T/bs])."""
+    B, T = len(rows_by_seq), rows_by_seq[0].shape[0]
+    nb = T // bs
+    perm = rng.permutation(B * nb).astype(np.int32)
+    bt = perm.reshape(B, nb)
+    pool = np.zeros((B * nb * bs, rows_by_seq[0].shape[1]), rows_by_seq[0].dtype)
+    for b in range(B):
+        for j in range(nb):
+            pool[bt[b, j] * bs:(bt[b, j] + 1) * bs] = rows_by_seq[b][j * bs:(j + 1) * bs]
+    return pool, bt
+
+
+def _dsa_step_check(d, kv, seq_len, t_max, k, theta=10000.0, oracle_rows=()):
+    """mla_dsa_decode == mla_rope_interleave (at seq_len - 1, on a copy) + dsa_index_select +
+    mla_absorbed_decode, bit for bit; q_rope is left unrotated; rows in oracle_rows are also
+    checked against the oracle (selection and attention)."""
+    to = dev_bf16 if d.bf16 else dev
+    qn, qr, kvb = to(d.q_nope), to(d.q_rope), to(d.kv_b)
+    qi, wi = dev(d.q_idx), dev(d.w_idx)
+    qr0 = qr.clone()
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    out, sc, sel, nsel = mla.mla_dsa_decode(qn, qr, qi, wi, kvb, kv, t_max, k, sm, theta=theta)
+    assert torch.equal(qr, qr0)
+    qr2 = qr.clone()
+    pos = dev(np.maximum(np.minimum(np.asarray(seq_len, np.int32), t_max) - 1, 0).astype(np.int32))
+    mla.mla_rope_interleave(qr2, pos, 0, d.rope, theta=theta)
+    sc2, sel2, nsel2 = mla.dsa_index_select(qi, wi, kv, t_max, k)
+    out2 = mla.mla_absorbed_decode(qn, qr2, kvb, kv, sm, sel=sel2, nsel=nsel2)
+    assert np.array_equal(host(sc).view(np.uint32), host(sc2).view(np.uint32))
+    assert np.array_equal(host(sel), host(sel2)) and np.array_equal(host(nsel), host(nsel2))
+    assert np.array_equal(host(out), host(out2))
+    cv = synth.bf16_bits_to_f32 if d.bf16 else (lambda a: a)
+    for b in oracle_rows:
+        n = min(seq_len[b], t_max)
+        ref_s = oracle.index_scores(d.q_idx[b], d.w_idx[b], d.ic[b * d.T:b * d.T + n])
+        ref_sel, ref_n = oracle.topk(ref_s, n, k)
+        ref_sel = ref_sel[:ref_n]
+        assert int(host(nsel)[b]) == ref_n and np.array_equal(host(sel)[b, :ref_n], ref_sel)
+        q_rot = oracle.rope_interleave(cv(d.q_rope[b])[None], np.array([n - 1], np.int32), 0, d.rope, theta)[0]
+        ref = oracle.absorbed_decode(cv(d.q_nope[b]), q_rot, cv(d.kv_b), cv(d.lc[b * d.T:(b + 1) * d.T]),
+                                     cv(d.rc[b * d.T:(b + 1) * d.T]), ref_sel, d.v, sm)
+        assert rel_err(host(out)[b], ref) <= (TOL_BF16 if d.bf16 else TOL_F32), b
+    return host(out), host(sel), host(nsel)
+
+
+def test_dsa_decode_call_full_context_131072():
+    T, k = 131072, 2048
+    d = synth.decode(3, T, dsa=True)
+    log("mla_dsa_decode T=131072 k=2048")
+    kv = _kv(d.lc, d.rc, d.ic, [T], T, seq_stride=T)
+    _dsa_step_check(d, kv, [T], T, k, oracle_rows=(0,))
+
+
+def test_dsa_decode_call_batched_and_short_rows():
+    """Rows above and below k (a short row keeps every key: the dense decode), a ragged
+    tail, and t_max beyond the longest row."""
+    T, k = 6000, 1024
+    seq_len = [6000, 700, 4097]
+    d = synth.decode(95, T, B=3, dsa=True)
+    log("mla_dsa_decode batched")
+    kv = _kv(d.lc, d.rc, d.ic, seq_len, T, seq_stride=T)
+    out, sel, nsel = _dsa_step_check(d, kv, seq_len, T, k, theta=50000.0, oracle_rows=(0, 1, 2))
+    assert int(nsel[1]) == 700 and np.array_equal(sel[1, :700], np.arange(700))
+
+
+def test_dsa_decode_call_paged():
+    T, k, bs = 4096, 512, 64
+    seq_len = [4096, 3000]
+    d = synth.decode(96, T, B=2, dsa=True)
+    rng = np.random.default_rng(97)
+    split = lambda a: [a[b * T:(b + 1) * T] for b in range(2)]
+    lc_p, bt = _paged_copy(split(d.lc), bs, rng)
+    rc_p, _ = _paged_copy(split(d.rc), bs, np.random.default_rng(97))
+    ic_p, _ = _paged_copy(split(d.ic), bs, np.random.default_rng(97))
+    log("mla_dsa_decode paged")
+    kv = _kv(lc_p, rc_p, ic_p, seq_len, T, block_table=bt, block_size=bs)
+    _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(1,))
+
+
+def test_dsa_decode_call_fp32_generic_path():
+    T, k = 1500, 256
+    d = synth.decode(98, T, B=2, dsa=True, bf16=False)
+    seq_len = [1500, 200]
+    log("mla_dsa_decode fp32")
+    kv = _kv(d.lc, d.rc, d.ic, seq_len, T, seq_stride=T, bf16=False)
+    _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(0, 1))
+
+
 def test_topk_all_equal_full_context():
     # every score in one threshold bin: all 131072 positions become candidates
     T = 131072
