@@ -1,17 +1,29 @@
-// prefill.hip -- chooses the kernels of mla_prefill_nonabsorbed for a given shape and dtype.
+// prefill.hip -- chooses the kernels of mla_prefill_nonabsorbed for a given shape and dtype:
+// the matrix-core kernels (prefill_mfma.hip) for bf16 with 64 heads, kv_lora 512, qk_rope 64,
+// v_head 256, qk_nope 128/192 and 16-byte aligned operands, the generic kernels otherwise.
 #include "prefill_plan.h"
 
 namespace mla {
 
-size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype)
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt)
 {
-    return prefill_generic_ws(d, S, T);
+    const size_t g = prefill_generic_ws(d, S, T);
+    if (prefill_mfma_supported(d, dt)) {
+        const size_t m = prefill_mfma_ws(d, T);
+        return m > g ? m : g;
+    }
+    return g;
 }
 
 mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d, const KvView &kv,
                           int32_t S, int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws,
                           size_t, hipStream_t s)
 {
+    if (prefill_mfma_supported(d, dt) && aligned16(q) && aligned16(kv_b) && aligned16(kv.lc) && aligned16(kv.rc) &&
+        aligned16(out))
+        return launch_prefill_mfma(q, kv_b, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s);
     return launch_prefill_generic(q, kv_b, dt, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s);
 }
 

@@ -1,0 +1,406 @@
+// prefill_mfma.hip -- non-absorbed causal prefill on bf16 matrix cores for 64 heads, kv_lora
+// 512, qk_rope 64, v_head 256 and qk_nope 128/192 (the GLM-5.2 geometry).  colibri-analysis 06
+// "MLA attention and KV cache", sec. 2.3, non-absorbed path: one kv_b matmul rebuilds k_nope
+// and v of every cached token, then causal softmax attention with
+// score = q_nope . k_nope + q_rope . Rc over the keys t <= pos_base + i.
+//
+//   pf_kvb    C[t][n] = sum_l kv_b[n][l] Lc(t)[l], bf16 out ([T][H (nope + v)], head h's k_nope
+//             then v in columns h (nope + v) ..).  Computed as C^T = kv_b . Lc^T in 256 x 256
+//             tiles (wave: 128 x 128) on v_mfma_f32_32x32x16_bf16, K = 512 in steps of 32 staged
+//             in LDS (rows padded to 80 B: conflict-free operand reads), the next step's global
+//             loads in flight during the current step's products.  With n as the row index of
+//             the product every lane holds four consecutive n of one token: 8-byte stores.
+//   pf_attn   per (128-query block, head), 4 waves x 32 queries, 64-key tiles of K (k_nope and
+//             Rc, 256 dims) and V (256 dims) staged in LDS:
+//               S^T = K Q^T      A = K rows from LDS, B = the wave's queries held in registers
+//               online softmax   lane l owns query l % 32 together with lane l ^ 32 (one
+//                                exchange per tile for the maximum and the sum)
+//               O^T += V^T P^T   A = V^T by transposed LDS reads, B = P^T straight from the
+//                                score registers after one v_permlane32_swap per register pair
+//             so all softmax bookkeeping is lane-local; blocks of late queries (the most keys)
+//             are dispatched first.
+//
+// MFMA operand layouts (gfx950): v_mfma_f32_32x32x16_bf16 lane l supplies A[l%32][8(l/32)+e]
+// and B[8(l/32)+e][l%32], e = 0..7; result register r of lane l is D[8(r/4)+4(l/32)+r%4][l%32].
+// ds_read_b64_tr_b16: in each group of 16 lanes, element e of lane j is element j%4 of the
+// 8-byte word addressed by lane 4e + j/4.
+#include "common.h"
+#include "prefill_plan.h"
+
+namespace mla {
+
+typedef __bf16 pbf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf32x16 __attribute__((ext_vector_type(16)));
+typedef short pv4s __attribute__((ext_vector_type(4)));
+typedef short pv8s __attribute__((ext_vector_type(8)));
+
+constexpr int PF_H = 64, PF_L = 512, PF_R = 64, PF_V = 256;
+
+__device__ __forceinline__ pbf16x8 pf_bf16x8(uint4 v) { return __builtin_bit_cast(pbf16x8, v); }
+
+__device__ __forceinline__ uint32_t pf_pack(float a, float b)
+{
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ------------------------------------------------------------------------------ kv_b GEMM
+__device__ __forceinline__ uint32_t pf_lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One 64-lane global_load_lds_dwordx4 (16 B per lane from g, lane i's to LDS byte lds + 16 i; lds
+// wave-uniform), from inline assembly so that the compiler does not make every later LDS access
+// wait for it; completion is awaited with an explicit s_waitcnt vmcnt.  M0 is restored.
+__device__ __forceinline__ void pf_dma16(const void *g, uint32_t lds)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(g), "s"(lds)
+                 : "memory");
+}
+
+constexpr int KG_BM = 256, KG_BN = 256, KG_BK = 32;   // rows of C^T (n), columns (tokens), K step
+constexpr int KG_NS = 3;                               // K steps staged at a time
+constexpr size_t KG_LDS = (size_t)KG_NS * (KG_BM + KG_BN) * KG_BK * 2;   // 96 KB
+
+// grid (ceil(N / 256), ceil(T / 256)), 256 threads; wave w: n rows 128 (w&1) .., tokens 128 (w>>1) ..
+// A K step of a tile is 256 rows x 64 B in LDS, the four 16-byte chunks of row r stored at
+// positions c ^ ((r >> 2) & 3): sixteen consecutive rows read at one chunk hit distinct banks.
+// Wave w copies rows 64 w .. 64 w + 63 of both tiles, 16 rows (1 KB) per DMA: lane L moves
+// chunk (L % 4) ^ ((r >> 2) & 3) of row r = 16 j + L / 4 into position L % 4.
+__global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restrict__ kv_b, int64_t T, int N,
+                                              bf16_t *__restrict__ C)
+{
+    extern __shared__ __attribute__((aligned(16))) char kg_smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * KG_BM;
+    const int64_t t0 = (int64_t)blockIdx.y * KG_BN;
+    const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc);
+    const bf16_t *ga[4];
+    const bf16_t *gb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 64 * wave + 16 * j + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int n = n0 + r;
+        ga[j] = kv_b + (int64_t)(n < N ? n : N - 1) * PF_L + 8 * c;
+        const int64_t t = t0 + r;
+        const int64_t row = kv_row(kv, 0, t < T ? t : T - 1);
+        gb[j] = lc + (row >= 0 ? row : 0) * PF_L + 8 * c;
+    }
+    auto stage = [&](int ks) {   // K step ks into ring slot ks % KG_NS
+        char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_BK * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pf_dma16(ga[j] + KG_BK * ks, pf_lds_addr(base + (64 * wave + 16 * j) * 64));
+            pf_dma16(gb[j] + KG_BK * ks, pf_lds_addr(base + KG_BM * 64 + (64 * wave + 16 * j) * 64));
+        }
+    };
+    pf32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int wm = 128 * (wave & 1), wn = 128 * (wave >> 1);
+    const int l32 = lane & 31, hi = lane >> 5;
+    constexpr int NK = PF_L / KG_BK;   // 16 K steps
+    stage(0);
+    stage(1);
+    for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 2 < NK) {
+            stage(ks + 2);
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // step ks has landed everywhere
+        } else if (ks + 1 < NK) {
+            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        const char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_BK * 2;
+#pragma unroll
+        for (int kk = 0; kk < KG_BK / 16; ++kk) {
+            uint4 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ra = wm + 32 * i + l32, rb = wn + 32 * i + l32, c = 2 * kk + hi;
+                a[i] = *reinterpret_cast<const uint4 *>(base + ra * 64 + 16 * (c ^ ((ra >> 2) & 3)));
+                b[i] = *reinterpret_cast<const uint4 *>(base + KG_BM * 64 + rb * 64 + 16 * (c ^ ((rb >> 2) & 3)));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(a[i]), pf_bf16x8(b[j]), acc[i][j],
+                                                                        0, 0, 0);
+        }
+        // the slot is copied over again two steps later: every wave has consumed its reads
+        asm volatile("s_barrier" ::: "memory");
+    }
+    // register r of tile (i, j): n = n0 + wm + 32 i + 8 (r/4) + 4 hi + r%4, token t0 + wn + 32 j + l32
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + wn + 32 * j + l32;
+        if (t >= T) continue;
+        bf16_t *crow = C + t * (int64_t)N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wm + 32 * i + 8 * g + 4 * hi;
+                if (n < N) {
+                    uint2 v;
+                    v.x = pf_pack(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+                    v.y = pf_pack(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    *reinterpret_cast<uint2 *>(crow + n) = v;
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------ attention
+constexpr int PA_BQ = 128, PA_BK = 64;
+constexpr int PA_ROW = 536;    // bf16 per staged key row: K (256) then V (256), pitch 1072 B so that
+                               // the K row reads and the transposed V reads fall in distinct banks
+constexpr size_t PA_LDS = (size_t)2 * PA_BK * PA_ROW * 2;   // two tiles
+
+
+// grid (ceil(S / 128), H), 256 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
+template <int NOPE, typename OUT>
+__global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C, KvView kv,
+                                               int S, int pos_base, float scale_log2, OUT *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) char pa_smem[];
+    bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 tiles][64 keys][PA_ROW]
+    constexpr int QD = NOPE + PF_R;            // query / key width (256 for nope 192)
+    constexpr int KS = QD / 16;                // K steps of the score product
+    constexpr int N = PF_H * (NOPE + PF_V);    // row length of C
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int nqb = gridDim.x;
+    const int qb = nqb - 1 - (int)blockIdx.x;  // late query blocks (most keys) first
+    const int h = blockIdx.y;
+    const int i0 = qb * PA_BQ;
+    const int iq = i0 + 32 * wave + l32;       // this lane's query
+    const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
+
+    // the wave's queries as the B operand of S^T (query l32, dims 16 ks + 8 hi ..)
+    uint4 bq[KS];
+    {
+        const bf16_t *qr = q + ((int64_t)(iq < S ? iq : S - 1) * PF_H + h) * QD + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
+    }
+    const int64_t qpos = (int64_t)pos_base + iq;                       // keys t <= qpos
+    const int i_last = i0 + PA_BQ - 1 < S - 1 ? i0 + PA_BQ - 1 : S - 1;
+    const int64_t kend = (int64_t)pos_base + i_last + 1;               // keys of the block
+    const int ntile = (int)((kend + PA_BK - 1) / PA_BK);
+    float m_run = -INFINITY, l_run = 0.f;
+    pf32x16 o[PF_V / 32];
+#pragma unroll
+    for (int dt = 0; dt < PF_V / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+
+    // staging: wave w copies key rows 16 w .. 16 w + 15 of a tile, one DMA per row: lanes 0..31
+    // the K row (dims 8 lane ..: k_nope from C, then Rc; lanes past the key width re-read the
+    // row's first chunk, never used), lanes 32..63 the V row behind it
+    const bool is_k = lane < 32;
+    const bool is_rc = is_k && 8 * lane >= NOPE && 8 * lane < QD;
+    const int c_off = h * (NOPE + PF_V) + (is_k ? (8 * lane < NOPE ? 8 * lane : 0) : NOPE + 8 * (lane - 32));
+    const int rc_off = is_rc ? 8 * lane - NOPE : 0;
+    auto stage = [&](int kt) {
+        bf16_t *dst = sT + (kt & 1) * PA_BK * PA_ROW;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * wave + i;
+            const int64_t t0 = (int64_t)kt * PA_BK + r;
+            const int64_t t = t0 < kend ? t0 : kend - 1;
+            const bf16_t *src;
+            if (is_rc) {
+                const int64_t row = kv_row(kv, 0, t);
+                src = rc + (row >= 0 ? row : 0) * PF_R + rc_off;
+            } else {
+                src = C + t * (int64_t)N + c_off;
+            }
+            pf_dma16(src, pf_lds_addr(dst + r * PA_ROW));
+        }
+    };
+    const int G = lane >> 4, j16 = lane & 15;   // transposed-read address inside a 16-key step
+    const int tr_off = (8 * (G >> 1) + (j16 >> 2)) * PA_ROW + 256 + 16 * (G & 1) + 4 * (j16 & 3);
+    stage(0);
+    for (int kt = 0; kt < ntile; ++kt) {
+        const int64_t k0 = (int64_t)kt * PA_BK;
+        if (kt + 1 < ntile) {
+            stage(kt + 1);
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // tile kt has landed
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        const bf16_t *tk = sT + (kt & 1) * PA_BK * PA_ROW;
+        // S^T: two 32-key tiles; register r of s[mt] is key k0 + 32 mt + 8 (r/4) + 4 hi + r%4
+        pf32x16 s[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+            const bf16_t *ka = tk + (32 * mt + l32) * PA_ROW + 8 * hi;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(*reinterpret_cast<const uint4 *>(ka + 16 * ks)),
+                                                                pf_bf16x8(bq[ks]), s[mt], 0, 0, 0);
+        }
+        // causal mask, scale, running maximum (lanes l and l ^ 32 hold the same query)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t t = k0 + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const float v = t <= qpos ? s[mt][r] * scale_log2 : -INFINITY;
+                s[mt][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt
+        uint2 pk[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = s[mt][4 * g + e];
+                    p[e] = v == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v - m_new);
+                }
+                pk[mt][g].x = pf_pack(p[0], p[1]);
+                pk[mt][g].y = pf_pack(p[2], p[3]);
+                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                const bf2 a = __builtin_bit_cast(bf2, pk[mt][g].x), b = __builtin_bit_cast(bf2, pk[mt][g].y);
+                psum += ((float)a[0] + (float)a[1]) + ((float)b[0] + (float)b[1]);
+            }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < PF_V / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        // O^T += V^T P^T over four 16-key steps: step kb covers keys 16 kb .. +15 (tile kb/2,
+        // groups g = 2 (kb%2), +1).  Lane l needs keys 8 hi .. 8 hi + 7 of the step for query l32;
+        // it holds keys 4 hi + 0..3 (group g) and 8 + 4 hi + 0..3 (group g + 1): one swap of the
+        // upper half's first group with the lower half's second group gives the operand.
+#pragma unroll
+        for (int kb = 0; kb < PA_BK / 16; ++kb) {
+            const int mt = kb >> 1, g = 2 * (kb & 1);
+            const auto x0 = __builtin_amdgcn_permlane32_swap(pk[mt][g].x, pk[mt][g + 1].x, false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(pk[mt][g].y, pk[mt][g + 1].y, false, false);
+            uint4 pb;
+            pb.x = x0[0];
+            pb.y = x1[0];
+            pb.z = x0[1];
+            pb.w = x1[1];
+            const bf16_t *vb = tk + 16 * kb * PA_ROW + tr_off;
+#pragma unroll
+            for (int dt = 0; dt < PF_V / 32; ++dt) {
+                const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) pv4s *)(vb + 32 * dt));
+                const pv4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_ROW + 32 * dt));
+                const pv8s vt = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt), pf_bf16x8(pb), o[dt],
+                                                                0, 0, 0);
+            }
+        }
+        // every wave has consumed its reads of this tile (they feed the products above) before
+        // the next iteration copies tile kt + 2 over it
+        asm volatile("s_barrier" ::: "memory");
+    }
+    if (iq >= S) return;
+    // register r of o[dt]: dim 32 dt + 8 (r/4) + 4 hi + r%4 of query iq
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    OUT *orow = out + ((int64_t)iq * PF_H + h) * PF_V;
+#pragma unroll
+    for (int dt = 0; dt < PF_V / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int dim = 32 * dt + 8 * g + 4 * hi;
+            const float a = o[dt][4 * g] * inv, b = o[dt][4 * g + 1] * inv, c = o[dt][4 * g + 2] * inv,
+                        d = o[dt][4 * g + 3] * inv;
+            if constexpr (sizeof(OUT) == 4) {
+                *reinterpret_cast<float4 *>(orow + dim) = make_float4(a, b, c, d);
+            } else {
+                uint2 v;
+                v.x = pf_pack(a, b);
+                v.y = pf_pack(c, d);
+                *reinterpret_cast<uint2 *>(orow + dim) = v;
+            }
+        }
+}
+
+// ------------------------------------------------------------------------------ host side
+bool prefill_mfma_supported(const mla_dims &d, mla_dtype dt)
+{
+    return dt == MLA_BF16 && d.n_heads == PF_H && d.kv_lora == PF_L && d.qk_rope == PF_R && d.v_head == PF_V &&
+           (d.qk_nope == 128 || d.qk_nope == 192);
+}
+
+size_t prefill_mfma_ws(const mla_dims &d, int64_t T)
+{
+    return 256 + (size_t)T * d.n_heads * (d.qk_nope + d.v_head) * 2;
+}
+
+template <int NOPE, typename OUT>
+static mla_status launch_attn(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
+                              float scale_log2, void *out, hipStream_t s)
+{
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)PA_LDS);
+        if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+        attr = true;
+    }
+    const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ), PF_H);
+    hipLaunchKernelGGL((pf_attn<NOPE, OUT>), g, dim3(256), PA_LDS, s, (const bf16_t *)q, C, kv, S, pos_base, scale_log2,
+                       (OUT *)out);
+    return check_launch("pf_attn");
+}
+
+mla_status launch_prefill_mfma(const void *q, const void *kv_b, const mla_dims &d, const KvView &kv, int32_t S,
+                               int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws, hipStream_t s)
+{
+    const int64_t T = (int64_t)pos_base + S;
+    const int N = d.n_heads * (d.qk_nope + d.v_head);
+    bf16_t *C = reinterpret_cast<bf16_t *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    const int64_t gy = (T + KG_BN - 1) / KG_BN;
+    if (gy > 65535) return fail(MLA_ERR_UNSUPPORTED, "prefill: too many tokens");
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_kvb),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)KG_LDS);
+        if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+        attr = true;
+    }
+    hipLaunchKernelGGL(pf_kvb, dim3((unsigned)((N + KG_BM - 1) / KG_BM), (unsigned)gy), dim3(256), KG_LDS, s, kv,
+                       (const bf16_t *)kv_b, T, N, C);
+    mla_status st = check_launch("pf_kvb");
+    if (st) return st;
+    const float sl2 = sm_scale * 1.4426950408889634f;
+    if (d.qk_nope == 192)
+        return out_dt == MLA_FP32 ? launch_attn<192, float>(q, C, kv, S, pos_base, sl2, out, s)
+                                  : launch_attn<192, bf16_t>(q, C, kv, S, pos_base, sl2, out, s);
+    return out_dt == MLA_FP32 ? launch_attn<128, float>(q, C, kv, S, pos_base, sl2, out, s)
+                              : launch_attn<128, bf16_t>(q, C, kv, S, pos_base, sl2, out, s);
+}
+
+}  // namespace mla

@@ -9,4 +9,9 @@ mla_status launch_prefill_generic(const void *q, const void *kv_b, mla_dtype dt,
                                   int32_t S, int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws,
                                   hipStream_t s);
 
+bool prefill_mfma_supported(const mla_dims &d, mla_dtype dt);
+size_t prefill_mfma_ws(const mla_dims &d, int64_t T);
+mla_status launch_prefill_mfma(const void *q, const void *kv_b, const mla_dims &d, const KvView &kv, int32_t S,
+                               int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws, hipStream_t s);
+
 }  // namespace mla

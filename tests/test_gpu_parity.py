@@ -437,6 +437,47 @@ def test_prefill_small_glm_heads(S, pos_base, out_bf16):
     assert rel_err(out[rows], ref) <= TOL_BF16
 
 
+def _prefill_glm_check(S, pos_base, seed, out_bf16, rows, heads, bs=0):
+    """64-head GLM geometry (the matrix-core path): rows x heads of the output against the oracle."""
+    p = synth.prefill(seed, S, pos_base)
+    T = pos_base + S
+    sm = 1.0 / math.sqrt(p.nope + p.rope)
+    if bs:
+        rng = np.random.default_rng(seed + 1)
+        lc_p, bt = _paged_copy([p.lc], bs, rng)
+        rc_p, _ = _paged_copy([p.rc], bs, np.random.default_rng(seed + 1))
+        kv = _kv(lc_p, rc_p, None, None, T, block_table=bt, block_size=bs)
+    else:
+        kv = _kv(p.lc, p.rc, None, None, T, seq_stride=T)
+    out = mla.mla_prefill_nonabsorbed(dev_bf16(p.q), dev_bf16(p.kv_b), kv, p.nope, pos_base, sm,
+                                      out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    out = host(out)
+    cv = synth.bf16_bits_to_f32
+    R = p.nope + p.v
+    kvb_h = np.concatenate([p.kv_b[h * R:(h + 1) * R] for h in heads])
+    ref = oracle.prefill_rows(cv(p.q)[:, heads], cv(kvb_h), cv(p.lc), cv(p.rc), pos_base, p.nope, p.v, sm, rows)
+    got = out[rows][:, heads]
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= TOL_BF16
+    return out
+
+
+@pytest.mark.parametrize("S,pos_base,out_bf16,bs", [(300, 0, False, 0), (200, 333, True, 0), (256, 64, False, 64)])
+def test_prefill_glm_64_heads(S, pos_base, out_bf16, bs):
+    """Ragged query blocks and token tiles, a pos_base offset, bf16 output, a paged cache."""
+    log(f"prefill 64 heads S={S} pos_base={pos_base} bf16={out_bf16} bs={bs}")
+    rows = np.unique(np.r_[0, 1, S - 1, np.linspace(0, S - 1, 7).astype(int)])
+    _prefill_glm_check(S, pos_base, 110 + S, out_bf16, rows, [0, 5, 31, 63], bs=bs)
+
+
+def test_prefill_full_4096_sampled_rows():
+    """S = T = 4096 (the benchmark configuration), rows at block edges and spread out."""
+    S = 4096
+    log("prefill S=T=4096")
+    rows = np.array([0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095])
+    _prefill_glm_check(S, 0, 4, False, rows, [0, 21, 42, 63])
+
+
 # ------------------------------------------------------------------------------ end to end
 def test_dsa_decode_step_end_to_end_small():
     """index -> top-k -> absorbed decode over the selected keys, at a size with T > k."""
