@@ -170,7 +170,10 @@ constexpr int PA_ROW = 536;    // bf16 per staged key row: K (256) then V (256),
 constexpr size_t PA_LDS = (size_t)2 * PA_BK * PA_ROW * 2;   // two tiles
 
 
-// grid (ceil(S / 128), H), 256 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
+// grid (ceil(S / 128) * H), 256 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
+// Workgroups go to the 8 XCDs round-robin (id % 8); XCD x runs heads x, x + 8, .. one after the
+// other, each as all of its query blocks at once (late ones first), so the head's K and V (4 MB
+// at 4096 tokens) are fetched into that XCD's L2 once and shared by its 32 CUs.
 template <int NOPE, typename OUT>
 __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C, KvView kv,
                                                int S, int pos_base, float scale_log2, OUT *__restrict__ out)
@@ -182,9 +185,10 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
     constexpr int N = PF_H * (NOPE + PF_V);    // row length of C
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
-    const int nqb = gridDim.x;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // late query blocks (most keys) first
-    const int h = blockIdx.y;
+    const int nqb = (S + PA_BQ - 1) / PA_BQ;
+    const int xcd = (int)blockIdx.x & 7, idx = (int)blockIdx.x >> 3;
+    const int h = xcd + 8 * (idx / nqb);
+    const int qb = nqb - 1 - idx % nqb;        // late query blocks (most keys) first
     const int i0 = qb * PA_BQ;
     const int iq = i0 + 32 * wave + l32;       // this lane's query
     const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
@@ -267,7 +271,12 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
                 mx = fmaxf(mx, v);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
+        // the reference maximum moves only when the tile's maximum exceeds it by more than 8
+        // (log2 units): until then P = exp2(s - m_run) stays below 2^8, which bf16 P and the
+        // fp32 sums hold exactly as well, and the accumulators need no rescaling (the final
+        // normalization divides by the sum taken against the same reference)
+        const bool move = mx > m_run + 8.f;
+        const float m_new = move ? mx : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt
         uint2 pk[2][4];
@@ -291,10 +300,12 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(move)) {   // wave-uniform: lanes that keep theirs scale by 1
 #pragma unroll
-        for (int dt = 0; dt < PF_V / 32; ++dt)
+            for (int dt = 0; dt < PF_V / 32; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
         // O^T += V^T P^T over four 16-key steps: step kb covers keys 16 kb .. +15 (tile kb/2,
         // groups g = 2 (kb%2), +1).  Lane l needs keys 8 hi .. 8 hi + 7 of the step for query l32;
         // it holds keys 4 hi + 0..3 (group g) and 8 + 4 hi + 0..3 (group g + 1): one swap of the
@@ -370,7 +381,7 @@ static mla_status launch_attn(const void *q, const bf16_t *C, const KvView &kv, 
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         attr = true;
     }
-    const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ), PF_H);
+    const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ * PF_H));
     hipLaunchKernelGGL((pf_attn<NOPE, OUT>), g, dim3(256), PA_LDS, s, (const bf16_t *)q, C, kv, S, pos_base, scale_log2,
                        (OUT *)out);
     return check_launch("pf_attn");
