@@ -82,7 +82,8 @@ def bench_dsa_decode(args):
     g.manual_seed(1003)
     for c in range(args.copies):
         if c == 0:
-            lc, rc, ic = bf(d.lc), bf(d.rc), torch.from_numpy(d.ic).to(dev)
+            # the indexer pool in the 64-row tiled layout (same rows; the indexer's fast layout)
+            lc, rc, ic = bf(d.lc), bf(d.rc), torch.from_numpy(synth.tile_index_keys(d.ic)).to(dev)
             qn, qr, kvb = bf(d.q_nope), bf(d.q_rope), bf(d.kv_b)
             qi, wi = torch.from_numpy(d.q_idx).to(dev), torch.from_numpy(d.w_idx).to(dev)
         else:
@@ -91,7 +92,7 @@ def bench_dsa_decode(args):
             qn, qr, kvb = rn(B, H, NOPE).bfloat16(), rn(B, H, ROPE).bfloat16(), rn(H * (NOPE + V), L, std=0.02).bfloat16()
             qi, wi = rn(B, N_IH, HD), rn(B, N_IH)
         seq_len = torch.full((B,), T, dtype=torch.int32, device=dev)
-        kv = mla.KvCache(lc, rc, ic, seq_len=seq_len, max_seq_len=T, seq_stride=T)
+        kv = mla.KvCache(lc, rc, ic, seq_len=seq_len, max_seq_len=T, seq_stride=T, ic_layout=mla.MLA_IC_TILE64)
         copies.append(dict(kv=kv, qn=qn, qr=qr, kvb=kvb, qi=qi, wi=wi, seq_len=seq_len,
                            pos=torch.full((B,), T - 1, dtype=torch.int32, device=dev),
                            scores=torch.empty((B, T), dtype=torch.float32, device=dev),
@@ -267,7 +268,8 @@ def bench_dsa_decode(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "dsa_decode_T131072_B1", "T": T, "B": B, "heads": H, "qk_nope": NOPE,
                    "qk_rope": ROPE, "v_head": V, "kv_lora": L, "index_heads": N_IH, "index_hd": HD,
-                   "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "input_copies": args.copies,
+                   "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "index_layout": "tile64",
+                   "input_copies": args.copies,
                    "hip_graphs": bool(graphs), "steps_per_graph_replay": len(copies) if graphs else 0},
         "roofline": {"kernel": "index_scores_mfma (dsa_index_scores; the step runs the same kernel with the "
                                "selection histogram added, inside dsa_index_select)",

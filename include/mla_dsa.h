@@ -63,7 +63,16 @@ typedef struct {
  *   contiguous (block_table == NULL): b*seq_stride + t
  * seq_len[b] (device int32) counts the cached tokens of sequence b INCLUDING the current
  * query's own token: a decode query sits at position seq_len[b]-1 and sees keys
- * 0..seq_len[b]-1.  Rows outside [0, rows) are never touched. */
+ * 0..seq_len[b]-1.  Rows outside [0, rows) are never touched.
+ * ic_layout places the indexer rows in their pool (the same 4 * index_hd bytes per token):
+ *   MLA_IC_ROWS   element d of row r at ic[r*index_hd + d]
+ *   MLA_IC_TILE64 rows in aligned groups of 64 stored dims-major in quads of 4:
+ *                 element d of row r at ic[(r/64)*64*index_hd + (d/4)*256 + (r%64)*4 + d%4]
+ *                 (a 64-row group is one contiguous 64*index_hd*4-byte tile).  Needs rows
+ *                 a multiple of 64, and block_size (paged) or seq_stride (contiguous,
+ *                 B > 1) a multiple of 64.  One lane per key then reads its key's four
+ *                 dims from 1 KB contiguous per instruction: the indexer's fast layout. */
+typedef enum { MLA_IC_ROWS = 0, MLA_IC_TILE64 = 1 } mla_ic_layout;
 typedef struct {
     const void *lc;
     const void *rc;
@@ -77,6 +86,7 @@ typedef struct {
     int64_t seq_stride;       /* rows between consecutive sequences (contiguous)        */
     const int32_t *seq_len;   /* device [B]                                             */
     int64_t max_seq_len;      /* host bound: every seq_len[b] <= max_seq_len            */
+    int32_t ic_layout;        /* mla_ic_layout of the ic pool                           */
 } mla_kv_view;
 
 /* ---------------------------------------------------------------------------------

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmla_dsa.so")
 
 MLA_OK, MLA_ERR_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_FP32, MLA_BF16 = 0, 1
+MLA_IC_ROWS, MLA_IC_TILE64 = 0, 1
 
 EXPORTED = (
     "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
@@ -52,7 +53,7 @@ class mla_kv_view(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("kv_dtype", ctypes.c_int), ("index_hd", ctypes.c_int32),
                 ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32), ("seq_stride", ctypes.c_int64),
-                ("seq_len", ctypes.c_void_p), ("max_seq_len", ctypes.c_int64)]
+                ("seq_len", ctypes.c_void_p), ("max_seq_len", ctypes.c_int64), ("ic_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -160,10 +161,12 @@ class KvCache:
     lc: [rows, kv_lora] and rc: [rows, qk_rope] (float32 or bfloat16); ic: [rows, index_hd]
     float32 or None.  Contiguous layout: token t of sequence b is row b*seq_stride + t.
     Paged layout: block_table int32 [B, max_blocks], row = block_table[b, t//bs]*bs + t%bs.
-    seq_len: int32 [B] on the GPU (tokens cached including the query's own)."""
+    seq_len: int32 [B] on the GPU (tokens cached including the query's own).
+    ic_layout: MLA_IC_ROWS (ic row-major) or MLA_IC_TILE64 (ic holds the same rows in aligned
+    64-row tiles, dims-major in quads of 4; see synth.tile_index_keys)."""
 
     def __init__(self, lc, rc, ic=None, *, seq_len=None, max_seq_len: int, block_table=None,
-                 block_size: int = 0, seq_stride: int = 0):
+                 block_size: int = 0, seq_stride: int = 0, ic_layout: int = 0):
         _dev(lc, rc, ic, seq_len, block_table)
         _contig(lc, rc, ic, seq_len, block_table)
         if seq_len is not None and seq_len.dtype != torch.int32:
@@ -185,6 +188,7 @@ class KvCache:
         v.seq_stride = seq_stride
         v.seq_len = seq_len.data_ptr() if seq_len is not None else None
         v.max_seq_len = max_seq_len
+        v.ic_layout = ic_layout
         for t in (rc, ic):
             if t is not None and t.shape[0] != lc.shape[0]:
                 raise ValueError("lc, rc and ic must have the same number of rows")

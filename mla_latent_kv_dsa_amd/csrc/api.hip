@@ -49,6 +49,15 @@ static mla_status check_view(const mla_kv_view *kv, int32_t B, bool need_lc_rc, 
     if (need_seq_len && !kv->seq_len) return fail(MLA_ERR_ARG, "kv->seq_len is NULL");
     if (kv->max_seq_len < 0) return fail(MLA_ERR_ARG, "kv->max_seq_len negative");
     if (kv->max_seq_len >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "kv->max_seq_len >= 2^31");
+    if (kv->ic_layout != MLA_IC_ROWS && kv->ic_layout != MLA_IC_TILE64) return fail(MLA_ERR_ARG, "kv->ic_layout invalid");
+    if (kv->ic_layout == MLA_IC_TILE64 && kv->ic) {
+        if (kv->rows % 64 != 0) return fail(MLA_ERR_ARG, "tiled indexer pool: rows must be a multiple of 64");
+        if (kv->index_hd % 4 != 0) return fail(MLA_ERR_ARG, "tiled indexer pool: index_hd must be a multiple of 4");
+        if (kv->block_table && kv->block_size % 64 != 0)
+            return fail(MLA_ERR_ARG, "tiled indexer pool: block_size must be a multiple of 64");
+        if (!kv->block_table && B > 1 && kv->seq_stride % 64 != 0)
+            return fail(MLA_ERR_ARG, "tiled indexer pool: seq_stride must be a multiple of 64");
+    }
     if (kv->block_table) {
         if (kv->block_size <= 0 || kv->max_blocks <= 0)
             return fail(MLA_ERR_ARG, "paged view needs block_size > 0 and max_blocks > 0");

@@ -48,6 +48,7 @@ struct KvView {
     int64_t seq_stride;
     const int32_t *seq_len;
     int64_t max_seq_len;
+    int32_t ic_tiled;   // indexer pool in 64-row tiles (MLA_IC_TILE64)
 };
 
 inline KvView to_view(const mla_kv_view &v)
@@ -63,7 +64,14 @@ inline KvView to_view(const mla_kv_view &v)
     k.seq_stride = v.seq_stride;
     k.seq_len = v.seq_len;
     k.max_seq_len = v.max_seq_len;
+    k.ic_tiled = v.ic_layout == MLA_IC_TILE64;
     return k;
+}
+
+// Dims 4g .. 4g+3 of indexer row `row` (hd dims per row), in either pool layout.
+__device__ __forceinline__ const float *ic_quad(const KvView &v, int64_t row, int g, int hd)
+{
+    return v.ic_tiled ? v.ic + ((row >> 6) * (hd >> 2) + g) * 256 + (row & 63) * 4 : v.ic + row * hd + 4 * g;
 }
 
 // Pool row of logical token t of sequence b, or -1 if it falls outside the pools.

@@ -33,11 +33,10 @@ __global__ __launch_bounds__(256) void index_scores_lane_per_key(const float *__
         out[t] = -INFINITY;
         return;
     }
-    const float4 *kp = reinterpret_cast<const float4 *>(kv.ic + row * HD);
     float k[HD];
 #pragma unroll
     for (int i = 0; i < HD / 4; ++i) {
-        const float4 v = kp[i];
+        const float4 v = *reinterpret_cast<const float4 *>(ic_quad(kv, row, i, HD));
         k[4 * i + 0] = v.x;
         k[4 * i + 1] = v.y;
         k[4 * i + 2] = v.z;
@@ -88,13 +87,12 @@ __global__ __launch_bounds__(256) void index_scores_generic(const float *__restr
         out[t] = -INFINITY;
         return;
     }
-    const float *k = kv.ic + row * hd;
     const float *qb = q + (int64_t)b * n_ih * hd;
     const float *wb = w + (int64_t)b * n_ih;
     float s = 0.0f;
     for (int h = 0; h < n_ih; ++h) {
         float a = 0.f;
-        for (int d = 0; d < hd; ++d) a = __builtin_fmaf(qb[h * hd + d], k[d], a);
+        for (int d = 0; d < hd; ++d) a = __builtin_fmaf(qb[h * hd + d], ic_quad(kv, row, d >> 2, hd)[d & 3], a);
         s = __builtin_fmaf(wb[h], a > 0.f ? a : 0.f, s);
     }
     out[t] = s;
@@ -120,15 +118,17 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 constexpr int IXM_WAVES = 4;
 constexpr int IXM_QROW = 128 + 4;    // floats per query row in LDS (pad against bank conflicts)
 
-// Row pointer of key (tile * 64 + lane) for lane-private loads.  A key with no score (past
-// the sequence or outside the pools) reads the query block instead (any readable 512 B will
-// do), so that every load is unconditional; its lane's result is replaced by -inf.
+// Pointer for the lane-private loads of key (tile * 64 + lane).  A key with no score (past the
+// sequence or outside the pools) reads from `dummy` instead (any readable range of the right
+// size), so that every load is unconditional; its lane's result is replaced by -inf.
 //   MODE 0: contiguous rows (no block table);
 //   MODE 1: block table with block_size % 64 == 0 -- the whole tile sits in one block, so the
 //           table entry is wave-uniform and is fetched with a scalar load, which leaves the
 //           vector-memory counter (and the key stream waiting on it) alone;
-//   MODE 2: any block size, one table lookup per lane.
-template <int MODE>
+//   MODE 2: any block size, one table lookup per lane (row layout only).
+// Row layout: the key's 512-byte row.  TILED (64-row tiles, 128 dims): the lane's first quad in
+// its tile, tile + 4 lane; the tile holds all 64 keys in dims-major quads.
+template <int MODE, bool TILED>
 __device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int64_t tile, int lane, int64_t n,
                                                    const float *dummy, bool &valid)
 {
@@ -144,15 +144,16 @@ __device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int6
         row = t < n ? kv_row(kv, b, t) : -1;
     }
     valid = t < n && row >= 0 && row < kv.rows;
+    if (TILED) return valid ? kv.ic + (row >> 6) * 64 * 128 + 4 * lane : dummy;
     return valid ? kv.ic + row * 128 : dummy;
 }
 
+template <bool TILED>
 __device__ __forceinline__ void ix_load_slice(v32f &dst, const float *p, int sl)
 {
-    const float4 *src = reinterpret_cast<const float4 *>(p + sl * 32);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float4 x = src[i];
+        const float4 x = *reinterpret_cast<const float4 *>(TILED ? p + (sl * 8 + i) * 256 : p + sl * 32 + 4 * i);
         dst[4 * i + 0] = x.x;
         dst[4 * i + 1] = x.y;
         dst[4 * i + 2] = x.z;
@@ -207,7 +208,7 @@ __device__ __forceinline__ float ix_fold(const v32f &acc, const float *__restric
 // block, added into ghist[b] with atomics at the end) -- the first pass of the top-k selection.
 constexpr int IX_BINS = 2048;
 
-template <int MODE, bool HIST>
+template <int MODE, bool HIST, bool TILED>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
                                                                      const float *__restrict__ w, KvView kv,
                                                                      int64_t t_max, float *__restrict__ scores,
@@ -245,30 +246,31 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
 
-    const float *qraw = q + (int64_t)b * 32 * 128;
+    // stand-in for keys without a row: the query block (512 B rows), or the pool's first tile
+    const float *qraw = TILED ? kv.ic + 4 * lane : q + (int64_t)b * 32 * 128;
     bool valid, valid_n = false;
-    const float *p = ix_key_ptr<MODE>(kv, b, tile, lane, n, qraw, valid);
+    const float *p = ix_key_ptr<MODE, TILED>(kv, b, tile, lane, n, qraw, valid);
     v32f KA, KB, acc;
-    ix_load_slice(KA, p, 0);
+    ix_load_slice<TILED>(KA, p, 0);
     __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
-    ix_load_slice(KB, p, 1);
+    ix_load_slice<TILED>(KB, p, 1);
     for (; tile < ntv; tile += waves_total) {
         // the next tile's first two slices are loaded unconditionally (from the query block
         // when there is no next tile) so every iteration leaves the same loads in flight
         const int64_t nxt = tile + waves_total;
         const float *pn = qraw;
         valid_n = false;
-        if (nxt < ntv) pn = ix_key_ptr<MODE>(kv, b, nxt, lane, n, qraw, valid_n);
+        if (nxt < ntv) pn = ix_key_ptr<MODE, TILED>(kv, b, nxt, lane, n, qraw, valid_n);
 #pragma unroll
         for (int r = 0; r < 32; ++r) acc[r] = 0.f;
         ix_slice(acc, KA, qrow, 0);
-        ix_load_slice(KA, p, 2);
+        ix_load_slice<TILED>(KA, p, 2);
         ix_slice(acc, KB, qrow, 1);
-        ix_load_slice(KB, p, 3);
+        ix_load_slice<TILED>(KB, p, 3);
         ix_slice(acc, KA, qrow, 2);
-        ix_load_slice(KA, pn, 0);
+        ix_load_slice<TILED>(KA, pn, 0);
         ix_slice(acc, KB, qrow, 3);
-        ix_load_slice(KB, pn, 1);
+        ix_load_slice<TILED>(KB, pn, 1);
         const float s = ix_fold(acc, wb);
         const int64_t t = tile * 64 + lane;
         const float sc = valid ? s : -INFINITY;
@@ -296,24 +298,34 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
     dim3 grid((unsigned)gx, (unsigned)B);
     const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv.ic)) & 15u) == 0;
     if (hd == 128 && n_ih == 32 && aligned) {
-        // about 3 resident waves per SIMD over the chip; each wave strides over the tiles
         const int64_t ntiles = (t_max + 63) / 64;
-        int64_t bx = 768 / B;
-        if (bx < 1) bx = 1;
-        const int64_t need = (ntiles + IXM_WAVES - 1) / IXM_WAVES;
-        if (bx > need) bx = need;
+        const int mode = !kv.bt ? 0 : (kv.bs % 64 == 0 ? 1 : 2);
+        if (kv.ic_tiled && mode == 2) return fail(MLA_ERR_UNSUPPORTED, "index: tiled keys need block_size % 64 == 0");
+        int64_t bx;
+        if (kv.ic_tiled) {
+            // tiled keys: one workgroup per CU over the chip (one wave per SIMD), two tiles or more
+            // per wave, so that a wave requests its next tile while it finishes the current one
+            bx = (ntiles + 2 * IXM_WAVES - 1) / (2 * IXM_WAVES);
+            const int64_t cap = 256 / B > 1 ? 256 / B : 1;
+            if (bx > cap) bx = cap;
+        } else {
+            // row keys: about 3 resident waves per SIMD over the chip; each wave strides over the tiles
+            bx = 768 / B;
+            const int64_t need = (ntiles + IXM_WAVES - 1) / IXM_WAVES;
+            if (bx > need) bx = need;
+        }
         if (bx < 1) bx = 1;
         const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
-        const int mode = !kv.bt ? 0 : (kv.bs % 64 == 0 ? 1 : 2);
-        if (ghist) {
-            if (mode == 0) hipLaunchKernelGGL((index_scores_mfma<0, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
-            else if (mode == 1) hipLaunchKernelGGL((index_scores_mfma<1, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
-            else hipLaunchKernelGGL((index_scores_mfma<2, true>), g, blk, 0, s, q, w, kv, t_max, scores, ghist);
-            return check_launch("index_scores");
-        }
-        if (mode == 0) hipLaunchKernelGGL((index_scores_mfma<0, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
-        else if (mode == 1) hipLaunchKernelGGL((index_scores_mfma<1, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
-        else hipLaunchKernelGGL((index_scores_mfma<2, false>), g, blk, 0, s, q, w, kv, t_max, scores, nullptr);
+#define IX_LAUNCH(M, H, TL) hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, ghist)
+        const bool h = ghist != nullptr;
+        if (kv.ic_tiled) {
+            if (mode == 0) { if (h) IX_LAUNCH(0, true, true); else IX_LAUNCH(0, false, true); }
+            else { if (h) IX_LAUNCH(1, true, true); else IX_LAUNCH(1, false, true); }
+        } else if (mode == 0) { if (h) IX_LAUNCH(0, true, false); else IX_LAUNCH(0, false, false); }
+        else if (mode == 1) { if (h) IX_LAUNCH(1, true, false); else IX_LAUNCH(1, false, false); }
+        else { if (h) IX_LAUNCH(2, true, false); else IX_LAUNCH(2, false, false); }
+#undef IX_LAUNCH
+        return check_launch("index_scores");
     } else if (hd == 128 && aligned)
         hipLaunchKernelGGL(index_scores_lane_per_key<128>, grid, dim3(256), 0, s, q, w, n_ih, kv, t_max, scores);
     else

@@ -41,6 +41,16 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def tile_index_keys(ic: np.ndarray) -> np.ndarray:
+    """The indexer pool [rows, hd] rearranged into the MLA_IC_TILE64 layout: rows in aligned
+    groups of 64, each group stored dims-major in quads of 4 (element d of row r at flat index
+    (r // 64) * 64 * hd + (d // 4) * 256 + (r % 64) * 4 + d % 4).  Same values, same shape."""
+    rows, hd = ic.shape
+    assert rows % 64 == 0 and hd % 4 == 0
+    t = ic.reshape(rows // 64, 64, hd // 4, 4).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(rows, hd)
+
+
 def _normal(rng, shape, std=1.0, chunk=1 << 26) -> np.ndarray:
     """N(0, std^2) float32 draws, generated in chunks to bound peak memory."""
     n = int(np.prod(shape))

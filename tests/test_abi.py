@@ -260,3 +260,15 @@ def test_dsa_decode_validation(L):
     assert f(out=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
     assert f(scores=None, ws=FAKE, wsb=need) == mla.MLA_ERR_ARG
     assert f(B=0) == mla.MLA_OK
+
+
+def test_tiled_index_pool_validation(L):
+    _no_gpu()
+
+    def f(v):
+        return L.dsa_index_scores(FAKE, FAKE, 2, 32, ctypes.byref(v), 4096, FAKE, None)
+    assert f(_view(ic_layout=2)) == mla.MLA_ERR_ARG
+    assert f(_view(ic_layout=mla.MLA_IC_TILE64, rows=4100)) == mla.MLA_ERR_ARG          # rows % 64
+    assert f(_view(ic_layout=mla.MLA_IC_TILE64, rows=2 * 4160, seq_stride=4100)) == mla.MLA_ERR_ARG   # stride % 64
+    bt = ctypes.c_void_p(0x5000)
+    assert f(_view(ic_layout=mla.MLA_IC_TILE64, block_table=bt.value, block_size=16, max_blocks=256)) == mla.MLA_ERR_ARG

@@ -26,13 +26,18 @@ import mla_latent_kv_dsa_amd as mla  # noqa: E402
 TOL_F32, TOL_BF16 = 2e-3, 1e-2
 
 
-def _kv(lc, rc, ic=None, seq_len=None, max_seq_len=0, block_table=None, block_size=0, seq_stride=0, bf16=True):
+def _kv(lc, rc, ic=None, seq_len=None, max_seq_len=0, block_table=None, block_size=0, seq_stride=0, bf16=True,
+        tiled=False):
+    """tiled: hand the indexer pool over in the 64-row tiled layout (same rows)."""
     to = dev_bf16 if bf16 else dev
+    if ic is not None and tiled:
+        ic = synth.tile_index_keys(ic)
     return mla.KvCache(to(lc), to(rc), dev(ic) if ic is not None else None,
                        seq_len=dev(np.asarray(seq_len, np.int32)) if seq_len is not None else None,
                        max_seq_len=max_seq_len,
                        block_table=dev(block_table) if block_table is not None else None,
-                       block_size=block_size, seq_stride=seq_stride)
+                       block_size=block_size, seq_stride=seq_stride,
+                       ic_layout=mla.MLA_IC_TILE64 if tiled else mla.MLA_IC_ROWS)
 
 
 # ------------------------------------------------------------------------------ RoPE
@@ -84,7 +89,7 @@ def test_rope_strided_view_and_odd_geometry():
 
 
 # ------------------------------------------------------------------------------ indexer
-def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed, bs=64, hole=False):
+def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed, bs=64, hole=False, tiled=False):
     """Random indexer problem.  Returns q, w, the view, and per sequence the logical key rows
     plus a mask of keys that have a row (a block-table hole leaves a gap of -1 entries)."""
     rng = np.random.default_rng(seed)
@@ -111,7 +116,7 @@ def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed, bs=64, hole=False):
             masks.append(m)
         kvd = dict(block_table=bt, block_size=bs)
     else:
-        stride = t_max
+        stride = (t_max + 63) // 64 * 64 if tiled else t_max
         ic = rng.standard_normal((B * stride, hd)).astype(np.float32)
         logical = [ic[b * stride: b * stride + seq_len[b]] for b in range(B)]
         masks = [np.ones(seq_len[b], bool) for b in range(B)]
@@ -120,7 +125,7 @@ def _index_case(B, seq_len, t_max, n_ih, hd, paged, seed, bs=64, hole=False):
     w = rng.standard_normal((B, n_ih)).astype(np.float32)
     lc = np.zeros((ic.shape[0], 8), np.uint16)
     rc = np.zeros((ic.shape[0], 8), np.uint16)
-    kv = _kv(lc, rc, ic, seq_len, t_max, **kvd)
+    kv = _kv(lc, rc, ic, seq_len, t_max, tiled=tiled, **kvd)
     return q, w, kv, logical, masks
 
 
@@ -140,6 +145,19 @@ def test_index_scores_bit_exact(paged, n_ih, hd):
     seq_len = [1100, 777, 1]
     log(f"index paged={paged} n_ih={n_ih} hd={hd}")
     q, w, kv, logical, masks = _index_case(B, seq_len, t_max, n_ih, hd, paged, 200 + n_ih + paged)
+    _index_check(q, w, kv, logical, masks, seq_len, t_max)
+
+
+@pytest.mark.parametrize("paged,bs,hole", [(False, 0, False), (True, 64, True), (True, 128, False)])
+@pytest.mark.parametrize("n_ih,hd", [(32, 128), (7, 128), (5, 64)])
+def test_index_scores_tiled_layout(paged, bs, hole, n_ih, hd):
+    """The 64-row tiled indexer pool gives the same bits as rows (matrix-core, lane-per-key and
+    generic kernels; contiguous and paged with a hole)."""
+    B, t_max = 3, 1100
+    seq_len = [1100, 777, 1]
+    log(f"index tiled paged={paged} bs={bs} n_ih={n_ih} hd={hd}")
+    q, w, kv, logical, masks = _index_case(B, seq_len, t_max, n_ih, hd, paged, 230 + n_ih + bs, bs=bs or 64,
+                                           hole=hole, tiled=True)
     _index_check(q, w, kv, logical, masks, seq_len, t_max)
 
 
@@ -187,10 +205,11 @@ def _select_check(q, w, kv, t_max, k, seq_len, logical=None, masks=None):
     return host(sel), host(nsel)
 
 
-def test_index_select_full_context_131072():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_index_select_full_context_131072(tiled):
     d = synth.decode(3, 131072, dsa=True, bf16=True)
-    log("index+select T=131072 k=2048")
-    kv = _kv(d.lc, d.rc, d.ic, [d.T], d.T, seq_stride=d.T)
+    log(f"index+select T=131072 k=2048 tiled={tiled}")
+    kv = _kv(d.lc, d.rc, d.ic, [d.T], d.T, seq_stride=d.T, tiled=tiled)
     _select_check(d.q_idx, d.w_idx, kv, d.T, 2048, [d.T])
 
 
@@ -544,11 +563,12 @@ def _dsa_step_check(d, kv, seq_len, t_max, k, theta=10000.0, oracle_rows=()):
     return host(out), host(sel), host(nsel)
 
 
-def test_dsa_decode_call_full_context_131072():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_dsa_decode_call_full_context_131072(tiled):
     T, k = 131072, 2048
     d = synth.decode(3, T, dsa=True)
-    log("mla_dsa_decode T=131072 k=2048")
-    kv = _kv(d.lc, d.rc, d.ic, [T], T, seq_stride=T)
+    log(f"mla_dsa_decode T=131072 k=2048 tiled={tiled}")
+    kv = _kv(d.lc, d.rc, d.ic, [T], T, seq_stride=T, tiled=tiled)
     _dsa_step_check(d, kv, [T], T, k, oracle_rows=(0,))
 
 
