@@ -4,8 +4,10 @@
 // the query, q_abs[b][h][:] = W_UK[h]^T q_nope[b][h], with W_UK[h] the first qk_nope rows of
 // head h's block of kv_b.
 //
-// Workgroup (cb, h), 256 threads, covers columns 128 cb .. 128 cb + 127 of head h for queries
-// 0..B-1.  Thread t: row group rg = t/16 (rows rg, rg+16, ...) and column group cg = t%16 (8 of
+// Job (cb, h), 256 threads, covers columns 128 cb .. 128 cb + 127 of head h for queries 0..B-1.
+// A workgroup may run several jobs side by side (tid = thread index inside the job, sh_abs = the
+// job's own LDS); they then pass the same barriers, since every job loops over the same B.
+// Thread t: row group rg = t/16 (rows rg, rg+16, ...) and column group cg = t%16 (8 of
 // the 128 columns).  The W_UK rows go out first, then the queries of head h are staged in LDS
 // (sh_abs: B * qk_nope + 4 * AB_QB * 128 floats), so both latencies overlap.  Queries are
 // handled eight at a time; row-group partial sums are reduced with lane shuffles inside a
@@ -21,10 +23,10 @@ constexpr int AB_QB = 8;
 template <int NR>   // qk_nope / 16
 __device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, const bf16_t *__restrict__ kv_b,
                                              int B, int v, bf16_t *__restrict__ q_abs, int cb, int h,
-                                             float *__restrict__ sh_abs)
+                                             float *__restrict__ sh_abs, int tid)
 {
     constexpr int nope = 16 * NR;
-    const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15, lane = tid & 63, wave = tid >> 6;
+    const int rg = tid >> 4, cg = tid & 15, lane = tid & 63, wave = tid >> 6;
     const int cbase = cb * 128;
     const bf16_t *W = kv_b + ((int64_t)h * (nope + v) + rg) * AB_L + cbase + cg * 8;
     uint4 w[NR];

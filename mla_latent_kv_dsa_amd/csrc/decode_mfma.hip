@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nop
                                                 int B, int v, bf16_t *__restrict__ q_abs)
 {
     extern __shared__ float sh_abs[];   // q [B][nope] fp32, then partials [4][AB_QB][128]
-    absorb_block<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs);
+    absorb_block<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs, threadIdx.x);
 }
 
 // ------------------------------------------------------------------------------ attention core

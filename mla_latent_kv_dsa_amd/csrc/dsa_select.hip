@@ -5,18 +5,16 @@
 // position ascending (-0.0 equals +0.0), kept positions in ascending order, nsel = min(k, n).
 //
 // Launches (all rows of the batch together):
-//   1. sel_zero     clears the row histograms and counters of the workspace
+//   1. sel_zero     clears the row histograms and candidate counters of the workspace
 //   2. indexer      writes the scores and, in the same pass, a histogram of the top 11
 //                   order-key bits of every score of a key t < n (per workgroup in LDS, then
 //                   added into the row histogram with atomics)
 //   3. sel_filter   grid (t_max / 1024, B): finds the threshold bin from the row histogram,
-//                   counts its keys above the bin and appends its keys inside the bin to the
-//                   row's candidate list
+//                   writes the row bitmask words of its keys above the bin and appends its keys
+//                   inside the bin to the row's candidate list
 //   4. sel_resolve  grid (B): the exact k-th key (two radix passes over the candidates'
-//                   remaining 21 bits) and the output offset of every filter workgroup
-//   5. sel_emit     grid (t_max / 1024, B): every workgroup re-reads its scores, keeps the
-//                   keys above the k-th key and the leading keys equal to it (position order),
-//                   and writes their positions at its offset -- ascending across the row
+//                   remaining 21 bits), the kept candidates' bits, ties resolved in position
+//                   order, and the kept positions written out of the bitmask in ascending order
 // Rows longer than SEL_TMAX positions take the general top-k (three launches, any length).
 #include "common.h"
 #include "absorb_body.h"
@@ -25,7 +23,7 @@ namespace mla {
 
 constexpr int SEL_BINS = 2048;             // top 11 key bits
 constexpr int SEL_CH = 1024;               // positions per filter workgroup
-constexpr int SEL_TMAX = 262144;           // longest row the LDS-resident final step handles
+constexpr int SEL_TMAX = 262144;           // longest row whose bitmasks the resolve step holds in LDS
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row shifts inside rows of 16
 // lanes, then row broadcasts of lanes 15 and 31), no LDS traffic.
@@ -110,190 +108,36 @@ mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, cons
 
 // ------------------------------------------------------------------------------ 3. filter
 // 256 threads; thread t of workgroup c handles positions c*1024 + 256 j + t (j = 0..3), so the
-// ballot of wave w for step j covers the 64 consecutive positions c*1024 + 256 j + 64 w ...
-// Every workgroup finds the threshold bin tb from the row histogram, counts its keys above the
-// bin and appends its keys inside the bin to the row's candidate list.
-constexpr int SEL_MAXCH = SEL_TMAX / SEL_CH;   // workgroups per row (256)
-constexpr int SEL_CPT = 16;                    // candidates per thread held in registers
+// ballot of wave w for step j covers the 64 consecutive positions c*1024 + 256 j + 64 w ..., the
+// word 16 c + 4 j + w of the row's bitmask.  Every workgroup finds the threshold bin tb from the
+// row histogram, writes the bitmask words of its keys above the bin and appends its keys inside
+// the bin to the row's candidate list.
+constexpr int SEL_CPT = 8;                     // candidates per thread held in registers
+constexpr int SR_NT = 512, SR_NW = SR_NT / 64; // threads / waves of the resolve workgroup
+constexpr int SR_WPT = 8;                      // bitmask words per resolve thread (SEL_TMAX)
+constexpr int SR_STATIC = SEL_BINS * 4 + 256;  // static LDS of the resolve workgroup (bytes)
+constexpr int SR_DYN_MAX = 160 * 1024 - SR_STATIC;
 
 struct SelRow {           // per-row results of the filter (uint32 words)
-    uint32_t tb, kth, remaining, pad;
+    uint32_t tb, above, pad0, pad1;
 };
 
-// One workgroup of 256 threads per row b: resolves the exact k-th key of the row among its
-// candidates and the output offset of every filter workgroup.
-__device__ __forceinline__ void resolve_row(int b, KvView kv, int nch, int k, const uint2 *__restrict__ cand,
-                                            int64_t cap, const uint32_t *__restrict__ cnt,
-                                            const uint32_t *__restrict__ blkabove, uint32_t *__restrict__ outpfx,
-                                            uint32_t *__restrict__ eqpfx, SelRow *__restrict__ row_out)
+// words per row bitmask: ceil(t_max / 64) rounded up to a multiple of SR_NT
+__host__ __device__ inline int sel_words(int64_t t_max)
 {
-    constexpr int NW = 4;
-    __shared__ uint32_t h[SEL_BINS];
-    __shared__ uint32_t gtc[SEL_MAXCH], eqc[SEL_MAXCH];
-    __shared__ uint32_t sh[NW];
-    __shared__ uint32_t s_bc[2];
-    const int tid = threadIdx.x;
-    if (seq_len_of(kv, b) <= k) return;
-    const SelRow rin = row_out[b];   // tb and the count above its bin, from the filter
-    uint32_t E = cnt[b];
-    // issued before anything waits: the filter workgroups' counts above the bin, and the first
-    // 256 * SEL_CPT candidates (thread t holds t + 256 i), as unconditional loads clamped into
-    // the buffers and masked on use
-    const uint32_t above_blk = blkabove[(int64_t)b * SEL_MAXCH + (tid < nch ? tid : 0)];
-    const uint2 *cb = cand + (int64_t)b * cap;
-    uint2 cr[SEL_CPT];
-#pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i) {
-        const int64_t j = tid + 256 * i;
-        cr[i] = cb[j < cap ? j : cap - 1];
-    }
-    const uint32_t tb = rin.tb, above_total = rin.kth;
-    if (E > cap) E = (uint32_t)cap;
-    // every candidate once: those held in registers, then the rest from memory in batches of
-    // eight independent loads per thread
-    auto for_each = [&](auto f) {
-#pragma unroll
-        for (int i = 0; i < SEL_CPT; ++i)
-            if (tid + 256u * i < E) f(cr[i]);
-        for (uint32_t base = 256u * SEL_CPT; base < E; base += 2048u) {
-            uint2 t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t j = base + tid + 256u * i;
-                t[i] = cb[j < E ? j : E - 1u];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (base + tid + 256u * i < E) f(t[i]);
-        }
-    };
-    // radix select of the need-th largest key: digits of bits 20..10, then 9..0
-    uint32_t prefix = tb << 21, mask = 0xFFE00000u, remaining = (uint32_t)k - above_total;   // >= 1
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int shift = p == 0 ? 10 : 0;
-        const int nb = p == 0 ? 2048 : 1024;
-        const uint32_t dm = (uint32_t)nb - 1u;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) h[tid + 256 * q] = 0u;
-        __syncthreads();
-        const uint32_t pf = prefix, mk = mask;
-        for_each([&](uint2 c) {
-            if ((c.x & mk) == pf) atomicAdd(&h[(c.x >> shift) & dm], 1u);
-        });
-        __syncthreads();
-        const int per = nb / 256;   // 8 or 4 bins per thread, thread order = descending bins
-        const int top = nb - 1 - per * tid;
-        uint32_t hv[8], local = 0u;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            hv[q] = q < per ? h[top - q] : 0u;
-            local += hv[q];
-        }
-        const uint32_t before = block_excl_scan_dpp<NW>(local, sh);
-        if (before < remaining && before + local >= remaining) {
-            uint32_t cum = before;
-            int bin = top;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (q < per && cum + hv[q] >= remaining) {
-                    bin = top - q;
-                    break;
-                }
-                cum += hv[q];
-            }
-            s_bc[0] = remaining - cum;
-            s_bc[1] = prefix | ((uint32_t)bin << shift);
-        }
-        __syncthreads();
-        remaining = s_bc[0];
-        prefix = s_bc[1];
-        mask |= dm << shift;
-    }
-    const uint32_t kth = prefix;
-    // per workgroup: candidates above the k-th key, and equal to it
-    gtc[tid] = 0u;
-    eqc[tid] = 0u;
-    __syncthreads();
-    for_each([&](uint2 c) {
-        if (c.x > kth) atomicAdd(&gtc[c.y / SEL_CH], 1u);
-        else if (c.x == kth) atomicAdd(&eqc[c.y / SEL_CH], 1u);
-    });
-    __syncthreads();
-    // thread t = workgroup t: keys equal to the k-th one are taken in position order, i.e. in
-    // workgroup order
-    const uint32_t ec = tid < nch ? eqc[tid] : 0u;
-    const uint32_t epf = block_excl_scan_dpp<NW>(ec, sh);
-    uint32_t take = remaining > epf ? remaining - epf : 0u;
-    if (take > ec) take = ec;
-    const uint32_t kept = tid < nch ? above_blk + gtc[tid] + take : 0u;
-    const uint32_t opf = block_excl_scan_dpp<NW>(kept, sh);
-    if (tid < nch) {
-        outpfx[(int64_t)b * SEL_MAXCH + tid] = opf;
-        eqpfx[(int64_t)b * SEL_MAXCH + tid] = epf;
-    }
-    if (tid == 0) {
-        SelRow r;
-        r.tb = tb;
-        r.kth = kth;
-        r.remaining = remaining;
-        r.pad = 0u;
-        row_out[b] = r;
-    }
-}
-
-// grid (B), 256 threads
-__global__ __launch_bounds__(256) void sel_resolve(KvView kv, int nch, int k, const uint2 *__restrict__ cand,
-                                                   int64_t cap, const uint32_t *__restrict__ cnt,
-                                                   const uint32_t *__restrict__ blkabove, uint32_t *__restrict__ outpfx,
-                                                   uint32_t *__restrict__ eqpfx, SelRow *__restrict__ row_out)
-{
-    resolve_row(blockIdx.x, kv, nch, k, cand, cap, cnt, blkabove, outpfx, eqpfx, row_out);
-}
-
-// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
-// work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
-// rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
-// grid (nres + 4 * 64): workgroups nres.. are absorb workgroup (cb, h) = (a % 4, a / 4); the
-// cb == 0 one of head h also rotates that head's query tails.
-template <int NR>
-__global__ __launch_bounds__(256) void sel_resolve_absorb(KvView kv, int nch, int k, const uint2 *__restrict__ cand,
-                                                          int64_t cap, const uint32_t *__restrict__ cnt,
-                                                          const uint32_t *__restrict__ blkabove,
-                                                          uint32_t *__restrict__ outpfx, uint32_t *__restrict__ eqpfx,
-                                                          SelRow *__restrict__ row_out, int nres, SideAbsorb sa)
-{
-    extern __shared__ float sh_abs[];
-    if ((int)blockIdx.x < nres) {
-        resolve_row(blockIdx.x, kv, nch, k, cand, cap, cnt, blkabove, outpfx, eqpfx, row_out);
-        return;
-    }
-    const int a = blockIdx.x - nres, cb = a & 3, h = a >> 2;
-    absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, sh_abs);
-    if (cb != 0) return;
-    const int half = sa.rope / 2;
-    for (int p = threadIdx.x; p < sa.B * half; p += 256) {
-        const int b = p / half, j = p - b * half;
-        const bf16_t *x = sa.q_rope + ((int64_t)b * AB_H + h) * sa.rope;
-        bf16_t *y = sa.q_rope_out + ((int64_t)b * AB_H + h) * sa.rope;
-        const int64_t sl = seq_len_of(kv, b);
-        float lo, hi;
-        rope_pair(bf2f(x[2 * j]), bf2f(x[2 * j + 1]), j, sa.rope, (double)(sl > 0 ? sl - 1 : 0), sa.theta, lo, hi);
-        y[j] = f2bf(lo);
-        y[half + j] = f2bf(hi);
-    }
+    return (int)(((t_max + 63) / 64 + SR_NT - 1) / SR_NT * SR_NT);
 }
 
 __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scores, int64_t t_max, KvView kv, int k,
                                                   const uint32_t *__restrict__ ghist, uint2 *__restrict__ cand,
-                                                  int64_t cap, uint32_t *__restrict__ cnt,
-                                                  uint32_t *__restrict__ blkabove, SelRow *__restrict__ rows)
+                                                  int64_t cap, uint32_t *__restrict__ cnt, uint64_t *__restrict__ gkeep,
+                                                  int wp, SelRow *__restrict__ rows)
 {
     constexpr int NW = 4;
     __shared__ uint32_t tot[SEL_BINS];
     __shared__ uint32_t sh[NW];
     __shared__ uint32_t s_tb, s_above, s_base;
-    __shared__ uint32_t s_wcnt[NW], s_wab[NW];
+    __shared__ uint32_t s_wcnt[NW];
     const int b = blockIdx.y, c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = seq_len_of(kv, b);
@@ -339,27 +183,25 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
     }
     __syncthreads();
     const uint32_t tb = s_tb;
-    // classify
+    // classify: the words of keys above the bin go straight to the row bitmask
     uint64_t cm[SEL_CH / 256];
-    uint32_t wtot = 0u, wab = 0u;
+    uint32_t wtot = 0u;
+    uint64_t *kw = gkeep + (int64_t)b * wp + 16 * c + wave;
 #pragma unroll
     for (int j = 0; j < SEL_CH / 256; ++j) {
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         const uint32_t kb = key[j] >> 21;
         const bool ok = t < n;
-        wab += (uint32_t)__popcll(__ballot(ok && kb > tb));
+        const uint64_t am = __ballot(ok && kb > tb);
+        if (lane == 0) kw[4 * j] = am;
         cm[j] = __ballot(ok && kb == tb);
         wtot += (uint32_t)__popcll(cm[j]);
     }
-    if (lane == 0) {
-        s_wcnt[wave] = wtot;
-        s_wab[wave] = wab;
-    }
+    if (lane == 0) s_wcnt[wave] = wtot;
     __syncthreads();
     if (tid == 0) {
         const uint32_t all = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
         s_base = all ? atomicAdd(&cnt[b], all) : 0u;
-        blkabove[(int64_t)b * SEL_MAXCH + c] = s_wab[0] + s_wab[1] + s_wab[2] + s_wab[3];
     }
     __syncthreads();
     uint32_t off = s_base;
@@ -375,99 +217,234 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
         off += (uint32_t)__popcll(cm[j]);
     }
     if (c == 0 && tid == 0) {
-        SelRow r;   // threshold bin and the count above it (sel_resolve replaces the row)
+        SelRow r;   // threshold bin and the count of keys above it
         r.tb = tb;
-        r.kth = s_above;
-        r.remaining = 0u;
-        r.pad = 0u;
+        r.above = s_above;
+        r.pad0 = r.pad1 = 0u;
         rows[b] = r;
     }
 }
 
-// ------------------------------------------------------------------------------ 4. emit
-// grid (max(nch, 1), B), 256 threads, same position mapping as the filter.  Rows with n <= k keep
-// every position; otherwise a position is kept when its key lies above the k-th key, or equals
-// it and ranks (in position order, across the row) below the number of equal keys still needed.
-// Kept positions are written at the workgroup's output offset plus their rank in the workgroup.
-__global__ __launch_bounds__(256) void sel_emit(const float *__restrict__ scores, int64_t t_max, KvView kv, int k,
-                                                const uint32_t *__restrict__ outpfx, const uint32_t *__restrict__ eqpfx,
-                                                const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
-                                                int32_t *__restrict__ nsel)
+// ------------------------------------------------------------------------------ 4. resolve + emit
+// One workgroup of SR_NT threads per row b:
+//   - the exact k-th key among the candidates (two radix digits, bits 20..10 and 9..0)
+//   - candidates above it set their bit in the row bitmask (held in LDS), candidates equal to it
+//     their bit in an eq bitmask
+//   - thread t owns the bitmask words [t wpt, (t+1) wpt), a run of positions: the first
+//     `remaining` eq bits in position order join the kept bits (block scan of eq popcounts), a
+//     block scan of the kept popcounts gives every thread its output offset, and the set bits are
+//     written out as positions -- ascending across the row.
+// dyn: keep[wp], eq[wp] (uint64).
+__device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k, const uint2 *__restrict__ cand,
+                                                 int64_t cap, const uint32_t *__restrict__ cnt,
+                                                 const uint64_t *__restrict__ gkeep, int wp,
+                                                 const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
+                                                 int32_t *__restrict__ nsel, uint64_t *__restrict__ dyn)
 {
-    __shared__ uint32_t s_eq[SEL_CH / 64], s_kp[SEL_CH / 64];   // per (step, wave), position order
-    const int b = blockIdx.y, c = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ uint32_t h[SEL_BINS];
+    __shared__ uint32_t sh[SR_NW];
+    __shared__ uint32_t s_bc[2];
+    const int tid = threadIdx.x;
     const int64_t n = seq_len_of(kv, b);
     int32_t *out = sel + (int64_t)b * k;
-    if (n <= k) {
-        for (int64_t base = (int64_t)c * SEL_CH; base < k; base += (int64_t)gridDim.x * SEL_CH) {
-#pragma unroll
-            for (int j = 0; j < SEL_CH / 256; ++j) {
-                const int64_t u = base + 256 * j + tid;
-                if (u < k) out[u] = u < n ? (int32_t)u : -1;
-            }
-        }
-        if (c == 0 && tid == 0) nsel[b] = (int32_t)n;
+    if (n <= k) {   // every position is kept
+        for (int u = tid; u < k; u += SR_NT) out[u] = u < n ? u : -1;
+        if (tid == 0) nsel[b] = (int32_t)n;
         return;
     }
-    const SelRow r = rows[b];
-    const uint32_t opf = outpfx[(int64_t)b * SEL_MAXCH + c], epf = eqpfx[(int64_t)b * SEL_MAXCH + c];
-    const float *row = scores + (int64_t)b * t_max;
-    bool gt[SEL_CH / 256], eq[SEL_CH / 256];
-    float sv[SEL_CH / 256];
+    // issued before anything waits: the row's threshold, candidate count, bitmask words and the
+    // first SR_NT * SEL_CPT candidates (thread t holds t + SR_NT i), as unconditional loads clamped
+    // into the buffers and masked on use
+    const SelRow rin = rows[b];
+    uint32_t E = cnt[b];
+    const int wpt = wp / SR_NT;
+    const int nw = (int)((n + 63) / 64);   // words that hold positions < n
+    const uint64_t *gk = gkeep + (int64_t)b * wp + tid * wpt;
+    uint64_t kw[SR_WPT];
 #pragma unroll
-    for (int j = 0; j < SEL_CH / 256; ++j) {   // n > k >= 1 here; loads clamped into the row
-        const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
-        sv[j] = row[t < n ? t : n - 1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < SR_WPT; ++i) kw[i] = gk[i < wpt ? i : 0];
+    const uint2 *cb = cand + (int64_t)b * cap;
+    uint2 cr[SEL_CPT];
 #pragma unroll
-    for (int j = 0; j < SEL_CH / 256; ++j) {
-        const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
-        const uint32_t key = t < n ? order_key(sv[j]) : 0u;
-        const uint32_t kb = key >> 21;
-        gt[j] = t < n && (kb > r.tb || (kb == r.tb && key > r.kth));
-        eq[j] = t < n && key == r.kth;
+    for (int i = 0; i < SEL_CPT; ++i) {
+        const int64_t j = tid + SR_NT * i;
+        cr[i] = cb[j < cap ? j : cap - 1];
     }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    // ranks among the equal keys of the workgroup, in position order
-    uint64_t em[SEL_CH / 256];
+    uint64_t *keep = dyn, *eqm = dyn + wp;
+    for (int i = tid; i < wp; i += SR_NT) eqm[i] = 0ull;
+    const uint32_t tb = rin.tb, above_total = rin.above;
+    if (E > cap) E = (uint32_t)cap;
+    // every candidate once: those held in registers, then the rest from memory in batches of
+    // eight independent loads per thread
+    auto for_each = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < SEL_CH / 256; ++j) {
-        em[j] = __ballot(eq[j]);
-        if (lane == 0) s_eq[4 * j + wave] = (uint32_t)__popcll(em[j]);
+        for (int i = 0; i < SEL_CPT; ++i)
+            if (tid + (uint32_t)SR_NT * i < E) f(cr[i]);
+        for (uint32_t base = (uint32_t)SR_NT * SEL_CPT; base < E; base += 8u * SR_NT) {
+            uint2 t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t j = base + tid + (uint32_t)SR_NT * i;
+                t[i] = cb[j < E ? j : E - 1u];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (base + tid + (uint32_t)SR_NT * i < E) f(t[i]);
+        }
+    };
+    // radix select of the need-th largest key: digits of bits 20..10, then 9..0
+    uint32_t prefix = tb << 21, mask = 0xFFE00000u, remaining = (uint32_t)k - above_total;   // >= 1
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int shift = p == 0 ? 10 : 0;
+        const int nb = p == 0 ? 2048 : 1024;
+        const uint32_t dm = (uint32_t)nb - 1u;
+#pragma unroll
+        for (int q = 0; q < SEL_BINS / SR_NT; ++q) h[tid + SR_NT * q] = 0u;
+        __syncthreads();
+        const uint32_t pf = prefix, mk = mask;
+        for_each([&](uint2 c) {
+            if ((c.x & mk) == pf) atomicAdd(&h[(c.x >> shift) & dm], 1u);
+        });
+        __syncthreads();
+        const int per = nb / SR_NT;   // 4 or 2 bins per thread, thread order = descending bins
+        const int top = nb - 1 - per * tid;
+        uint32_t hv[4], local = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hv[q] = q < per ? h[top - q] : 0u;
+            local += hv[q];
+        }
+        const uint32_t before = block_excl_scan_dpp<SR_NW>(local, sh);
+        if (before < remaining && before + local >= remaining) {
+            uint32_t cum = before;
+            int bin = top;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < per && cum + hv[q] >= remaining) {
+                    bin = top - q;
+                    break;
+                }
+                cum += hv[q];
+            }
+            s_bc[0] = remaining - cum;
+            s_bc[1] = prefix | ((uint32_t)bin << shift);
+        }
+        __syncthreads();
+        remaining = s_bc[0];
+        prefix = s_bc[1];
+        mask |= dm << shift;
     }
+    const uint32_t kth = prefix;
+    // the filter's bitmask of keys above the threshold bin, then the candidates' bits
+#pragma unroll
+    for (int i = 0; i < SR_WPT; ++i)
+        if (i < wpt) keep[tid * wpt + i] = tid * wpt + i < nw ? kw[i] : 0ull;
     __syncthreads();
-    uint64_t km[SEL_CH / 256];
-    bool kp[SEL_CH / 256];
-#pragma unroll
-    for (int j = 0; j < SEL_CH / 256; ++j) {
-        uint32_t before = 0u;
-        for (int i = 0; i < 4 * j + wave; ++i) before += s_eq[i];
-        const uint32_t erank = epf + before + (uint32_t)__popcll(em[j] & below);
-        kp[j] = gt[j] || (eq[j] && erank < r.remaining);
-        km[j] = __ballot(kp[j]);
-        if (lane == 0) s_kp[4 * j + wave] = (uint32_t)__popcll(km[j]);
-    }
+    for_each([&](uint2 c) {
+        if (c.x > kth) atomicOr(reinterpret_cast<unsigned long long *>(&keep[c.y >> 6]), 1ull << (c.y & 63));
+        else if (c.x == kth) atomicOr(reinterpret_cast<unsigned long long *>(&eqm[c.y >> 6]), 1ull << (c.y & 63));
+    });
     __syncthreads();
+    uint64_t ew[SR_WPT];
+    uint32_t ec = 0u;
 #pragma unroll
-    for (int j = 0; j < SEL_CH / 256; ++j) {
-        if (kp[j]) {
-            uint32_t before = 0u;
-            for (int i = 0; i < 4 * j + wave; ++i) before += s_kp[i];
-            const uint32_t o = opf + before + (uint32_t)__popcll(km[j] & below);
-            if (o < (uint32_t)k) out[o] = (int32_t)((int64_t)c * SEL_CH + 256 * j + tid);
+    for (int i = 0; i < SR_WPT; ++i) {
+        kw[i] = i < wpt ? keep[tid * wpt + i] : 0ull;
+        ew[i] = i < wpt ? eqm[tid * wpt + i] : 0ull;
+        ec += (uint32_t)__popcll(ew[i]);
+    }
+    uint32_t erank = block_excl_scan_dpp<SR_NW>(ec, sh);   // equal keys before this run
+    uint32_t kc = 0u;
+#pragma unroll
+    for (int i = 0; i < SR_WPT; ++i) {
+        uint64_t e = ew[i];
+        const uint32_t c = (uint32_t)__popcll(e);
+        if (erank >= remaining) e = 0ull;
+        else if (erank + c > remaining) {   // only the first remaining - erank of them
+            uint64_t take = 0ull;
+            for (uint32_t m = remaining - erank; m; --m) {
+                const uint64_t low = e & (~e + 1ull);
+                take |= low;
+                e ^= low;
+            }
+            e = take;
+        }
+        erank += c;
+        kw[i] |= e;
+        kc += (uint32_t)__popcll(kw[i]);
+    }
+    uint32_t o = block_excl_scan_dpp<SR_NW>(kc, sh);
+#pragma unroll
+    for (int i = 0; i < SR_WPT; ++i) {
+        uint64_t x = kw[i];
+        const int base = 64 * (tid * wpt + i);
+        while (x) {
+            const int bit = __builtin_ctzll(x);
+            x &= x - 1ull;
+            if (o < (uint32_t)k) out[o] = base + bit;
+            ++o;
         }
     }
-    if (c == 0 && tid == 0) nsel[b] = k;
+    if (tid == 0) nsel[b] = k;
+}
+
+// grid (B), SR_NT threads, dynamic LDS 16 wp bytes
+__global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uint2 *__restrict__ cand, int64_t cap,
+                                                     const uint32_t *__restrict__ cnt,
+                                                     const uint64_t *__restrict__ gkeep, int wp,
+                                                     const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
+                                                     int32_t *__restrict__ nsel)
+{
+    extern __shared__ uint64_t sr_dyn[];
+    resolve_emit_row(blockIdx.x, kv, k, cand, cap, cnt, gkeep, wp, rows, sel, nsel, sr_dyn);
+}
+
+// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
+// work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
+// rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
+// grid (nres + 2 * 64): workgroups nres.. run two absorb jobs a = 2 (blockIdx - nres) + half,
+// (cb, h) = (a % 4, a / 4), one per 256 threads; the cb == 0 job of head h also rotates that
+// head's query tails.
+template <int NR>
+__global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
+                                                            int64_t cap, const uint32_t *__restrict__ cnt,
+                                                            const uint64_t *__restrict__ gkeep, int wp,
+                                                            const SelRow *__restrict__ rows,
+                                                            int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
+                                                            int nres, SideAbsorb sa)
+{
+    extern __shared__ uint64_t sr_dyn[];
+    if ((int)blockIdx.x < nres) {
+        resolve_emit_row(blockIdx.x, kv, k, cand, cap, cnt, gkeep, wp, rows, sel, nsel, sr_dyn);
+        return;
+    }
+    const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
+    const int a = 2 * ((int)blockIdx.x - nres) + half, cb = a & 3, h = a >> 2;
+    float *shj = reinterpret_cast<float *>(sr_dyn) + half * (sa.B * 16 * NR + 4 * AB_QB * 128);
+    absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, shj, jt);
+    if (cb != 0) return;
+    const int hr = sa.rope / 2;
+    for (int p = jt; p < sa.B * hr; p += 256) {
+        const int b = p / hr, j = p - b * hr;
+        const bf16_t *x = sa.q_rope + ((int64_t)b * AB_H + h) * sa.rope;
+        bf16_t *y = sa.q_rope_out + ((int64_t)b * AB_H + h) * sa.rope;
+        const int64_t sl = seq_len_of(kv, b);
+        float lo, hi;
+        rope_pair(bf2f(x[2 * j]), bf2f(x[2 * j + 1]), j, sa.rope, (double)(sl > 0 ? sl - 1 : 0), sa.theta, lo, hi);
+        y[j] = f2bf(lo);
+        y[hr + j] = f2bf(hi);
+    }
 }
 
 // ------------------------------------------------------------------------------ host side
 struct SelWs {
-    uint32_t *ghist, *cnt, *blkabove, *outpfx, *eqpfx;
+    uint32_t *ghist, *cnt;
     SelRow *rows;
+    uint64_t *keep;
     uint2 *cand;
     int64_t nch, cap;
+    int wp;
 };
 
 static size_t sal(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -477,6 +454,7 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
     SelWs w;
     w.nch = (t_max + SEL_CH - 1) / SEL_CH;
     w.cap = w.nch * SEL_CH;
+    w.wp = sel_words(t_max);
     char *p = reinterpret_cast<char *>(ws);
     size_t off = 0;
     auto take = [&](size_t sz) {
@@ -486,10 +464,8 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
     };
     w.ghist = reinterpret_cast<uint32_t *>(take((size_t)B * SEL_BINS * 4));
     w.cnt = reinterpret_cast<uint32_t *>(take((size_t)B * 4));
-    w.blkabove = reinterpret_cast<uint32_t *>(take((size_t)B * SEL_MAXCH * 4));
-    w.outpfx = reinterpret_cast<uint32_t *>(take((size_t)B * SEL_MAXCH * 4));
-    w.eqpfx = reinterpret_cast<uint32_t *>(take((size_t)B * SEL_MAXCH * 4));
     w.rows = reinterpret_cast<SelRow *>(take((size_t)B * sizeof(SelRow)));
+    w.keep = reinterpret_cast<uint64_t *>(take((size_t)B * w.wp * 8));
     w.cand = reinterpret_cast<uint2 *>(take((size_t)B * w.cap * 8));
     if (bytes) *bytes = off;
     return w;
@@ -497,10 +473,27 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
 
 size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k)
 {
+    if (t_max > SEL_TMAX) return topk_workspace_bytes(B, t_max, k);
     size_t fast = 0;
     sel_ws(nullptr, B, t_max, &fast);
-    const size_t general = topk_workspace_bytes(B, t_max, k);
-    return t_max <= SEL_TMAX ? fast : general;
+    return fast;
+}
+
+static mla_status enable_sel_lds()
+{
+    static bool done = false;
+    if (!done) {
+        const void *f[4] = {reinterpret_cast<const void *>(&sel_resolve),
+                            reinterpret_cast<const void *>(&sel_resolve_absorb<8>),
+                            reinterpret_cast<const void *>(&sel_resolve_absorb<12>),
+                            reinterpret_cast<const void *>(&sel_resolve_absorb<16>)};
+        for (int i = 0; i < 4; ++i) {
+            const hipError_t e = hipFuncSetAttribute(f[i], hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+            if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+        }
+        done = true;
+    }
+    return MLA_OK;
 }
 
 mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
@@ -516,48 +509,42 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
         if (st) return st;
         return launch_topk(scores, B, t_max, kv.seq_len, kv.max_seq_len, k, sel, nsel, ws, ws_bytes, s);
     }
-    const SelWs sw = sel_ws(ws, B, t_max, nullptr);
-    hipLaunchKernelGGL(sel_zero, dim3(B), dim3(256), 0, s, sw.ghist, sw.cnt);
-    st = check_launch("sel_zero");
+    st = enable_sel_lds();
     if (st) return st;
-    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
-                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
-    const int nres = t_max > 0 ? B : 0;
+    const SelWs sw = sel_ws(ws, B, t_max, nullptr);
     if (t_max > 0) {
+        hipLaunchKernelGGL(sel_zero, dim3(B), dim3(256), 0, s, sw.ghist, sw.cnt);
+        st = check_launch("sel_zero");
+        if (st) return st;
         st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, sw.ghist, s);
         if (st) return st;
         hipLaunchKernelGGL(sel_filter, dim3((unsigned)sw.nch, B), dim3(256), 0, s, scores, t_max, kv, k, sw.ghist,
-                           sw.cand, sw.cap, sw.cnt, sw.blkabove, sw.rows);
+                           sw.cand, sw.cap, sw.cnt, sw.keep, sw.wp, sw.rows);
         st = check_launch("sel_filter");
         if (st) return st;
-        if (!with_side) {
-            hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(256), 0, s, kv, (int)sw.nch, k, sw.cand, sw.cap, sw.cnt,
-                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows);
-            st = check_launch("sel_resolve");
-            if (st) return st;
-        }
     }
-    if (with_side) {
-        const dim3 g((unsigned)(nres + 4 * AB_H));
-        const size_t shm = (size_t)B * side->nope * 4 + 4 * AB_QB * 128 * 4;
-        const int nch = (int)sw.nch;
-        if (side->nope == 128)
-            hipLaunchKernelGGL(sel_resolve_absorb<8>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
-                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
-        else if (side->nope == 192)
-            hipLaunchKernelGGL(sel_resolve_absorb<12>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
-                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
-        else
-            hipLaunchKernelGGL(sel_resolve_absorb<16>, g, dim3(256), shm, s, kv, nch, k, sw.cand, sw.cap, sw.cnt,
-                               sw.blkabove, sw.outpfx, sw.eqpfx, sw.rows, nres, *side);
-        st = check_launch("sel_resolve_absorb");
-        if (st) return st;
-        if (side_done) *side_done = true;
+    const size_t dyn_sel = (size_t)sw.wp * 16;
+    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
+                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
+    if (!with_side) {
+        hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.cap, sw.cnt, sw.keep,
+                           sw.wp, sw.rows, sel, nsel);
+        return check_launch("sel_resolve");
     }
-    const unsigned ge = sw.nch > 0 ? (unsigned)sw.nch : 1u;
-    hipLaunchKernelGGL(sel_emit, dim3(ge, B), dim3(256), 0, s, scores, t_max, kv, k, sw.outpfx, sw.eqpfx, sw.rows, sel,
-                       nsel);
-    return check_launch("sel_emit");
+    const size_t dyn_abs = 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
+    const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
+    const dim3 g((unsigned)(B + 2 * AB_H));
+#define SRA_LAUNCH(NR)                                                                                            \
+    hipLaunchKernelGGL(sel_resolve_absorb<NR>, g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.cap, sw.cnt, sw.keep, \
+                       sw.wp, sw.rows, sel, nsel, B, *side)
+    if (side->nope == 128) SRA_LAUNCH(8);
+    else if (side->nope == 192) SRA_LAUNCH(12);
+    else SRA_LAUNCH(16);
+#undef SRA_LAUNCH
+    st = check_launch("sel_resolve_absorb");
+    if (st) return st;
+    if (side_done) *side_done = true;
+    return MLA_OK;
 }
 
 }  // namespace mla
