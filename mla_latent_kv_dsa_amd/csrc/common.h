@@ -114,6 +114,11 @@ __device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim,
 
 // ------------------------------------------------------------------ selection keys
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0.0 maps like +0.0.
+// Row histogram of the top 11 order-key bits used by the key selection: HIST_COPIES partial
+// copies per row ([B][HIST_COPIES][HIST_BINS] uint32), one per XCD (workgroup id % 8), so that the
+// atomics of workgroups on different XCDs do not meet on the same words; readers sum the copies.
+constexpr int HIST_BINS = 2048, HIST_COPIES = 8;
+
 __device__ __forceinline__ uint32_t order_key(float f)
 {
     uint32_t u = __float_as_uint(f);

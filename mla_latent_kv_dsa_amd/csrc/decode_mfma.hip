@@ -9,7 +9,9 @@
 //   dec_core         per (key split, group of 16 heads): scores S = q_abs . Lc + q_rope . Rc on
 //                    v_mfma_f32_16x16x32_bf16, an online softmax over the split's keys in 64-key
 //                    chunks, and O = sum_j P_j Lc[t_j] on the same instruction; the split's O,
-//                    running maximum and sum are written as partials
+//                    running maximum and sum are written as partials.  When the chip has CUs
+//                    to spare, an extra slice of workgroups reads W_UV meanwhile (into an LDS
+//                    sink), so that the next launch finds it in the Infinity Cache.
 //   combine_unabsorb clat = sum_s f_s O_s / sum_s f_s l_s with f_s = exp2(m_s - max m), then
 //                    out[b][h][:] = W_UV[h] clat on v_mfma_f32_16x16x32_bf16
 // Each split keeps its own maximum, so the splits need no common pass before the values.
@@ -118,13 +120,35 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
                  : "memory");
 }
 
+// grid (NS, 4, B + pf): slice z == B (present when pf = 1) only reads W_UV (wuv = row 0 of
+// head 0's W_UV block, rph rows per head block, v W_UV rows per head): workgroup (x, y) takes
+// rows 128 x .. 128 x + 127 of the 16 v rows of heads 16 y .. 16 y + 15.
+// ONE: every split fits in one staged chunk (kps <= DC_SUP * DC_KC); the chunk's selection entries
+// are then requested before the query operands, so resolving them into cache rows waits for
+// nothing else (loads complete in issue order).
+template <bool ONE>
 __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs, const bf16_t *__restrict__ q_rope,
                                                 KvView kv, const int32_t *__restrict__ sel,
                                                 const int32_t *__restrict__ nsel, int sel_stride, float scale_log2,
                                                 int kps, float *__restrict__ o_part, float *__restrict__ m_part,
-                                                float *__restrict__ l_part)
+                                                float *__restrict__ l_part, int B, const bf16_t *__restrict__ wuv,
+                                                int rph, int v)
 {
     extern __shared__ __attribute__((aligned(16))) char dc_smem[];
+    if ((int)blockIdx.z == B) {
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), ln = threadIdx.x & 63;
+        const int rows = 16 * v, lr0 = 128 * (int)blockIdx.x + 32 * wv;
+        if (lr0 < rows) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const int lr = lr0 + i < rows ? lr0 + i : rows - 1;
+                const int hh = 16 * (int)blockIdx.y + lr / v;
+                lds_dma16(wuv + ((int64_t)hh * rph + lr % v) * DM_L + 8 * ln, lds_addr(dc_smem + 1024 * wv));
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may outlive the workgroup's LDS
+        return;
+    }
     char *sL = dc_smem;
     bf16_t *sP = reinterpret_cast<bf16_t *>(dc_smem + DC_SUP * DC_KC * DC_ROWB);
     float *sMx = reinterpret_cast<float *>(sP + 16 * DC_PROW);   // [wave][head] chunk maxima
@@ -137,6 +161,15 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
     const bf16_t *qa = q_abs + ((int64_t)b * DM_H + h) * DM_L + 8 * quad;
     const bf16_t *qr = q_rope + ((int64_t)b * DM_H + h) * DM_R + 8 * quad;
     const bf16_t *dummy = q_abs + ((int64_t)b * DM_H + h0) * DM_L + 8 * lane;   // any readable 1 KB
+    const int64_t k0 = (int64_t)s * kps;
+    int32_t t_first[DC_SUP];
+    if (ONE) {
+#pragma unroll
+        for (int u = 0; u < DC_SUP; ++u) {
+            const int64_t j = k0 + 64 * u + 16 * wave + jj;
+            t_first[u] = sel ? sel[(int64_t)b * sel_stride + (j < sel_stride ? j : sel_stride - 1)] : (int32_t)j;
+        }
+    }
     uint4 Bq[18];
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) Bq[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
@@ -144,7 +177,6 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
     for (int ks = 0; ks < 2; ++ks) Bq[16 + ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
     const int64_t sl = seq_len_of(kv, b);
     const int64_t nk = dec_nkeys(kv, b, sel, nsel, sel_stride);
-    const int64_t k0 = (int64_t)s * kps;
     const int64_t k1 = k0 + kps < nk ? k0 + kps : nk;
     const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc);
     const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
@@ -163,7 +195,8 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
         for (int u = 0; u < DC_SUP; ++u) {
             const int64_t j = c0 + 64 * u + 16 * wave + jj;
             int64_t t = j;
-            if (sel) t = sel[(int64_t)b * sel_stride + (j < sel_stride ? j : sel_stride - 1)];
+            if (ONE) t = t_first[u];
+            else if (sel) t = sel[(int64_t)b * sel_stride + (j < sel_stride ? j : sel_stride - 1)];
             row[u] = (j < k1 && t >= 0 && t < sl) ? kv_row(kv, b, t) : -1;
             const bf16_t *kr = row[u] >= 0 ? rc + row[u] * DM_R + 8 * quad : qr;
 #pragma unroll
@@ -247,6 +280,7 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
             }
         }
         __syncthreads();   // the staged rows are no longer read
+        if (ONE) break;
     }
     float *po = o_part + (((int64_t)b * NS + s) * DM_H + h0 + 4 * quad) * DM_L + 128 * wave + jj;
 #pragma unroll
@@ -400,6 +434,81 @@ __global__ __launch_bounds__(256) void combine_unabsorb(const float *__restrict_
     }
 }
 
+// ------------------------------------------------------------------------------ combine, one query
+// B = 1: grid (v / 128, H), 512 threads.  Waves 4..7 copy the workgroup's 128 W_UV rows of head h
+// (rows 128 bx ..) into LDS, 32 rows each, and only wait for them; waves 0..3 load the split
+// maxima and sums (lane = split) and the split partials of head h (thread t: columns 2t, 2t + 1
+// of every split), so their waits never include the W_UV copies (wait counts are per wave).
+// Wave 0 reduces the factors f_s as in combine_unabsorb, waves 0..3 form clat = sum_s f_s O_s
+// (split order) as bf16 in LDS, and then all eight waves contract 16 W_UV rows each with clat on
+// v_mfma_f32_16x16x32_bf16 (A rows other than 0 are never read into an output).
+constexpr int C1_ROWS = 128;
+constexpr size_t C1_LDS = (size_t)(C1_ROWS * CU_WROW + 16 * CU_ROW) * 2 + (size_t)CU_MAXNS * 4;
+
+template <int SB>   // splits held per thread, NS <= SB
+__global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_part, const float *__restrict__ m_part,
+                                                   const float *__restrict__ l_part, int NS,
+                                                   const bf16_t *__restrict__ kv_b, int nope, int v,
+                                                   float *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) char c1_smem[];
+    bf16_t *sW = reinterpret_cast<bf16_t *>(c1_smem);
+    bf16_t *sC = sW + C1_ROWS * CU_WROW;
+    float *sF = reinterpret_cast<float *>(sC + 16 * CU_ROW);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.y, jb = C1_ROWS * blockIdx.x;
+    if (wave >= 4) {
+        const int w4 = wave - 4;
+        const bf16_t *wsrc = kv_b + ((int64_t)h * (nope + v) + nope + jb + 32 * w4) * DM_L + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lds_dma16(wsrc + (int64_t)i * DM_L, lds_addr(sW + (32 * w4 + i) * CU_WROW));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies have landed
+        __syncthreads();
+        __syncthreads();
+    } else {
+        const int sc = lane < NS ? lane : NS - 1;
+        float m = 0.f, l = 0.f;
+        if (wave == 0) {
+            m = m_part[(int64_t)sc * DM_H + h];
+            l = l_part[(int64_t)sc * DM_H + h];
+        }
+        float2 x[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {   // unconditional loads, the split clamped into range
+            const int uc = u < NS ? u : NS - 1;
+            x[u] = *reinterpret_cast<const float2 *>(o_part + ((int64_t)uc * DM_H + h) * DM_L + 2 * tid);
+        }
+        if (wave == 0) {
+            const float mm = lane < NS ? m : -INFINITY;
+            const float M = wave_max_dpp(mm);
+            const float e = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - M);
+            const float L = wave_sum_dpp(e * (lane < NS ? l : 0.f));
+            sF[lane] = L > 0.f ? e / L : 0.f;
+        }
+        __syncthreads();
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {   // factors past the last split are zero
+            const float f = sF[u < CU_MAXNS ? u : CU_MAXNS - 1];
+            o0 = fmaf(f, x[u].x, o0);
+            o1 = fmaf(f, x[u].y, o1);
+        }
+        const bf16x2 c = {(__bf16)o0, (__bf16)o1};
+        *reinterpret_cast<uint32_t *>(&sC[2 * tid]) = __builtin_bit_cast(uint32_t, c);
+        __syncthreads();
+    }
+    const int r16 = lane & 15, q4 = lane >> 4;
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    const bf16_t *wl = sW + (16 * wave + r16) * CU_WROW + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(&sC[r16 * CU_ROW + 32 * ks + 8 * q4]);
+        const uint4 wq = *reinterpret_cast<const uint4 *>(wl + 32 * ks);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wq), d, 0, 0, 0);
+    }
+    if (q4 == 0) out[(int64_t)h * v + jb + 16 * wave + r16] = d[0];
+}
+
 // ------------------------------------------------------------------------------ host side
 bool decode_mfma_supported(const mla_dims &d, mla_dtype dt)
 {
@@ -436,14 +545,22 @@ static mla_status enable_big_lds()
 {
     static bool done = false;
     if (!done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<true>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<false>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
         const void *cu[4] = {reinterpret_cast<const void *>(&combine_unabsorb<1, 16>),
                              reinterpret_cast<const void *>(&combine_unabsorb<1, 32>),
                              reinterpret_cast<const void *>(&combine_unabsorb<1, 64>),
                              reinterpret_cast<const void *>(&combine_unabsorb<4, 16>)};
         for (int i = 0; i < 4 && e == hipSuccess; ++i)
             e = hipFuncSetAttribute(cu[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)CU_LDS);
+        const void *c1[3] = {reinterpret_cast<const void *>(&combine_one<16>),
+                             reinterpret_cast<const void *>(&combine_one<32>),
+                             reinterpret_cast<const void *>(&combine_one<64>)};
+        for (int i = 0; i < 3 && e == hipSuccess; ++i)
+            e = hipFuncSetAttribute(c1[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)C1_LDS);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
     }
@@ -526,13 +643,33 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     mla_status st = enable_big_lds();
     if (st) return st;
-    hipLaunchKernelGGL(dec_core, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv,
-                       sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
+    // the W_UV slice when the decode leaves at least as many CUs idle
+    const int pf = (int64_t)B * p.ns * (DM_H / 16) <= 128 ? 1 : 0;
+    const bf16_t *wuv = (const bf16_t *)kv_b + (int64_t)d.qk_nope * DM_L;
+    if (p.kps <= DC_SUP * DC_KC)
+        hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+    else
+        hipLaunchKernelGGL(dec_core<false>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
     st = check_launch("dec_core");
     if (st) return st;
     const dim3 gc(d.v_head / 64, DM_H, (B + 15) / 16);
     const bf16_t *kb = (const bf16_t *)kv_b;
-    if (B == 1 && p.ns <= 16)
+    if (B == 1 && d.v_head % C1_ROWS == 0) {
+        const dim3 g1(d.v_head / C1_ROWS, DM_H);
+        if (p.ns <= 16)
+            hipLaunchKernelGGL(combine_one<16>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
+                               d.qk_nope, d.v_head, out);
+        else if (p.ns <= 32)
+            hipLaunchKernelGGL(combine_one<32>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
+                               d.qk_nope, d.v_head, out);
+        else
+            hipLaunchKernelGGL(combine_one<64>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
+                               d.qk_nope, d.v_head, out);
+    } else if (B == 1 && p.ns <= 16)
         hipLaunchKernelGGL((combine_unabsorb<1, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
                            kb, B, d.qk_nope, d.v_head, out);
     else if (B == 1 && p.ns <= 32)

@@ -205,8 +205,9 @@ __device__ __forceinline__ float ix_fold(const v32f &acc, const float *__restric
 }
 
 // HIST: also count the top 11 order-key bits of every score with t < n (LDS histogram per
-// block, added into ghist[b] with atomics at the end) -- the first pass of the top-k selection.
-constexpr int IX_BINS = 2048;
+// block, added into the row's histogram copy blockIdx.x % HIST_COPIES with atomics at the end)
+// -- the first pass of the top-k selection.
+constexpr int IX_BINS = HIST_BINS;
 
 template <int MODE, bool HIST, bool TILED>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     }
     if (HIST) {
         __syncthreads();
-        uint32_t *gh = ghist + (int64_t)b * IX_BINS;
+        uint32_t *gh = ghist + ((int64_t)b * HIST_COPIES + blockIdx.x % HIST_COPIES) * IX_BINS;
         for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) {
             const uint32_t c = hs[i];
             if (c) atomicAdd(&gh[i], c);

@@ -21,7 +21,7 @@
 
 namespace mla {
 
-constexpr int SEL_BINS = 2048;             // top 11 key bits
+constexpr int SEL_BINS = HIST_BINS;        // top 11 key bits
 constexpr int SEL_CH = 1024;               // positions per filter workgroup
 constexpr int SEL_TMAX = 262144;           // longest row whose bitmasks the resolve step holds in LDS
 
@@ -62,7 +62,8 @@ __device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *sh
 __global__ __launch_bounds__(256) void sel_zero(uint32_t *__restrict__ ghist, uint32_t *__restrict__ cnt)
 {
     const int b = blockIdx.x;
-    for (int i = threadIdx.x; i < SEL_BINS; i += 256) ghist[(int64_t)b * SEL_BINS + i] = 0u;
+    uint4 *g = reinterpret_cast<uint4 *>(ghist + (int64_t)b * HIST_COPIES * SEL_BINS);
+    for (int i = threadIdx.x; i < HIST_COPIES * SEL_BINS / 4; i += 256) g[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) cnt[b] = 0u;
 }
 
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void sel_hist(const float *__restrict__ scores
     __syncthreads();
     for (int i = tid; i < SEL_BINS; i += 256) {
         const uint32_t c = hs[i];
-        if (c) atomicAdd(&ghist[(int64_t)b * SEL_BINS + i], c);
+        if (c) atomicAdd(&ghist[((int64_t)b * HIST_COPIES + blockIdx.x % HIST_COPIES) * SEL_BINS + i], c);
     }
 }
 
@@ -142,11 +143,16 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = seq_len_of(kv, b);
     if (n <= k) return;
-    // threshold bin: thread t owns the 8 bins [2040-8t, 2048-8t) (thread order = descending bins)
+    // threshold bin: thread t owns the 8 bins [2040-8t, 2048-8t) (thread order = descending bins),
+    // summed over the row's histogram copies
     const int lo_bin = SEL_BINS - 8 * (tid + 1);
-    const uint4 *hp = reinterpret_cast<const uint4 *>(ghist + (int64_t)b * SEL_BINS + lo_bin);
-    const uint4 x0 = hp[0], x1 = hp[1];
-    const uint32_t bin8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint4 *hp = reinterpret_cast<const uint4 *>(ghist + (int64_t)b * HIST_COPIES * SEL_BINS + lo_bin);
+    uint4 hx[2 * HIST_COPIES];
+#pragma unroll
+    for (int cp = 0; cp < HIST_COPIES; ++cp) {
+        hx[2 * cp] = hp[cp * SEL_BINS / 4];
+        hx[2 * cp + 1] = hp[cp * SEL_BINS / 4 + 1];
+    }
     // the scores of this workgroup's positions go out while the histogram is scanned
     const float *row = scores + (int64_t)b * t_max;
     uint32_t key[SEL_CH / 256];
@@ -156,7 +162,14 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         sv[j] = row[t < n ? t : n - 1];
     }
-    __builtin_amdgcn_sched_barrier(0);   // all four loads in flight together
+    __builtin_amdgcn_sched_barrier(0);   // all loads in flight together
+    uint32_t bin8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cp = 0; cp < HIST_COPIES; ++cp) {
+        const uint4 x0 = hx[2 * cp], x1 = hx[2 * cp + 1];
+        bin8[0] += x0.x; bin8[1] += x0.y; bin8[2] += x0.z; bin8[3] += x0.w;
+        bin8[4] += x1.x; bin8[5] += x1.y; bin8[6] += x1.z; bin8[7] += x1.w;
+    }
 #pragma unroll
     for (int j = 0; j < SEL_CH / 256; ++j) {
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
@@ -462,7 +475,7 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
         off += sal(sz);
         return q;
     };
-    w.ghist = reinterpret_cast<uint32_t *>(take((size_t)B * SEL_BINS * 4));
+    w.ghist = reinterpret_cast<uint32_t *>(take((size_t)B * HIST_COPIES * SEL_BINS * 4));
     w.cnt = reinterpret_cast<uint32_t *>(take((size_t)B * 4));
     w.rows = reinterpret_cast<SelRow *>(take((size_t)B * sizeof(SelRow)));
     w.keep = reinterpret_cast<uint64_t *>(take((size_t)B * w.wp * 8));
