@@ -114,10 +114,14 @@ __device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim,
 
 // ------------------------------------------------------------------ selection keys
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0.0 maps like +0.0.
-// Row histogram of the top 11 order-key bits used by the key selection: HIST_COPIES partial
-// copies per row ([B][HIST_COPIES][HIST_BINS] uint32), one per XCD (workgroup id % 8), so that the
-// atomics of workgroups on different XCDs do not meet on the same words; readers sum the copies.
-constexpr int HIST_BINS = 2048, HIST_COPIES = 8;
+// Histogram of the top 11 order-key bits used by the key selection, written without atomics:
+// every workgroup p of a producing kernel (the indexer, or the histogram kernel) writes the
+// nonzero bins of its own keys as a list: entry i of part p is hl[b][i][p] = (bin << 21) | count,
+// i < hcnt[b][p], in descending bin order (entry-major, so that entry i of consecutive parts is
+// contiguous for the reader).  The row histogram is the sum of its parts' lists.
+constexpr int HIST_BINS = 2048;
+constexpr int HL_CAP = HIST_BINS;          // entries per part (every bin nonzero at most)
+__device__ __forceinline__ uint32_t hl_entry(uint32_t bin, uint32_t count) { return (bin << 21) | count; }
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -141,6 +145,63 @@ __device__ __forceinline__ float wave_max(float x)
     return x;
 }
 
+// ------------------------------------------------------------------ scans (wave64)
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row shifts inside rows of 16
+// lanes, then row broadcasts of lanes 15 and 31), no LDS traffic.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Block-wide exclusive scan (NW waves) on DPP wave scans; sh needs NW words.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *sh, uint32_t *total = nullptr)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_scan_dpp(v);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t t = sh[w];
+        before += w < wave ? t : 0u;
+        all += t;
+    }
+    if (total) *total = all;
+    __syncthreads();
+    return before + inc - v;
+}
+
+// Writes the nonzero bins of the complete LDS histogram hs (HIST_BINS, every thread of an NT-thread
+// block calls it) as a list (descending bins; entry i at list[i * stride]) and its length `count`;
+// sh: NT / 64 words.
+template <int NT>
+__device__ __forceinline__ void hist_write_list(const uint32_t *hs, uint32_t *__restrict__ list, int64_t stride,
+                                                uint32_t *__restrict__ count, uint32_t *sh)
+{
+    constexpr int PER = HIST_BINS / NT;   // bins per thread, thread order = descending bins
+    const int top = HIST_BINS - 1 - PER * (int)threadIdx.x;
+    uint32_t c[PER], nz = 0u;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        c[q] = hs[top - q];
+        nz += c[q] ? 1u : 0u;
+    }
+    uint32_t total;
+    uint32_t off = block_excl_scan_dpp<NT / 64>(nz, sh, &total);
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (c[q]) list[(int64_t)(off++) * stride] = hl_entry((uint32_t)(top - q), c[q]);
+    if (threadIdx.x == 0) *count = total;
+}
+
 // ------------------------------------------------------------------ internal launchers
 mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, int64_t tok_stride,
                        int64_t head_stride, int32_t rope_off, int32_t rope_dim, const int32_t *pos,
@@ -148,12 +209,20 @@ mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, in
 mla_status launch_rope_decode(const void *x, void *y, mla_dtype dt, int32_t B, int32_t n_heads, int32_t rope_dim,
                               const KvView &kv, double theta, hipStream_t s);
 
-// ghist (optional): [B][2048] histogram of the top 11 order-key bits of the scores of keys
-// t < seq_len, accumulated with atomics (the caller zeroes it first)
+// hl, hcnt (optional): the histogram lists of the scores of keys t < seq_len (format above), one
+// part per workgroup of the launch; *parts receives the number of parts per row, at most
+// hist_parts_max(B, t_max).
+struct HistOut {
+    uint32_t *hl;     // [B][HL_CAP][parts_max]
+    uint32_t *hcnt;   // [B][parts_max]
+    int parts_max;    // row stride in parts
+    int parts;        // set by the launch
+};
+int hist_parts_max(int32_t B, int64_t t_max);
 mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd,
-                               const KvView &kv, int64_t t_max, float *scores, uint32_t *ghist, hipStream_t s);
+                               const KvView &kv, int64_t t_max, float *scores, HistOut *hist, hipStream_t s);
 
-mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, uint32_t *ghist,
+mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, HistOut *hist,
                              hipStream_t s);
 size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
 // Work that the fused decode step runs beside the select's resolve step (matrix-core decode

@@ -204,19 +204,21 @@ __device__ __forceinline__ float ix_fold(const v32f &acc, const float *__restric
     return s;
 }
 
-// HIST: also count the top 11 order-key bits of every score with t < n (LDS histogram per
-// block, added into the row's histogram copy blockIdx.x % HIST_COPIES with atomics at the end)
-// -- the first pass of the top-k selection.
+// HIST: also count the top 11 order-key bits of every score with t < n in an LDS histogram and
+// write its nonzero bins as this workgroup's list (part blockIdx.x of row b) -- the first pass of
+// the top-k selection.
 constexpr int IX_BINS = HIST_BINS;
 
 template <int MODE, bool HIST, bool TILED>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
                                                                      const float *__restrict__ w, KvView kv,
                                                                      int64_t t_max, float *__restrict__ scores,
-                                                                     uint32_t *__restrict__ ghist)
+                                                                     uint32_t *__restrict__ hl,
+                                                                     uint32_t *__restrict__ hcnt, int parts_max)
 {
     __shared__ float sq[32 * IXM_QROW];
     __shared__ uint32_t hs[HIST ? IX_BINS : 1];
+    __shared__ uint32_t sh_scan[IXM_WAVES];
     const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile math stays scalar
     const int64_t n = seq_len_of(kv, b) < t_max ? seq_len_of(kv, b) : t_max;
@@ -283,42 +285,64 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     }
     if (HIST) {
         __syncthreads();
-        uint32_t *gh = ghist + ((int64_t)b * HIST_COPIES + blockIdx.x % HIST_COPIES) * IX_BINS;
-        for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) {
-            const uint32_t c = hs[i];
-            if (c) atomicAdd(&gh[i], c);
-        }
+        hist_write_list<64 * IXM_WAVES>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max,
+                                        hcnt + (int64_t)b * parts_max + blockIdx.x, sh_scan);
     }
 }
 
+// workgroups per row of index_scores_mfma (the histogram parts of a row)
+static int64_t ixm_grid_x(int32_t B, int64_t t_max, bool tiled)
+{
+    const int64_t ntiles = (t_max + 63) / 64;
+    int64_t bx;
+    if (tiled) {
+        // tiled keys: one workgroup per CU over the chip (one wave per SIMD), two tiles or more
+        // per wave, so that a wave requests its next tile while it finishes the current one
+        bx = (ntiles + 2 * IXM_WAVES - 1) / (2 * IXM_WAVES);
+        const int64_t cap = 256 / B > 1 ? 256 / B : 1;
+        if (bx > cap) bx = cap;
+    } else {
+        // row keys: about 3 resident waves per SIMD over the chip; each wave strides over the tiles
+        bx = 768 / B;
+        const int64_t need = (ntiles + IXM_WAVES - 1) / IXM_WAVES;
+        if (bx > need) bx = need;
+    }
+    return bx < 1 ? 1 : bx;
+}
+
+int hist_parts_max(int32_t B, int64_t t_max)
+{
+    int64_t m = (t_max + 1023) / 1024;   // the histogram kernel: one part per 1024 positions
+    const int64_t a = ixm_grid_x(B, t_max, false), c = ixm_grid_x(B, t_max, true);
+    if (a > m) m = a;
+    if (c > m) m = c;
+    return (int)(m < 1 ? 1 : m);
+}
+
 mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd,
-                               const KvView &kv, int64_t t_max, float *scores, uint32_t *ghist, hipStream_t s)
+                               const KvView &kv, int64_t t_max, float *scores, HistOut *hist, hipStream_t s)
 {
     const int64_t gx = (t_max + 255) / 256;
     if (gx > 0x7fffffff || B > 65535) return fail(MLA_ERR_UNSUPPORTED, "index: grid too large");
     dim3 grid((unsigned)gx, (unsigned)B);
     const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv.ic)) & 15u) == 0;
     if (hd == 128 && n_ih == 32 && aligned) {
-        const int64_t ntiles = (t_max + 63) / 64;
         const int mode = !kv.bt ? 0 : (kv.bs % 64 == 0 ? 1 : 2);
         if (kv.ic_tiled && mode == 2) return fail(MLA_ERR_UNSUPPORTED, "index: tiled keys need block_size % 64 == 0");
-        int64_t bx;
-        if (kv.ic_tiled) {
-            // tiled keys: one workgroup per CU over the chip (one wave per SIMD), two tiles or more
-            // per wave, so that a wave requests its next tile while it finishes the current one
-            bx = (ntiles + 2 * IXM_WAVES - 1) / (2 * IXM_WAVES);
-            const int64_t cap = 256 / B > 1 ? 256 / B : 1;
-            if (bx > cap) bx = cap;
-        } else {
-            // row keys: about 3 resident waves per SIMD over the chip; each wave strides over the tiles
-            bx = 768 / B;
-            const int64_t need = (ntiles + IXM_WAVES - 1) / IXM_WAVES;
-            if (bx > need) bx = need;
+        const int64_t bx = ixm_grid_x(B, t_max, kv.ic_tiled != 0);
+        uint32_t *hl = nullptr, *hc = nullptr;
+        int pm = 0;
+        if (hist) {
+            if (bx > hist->parts_max) return fail(MLA_ERR_UNSUPPORTED, "index: histogram parts exceed the workspace");
+            hist->parts = (int)bx;
+            hl = hist->hl;
+            hc = hist->hcnt;
+            pm = hist->parts_max;
         }
-        if (bx < 1) bx = 1;
         const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
-#define IX_LAUNCH(M, H, TL) hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, ghist)
-        const bool h = ghist != nullptr;
+#define IX_LAUNCH(M, H, TL) \
+    hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, hl, hc, pm)
+        const bool h = hist != nullptr;
         if (kv.ic_tiled) {
             if (mode == 0) { if (h) IX_LAUNCH(0, true, true); else IX_LAUNCH(0, false, true); }
             else { if (h) IX_LAUNCH(1, true, true); else IX_LAUNCH(1, false, true); }
@@ -332,8 +356,8 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
     else
         hipLaunchKernelGGL(index_scores_generic, grid, dim3(256), 0, s, q, w, n_ih, hd, kv, t_max, scores);
     mla_status st = check_launch("index_scores");
-    if (st || !ghist) return st;
-    return launch_score_hist(scores, B, t_max, kv, ghist, s);   // kernels without a built-in histogram
+    if (st || !hist) return st;
+    return launch_score_hist(scores, B, t_max, kv, hist, s);   // kernels without a built-in histogram
 }
 
 }  // namespace mla

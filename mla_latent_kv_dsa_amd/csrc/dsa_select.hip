@@ -4,15 +4,15 @@
 // dsa_index_scores followed by dsa_topk_select with n_valid = seq_len: score descending, then
 // position ascending (-0.0 equals +0.0), kept positions in ascending order, nsel = min(k, n).
 //
-// Launches (all rows of the batch together):
-//   1. sel_zero     clears the row histograms and candidate counters of the workspace
-//   2. indexer      writes the scores and, in the same pass, a histogram of the top 11
-//                   order-key bits of every score of a key t < n (per workgroup in LDS, then
-//                   added into the row histogram with atomics)
-//   3. sel_filter   grid (t_max / 1024, B): finds the threshold bin from the row histogram,
-//                   writes the row bitmask words of its keys above the bin and appends its keys
-//                   inside the bin to the row's candidate list
-//   4. sel_resolve  grid (B): the exact k-th key (two radix passes over the candidates'
+// Launches (all rows of the batch together); no step accumulates into memory with atomics, so the
+// workspace needs no clearing between calls:
+//   1. indexer      writes the scores and, in the same pass, a histogram of the top 11
+//                   order-key bits of its keys t < n (per workgroup in LDS), written as that
+//                   workgroup's list of nonzero bins (common.h)
+//   2. sel_filter   grid (t_max / 1024, B): sums the lists into the row histogram (only as deep
+//                   as the threshold needs), finds the threshold bin, writes the row bitmask words
+//                   of its keys above the bin and its keys inside the bin into its own slot
+//   3. sel_resolve  grid (B): the exact k-th key (two radix passes over the candidates'
 //                   remaining 21 bits), the kept candidates' bits, ties resolved in position
 //                   order, and the kept positions written out of the bitmask in ascending order
 // Rows longer than SEL_TMAX positions take the general top-k (three launches, any length).
@@ -22,57 +22,19 @@
 namespace mla {
 
 constexpr int SEL_BINS = HIST_BINS;        // top 11 key bits
-constexpr int SEL_CH = 1024;               // positions per filter workgroup
+constexpr int SEL_CH = 1024;               // positions per filter workgroup (one candidate slot)
 constexpr int SEL_TMAX = 262144;           // longest row whose bitmasks the resolve step holds in LDS
+constexpr int HL_TOP = 16;                 // list entries per part the filter reads first
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row shifts inside rows of 16
-// lanes, then row broadcasts of lanes 15 and 31), no LDS traffic.
-__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x)
-{
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);   // row_shr:8
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31
-    return x;
-}
-
-// Block-wide exclusive scan (NW waves) on DPP wave scans; sh needs NW words.
-template <int NW>
-__device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *sh, uint32_t *total = nullptr)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t inc = wave_incl_scan_dpp(v);
-    if (lane == 63) sh[wave] = inc;
-    __syncthreads();
-    uint32_t before = 0u, all = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t t = sh[w];
-        before += w < wave ? t : 0u;
-        all += t;
-    }
-    if (total) *total = all;
-    __syncthreads();
-    return before + inc - v;
-}
-
-// ------------------------------------------------------------------------------ 1. zero
-__global__ __launch_bounds__(256) void sel_zero(uint32_t *__restrict__ ghist, uint32_t *__restrict__ cnt)
-{
-    const int b = blockIdx.x;
-    uint4 *g = reinterpret_cast<uint4 *>(ghist + (int64_t)b * HIST_COPIES * SEL_BINS);
-    for (int i = threadIdx.x; i < HIST_COPIES * SEL_BINS / 4; i += 256) g[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x == 0) cnt[b] = 0u;
-}
-
-// ------------------------------------------------------------------------------ 2'. histogram
-// For indexer kernels without a built-in histogram: grid (ceil(t_max/1024), B).
+// ------------------------------------------------------------------------------ 1'. histogram
+// For indexer kernels without a built-in histogram: grid (ceil(t_max/1024), B), one list part per
+// workgroup.
 __global__ __launch_bounds__(256) void sel_hist(const float *__restrict__ scores, int64_t t_max, KvView kv,
-                                                uint32_t *__restrict__ ghist)
+                                                uint32_t *__restrict__ hl, uint32_t *__restrict__ hcnt,
+                                                int parts_max)
 {
     __shared__ uint32_t hs[SEL_BINS];
+    __shared__ uint32_t sh[4];
     const int b = blockIdx.y, tid = threadIdx.x;
     const int64_t n = seq_len_of(kv, b);
     for (int i = tid; i < SEL_BINS; i += 256) hs[i] = 0u;
@@ -92,31 +54,36 @@ __global__ __launch_bounds__(256) void sel_hist(const float *__restrict__ scores
         }
     }
     __syncthreads();
-    for (int i = tid; i < SEL_BINS; i += 256) {
-        const uint32_t c = hs[i];
-        if (c) atomicAdd(&ghist[((int64_t)b * HIST_COPIES + blockIdx.x % HIST_COPIES) * SEL_BINS + i], c);
-    }
+    hist_write_list<256>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max,
+                         hcnt + (int64_t)b * parts_max + blockIdx.x, sh);
 }
 
-mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, uint32_t *ghist,
+mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, const KvView &kv, HistOut *hist,
                              hipStream_t s)
 {
     const int64_t nch = (t_max + SEL_CH - 1) / SEL_CH;
     if (nch == 0) return MLA_OK;
-    hipLaunchKernelGGL(sel_hist, dim3((unsigned)nch, B), dim3(256), 0, s, scores, t_max, kv, ghist);
+    if (nch > hist->parts_max) return fail(MLA_ERR_UNSUPPORTED, "select: histogram parts exceed the workspace");
+    hist->parts = (int)nch;
+    hipLaunchKernelGGL(sel_hist, dim3((unsigned)nch, B), dim3(256), 0, s, scores, t_max, kv, hist->hl, hist->hcnt,
+                       hist->parts_max);
     return check_launch("sel_hist");
 }
 
-// ------------------------------------------------------------------------------ 3. filter
+// ------------------------------------------------------------------------------ 2. filter
 // 256 threads; thread t of workgroup c handles positions c*1024 + 256 j + t (j = 0..3), so the
 // ballot of wave w for step j covers the 64 consecutive positions c*1024 + 256 j + 64 w ..., the
-// word 16 c + 4 j + w of the row's bitmask.  Every workgroup finds the threshold bin tb from the
-// row histogram, writes the bitmask words of its keys above the bin and appends its keys inside
-// the bin to the row's candidate list.
-constexpr int SEL_CPT = 8;                     // candidates per thread held in registers
+// word 16 c + 4 j + w of the row's bitmask.
+//
+// Row histogram: thread t reads parts t, t + 256, .. (PPT of them): the part's length and its
+// first HL_TOP entries (the highest bins), added into an LDS histogram.  For a part longer than
+// that, every bin at or above its last entry read is complete; the histogram is therefore exact
+// from F = the highest such bin over the truncated parts upwards.  When the threshold lies below F
+// the remaining entries of the truncated parts are added as well (then it is exact everywhere).
+constexpr int SEL_CPT = 8;                     // candidates per thread held in registers (resolve)
 constexpr int SR_NT = 512, SR_NW = SR_NT / 64; // threads / waves of the resolve workgroup
 constexpr int SR_WPT = 8;                      // bitmask words per resolve thread (SEL_TMAX)
-constexpr int SR_STATIC = SEL_BINS * 4 + 256;  // static LDS of the resolve workgroup (bytes)
+constexpr int SR_STATIC = SEL_BINS * 4 + 2048; // static LDS of the resolve workgroup (bytes)
 constexpr int SR_DYN_MAX = 160 * 1024 - SR_STATIC;
 
 struct SelRow {           // per-row results of the filter (uint32 words)
@@ -129,72 +96,102 @@ __host__ __device__ inline int sel_words(int64_t t_max)
     return (int)(((t_max + 63) / 64 + SR_NT - 1) / SR_NT * SR_NT);
 }
 
+template <int PPT>   // list parts per thread: parts <= 256 PPT
 __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scores, int64_t t_max, KvView kv, int k,
-                                                  const uint32_t *__restrict__ ghist, uint2 *__restrict__ cand,
-                                                  int64_t cap, uint32_t *__restrict__ cnt, uint64_t *__restrict__ gkeep,
-                                                  int wp, SelRow *__restrict__ rows)
+                                                  const uint32_t *__restrict__ hl, const uint32_t *__restrict__ hcnt,
+                                                  int parts_max, int parts, uint2 *__restrict__ cand,
+                                                  uint32_t *__restrict__ fcnt, uint64_t *__restrict__ gkeep, int wp,
+                                                  SelRow *__restrict__ rows)
 {
     constexpr int NW = 4;
-    __shared__ uint32_t tot[SEL_BINS];
+    __shared__ uint32_t hs[SEL_BINS];
     __shared__ uint32_t sh[NW];
-    __shared__ uint32_t s_tb, s_above, s_base;
+    __shared__ uint32_t s_tb, s_above, s_floor, s_found;
     __shared__ uint32_t s_wcnt[NW];
     const int b = blockIdx.y, c = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = seq_len_of(kv, b);
     if (n <= k) return;
-    // threshold bin: thread t owns the 8 bins [2040-8t, 2048-8t) (thread order = descending bins),
-    // summed over the row's histogram copies
-    const int lo_bin = SEL_BINS - 8 * (tid + 1);
-    const uint4 *hp = reinterpret_cast<const uint4 *>(ghist + (int64_t)b * HIST_COPIES * SEL_BINS + lo_bin);
-    uint4 hx[2 * HIST_COPIES];
-#pragma unroll
-    for (int cp = 0; cp < HIST_COPIES; ++cp) {
-        hx[2 * cp] = hp[cp * SEL_BINS / 4];
-        hx[2 * cp + 1] = hp[cp * SEL_BINS / 4 + 1];
-    }
-    // the scores of this workgroup's positions go out while the histogram is scanned
+    // this workgroup's scores and the top of every list part go out together
     const float *row = scores + (int64_t)b * t_max;
-    uint32_t key[SEL_CH / 256];
     float sv[SEL_CH / 256];
 #pragma unroll
     for (int j = 0; j < SEL_CH / 256; ++j) {   // unconditional loads (clamped into the row), masked after
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         sv[j] = row[t < n ? t : n - 1];
     }
-    __builtin_amdgcn_sched_barrier(0);   // all loads in flight together
-    uint32_t bin8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    const uint32_t *hlb = hl + (int64_t)b * HL_CAP * parts_max;
+    uint32_t pc[PPT], pe[PPT][HL_TOP];
 #pragma unroll
-    for (int cp = 0; cp < HIST_COPIES; ++cp) {
-        const uint4 x0 = hx[2 * cp], x1 = hx[2 * cp + 1];
-        bin8[0] += x0.x; bin8[1] += x0.y; bin8[2] += x0.z; bin8[3] += x0.w;
-        bin8[4] += x1.x; bin8[5] += x1.y; bin8[6] += x1.z; bin8[7] += x1.w;
+    for (int r = 0; r < PPT; ++r) {   // clamped to the last part; parts past the end are skipped
+        const int p = tid + 256 * r < parts ? tid + 256 * r : parts - 1;
+        pc[r] = hcnt[(int64_t)b * parts_max + p];
+#pragma unroll
+        for (int i = 0; i < HL_TOP; ++i) pe[r][i] = hlb[(int64_t)i * parts_max + p];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SEL_BINS / 256; ++i) hs[tid + 256 * i] = 0u;
+    if (tid == 0) {
+        s_floor = 0u;
+        s_found = 0u;
+    }
+    __syncthreads();
+    uint32_t key[SEL_CH / 256];
 #pragma unroll
     for (int j = 0; j < SEL_CH / 256; ++j) {
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         key[j] = t < n ? order_key(sv[j]) : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tot[lo_bin + j] = bin8[j];
-    uint32_t local = 0u;
+    for (int r = 0; r < PPT; ++r) {
+        if (tid + 256 * r >= parts) break;
+        const uint32_t ne = pc[r] < HL_TOP ? pc[r] : HL_TOP;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) local += bin8[j];
-    const uint32_t before = block_excl_scan_dpp<NW>(local, sh);
-    if (before < (uint32_t)k && before + local >= (uint32_t)k) {
-        uint32_t cum = before;
-        const int hi = lo_bin + 7;
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t ct = tot[hi - j];
-            if (cum + ct >= (uint32_t)k) {
-                s_tb = (uint32_t)(hi - j);
-                s_above = cum;
-                break;
-            }
-            cum += ct;
-        }
+        for (int i = 0; i < HL_TOP; ++i)
+            if ((uint32_t)i < ne) atomicAdd(&hs[pe[r][i] >> 21], pe[r][i] & 0x1FFFFFu);
+        if (pc[r] > HL_TOP) atomicMax(&s_floor, pe[r][HL_TOP - 1] >> 21);
     }
     __syncthreads();
+    // threshold bin: thread t owns the 8 bins [2040-8t, 2048-8t) (thread order = descending bins)
+    for (int pass = 0; pass < 2; ++pass) {
+        const int lo_bin = SEL_BINS - 8 * (tid + 1), hi = lo_bin + 7;
+        uint32_t bin8[8], local = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bin8[j] = hs[hi - j];
+            local += bin8[j];
+        }
+        const uint32_t before = block_excl_scan_dpp<NW>(local, sh);
+        const uint32_t fl = pass == 0 ? s_floor : 0u;
+        if (before < (uint32_t)k && before + local >= (uint32_t)k) {
+            uint32_t cum = before;
+            for (int j = 0; j < 8; ++j) {
+                if (cum + bin8[j] >= (uint32_t)k) {
+                    if ((uint32_t)(hi - j) >= fl) {   // counts at and above this bin are complete
+                        s_tb = (uint32_t)(hi - j);
+                        s_above = cum;
+                        s_found = 1u;
+                    }
+                    break;
+                }
+                cum += bin8[j];
+            }
+        }
+        __syncthreads();
+        if (s_found) break;
+        // the threshold lies below the complete range: add the rest of the truncated parts
+#pragma unroll
+        for (int r = 0; r < PPT; ++r) {
+            if (tid + 256 * r >= parts) break;
+            const uint32_t *lp = hlb + tid + 256 * r;
+            for (uint32_t i = HL_TOP; i < pc[r]; ++i) {
+                const uint32_t e = lp[(int64_t)i * parts_max];
+                atomicAdd(&hs[e >> 21], e & 0x1FFFFFu);
+            }
+        }
+        __syncthreads();
+    }
     const uint32_t tb = s_tb;
     // classify: the words of keys above the bin go straight to the row bitmask
     uint64_t cm[SEL_CH / 256];
@@ -212,20 +209,19 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
     }
     if (lane == 0) s_wcnt[wave] = wtot;
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t all = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-        s_base = all ? atomicAdd(&cnt[b], all) : 0u;
-    }
-    __syncthreads();
-    uint32_t off = s_base;
+    // the keys inside the bin, in this workgroup's own slot
+    const int64_t slot = (int64_t)b * gridDim.x + c;
+    if (tid == 0) fcnt[slot] = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    uint32_t off = 0u;
     for (int w = 0; w < wave; ++w) off += s_wcnt[w];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint2 *cs = cand + slot * SEL_CH;
 #pragma unroll
     for (int j = 0; j < SEL_CH / 256; ++j) {
         if ((cm[j] >> lane) & 1ull) {
             const uint32_t at = off + (uint32_t)__popcll(cm[j] & below);
             const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
-            if (at < (uint64_t)cap) cand[(int64_t)b * cap + at] = make_uint2(key[j], (uint32_t)t);
+            cs[at] = make_uint2(key[j], (uint32_t)t);
         }
         off += (uint32_t)__popcll(cm[j]);
     }
@@ -238,8 +234,13 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
     }
 }
 
-// ------------------------------------------------------------------------------ 4. resolve + emit
+// ------------------------------------------------------------------------------ 3. resolve + emit
 // One workgroup of SR_NT threads per row b:
+//   - the candidates sit in nch slots (one per filter workgroup, fcnt[c] each).  The tps = SR_NT /
+//     nch consecutive threads t of slot c = t / tps take its entries in pairs: thread r = t % tps
+//     the pairs r + tps i, i < SEL_CPT / 2 (the first D = SEL_CPT tps entries, loaded before
+//     anything waits); entries past D (long slots) are spread evenly over all threads through a
+//     prefix of the slots' overflow counts
 //   - the exact k-th key among the candidates (two radix digits, bits 20..10 and 9..0)
 //   - candidates above it set their bit in the row bitmask (held in LDS), candidates equal to it
 //     their bit in an eq bitmask
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
 //     written out as positions -- ascending across the row.
 // dyn: keep[wp], eq[wp] (uint64).
 __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k, const uint2 *__restrict__ cand,
-                                                 int64_t cap, const uint32_t *__restrict__ cnt,
+                                                 const uint32_t *__restrict__ fcnt, int nch,
                                                  const uint64_t *__restrict__ gkeep, int wp,
                                                  const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
                                                  int32_t *__restrict__ nsel, uint64_t *__restrict__ dyn)
@@ -257,6 +258,7 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     __shared__ uint32_t h[SEL_BINS];
     __shared__ uint32_t sh[SR_NW];
     __shared__ uint32_t s_bc[2];
+    __shared__ uint32_t s_ov[SEL_TMAX / SEL_CH + 1];   // overflow prefix over the slots
     const int tid = threadIdx.x;
     const int64_t n = seq_len_of(kv, b);
     int32_t *out = sel + (int64_t)b * k;
@@ -265,44 +267,65 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         if (tid == 0) nsel[b] = (int32_t)n;
         return;
     }
-    // issued before anything waits: the row's threshold, candidate count, bitmask words and the
-    // first SR_NT * SEL_CPT candidates (thread t holds t + SR_NT i), as unconditional loads clamped
-    // into the buffers and masked on use
+    // issued before anything waits: the row's threshold, the slot counts, bitmask words and the
+    // first SEL_CPT entries of this thread in its slot, as unconditional loads clamped into the
+    // buffers and masked on use
     const SelRow rin = rows[b];
-    uint32_t E = cnt[b];
+    const int tps = SR_NT / nch;                     // threads per slot (nch <= 256: at least 2)
+    const bool active = tid < tps * nch;             // threads past tps nch idle
+    const int my_c = active ? tid / tps : 0, my_r = tid % tps;
+    const uint32_t *fc = fcnt + (int64_t)b * nch;
+    const uint32_t cnt_mine = fc[my_c];
+    const uint32_t cnt_t = fc[tid < nch ? tid : 0];  // thread t < nch: slot t, for the overflow prefix
     const int wpt = wp / SR_NT;
     const int nw = (int)((n + 63) / 64);   // words that hold positions < n
     const uint64_t *gk = gkeep + (int64_t)b * wp + tid * wpt;
     uint64_t kw[SR_WPT];
 #pragma unroll
     for (int i = 0; i < SR_WPT; ++i) kw[i] = gk[i < wpt ? i : 0];
-    const uint2 *cb = cand + (int64_t)b * cap;
+    const uint2 *cb = cand + (int64_t)b * nch * SEL_CH;
+    const uint4 *cmine = reinterpret_cast<const uint4 *>(cb + (int64_t)my_c * SEL_CH);
     uint2 cr[SEL_CPT];
 #pragma unroll
-    for (int i = 0; i < SEL_CPT; ++i) {
-        const int64_t j = tid + SR_NT * i;
-        cr[i] = cb[j < cap ? j : cap - 1];
+    for (int i = 0; i < SEL_CPT / 2; ++i) {   // pair my_r + tps i: entries 2 (my_r + tps i), +1
+        const int pr = my_r + tps * i;
+        const uint4 v = cmine[pr < SEL_CH / 2 ? pr : SEL_CH / 2 - 1];
+        cr[2 * i] = make_uint2(v.x, v.y);
+        cr[2 * i + 1] = make_uint2(v.z, v.w);
     }
     uint64_t *keep = dyn, *eqm = dyn + wp;
     for (int i = tid; i < wp; i += SR_NT) eqm[i] = 0ull;
     const uint32_t tb = rin.tb, above_total = rin.above;
-    if (E > cap) E = (uint32_t)cap;
-    // every candidate once: those held in registers, then the rest from memory in batches of
-    // eight independent loads per thread
+    // entries past the first D of each slot: prefix over the slots (thread t < nch: slot t)
+    const uint32_t D = (uint32_t)tps * SEL_CPT;
+    const uint32_t ov_t = tid < nch && cnt_t > D ? cnt_t - D : 0u;
+    uint32_t OV = 0u;
+    const uint32_t ov_pre = block_excl_scan_dpp<SR_NW>(ov_t, sh, &OV);
+    if (tid < nch) s_ov[tid] = ov_pre;
+    if (tid == 0) s_ov[nch] = OV;
+    // every candidate once: those held in registers, then the overflow entries in batches of
+    // eight independent loads per thread (overflow item i: slot c with s_ov[c] <= i < s_ov[c+1])
     auto for_each = [&](auto f) {
 #pragma unroll
         for (int i = 0; i < SEL_CPT; ++i)
-            if (tid + (uint32_t)SR_NT * i < E) f(cr[i]);
-        for (uint32_t base = (uint32_t)SR_NT * SEL_CPT; base < E; base += 8u * SR_NT) {
+            if (active && (uint32_t)(2 * (my_r + tps * (i >> 1)) + (i & 1)) < cnt_mine) f(cr[i]);
+        for (uint32_t base = 0u; base < OV; base += 8u * SR_NT) {
             uint2 t[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t j = base + tid + (uint32_t)SR_NT * i;
-                t[i] = cb[j < E ? j : E - 1u];
+                const uint32_t it = base + tid + (uint32_t)SR_NT * i;
+                const uint32_t ic = it < OV ? it : OV - 1u;
+                int lo = 0, hi = nch - 1;   // last slot with s_ov[slot] <= ic
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_ov[mid] <= ic) lo = mid;
+                    else hi = mid - 1;
+                }
+                t[i] = cb[(int64_t)lo * SEL_CH + D + (ic - s_ov[lo])];
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (base + tid + (uint32_t)SR_NT * i < E) f(t[i]);
+                if (base + tid + (uint32_t)SR_NT * i < OV) f(t[i]);
         }
     };
     // radix select of the need-th largest key: digits of bits 20..10, then 9..0
@@ -403,14 +426,14 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
 }
 
 // grid (B), SR_NT threads, dynamic LDS 16 wp bytes
-__global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uint2 *__restrict__ cand, int64_t cap,
-                                                     const uint32_t *__restrict__ cnt,
+__global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uint2 *__restrict__ cand,
+                                                     const uint32_t *__restrict__ fcnt, int nch,
                                                      const uint64_t *__restrict__ gkeep, int wp,
                                                      const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
                                                      int32_t *__restrict__ nsel)
 {
     extern __shared__ uint64_t sr_dyn[];
-    resolve_emit_row(blockIdx.x, kv, k, cand, cap, cnt, gkeep, wp, rows, sel, nsel, sr_dyn);
+    resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn);
 }
 
 // The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
@@ -421,7 +444,7 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
 // head's query tails.
 template <int NR>
 __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
-                                                            int64_t cap, const uint32_t *__restrict__ cnt,
+                                                            const uint32_t *__restrict__ fcnt, int nch,
                                                             const uint64_t *__restrict__ gkeep, int wp,
                                                             const SelRow *__restrict__ rows,
                                                             int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
@@ -429,7 +452,7 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
 {
     extern __shared__ uint64_t sr_dyn[];
     if ((int)blockIdx.x < nres) {
-        resolve_emit_row(blockIdx.x, kv, k, cand, cap, cnt, gkeep, wp, rows, sel, nsel, sr_dyn);
+        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn);
         return;
     }
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
@@ -452,11 +475,12 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
 
 // ------------------------------------------------------------------------------ host side
 struct SelWs {
-    uint32_t *ghist, *cnt;
+    HistOut hist;
+    uint32_t *fcnt;
     SelRow *rows;
     uint64_t *keep;
     uint2 *cand;
-    int64_t nch, cap;
+    int64_t nch;
     int wp;
 };
 
@@ -466,8 +490,9 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
 {
     SelWs w;
     w.nch = (t_max + SEL_CH - 1) / SEL_CH;
-    w.cap = w.nch * SEL_CH;
     w.wp = sel_words(t_max);
+    w.hist.parts_max = hist_parts_max(B, t_max);
+    w.hist.parts = 0;
     char *p = reinterpret_cast<char *>(ws);
     size_t off = 0;
     auto take = [&](size_t sz) {
@@ -475,11 +500,12 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
         off += sal(sz);
         return q;
     };
-    w.ghist = reinterpret_cast<uint32_t *>(take((size_t)B * HIST_COPIES * SEL_BINS * 4));
-    w.cnt = reinterpret_cast<uint32_t *>(take((size_t)B * 4));
+    w.hist.hl = reinterpret_cast<uint32_t *>(take((size_t)B * w.hist.parts_max * HL_CAP * 4));
+    w.hist.hcnt = reinterpret_cast<uint32_t *>(take((size_t)B * w.hist.parts_max * 4));
+    w.fcnt = reinterpret_cast<uint32_t *>(take((size_t)B * w.nch * 4));
     w.rows = reinterpret_cast<SelRow *>(take((size_t)B * sizeof(SelRow)));
     w.keep = reinterpret_cast<uint64_t *>(take((size_t)B * w.wp * 8));
-    w.cand = reinterpret_cast<uint2 *>(take((size_t)B * w.cap * 8));
+    w.cand = reinterpret_cast<uint2 *>(take((size_t)B * w.nch * SEL_CH * 8));
     if (bytes) *bytes = off;
     return w;
 }
@@ -524,32 +550,38 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     }
     st = enable_sel_lds();
     if (st) return st;
-    const SelWs sw = sel_ws(ws, B, t_max, nullptr);
+    SelWs sw = sel_ws(ws, B, t_max, nullptr);
     if (t_max > 0) {
-        hipLaunchKernelGGL(sel_zero, dim3(B), dim3(256), 0, s, sw.ghist, sw.cnt);
-        st = check_launch("sel_zero");
+        st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, &sw.hist, s);
         if (st) return st;
-        st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, sw.ghist, s);
-        if (st) return st;
-        hipLaunchKernelGGL(sel_filter, dim3((unsigned)sw.nch, B), dim3(256), 0, s, scores, t_max, kv, k, sw.ghist,
-                           sw.cand, sw.cap, sw.cnt, sw.keep, sw.wp, sw.rows);
+        const int P = sw.hist.parts;
+        const dim3 gf((unsigned)sw.nch, B);
+#define SF_LAUNCH(PPT)                                                                                         \
+    hipLaunchKernelGGL(sel_filter<PPT>, gf, dim3(256), 0, s, scores, t_max, kv, k, sw.hist.hl, sw.hist.hcnt, \
+                       sw.hist.parts_max, P, sw.cand, sw.fcnt, sw.keep, sw.wp, sw.rows)
+        if (P <= 256) SF_LAUNCH(1);
+        else if (P <= 512) SF_LAUNCH(2);
+        else if (P <= 768) SF_LAUNCH(3);
+        else return fail(MLA_ERR_UNSUPPORTED, "select: more than 768 histogram parts");
+#undef SF_LAUNCH
         st = check_launch("sel_filter");
         if (st) return st;
     }
+    const int nch = sw.nch > 0 ? (int)sw.nch : 1;
     const size_t dyn_sel = (size_t)sw.wp * 16;
     const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
                            (side->nope == 128 || side->nope == 192 || side->nope == 256);
     if (!with_side) {
-        hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.cap, sw.cnt, sw.keep,
+        hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
                            sw.wp, sw.rows, sel, nsel);
         return check_launch("sel_resolve");
     }
     const size_t dyn_abs = 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
     const dim3 g((unsigned)(B + 2 * AB_H));
-#define SRA_LAUNCH(NR)                                                                                            \
-    hipLaunchKernelGGL(sel_resolve_absorb<NR>, g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.cap, sw.cnt, sw.keep, \
-                       sw.wp, sw.rows, sel, nsel, B, *side)
+#define SRA_LAUNCH(NR)                                                                                              \
+    hipLaunchKernelGGL(sel_resolve_absorb<NR>, g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, sw.wp, \
+                       sw.rows, sel, nsel, B, *side)
     if (side->nope == 128) SRA_LAUNCH(8);
     else if (side->nope == 192) SRA_LAUNCH(12);
     else SRA_LAUNCH(16);
