@@ -249,6 +249,50 @@ def test_index_select_ties_and_all_equal():
     assert np.array_equal(sel[0], np.arange(k))
 
 
+def _ixm_parts(B, T, tiled):
+    """Workgroups per row of the matrix-core indexer and the keys each one scores (the kernel's
+    grid: tiles of 64 keys, 4 waves per workgroup, wave (p, w) takes tiles 4 p + w + 4 bx j)."""
+    ntiles = (T + 63) // 64
+    if tiled:
+        bx = min(max(256 // B, 1), (ntiles + 7) // 8)
+    else:
+        bx = min(max(768 // B, 1), (ntiles + 3) // 4)
+    bx = max(bx, 1)
+    parts = []
+    for p in range(bx):
+        tiles = [t for w in range(4) for t in range(4 * p + w, ntiles, 4 * bx)]
+        parts.append(np.concatenate([np.arange(64 * t, min(64 * t + 64, T)) for t in tiles]))
+    return parts
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_index_select_deep_histogram_parts(tiled):
+    """Scores spread over ~480 quarter-octave bins (about one key per bin) with k = T / 8: every
+    indexer workgroup has more than 16 nonzero bins above the threshold, so the filter's first
+    read of the lists stops above the threshold bin and it must add the rest of the lists
+    (checked here on the CPU first)."""
+    rng = np.random.default_rng(292)
+    B, T, k = 2, 32768, 4096
+    seq = [T, 20001]
+    ic = rng.standard_normal((B * T, 128)).astype(np.float32)
+    ic[:, 0] = np.exp2(rng.uniform(0.0, 120.0, B * T)).astype(np.float32)
+    q = rng.standard_normal((B, 32, 128)).astype(np.float32)
+    q[:, 0, :] = 0.0
+    q[:, 0, 0] = 1.0                       # head 0 scores max(Ic[t, 0], 0) exactly
+    w = np.zeros((B, 32), np.float32)
+    w[:, 0] = 1.0
+    score0 = np.maximum(ic[:T, 0], 0.0)
+    key = score0.view(np.uint32) | np.uint32(0x80000000)   # positive scores: order key
+    bins = (key >> 21).astype(np.int64)
+    tb = np.sort(bins)[::-1][k - 1]
+    floor = max(np.unique(bins[pk])[::-1][15] for pk in _ixm_parts(B, T, tiled) if np.unique(bins[pk]).size > 16)
+    assert floor > tb, (floor, tb)
+    z = np.zeros((B * T, 8), np.uint16)
+    log(f"index+select deep histogram lists tiled={tiled}")
+    kv = _kv(z, z, ic, seq, T, seq_stride=T, tiled=tiled)
+    _select_check(q, w, kv, T, k, seq)
+
+
 def test_index_select_long_row_general_path():
     T, k = 300000, 2048
     rng = np.random.default_rng(291)
