@@ -261,6 +261,10 @@ def bench_dsa_decode(args):
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_decode(d, T, K, sm)
+    extra = {}
+    if not args.no_extra:   # the batched paged and the dense decode configurations
+        extra["batched_paged_B32"] = bench_batched_paged(args)
+        extra["dense_decode_T4096"] = bench_dense_decode(args)
 
     line = {
         "metric": METRIC, "value": value, "unit": "keys·heads/s", "n_gpus": 1, "steps": args.steps,
@@ -285,8 +289,131 @@ def bench_dsa_decode(args):
                        "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "wall_s_timed": t_wall,
         "ms_per_step_one_graph_per_step": ms_step_single,
+        "extra_configs": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def _graph_time(torch, fn, warmup, steps):
+    """Mean ms per call of fn captured in a HIP graph (one call per replay), events on the stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    for _ in range(warmup):
+        gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_batched_paged(args):
+    """The batched paged decode step (32 sequences, lengths ~ U{8192..131072}, 64-token blocks
+    in a seeded random physical order, every sequence past k so DSA is on everywhere): one
+    mla_dsa_decode call per step.  Lengths and block table from synth.paged_batch's draws; pool
+    and query values from synth.paged_values_torch (drawn on the GPU, seeded, same
+    distributions).  The 3.4 GB of pools exceed the Infinity Cache, so no input rotation is
+    needed."""
+    import torch
+
+    import mla_latent_kv_dsa_amd as mla
+    from mla_latent_kv_dsa_amd import synth
+
+    dev = torch.device("cuda:0")
+    H, NOPE, ROPE, V, L = synth.H, synth.QK_NOPE, synth.QK_ROPE, synth.V_HEAD, synth.KV_LORA
+    N_IH, HD, K = synth.N_IH, synth.INDEX_HD, synth.TOPK
+    pb = synth.paged_batch(5, meta_only=True)
+    B, T = pb.B, pb.max_blocks * pb.block_size
+    d = synth.paged_values_torch(pb, 1005, dev)
+    qn, qr, kvb, qi, wi = d["q_nope"], d["q_rope"], d["kv_b"], d["q_idx"], d["w_idx"]
+    ic = synth.tile_index_keys(d.pop("ic"))
+    seq_len = torch.from_numpy(pb.seq_len).to(dev)
+    bt = torch.from_numpy(pb.block_table).to(dev)
+    kv = mla.KvCache(d["lc"], d["rc"], ic, seq_len=seq_len, max_seq_len=T, block_table=bt, block_size=pb.block_size,
+                     ic_layout=mla.MLA_IC_TILE64)
+    sm = 1.0 / math.sqrt(NOPE + ROPE)
+    scores = torch.empty((B, T), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, K), dtype=torch.int32, device=dev)
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(mla.mla_dsa_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, T, K), dtype=torch.uint8, device=dev)
+
+    def step():
+        mla.mla_dsa_decode(qn, qr, qi, wi, kvb, kv, T, K, sm, scores=scores, sel=sel, nsel=nsel, out=out, ws=ws)
+
+    def index():
+        mla.dsa_index_scores(qi, wi, kv, T, scores=scores)
+
+    ms = _graph_time(torch, step, 3, 20)
+    ms_idx = _graph_time(torch, index, 3, 20)
+    sum_t = int(pb.seq_len.sum())
+    keys_heads = sum_t * H
+    ic_bytes = sum_t * HD * 4
+    sel_kv = B * K * (L + ROPE) * 2
+    kvb_bytes = H * (NOPE + V) * L * 2
+    stream = ic_bytes + sel_kv
+    whole = stream + kvb_bytes + sum_t * 4 + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
+    idx_bytes = ic_bytes + sum_t * 4 + B * N_IH * (HD + 1) * 4
+    gbs = lambda nbytes, m: nbytes / (m * 1e-3) / 1e9
+    return {"workload": "dsa_decode_paged_B32", "B": B, "sum_seq_len": sum_t, "block_size": pb.block_size,
+            "seq_len_range": [int(pb.seq_len.min()), int(pb.seq_len.max())], "topk": K, "index_layout": "tile64",
+            "ms_per_step": ms, "keys_heads_per_s": keys_heads / (ms * 1e-3),
+            "stream": {"bytes": stream, "GBs": gbs(stream, ms), "frac": gbs(stream, ms) / HBM_PEAK_GBS},
+            "whole_step": {"bytes": whole, "GBs": gbs(whole, ms), "frac": gbs(whole, ms) / HBM_PEAK_GBS},
+            "indexer": {"ms": ms_idx, "algorithmic_bytes": idx_bytes, "GBs": gbs(idx_bytes, ms_idx),
+                        "frac": gbs(idx_bytes, ms_idx) / HBM_PEAK_GBS},
+            "data": "synthetic: lengths and block permutation from numpy seed 5, values torch seed 1005"}
+
+
+def bench_dense_decode(args):
+    """Dense absorbed decode at T = 4096 (B = 1, no selection): mla_absorbed_decode over every
+    causal key, one call per step, over 16 rotated input copies (34 MB each) so that no step
+    finds its inputs in the Infinity Cache."""
+    import torch
+
+    import mla_latent_kv_dsa_amd as mla
+    from mla_latent_kv_dsa_amd import synth
+
+    dev = torch.device("cuda:0")
+    H, NOPE, ROPE, V, L = synth.H, synth.QK_NOPE, synth.QK_ROPE, synth.V_HEAD, synth.KV_LORA
+    T, B, NC = 4096, 1, 16
+    g = torch.Generator(device=dev)
+    g.manual_seed(1002)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, generator=g, device=dev) * std
+    sm = 1.0 / math.sqrt(NOPE + ROPE)
+    cps = []
+    for _ in range(NC):
+        kv = mla.KvCache(rn(T, L).bfloat16(), rn(T, ROPE).bfloat16(),
+                         seq_len=torch.full((B,), T, dtype=torch.int32, device=dev), max_seq_len=T, seq_stride=T)
+        cps.append(dict(kv=kv, qn=rn(B, H, NOPE).bfloat16(), qr=rn(B, H, ROPE).bfloat16(),
+                        kvb=rn(H * (NOPE + V), L, std=0.02).bfloat16(),
+                        out=torch.empty((B, H, V), dtype=torch.float32, device=dev),
+                        ws=torch.empty(mla.mla_decode_workspace_bytes(H, NOPE, ROPE, V, L, B, T), dtype=torch.uint8,
+                                       device=dev)))
+
+    def step_all():
+        for c in cps:
+            mla.mla_absorbed_decode(c["qn"], c["qr"], c["kvb"], c["kv"], sm, out=c["out"], ws=c["ws"])
+
+    ms = _graph_time(torch, step_all, 3, 10) / NC
+    kv_bytes = T * (L + ROPE) * 2
+    kvb_bytes = H * (NOPE + V) * L * 2
+    whole = kv_bytes + kvb_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
+    gbs = lambda nbytes: nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "dense_decode_T4096_B1", "T": T, "ms_per_step": ms, "keys_heads_per_s": T * H / (ms * 1e-3),
+            "whole_step": {"bytes": whole, "GBs": gbs(whole), "frac": gbs(whole) / HBM_PEAK_GBS},
+            "kv_core": {"bytes": kv_bytes, "GBs": gbs(kv_bytes), "frac": gbs(kv_bytes) / HBM_PEAK_GBS},
+            "input_copies": NC, "data": "synthetic: torch seed 1002"}
 
 
 def cpu_baseline_decode(d, T, K, sm):
@@ -464,11 +591,13 @@ def main():
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the batched paged and dense decode configurations (profiling runs of the headline step)")
     ap.add_argument("--counters-dir", help="summarize rocprofv3 --pmc runs found in this directory and exit")
     ap.add_argument("--kernel", default="index_scores_mfma")
     ap.add_argument("--kernel-src", default="dsa_index.hip")
     ap.add_argument("--counters-name", default="dsa_index_scores_T131072")
-    ap.add_argument("--counters-cmd", default="--steps 5 --warmup 1 --no-cpu")
+    ap.add_argument("--counters-cmd", default="--steps 5 --warmup 1 --no-cpu --no-extra")
     ap.add_argument("--stats-csv", help="summarize a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--stats-name", default="dsa_decode_T131072_B1")
     ap.add_argument("--stats-cmd", default="")

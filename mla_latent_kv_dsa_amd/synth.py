@@ -47,6 +47,8 @@ def tile_index_keys(ic: np.ndarray) -> np.ndarray:
     (r // 64) * 64 * hd + (d // 4) * 256 + (r % 64) * 4 + d % 4).  Same values, same shape."""
     rows, hd = ic.shape
     assert rows % 64 == 0 and hd % 4 == 0
+    if not isinstance(ic, np.ndarray):   # a torch tensor: the same rearrangement on its device
+        return ic.reshape(rows // 64, 64, hd // 4, 4).permute(0, 2, 1, 3).contiguous().reshape(rows, hd)
     t = ic.reshape(rows // 64, 64, hd // 4, 4).transpose(0, 2, 1, 3)
     return np.ascontiguousarray(t).reshape(rows, hd)
 
@@ -220,9 +222,10 @@ class PagedBatch:
 def paged_batch(seed: int, B: int = 32, t_lo: int = 8192, t_hi: int = 131072, *,
                 block_size: int = BLOCK, max_ctx: int = 131072, H_=H, nope=QK_NOPE,
                 rope=QK_ROPE, v=V_HEAD, L=KV_LORA, n_ih=N_IH, hd=INDEX_HD,
-                w_std=0.02) -> PagedBatch:
+                w_std=0.02, meta_only: bool = False) -> PagedBatch:
     """seq_len ~ U{t_lo..t_hi} (inclusive); pools filled in physical order after a seeded
-    random permutation of the blocks; values distributed as in ``decode``."""
+    random permutation of the blocks; values distributed as in ``decode``.  meta_only: only the
+    lengths and the block table (the same draws), no pools or queries."""
     rng = np.random.default_rng(seed)
     seq_len = rng.integers(t_lo, t_hi + 1, size=B).astype(np.int32)
     max_blocks = (max_ctx + block_size - 1) // block_size
@@ -236,6 +239,8 @@ def paged_batch(seed: int, B: int = 32, t_lo: int = 8192, t_hi: int = 131072, *,
         o += nb[b]
     pb = PagedBatch(B, seq_len, block_size, max_blocks, bt, n_blocks, H=H_, nope=nope, rope=rope,
                     v=v, L=L, n_ih=n_ih, hd=hd)
+    if meta_only:
+        return pb
     rows = n_blocks * block_size
     pb.lc = _normal_bf16(rng, (rows, L))
     pb.rc = _normal_bf16(rng, (rows, rope))
@@ -246,3 +251,27 @@ def paged_batch(seed: int, B: int = 32, t_lo: int = 8192, t_hi: int = 131072, *,
     pb.q_idx = _normal(rng, (B, n_ih, hd))
     pb.w_idx = _normal(rng, (B, n_ih))
     return pb
+
+
+def paged_values_torch(pb: PagedBatch, seed: int, device, w_std=0.02) -> dict:
+    """Pool and query values for the lengths and block table of ``pb`` (from
+    ``paged_batch(..., meta_only=True)``), drawn on a torch device with a seeded
+    torch.Generator: the distributions of ``paged_batch`` (N(0, 1), kv_b N(0, w_std^2), bf16
+    where the numpy draw is bf16), without the minutes a host draw of 2M cached rows takes.
+    ic comes row-major (tile it with ``tile_index_keys``)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    rows = pb.n_blocks * pb.block_size
+
+    def rn(*shape, std=1.0, bf16=False):
+        x = torch.randn(*shape, generator=g, device=device)
+        if std != 1.0:
+            x *= std
+        return x.bfloat16() if bf16 else x
+
+    return dict(lc=rn(rows, pb.L, bf16=True), rc=rn(rows, pb.rope, bf16=True), ic=rn(rows, pb.hd),
+                q_nope=rn(pb.B, pb.H, pb.nope, bf16=True), q_rope=rn(pb.B, pb.H, pb.rope, bf16=True),
+                kv_b=rn(pb.H * (pb.nope + pb.v), pb.L, std=w_std, bf16=True),
+                q_idx=rn(pb.B, pb.n_ih, pb.hd), w_idx=rn(pb.B, pb.n_ih))

@@ -642,6 +642,45 @@ def test_dsa_decode_call_paged():
     _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(1,))
 
 
+def test_dsa_decode_call_batched_paged_full_size():
+    """The batched paged step at full size, as the benchmark launches it: 32 sequences of
+    8k..131k tokens in 64-token blocks in a random physical order, the indexer pool tiled,
+    k = 2048.  The fused call equals the composed calls bit for bit on every row; the
+    shortest, the longest and the first sequence also meet the oracle."""
+    pb = synth.paged_batch(5, meta_only=True)
+    T, k, bs = pb.max_blocks * pb.block_size, synth.TOPK, pb.block_size
+    log(f"mla_dsa_decode batched paged B={pb.B} sum_len={int(pb.seq_len.sum())} T={T} k={k}")
+    d = synth.paged_values_torch(pb, 1005, torch.device("cuda:0"))
+    qn, qr, qi, wi, kvb = d["q_nope"], d["q_rope"], d["q_idx"], d["w_idx"], d["kv_b"]
+    kv = mla.KvCache(d["lc"], d["rc"], synth.tile_index_keys(d["ic"]), seq_len=dev(pb.seq_len), max_seq_len=T,
+                     block_table=dev(pb.block_table), block_size=bs, ic_layout=mla.MLA_IC_TILE64)
+    sm = 1.0 / math.sqrt(pb.nope + pb.rope)
+    qr0 = qr.clone()
+    out, sc, sel, nsel = mla.mla_dsa_decode(qn, qr, qi, wi, kvb, kv, T, k, sm)
+    assert torch.equal(qr, qr0)
+    qr2 = qr.clone()
+    mla.mla_rope_interleave(qr2, dev(pb.seq_len - 1), 0, pb.rope)
+    sc2, sel2, nsel2 = mla.dsa_index_select(qi, wi, kv, T, k)
+    out2 = mla.mla_absorbed_decode(qn, qr2, kvb, kv, sm, sel=sel2, nsel=nsel2)
+    assert torch.equal(sc.view(torch.int32), sc2.view(torch.int32))
+    assert torch.equal(sel, sel2) and torch.equal(nsel, nsel2) and torch.equal(out, out2)
+    assert bool((nsel == k).all())
+    sc_h, sel_h, out_h = host(sc), host(sel), host(out)
+    for b in sorted({int(np.argmin(pb.seq_len)), int(np.argmax(pb.seq_len)), 0}):
+        n = int(pb.seq_len[b])
+        log(f"  oracle row {b} len {n}")
+        r = dev(pb.rows(b, np.arange(n)))
+        ref_s = oracle.index_scores(host(qi[b]), host(wi[b]), host(d["ic"].index_select(0, r)))
+        assert np.array_equal(sc_h[b, :n].view(np.uint32), ref_s.view(np.uint32)), b
+        assert np.all(np.isneginf(sc_h[b, n:])), b
+        ref_sel, ref_n = oracle.topk(ref_s, n, k)
+        assert ref_n == k and np.array_equal(sel_h[b], ref_sel[:k]), b
+        q_rot = oracle.rope_interleave(host(qr0[b])[None], np.array([n - 1], np.int32), 0, pb.rope)[0]
+        ref = oracle.absorbed_decode(host(qn[b]), q_rot, host(kvb), host(d["lc"].index_select(0, r)),
+                                     host(d["rc"].index_select(0, r)), ref_sel[:k], pb.v, sm)
+        assert rel_err(out_h[b], ref) <= TOL_BF16, b
+
+
 def test_dsa_decode_call_fp32_generic_path():
     T, k = 1500, 256
     d = synth.decode(98, T, B=2, dsa=True, bf16=False)
