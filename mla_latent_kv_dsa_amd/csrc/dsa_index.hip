@@ -230,6 +230,10 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     // whole tiles past the last scored key
     for (int64_t t = ntv * 64 + (int64_t)blockIdx.x * 64 * IXM_WAVES + tid; t < t_max; t += waves_total * 64)
         out[t] = -INFINITY;
+    if ((int64_t)blockIdx.x * IXM_WAVES >= ntv) {   // no tile of a shorter row: an empty list, no query staging
+        if (HIST && tid == 0) hcnt[(int64_t)b * parts_max + blockIdx.x] = 0u;
+        return;
+    }
 
     if (HIST)
         for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) hs[i] = 0u;
@@ -296,11 +300,12 @@ static int64_t ixm_grid_x(int32_t B, int64_t t_max, bool tiled)
     const int64_t ntiles = (t_max + 63) / 64;
     int64_t bx;
     if (tiled) {
-        // tiled keys: one workgroup per CU over the chip (one wave per SIMD), two tiles or more
-        // per wave, so that a wave requests its next tile while it finishes the current one
+        // tiled keys: two tiles or more per wave, so that a wave requests its next tile while it
+        // finishes the current one, and at most 256 workgroups per row (one per CU for a single
+        // row).  Rows of a batch differ in length: the workgroups past a row's last key exit at
+        // once and the many short workgroups keep every CU busy until the longest rows are done.
         bx = (ntiles + 2 * IXM_WAVES - 1) / (2 * IXM_WAVES);
-        const int64_t cap = 256 / B > 1 ? 256 / B : 1;
-        if (bx > cap) bx = cap;
+        if (bx > 256) bx = 256;
     } else {
         // row keys: about 3 resident waves per SIMD over the chip; each wave strides over the tiles
         bx = 768 / B;

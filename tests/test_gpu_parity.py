@@ -254,7 +254,7 @@ def _ixm_parts(B, T, tiled):
     grid: tiles of 64 keys, 4 waves per workgroup, wave (p, w) takes tiles 4 p + w + 4 bx j)."""
     ntiles = (T + 63) // 64
     if tiled:
-        bx = min(max(256 // B, 1), (ntiles + 7) // 8)
+        bx = min(256, (ntiles + 7) // 8)
     else:
         bx = min(max(768 // B, 1), (ntiles + 3) // 4)
     bx = max(bx, 1)
