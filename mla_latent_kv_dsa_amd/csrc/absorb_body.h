@@ -96,4 +96,74 @@ __device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, 
     }
 }
 
+// Batches of at least AB_MFMA_B queries: the same job on v_mfma_f32_16x16x32_bf16.  The job's
+// W_UK block (qk_nope rows x 128 columns) is staged in LDS once (rows padded to AB_WROWB bytes
+// so the transposed reads of four rows fall in distinct banks); the queries go straight from
+// memory into registers as the A operand (16 queries x 32 dims per product), the transposed LDS
+// reads of W_UK give the B operand, and wave w produces columns 32w .. 32w+31 for every query
+// (fp32 products summed in the matrix core, bf16 out).  sh: nope * AB_WROWB bytes.
+constexpr int AB_MFMA_B = 4;
+constexpr int AB_WROWB = 288;
+
+typedef short ab_v4s __attribute__((ext_vector_type(4)));
+typedef short ab_v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 ab_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float ab_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NR>   // qk_nope / 16
+__device__ __forceinline__ void absorb_block_mfma(const bf16_t *__restrict__ q_nope, const bf16_t *__restrict__ kv_b,
+                                                  int B, int v, bf16_t *__restrict__ q_abs, int cb, int h,
+                                                  char *__restrict__ sh, int tid)
+{
+    constexpr int nope = 16 * NR, KS = nope / 32;
+    static_assert(nope % 32 == 0, "qk_nope must be a multiple of 32");
+    const int lane = tid & 63, wave = tid >> 6, jj = lane & 15, quad = lane >> 4;
+    // stage W_UK[h][:, 128 cb .. 128 cb + 127]: nope rows x 16 pieces of 16 B, NR pieces per thread
+    {
+        const bf16_t *W = kv_b + (int64_t)h * (nope + v) * AB_L + cb * 128;
+        uint4 t[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int pcs = tid + 256 * i, r = pcs >> 4, pc = pcs & 15;
+            t[i] = *reinterpret_cast<const uint4 *>(W + (int64_t)r * AB_L + 8 * pc);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int pcs = tid + 256 * i, r = pcs >> 4, pc = pcs & 15;
+            *reinterpret_cast<uint4 *>(sh + r * AB_WROWB + 16 * pc) = t[i];
+        }
+    }
+    __syncthreads();
+    // B operand of dims 32 ks + 8 quad + e, column jj of tile nt: rows 32 ks + 8 quad + (0..3 | 4..7)
+    const char *wb = sh + (8 * quad + (jj >> 2)) * AB_WROWB + 2 * (32 * wave + 4 * (jj & 3));
+    for (int b0 = 0; b0 < B; b0 += 16) {
+        const int bq = b0 + jj < B ? b0 + jj : B - 1;
+        const bf16_t *qa = q_nope + ((int64_t)bq * AB_H + h) * nope + 8 * quad;
+        uint4 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
+        ab_f32x4 acc[2] = {ab_f32x4{0.f, 0.f, 0.f, 0.f}, ab_f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const char *p = wb + 32 * ks * AB_WROWB + 32 * nt;
+                const ab_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ab_v4s *)p);
+                const ab_v4s hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ab_v4s *)(p + 4 * AB_WROWB));
+                const ab_v8s bt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(ab_bf16x8, a[ks]),
+                                                                  __builtin_bit_cast(ab_bf16x8, bt), acc[nt], 0, 0, 0);
+            }
+        // result register r of lane (jj, quad): query b0 + 4 quad + r, column 16 nt + jj of the wave
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int b = b0 + 4 * quad + r;
+                if (b < B) q_abs[((int64_t)b * AB_H + h) * AB_L + cb * 128 + 32 * wave + 16 * nt + jj] = f2bf(acc[nt][r]);
+            }
+    }
+}
+
 }  // namespace mla

@@ -71,6 +71,16 @@ __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nop
     absorb_block<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs, threadIdx.x);
 }
 
+// grid (DM_L / 128, H): the matrix-core job for batches (absorb_block_mfma).
+template <int NR>
+__global__ __launch_bounds__(256) void absorb_q_mfma(const bf16_t *__restrict__ q_nope,
+                                                     const bf16_t *__restrict__ kv_b, int B, int v,
+                                                     bf16_t *__restrict__ q_abs)
+{
+    extern __shared__ __attribute__((aligned(16))) char sh_w[];   // W_UK block, nope rows of AB_WROWB bytes
+    absorb_block_mfma<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_w, threadIdx.x);
+}
+
 // ------------------------------------------------------------------------------ attention core
 // grid (NS, DM_H / 16, B), 256 threads: split s of sequence b (keys [s*kps, min((s+1)*kps, nk)))
 // against heads 16g .. 16g+15.  Up to 128 keys at a time are staged in LDS: every wave copies
@@ -288,6 +298,254 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
 #pragma unroll
         for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = acc[ct][r];
     if (wave == 0 && quad == 0) {
+        m_part[((int64_t)b * NS + s) * DM_H + h] = m_run;
+        l_part[((int64_t)b * NS + s) * DM_H + h] = l_run;
+    }
+}
+
+// ------------------------------------------------------------------------------ attention core, batches
+// grid (NS, B), 256 threads: split s of sequence b against all 64 heads, wave w owning heads
+// 16w .. 16w+15, so every key reaches the CU once for all heads (dec_core above brings it in once
+// per group of 16 heads, which only pays when a single query leaves CUs idle).  The split's keys
+// go in groups of 256: thread t resolves key g0 + t to its cache row (LDS), then 32-key chunks
+// are staged through four LDS buffers, three chunks in flight while one is computed.  Wave w
+// copies the latent rows of keys 8w .. 8w+7 of a chunk (one 1 KB row per DMA) and their rope
+// rows (eight 128 B rows in one DMA; the 16-byte pieces of key t's row are stored in the order
+// piece ^ (t % 8), which spreads the operand reads over the banks).  Per chunk, in every wave:
+//   S[key][head] = q_abs . Lc + q_rope . Rc over two 16-key tiles, v_mfma_f32_16x16x32_bf16;
+//   the online softmax of the chunk is wave-local (all keys of the chunk are in the wave), with
+//   a lazy reference maximum: it moves only when a chunk exceeds it by more than 2^MH_LAZY, so
+//   the O rows are rescaled rarely and P stays below 2^MH_LAZY (the partials carry that
+//   reference, which is all the combine needs);
+//   P stays in registers as the A operand of O += P Lc: the k slots of lane (j, q) are keys
+//   4q .. 4q+3 of the two key tiles, and the transposed reads of Lc fetch the same keys for the
+//   B operand, so P needs no pass through LDS.
+// O (16 heads x 512 columns per wave), the reference maximum and the sum of the rounded P go to
+// the same partials as dec_core's.
+constexpr int MH_ROWB = 1072;   // bytes per staged latent row (conflict-free, as dec_core)
+constexpr int MH_RCB = 128;     // bytes per staged rope row
+constexpr int MH_KC = 32;       // keys per chunk
+constexpr int MH_NBUF = 4;      // chunk buffers
+constexpr int MH_DMA = MH_KC / 4 + 1;   // DMAs per wave and chunk
+constexpr float MH_LAZY = 8.f;  // slack of the reference maximum (log2 units)
+constexpr int MH_PF = 6;        // score operand reads in flight
+constexpr int MH_PV = 4;        // value column tiles read ahead
+constexpr size_t MH_LDS = (size_t)MH_NBUF * MH_KC * (MH_ROWB + MH_RCB) + 256 * sizeof(int64_t);
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int i)
+{
+    return ((int64_t)__builtin_amdgcn_readlane((int)(x >> 32), i) << 32) | (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+}
+
+// Maximum and sum over the four 16-lane rows (lanes j, j+16, j+32, j+48), left in every lane:
+// v_permlane32_swap and v_permlane16_swap on two copies exchange the halves and rows (no LDS).
+__device__ __forceinline__ float mh_max4(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float mh_sum4(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// s_waitcnt vmcnt(n * MH_DMA) for a wave-uniform n in 0..MH_NBUF-1, then the block barrier
+__device__ __forceinline__ void mh_wait_chunks(int n)
+{
+    static_assert(MH_NBUF == 4 && MH_DMA == 9, "wait counts below");
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(27)\n\ts_barrier" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) void dec_core_mh(const bf16_t *__restrict__ q_abs, const bf16_t *__restrict__ q_rope,
+                                                   KvView kv, const int32_t *__restrict__ sel,
+                                                   const int32_t *__restrict__ nsel, int sel_stride, float scale_log2,
+                                                   int kps, float *__restrict__ o_part, float *__restrict__ m_part,
+                                                   float *__restrict__ l_part)
+{
+    extern __shared__ __attribute__((aligned(16))) char mh_smem[];
+    char *sL = mh_smem;                                                          // [NBUF][KC][MH_ROWB]
+    char *sR = mh_smem + MH_NBUF * MH_KC * MH_ROWB;                              // [NBUF][KC][MH_RCB]
+    int64_t *sRow = reinterpret_cast<int64_t *>(sR + MH_NBUF * MH_KC * MH_RCB);  // [256]
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = blockIdx.x, NS = gridDim.x, b = blockIdx.y;
+    const int jj = lane & 15, quad = lane >> 4;
+    const int h = 16 * wave + jj;
+    const bf16_t *qa = q_abs + ((int64_t)b * DM_H + h) * DM_L + 8 * quad;
+    const bf16_t *qr = q_rope + ((int64_t)b * DM_H + h) * DM_R + 8 * quad;
+    const bf16_t *dummy = q_abs + (int64_t)b * DM_H * DM_L + 8 * lane;   // any readable 1 KB
+    uint4 Bq[18];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) Bq[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Bq[16 + ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
+    const int64_t sl = seq_len_of(kv, b);
+    const int64_t nk = dec_nkeys(kv, b, sel, nsel, sel_stride);
+    const int64_t k0 = (int64_t)s * kps;
+    const int64_t k1 = k0 + kps < nk ? k0 + kps : nk;
+    const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc);
+    const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
+
+    float m_run = -INFINITY, l_run = 0.f;   // head h
+    f32x4 acc[32];                           // column tile ct: heads 16 wave + 4 quad + r, column 16 ct + jj
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // latent and rope rows of chunk c (keys MH_KC c .. of the group) into buffer buf
+    auto issue = [&](int c, int buf) {
+        const int64_t rw = sRow[MH_KC * c + 8 * wave + (lane & 7)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = readlane64(rw, i);
+            const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * lane : dummy;
+            lds_dma16(src, lds_addr(sL + (MH_KC * buf + 8 * wave + i) * MH_ROWB));
+        }
+        const int kc = 8 * wave + (lane >> 3);   // key of the chunk whose rope piece this lane copies
+        const int64_t r = sRow[MH_KC * c + kc];
+        const int pc = (lane & 7) ^ (kc & 7);
+        const bf16_t *src = r >= 0 ? rc + r * DM_R + 8 * pc : dummy;
+        lds_dma16(src, lds_addr(sR + (MH_KC * buf + 8 * wave) * MH_RCB));
+    };
+
+    for (int64_t g0 = k0; g0 < k1; g0 += 256) {
+        const int64_t j = g0 + tid;
+        sRow[tid] = j < k1 ? dec_row(kv, b, j, sl, sel, sel_stride) : -1;
+        __syncthreads();
+        const int nc = (int)(((k1 - g0 < 256 ? k1 - g0 : 256) + MH_KC - 1) / MH_KC);
+        // the query operands are complete before the first DMA: the compiler's own wait for them
+        // would otherwise count the DMAs (which it does not see) and wait for later chunks too
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) asm volatile("" ::"v"(Bq[ks].x), "v"(Bq[ks].y), "v"(Bq[ks].z), "v"(Bq[ks].w));
+        for (int c = 0; c < MH_NBUF - 1 && c < nc; ++c) issue(c, c);
+        for (int c = 0; c < nc; ++c) {
+            const int buf = c % MH_NBUF;
+            if (c + MH_NBUF - 1 < nc) issue(c + MH_NBUF - 1, (c + MH_NBUF - 1) % MH_NBUF);
+            mh_wait_chunks(nc - 1 - c);   // the chunks issued after c may stay in flight
+            const uint64_t vmask = __ballot(lane < MH_KC && sRow[MH_KC * c + (lane & (MH_KC - 1))] >= 0);
+            const char *bL = sL + MH_KC * buf * MH_ROWB;
+            const char *bR = sR + MH_KC * buf * MH_RCB;
+            // scores: register r of tile kt is key 16 kt + 4 quad + r, head h.  Step i of 36 takes
+            // tile i % 2, operand slice i / 2 (16 latent slices, then 2 rope slices); the LDS
+            // reads run MH_PF steps ahead of their products.
+            f32x4 d[2];
+            {
+                // four accumulator chains: tile i % 2, even or odd slice (i / 2) % 2
+                f32x4 dd[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dd[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                auto a_op = [&](int i) -> uint4 {
+                    const int kt = i & 1, ks = i >> 1, key = 16 * kt + jj;
+                    if (ks < 16) return *reinterpret_cast<const uint4 *>(bL + key * MH_ROWB + 16 * quad + 64 * ks);
+                    return *reinterpret_cast<const uint4 *>(bR + key * MH_RCB + 16 * ((4 * (ks - 16) + quad) ^ (key & 7)));
+                };
+                uint4 ring[MH_PF];
+#pragma unroll
+                for (int i = 0; i < MH_PF; ++i) ring[i] = a_op(i);
+#pragma unroll
+                for (int i = 0; i < 36; ++i) {
+                    const uint4 a = ring[i % MH_PF];
+                    if (i + MH_PF < 36) ring[i % MH_PF] = a_op(i + MH_PF);
+                    dd[i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(Bq[i >> 1]), dd[i & 3], 0, 0, 0);
+                }
+                d[0] = dd[0] + dd[2];
+                d[1] = dd[1] + dd[3];
+#pragma unroll
+                for (int i = 0; i < MH_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS reads
+#pragma unroll
+                for (int i = 0; i < 36 - MH_PF; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < MH_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            float sv[2][4], mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sv[kt][r] = ((vmask >> (16 * kt + 4 * quad + r)) & 1) ? d[kt][r] * scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, sv[kt][r]);
+                }
+            mx = mh_max4(mx);
+            const bool move = mx > m_run + MH_LAZY;
+            const float m_new = move ? mx : m_run;
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            float psum = 0.f;
+            uint4 pa;   // A operand: keys 4 quad .. 4 quad + 3 of tile 0, then of tile 1
+            {
+                float p[2][4];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p[kt][r] = sv[kt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[kt][r] - m_new);
+                pa.x = pack_bf16(p[0][0], p[0][1], psum);
+                pa.y = pack_bf16(p[0][2], p[0][3], psum);
+                pa.z = pack_bf16(p[1][0], p[1][1], psum);
+                pa.w = pack_bf16(p[1][2], p[1][3], psum);
+            }
+            psum = mh_sum4(psum);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            // values: output rows are heads 4 quad + r, whose factors sit in lanes 4 quad + r
+            if (__ballot(move) != 0) {
+                float al[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * quad + r, 64);
+#pragma unroll
+                for (int ct = 0; ct < 32; ++ct) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[ct][r] *= al[r];
+                    __builtin_amdgcn_sched_barrier(0);   // one tile at a time: no VGPR copy of all of O
+                }
+            }
+            {
+                // values: the transposed reads of column tile ct run MH_PV tiles ahead of its product
+                const char *vb = bL + (4 * quad + (jj >> 2)) * MH_ROWB + 8 * (jj & 3);
+                auto b_op = [&](int ct) -> v8s {
+                    const v4s lo =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + 32 * ct));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(vb + 16 * MH_ROWB + 32 * ct));
+                    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
+                v8s ring[MH_PV];
+#pragma unroll
+                for (int i = 0; i < MH_PV; ++i) ring[i] = b_op(i);
+#pragma unroll
+                for (int ct = 0; ct < 32; ++ct) {
+                    const v8s vt = ring[ct % MH_PV];
+                    if (ct + MH_PV < 32) ring[ct % MH_PV] = b_op(ct + MH_PV);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), __builtin_bit_cast(bf16x8, vt),
+                                                                      acc[ct], 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * MH_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < 32 - MH_PV; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < MH_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __syncthreads();   // buffer buf is free for chunk c + MH_NBUF; sRow is free after the last chunk
+        }
+    }
+    float *po = o_part + (((int64_t)b * NS + s) * DM_H + 16 * wave + 4 * quad) * DM_L + jj;
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = acc[ct][r];
+    if (quad == 0) {
         m_part[((int64_t)b * NS + s) * DM_H + h] = m_run;
         l_part[((int64_t)b * NS + s) * DM_H + h] = l_run;
     }
@@ -521,13 +779,16 @@ struct DecPlan {
     int64_t kps;   // keys per split (multiple of 64)
 };
 
-// Splits: at most 256 keys per split, enough splits for ~256 blocks (4 head groups each), at
-// least 64 keys per split and at most CU_MAXNS splits.
+// Batches of at least MH_MIN_B queries run dec_core_mh (all heads per workgroup).
+constexpr int MH_MIN_B = 4;
+
+// Splits: at most 256 keys per split, enough splits for ~256 workgroups (dec_core: 4 head groups
+// each), at least 64 keys per split and at most CU_MAXNS splits.
 static DecPlan dec_plan(int32_t B, int64_t max_keys)
 {
     DecPlan p;
     const int64_t by_len = (max_keys + 255) / 256;
-    const int64_t by_fill = (64 + B - 1) / (int64_t)B;
+    const int64_t by_fill = ((B >= MH_MIN_B ? 256 : 64) + B - 1) / (int64_t)B;
     const int64_t most = (max_keys + DC_KC - 1) / DC_KC;
     int64_t ns = by_len > by_fill ? by_len : by_fill;
     if (ns > most) ns = most;
@@ -550,6 +811,14 @@ static mla_status enable_big_lds()
         if (e == hipSuccess)
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<false>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core_mh),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)MH_LDS);
+        const void *am[3] = {reinterpret_cast<const void *>(&absorb_q_mfma<8>),
+                             reinterpret_cast<const void *>(&absorb_q_mfma<12>),
+                             reinterpret_cast<const void *>(&absorb_q_mfma<16>)};
+        for (int i = 0; i < 3 && e == hipSuccess; ++i)
+            e = hipFuncSetAttribute(am[i], hipFuncAttributeMaxDynamicSharedMemorySize, 16 * 16 * AB_WROWB);
         const void *cu[4] = {reinterpret_cast<const void *>(&combine_unabsorb<1, 16>),
                              reinterpret_cast<const void *>(&combine_unabsorb<1, 32>),
                              reinterpret_cast<const void *>(&combine_unabsorb<1, 64>),
@@ -613,6 +882,17 @@ mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_di
 {
     if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: B > 65535");
     const DecWs w = dec_ws(ws, B, dec_plan(B, 0));
+    if (B >= AB_MFMA_B) {
+        mla_status st = enable_big_lds();
+        if (st) return st;
+        const dim3 g(DM_L / 128, DM_H), blk(256);
+        const size_t shm = (size_t)d.qk_nope * AB_WROWB;
+        const bf16_t *qn = (const bf16_t *)q_nope, *kb = (const bf16_t *)kv_b;
+        if (d.qk_nope == 128) hipLaunchKernelGGL(absorb_q_mfma<8>, g, blk, shm, s, qn, kb, B, d.v_head, w.q_abs);
+        else if (d.qk_nope == 192) hipLaunchKernelGGL(absorb_q_mfma<12>, g, blk, shm, s, qn, kb, B, d.v_head, w.q_abs);
+        else hipLaunchKernelGGL(absorb_q_mfma<16>, g, blk, shm, s, qn, kb, B, d.v_head, w.q_abs);
+        return check_launch("absorb_q_mfma");
+    }
     // at most 32 queries' worth of q staged in LDS per launch
     for (int b0 = 0; b0 < B; b0 += 32) {
         const int nb = B - b0 < 32 ? B - b0 : 32;
@@ -646,7 +926,10 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     // the W_UV slice when the decode leaves at least as many CUs idle
     const int pf = (int64_t)B * p.ns * (DM_H / 16) <= 128 ? 1 : 0;
     const bf16_t *wuv = (const bf16_t *)kv_b + (int64_t)d.qk_nope * DM_L;
-    if (p.kps <= DC_SUP * DC_KC)
+    if (B >= MH_MIN_B)
+        hipLaunchKernelGGL(dec_core_mh, dim3(p.ns, B), dim3(256), MH_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv, sel,
+                           nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
+    else if (p.kps <= DC_SUP * DC_KC)
         hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
                            w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);

@@ -457,8 +457,13 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
     }
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
     const int a = 2 * ((int)blockIdx.x - nres) + half, cb = a & 3, h = a >> 2;
-    float *shj = reinterpret_cast<float *>(sr_dyn) + half * (sa.B * 16 * NR + 4 * AB_QB * 128);
-    absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, shj, jt);
+    if (sa.B >= AB_MFMA_B) {
+        absorb_block_mfma<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h,
+                              reinterpret_cast<char *>(sr_dyn) + half * 16 * NR * AB_WROWB, jt);
+    } else {
+        float *shj = reinterpret_cast<float *>(sr_dyn) + half * (sa.B * 16 * NR + 4 * AB_QB * 128);
+        absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, shj, jt);
+    }
     if (cb != 0) return;
     const int hr = sa.rope / 2;
     for (int p = jt; p < sa.B * hr; p += 256) {
@@ -576,7 +581,8 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
                            sw.wp, sw.rows, sel, nsel);
         return check_launch("sel_resolve");
     }
-    const size_t dyn_abs = 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
+    const size_t dyn_abs = B >= AB_MFMA_B ? 2 * (size_t)side->nope * AB_WROWB
+                                          : 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
     const dim3 g((unsigned)(B + 2 * AB_H));
 #define SRA_LAUNCH(NR)                                                                                              \

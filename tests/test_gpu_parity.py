@@ -720,6 +720,38 @@ def test_decode_generic_and_matrix_core_paths_agree():
         assert rel_err(slow[b], ref) <= TOL_BF16
 
 
+def test_decode_batched_long_splits_and_growing_scores():
+    """A batch on the all-heads kernel with more than 256 keys per split (dense, 20000 keys:
+    64 splits of 320) and scores that grow along the sequence (latent rows scaled up with the
+    position), so later chunks keep raising the running maximum."""
+    B, T = 4, 20000
+    d = synth.decode(83, T, B=B)
+    lc = synth.bf16_bits_to_f32(d.lc).reshape(B, T, -1)
+    lc *= (1.0 + np.arange(T, dtype=np.float32) / 2000.0)[None, :, None]
+    d.lc = synth.to_bf16_bits(lc.reshape(B * T, -1))
+    seq_len = [T, 19999, 16385, 300]
+    log("decode batched long splits")
+    out, sm = _run_decode(d, seq_len)
+    for b in (0, 2, 3):
+        assert rel_err(out[b], _decode_ref(d, b, np.arange(seq_len[b]), sm)) <= TOL_BF16, b
+
+
+@pytest.mark.parametrize("nope,v", [(128, 128), (256, 192)])
+def test_decode_batched_other_head_dims(nope, v):
+    """Batches on the matrix-core absorption and all-heads attention with the other supported
+    qk_nope sizes, as separate calls and inside the fused step (its absorption runs beside the
+    selection); the two equal each other bit for bit and meet the oracle."""
+    B, T, k = 5, 1500, 512
+    d = synth.decode(84 + nope, T, B=B, nope=nope, v=v, dsa=True)
+    seq_len = [T, 1499, 900, 513, 200]
+    log(f"decode batched nope={nope} v={v}")
+    out, sm = _run_decode(d, seq_len)
+    for b in (0, 4):
+        assert rel_err(out[b], _decode_ref(d, b, np.arange(seq_len[b]), sm)) <= TOL_BF16, b
+    kv = _kv(d.lc, d.rc, d.ic, seq_len, T, seq_stride=T)
+    _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(1, 4))
+
+
 def test_decode_batched_selected_large():
     """Many sequences with selections of different sizes (covers multi-tile splits)."""
     B, T, k = 6, 3000, 2048
