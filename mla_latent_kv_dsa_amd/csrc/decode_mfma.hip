@@ -692,6 +692,114 @@ __global__ __launch_bounds__(256) void combine_unabsorb(const float *__restrict_
     }
 }
 
+// ------------------------------------------------------------------------------ combine, batches
+// Batches of at least MH_MIN_B queries combine in two launches, so that every split partial
+// and every W_UV row is read once (combine_unabsorb re-reads the partials for each 64-row slice
+// of W_UV):
+//   combine_reduce  grid (ceil(B H / 8)), 256 threads: eight (query, head) pairs per workgroup;
+//                   wave w reduces the split maxima and sums of pairs 2w, 2w + 1 into the
+//                   factors f_s (as combine_unabsorb), then thread t forms columns 2t, 2t + 1 of
+//                   clat = sum_s f_s O_s (in split order) for the eight pairs, stored as bf16;
+//   unabsorb        grid (v / 64, H), 256 threads: wave w holds rows 64 bx + 16 w .. +16 of W_UV[h]
+//                   as the A operand (read straight from memory, K = 512 latent columns) and
+//                   multiplies them with clat of 16 queries at a time (B operand, also straight
+//                   from memory): out[b][h][j] on v_mfma_f32_16x16x32_bf16.
+constexpr int CR_PAIRS = 8;
+constexpr int CR_SB = 8;   // splits loaded per batch (all of them at once for up to 8 splits)
+
+__global__ __launch_bounds__(256) void combine_reduce(const float *__restrict__ o_part, const float *__restrict__ m_part,
+                                                      const float *__restrict__ l_part, int NS, int npairs,
+                                                      bf16_t *__restrict__ clat)
+{
+    __shared__ float sF[CR_PAIRS][CU_MAXNS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p0 = CR_PAIRS * blockIdx.x;
+    // pair p = b * DM_H + h; its split s partials sit at ((b * NS + s) * DM_H + h)
+    auto part = [&](int p, int s) { return ((int64_t)(p / DM_H) * NS + s) * DM_H + p % DM_H; };
+    float2 x[CR_PAIRS][CR_SB];
+    auto load = [&](int s0) {
+#pragma unroll
+        for (int q = 0; q < CR_PAIRS; ++q)
+#pragma unroll
+            for (int u = 0; u < CR_SB; ++u) {
+                const int p = p0 + q < npairs ? p0 + q : npairs - 1, s = s0 + u < NS ? s0 + u : NS - 1;
+                x[q][u] = *reinterpret_cast<const float2 *>(o_part + part(p, s) * DM_L + 2 * tid);
+            }
+    };
+    load(0);
+#pragma unroll
+    for (int k = 0; k < CR_PAIRS / 4; ++k) {
+        const int q = 2 * wave + k;
+        const int p = p0 + q < npairs ? p0 + q : npairs - 1;
+        const int sc = lane < NS ? lane : NS - 1;
+        const float m = lane < NS ? m_part[part(p, sc)] : -INFINITY;
+        const float l = lane < NS ? l_part[part(p, sc)] : 0.f;
+        const float M = wave_max_dpp(m);
+        const float e = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        const float L = wave_sum_dpp(e * l);
+        sF[q][lane] = L > 0.f ? e / L : 0.f;
+    }
+    __syncthreads();
+    float o[CR_PAIRS][2];
+#pragma unroll
+    for (int q = 0; q < CR_PAIRS; ++q) o[q][0] = o[q][1] = 0.f;
+    for (int s0 = 0; s0 < NS; s0 += CR_SB) {
+        if (s0 > 0) load(s0);
+#pragma unroll
+        for (int q = 0; q < CR_PAIRS; ++q)
+#pragma unroll
+            for (int u = 0; u < CR_SB; ++u) {
+                // factors past the last split are zero (sF holds CU_MAXNS >= NS entries)
+                const float f = s0 + u < NS ? sF[q][s0 + u] : 0.f;
+                o[q][0] = fmaf(f, x[q][u].x, o[q][0]);
+                o[q][1] = fmaf(f, x[q][u].y, o[q][1]);
+            }
+    }
+#pragma unroll
+    for (int q = 0; q < CR_PAIRS; ++q)
+        if (p0 + q < npairs) {
+            const bf16x2 c = {(__bf16)o[q][0], (__bf16)o[q][1]};
+            *reinterpret_cast<uint32_t *>(clat + (int64_t)(p0 + q) * DM_L + 2 * tid) = __builtin_bit_cast(uint32_t, c);
+        }
+}
+
+__global__ __launch_bounds__(256) void unabsorb(const bf16_t *__restrict__ clat, const bf16_t *__restrict__ kv_b, int B,
+                                                int nope, int v, float *__restrict__ out)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.y, j0 = 64 * blockIdx.x + 16 * wave;
+    const int jj = lane & 15, quad = lane >> 4;
+    const bf16_t *wr = kv_b + ((int64_t)h * (nope + v) + nope + j0 + jj) * DM_L + 8 * quad;
+    uint4 a[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const uint4 *>(wr + 32 * ks);
+    // B operand of the query tile starting at b0: clat of query b0 + jj (clamped), 32 ks + 8 quad
+    auto load_c = [&](uint4 (&c)[16], int b0) {
+        const int bq = b0 + jj < B ? b0 + jj : B - 1;
+        const bf16_t *cr = clat + ((int64_t)bq * DM_H + h) * DM_L + 8 * quad;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) c[ks] = *reinterpret_cast<const uint4 *>(cr + 32 * ks);
+    };
+    uint4 cn[16];
+    load_c(cn, 0);
+    for (int b0 = 0; b0 < B; b0 += 16) {
+        uint4 c[16];
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) c[ks] = cn[ks];
+        if (b0 + 16 < B) load_c(cn, b0 + 16);   // the next tile is in flight during this one
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[ks]), as_bf16x8(c[ks]), d, 0, 0, 0);
+        // register r of lane (jj, quad): row j0 + 4 quad + r of W_UV, query b0 + jj
+        if (b0 + jj < B) {
+            float *o = out + ((int64_t)(b0 + jj) * DM_H + h) * v + j0 + 4 * quad;   // 4-byte aligned only
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = d[r];
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------ combine, one query
 // B = 1: grid (v / 128, H), 512 threads.  Waves 4..7 copy the workgroup's 128 W_UV rows of head h
 // (rows 128 bx ..) into LDS, 32 rows each, and only wait for them; waves 0..3 load the split
@@ -846,17 +954,19 @@ size_t decode_mfma_ws(const mla_dims &d, int32_t B, int64_t max_keys)
     bytes += al256((size_t)B * p.ns * DM_H * 4);                // split maxima
     bytes += al256((size_t)B * p.ns * DM_H * 4);                // split sums
     bytes += al256((size_t)B * p.ns * DM_H * DM_L * 4);         // split outputs
+    bytes += al256((size_t)B * DM_H * DM_L * 2);                // combined latent rows (batches)
     (void)d;
     return bytes;
 }
 
 // Workspace layout (the first part depends on B only, so the absorb step can run without
-// knowing the key count): q_abs | split maxima | split sums | split outputs
+// knowing the key count): q_abs | split maxima | split sums | split outputs | combined latent rows
 struct DecWs {
     bf16_t *q_abs;
     float *m_part;
     float *l_part;
     float *o_part;
+    bf16_t *clat;
 };
 
 static DecWs dec_ws(void *ws, int32_t B, const DecPlan &p)
@@ -870,6 +980,8 @@ static DecWs dec_ws(void *ws, int32_t B, const DecPlan &p)
     w.l_part = reinterpret_cast<float *>(c);
     c += al256((size_t)B * p.ns * DM_H * 4);
     w.o_part = reinterpret_cast<float *>(c);
+    c += al256((size_t)B * p.ns * DM_H * DM_L * 4);
+    w.clat = reinterpret_cast<bf16_t *>(c);
     return w;
 }
 
@@ -941,6 +1053,15 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     if (st) return st;
     const dim3 gc(d.v_head / 64, DM_H, (B + 15) / 16);
     const bf16_t *kb = (const bf16_t *)kv_b;
+    if (B >= MH_MIN_B) {
+        const int npairs = B * DM_H;
+        hipLaunchKernelGGL(combine_reduce, dim3((npairs + CR_PAIRS - 1) / CR_PAIRS), dim3(256), 0, s, w.o_part, w.m_part,
+                           w.l_part, p.ns, npairs, w.clat);
+        st = check_launch("combine_reduce");
+        if (st) return st;
+        hipLaunchKernelGGL(unabsorb, dim3(d.v_head / 64, DM_H), dim3(256), 0, s, w.clat, kb, B, d.qk_nope, d.v_head, out);
+        return check_launch("unabsorb");
+    }
     if (B == 1 && d.v_head % C1_ROWS == 0) {
         const dim3 g1(d.v_head / C1_ROWS, DM_H);
         if (p.ns <= 16)
