@@ -112,6 +112,10 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = seq_len_of(kv, b);
     if (n <= k) return;
+    if ((int64_t)c * SEL_CH >= n) {   // past the row's last key (a shorter row of a batch): an empty slot
+        if (tid == 0) fcnt[(int64_t)b * gridDim.x + c] = 0u;
+        return;
+    }
     // this workgroup's scores and the top of every list part go out together
     const float *row = scores + (int64_t)b * t_max;
     float sv[SEL_CH / 256];
