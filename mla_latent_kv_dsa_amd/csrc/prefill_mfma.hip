@@ -218,30 +218,46 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
     const bool is_rc = is_k && 8 * lane >= NOPE && 8 * lane < QD;
     const int c_off = h * (NOPE + PF_V) + (is_k ? (8 * lane < NOPE ? 8 * lane : 0) : NOPE + 8 * (lane - 32));
     const int rc_off = is_rc ? 8 * lane - NOPE : 0;
-    auto stage = [&](int kt) {
+    // Rc rows of the wave's 16 keys of tile kt: lane i < 16 resolves key 64 kt + 16 wave + i (the
+    // other lanes repeat them).  Resolved before the tile's copies are issued and complete before
+    // the first one: a block-table load consumed between the copies would make the compiler wait
+    // for every copy in flight (it does not see them).
+    auto rows_of = [&](int kt) -> int64_t {
+        const int64_t t0 = (int64_t)kt * PA_BK + 16 * wave + (lane & 15);
+        const int64_t row = kv_row(kv, 0, t0 < kend ? t0 : kend - 1);
+        return row >= 0 ? row : 0;
+    };
+    auto settle = [](int64_t x) { asm volatile("" ::"v"((uint32_t)x), "v"((uint32_t)(x >> 32))); };
+    auto stage = [&](int kt, int64_t rrow) {
         bf16_t *dst = sT + (kt & 1) * PA_BK * PA_ROW;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 16 * wave + i;
             const int64_t t0 = (int64_t)kt * PA_BK + r;
             const int64_t t = t0 < kend ? t0 : kend - 1;
-            const bf16_t *src;
-            if (is_rc) {
-                const int64_t row = kv_row(kv, 0, t);
-                src = rc + (row >= 0 ? row : 0) * PF_R + rc_off;
-            } else {
-                src = C + t * (int64_t)N + c_off;
-            }
+            const int64_t row = ((int64_t)__builtin_amdgcn_readlane((int)(rrow >> 32), i) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)rrow, i);
+            const bf16_t *src = is_rc ? rc + row * PF_R + rc_off : C + t * (int64_t)N + c_off;
             pf_dma16(src, pf_lds_addr(dst + r * PA_ROW));
         }
     };
     const int G = lane >> 4, j16 = lane & 15;   // transposed-read address inside a 16-key step
     const int tr_off = (8 * (G >> 1) + (j16 >> 2)) * PA_ROW + 256 + 16 * (G & 1) + 4 * (j16 & 3);
-    stage(0);
+    {
+        const int64_t rr = rows_of(0);
+        settle(rr);
+        // the query operands too are complete before the first copy (same reason)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bq[ks].x), "v"(bq[ks].y), "v"(bq[ks].z), "v"(bq[ks].w));
+        stage(0, rr);
+    }
     for (int kt = 0; kt < ntile; ++kt) {
         const int64_t k0 = (int64_t)kt * PA_BK;
         if (kt + 1 < ntile) {
-            stage(kt + 1);
+            // with a block table, the wait for these lookups also lands tile kt (issued earlier)
+            const int64_t rr = rows_of(kt + 1);
+            settle(rr);
+            stage(kt + 1, rr);
             asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // tile kt has landed
         } else {
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -259,45 +275,58 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(*reinterpret_cast<const uint4 *>(ka + 16 * ks)),
                                                                 pf_bf16x8(bq[ks]), s[mt], 0, 0, 0);
         }
-        // causal mask, scale, running maximum (lanes l and l ^ 32 hold the same query)
+        // causal mask, only on tiles that reach past the wave's first query (positions < 2^31);
+        // running maximum of the raw scores (lanes l and l ^ 32 hold the same query)
+        const int qpos32 = (int)qpos;
+        if (k0 + PA_BK - 1 > (int64_t)pos_base + i0 + 32 * wave) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = (int)k0 + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (t > qpos32) s[mt][r] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t t = k0 + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const float v = t <= qpos ? s[mt][r] * scale_log2 : -INFINITY;
-                s[mt][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        }
         // the reference maximum moves only when the tile's maximum exceeds it by more than 8
         // (log2 units): until then P = exp2(s - m_run) stays below 2^8, which bf16 P and the
         // fp32 sums hold exactly as well, and the accumulators need no rescaling (the final
-        // normalization divides by the sum taken against the same reference)
+        // normalization divides by the sum taken against the same reference).  Key 0 is in tile
+        // 0 and precedes every query, so the reference is finite from the first tile on and a
+        // masked score (-inf) gives P = exp2(-inf) = 0.
         const bool move = mx > m_run + 8.f;
         const float m_new = move ? mx : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt
+        // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt;
+        // the sum is taken over the rounded values (two-element bf16 dot products with ones)
         uint2 pk[2][4];
         float psum = 0.f;
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        const bf2 one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = s[mt][4 * g + e];
-                    p[e] = v == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v - m_new);
-                }
+                for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][4 * g + e], scale_log2, -m_new));
                 pk[mt][g].x = pf_pack(p[0], p[1]);
                 pk[mt][g].y = pf_pack(p[2], p[3]);
-                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-                const bf2 a = __builtin_bit_cast(bf2, pk[mt][g].x), b = __builtin_bit_cast(bf2, pk[mt][g].y);
-                psum += ((float)a[0] + (float)a[1]) + ((float)b[0] + (float)b[1]);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].x), one2, psum, false);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].y), one2, psum, false);
             }
-        psum += __shfl_xor(psum, 32, 64);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+            psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
         l_run = l_run * alpha + psum;
         m_run = m_new;
         if (__builtin_amdgcn_ballot_w64(move)) {   // wave-uniform: lanes that keep theirs scale by 1
