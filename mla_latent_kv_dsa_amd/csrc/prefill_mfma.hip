@@ -168,6 +168,7 @@ constexpr int PA_BQ = 128, PA_BK = 64;
 constexpr int PA_ROW = 536;    // bf16 per staged key row: K (256) then V (256), pitch 1072 B so that
                                // the K row reads and the transposed V reads fall in distinct banks
 constexpr size_t PA_LDS = (size_t)2 * PA_BK * PA_ROW * 2;   // two tiles
+constexpr int PA_PF = 6;       // score operand reads in flight
 
 
 // grid (ceil(S / 128) * H), 256 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
@@ -264,16 +265,35 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         }
         const bf16_t *tk = sT + (kt & 1) * PA_BK * PA_ROW;
         // S^T: two 32-key tiles; register r of s[mt] is key k0 + 32 mt + 8 (r/4) + 4 hi + r%4
+        // Step i of 2 KS takes key tile i % 2 and slice i / 2; the LDS operand reads run PA_PF steps
+        // ahead of their products (a ring of registers), so their latency hides behind the
+        // matrix cores instead of stalling each product.
         pf32x16 s[2];
+        {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-            const bf16_t *ka = tk + (32 * mt + l32) * PA_ROW + 8 * hi;
+                for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+            const bf16_t *ka = tk + l32 * PA_ROW + 8 * hi;
+            auto a_op = [&](int i) { return *reinterpret_cast<const uint4 *>(ka + (i & 1) * 32 * PA_ROW + 16 * (i >> 1)); };
+            uint4 ring[PA_PF];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(*reinterpret_cast<const uint4 *>(ka + 16 * ks)),
-                                                                pf_bf16x8(bq[ks]), s[mt], 0, 0, 0);
+            for (int i = 0; i < PA_PF; ++i) ring[i] = a_op(i);
+#pragma unroll
+            for (int i = 0; i < 2 * KS; ++i) {
+                const uint4 a = ring[i % PA_PF];
+                if (i + PA_PF < 2 * KS) ring[i % PA_PF] = a_op(i + PA_PF);
+                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(a), pf_bf16x8(bq[i >> 1]), s[i & 1], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS reads
+#pragma unroll
+            for (int i = 0; i < 2 * KS - PA_PF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         // causal mask, only on tiles that reach past the wave's first query (positions < 2^31);
         // running maximum of the raw scores (lanes l and l ^ 32 hold the same query)

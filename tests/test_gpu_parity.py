@@ -525,7 +525,8 @@ def _prefill_glm_check(S, pos_base, seed, out_bf16, rows, heads, bs=0):
     return out
 
 
-@pytest.mark.parametrize("S,pos_base,out_bf16,bs", [(300, 0, False, 0), (200, 333, True, 0), (256, 64, False, 64)])
+@pytest.mark.parametrize("S,pos_base,out_bf16,bs", [(300, 0, False, 0), (200, 333, True, 0), (256, 64, False, 64),
+                                                    (280, 40, False, 32), (300, 36, True, 16)])
 def test_prefill_glm_64_heads(S, pos_base, out_bf16, bs):
     """Ragged query blocks and token tiles, a pos_base offset, bf16 output, a paged cache."""
     log(f"prefill 64 heads S={S} pos_base={pos_base} bf16={out_bf16} bs={bs}")
