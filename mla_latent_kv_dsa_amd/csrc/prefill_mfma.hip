@@ -254,14 +254,13 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
     }
     for (int kt = 0; kt < ntile; ++kt) {
         const int64_t k0 = (int64_t)kt * PA_BK;
+        // tile kt has landed in every wave's share, and every wave is done with tile kt - 1, whose
+        // buffer the next copies fill: one barrier per tile
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 1 < ntile) {
-            // with a block table, the wait for these lookups also lands tile kt (issued earlier)
             const int64_t rr = rows_of(kt + 1);
             settle(rr);
             stage(kt + 1, rr);
-            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // tile kt has landed
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         }
         const bf16_t *tk = sT + (kt & 1) * PA_BK * PA_ROW;
         // S^T: two 32-key tiles; register r of s[mt] is key k0 + 32 mt + 8 (r/4) + 4 hi + r%4
@@ -381,9 +380,6 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
                                                                 0, 0, 0);
             }
         }
-        // every wave has consumed its reads of this tile (they feed the products above) before
-        // the next iteration copies tile kt + 2 over it
-        asm volatile("s_barrier" ::: "memory");
     }
     if (iq >= S) return;
     // register r of o[dt]: dim 32 dt + 8 (r/4) + 4 hi + r%4 of query iq
