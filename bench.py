@@ -587,7 +587,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "prefill", "copy"])
+    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "dsa_decode_paged_b32", "prefill", "copy"])
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -618,6 +618,11 @@ def main():
         sys.exit(1)
     if args.workload == "dsa_decode":
         bench_dsa_decode(args)
+    elif args.workload == "dsa_decode_paged_b32":   # the batched paged configuration on its own line
+        r = bench_batched_paged(args)
+        print(json.dumps({"metric": "MLA+DSA batched paged decode keys·heads/sec", "value": r["keys_heads_per_s"],
+                          "unit": "keys·heads/s", "n_gpus": 1, "ms_per_step": r["ms_per_step"],
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "config": r}), flush=True)
     elif args.workload == "copy":
         bench_copy(args)
     else:
