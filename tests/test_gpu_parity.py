@@ -753,6 +753,20 @@ def test_decode_batched_other_head_dims(nope, v):
     _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(1, 4))
 
 
+def test_dsa_decode_call_batch_over_side_limit():
+    """40 sequences (more than the selection's side workgroups take: the absorption runs as its
+    own launch) of ragged lengths, some shorter than k; fused call == composed calls, rows
+    against the oracle."""
+    B, T, k = 40, 700, 256
+    d = synth.decode(85, T, B=B, dsa=True)
+    seq_len = [T - 13 * b for b in range(B)]
+    seq_len[7] = 100
+    log("mla_dsa_decode B=40")
+    kv = _kv(d.lc, d.rc, d.ic, seq_len, T, seq_stride=T)
+    out, sel, nsel = _dsa_step_check(d, kv, seq_len, T, k, oracle_rows=(0, 7, 39))
+    assert int(nsel[7]) == 100
+
+
 def test_decode_batched_selected_large():
     """Many sequences with selections of different sizes (covers multi-tile splits)."""
     B, T, k = 6, 3000, 2048
