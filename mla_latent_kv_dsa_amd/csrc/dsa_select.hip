@@ -257,7 +257,7 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
                                                  const uint32_t *__restrict__ fcnt, int nch,
                                                  const uint64_t *__restrict__ gkeep, int wp,
                                                  const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
-                                                 int32_t *__restrict__ nsel, uint64_t *__restrict__ dyn)
+                                                 int32_t *__restrict__ nsel, uint64_t *__restrict__ dyn, int ov_cap)
 {
     __shared__ uint32_t h[SEL_BINS];
     __shared__ uint32_t sh[SR_NW];
@@ -307,25 +307,51 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     const uint32_t ov_pre = block_excl_scan_dpp<SR_NW>(ov_t, sh, &OV);
     if (tid < nch) s_ov[tid] = ov_pre;
     if (tid == 0) s_ov[nch] = OV;
-    // every candidate once: those held in registers, then the overflow entries in batches of
-    // eight independent loads per thread (overflow item i: slot c with s_ov[c] <= i < s_ov[c+1])
-    auto for_each = [&](auto f) {
-#pragma unroll
-        for (int i = 0; i < SEL_CPT; ++i)
-            if (active && (uint32_t)(2 * (my_r + tps * (i >> 1)) + (i & 1)) < cnt_mine) f(cr[i]);
+    // the overflow entries (item i: slot c with s_ov[c] <= i < s_ov[c+1]) are read from memory
+    // once into LDS behind the bitmasks when they fit (ov_cap entries), else in every pass
+    uint2 *ovs = reinterpret_cast<uint2 *>(dyn + 2 * wp);
+    const bool ov_lds = OV <= (uint32_t)ov_cap;
+    auto ov_item = [&](uint32_t ic) {
+        int lo = 0, hi = nch - 1;   // last slot with s_ov[slot] <= ic
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_ov[mid] <= ic) lo = mid;
+            else hi = mid - 1;
+        }
+        return cb[(int64_t)lo * SEL_CH + D + (ic - s_ov[lo])];
+    };
+    if (OV > 0u && ov_lds) {
+        __syncthreads();   // s_ov
         for (uint32_t base = 0u; base < OV; base += 8u * SR_NT) {
             uint2 t[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t it = base + tid + (uint32_t)SR_NT * i;
-                const uint32_t ic = it < OV ? it : OV - 1u;
-                int lo = 0, hi = nch - 1;   // last slot with s_ov[slot] <= ic
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_ov[mid] <= ic) lo = mid;
-                    else hi = mid - 1;
-                }
-                t[i] = cb[(int64_t)lo * SEL_CH + D + (ic - s_ov[lo])];
+                t[i] = ov_item(it < OV ? it : OV - 1u);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t it = base + tid + (uint32_t)SR_NT * i;
+                if (it < OV) ovs[it] = t[i];
+            }
+        }
+    }
+    // every candidate once: those held in registers, then the overflow entries (from LDS, or in
+    // batches of eight independent loads per thread)
+    auto for_each = [&](auto f) {
+#pragma unroll
+        for (int i = 0; i < SEL_CPT; ++i)
+            if (active && (uint32_t)(2 * (my_r + tps * (i >> 1)) + (i & 1)) < cnt_mine) f(cr[i]);
+        if (ov_lds) {
+            for (uint32_t it = tid; it < OV; it += SR_NT) f(ovs[it]);
+            return;
+        }
+        for (uint32_t base = 0u; base < OV; base += 8u * SR_NT) {
+            uint2 t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t it = base + tid + (uint32_t)SR_NT * i;
+                t[i] = ov_item(it < OV ? it : OV - 1u);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -434,10 +460,10 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
                                                      const uint32_t *__restrict__ fcnt, int nch,
                                                      const uint64_t *__restrict__ gkeep, int wp,
                                                      const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
-                                                     int32_t *__restrict__ nsel)
+                                                     int32_t *__restrict__ nsel, int ov_cap)
 {
     extern __shared__ uint64_t sr_dyn[];
-    resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn);
+    resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
 }
 
 // The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
@@ -452,11 +478,11 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
                                                             const uint64_t *__restrict__ gkeep, int wp,
                                                             const SelRow *__restrict__ rows,
                                                             int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
-                                                            int nres, SideAbsorb sa)
+                                                            int nres, SideAbsorb sa, int ov_cap)
 {
     extern __shared__ uint64_t sr_dyn[];
     if ((int)blockIdx.x < nres) {
-        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn);
+        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
         return;
     }
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
@@ -577,12 +603,14 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
         if (st) return st;
     }
     const int nch = sw.nch > 0 ? (int)sw.nch : 1;
-    const size_t dyn_sel = (size_t)sw.wp * 16;
+    // the bitmasks, then room for staged overflow candidates (at least 64 KB or what is left)
+    const size_t dyn_masks = (size_t)sw.wp * 16;
+    const size_t dyn_sel = dyn_masks + 65536 < (size_t)SR_DYN_MAX ? dyn_masks + 65536 : (size_t)SR_DYN_MAX;
     const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
                            (side->nope == 128 || side->nope == 192 || side->nope == 256);
     if (!with_side) {
         hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
-                           sw.wp, sw.rows, sel, nsel);
+                           sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
         return check_launch("sel_resolve");
     }
     const size_t dyn_abs = B >= AB_MFMA_B ? 2 * (size_t)side->nope * AB_WROWB
@@ -591,7 +619,7 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     const dim3 g((unsigned)(B + 2 * AB_H));
 #define SRA_LAUNCH(NR)                                                                                              \
     hipLaunchKernelGGL(sel_resolve_absorb<NR>, g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, sw.wp, \
-                       sw.rows, sel, nsel, B, *side)
+                       sw.rows, sel, nsel, B, *side, (int)((dyn - dyn_masks) / 8))
     if (side->nope == 128) SRA_LAUNCH(8);
     else if (side->nope == 192) SRA_LAUNCH(12);
     else SRA_LAUNCH(16);
