@@ -165,9 +165,14 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
 
 // ------------------------------------------------------------------------------ attention
 constexpr int PA_BQ = 128, PA_BK = 64;
-constexpr int PA_ROW = 536;    // bf16 per staged key row: K (256) then V (256), pitch 1072 B so that
-                               // the K row reads and the transposed V reads fall in distinct banks
-constexpr size_t PA_LDS = (size_t)2 * PA_BK * PA_ROW * 2;   // two tiles
+// A staged tile holds the 64 K rows, then the 64 V rows, 512 B each and unpadded.  The 16-byte
+// chunks of a row are placed through the copies' source addresses: chunk c of K row r sits at
+// c ^ (r % 32), so the 16-byte score-operand reads of 16 consecutive rows hit distinct banks;
+// chunk c of V row r at c ^ 4 (r % 4), so each transposed read (rows r .. r+3, 64 bytes of
+// columns) covers all 64 banks once.
+constexpr int PA_KROW = 256;                              // bf16 per staged K or V row
+constexpr int PA_TILE = 2 * PA_BK * PA_KROW;              // bf16 per staged tile
+constexpr size_t PA_LDS = (size_t)2 * PA_TILE * 2;        // two tiles
 constexpr int PA_PF = 6;       // score operand reads in flight
 
 
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
                                                int S, int pos_base, float scale_log2, OUT *__restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) char pa_smem[];
-    bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 tiles][64 keys][PA_ROW]
+    bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 tiles][K rows, V rows][64][PA_KROW]
     constexpr int QD = NOPE + PF_R;            // query / key width (256 for nope 192)
     constexpr int KS = QD / 16;                // K steps of the score product
     constexpr int N = PF_H * (NOPE + PF_V);    // row length of C
@@ -212,13 +217,11 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
-    // staging: wave w copies key rows 16 w .. 16 w + 15 of a tile, one DMA per row: lanes 0..31
-    // the K row (dims 8 lane ..: k_nope from C, then Rc; lanes past the key width re-read the
-    // row's first chunk, never used), lanes 32..63 the V row behind it
-    const bool is_k = lane < 32;
-    const bool is_rc = is_k && 8 * lane >= NOPE && 8 * lane < QD;
-    const int c_off = h * (NOPE + PF_V) + (is_k ? (8 * lane < NOPE ? 8 * lane : 0) : NOPE + 8 * (lane - 32));
-    const int rc_off = is_rc ? 8 * lane - NOPE : 0;
+    // staging: wave w copies keys 16 w .. 16 w + 15 of a tile in pairs, one DMA for the K rows and
+    // one for the V rows of a pair (lanes 0..31 the first key, 32..63 the second): position p =
+    // lane % 32 of a K row takes chunk p ^ (key % 32) (k_nope from C, then Rc; chunks past the key
+    // width take chunk 0, never read), of a V row chunk p ^ 4 (key % 4).
+    const int pp = lane & 31, kh = lane >> 5;
     // Rc rows of the wave's 16 keys of tile kt: lane i < 16 resolves key 64 kt + 16 wave + i (the
     // other lanes repeat them).  Resolved before the tile's copies are issued and complete before
     // the first one: a block-table load consumed between the copies would make the compiler wait
@@ -230,20 +233,28 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
     };
     auto settle = [](int64_t x) { asm volatile("" ::"v"((uint32_t)x), "v"((uint32_t)(x >> 32))); };
     auto stage = [&](int kt, int64_t rrow) {
-        bf16_t *dst = sT + (kt & 1) * PA_BK * PA_ROW;
+        bf16_t *dst = sT + (kt & 1) * PA_TILE;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * wave + i;
-            const int64_t t0 = (int64_t)kt * PA_BK + r;
+        for (int i = 0; i < 8; ++i) {
+            const int r0 = 16 * wave + 2 * i, key = r0 + kh;   // this lane's key of the pair
+            const int64_t t0 = (int64_t)kt * PA_BK + key;
             const int64_t t = t0 < kend ? t0 : kend - 1;
-            const int64_t row = ((int64_t)__builtin_amdgcn_readlane((int)(rrow >> 32), i) << 32) |
-                                (uint32_t)__builtin_amdgcn_readlane((int)rrow, i);
-            const bf16_t *src = is_rc ? rc + row * PF_R + rc_off : C + t * (int64_t)N + c_off;
-            pf_dma16(src, pf_lds_addr(dst + r * PA_ROW));
+            const int64_t ra = ((int64_t)__builtin_amdgcn_readlane((int)(rrow >> 32), 2 * i) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)rrow, 2 * i);
+            const int64_t rb = ((int64_t)__builtin_amdgcn_readlane((int)(rrow >> 32), 2 * i + 1) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)rrow, 2 * i + 1);
+            const int64_t rrc = kh ? rb : ra;
+            const bf16_t *crow = C + t * (int64_t)N + h * (NOPE + PF_V);
+            const int ck = pp ^ (key & 31), cv = pp ^ (4 * (key & 3));
+            const bf16_t *sk = ck < NOPE / 8 ? crow + 8 * ck : (ck < QD / 8 ? rc + rrc * PF_R + 8 * ck - NOPE : crow);
+            pf_dma16(sk, pf_lds_addr(dst + r0 * PA_KROW));
+            pf_dma16(crow + NOPE + 8 * cv, pf_lds_addr(dst + (PA_BK + r0) * PA_KROW));
         }
     };
     const int G = lane >> 4, j16 = lane & 15;   // transposed-read address inside a 16-key step
-    const int tr_off = (8 * (G >> 1) + (j16 >> 2)) * PA_ROW + 256 + 16 * (G & 1) + 4 * (j16 & 3);
+    const int r3 = j16 >> 2;                    // row % 4 of this lane's transposed reads
+    const int tr_off = PA_BK * PA_KROW + (8 * (G >> 1) + r3) * PA_KROW + 8 * (2 * (G & 1) + ((j16 & 3) >> 1)) +
+                       4 * (j16 & 1);
     {
         const int64_t rr = rows_of(0);
         settle(rr);
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
             settle(rr);
             stage(kt + 1, rr);
         }
-        const bf16_t *tk = sT + (kt & 1) * PA_BK * PA_ROW;
+        const bf16_t *tk = sT + (kt & 1) * PA_TILE;
         // S^T: two 32-key tiles; register r of s[mt] is key k0 + 32 mt + 8 (r/4) + 4 hi + r%4
         // Step i of 2 KS takes key tile i % 2 and slice i / 2; the LDS operand reads run PA_PF steps
         // ahead of their products (a ring of registers), so their latency hides behind the
@@ -273,8 +284,11 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-            const bf16_t *ka = tk + l32 * PA_ROW + 8 * hi;
-            auto a_op = [&](int i) { return *reinterpret_cast<const uint4 *>(ka + (i & 1) * 32 * PA_ROW + 16 * (i >> 1)); };
+            // K row 32 mt + l32, dims 16 ks + 8 hi ..: chunk 2 ks + hi at position (2 ks + hi) ^ l32
+            const bf16_t *ka = tk + l32 * PA_KROW;
+            auto a_op = [&](int i) {
+                return *reinterpret_cast<const uint4 *>(ka + (i & 1) * 32 * PA_KROW + 8 * ((2 * (i >> 1) + hi) ^ l32));
+            };
             uint4 ring[PA_PF];
 #pragma unroll
             for (int i = 0; i < PA_PF; ++i) ring[i] = a_op(i);
@@ -368,13 +382,14 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
             pb.y = x1[0];
             pb.z = x0[1];
             pb.w = x1[1];
-            const bf16_t *vb = tk + 16 * kb * PA_ROW + tr_off;
+            const bf16_t *vb = tk + 16 * kb * PA_KROW + tr_off;
 #pragma unroll
             for (int dt = 0; dt < PF_V / 32; ++dt) {
+                // V chunk 4 dt + .. of rows with row % 4 == r3 sits at 4 (dt ^ r3) + ..
                 const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) pv4s *)(vb + 32 * dt));
+                    (__attribute__((address_space(3))) pv4s *)(vb + 32 * (dt ^ r3)));
                 const pv4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_ROW + 32 * dt));
+                    (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_KROW + 32 * (dt ^ r3)));
                 const pv8s vt = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt), pf_bf16x8(pb), o[dt],
                                                                 0, 0, 0);
