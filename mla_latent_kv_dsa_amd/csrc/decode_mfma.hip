@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
 //   B operand, so P needs no pass through LDS.
 // O (16 heads x 512 columns per wave), the reference maximum and the sum of the rounded P go to
 // the same partials as dec_core's.
-constexpr int MH_ROWB = 1072;   // bytes per staged latent row (conflict-free, as dec_core)
+constexpr int MH_ROWB = 1024;   // bytes per staged latent row (unpadded; 16-byte chunks swizzled, mh_swz)
 constexpr int MH_RCB = 128;     // bytes per staged rope row
 constexpr int MH_KC = 32;       // keys per chunk
 constexpr int MH_NBUF = 4;      // chunk buffers
@@ -331,6 +331,11 @@ constexpr float MH_LAZY = 8.f;  // slack of the reference maximum (log2 units)
 constexpr int MH_PF = 6;        // score operand reads in flight
 constexpr int MH_PV = 4;        // value column tiles read ahead
 constexpr size_t MH_LDS = (size_t)MH_NBUF * MH_KC * (MH_ROWB + MH_RCB) + 256 * sizeof(int64_t);
+
+// Position of chunk c of staged latent row r is c ^ mh_swz(r): the score-operand reads (16
+// consecutive rows, one chunk) and the transposed value reads (8 rows, two chunks per pass of 32
+// lanes) then hit distinct banks.
+__device__ __forceinline__ int mh_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
 
 __device__ __forceinline__ int64_t readlane64(int64_t x, int i)
 {
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(256) void dec_core_mh(const bf16_t *__restrict__ q_
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t r = readlane64(rw, i);
-            const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * lane : dummy;
+            const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * (lane ^ mh_swz(8 * wave + i)) : dummy;
             lds_dma16(src, lds_addr(sL + (MH_KC * buf + 8 * wave + i) * MH_ROWB));
         }
         const int kc = 8 * wave + (lane >> 3);   // key of the chunk whose rope piece this lane copies
@@ -442,7 +447,8 @@ __global__ __launch_bounds__(256) void dec_core_mh(const bf16_t *__restrict__ q_
                 for (int u = 0; u < 4; ++u) dd[u] = f32x4{0.f, 0.f, 0.f, 0.f};
                 auto a_op = [&](int i) -> uint4 {
                     const int kt = i & 1, ks = i >> 1, key = 16 * kt + jj;
-                    if (ks < 16) return *reinterpret_cast<const uint4 *>(bL + key * MH_ROWB + 16 * quad + 64 * ks);
+                    if (ks < 16)
+                        return *reinterpret_cast<const uint4 *>(bL + key * MH_ROWB + 16 * ((4 * ks + quad) ^ mh_swz(key)));
                     return *reinterpret_cast<const uint4 *>(bR + key * MH_RCB + 16 * ((4 * (ks - 16) + quad) ^ (key & 7)));
                 };
                 uint4 ring[MH_PF];
@@ -509,12 +515,15 @@ __global__ __launch_bounds__(256) void dec_core_mh(const bf16_t *__restrict__ q_
             }
             {
                 // values: the transposed reads of column tile ct run MH_PV tiles ahead of its product
-                const char *vb = bL + (4 * quad + (jj >> 2)) * MH_ROWB + 8 * (jj & 3);
+                // row 4 quad + jj/4 (and 16 rows on), columns 16 ct + 4 (jj % 4) ..: chunk 2 ct + (jj % 4) / 2
+                const int vrow = 4 * quad + (jj >> 2), vsw = mh_swz(vrow);
+                const char *vb = bL + vrow * MH_ROWB + 8 * (jj & 1);
                 auto b_op = [&](int ct) -> v8s {
+                    const int pos = (2 * ct + ((jj & 3) >> 1)) ^ vsw;
                     const v4s lo =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + 32 * ct));
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + 16 * pos));
                     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s *)(vb + 16 * MH_ROWB + 32 * ct));
+                        (__attribute__((address_space(3))) v4s *)(vb + 16 * MH_ROWB + 16 * pos));
                     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 };
                 v8s ring[MH_PV];
