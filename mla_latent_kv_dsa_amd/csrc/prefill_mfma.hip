@@ -180,7 +180,10 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 // Workgroups go to the 8 XCDs round-robin (id % 8); XCD x runs heads x, x + 8, .. one after the
 // other, each as all of its query blocks at once (late ones first), so the head's K and V (4 MB
 // at 4096 tokens) are fetched into that XCD's L2 once and shared by its 32 CUs.
-template <int NOPE, typename OUT>
+// MODE 0: Rc rows contiguous (row = position); 1: block table with block_size % 64 == 0 (a tile's
+// keys in one block, looked up once per tile with a scalar load); 2: any block table (one lookup
+// per key, a vector load whose wait also lands the copies in flight).
+template <int NOPE, typename OUT, int MODE>
 __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C, KvView kv,
                                                int S, int pos_base, float scale_log2, OUT *__restrict__ out)
 {
@@ -228,14 +231,32 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
     // for every copy in flight (it does not see them).
     auto rows_of = [&](int kt) -> int64_t {
         const int64_t t0 = (int64_t)kt * PA_BK + 16 * wave + (lane & 15);
-        const int64_t row = kv_row(kv, 0, t0 < kend ? t0 : kend - 1);
+        const int64_t t = t0 < kend ? t0 : kend - 1;
+        int64_t row;
+        if (MODE == 0) {
+            row = t < kv.rows ? t : -1;   // sequence 0 of a contiguous view: row = position
+        } else if (MODE == 1) {
+            // the tile's block (uniform address): a scalar load, whose wait counts LDS and
+            // scalar traffic only
+            const int32_t *pb = kv.bt + (int)((int64_t)kt * PA_BK / kv.bs);
+            int32_t blk;
+            asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(pb) : "memory");
+            row = blk < 0 ? -1 : (int64_t)blk * kv.bs + t % kv.bs;
+            if (row >= kv.rows) row = -1;
+        } else {
+            row = kv_row(kv, 0, t);
+        }
         return row >= 0 ? row : 0;
     };
     auto settle = [](int64_t x) { asm volatile("" ::"v"((uint32_t)x), "v"((uint32_t)(x >> 32))); };
+    // the eight K copies of the wave go out first, then the eight V copies: the score product of
+    // a tile waits for its K rows only (vmcnt(8)), the value product for the V rows
     auto stage = [&](int kt, int64_t rrow) {
         bf16_t *dst = sT + (kt & 1) * PA_TILE;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int u = 0; u < 16; ++u) {
+            const int i = u & 7;
+            const bool isv = u >= 8;
             const int r0 = 16 * wave + 2 * i, key = r0 + kh;   // this lane's key of the pair
             const int64_t t0 = (int64_t)kt * PA_BK + key;
             const int64_t t = t0 < kend ? t0 : kend - 1;
@@ -247,8 +268,8 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
             const bf16_t *crow = C + t * (int64_t)N + h * (NOPE + PF_V);
             const int ck = pp ^ (key & 31), cv = pp ^ (4 * (key & 3));
             const bf16_t *sk = ck < NOPE / 8 ? crow + 8 * ck : (ck < QD / 8 ? rc + rrc * PF_R + 8 * ck - NOPE : crow);
-            pf_dma16(sk, pf_lds_addr(dst + r0 * PA_KROW));
-            pf_dma16(crow + NOPE + 8 * cv, pf_lds_addr(dst + (PA_BK + r0) * PA_KROW));
+            if (!isv) pf_dma16(sk, pf_lds_addr(dst + r0 * PA_KROW));
+            else pf_dma16(crow + NOPE + 8 * cv, pf_lds_addr(dst + (PA_BK + r0) * PA_KROW));
         }
     };
     const int G = lane >> 4, j16 = lane & 15;   // transposed-read address inside a 16-key step
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         const int64_t k0 = (int64_t)kt * PA_BK;
         // tile kt has landed in every wave's share, and every wave is done with tile kt - 1, whose
         // buffer the next copies fill: one barrier per tile
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");   // the K rows of tile kt
         if (kt + 1 < ntile) {
             const int64_t rr = rows_of(kt + 1);
             settle(rr);
@@ -368,6 +389,9 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
+        // the V rows of tile kt (the next tile's sixteen copies, if any, were issued after them)
+        if (kt + 1 < ntile) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         // O^T += V^T P^T over four 16-key steps: step kb covers keys 16 kb .. +15 (tile kb/2,
         // groups g = 2 (kb%2), +1).  Lane l needs keys 8 hi .. 8 hi + 7 of the step for query l32;
         // it holds keys 4 hi + 0..3 (group g) and 8 + 4 hi + 0..3 (group g + 1): one swap of the
@@ -430,21 +454,30 @@ size_t prefill_mfma_ws(const mla_dims &d, int64_t T)
     return 256 + (size_t)T * d.n_heads * (d.qk_nope + d.v_head) * 2;
 }
 
-template <int NOPE, typename OUT>
-static mla_status launch_attn(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
-                              float scale_log2, void *out, hipStream_t s)
+template <int NOPE, typename OUT, int MODE>
+static mla_status launch_attn_mode(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
+                                   float scale_log2, void *out, hipStream_t s)
 {
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT, MODE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)PA_LDS);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         attr = true;
     }
     const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ * PF_H));
-    hipLaunchKernelGGL((pf_attn<NOPE, OUT>), g, dim3(256), PA_LDS, s, (const bf16_t *)q, C, kv, S, pos_base, scale_log2,
-                       (OUT *)out);
+    hipLaunchKernelGGL((pf_attn<NOPE, OUT, MODE>), g, dim3(256), PA_LDS, s, (const bf16_t *)q, C, kv, S, pos_base,
+                       scale_log2, (OUT *)out);
     return check_launch("pf_attn");
+}
+
+template <int NOPE, typename OUT>
+static mla_status launch_attn(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
+                              float scale_log2, void *out, hipStream_t s)
+{
+    if (!kv.bt) return launch_attn_mode<NOPE, OUT, 0>(q, C, kv, S, pos_base, scale_log2, out, s);
+    if (kv.bs % PA_BK == 0) return launch_attn_mode<NOPE, OUT, 1>(q, C, kv, S, pos_base, scale_log2, out, s);
+    return launch_attn_mode<NOPE, OUT, 2>(q, C, kv, S, pos_base, scale_log2, out, s);
 }
 
 mla_status launch_prefill_mfma(const void *q, const void *kv_b, const mla_dims &d, const KvView &kv, int32_t S,
