@@ -767,6 +767,20 @@ def test_dsa_decode_call_batch_over_side_limit():
     assert int(nsel[7]) == 100
 
 
+def test_decode_dense_4096_full_heads():
+    """The dense decode configuration at full size: one query over all 4096 cached keys, 64
+    heads (sel = NULL, the path `dense_decode_T4096` of the benchmark times), against the
+    oracle; the same keys passed as an explicit selection give the same bits."""
+    T = 4096
+    d = synth.decode(2, T)
+    log("decode dense T=4096")
+    out, sm = _run_decode(d, [T])
+    assert rel_err(out[0], _decode_ref(d, 0, np.arange(T), sm)) <= TOL_BF16
+    sel = np.arange(T, dtype=np.int32)[None]
+    out_sel, _ = _run_decode(d, [T], sel, np.array([T], np.int32))
+    assert np.array_equal(out, out_sel)
+
+
 def test_decode_batched_selected_large():
     """Many sequences with selections of different sizes (covers multi-tile splits)."""
     B, T, k = 6, 3000, 2048
