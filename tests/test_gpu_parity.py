@@ -409,25 +409,28 @@ def test_decode_selected_keys_and_keep_all_equals_dense():
     assert np.array_equal(dense, kept)
 
 
-@pytest.mark.parametrize("bf16", [True, False])
-def test_decode_split_steps_equal_fused(bf16):
+@pytest.mark.parametrize("bf16,B", [(True, 2), (False, 2), (True, 6)])
+def test_decode_split_steps_equal_fused(bf16, B):
     """mla_decode_absorb followed by mla_decode_attend on one workspace gives the fused call's
-    output bit for bit (matrix-core path for bf16 GLM shapes, generic kernels for fp32)."""
+    output bit for bit (matrix-core path for bf16 GLM shapes, with the batch kernels at B = 6;
+    generic kernels for fp32)."""
     T, k = 900, 300
-    d = synth.decode(40, T, B=2, bf16=bf16)
+    d = synth.decode(40, T, B=B, bf16=bf16)
     rng = np.random.default_rng(41)
-    sel = np.full((2, k), -1, np.int32)
+    sel = np.full((B, k), -1, np.int32)
+    nsel = np.array([k, 77] + [int(rng.integers(1, k + 1)) for _ in range(B - 2)], np.int32)
     sel[0] = np.sort(rng.choice(T, k, replace=False))
     sel[1, :77] = np.sort(rng.choice(600, 77, replace=False))
-    nsel = np.array([k, 77], np.int32)
+    for b in range(2, B):
+        sel[b, : nsel[b]] = np.sort(rng.choice(600, nsel[b], replace=False))
     to = dev_bf16 if bf16 else dev
-    kv = _kv(d.lc, d.rc, None, [T, 600], T, seq_stride=T, bf16=bf16)
+    kv = _kv(d.lc, d.rc, None, [T] + [600] * (B - 1), T, seq_stride=T, bf16=bf16)
     sm = 1.0 / math.sqrt(d.nope + d.rope)
     qn, qr, kvb = to(d.q_nope), to(d.q_rope), to(d.kv_b)
     sl, ns = dev(sel), dev(nsel)
-    log(f"decode split steps bf16={bf16}")
+    log(f"decode split steps bf16={bf16} B={B}")
     fused = host(mla.mla_absorbed_decode(qn, qr, kvb, kv, sm, sel=sl, nsel=ns))
-    need = mla.mla_decode_workspace_bytes(d.H, d.nope, d.rope, d.v, d.L, 2, k)
+    need = mla.mla_decode_workspace_bytes(d.H, d.nope, d.rope, d.v, d.L, B, k)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     mla.mla_decode_absorb(qn, kvb, ws, qk_rope=d.rope)
     split = host(mla.mla_decode_attend(qr, kvb, kv, d.nope, sm, ws, sel=sl, nsel=ns))
