@@ -97,7 +97,12 @@ __global__ __launch_bounds__(256) void absorb_q_mfma(const bf16_t *__restrict__ 
 // the combine step rescales the splits to their common maximum.
 constexpr int DC_KC = 64;                        // keys per chunk (four waves x 16)
 constexpr int DC_SUP = 2;                        // chunks staged at a time
-constexpr int DC_ROWB = 1072;                    // bytes per staged latent row
+constexpr int DC_ROWB = 1024;                    // bytes per staged latent row (unpadded, dc_swz)
+
+// Position of chunk c of staged latent row r is c ^ dc_swz(r % 16): the score-operand reads (16
+// consecutive rows, one chunk) and the transposed value reads (rows 0-3 with 8-11, or 4-7 with
+// 12-15, two chunks, per pass of 32 lanes) then hit distinct banks.
+__device__ __forceinline__ int dc_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1); }
 constexpr int DC_PROW = 72;                      // bf16 per P row (64 keys + pad: 144 B)
 constexpr size_t DC_LDS = (size_t)DC_SUP * DC_KC * DC_ROWB + 16 * DC_PROW * 2 + (64 + 64 + 16) * 4;
 
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
             for (int i = 0; i < 16; ++i) {
                 const int64_t r = ((int64_t)__builtin_amdgcn_readlane((int)(row[u] >> 32), i) << 32) |
                                   (uint32_t)__builtin_amdgcn_readlane((int)row[u], i);
-                const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * lane : dummy;
+                const bf16_t *src = r >= 0 ? lc + r * DM_L + 8 * (lane ^ dc_swz(i)) : dummy;
                 lds_dma16(src, lds_addr(sL + (64 * u + 16 * wave + i) * DC_ROWB));
             }
         }
@@ -229,11 +234,13 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
             if (c0 + 64 * u >= k1) break;
             // scores: register r is key 16 wave + 4 quad + r of the chunk, head h
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            const char *ka = sL + (64 * u + 16 * wave + jj) * DC_ROWB + 16 * quad;
+            const char *ka = sL + (64 * u + 16 * wave + jj) * DC_ROWB;
+            const int fj = dc_swz(jj);
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks)
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const uint4 *>(ka + 64 * ks)),
-                                                            as_bf16x8(Bq[ks]), d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(ka + 16 * ((4 * ks + quad) ^ fj))), as_bf16x8(Bq[ks]), d, 0,
+                    0, 0);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Arc[u][ks]), as_bf16x8(Bq[16 + ks]), d, 0, 0, 0);
@@ -276,13 +283,17 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const uint4 pa = *reinterpret_cast<const uint4 *>(&sP[jj * DC_PROW + 32 * kk + 8 * quad]);
-                const char *vb = sL + (64 * u + 32 * kk + 8 * quad + (jj >> 2)) * DC_ROWB + 2 * (128 * wave + 4 * (jj & 3));
+                // rows 8 quad + jj/4 (and 4 on) of this 32-key step, columns 128 wave + 16 ct + 4 (jj % 4) ..:
+                // chunk 16 wave + 2 ct + (jj % 4) / 2
+                const int rl = (8 * quad + (jj >> 2)) & 15, flo = dc_swz(rl), fhi = dc_swz(rl + 4);
+                const char *vb = sL + (64 * u + 32 * kk + 8 * quad + (jj >> 2)) * DC_ROWB + 8 * (jj & 1);
+                const int c0 = 16 * wave + ((jj & 3) >> 1);
 #pragma unroll
                 for (int ct = 0; ct < 8; ++ct) {
                     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s *)(vb + 32 * ct));
+                        (__attribute__((address_space(3))) v4s *)(vb + 16 * ((c0 + 2 * ct) ^ flo)));
                     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s *)(vb + 4 * DC_ROWB + 32 * ct));
+                        (__attribute__((address_space(3))) v4s *)(vb + 4 * DC_ROWB + 16 * ((c0 + 2 * ct) ^ fhi)));
                     const v8s vt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), __builtin_bit_cast(bf16x8, vt),
                                                                       acc[ct], 0, 0, 0);
