@@ -64,15 +64,16 @@ __device__ __forceinline__ void pf_dma16(const void *g, uint32_t lds)
                  : "memory");
 }
 
-constexpr int KG_BM = 256, KG_BN = 256, KG_BK = 32;   // rows of C^T (n), columns (tokens), K step
-constexpr int KG_NS = 3;                               // K steps staged at a time
-constexpr size_t KG_LDS = (size_t)KG_NS * (KG_BM + KG_BN) * KG_BK * 2;   // 96 KB
+constexpr int KG_BM = 256, KG_BN = 256, KG_BK = 64;   // rows of C^T (n), columns (tokens), K step
+constexpr int KG_NS = 2;                               // K steps staged at a time
+constexpr int KG_RB = KG_BK * 2;                       // bytes per staged row (one 128-byte line)
+constexpr size_t KG_LDS = (size_t)KG_NS * (KG_BM + KG_BN) * KG_RB;   // 128 KB
 
 // grid (ceil(N / 256), ceil(T / 256)), 256 threads; wave w: n rows 128 (w&1) .., tokens 128 (w>>1) ..
-// A K step of a tile is 256 rows x 64 B in LDS, the four 16-byte chunks of row r stored at
-// positions c ^ ((r >> 2) & 3): sixteen consecutive rows read at one chunk hit distinct banks.
-// Wave w copies rows 64 w .. 64 w + 63 of both tiles, 16 rows (1 KB) per DMA: lane L moves
-// chunk (L % 4) ^ ((r >> 2) & 3) of row r = 16 j + L / 4 into position L % 4.
+// A K step of a tile is 256 rows x 128 B in LDS, the eight 16-byte chunks of row r stored at
+// positions c ^ ((r >> 1) & 7): sixteen consecutive rows read at one chunk hit distinct banks.
+// Wave w copies rows 64 w .. 64 w + 63 of both tiles, 8 rows (1 KB, whole lines) per DMA: lane L
+// moves chunk (L % 8) ^ ((r >> 1) & 7) of row r = 8 j + L / 8 into position L % 8.
 __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restrict__ kv_b, int64_t T, int N,
                                               bf16_t *__restrict__ C)
 {
@@ -81,12 +82,12 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
     const int n0 = blockIdx.x * KG_BM;
     const int64_t t0 = (int64_t)blockIdx.y * KG_BN;
     const bf16_t *lc = reinterpret_cast<const bf16_t *>(kv.lc);
-    const bf16_t *ga[4];
-    const bf16_t *gb[4];
+    const bf16_t *ga[8];
+    const bf16_t *gb[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 64 * wave + 16 * j + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+    for (int j = 0; j < 8; ++j) {
+        const int r = 64 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         const int n = n0 + r;
         ga[j] = kv_b + (int64_t)(n < N ? n : N - 1) * PF_L + 8 * c;
         const int64_t t = t0 + r;
@@ -94,11 +95,11 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
         gb[j] = lc + (row >= 0 ? row : 0) * PF_L + 8 * c;
     }
     auto stage = [&](int ks) {   // K step ks into ring slot ks % KG_NS
-        char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_BK * 2;
+        char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_RB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pf_dma16(ga[j] + KG_BK * ks, pf_lds_addr(base + (64 * wave + 16 * j) * 64));
-            pf_dma16(gb[j] + KG_BK * ks, pf_lds_addr(base + KG_BM * 64 + (64 * wave + 16 * j) * 64));
+        for (int j = 0; j < 8; ++j) {
+            pf_dma16(ga[j] + KG_BK * ks, pf_lds_addr(base + (64 * wave + 8 * j) * KG_RB));
+            pf_dma16(gb[j] + KG_BK * ks, pf_lds_addr(base + KG_BM * KG_RB + (64 * wave + 8 * j) * KG_RB));
         }
     };
     pf32x16 acc[4][4];
@@ -110,27 +111,22 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int wm = 128 * (wave & 1), wn = 128 * (wave >> 1);
     const int l32 = lane & 31, hi = lane >> 5;
-    constexpr int NK = PF_L / KG_BK;   // 16 K steps
+    constexpr int NK = PF_L / KG_BK;   // 8 K steps
     stage(0);
-    stage(1);
     for (int ks = 0; ks < NK; ++ks) {
-        if (ks + 2 < NK) {
-            stage(ks + 2);
-            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // step ks has landed everywhere
-        } else if (ks + 1 < NK) {
-            asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        }
-        const char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_BK * 2;
+        // step ks has landed everywhere, and every wave is done with step ks - 1, whose slot the
+        // copies of step ks + 1 fill
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (ks + 1 < NK) stage(ks + 1);
+        const char *base = kg_smem + (ks % KG_NS) * (KG_BM + KG_BN) * KG_RB;
 #pragma unroll
         for (int kk = 0; kk < KG_BK / 16; ++kk) {
             uint4 a[4], b[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ra = wm + 32 * i + l32, rb = wn + 32 * i + l32, c = 2 * kk + hi;
-                a[i] = *reinterpret_cast<const uint4 *>(base + ra * 64 + 16 * (c ^ ((ra >> 2) & 3)));
-                b[i] = *reinterpret_cast<const uint4 *>(base + KG_BM * 64 + rb * 64 + 16 * (c ^ ((rb >> 2) & 3)));
+                a[i] = *reinterpret_cast<const uint4 *>(base + ra * KG_RB + 16 * (c ^ ((ra >> 1) & 7)));
+                b[i] = *reinterpret_cast<const uint4 *>(base + KG_BM * KG_RB + rb * KG_RB + 16 * (c ^ ((rb >> 1) & 7)));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -139,8 +135,6 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(a[i]), pf_bf16x8(b[j]), acc[i][j],
                                                                         0, 0, 0);
         }
-        // the slot is copied over again two steps later: every wave has consumed its reads
-        asm volatile("s_barrier" ::: "memory");
     }
     // register r of tile (i, j): n = n0 + wm + 32 i + 8 (r/4) + 4 hi + r%4, token t0 + wn + 32 j + l32
 #pragma unroll
