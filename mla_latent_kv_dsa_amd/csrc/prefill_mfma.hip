@@ -136,23 +136,26 @@ __global__ __launch_bounds__(256) void pf_kvb(KvView kv, const bf16_t *__restric
                                                                         0, 0, 0);
         }
     }
-    // register r of tile (i, j): n = n0 + wm + 32 i + 8 (r/4) + 4 hi + r%4, token t0 + wn + 32 j + l32
+    // Register r of tile (i, j): n = n0 + wm + 32 i + 8 (r/4) + 4 hi + r%4, token t0 + wn + 32 j + l32.
+    // Per pair of register groups (g = 2 gp, 2 gp + 1), one v_permlane32_swap of the packed values
+    // trades lane half hi = 1's group 2 gp for half 0's group 2 gp + 1: lane (l32, hi) then holds
+    // n = 32 i + 16 gp + 8 hi .. + 7 and stores 16 bytes, 32 contiguous bytes per token and pair.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t t = t0 + wn + 32 * j + l32;
-        if (t >= T) continue;
-        bf16_t *crow = C + t * (int64_t)N;
+        bf16_t *crow = C + (t < T ? t : 0) * (int64_t)N;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wm + 32 * i + 8 * g + 4 * hi;
-                if (n < N) {
-                    uint2 v;
-                    v.x = pf_pack(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-                    v.y = pf_pack(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    *reinterpret_cast<uint2 *>(crow + n) = v;
-                }
+            for (int gp = 0; gp < 2; ++gp) {
+                const pf32x16 &r = acc[i][j];
+                const int q = 8 * gp;
+                const auto x = __builtin_amdgcn_permlane32_swap(pf_pack(r[q], r[q + 1]), pf_pack(r[q + 4], r[q + 5]),
+                                                                false, false);
+                const auto y = __builtin_amdgcn_permlane32_swap(pf_pack(r[q + 2], r[q + 3]),
+                                                                pf_pack(r[q + 6], r[q + 7]), false, false);
+                const int n = n0 + wm + 32 * i + 16 * gp + 8 * hi;
+                if (t < T && n < N) *reinterpret_cast<uint4 *>(crow + n) = make_uint4(x[0], y[0], x[1], y[1]);
             }
     }
 }
