@@ -36,6 +36,10 @@ MUTATIONS = [
     ("prefill ignores pos_base", "const int64_t nk = (int64_t)pos_base + i + 1;", "const int64_t nk = (int64_t)i + 1;", 1),
     ("prefill rope term dropped", "s[t] = sm_scale * (dn + dr);", "s[t] = sm_scale * dn;", 1),
     ("rmsnorm eps dropped", "double inv = 1.0 / sqrt(ms + eps);", "double inv = 1.0 / sqrt(ms);", 1),
+    ("tiny layer rotates at position 0", "int32_t pos = t;", "int32_t pos = 0;", 1),
+    ("tiny layer positions off by one", "int32_t pos = t;", "int32_t pos = t + 1;", 1),
+    ("tiny layer query one position late", "orc_rope_interleave(qf, q, 1, H, qh, nope, rope, &pos, theta);",
+     "{ int32_t qp = pos + 1; orc_rope_interleave(qf, q, 1, H, qh, nope, rope, &qp, theta); }", 1),
 ]
 
 

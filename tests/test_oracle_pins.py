@@ -368,3 +368,37 @@ def test_tiny_layer_pins(oracle):
     assert _rel(o1, o2) <= 1e-10
     y = oracle.o_proj(t.o_w, o1)
     assert _rel(y, t.o_w.astype(np.float64) @ o1.reshape(-1)) <= 1e-12
+
+
+def test_tiny_layer_rope_positions(oracle):
+    """Rc[t] is the kv_a tail rotated at the token's own position t, and the query tail is rotated
+    at the last token's position T-1 (colibri-analysis 06, sec. 2.1: the cache row of position pos
+    holds the RoPE'd key; the query head tails rotate at the query's position).  Viewed as complex
+    numbers, an output pair (y[j], y[half+j]) is the input pair (x[2j], x[2j+1]) multiplied by
+    exp(i*pos*theta^(-2j/rope)); every angle is checked against that closed form at its position,
+    and the attention logits against the relative-position identity through the separately pinned
+    rope function."""
+    from mla_latent_kv_dsa_amd import synth
+    t = synth.tiny_layer(1)
+    lc, rc, q = oracle.tiny_layer(t.x, t.q_a, t.q_b, t.kv_a, t.H, t.nope, t.rope, t.L)
+    half = t.rope // 2
+    inv = 10000.0 ** (-2.0 * np.arange(half) / t.rope)
+    # raw (unrotated) tails from plain float64 matmuls of the layer's weights
+    comp = t.x.astype(np.float64) @ t.kv_a.astype(np.float64).T
+    k_raw = comp[:, t.L:]
+    qa = t.q_a.astype(np.float64) @ t.x[-1].astype(np.float64)
+    qa = qa / np.sqrt((qa ** 2).mean() + 1e-6)
+    q_raw = (t.q_b.astype(np.float64) @ qa).reshape(t.H, t.nope + t.rope)[:, t.nope:]
+    z_in_k = k_raw[:, 0::2] + 1j * k_raw[:, 1::2]
+    z_out_k = rc[:, :half] + 1j * rc[:, half:]
+    pos = np.arange(t.T, dtype=np.float64)[:, None]
+    assert np.max(np.abs(z_out_k - z_in_k * np.exp(1j * pos * inv))) <= 1e-12 * np.abs(z_in_k).max()
+    z_in_q = q_raw[:, 0::2] + 1j * q_raw[:, 1::2]
+    z_out_q = q[:, t.nope:t.nope + half] + 1j * q[:, t.nope + half:]
+    assert np.max(np.abs(z_out_q - z_in_q * np.exp(1j * (t.T - 1) * inv))) <= 1e-12 * np.abs(z_in_q).max()
+    # logits q_rot(T-1) . Rc[t] depend on T-1-t only: rotate the raw query by T-1-t and the raw key by 0
+    for tt in (0, 17, t.T - 1):
+        qr = oracle.rope_interleave(q_raw[None], np.array([t.T - 1 - tt]), 0, t.rope)[0]
+        k0 = oracle.rope_interleave(k_raw[tt][None, None], np.array([0]), 0, t.rope)[0, 0]
+        lhs = q[:, t.nope:] @ rc[tt]
+        assert np.max(np.abs(lhs - qr @ k0)) <= 1e-10 * max(np.abs(lhs).max(), 1e-30)
