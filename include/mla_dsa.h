@@ -20,6 +20,11 @@
  *     unspecified values but never an out-of-bounds access.
  *   - Row-major layouts; all strides are in elements.
  *   - Shapes outside what the library implements return MLA_ERR_UNSUPPORTED.
+ *   - The matrix-core kernels serve bf16 with 64 heads, kv_lora 512 and qk_rope 64 (decode),
+ *     plus v_head 256 and qk_nope 128/192 (prefill).  They read in 16-byte pieces: on that
+ *     geometry every tensor pointer a call takes must be 16-byte aligned, or the call returns
+ *     MLA_ERR_UNSUPPORTED (every entry point alike; no call changes kernels because of where a
+ *     pointer sits).  fp32 and every other geometry run on generic kernels.
  */
 #ifndef MLA_DSA_H
 #define MLA_DSA_H
@@ -190,9 +195,7 @@ mla_status mla_absorbed_decode(const void *q_nope, const void *q_rope, mla_dtype
  * Arguments mean what they mean for mla_absorbed_decode.  The two calls must see the same
  * d, B, dtypes and kv_b, and the same ws (of at least mla_decode_workspace_bytes(d, B,
  * max_keys) bytes; the absorb step alone uses only its first part), in stream order, and
- * with no other decode on that workspace in between.  Unlike the fused call, attend on the
- * matrix-core path (bf16, 64 heads, kv_lora 512, qk_rope 64, 16-byte aligned kv_b) returns
- * MLA_ERR_UNSUPPORTED for q_rope, Lc or Rc that are not 16-byte aligned. */
+ * with no other decode on that workspace in between. */
 mla_status mla_decode_absorb(const void *q_nope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
                              const mla_dims *d, int32_t B, void *ws, size_t ws_bytes, void *stream);
 mla_status mla_decode_attend(const void *q_rope, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt,
@@ -238,7 +241,9 @@ mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt
  *   s = sm_scale * (q[i][h][:qk_nope] . k_nope(t,h) + q[i][h][qk_nope:] . Rc(t)),
  * softmax, out[i][h] = sum_t p v(t,h).
  *   q     device [S][H][qk_nope+qk_rope] (tail already rotated), q_dt
- *   kv    host struct for sequence 0 (seq_len is not read); rows 0..pos_base+S-1 used
+ *   kv    host struct for sequence 0 (seq_len is not read); rows 0..pos_base+S-1 used.
+ *         Every position 0..pos_base+S-1 must map to a pool row: a block-table hole there
+ *         gives unspecified values (never an access outside the pools).
  *   out   device [S][H][v_head], out_dt
  *   ws    workspace of at least mla_prefill_workspace_bytes(d, S, pos_base+S) bytes
  * q_dt, w_dt and kv->kv_dtype must match.

@@ -4,16 +4,27 @@
 // absorb (W_UK folded into the query; needs only q_nope and kv_b) and attend (scores,
 // softmax, latent accumulation, W_UV).  The absorb step can therefore be issued early, e.g.
 // on a second stream while the indexer and the top-k run.
+#include <initializer_list>
+
 #include "decode_plan.h"
 
 namespace mla {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The path both steps take: decided from what the absorb step sees (shape, dtype, kv_b).
-static bool use_mfma(const mla_dims &d, mla_dtype dt, const void *kv_b)
+// The matrix-core kernels serve their geometry (decode_mfma_supported) only.  They read every
+// operand in 16-byte pieces, so on that geometry a tensor that is not 16-byte aligned is
+// rejected with MLA_ERR_UNSUPPORTED by every decode entry point alike: no call switches
+// kernels because of where a pointer sits.  Other geometries and fp32 take the generic kernels.
+static bool use_mfma(const mla_dims &d, mla_dtype dt) { return decode_mfma_supported(d, dt); }
+
+static mla_status need_aligned(const char *what, std::initializer_list<const void *> ps)
 {
-    return decode_mfma_supported(d, dt) && aligned16(kv_b);
+    for (const void *p : ps)
+        if (!aligned16(p))
+            return fail(MLA_ERR_UNSUPPORTED, "%s: on the matrix-core geometry (bf16, 64 heads, kv_lora 512, "
+                        "qk_rope 64) every tensor must be 16-byte aligned", what);
+    return MLA_OK;
 }
 
 size_t decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t max_keys, mla_dtype dt)
@@ -39,7 +50,11 @@ size_t decode_absorb_workspace_bytes(const mla_dims &d, int32_t B, mla_dtype dt)
 mla_status launch_decode_absorb(const void *q_nope, const void *kv_b, mla_dtype dt, const mla_dims &d, int32_t B,
                                 void *ws, hipStream_t s)
 {
-    if (use_mfma(d, dt, kv_b)) return launch_absorb_mfma(q_nope, kv_b, d, B, ws, s);
+    if (use_mfma(d, dt)) {
+        mla_status st = need_aligned("decode absorb", {q_nope, kv_b});
+        if (st) return st;
+        return launch_absorb_mfma(q_nope, kv_b, d, B, ws, s);
+    }
     return launch_absorb_generic(q_nope, kv_b, dt, d, B, ws, s);
 }
 
@@ -47,11 +62,9 @@ mla_status launch_decode_attend(const void *q_rope, const void *kv_b, mla_dtype 
                                 const KvView &kv, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
                                 int64_t max_keys, float sm_scale, float *out, void *ws, hipStream_t s)
 {
-    if (use_mfma(d, dt, kv_b)) {
-        if (!aligned16(q_rope) || !aligned16(kv.lc) || !aligned16(kv.rc))
-            return fail(MLA_ERR_UNSUPPORTED,
-                        "decode: the matrix-core path needs 16-byte aligned q_rope, Lc and Rc (the fused call "
-                        "mla_absorbed_decode falls back to the generic kernels instead)");
+    if (use_mfma(d, dt)) {
+        mla_status st = need_aligned("decode attend", {q_rope, kv_b, kv.lc, kv.rc});
+        if (st) return st;
         return launch_attend_mfma(q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
     }
     return launch_attend_generic(q_rope, kv_b, dt, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
@@ -63,7 +76,9 @@ mla_status launch_decode(const void *q_nope, const void *q_rope, const void *kv_
                          float *out, void *ws, size_t, hipStream_t s)
 {
     mla_status st;
-    if (use_mfma(d, dt, kv_b) && aligned16(q_rope) && aligned16(kv.lc) && aligned16(kv.rc)) {
+    if (use_mfma(d, dt)) {
+        st = need_aligned("decode", {q_nope, q_rope, kv_b, kv.lc, kv.rc});
+        if (st) return st;
         st = launch_absorb_mfma(q_nope, kv_b, d, B, ws, s);
         if (st) return st;
         return launch_attend_mfma(q_rope, kv_b, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s);
@@ -100,9 +115,11 @@ mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype d
     p += al256(decode_workspace_bytes(d, B, k, dt));
     void *qr = p;
     mla_status st;
-    const bool mfma = use_mfma(d, dt, kv_b) && aligned16(q_nope) && aligned16(q_rope) && aligned16(kv.lc) &&
-                      aligned16(kv.rc) && B <= SIDE_MAXB;
-    if (mfma) {
+    if (use_mfma(d, dt)) {
+        st = need_aligned("dsa decode", {q_nope, q_rope, kv_b, kv.lc, kv.rc});
+        if (st) return st;
+    }
+    if (use_mfma(d, dt) && B <= SIDE_MAXB) {
         // the query absorption and the rotation run as extra workgroups of the selection's
         // resolve step, which occupies only B workgroups
         SideAbsorb sa;

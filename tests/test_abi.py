@@ -272,3 +272,34 @@ def test_tiled_index_pool_validation(L):
     assert f(_view(ic_layout=mla.MLA_IC_TILE64, rows=2 * 4160, seq_stride=4100)) == mla.MLA_ERR_ARG   # stride % 64
     bt = ctypes.c_void_p(0x5000)
     assert f(_view(ic_layout=mla.MLA_IC_TILE64, block_table=bt.value, block_size=16, max_blocks=256)) == mla.MLA_ERR_ARG
+
+
+def test_misaligned_pointers_rejected_alike(L):
+    """On the matrix-core geometry a tensor that is not 16-byte aligned gives MLA_ERR_UNSUPPORTED in
+    every decode and prefill call (fused, split, whole step, prefill), before anything is launched:
+    no call switches kernels because of where a pointer sits.  fp32 inputs take the generic kernels."""
+    _no_gpu()
+    d = _dims()
+    MIS = ctypes.c_void_p(0x1002)
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 4096)
+    ws = ctypes.c_void_p(0x100000)
+    for args in ((MIS, FAKE, FAKE), (FAKE, MIS, FAKE), (FAKE, FAKE, MIS)):
+        qn, qr, kvb = args
+        st = L.mla_absorbed_decode(qn, qr, 1, kvb, 1, ctypes.byref(d), 1, ctypes.byref(_view()), None, None, 0,
+                                   0.0625, FAKE, ws, need, None)
+        assert st == mla.MLA_ERR_UNSUPPORTED, args
+    st = L.mla_absorbed_decode(FAKE, FAKE, 1, FAKE, 1, ctypes.byref(d), 1, ctypes.byref(_view(lc=0x1002)), None,
+                               None, 0, 0.0625, FAKE, ws, need, None)
+    assert st == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_decode_absorb(MIS, 1, FAKE, 1, ctypes.byref(d), 1, ws, need, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_decode_attend(FAKE, 1, FAKE, 1, ctypes.byref(d), 1, ctypes.byref(_view(rc=0x2002)), None, None, 0,
+                               0.0625, FAKE, ws, need, None) == mla.MLA_ERR_UNSUPPORTED
+    need2 = L.mla_dsa_decode_workspace_bytes(ctypes.byref(d), 1, 4096, 2048)
+    assert L.mla_dsa_decode(MIS, FAKE, 1, 1e4, FAKE, FAKE, 32, FAKE, 1, ctypes.byref(d), 1, ctypes.byref(_view()),
+                            4096, 2048, 0.0625, FAKE, FAKE, FAKE, FAKE, ws, need2, None) == mla.MLA_ERR_UNSUPPORTED
+    needp = L.mla_prefill_workspace_bytes(ctypes.byref(d), 4096, 4096)
+    for q, out, v in ((MIS, FAKE, _view(seq_len=None)), (FAKE, MIS, _view(seq_len=None)),
+                      (FAKE, FAKE, _view(seq_len=None, lc=0x1008))):
+        assert L.mla_prefill_nonabsorbed(q, 1, FAKE, 1, ctypes.byref(d), ctypes.byref(v), 4096, 0, 0.0625, out, 0,
+                                         ws, needp, None) == mla.MLA_ERR_UNSUPPORTED
+    assert "16-byte aligned" in mla.mla_last_error()

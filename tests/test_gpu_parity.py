@@ -705,8 +705,9 @@ def test_topk_all_equal_full_context():
 
 
 def test_decode_generic_and_matrix_core_paths_agree():
-    """A 2-byte offset makes the query pointer misaligned, which routes the same GLM-shape
-    inputs to the generic kernels; both paths must meet the oracle bar."""
+    """The same GLM-shape values through the matrix-core kernels (bf16) and the generic kernels
+    (the same values widened to fp32) both meet the oracle; a query pointer 2 bytes off is
+    rejected with MLA_ERR_UNSUPPORTED, never routed to other kernels."""
     T = 900
     d = synth.decode(80, T, B=2)
     sm = 1.0 / math.sqrt(d.nope + d.rope)
@@ -717,11 +718,17 @@ def test_decode_generic_and_matrix_core_paths_agree():
     qn_mis.copy_(qn)
     log("decode generic vs matrix-core")
     fast = host(mla.mla_absorbed_decode(qn, dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm))
-    slow = host(mla.mla_absorbed_decode(qn_mis, dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm))
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_absorbed_decode(qn_mis, dev_bf16(d.q_rope), dev_bf16(d.kv_b), kv, sm)
+    assert e.value.status == mla.MLA_ERR_UNSUPPORTED
+    f32 = lambda bits: dev(synth.bf16_bits_to_f32(bits))
+    kv32 = _kv(synth.bf16_bits_to_f32(d.lc), synth.bf16_bits_to_f32(d.rc), None, [T, 611], T, seq_stride=T,
+               bf16=False)
+    slow = host(mla.mla_absorbed_decode(f32(d.q_nope), f32(d.q_rope), f32(d.kv_b), kv32, sm))
     for b, n in enumerate([T, 611]):
         ref = _decode_ref(d, b, np.arange(n), sm)
         assert rel_err(fast[b], ref) <= TOL_BF16
-        assert rel_err(slow[b], ref) <= TOL_BF16
+        assert rel_err(slow[b], ref) <= TOL_F32
 
 
 def test_decode_batched_long_splits_and_growing_scores():
