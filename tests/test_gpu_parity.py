@@ -182,6 +182,37 @@ def test_index_scores_full_context_131072():
     assert np.array_equal(s.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+def test_index_scores_subnormal_products_bit_exact(tiled):
+    """Products and partial sums in the subnormal range and near FLT_MIN, with mixed magnitudes and
+    signs: heads scaled by 2^-70 .. 1 and key rows by 2^-70 .. 1, so per-head dot products land
+    anywhere from 2^-140 (subnormal) to O(1).  The scores must equal the fixed-order fmaf oracle bit
+    for bit (a flush of subnormal products or sums to zero would change them), and so must the
+    selection that ranks them."""
+    rng = np.random.default_rng(240 + tiled)
+    T, n_ih, hd, k = 9000, 32, 128, 512
+    q = rng.standard_normal((1, n_ih, hd)).astype(np.float32)
+    q *= np.float32(2.0) ** rng.choice([-70, -64, -60, -40, 0], n_ih).astype(np.float32)[None, :, None]
+    ic = rng.standard_normal((T, hd)).astype(np.float32)
+    ic *= np.float32(2.0) ** rng.choice([-70, -66, -56, -20, 0], T).astype(np.float32)[:, None]
+    ic[::7, ::3] = np.float32(2.0 ** -126) * rng.choice([-1, 1], ic[::7, ::3].shape).astype(np.float32)
+    w = (rng.standard_normal((1, n_ih)) * np.float32(2.0) ** rng.choice([-10, 0], (1, n_ih))).astype(np.float32)
+    ref = oracle.index_scores(q[0], w[0], ic)
+    sub = np.abs(ref[ref != 0]) < np.finfo(np.float32).tiny
+    assert sub.sum() > 100, "the case must produce subnormal scores"
+    log(f"index subnormal tiled={tiled}")
+    Tp = (T + 63) // 64 * 64             # the tiled pool holds whole 64-row tiles
+    icp = np.zeros((Tp, hd), np.float32)
+    icp[:T] = ic
+    zero = np.zeros((Tp, 8), np.uint16)
+    kv = _kv(zero, zero, icp, [T], T, seq_stride=Tp, tiled=tiled)
+    s = host(mla.dsa_index_scores(dev(q), dev(w), kv, T))[0]
+    assert np.array_equal(s.view(np.uint32), ref.view(np.uint32))
+    sel, nsel = _select_check(q, w, kv, T, k, [T])
+    rs, rn = oracle.topk(ref, T, k)
+    assert int(nsel[0]) == rn and np.array_equal(sel[0], rs)
+
+
 def test_index_empty_and_zero_length():
     q, w, kv, logical, _ = _index_case(2, [0, 5], 64, 32, 128, False, 250)
     s = host(mla.dsa_index_scores(dev(q), dev(w), kv, 64))
@@ -475,6 +506,37 @@ def test_decode_repeat_runs_bit_identical():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------------------ tiny layer (config 1)
+def test_tiny_layer_gpu_rope_absorbed_and_nonabsorbed():
+    """The tiny fp32 layer with the GPU doing the rotations: the raw kv_a and q_b tails (plain float64
+    matmuls of the layer's weights, rounded to fp32) are rotated by mla_rope_interleave at each
+    token's position (Rc) and at T - 1 (the query); the absorbed decode and the non-absorbed prefill
+    (S = 1) of the rotated query then both match the oracle's tiny layer, whose RoPE is its own."""
+    t = synth.tiny_layer(1)
+    lc, rc, q = oracle.tiny_layer(t.x, t.q_a, t.q_b, t.kv_a, t.H, t.nope, t.rope, t.L)
+    sm = 1.0 / math.sqrt(t.nope + t.rope)
+    ref = oracle.absorbed_decode(q[:, : t.nope].astype(np.float32), q[:, t.nope:].astype(np.float32), t.kv_b,
+                                 lc.astype(np.float32), rc.astype(np.float32), np.arange(t.T), t.v, sm)
+    comp = t.x.astype(np.float64) @ t.kv_a.astype(np.float64).T
+    qa = t.q_a.astype(np.float64) @ t.x[-1].astype(np.float64)
+    qa = qa / np.sqrt((qa ** 2).mean() + 1e-6)
+    qf = (t.q_b.astype(np.float64) @ qa).reshape(t.H, t.nope + t.rope).astype(np.float32)
+    log("tiny layer: GPU RoPE, absorbed and non-absorbed")
+    rc_d = dev(np.ascontiguousarray(comp[:, t.L:].astype(np.float32)).reshape(t.T, 1, t.rope))
+    mla.mla_rope_interleave(rc_d, dev(np.arange(t.T, dtype=np.int32)), 0, t.rope)
+    q_d = dev(qf[None])
+    mla.mla_rope_interleave(q_d, dev(np.array([t.T - 1], np.int32)), t.nope, t.rope)
+    assert np.abs(host(rc_d).reshape(t.T, t.rope) - rc).max() <= 2e-6 * np.abs(rc).max()
+    kv = mla.KvCache(dev(lc.astype(np.float32)), rc_d.reshape(t.T, t.rope), max_seq_len=t.T, seq_stride=t.T,
+                     seq_len=dev(np.array([t.T], np.int32)))
+    q_h = q_d[0]
+    out_a = host(mla.mla_absorbed_decode(q_h[None, :, : t.nope].contiguous(), q_h[None, :, t.nope:].contiguous(),
+                                         dev(t.kv_b), kv, sm))[0]
+    out_n = host(mla.mla_prefill_nonabsorbed(q_d, dev(t.kv_b), kv, t.nope, t.T - 1, sm))[0]
+    assert rel_err(out_a, ref) <= TOL_F32
+    assert rel_err(out_n, ref) <= TOL_F32
+
+
 # ------------------------------------------------------------------------------ prefill
 def test_prefill_tiny_fp32_last_row_equals_decode():
     t = synth.tiny_layer(1)
@@ -538,11 +600,30 @@ def test_prefill_glm_64_heads(S, pos_base, out_bf16, bs):
 
 
 def test_prefill_full_4096_sampled_rows():
-    """S = T = 4096 (the benchmark configuration), rows at block edges and spread out."""
+    """S = T = 4096 (the benchmark configuration): 64 evenly spaced query rows, including 0 and
+    S - 1, on all 64 heads, against the oracle."""
     S = 4096
-    log("prefill S=T=4096")
-    rows = np.array([0, 1, 127, 128, 1000, 2047, 2048, 3333, 4094, 4095])
-    _prefill_glm_check(S, 0, 4, False, rows, [0, 21, 42, 63])
+    log("prefill S=T=4096, 64 rows x 64 heads")
+    rows = np.unique(np.linspace(0, S - 1, 64).round().astype(int))
+    assert rows.size == 64 and rows[0] == 0 and rows[-1] == S - 1
+    _prefill_glm_check(S, 0, 4, False, rows, list(range(64)))
+
+
+@pytest.mark.parametrize("T", [1, 777, 4096])
+def test_prefill_single_query_equals_absorbed_decode(T):
+    """colibri-analysis 06, sec. 2.3: the two attention paths compute the same function.  One
+    prefill query at pos_base = T - 1 on the matrix-core kernels (64 heads, GLM shapes) equals the
+    oracle's absorbed decode of that query over keys 0..T-1."""
+    p = synth.prefill(170 + T, 1, T - 1)
+    sm = 1.0 / math.sqrt(p.nope + p.rope)
+    log(f"prefill S=1 pos_base={T - 1} vs absorbed decode")
+    kv = _kv(p.lc, p.rc, None, None, T, seq_stride=T)
+    out = host(mla.mla_prefill_nonabsorbed(dev_bf16(p.q), dev_bf16(p.kv_b), kv, p.nope, T - 1, sm))[0]
+    cv = synth.bf16_bits_to_f32
+    q = cv(p.q)[0]
+    ref = oracle.absorbed_decode(q[:, : p.nope], q[:, p.nope:], cv(p.kv_b), cv(p.lc), cv(p.rc), np.arange(T),
+                                 p.v, sm)
+    assert rel_err(out, ref) <= TOL_BF16
 
 
 # ------------------------------------------------------------------------------ end to end
