@@ -190,16 +190,17 @@ def test_index_scores_subnormal_products_bit_exact(tiled):
     for bit (a flush of subnormal products or sums to zero would change them), and so must the
     selection that ranks them."""
     rng = np.random.default_rng(240 + tiled)
-    T, n_ih, hd, k = 9000, 32, 128, 512
+    T, n_ih, hd, k = 9000, 32, 128, 8000     # k so large that the threshold sits among subnormal scores
     q = rng.standard_normal((1, n_ih, hd)).astype(np.float32)
-    q *= np.float32(2.0) ** rng.choice([-70, -64, -60, -40, 0], n_ih).astype(np.float32)[None, :, None]
+    q *= np.float32(2.0) ** rng.choice([-70, -64, -40, -3, 0], n_ih).astype(np.float32)[None, :, None]
     ic = rng.standard_normal((T, hd)).astype(np.float32)
-    ic *= np.float32(2.0) ** rng.choice([-70, -66, -56, -20, 0], T).astype(np.float32)[:, None]
+    ic *= np.float32(2.0) ** rng.choice([-70, -56, -20, 0, -126, -130, -134], T).astype(np.float32)[:, None]
     ic[::7, ::3] = np.float32(2.0 ** -126) * rng.choice([-1, 1], ic[::7, ::3].shape).astype(np.float32)
-    w = (rng.standard_normal((1, n_ih)) * np.float32(2.0) ** rng.choice([-10, 0], (1, n_ih))).astype(np.float32)
+    w = (rng.standard_normal((1, n_ih)) * np.float32(2.0) ** rng.choice([-6, 0], (1, n_ih))).astype(np.float32)
     ref = oracle.index_scores(q[0], w[0], ic)
-    sub = np.abs(ref[ref != 0]) < np.finfo(np.float32).tiny
-    assert sub.sum() > 100, "the case must produce subnormal scores"
+    tiny = np.finfo(np.float32).tiny
+    assert ((ref != 0) & (np.abs(ref) < tiny)).sum() > 1000, "the case must produce subnormal scores"
+    assert ((ic != 0) & (np.abs(ic) < tiny)).sum() > 1000, "and subnormal key inputs"
     log(f"index subnormal tiled={tiled}")
     Tp = (T + 63) // 64 * 64             # the tiled pool holds whole 64-row tiles
     icp = np.zeros((Tp, hd), np.float32)
