@@ -233,6 +233,25 @@ mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt
                           int32_t *nsel, float *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * mla_dsa_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops or harnesses that forbid hipMalloc).  Same
+ * arguments, results (bit for bit) and errors as mla_dsa_decode, minus ws / ws_bytes: the scratch
+ * is a static device array of the library, 64 MiB (MLA_NOALLOC_SCRATCH_BYTES), one copy per GPU,
+ * held from the library's first use on that GPU until the process ends.  The call uses the copy of
+ * the calling thread's current device (the stream must belong to it), allocates nothing and calls
+ * no allocating routine.  A step whose workspace (mla_dsa_decode_workspace_bytes) exceeds the
+ * array returns MLA_ERR_WORKSPACE: at the GLM geometry that admits e.g. B = 8 at t_max = 131072,
+ * k = 2048 (57.3 MiB).  Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race; calls in stream order do not.
+ * --------------------------------------------------------------------------------- */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status mla_dsa_decode_noalloc(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                  const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b,
+                                  mla_dtype w_dt, const mla_dims *d, int32_t B, const mla_kv_view *kv,
+                                  int64_t t_max, int32_t k, float sm_scale, float *scores, int32_t *sel,
+                                  int32_t *nsel, float *out, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Non-absorbed causal prefill of S queries of one sequence.  [MLA] sec. 2.3
  * (non-absorbed path): one kv_b matmul rebuilds k_nope and v for every token,
  *   [k_nope | v](t, h) = kv_b[h*(qk_nope+v_head) .. +qk_nope+v_head) . Lc(t),

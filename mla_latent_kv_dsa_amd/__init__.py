@@ -31,7 +31,7 @@ EXPORTED = (
     "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
     "dsa_index_select_workspace_bytes", "dsa_index_select",
     "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
-    "mla_dsa_decode_workspace_bytes", "mla_dsa_decode",
+    "mla_dsa_decode_workspace_bytes", "mla_dsa_decode", "mla_dsa_decode_noalloc",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
@@ -100,6 +100,10 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(mla_dims), i32, ctypes.POINTER(mla_kv_view), i64, i32, ctypes.c_float,
                                  P, P, P, P, P, ctypes.c_size_t, P]
     L.mla_dsa_decode.restype = st
+    L.mla_dsa_decode_noalloc.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P, P, i32, P, ctypes.c_int,
+                                         ctypes.POINTER(mla_dims), i32, ctypes.POINTER(mla_kv_view), i64, i32,
+                                         ctypes.c_float, P, P, P, P, P]
+    L.mla_dsa_decode_noalloc.restype = st
     L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
     L.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.mla_prefill_nonabsorbed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims),
@@ -378,10 +382,13 @@ def mla_dsa_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, q_idx: torch.Tens
                    kv_b: torch.Tensor, kv: KvCache, t_max: int, k: int, sm_scale: float, theta: float = 10000.0,
                    scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
                    nsel: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None):
+                   ws: Optional[torch.Tensor] = None, noalloc: bool = False):
     """The whole decode step: RoPE of q_rope [B, H, rope] (before rotation; not modified) at
     position seq_len - 1, indexer scores and top-k selection, absorbed attention over the
-    selected keys.  Returns (out [B, H, v] float32, scores [B, t_max], sel [B, k], nsel [B])."""
+    selected keys.  Returns (out [B, H, v] float32, scores [B, t_max], sel [B, k], nsel [B]).
+    noalloc=True calls mla_dsa_decode_noalloc (the library's static scratch; no ws)."""
+    if noalloc and ws is not None:
+        raise ValueError("noalloc takes no workspace")
     _dev(q_nope, q_rope, q_idx, w_idx, kv_b, scores, sel, nsel, out, ws)
     _contig(q_nope, q_rope, q_idx, w_idx, kv_b, scores, sel, nsel, out, ws)
     B, H, nope = q_nope.shape
@@ -409,6 +416,12 @@ def mla_dsa_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, q_idx: torch.Tens
     if out is None:
         out = torch.empty((B, H, v), dtype=torch.float32, device=dev)
     d = _dims(H, nope, rope, v, L)
+    if noalloc:
+        _check(lib().mla_dsa_decode_noalloc(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), float(theta), _ptr(q_idx),
+                                            _ptr(w_idx), n_ih, _ptr(kv_b), _dt(kv_b), ctypes.byref(d), B,
+                                            ctypes.byref(kv.view), t_max, k, float(sm_scale), _ptr(scores),
+                                            _ptr(sel), _ptr(nsel), _ptr(out), _stream(dev)))
+        return out, scores, sel, nsel
     need = int(lib().mla_dsa_decode_workspace_bytes(ctypes.byref(d), B, t_max, k))
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

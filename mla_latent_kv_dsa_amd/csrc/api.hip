@@ -307,13 +307,16 @@ size_t mla_dsa_decode_workspace_bytes(const mla_dims *d, int32_t B, int64_t t_ma
     return a > b ? a : b;
 }
 
-mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
-                          const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b, mla_dtype w_dt,
-                          const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
-                          float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
-                          size_t ws_bytes, void *stream)
+}  // extern "C"
+
+// Checks of the whole decode step, everything but the workspace (shared by the call that takes a
+// workspace and the one that uses the library's static scratch).
+static mla_status check_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                   const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b,
+                                   mla_dtype w_dt, const mla_dims *d, int32_t B, const mla_kv_view *kv,
+                                   int64_t t_max, int32_t k, float sm_scale, const float *scores, const int32_t *sel,
+                                   const int32_t *nsel, const float *out)
 {
-    g_err[0] = 0;
     mla_status st = check_decode_common(d, B, q_dt, w_dt);
     if (st) return st;
     st = check_view(kv, B, true, true, true);
@@ -334,13 +337,60 @@ mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt
     if (B == 0) return MLA_OK;
     if (!q_nope || !q_rope || !q_idx || !w_idx || !kv_b || !sel || !nsel || !out || (!scores && t_max > 0))
         return fail(MLA_ERR_ARG, "dsa decode: NULL tensor");
-    st = check_ws("dsa decode", dsa_decode_workspace_bytes(*d, B, t_max, k, q_dt), ws, ws_bytes);
-    if (st) return st;
+    return MLA_OK;
+}
+
+static mla_status run_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                 const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b,
+                                 const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
+                                 float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                                 void *stream)
+{
     const KvView v = to_view(*kv);
     KvView vs = v;
     if (vs.max_seq_len > t_max) vs.max_seq_len = t_max;
     return launch_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv->index_hd, kv_b, *d, B, vs, v,
                              t_max, k, sm_scale, scores, sel, nsel, out, ws, (hipStream_t)stream);
+}
+
+extern "C" {
+
+mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                          const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b, mla_dtype w_dt,
+                          const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
+                          float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv_b, w_dt, d, B, kv,
+                                     t_max, k, sm_scale, scores, sel, nsel, out);
+    if (st || B == 0) return st;
+    st = check_ws("dsa decode", dsa_decode_workspace_bytes(*d, B, t_max, k, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return run_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv_b, d, B, kv, t_max, k, sm_scale,
+                          scores, sel, nsel, out, ws, stream);
+}
+
+mla_status mla_dsa_decode_noalloc(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                  const float *q_idx, const float *w_idx, int32_t n_ih, const void *kv_b,
+                                  mla_dtype w_dt, const mla_dims *d, int32_t B, const mla_kv_view *kv,
+                                  int64_t t_max, int32_t k, float sm_scale, float *scores, int32_t *sel,
+                                  int32_t *nsel, float *out, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv_b, w_dt, d, B, kv,
+                                     t_max, k, sm_scale, scores, sel, nsel, out);
+    if (st || B == 0) return st;
+    const size_t need = dsa_decode_workspace_bytes(*d, B, t_max, k, q_dt);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MLA_ERR_WORKSPACE,
+                    "dsa decode (no allocation): this step needs %zu bytes of scratch, the library's static "
+                    "scratch holds %zu (use mla_dsa_decode with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    st = noalloc_scratch(&scratch);
+    if (st) return st;
+    return run_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, kv_b, d, B, kv, t_max, k, sm_scale,
+                          scores, sel, nsel, out, scratch, stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T)

@@ -265,6 +265,11 @@ mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype d
                              float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
                              hipStream_t s);
 
+// The library's static device scratch (noalloc.hip): its size, and its address on the calling
+// thread's current device (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = MLA_NOALLOC_SCRATCH_BYTES;
+mla_status noalloc_scratch(void **ptr);
+
 size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt);
 mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d,
                           const KvView &kv, int32_t S, int32_t pos_base, float sm_scale,

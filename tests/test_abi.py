@@ -303,3 +303,24 @@ def test_misaligned_pointers_rejected_alike(L):
         assert L.mla_prefill_nonabsorbed(q, 1, FAKE, 1, ctypes.byref(d), ctypes.byref(v), 4096, 0, 0.0625, out, 0,
                                          ws, needp, None) == mla.MLA_ERR_UNSUPPORTED
     assert "16-byte aligned" in mla.mla_last_error()
+
+
+def test_noalloc_decode_validation(L):
+    """mla_dsa_decode_noalloc validates like mla_dsa_decode, and a step whose workspace exceeds the
+    library's static scratch is refused with MLA_ERR_WORKSPACE before any HIP call."""
+    _no_gpu()
+    d = _dims()
+    BT = ctypes.c_void_p(0x5000)
+
+    def f(B=1, v=None, t=4096, k=2048, q_dt=1, out=FAKE):
+        return L.mla_dsa_decode_noalloc(FAKE, FAKE, q_dt, 1e4, FAKE, FAKE, 32, FAKE, 1, ctypes.byref(d), B,
+                                        ctypes.byref(v or _view()), t, k, 0.0625, FAKE, FAKE, FAKE, out, None)
+    assert f(q_dt=0) == mla.MLA_ERR_UNSUPPORTED
+    assert f(out=None) == mla.MLA_ERR_ARG
+    assert f(k=0) == mla.MLA_ERR_ARG
+    assert f(B=0) == mla.MLA_OK
+    paged = _view(block_table=BT.value, block_size=64, max_blocks=2048, rows=4096, max_seq_len=131072)
+    need = L.mla_dsa_decode_workspace_bytes(ctypes.byref(d), 32, 131072, 2048)
+    assert need > (64 << 20)
+    assert f(B=32, v=paged, t=131072) == mla.MLA_ERR_WORKSPACE
+    assert "static scratch" in mla.mla_last_error()
