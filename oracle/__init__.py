@@ -64,6 +64,8 @@ def _load():
     lib.orc_prefill_rows.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f64, P, i32, P]
     lib.orc_tiny_layer.argtypes = [P, i32, i32, P, i32, P, P, i32, i32, i32, i32, f64, f64, P, P, P]
     lib.orc_o_proj.argtypes = [P, P, i32, i32, P]
+    lib.orc_cache_write.argtypes = [P, P, i64, P, P, i32, i32, i32, P, P, P, i32, i32, f64, f64, f64, P, i32, i32,
+                                    i64, i64, P, P, P]
     _lib = lib
     return lib
 
@@ -222,3 +224,39 @@ def o_proj(o_w, attn) -> np.ndarray:
     y = np.empty(hidden, dtype=np.float64)
     _load().orc_o_proj(_p(o_w), _p(a), hidden, hv, _p(y))
     return y
+
+
+def cache_write(comp, ik, seq, pos, L: int, rope: int, *, rows: int, hd: int = 0, kv_gain=None, gamma=None,
+                beta=None, ix_off: int = 0, ix_rdim: int = 0, eps_kv: float = 1e-6, eps_ix: float = 1e-6,
+                theta: float = 10000.0, block_table=None, block_size: int = 0, seq_stride: int = 0,
+                lc=None, rc=None, ic=None):
+    """Write new tokens into the cache pools (colibri-analysis 06, sec. 2.1 KV path and sec. 2.2
+    indexer key): Lc = RMSNorm(comp[:L]) * kv_gain, Rc = RoPE(comp[L:]), Ic = RoPE over
+    [ix_off, ix_off + ix_rdim) of LayerNorm(ik), at each token's position.  Pools are float64
+    [rows, width]; pass existing pools (lc, rc, ic) to write into them, otherwise they start as NaN
+    so that untouched rows stay recognisable.  Returns (lc, rc, ic)."""
+    comp = _f32(comp)
+    n = comp.shape[0]
+    assert comp.shape == (n, L + rope)
+    seq, pos = _i32(seq), _i32(pos)
+    assert seq.shape == (n,) and pos.shape == (n,)
+    if ik is not None:
+        ik = _f32(ik)
+        hd = ik.shape[1]
+        assert ik.shape == (n, hd) and ix_rdim % 2 == 0 and ix_off + ix_rdim <= hd
+    lc = np.full((rows, L), np.nan) if lc is None else lc
+    rc = np.full((rows, rope), np.nan) if rc is None else rc
+    ic = (np.full((rows, hd), np.nan) if ic is None else ic) if ik is not None else None
+    assert lc.dtype == np.float64 and lc.flags.c_contiguous and lc.shape == (rows, L)
+    assert rc.dtype == np.float64 and rc.flags.c_contiguous and rc.shape == (rows, rope)
+    if ic is not None:
+        assert ic.dtype == np.float64 and ic.flags.c_contiguous and ic.shape == (rows, hd)
+    gains = [None if a is None else np.ascontiguousarray(_f32(a)) for a in (kv_gain, gamma, beta)]
+    bt = None if block_table is None else _i32(block_table)
+    _load().orc_cache_write(_p(comp), None if ik is None else _p(ik), n, _p(seq), _p(pos), L, rope, hd,
+                            None if gains[0] is None else _p(gains[0]), None if gains[1] is None else _p(gains[1]),
+                            None if gains[2] is None else _p(gains[2]), ix_off, ix_rdim, float(eps_kv),
+                            float(eps_ix), float(theta), None if bt is None else _p(bt), int(block_size),
+                            0 if bt is None else bt.shape[1], int(seq_stride), int(rows), _p(lc), _p(rc),
+                            None if ic is None else _p(ic))
+    return lc, rc, ic

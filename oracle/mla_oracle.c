@@ -439,3 +439,61 @@ void orc_o_proj(const float *o_w, const double *attn, int32_t hidden, int32_t hv
 {
     orc_matvec(o_w, attn, hidden, hv, y);
 }
+
+/* ------------------------------------------------------------------------------------
+ * Cache write of new tokens  [P2 sec. 2.1 KV path; sec. 2.2 indexer key]
+ * For each new token j (sequence seq[j], position pos[j]) with kv_a output comp[j] (L + rope
+ * wide) and indexer key projection ik[j] (hd wide, the ix_wk output):
+ *   Lc[row]  = RMSNorm(comp[0:L]) * kv_gain           (u / sqrt(mean(u^2) + eps_kv))
+ *   Rc[row]  = RoPE(comp[L:L+rope]) at pos[j]          (interleaved, as orc_rope_interleave)
+ *   Ic[row]  = RoPE over dims [ix_off, ix_off + ix_rdim) of
+ *              LayerNorm(ik) = (ik - mean) / sqrt(var + eps_ix) * gamma + beta   (var: mean of
+ *              squared deviations), at pos[j]
+ * row = block_table[seq*max_blocks + pos/bs]*bs + pos%bs (paged, bt != NULL) or
+ * seq*seq_stride + pos (contiguous); a row outside [0, rows) is skipped.  kv_gain, gamma, beta
+ * NULL mean ones / ones / zeros; ik NULL skips Ic.  Pools are double [rows][width].
+ * Readings: the pages name RMSNorm(kv_a_ln) and "layernorm(eps 1e-6) + RoPE" without the
+ * rotated slice of the indexer key; the slice is an argument (the MLA query puts its rotated
+ * part in the tail), both eps are arguments (1e-6 is the only value the pages give).
+ * ----------------------------------------------------------------------------------*/
+void orc_cache_write(const float *comp, const float *ik, int64_t n, const int32_t *seq, const int32_t *pos,
+                     int32_t L, int32_t rope, int32_t hd, const float *kv_gain, const float *gamma,
+                     const float *beta, int32_t ix_off, int32_t ix_rdim, double eps_kv, double eps_ix,
+                     double theta, const int32_t *bt, int32_t bs, int32_t max_blocks, int64_t seq_stride,
+                     int64_t rows, double *lc, double *rc, double *ic)
+{
+    double *u = (double *)malloc(sizeof(double) * (size_t)(L + rope + hd + 1));
+    double *y = (double *)malloc(sizeof(double) * (size_t)(hd + rope + 1));
+    for (int64_t j = 0; j < n; ++j) {
+        int64_t row;
+        if (bt) {
+            int32_t blk = bt[(int64_t)seq[j] * max_blocks + pos[j] / bs];
+            row = blk < 0 ? -1 : (int64_t)blk * bs + pos[j] % bs;
+        } else {
+            row = (int64_t)seq[j] * seq_stride + pos[j];
+        }
+        if (row < 0 || row >= rows) continue;
+        const float *cj = comp + j * (int64_t)(L + rope);
+        double ms = 0.0;
+        for (int32_t c = 0; c < L; ++c) ms += (double)cj[c] * (double)cj[c];
+        ms /= (double)L;
+        double inv = 1.0 / sqrt(ms + eps_kv);
+        for (int32_t c = 0; c < L; ++c)
+            lc[row * L + c] = (double)cj[c] * inv * (kv_gain ? (double)kv_gain[c] : 1.0);
+        for (int32_t c = 0; c < rope; ++c) u[c] = (double)cj[L + c];
+        orc_rope_interleave(u, rc + row * rope, 1, 1, rope, 0, rope, pos + j, theta);
+        if (!ik) continue;
+        const float *kj = ik + j * (int64_t)hd;
+        double mean = 0.0, var = 0.0;
+        for (int32_t c = 0; c < hd; ++c) mean += (double)kj[c];
+        mean /= (double)hd;
+        for (int32_t c = 0; c < hd; ++c) var += ((double)kj[c] - mean) * ((double)kj[c] - mean);
+        var /= (double)hd;
+        double is = 1.0 / sqrt(var + eps_ix);
+        for (int32_t c = 0; c < hd; ++c)
+            y[c] = ((double)kj[c] - mean) * is * (gamma ? (double)gamma[c] : 1.0) + (beta ? (double)beta[c] : 0.0);
+        orc_rope_interleave(y, ic + row * hd, 1, 1, hd, ix_off, ix_rdim, pos + j, theta);
+    }
+    free(u);
+    free(y);
+}

@@ -40,6 +40,19 @@ MUTATIONS = [
     ("tiny layer positions off by one", "int32_t pos = t;", "int32_t pos = t + 1;", 1),
     ("tiny layer query one position late", "orc_rope_interleave(qf, q, 1, H, qh, nope, rope, &pos, theta);",
      "{ int32_t qp = pos + 1; orc_rope_interleave(qf, q, 1, H, qh, nope, rope, &qp, theta); }", 1),
+    ("cache write rmsnorm over the rope tail too", "for (int32_t c = 0; c < L; ++c) ms += (double)cj[c] * (double)cj[c];",
+     "for (int32_t c = 0; c < L + rope; ++c) ms += (double)cj[c] * (double)cj[c];", 1),
+    ("cache write gain reversed", "(kv_gain ? (double)kv_gain[c] : 1.0)", "(kv_gain ? (double)kv_gain[L - 1 - c] : 1.0)", 1),
+    ("cache write rope key at the sequence index", "orc_rope_interleave(u, rc + row * rope, 1, 1, rope, 0, rope, pos + j, theta);",
+     "orc_rope_interleave(u, rc + row * rope, 1, 1, rope, 0, rope, seq + j, theta);", 1),
+    ("cache write paged offset dropped", "row = blk < 0 ? -1 : (int64_t)blk * bs + pos[j] % bs;",
+     "row = blk < 0 ? -1 : (int64_t)blk * bs;", 1),
+    ("cache write layernorm without the mean", "y[c] = ((double)kj[c] - mean) * is", "y[c] = ((double)kj[c]) * is", 1),
+    ("cache write variance of raw values", "var += ((double)kj[c] - mean) * ((double)kj[c] - mean);",
+     "var += (double)kj[c] * (double)kj[c];", 1),
+    ("cache write indexer rope slice at 0", "orc_rope_interleave(y, ic + row * hd, 1, 1, hd, ix_off, ix_rdim, pos + j, theta);",
+     "orc_rope_interleave(y, ic + row * hd, 1, 1, hd, 0, ix_rdim, pos + j, theta);", 1),
+    ("cache write beta dropped", "+ (beta ? (double)beta[c] : 0.0);", ";", 1),
 ]
 
 

@@ -402,3 +402,93 @@ def test_tiny_layer_rope_positions(oracle):
         k0 = oracle.rope_interleave(k_raw[tt][None, None], np.array([0]), 0, t.rope)[0, 0]
         lhs = q[:, t.nope:] @ rc[tt]
         assert np.max(np.abs(lhs - qr @ k0)) <= 1e-10 * max(np.abs(lhs).max(), 1e-30)
+
+
+# ----------------------------------------------------------------------------- cache write
+def _cw_case(seed, n=7, L=32, rope=8, hd=24):
+    rng = np.random.default_rng(seed)
+    comp = (rng.standard_normal((n, L + rope)) * 3.0 + 0.5).astype(np.float32)
+    ik = (rng.standard_normal((n, hd)) * 2.0 - 1.5).astype(np.float32)
+    pos = rng.integers(0, 5000, n).astype(np.int32)
+    return comp, ik, pos
+
+
+def test_cache_write_latent_is_rms_normalised(oracle):
+    """colibri-analysis 06, sec. 2.1: Lc = RMSNorm(first kv_lora values of the kv_a output).  With unit
+    gain the mean square of a row is ms / (ms + eps) exactly; a gain vector scales each column."""
+    comp, ik, pos = _cw_case(500)
+    n, L, rope = comp.shape[0], 32, 8
+    eps = 1e-3
+    seq = np.zeros(n, np.int32)
+    p = np.arange(n, dtype=np.int32)
+    lc, rc, _ = oracle.cache_write(comp, None, seq, p, L, rope, rows=n, seq_stride=n, eps_kv=eps)
+    ms = (comp[:, :L].astype(np.float64) ** 2).mean(1)
+    assert np.max(np.abs((lc ** 2).mean(1) - ms / (ms + eps))) <= 1e-12
+    assert np.all(np.sign(lc) == np.sign(comp[:, :L]))
+    g = np.random.default_rng(501).uniform(0.5, 2.0, L).astype(np.float32)
+    lg, _, _ = oracle.cache_write(comp, None, seq, p, L, rope, rows=n, seq_stride=n, eps_kv=eps, kv_gain=g)
+    assert np.max(np.abs(lg - lc * g.astype(np.float64))) <= 1e-12 * np.abs(lg).max()
+
+
+def test_cache_write_rope_key_rotates_at_token_position(oracle):
+    """Rc is the qk_rope tail of the kv_a output rotated at the token's position (sec. 2.1): each
+    output pair (y[j], y[half+j]) is the input pair (x[2j], x[2j+1]) times exp(i pos theta_j)."""
+    comp, ik, pos = _cw_case(502)
+    n, L, rope = comp.shape[0], 32, 8
+    seq = np.arange(n, dtype=np.int32) % 3
+    _, rc, _ = oracle.cache_write(comp, None, seq, pos, L, rope, rows=3 * 5000, seq_stride=5000)
+    rows = seq.astype(np.int64) * 5000 + pos
+    half = rope // 2
+    inv = 10000.0 ** (-2.0 * np.arange(half) / rope)
+    zin = comp[:, L::2].astype(np.float64) + 1j * comp[:, L + 1::2]
+    zout = rc[rows, :half] + 1j * rc[rows, half:]
+    assert np.max(np.abs(zout - zin * np.exp(1j * pos[:, None] * inv))) <= 1e-12 * np.abs(zin).max()
+
+
+def test_cache_write_indexer_key_layernorm_and_rope_slice(oracle):
+    """sec. 2.2: Ic = RoPE(LayerNorm(ix_wk output), eps 1e-6).  Unrotated, a row has mean 0 and variance
+    var / (var + eps); gamma and beta act per column; only dims [off, off + rdim) rotate, by
+    exp(i pos theta_j) on the interleaved pairs of that slice."""
+    comp, ik, pos = _cw_case(503)
+    n, L, rope, hd = comp.shape[0], 32, 8, 24
+    seq = np.zeros(n, np.int32)
+    p = np.arange(n, dtype=np.int32)
+    kw = dict(rows=n, seq_stride=n, eps_ix=1e-2)
+    _, _, y = oracle.cache_write(comp, ik, seq, p, L, rope, ix_off=0, ix_rdim=0, **kw)
+    var = ik.astype(np.float64).var(1)
+    assert np.max(np.abs(y.mean(1))) <= 1e-14
+    assert np.max(np.abs(y.var(1) - var / (var + 1e-2))) <= 1e-12
+    rng = np.random.default_rng(504)
+    gm, bt = rng.uniform(0.5, 2, hd).astype(np.float32), rng.standard_normal(hd).astype(np.float32)
+    _, _, yg = oracle.cache_write(comp, ik, seq, p, L, rope, ix_off=0, ix_rdim=0, gamma=gm, beta=bt, **kw)
+    assert np.max(np.abs(yg - (y * gm + bt))) <= 1e-12 * np.abs(yg).max()
+    off, rd = 10, 12
+    _, _, yr = oracle.cache_write(comp, ik, seq, p, L, rope, ix_off=off, ix_rdim=rd, gamma=gm, beta=bt, **kw)
+    keep = np.r_[0:off, off + rd:hd]
+    assert np.array_equal(yr[:, keep], yg[:, keep])
+    h = rd // 2
+    inv = 10000.0 ** (-2.0 * np.arange(h) / rd)
+    zin = yg[:, off:off + rd:2] + 1j * yg[:, off + 1:off + rd:2]
+    zout = yr[:, off:off + h] + 1j * yr[:, off + h:off + rd]
+    assert np.max(np.abs(zout - zin * np.exp(1j * p[:, None] * inv))) <= 1e-12 * np.abs(zin).max()
+
+
+def test_cache_write_paged_rows_worked_example(oracle):
+    """Row placement (the cache view: row = block_table[seq][pos / bs] * bs + pos % bs), worked by hand
+    for bs = 4 and block table [[2, 0], [1, -1]]: (seq 0, pos 5) -> block 0, row 1; (seq 0, pos 2) ->
+    block 2, row 10; (seq 1, pos 3) -> block 1, row 7; (seq 1, pos 6) -> a hole, not written.  Every
+    other row keeps its contents; each written row equals the same token written to a contiguous pool."""
+    comp, ik, _ = _cw_case(505, n=4)
+    L, rope, hd = 32, 8, 24
+    seq = np.array([0, 0, 1, 1], np.int32)
+    pos = np.array([5, 2, 3, 6], np.int32)
+    bt = np.array([[2, 0], [1, -1]], np.int32)
+    lc, rc, ic = oracle.cache_write(comp, ik, seq, pos, L, rope, rows=12, block_table=bt, block_size=4,
+                                    ix_off=16, ix_rdim=8)
+    written = {0: 1, 1: 10, 2: 7}
+    assert sorted(np.flatnonzero(~np.isnan(lc[:, 0]))) == sorted(written.values())
+    assert sorted(np.flatnonzero(~np.isnan(ic[:, 0]))) == sorted(written.values())
+    lc2, rc2, ic2 = oracle.cache_write(comp, ik, seq, pos, L, rope, rows=2 * 8, seq_stride=8, ix_off=16, ix_rdim=8)
+    for j, r in written.items():
+        c = seq[j] * 8 + pos[j]
+        assert np.array_equal(lc[r], lc2[c]) and np.array_equal(rc[r], rc2[c]) and np.array_equal(ic[r], ic2[c])
