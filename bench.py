@@ -262,9 +262,10 @@ def bench_dsa_decode(args):
     if not args.no_cpu:
         cpu = cpu_baseline_decode(d, T, K, sm)
     extra = {}
-    if not args.no_extra:   # the batched paged and the dense decode configurations
+    if not args.no_extra:   # the batched paged and dense decode configurations, and the prefill
         extra["batched_paged_B32"] = bench_batched_paged(args)
         extra["dense_decode_T4096"] = bench_dense_decode(args)
+        extra["prefill_S4096"] = measure_prefill(args, cpu=not args.no_cpu)
 
     line = {
         "metric": METRIC, "value": value, "unit": "keys·heads/s", "n_gpus": 1, "steps": args.steps,
@@ -416,9 +417,36 @@ def bench_dense_decode(args):
             "input_copies": NC, "data": "synthetic: torch seed 1002"}
 
 
+def _host_cores():
+    """Host cores this process may run on (the OpenMP team of the all-cores oracle run)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _oracle_timed(fn, reps, threads):
+    """Median wall time of fn() over reps runs with the oracle's OpenMP team set to threads."""
+    import oracle
+
+    oracle._load()
+    keep = oracle.num_threads()
+    oracle.set_num_threads(threads)
+    try:
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(keep)
+    return statistics.median(times)
+
+
 def cpu_baseline_decode(d, T, K, sm):
-    """The oracle (as it stands) on one full decode step of the same workload: indexer over
-    all T keys, top-k, absorbed decode over the selected keys, on the host's cores."""
+    """The oracle (as it stands) on one full decode step of the same workload: RoPE of the query,
+    indexer over all T keys, top-k, absorbed decode over the selected keys -- on all host cores and
+    on one thread (median of 3 each)."""
     import numpy as np
 
     import oracle
@@ -426,24 +454,32 @@ def cpu_baseline_decode(d, T, K, sm):
 
     cv = synth.bf16_bits_to_f32
     lc, rc, kvb = cv(d.lc), cv(d.rc), cv(d.kv_b)
-    qn, qr = cv(d.q_nope[0]), cv(d.q_rope[0])
-    qr = oracle.rope_interleave(qr[None], np.array([T - 1], np.int32), 0, d.rope)[0]
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
+    qn, qr0 = cv(d.q_nope[0]), cv(d.q_rope[0])
+
+    def step():
+        qr = oracle.rope_interleave(qr0[None], np.array([T - 1], np.int32), 0, d.rope)[0]
         s = oracle.index_scores(d.q_idx[0], d.w_idx[0], d.ic)
         sel, n = oracle.topk(s, T, K)
         oracle.absorbed_decode(qn, qr, kvb, lc, rc, sel[:n], d.v, sm)
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": T * d.H / t, "unit": "keys·heads/s", "cores": oracle.num_threads(), "kind": "oracle",
+
+    cores = _host_cores()
+    t_all = _oracle_timed(step, 3, cores)
+    t_one = _oracle_timed(step, 3, 1)
+    return {"value": T * d.H / t_all, "unit": "keys·heads/s", "cores": cores, "kind": "oracle",
             "sample": f"one full decode step at T={T} (RoPE of the query, fixed-order fp32 indexer over all keys, "
                       f"sort-based top-{K}, fp64 absorbed decode over the selected keys), median of 3 runs",
-            "seconds_per_step": t}
+            "seconds_per_step": t_all,
+            "single_thread": {"value": T * d.H / t_one, "cores": 1, "seconds_per_step": t_one}}
 
 
 # ----------------------------------------------------------------------------- prefill
-def bench_prefill(args):
+PREFILL_METRIC = "MLA prefill (non-absorbed) TFLOP/s at S=T=4096"
+
+
+def measure_prefill(args, cpu=True):
+    """S = T = 4096 non-absorbed prefill (kv_b GEMM + causal attention, 64 heads, bf16 in, bf16
+    out): TFLOP/s over the algorithmic flops (causal pairs only) against the bf16 matrix-core peak,
+    and the oracle's kv_b rebuild plus 64 evenly spaced query rows as the CPU baseline."""
     import numpy as np
     import torch
 
@@ -464,27 +500,65 @@ def bench_prefill(args):
     ws = torch.empty(mla.mla_prefill_workspace_bytes(p.H, p.nope, p.rope, p.v, p.L, S, S), dtype=torch.uint8,
                      device=dev)
     f = lambda: mla.mla_prefill_nonabsorbed(q, kvb, kv, p.nope, 0, sm, out=out, ws=ws)
-    for _ in range(args.warmup):
+    steps = max(5, args.steps // 5)
+    for _ in range(max(2, args.warmup)):
         f()
     torch.cuda.synchronize()
     e0, e1 = _events(torch, 2)
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         f()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    flops = 2 * S * (p.H * (p.nope + p.v)) * p.L + 2 * p.H * (S * (S + 1) // 2) * (p.nope + p.rope) \
-        + 2 * p.H * (S * (S + 1) // 2) * p.v
+    ms = e0.elapsed_time(e1) / steps
+    pairs = S * (S + 1) // 2
+    f_kvb = 2 * S * (p.H * (p.nope + p.v)) * p.L
+    f_attn = 2 * p.H * pairs * (p.nope + p.rope) + 2 * p.H * pairs * p.v
+    flops = f_kvb + f_attn
     tf = flops / (ms * 1e-3) / 1e12
-    line = {"metric": "MLA prefill (non-absorbed) TFLOP/s at S=T=4096", "value": tf, "unit": "TFLOP/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+    res = {"workload": "prefill_S4096", "S": S, "T": S, "heads": p.H, "qk_nope": p.nope, "qk_rope": p.rope,
+           "v_head": p.v, "kv_lora": p.L, "out_dtype": "bf16", "steps": steps, "ms_per_step": ms,
+           "TFLOPs": tf,
+           "roofline": {"kernel": "pf_kvb + pf_attn (the whole mla_prefill_nonabsorbed call)", "bound": "mfma",
+                        "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                        "traffic": None, "algorithmic_flops": flops, "flops_kv_b_gemm": f_kvb,
+                        "flops_attention": f_attn},
+           "data": "synthetic: numpy seed 4"}
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_prefill(p, sm)
+    return res
+
+
+def cpu_baseline_prefill(p, sm):
+    """The oracle on a bounded subset of the prefill: its kv_b rebuild of all 4096 tokens and 64
+    evenly spaced query rows (0 .. S-1), all 64 heads on all host cores, and 4 of the heads on one
+    thread (scaled by 16 to all heads).  Reported as query rows per second, the subset stated."""
+    import numpy as np
+
+    import oracle
+    from mla_latent_kv_dsa_amd import synth
+
+    cv = synth.bf16_bits_to_f32
+    q, kvb, lc, rc = cv(p.q), cv(p.kv_b), cv(p.lc), cv(p.rc)
+    rows = np.unique(np.linspace(0, p.S - 1, 64).round().astype(np.int32))
+    R = p.nope + p.v
+    q4, kvb4 = np.ascontiguousarray(q[:, :4]), np.ascontiguousarray(kvb[: 4 * R])
+    cores = _host_cores()
+    t_all = _oracle_timed(lambda: oracle.prefill_rows(q, kvb, lc, rc, 0, p.nope, p.v, sm, rows), 1, cores)
+    t_one = _oracle_timed(lambda: oracle.prefill_rows(q4, kvb4, lc, rc, 0, p.nope, p.v, sm, rows), 1, 1) * 16
+    return {"value": rows.size / t_all, "unit": "query rows/s (64 heads)", "cores": cores, "kind": "oracle",
+            "sample": "subset: the oracle's fp64 kv_b rebuild of all 4096 tokens plus 64 evenly spaced query rows "
+                      "(0 .. 4095), all heads; single thread on 4 heads scaled x16",
+            "seconds": t_all, "single_thread": {"value": rows.size / t_one, "cores": 1, "seconds": t_one}}
+
+
+def bench_prefill(args):
+    r = measure_prefill(args, cpu=not args.no_cpu)
+    line = {"metric": PREFILL_METRIC, "value": r["TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "prefill_S4096", "S": S, "heads": p.H, "qk_nope": p.nope, "qk_rope": p.rope,
-                       "v_head": p.v, "kv_lora": p.L},
-            "roofline": {"kernel": "mla_prefill_nonabsorbed", "bound": "mfma", "achieved": tf,
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
-                         "algorithmic_flops": flops}}
+            "config": {k: r[k] for k in ("workload", "S", "T", "heads", "qk_nope", "qk_rope", "v_head", "kv_lora")},
+            "roofline": r["roofline"], "cpu_baseline": r.get("cpu_baseline")}
     print(json.dumps(line), flush=True)
 
 
@@ -502,8 +576,12 @@ def bench_copy(args):
     a = torch.randn(n, device=dev)
     b = torch.empty_like(a)
     res = {}
-    # the runtime's blit kernel (copy_) and a one-pass elementwise kernel (mul by 1)
-    for name, f in (("copyBuffer", lambda: b.copy_(a)), ("elementwise", lambda: torch.mul(a, 1.0, out=b))):
+    r = torch.empty(1, device=dev)
+    # the runtime's blit kernel (copy_), a one-pass elementwise kernel (mul by 1), a read-only
+    # reduction (sum of the buffer into one value) and a write-only fill
+    for name, f in (("copyBuffer", lambda: b.copy_(a)), ("elementwise", lambda: torch.mul(a, 1.0, out=b)),
+                    ("reduce_read_only", lambda: torch.sum(a, 0, keepdim=True, out=r)),
+                    ("fill_write_only", lambda: b.fill_(1.0))):
         for _ in range(args.warmup):
             f()
         torch.cuda.synchronize()
@@ -565,6 +643,78 @@ def summarize_counters(args):
     print(open(out).read())
 
 
+def _pmc_rows(csv_path):
+    import csv
+
+    return list(csv.DictReader(open(csv_path)))
+
+
+def summarize_pmc(args):
+    """Write profiles/<name>.counters.txt: per-dispatch means of every counter found in the
+    rocprofv3 --pmc runs under --pmc-dirs (one pass per directory), for each kernel named in
+    --pmc-kernels, plus the HBM bytes per launch from FETCH_SIZE / WRITE_SIZE scaled by the
+    calibration runs under --calib-dir (a 256 MiB read-only reduction and a 256 MiB write-only fill
+    of `bench.py --workload copy`)."""
+    from collections import defaultdict
+
+    def csvs(d):
+        return [os.path.join(r, f) for r, _, fs in os.walk(d) for f in fs if f.endswith("counter_collection.csv")]
+
+    kernels = args.pmc_kernels.split("|")
+    means = {k: {} for k in kernels}
+    for d in args.pmc_dirs.split(","):
+        for path in csvs(d):
+            acc = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+            for r in _pmc_rows(path):
+                for k in kernels:
+                    if k in r["Kernel_Name"]:
+                        acc[k][r["Counter_Name"]][r.get("Dispatch_Id") or r.get("Correlation_Id")] += \
+                            float(r["Counter_Value"])
+            for k, cs in acc.items():
+                for c, per in cs.items():
+                    means[k][c] = (statistics.mean(per.values()), len(per))
+    fetch_unit = write_unit = None
+    if args.calib_dir:
+        cal = defaultdict(dict)
+        for path in [c for d in args.calib_dir.split(",") for c in csvs(d)]:
+            for name in ("reduce_kernel", "FillFunctor", "copyBuffer"):
+                m = defaultdict(lambda: defaultdict(float))
+                for r in _pmc_rows(path):
+                    if name in r["Kernel_Name"]:
+                        m[r["Counter_Name"]][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+                for c, per in m.items():
+                    cal[name][c] = statistics.median(per.values())
+        nbytes = COPY_MIB * 2**20
+        if cal["reduce_kernel"].get("FETCH_SIZE"):
+            fetch_unit = nbytes / cal["reduce_kernel"]["FETCH_SIZE"]
+        if cal["FillFunctor"].get("WRITE_SIZE"):
+            write_unit = nbytes / cal["FillFunctor"]["WRITE_SIZE"]
+    out = os.path.join(ROOT, "profiles", f"{args.counters_name}.counters.txt")
+    with open(out, "w") as fo:
+        fo.write(f"# rocprofv3 --pmc counters, mean per dispatch.  One pass per counter group:\n")
+        for grp in args.pmc_groups.split(";"):
+            fo.write(f"#   cd /tmp && rocprofv3 --pmc {grp} --output-format csv -d <dir> -- "
+                     f"python3 <repo>/bench.py {args.counters_cmd}\n")
+        if args.calib_dir:
+            fo.write("# calibration: the same FETCH_SIZE and WRITE_SIZE passes over python3 <repo>/bench.py "
+                     "--workload copy --steps 5 --warmup 1\n")
+            for name, c in sorted(cal.items()):
+                fo.write(f"#   {name}: " + ", ".join(f"{k} {v:.1f}" for k, v in sorted(c.items())) + "\n")
+            fo.write(f"fetch_bytes_per_unit = {fetch_unit}   # {COPY_MIB} MiB read-only reduction / its FETCH_SIZE\n")
+            fo.write(f"write_bytes_per_unit = {write_unit}   # {COPY_MIB} MiB write-only fill / its WRITE_SIZE\n")
+        for k in kernels:
+            fo.write(f"\n[{k}]\n")
+            for c, (v, n) in sorted(means[k].items()):
+                fo.write(f"{c} = {v:.6g}   # {n} dispatches\n")
+            f = means[k].get("FETCH_SIZE")
+            w = means[k].get("WRITE_SIZE")
+            if f and fetch_unit:
+                fo.write(f"hbm_read_bytes_per_launch = {f[0] * fetch_unit:.0f}\n")
+            if w and write_unit:
+                fo.write(f"hbm_write_bytes_per_launch = {w[0] * write_unit:.0f}\n")
+    print(open(out).read())
+
+
 def summarize_trace(args):
     """Write profiles/<name>.kernel_stats.txt from a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -598,6 +748,11 @@ def main():
     ap.add_argument("--kernel-src", default="dsa_index.hip")
     ap.add_argument("--counters-name", default="dsa_index_scores_T131072")
     ap.add_argument("--counters-cmd", default="--steps 5 --warmup 1 --no-cpu --no-extra")
+    ap.add_argument("--pmc-dirs", help="summarize rocprofv3 --pmc passes (comma-separated directories) and exit")
+    ap.add_argument("--pmc-kernels", default="index_scores_mfma", help="'|'-separated kernel name substrings")
+    ap.add_argument("--pmc-groups", default="", help="the counter groups of the passes, ';'-separated (recorded)")
+    ap.add_argument("--calib-dir", help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes of --workload copy "
+                                        "(comma-separated directories)")
     ap.add_argument("--stats-csv", help="summarize a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--stats-name", default="dsa_decode_T131072_B1")
     ap.add_argument("--stats-cmd", default="")
@@ -607,6 +762,9 @@ def main():
         return
     if args.counters_dir:
         summarize_counters(args)
+        return
+    if args.pmc_dirs:
+        summarize_pmc(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",

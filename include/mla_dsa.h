@@ -110,6 +110,37 @@ mla_status mla_rope_interleave(void *x, mla_dtype dt, int64_t n_tok, int32_t n_h
                                void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Cache write of new tokens.  [MLA] sec. 2.1 (KV path: the kv_a output comp[kv_lora + qk_rope]
+ * splits into a kv_lora part, RMS-normalised (kv_a_ln) into the latent row Lc[pos], and a qk_rope
+ * part, rotated by the interleaved RoPE shared by all heads into Rc[pos]) and sec. 2.2 (indexer
+ * key: the ix_wk output, LayerNorm'd and rotated, into Ic[pos]).  For token j:
+ *   row      = the view's row of (sequence seq[j], position pos[j]); tokens whose row falls
+ *              outside the view (seq outside [0, n_seq), a block-table hole, a row outside the
+ *              pools) are skipped
+ *   Lc[row]  = comp[j][0:kv_lora] / sqrt(mean(comp[j][0:kv_lora]^2) + eps_kv) * kv_gain
+ *   Rc[row]  = RoPE(comp[j][kv_lora:], pos[j])          (exactly as mla_rope_interleave)
+ *   Ic[row]  = RoPE over dims [ix_rope_off, ix_rope_off + ix_rope_dim) at pos[j] of
+ *              (ik[j] - mean) / sqrt(var + eps_ix) * ix_gamma + ix_beta   (var: mean square
+ *              deviation; nothing rotates when ix_rope_dim = 0)
+ * in fp32 arithmetic, stored in kv->kv_dtype (Lc, Rc) and fp32 (Ic, either ic_layout).
+ *   comp     device [n_tok][kv_lora + qk_rope], in_dt;  ik: device [n_tok][kv->index_hd], in_dt,
+ *            or NULL (Ic not written)
+ *   seq, pos device int32 [n_tok]
+ *   kv_gain  device fp32 [kv_lora] or NULL (ones); ix_gamma / ix_beta device fp32 [index_hd] or
+ *            NULL (ones / zeros)
+ *   eps_kv, eps_ix  positive (the page gives 1e-6); theta as for mla_rope_interleave
+ *   kv       host struct: the pools written (lc, rc, and ic when ik is given); seq_len is not read
+ * Two tokens with the same row race (their order is unspecified).
+ * Supported: kv_lora <= 2048, qk_rope <= 512 (even), index_hd a multiple of 4 up to 256.
+ * --------------------------------------------------------------------------------- */
+mla_status mla_cache_write(const void *comp, const void *ik, mla_dtype in_dt, int64_t n_tok,
+                           const int32_t *seq, const int32_t *pos, int32_t n_seq, int32_t kv_lora,
+                           int32_t qk_rope, const float *kv_gain, const float *ix_gamma,
+                           const float *ix_beta, int32_t ix_rope_off, int32_t ix_rope_dim,
+                           double eps_kv, double eps_ix, double theta, const mla_kv_view *kv,
+                           void *stream);
+
+/* ---------------------------------------------------------------------------------
  * DSA lightning-indexer scores.  [MLA] sec. 2.2: per query and causal key t, a
  * ReLU-gated, per-head-weighted score; [FDSA] sec. 2: the key cache Ic is fp32.
  *   scores[b][t] = sum_h w_idx[b][h] * ReLU( sum_d q_idx[b][h][d] * Ic(b,t)[d] )
@@ -231,6 +262,22 @@ mla_status mla_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype q_dt
                           mla_dtype w_dt, const mla_dims *d, int32_t B, const mla_kv_view *kv,
                           int64_t t_max, int32_t k, float sm_scale, float *scores, int32_t *sel,
                           int32_t *nsel, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * The decode step of a DSA-shared layer.  [MLA] sec. 2.2: the indexer runs on the full layers
+ * only; the shared layers that follow reuse its selection (dsa_sel / dsa_nsel).  Equals
+ * mla_rope_interleave (on a copy of q_rope, at position seq_len[b] - 1) followed by
+ * mla_absorbed_decode over the keys sel[b][0 .. nsel[b]) of this layer's own cache, bit for bit.
+ *   sel, nsel  device int32 [B][k], [B]: INPUTS (e.g. the sel / nsel an earlier mla_dsa_decode of
+ *              the same step wrote); entries outside [0, seq_len[b]) are skipped
+ *   other arguments as for mla_dsa_decode (kv needs Lc, Rc and seq_len; Ic is not read)
+ *   ws         device workspace of at least mla_dsa_decode_shared_workspace_bytes(d, B, k) bytes
+ * --------------------------------------------------------------------------------- */
+size_t mla_dsa_decode_shared_workspace_bytes(const mla_dims *d, int32_t B, int32_t k);
+mla_status mla_dsa_decode_shared(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                 const void *kv_b, mla_dtype w_dt, const mla_dims *d, int32_t B,
+                                 const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel, int32_t k,
+                                 float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * mla_dsa_decode without a workspace argument, for callers that cannot allocate device memory

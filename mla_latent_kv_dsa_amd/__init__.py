@@ -28,10 +28,11 @@ MLA_FP32, MLA_BF16 = 0, 1
 MLA_IC_ROWS, MLA_IC_TILE64 = 0, 1
 
 EXPORTED = (
-    "mla_rope_interleave", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
+    "mla_rope_interleave", "mla_cache_write", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
     "dsa_index_select_workspace_bytes", "dsa_index_select",
     "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
     "mla_dsa_decode_workspace_bytes", "mla_dsa_decode", "mla_dsa_decode_noalloc",
+    "mla_dsa_decode_shared_workspace_bytes", "mla_dsa_decode_shared",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
     st = ctypes.c_int
     L.mla_rope_interleave.argtypes = [P, ctypes.c_int, i64, i32, i64, i64, i32, i32, P, ctypes.c_double, P]
     L.mla_rope_interleave.restype = st
+    L.mla_cache_write.argtypes = [P, P, ctypes.c_int, i64, P, P, i32, i32, i32, P, P, P, i32, i32, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_double, ctypes.POINTER(mla_kv_view), P]
+    L.mla_cache_write.restype = st
     L.dsa_index_scores.argtypes = [P, P, i32, i32, ctypes.POINTER(mla_kv_view), i64, P, P]
     L.dsa_index_scores.restype = st
     L.dsa_topk_workspace_bytes.argtypes = [i32, i64, i32]
@@ -104,6 +108,12 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(mla_dims), i32, ctypes.POINTER(mla_kv_view), i64, i32,
                                          ctypes.c_float, P, P, P, P, P]
     L.mla_dsa_decode_noalloc.restype = st
+    L.mla_dsa_decode_shared_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i32]
+    L.mla_dsa_decode_shared_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_dsa_decode_shared.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P, ctypes.c_int, ctypes.POINTER(mla_dims),
+                                        i32, ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P,
+                                        ctypes.c_size_t, P]
+    L.mla_dsa_decode_shared.restype = st
     L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i64]
     L.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.mla_prefill_nonabsorbed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims),
@@ -213,6 +223,32 @@ def mla_rope_interleave(x: torch.Tensor, pos: torch.Tensor, rope_off: int, rope_
     _check(lib().mla_rope_interleave(_ptr(x), _dt(x), x.shape[0], x.shape[1], x.stride(0), x.stride(1),
                                      rope_off, rope_dim, _ptr(pos), float(theta), _stream(x.device)))
     return x
+
+
+def mla_cache_write(comp: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor, kv: KvCache, n_seq: int,
+                    ik: Optional[torch.Tensor] = None, kv_gain: Optional[torch.Tensor] = None,
+                    ix_gamma: Optional[torch.Tensor] = None, ix_beta: Optional[torch.Tensor] = None,
+                    ix_rope_off: int = 0, ix_rope_dim: int = 0, eps_kv: float = 1e-6, eps_ix: float = 1e-6,
+                    theta: float = 10000.0) -> None:
+    """Write new tokens into the cache pools of kv: comp [n, kv_lora + qk_rope] (the kv_a output) and
+    optionally ik [n, index_hd] (the indexer key projection), same dtype; seq / pos int32 [n]."""
+    _dev(comp, seq, pos, ik, kv_gain, ix_gamma, ix_beta)
+    _contig(comp, seq, pos, ik, kv_gain, ix_gamma, ix_beta)
+    n = comp.shape[0]
+    L, rope = kv.lc.shape[1], kv.rc.shape[1]
+    if comp.dim() != 2 or comp.shape[1] != L + rope:
+        raise ValueError("comp must be [n, kv_lora + qk_rope]")
+    if seq.dtype != torch.int32 or pos.dtype != torch.int32 or seq.shape != (n,) or pos.shape != (n,):
+        raise ValueError("seq and pos must be int32 [n]")
+    if ik is not None and (ik.dtype != comp.dtype or kv.ic is None or ik.shape != (n, kv.ic.shape[1])):
+        raise ValueError("ik must be [n, index_hd] in comp's dtype, with an indexer pool in kv")
+    for g in (kv_gain, ix_gamma, ix_beta):
+        if g is not None and g.dtype != torch.float32:
+            raise TypeError("gains must be float32")
+    _check(lib().mla_cache_write(_ptr(comp), _ptr(ik), _dt(comp), n, _ptr(seq), _ptr(pos), n_seq, L, rope,
+                                 _ptr(kv_gain), _ptr(ix_gamma), _ptr(ix_beta), ix_rope_off, ix_rope_dim,
+                                 float(eps_kv), float(eps_ix), float(theta), ctypes.byref(kv.view),
+                                 _stream(comp.device)))
 
 
 def dsa_index_scores(q_idx: torch.Tensor, w_idx: torch.Tensor, kv: KvCache, t_max: int,
@@ -430,6 +466,37 @@ def mla_dsa_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, q_idx: torch.Tens
                                 float(sm_scale), _ptr(scores), _ptr(sel), _ptr(nsel), _ptr(out), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(dev)))
     return out, scores, sel, nsel
+
+
+def mla_dsa_decode_shared(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_b: torch.Tensor, kv: KvCache,
+                          sel: torch.Tensor, nsel: torch.Tensor, sm_scale: float, theta: float = 10000.0,
+                          out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The decode step of a DSA-shared layer: RoPE of q_rope [B, H, rope] (not modified) at seq_len - 1
+    and absorbed attention over the given selection sel [B, k] / nsel [B] (an earlier layer's).
+    Returns out [B, H, v] float32."""
+    _dev(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, kv_b, sel, nsel, out, ws)
+    B, H, nope = q_nope.shape
+    rope = q_rope.shape[2]
+    L = kv_b.shape[1]
+    if q_rope.shape[:2] != (B, H) or kv_b.shape[0] % H:
+        raise ValueError("shape mismatch between q_nope, q_rope and kv_b")
+    v = kv_b.shape[0] // H - nope
+    if sel.dtype != torch.int32 or nsel.dtype != torch.int32 or sel.dim() != 2 or sel.shape[0] != B \
+            or nsel.shape != (B,):
+        raise ValueError("sel must be int32 [B, k] and nsel int32 [B]")
+    k = sel.shape[1]
+    if out is None:
+        out = torch.empty((B, H, v), dtype=torch.float32, device=q_nope.device)
+    d = _dims(H, nope, rope, v, L)
+    if ws is None:
+        need = int(lib().mla_dsa_decode_shared_workspace_bytes(ctypes.byref(d), B, k))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_dsa_decode_shared(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), float(theta), _ptr(kv_b), _dt(kv_b),
+                                       ctypes.byref(d), B, ctypes.byref(kv.view), _ptr(sel), _ptr(nsel), k,
+                                       float(sm_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(q_nope.device)))
+    return out
 
 
 def mla_prefill_workspace_bytes(H: int, nope: int, rope: int, v: int, L: int, S: int, T: int) -> int:

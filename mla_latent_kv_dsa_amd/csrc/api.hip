@@ -393,6 +393,64 @@ mla_status mla_dsa_decode_noalloc(const void *q_nope, const void *q_rope, mla_dt
                           scores, sel, nsel, out, scratch, stream);
 }
 
+size_t mla_dsa_decode_shared_workspace_bytes(const mla_dims *d, int32_t B, int32_t k)
+{
+    if (!d || B <= 0 || k <= 0) return 0;
+    if (check_dims(d) != MLA_OK) return 0;
+    const size_t a = dsa_shared_workspace_bytes(*d, B, k, MLA_BF16), b = dsa_shared_workspace_bytes(*d, B, k, MLA_FP32);
+    return a > b ? a : b;
+}
+
+mla_status mla_dsa_decode_shared(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                                 const void *kv_b, mla_dtype w_dt, const mla_dims *d, int32_t B,
+                                 const mla_kv_view *kv, const int32_t *sel, const int32_t *nsel, int32_t k,
+                                 float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!sel || !nsel) return fail(MLA_ERR_ARG, "shared decode: sel and nsel are inputs and must be given");
+    if (k <= 0) return fail(MLA_ERR_ARG, "shared decode: k must be positive");
+    if (k > 65536) return fail(MLA_ERR_UNSUPPORTED, "shared decode: k > 65536");
+    mla_status st = check_decode_attend(d, B, q_dt, w_dt, kv, sel, nsel, k, sm_scale);
+    if (st) return st;
+    if (!(rope_theta > 0.0) || !isfinite(rope_theta))
+        return fail(MLA_ERR_ARG, "shared decode: rope_theta must be positive and finite");
+    if (B == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !kv_b || !out) return fail(MLA_ERR_ARG, "shared decode: NULL tensor");
+    st = check_ws("shared decode", dsa_shared_workspace_bytes(*d, B, k, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return launch_dsa_shared(q_nope, q_rope, q_dt, rope_theta, kv_b, *d, B, to_view(*kv), sel, nsel, k, sm_scale,
+                             out, ws, (hipStream_t)stream);
+}
+
+mla_status mla_cache_write(const void *comp, const void *ik, mla_dtype in_dt, int64_t n_tok, const int32_t *seq,
+                           const int32_t *pos, int32_t n_seq, int32_t kv_lora, int32_t qk_rope, const float *kv_gain,
+                           const float *ix_gamma, const float *ix_beta, int32_t ix_rope_off, int32_t ix_rope_dim,
+                           double eps_kv, double eps_ix, double theta, const mla_kv_view *kv, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_dtype(in_dt)) return fail(MLA_ERR_ARG, "cache write: dtype invalid");
+    if (n_tok < 0 || n_seq <= 0) return fail(MLA_ERR_ARG, "cache write: n_tok < 0 or n_seq <= 0");
+    if (kv_lora <= 0 || qk_rope <= 0 || (qk_rope & 1)) return fail(MLA_ERR_ARG, "cache write: kv_lora / qk_rope invalid");
+    if (kv_lora > 2048 || qk_rope > 512) return fail(MLA_ERR_UNSUPPORTED, "cache write: kv_lora > 2048 or qk_rope > 512");
+    if (!(eps_kv > 0.0) || !isfinite(eps_kv) || !(eps_ix > 0.0) || !isfinite(eps_ix))
+        return fail(MLA_ERR_ARG, "cache write: eps must be positive and finite");
+    if (!(theta > 0.0) || !isfinite(theta)) return fail(MLA_ERR_ARG, "cache write: theta must be positive and finite");
+    mla_status st = check_view(kv, n_seq, true, ik != nullptr, false);
+    if (st) return st;
+    if (ik) {
+        const int32_t hd = kv->index_hd;
+        if (hd <= 0 || hd % 4 != 0) return fail(MLA_ERR_ARG, "cache write: index_hd must be a positive multiple of 4");
+        if (hd > 256) return fail(MLA_ERR_UNSUPPORTED, "cache write: index_hd > 256");
+        if (ix_rope_off < 0 || ix_rope_dim < 0 || (ix_rope_dim & 1) || ix_rope_off + ix_rope_dim > hd)
+            return fail(MLA_ERR_ARG, "cache write: indexer rope slice outside the key");
+    }
+    if (n_tok == 0) return MLA_OK;
+    if (!comp || !seq || !pos) return fail(MLA_ERR_ARG, "cache write: NULL tensor");
+    return launch_cache_write(comp, ik, in_dt, n_tok, seq, pos, n_seq, to_view(*kv), kv->kv_dtype, kv_lora, qk_rope,
+                              ik ? kv->index_hd : 0, kv_gain, ix_gamma, ix_beta, ix_rope_off, ix_rope_dim,
+                              (float)eps_kv, (float)eps_ix, theta, (hipStream_t)stream);
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims *d, int32_t S, int64_t T)
 {
     if (!d || S <= 0 || T <= 0) return 0;

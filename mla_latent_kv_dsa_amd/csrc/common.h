@@ -265,10 +265,21 @@ mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype d
                              float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
                              hipStream_t s);
 
+mla_status launch_cache_write(const void *comp, const void *ik, mla_dtype in_dt, int64_t n, const int32_t *seq,
+                              const int32_t *pos, int32_t n_seq, const KvView &kv, mla_dtype kv_dt, int32_t L,
+                              int32_t rope, int32_t hd, const float *kv_gain, const float *gamma, const float *beta,
+                              int32_t ix_off, int32_t ix_rdim, float eps_kv, float eps_ix, double theta,
+                              hipStream_t s);
+
 // The library's static device scratch (noalloc.hip): its size, and its address on the calling
 // thread's current device (looked up once per device).
 constexpr size_t NOALLOC_SCRATCH_BYTES = MLA_NOALLOC_SCRATCH_BYTES;
 mla_status noalloc_scratch(void **ptr);
+
+size_t dsa_shared_workspace_bytes(const mla_dims &d, int32_t B, int32_t k, mla_dtype dt);
+mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const void *kv_b,
+                             const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel, const int32_t *nsel,
+                             int32_t k, float sm_scale, float *out, void *ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt);
 mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d,

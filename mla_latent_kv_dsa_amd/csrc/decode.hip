@@ -152,4 +152,26 @@ mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype d
     return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
 }
 
+// ------------------------------------------------------------------------------ shared layer
+// A DSA-shared layer reuses the selection of an earlier layer: RoPE of its query tails at
+// seq_len - 1 (out of place) and the absorbed decode over the given keys.
+// Workspace: decode part | rotated query tails.
+size_t dsa_shared_workspace_bytes(const mla_dims &d, int32_t B, int32_t k, mla_dtype dt)
+{
+    const size_t esz = dt == MLA_FP32 ? 4 : 2;
+    return 256 + al256(decode_workspace_bytes(d, B, k, dt)) + al256((size_t)B * d.n_heads * d.qk_rope * esz);
+}
+
+mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const void *kv_b,
+                             const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel, const int32_t *nsel,
+                             int32_t k, float sm_scale, float *out, void *ws, hipStream_t s)
+{
+    char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    void *dec_ws = p;
+    void *qr = p + al256(decode_workspace_bytes(d, B, k, dt));
+    mla_status st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv, theta, s);
+    if (st) return st;
+    return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
+}
+
 }  // namespace mla

@@ -324,3 +324,33 @@ def test_noalloc_decode_validation(L):
     assert need > (64 << 20)
     assert f(B=32, v=paged, t=131072) == mla.MLA_ERR_WORKSPACE
     assert "static scratch" in mla.mla_last_error()
+
+
+def test_cache_write_and_shared_decode_validation(L):
+    _no_gpu()
+    d = _dims()
+
+    def cw(n=4, dt=1, ik=FAKE, nseq=2, kvl=512, rope=64, off=64, rd=64, eps=1e-6, v=None):
+        return L.mla_cache_write(FAKE, ik, dt, n, FAKE, FAKE, nseq, kvl, rope, None, None, None, off, rd, eps, 1e-6,
+                                 1e4, ctypes.byref(v or _view(seq_len=None)), None)
+    assert cw(dt=3) == mla.MLA_ERR_ARG
+    assert cw(n=-1) == mla.MLA_ERR_ARG
+    assert cw(nseq=0) == mla.MLA_ERR_ARG
+    assert cw(rope=63) == mla.MLA_ERR_ARG
+    assert cw(kvl=4096) == mla.MLA_ERR_UNSUPPORTED
+    assert cw(eps=0.0) == mla.MLA_ERR_ARG
+    assert cw(off=100, rd=64) == mla.MLA_ERR_ARG            # slice past the 128-wide key
+    assert cw(rd=3) == mla.MLA_ERR_ARG
+    assert cw(v=_view(seq_len=None, ic=None)) == mla.MLA_ERR_ARG   # ik given, no indexer pool
+    assert cw(n=0) == mla.MLA_OK
+
+    def sh(sel=FAKE, nsel=FAKE, k=2048, ws=None, wsb=0, theta=1e4):
+        return L.mla_dsa_decode_shared(FAKE, FAKE, 1, theta, FAKE, 1, ctypes.byref(d), 1, ctypes.byref(_view()), sel,
+                                       nsel, k, 0.0625, FAKE, ws, wsb, None)
+    need = L.mla_dsa_decode_shared_workspace_bytes(ctypes.byref(d), 1, 2048)
+    assert need >= L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 2048)
+    assert sh(sel=None) == mla.MLA_ERR_ARG
+    assert sh(k=0) == mla.MLA_ERR_ARG
+    assert sh(theta=-1.0) == mla.MLA_ERR_ARG
+    assert sh() == mla.MLA_ERR_WORKSPACE
+    assert sh(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
