@@ -342,7 +342,7 @@ def test_cache_write_and_shared_decode_validation(L):
     assert cw(off=100, rd=64) == mla.MLA_ERR_ARG            # slice past the 128-wide key
     assert cw(rd=3) == mla.MLA_ERR_ARG
     assert cw(v=_view(seq_len=None, ic=None)) == mla.MLA_ERR_ARG   # ik given, no indexer pool
-    assert cw(n=0) == mla.MLA_OK
+    assert cw(n=0, nseq=1) == mla.MLA_OK
 
     def sh(sel=FAKE, nsel=FAKE, k=2048, ws=None, wsb=0, theta=1e4):
         return L.mla_dsa_decode_shared(FAKE, FAKE, 1, theta, FAKE, 1, ctypes.byref(d), 1, ctypes.byref(_view()), sel,
