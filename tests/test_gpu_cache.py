@@ -3,7 +3,7 @@
 Pages: chen3feng, "colibri-analysis 06: MLA attention and KV cache", sec. 2.1 (KV path: RMSNorm of the
 kv_a latent into Lc, RoPE of the shared key into Rc) and sec. 2.2 (indexer key: LayerNorm + RoPE into
 Ic; shared layers reuse the full layer's selection).  Bars: written rows against the oracle's float64
-rows within one bf16 ulp (bf16 pools) or 2e-6 / 2e-5 relative (fp32 Lc, Rc / Ic); rows the call does not
+rows within one bf16 ulp plus 2e-6 of the row scale (bf16 pools) or 2e-6 / 2e-5 relative (fp32 Lc, Rc / Ic); rows the call does not
 address stay bit-identical; the rotated key equals mla_rope_interleave bit for bit; attention outputs
 within 2e-3 (fp32) / 1e-2 (bf16) of the oracle.
 """
@@ -40,7 +40,9 @@ def _in_vals(a, bf16):
                                                    (True, False, True)])
 def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled):
     rng = np.random.default_rng(600 + 2 * in_bf16 + kv_bf16)
-    B, bs, max_blocks, L, rope, hd = 3, 16, 32, 512, 64, 128
+    B, L, rope, hd = 3, 512, 64, 128
+    bs = 64 if tiled else 16                        # a tiled indexer pool holds whole 64-row tiles per block
+    max_blocks = 512 // bs
     n_blocks = B * max_blocks
     rows = n_blocks * bs
     perm = rng.permutation(n_blocks).astype(np.int32)
@@ -79,8 +81,8 @@ def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled):
     assert np.all(g_lc[~written] == 7.0) and np.all(g_rc[~written] == 7.0) and np.all(g_ic[~written] == 7.0)
     for g, r in ((g_lc, r_lc), (g_rc, r_rc)):
         g, r = g[written], r[written]
-        if kv_bf16:
-            assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 1e-30)
+        if kv_bf16:   # one bf16 rounding of the fp32 result (whose own error is ~1e-7 of the inputs)
+            assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 2e-6 * np.abs(r).max())
         else:
             assert np.abs(g - r).max() <= 2e-6 * np.abs(r).max()
     assert np.abs(g_ic[written] - r_ic[written]).max() <= 2e-5 * np.abs(r_ic[written]).max()
