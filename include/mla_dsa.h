@@ -320,6 +320,49 @@ mla_status mla_prefill_nonabsorbed(const void *q, mla_dtype q_dt, const void *kv
                                    int32_t S, int32_t pos_base, float sm_scale, void *out,
                                    mla_dtype out_dt, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Attention of S queries of one sequence, on the path the g_absorb rule picks.  [MLA] sec. 2
+ * (attention over Tk = pos_base + S keys; query i at position pos_base + i sees keys 0 .. pos_base
+ * + i) and sec. 2.3 (g_absorb: -1 auto = absorbed when S <= 4, the decode and draft-verification
+ * case; 0 never; 1 always).  Both paths compute the same function (they differ in rounding only):
+ *   absorbed      q_abs = W_UK^T q_nope per query and head, scores against Lc / Rc, softmax,
+ *                 latent accumulation, W_UV (as mla_absorbed_decode, one query per position)
+ *   non-absorbed  one kv_b matmul rebuilds k_nope and v of keys 0 .. Tk-1, then causal softmax
+ *                 attention (as mla_prefill_nonabsorbed)
+ * With sel != NULL (DSA, [MLA] sec. 2.2) query i attends only the keys sel[i][0 .. nsel[i]) that
+ * are <= pos_base + i (entries outside that range are skipped; a query with none gives zeros).
+ *   q      device [S][H][qk_nope + qk_rope] (tail already rotated), q_dt
+ *   kv     host struct for sequence 0 (seq_len is not read; rows 0 .. pos_base + S - 1 used, every
+ *          one mapped to a pool row)
+ *   sel    device int32 [S][sel_stride] or NULL; nsel device int32 [S]
+ *   out    device fp32 [S][H][v_head]
+ *   ws     at least mla_attention_workspace_bytes(d, S, pos_base, sel ? sel_stride : 0, g_absorb)
+ * mla_attention_absorbs(S, g_absorb) returns 1 when the call takes the absorbed path.
+ * --------------------------------------------------------------------------------- */
+int32_t mla_attention_absorbs(int32_t S, int32_t g_absorb);
+size_t mla_attention_workspace_bytes(const mla_dims *d, int32_t S, int32_t pos_base, int32_t sel_stride,
+                                     int32_t g_absorb);
+mla_status mla_attention(const void *q, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt, const mla_dims *d,
+                         const mla_kv_view *kv, int32_t S, int32_t pos_base, const int32_t *sel,
+                         const int32_t *nsel, int32_t sel_stride, float sm_scale, int32_t g_absorb, float *out,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * DSA selection for S queries of one sequence (prefill).  [MLA] sec. 2.2: the indexer is active
+ * whenever the context exceeds the top-k, prefill included; every query keeps its own top-k
+ * causal keys.  Query i sits at position pos_base + i: row i of the result equals dsa_index_select
+ * for a sequence of pos_base + i + 1 keys with query q_idx[i], w_idx[i] -- the same scores
+ * (bit for bit, -INFINITY past the row's causal end), sel and nsel (= min(k, pos_base + i + 1)).
+ *   q_idx   device fp32 [S][n_ih][kv->index_hd];  w_idx device fp32 [S][n_ih]
+ *   kv      host struct for sequence 0 (Ic used; seq_len is not read)
+ *   scores  device fp32 [S][pos_base + S];  sel device int32 [S][k];  nsel device int32 [S]
+ *   ws      at least dsa_prefill_select_workspace_bytes(S, pos_base, k) bytes
+ * --------------------------------------------------------------------------------- */
+size_t dsa_prefill_select_workspace_bytes(int32_t S, int32_t pos_base, int32_t k);
+mla_status dsa_prefill_select(const float *q_idx, const float *w_idx, int32_t n_ih, const mla_kv_view *kv,
+                              int32_t S, int32_t pos_base, int32_t k, float *scores, int32_t *sel,
+                              int32_t *nsel, void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status, and the detail of the last failure on this thread. */
 const char *mla_status_string(mla_status s);
 const char *mla_last_error(void);

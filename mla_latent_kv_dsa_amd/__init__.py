@@ -33,6 +33,8 @@ EXPORTED = (
     "mla_decode_workspace_bytes", "mla_absorbed_decode", "mla_decode_absorb", "mla_decode_attend",
     "mla_dsa_decode_workspace_bytes", "mla_dsa_decode", "mla_dsa_decode_noalloc",
     "mla_dsa_decode_shared_workspace_bytes", "mla_dsa_decode_shared",
+    "mla_attention_absorbs", "mla_attention_workspace_bytes", "mla_attention",
+    "dsa_prefill_select_workspace_bytes", "dsa_prefill_select",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
@@ -120,6 +122,18 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(mla_kv_view), i32, i32, ctypes.c_float, P,
                                           ctypes.c_int, P, ctypes.c_size_t, P]
     L.mla_prefill_nonabsorbed.restype = st
+    L.mla_attention_absorbs.argtypes = [i32, i32]
+    L.mla_attention_absorbs.restype = i32
+    L.mla_attention_workspace_bytes.argtypes = [ctypes.POINTER(mla_dims), i32, i32, i32, i32]
+    L.mla_attention_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_attention.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(mla_dims), ctypes.POINTER(mla_kv_view),
+                                i32, i32, P, P, i32, ctypes.c_float, i32, P, P, ctypes.c_size_t, P]
+    L.mla_attention.restype = st
+    L.dsa_prefill_select_workspace_bytes.argtypes = [i32, i32, i32]
+    L.dsa_prefill_select_workspace_bytes.restype = ctypes.c_size_t
+    L.dsa_prefill_select.argtypes = [P, P, i32, ctypes.POINTER(mla_kv_view), i32, i32, i32, P, P, P, P,
+                                     ctypes.c_size_t, P]
+    L.dsa_prefill_select.restype = st
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
@@ -527,3 +541,67 @@ def mla_prefill_nonabsorbed(q: torch.Tensor, kv_b: torch.Tensor, kv: KvCache, qk
                                          _dt(out), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(q.device)))
     return out
+
+
+def mla_attention_absorbs(S: int, g_absorb: int = -1) -> bool:
+    """True when mla_attention takes the absorbed path for S queries under g_absorb."""
+    return bool(lib().mla_attention_absorbs(int(S), int(g_absorb)))
+
+
+def mla_attention(q: torch.Tensor, kv_b: torch.Tensor, kv: KvCache, qk_nope: int, pos_base: int, sm_scale: float,
+                  g_absorb: int = -1, sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S queries q [S, H, nope+rope] (rotated tail) of one sequence at positions pos_base .. pos_base+S-1,
+    on the path g_absorb picks (-1: absorbed when S <= 4; 0: never; 1: always), optionally restricted to
+    per-query selections sel [S, k] / nsel [S].  Returns out [S, H, v] float32."""
+    _dev(q, kv_b, sel, nsel, out, ws)
+    _contig(q, kv_b, sel, nsel, out, ws)
+    S, H, qh = q.shape
+    rope = qh - qk_nope
+    L = kv_b.shape[1]
+    if kv_b.shape[0] % H:
+        raise ValueError("kv_b rows must be a multiple of the head count")
+    v = kv_b.shape[0] // H - qk_nope
+    sel_stride = 0
+    if sel is not None:
+        if sel.dtype != torch.int32 or sel.dim() != 2 or sel.shape[0] != S or nsel is None \
+                or nsel.dtype != torch.int32 or nsel.shape != (S,):
+            raise ValueError("sel must be int32 [S, k] with nsel int32 [S]")
+        sel_stride = sel.shape[1]
+    d = _dims(H, qk_nope, rope, v, L)
+    if out is None:
+        out = torch.empty((S, H, v), dtype=torch.float32, device=q.device)
+    if ws is None:
+        need = int(lib().mla_attention_workspace_bytes(ctypes.byref(d), S, pos_base, sel_stride, g_absorb))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mla_attention(_ptr(q), _dt(q), _ptr(kv_b), _dt(kv_b), ctypes.byref(d), ctypes.byref(kv.view), S,
+                               pos_base, _ptr(sel), _ptr(nsel), sel_stride, float(sm_scale), int(g_absorb), _ptr(out),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
+    return out
+
+
+def dsa_prefill_select(q_idx: torch.Tensor, w_idx: torch.Tensor, kv: KvCache, pos_base: int, k: int,
+                       scores: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                       nsel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Per-query DSA selection of S prefill queries (query i at pos_base + i): q_idx [S, n_ih, hd],
+    w_idx [S, n_ih] float32.  Returns (scores [S, pos_base+S], sel [S, k], nsel [S])."""
+    _dev(q_idx, w_idx, scores, sel, nsel, ws)
+    _contig(q_idx, w_idx, scores, sel, nsel, ws)
+    S, n_ih, hd = q_idx.shape
+    if w_idx.shape != (S, n_ih) or q_idx.dtype != torch.float32 or w_idx.dtype != torch.float32:
+        raise ValueError("q_idx [S, n_ih, hd] and w_idx [S, n_ih] must be float32")
+    if kv.ic is None or kv.ic.shape[1] != hd:
+        raise ValueError("kv.ic width must equal q_idx's last dim")
+    T = pos_base + S
+    dev = q_idx.device
+    scores = torch.empty((S, T), dtype=torch.float32, device=dev) if scores is None else scores
+    sel = torch.empty((S, k), dtype=torch.int32, device=dev) if sel is None else sel
+    nsel = torch.empty((S,), dtype=torch.int32, device=dev) if nsel is None else nsel
+    if scores.shape != (S, T) or sel.shape != (S, k) or nsel.shape != (S,):
+        raise ValueError("scores [S, pos_base+S], sel [S, k], nsel [S]")
+    if ws is None:
+        ws = torch.empty(max(int(lib().dsa_prefill_select_workspace_bytes(S, pos_base, k)), 1), dtype=torch.uint8,
+                         device=dev)
+    _check(lib().dsa_prefill_select(_ptr(q_idx), _ptr(w_idx), n_ih, ctypes.byref(kv.view), S, pos_base, k, _ptr(scores),
+                                    _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return scores, sel, nsel

@@ -393,6 +393,90 @@ mla_status mla_dsa_decode_noalloc(const void *q_nope, const void *q_rope, mla_dt
                           scores, sel, nsel, out, scratch, stream);
 }
 
+int32_t mla_attention_absorbs(int32_t S, int32_t g_absorb) { return attention_absorbs(S, g_absorb) ? 1 : 0; }
+
+size_t mla_attention_workspace_bytes(const mla_dims *d, int32_t S, int32_t pos_base, int32_t sel_stride,
+                                     int32_t g_absorb)
+{
+    if (!d || S <= 0 || pos_base < 0 || sel_stride < 0) return 0;
+    if (check_dims(d) != MLA_OK) return 0;
+    const bool ab = attention_absorbs(S, g_absorb);
+    const int64_t T = (int64_t)pos_base + S;
+    const size_t a = attention_workspace_bytes(*d, S, T, sel_stride, ab, MLA_BF16);
+    const size_t b = attention_workspace_bytes(*d, S, T, sel_stride, ab, MLA_FP32);
+    return a > b ? a : b;
+}
+
+mla_status mla_attention(const void *q, mla_dtype q_dt, const void *kv_b, mla_dtype w_dt, const mla_dims *d,
+                         const mla_kv_view *kv, int32_t S, int32_t pos_base, const int32_t *sel, const int32_t *nsel,
+                         int32_t sel_stride, float sm_scale, int32_t g_absorb, float *out, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_dims(d);
+    if (st) return st;
+    if (S < 0 || pos_base < 0) return fail(MLA_ERR_ARG, "attention: S or pos_base negative");
+    if (S > 65535) return fail(MLA_ERR_UNSUPPORTED, "attention: S > 65535");
+    if (g_absorb < -1 || g_absorb > 1) return fail(MLA_ERR_ARG, "attention: g_absorb must be -1, 0 or 1");
+    if (!valid_dtype(q_dt) || !valid_dtype(w_dt)) return fail(MLA_ERR_ARG, "attention: dtype invalid");
+    if (!kv) return fail(MLA_ERR_ARG, "attention: kv view is NULL");
+    const int64_t T = (int64_t)pos_base + S;
+    if (T >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "attention: pos_base + S >= 2^31");
+    mla_kv_view v1 = *kv;
+    if (v1.max_seq_len < T) v1.max_seq_len = T;   // sequence 0 spans rows for t < T
+    st = check_view(&v1, 1, true, false, false);
+    if (st) return st;
+    if (q_dt != w_dt || q_dt != kv->kv_dtype) return fail(MLA_ERR_UNSUPPORTED, "attention: q, kv_b and cache dtypes must match");
+    if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "attention: sm_scale not finite");
+    if (sel && (!nsel || sel_stride <= 0)) return fail(MLA_ERR_ARG, "attention: sel needs nsel and sel_stride > 0");
+    if (S == 0) return MLA_OK;
+    if (!q || !kv_b || !out) return fail(MLA_ERR_ARG, "attention: NULL tensor");
+    const bool ab = attention_absorbs(S, g_absorb);
+    st = check_ws("attention", attention_workspace_bytes(*d, S, T, sel ? sel_stride : 0, ab, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return launch_attention(q, q_dt, kv_b, *d, to_view(v1), S, pos_base, sel, nsel, sel ? sel_stride : 0, sm_scale, ab,
+                            out, ws, (hipStream_t)stream);
+}
+
+size_t dsa_prefill_select_workspace_bytes(int32_t S, int32_t pos_base, int32_t k)
+{
+    if (S <= 0 || pos_base < 0 || k <= 0) return 0;
+    return index_select_workspace_bytes(S, (int64_t)pos_base + S, k);
+}
+
+mla_status dsa_prefill_select(const float *q_idx, const float *w_idx, int32_t n_ih, const mla_kv_view *kv, int32_t S,
+                              int32_t pos_base, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (S < 0 || pos_base < 0) return fail(MLA_ERR_ARG, "prefill select: S or pos_base negative");
+    if (S > 65535) return fail(MLA_ERR_UNSUPPORTED, "prefill select: S > 65535");
+    if (n_ih <= 0) return fail(MLA_ERR_ARG, "prefill select: n_ih must be positive");
+    if (n_ih > 64) return fail(MLA_ERR_UNSUPPORTED, "prefill select: n_ih > 64");
+    if (k <= 0) return fail(MLA_ERR_ARG, "prefill select: k must be positive");
+    if (k > 65536) return fail(MLA_ERR_UNSUPPORTED, "prefill select: k > 65536");
+    if (!kv) return fail(MLA_ERR_ARG, "prefill select: kv view is NULL");
+    const int64_t T = (int64_t)pos_base + S;
+    if (T >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "prefill select: pos_base + S >= 2^31");
+    mla_kv_view v1 = *kv;
+    if (v1.max_seq_len < T) v1.max_seq_len = T;
+    mla_status st = check_view(&v1, 1, false, true, false);
+    if (st) return st;
+    if (kv->index_hd <= 0 || kv->index_hd % 4 != 0)
+        return fail(MLA_ERR_ARG, "prefill select: index_hd must be a positive multiple of 4");
+    if (kv->index_hd > 256) return fail(MLA_ERR_UNSUPPORTED, "prefill select: index_hd > 256");
+    if (S == 0) return MLA_OK;
+    if (!q_idx || !w_idx || !scores || !sel || !nsel) return fail(MLA_ERR_ARG, "prefill select: NULL tensor");
+    st = check_ws("prefill select", index_select_workspace_bytes(S, T, k), ws, ws_bytes);
+    if (st) return st;
+    KvView v = to_view(v1);
+    v.seq_len = nullptr;
+    v.max_seq_len = T;
+    v.qps = S;   // launch row i = query i at position pos_base + i
+    return launch_index_select(q_idx, w_idx, S, n_ih, kv->index_hd, v, T, k, scores, sel, nsel, ws, ws_bytes,
+                               (hipStream_t)stream);
+}
+
 size_t mla_dsa_decode_shared_workspace_bytes(const mla_dims *d, int32_t B, int32_t k)
 {
     if (!d || B <= 0 || k <= 0) return 0;

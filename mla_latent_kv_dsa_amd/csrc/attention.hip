@@ -1,0 +1,113 @@
+// attention.hip -- attention of S queries of one sequence at positions pos_base .. pos_base + S - 1
+// (colibri-analysis 06 "MLA attention and KV cache", sec. 2: Tk = pos_base + S), on either path of
+// sec. 2.3 as the g_absorb rule picks it: -1 absorbs when S <= 4 (decode, draft verification), 0
+// never, 1 always.  Query i sees keys 0 .. pos_base + i, optionally restricted to its own
+// selection (sec. 2.2, the DSA top-k of that query).
+//   absorbed      the decode kernels over S launch rows of the same sequence (KvView.qps = S):
+//                 q split into its nope and rope parts, W_UK folded into every query, scores against
+//                 Lc / Rc, softmax, latent accumulation, W_UV
+//   non-absorbed  the prefill kernels (kv_b GEMM rebuilding k_nope and v, causal attention); a
+//                 selection becomes a per-query key bitmap that the attention applies tile by tile
+#include "common.h"
+
+namespace mla {
+
+bool attention_absorbs(int32_t S, int32_t g_absorb) { return g_absorb > 0 || (g_absorb < 0 && S <= 4); }
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// mask geometry for T keys and S queries: words per query column (two per 64-key tile), and the
+// padded column count (query blocks of 128 read whole blocks)
+static int64_t mask_groups(int64_t T) { return 2 * ((T + 63) / 64); }
+static int64_t mask_cols(int32_t S) { return ((int64_t)S + 127) / 128 * 128; }
+
+size_t attention_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, int32_t sel_stride, bool absorbed,
+                                 mla_dtype dt)
+{
+    const size_t esz = dt == MLA_FP32 ? 4 : 2;
+    if (absorbed) {
+        const int64_t max_keys = sel_stride > 0 ? sel_stride : T;
+        return 256 + al256((size_t)S * d.n_heads * (d.qk_nope + d.qk_rope) * esz) +
+               al256(decode_workspace_bytes(d, S, max_keys, dt));
+    }
+    size_t m = sel_stride > 0 ? al256((size_t)mask_groups(T) * mask_cols(S) * 4) : 0;
+    return 256 + m + al256(prefill_workspace_bytes(d, S, T, dt));
+}
+
+// q [S][H][nope + rope] -> qn [S][H][nope], qr [S][H][rope] (element copies)
+template <typename E>
+__global__ __launch_bounds__(256) void split_q_kernel(const E *__restrict__ q, E *__restrict__ qn, E *__restrict__ qr,
+                                                      int64_t units, int nope, int rope)
+{
+    const int qh = nope + rope;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= units * qh) return;
+    const int64_t u = e / qh;
+    const int c = (int)(e - u * qh);
+    if (c < nope) qn[u * nope + c] = q[e];
+    else qr[u * rope + (c - nope)] = q[e];
+}
+
+// Key bitmap of the selections: column i (query i), word g holds keys 32 g .. 32 g + 31.  One
+// workgroup per column clears it, then sets the bits of the query's kept positions in [0, T).
+__global__ __launch_bounds__(256) void sel_mask_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ nsel,
+                                                       int sel_stride, int S, int64_t T, int64_t groups, int64_t cols,
+                                                       uint32_t *__restrict__ mask)
+{
+    const int i = blockIdx.x, tid = threadIdx.x;
+    for (int64_t g = tid; g < groups; g += 256) mask[g * cols + i] = 0u;
+    __syncthreads();
+    if (i >= S) return;
+    int n = nsel[i];
+    n = n < 0 ? 0 : (n > sel_stride ? sel_stride : n);
+    for (int j = tid; j < n; j += 256) {
+        const int32_t t = sel[(int64_t)i * sel_stride + j];
+        if (t >= 0 && t < T) atomicOr(&mask[(int64_t)(t >> 5) * cols + i], 1u << (t & 31));
+    }
+}
+
+mla_status launch_attention(const void *q, mla_dtype dt, const void *kv_b, const mla_dims &d, const KvView &kv0,
+                            int32_t S, int32_t pos_base, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                            float sm_scale, bool absorbed, float *out, void *ws, hipStream_t s)
+{
+    const int64_t T = (int64_t)pos_base + S;
+    char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    KvView kv = kv0;
+    kv.seq_len = nullptr;    // one sequence of T tokens
+    kv.max_seq_len = T;
+    if (absorbed) {
+        kv.qps = S;          // launch row i = query i, keys 0 .. pos_base + i
+        const size_t esz = dt == MLA_FP32 ? 4 : 2;
+        const int64_t units = (int64_t)S * d.n_heads;
+        char *qn = p;
+        char *qr = p + (size_t)units * d.qk_nope * esz;
+        void *dec_ws = p + al256((size_t)units * (d.qk_nope + d.qk_rope) * esz);
+        const int64_t n = units * (d.qk_nope + d.qk_rope);
+        const int64_t blocks = (n + 255) / 256;
+        if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "attention: too many queries");
+        if (esz == 4)
+            hipLaunchKernelGGL(split_q_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t *)q,
+                               (uint32_t *)qn, (uint32_t *)qr, units, d.qk_nope, d.qk_rope);
+        else
+            hipLaunchKernelGGL(split_q_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
+                               (uint16_t *)qn, (uint16_t *)qr, units, d.qk_nope, d.qk_rope);
+        mla_status st = check_launch("split_q_kernel");
+        if (st) return st;
+        const int64_t max_keys = sel ? (int64_t)sel_stride : T;
+        return launch_decode(qn, qr, kv_b, dt, d, S, kv, sel, nsel, sel ? sel_stride : 0, max_keys, sm_scale, out,
+                             dec_ws, 0, s);
+    }
+    uint32_t *mask = nullptr;
+    const int64_t cols = mask_cols(S);
+    if (sel) {
+        mask = reinterpret_cast<uint32_t *>(p);
+        p += al256((size_t)mask_groups(T) * cols * 4);
+        hipLaunchKernelGGL(sel_mask_kernel, dim3((unsigned)cols), dim3(256), 0, s, sel, nsel, sel_stride, S, T,
+                           mask_groups(T), cols, mask);
+        mla_status st = check_launch("sel_mask_kernel");
+        if (st) return st;
+    }
+    return launch_prefill(q, kv_b, dt, d, kv, S, pos_base, sm_scale, out, MLA_FP32, p, 0, s, mask, (int)cols);
+}
+
+}  // namespace mla

@@ -49,6 +49,10 @@ struct KvView {
     const int32_t *seq_len;
     int64_t max_seq_len;
     int32_t ic_tiled;   // indexer pool in 64-row tiles (MLA_IC_TILE64)
+    // queries per sequence: row b of a launch is query b % qps of sequence b / qps, at position
+    // len - qps + b % qps where len is that sequence's length (seq_len or max_seq_len); it sees
+    // keys 0 .. that position.  1 for one query per sequence at len - 1.
+    int32_t qps;
 };
 
 inline KvView to_view(const mla_kv_view &v)
@@ -65,8 +69,12 @@ inline KvView to_view(const mla_kv_view &v)
     k.seq_len = v.seq_len;
     k.max_seq_len = v.max_seq_len;
     k.ic_tiled = v.ic_layout == MLA_IC_TILE64;
+    k.qps = 1;
     return k;
 }
+
+// The sequence that launch row b belongs to.
+__device__ __forceinline__ int kv_seq(const KvView &v, int b) { return v.qps > 1 ? b / v.qps : b; }
 
 // Dims 4g .. 4g+3 of indexer row `row` (hd dims per row), in either pool layout.
 __device__ __forceinline__ const float *ic_quad(const KvView &v, int64_t row, int g, int hd)
@@ -74,10 +82,11 @@ __device__ __forceinline__ const float *ic_quad(const KvView &v, int64_t row, in
     return v.ic_tiled ? v.ic + ((row >> 6) * (hd >> 2) + g) * 256 + (row & 63) * 4 : v.ic + row * hd + 4 * g;
 }
 
-// Pool row of logical token t of sequence b, or -1 if it falls outside the pools.
+// Pool row of logical token t of launch row b, or -1 if it falls outside the pools.
 // t must satisfy 0 <= t < max_seq_len (callers clamp), so the table index is in range.
 __device__ __forceinline__ int64_t kv_row(const KvView &v, int b, int64_t t)
 {
+    b = kv_seq(v, b);
     int64_t r;
     if (v.bt) {
         int32_t blk = v.bt[(int64_t)b * v.max_blocks + t / v.bs];
@@ -88,10 +97,13 @@ __device__ __forceinline__ int64_t kv_row(const KvView &v, int b, int64_t t)
     return (r >= 0 && r < v.rows) ? r : -1;
 }
 
-// seq_len[b] clamped to [0, max_seq_len].
+// Keys launch row b sees (its query's position + 1), clamped to [0, max_seq_len]: seq_len[b] for one
+// query per sequence.
 __device__ __forceinline__ int64_t seq_len_of(const KvView &v, int b)
 {
-    int64_t s = v.seq_len ? (int64_t)v.seq_len[b] : v.max_seq_len;
+    const int sb = kv_seq(v, b);
+    int64_t s = v.seq_len ? (int64_t)v.seq_len[sb] : v.max_seq_len;
+    if (v.qps > 1) s -= v.qps - 1 - (b - sb * v.qps);
     if (s < 0) s = 0;
     if (s > v.max_seq_len) s = v.max_seq_len;
     return s;
@@ -282,8 +294,19 @@ mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype d
                              int32_t k, float sm_scale, float *out, void *ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, mla_dtype dt);
+// mask (optional): keys further restricted per query, bit t % 32 of mask[(t / 32) * mask_stride + i];
+// mask_stride >= S rounded up to 128, 2 * ceil((pos_base + S) / 64) words per query column
 mla_status launch_prefill(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d,
                           const KvView &kv, int32_t S, int32_t pos_base, float sm_scale,
-                          void *out, mla_dtype out_dt, void *ws, size_t ws_bytes, hipStream_t s);
+                          void *out, mla_dtype out_dt, void *ws, size_t ws_bytes, hipStream_t s,
+                          const uint32_t *mask = nullptr, int mask_stride = 0);
+
+// S queries of one sequence ([MLA] sec. 2.3 g_absorb rule) and their selections
+bool attention_absorbs(int32_t S, int32_t g_absorb);
+size_t attention_workspace_bytes(const mla_dims &d, int32_t S, int64_t T, int32_t sel_stride, bool absorbed,
+                                 mla_dtype dt);
+mla_status launch_attention(const void *q, mla_dtype dt, const void *kv_b, const mla_dims &d, const KvView &kv,
+                            int32_t S, int32_t pos_base, const int32_t *sel, const int32_t *nsel, int32_t sel_stride,
+                            float sm_scale, bool absorbed, float *out, void *ws, hipStream_t s);
 
 }  // namespace mla

@@ -135,10 +135,10 @@ __device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int6
     const int64_t t = tile * 64 + lane;
     int64_t row;
     if (MODE == 0) {
-        row = (int64_t)b * kv.seq_stride + t;
+        row = (int64_t)kv_seq(kv, b) * kv.seq_stride + t;
     } else if (MODE == 1) {
         const int64_t t0 = tile * 64;
-        const int64_t blk = kv.bt[(int64_t)b * kv.max_blocks + t0 / kv.bs];
+        const int64_t blk = kv.bt[(int64_t)kv_seq(kv, b) * kv.max_blocks + t0 / kv.bs];
         row = blk < 0 ? -1 : blk * kv.bs + t0 % kv.bs + lane;
     } else {
         row = t < n ? kv_row(kv, b, t) : -1;

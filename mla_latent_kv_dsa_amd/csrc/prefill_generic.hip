@@ -64,10 +64,12 @@ __global__ __launch_bounds__(256) void kvb_gemm_generic(KvView kv, const T *__re
 
 constexpr int kPChunk = 256;
 
+// mask (optional): query i attends key t only if bit t % 32 of mask[(t / 32) * mask_stride + i] is set
 template <typename T, typename O>
 __global__ __launch_bounds__(256) void attn_generic(const T *__restrict__ q, const float *__restrict__ kvw, KvView kv,
                                                     int H, int nope, int rope, int v, int pos_base,
-                                                    float sm_scale, O *__restrict__ out)
+                                                    float sm_scale, O *__restrict__ out,
+                                                    const uint32_t *__restrict__ mask, int mask_stride)
 {
     extern __shared__ int64_t sh_rows[];
     int64_t *srow = sh_rows;                                   // [kPChunk] pool rows
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(256) void attn_generic(const T *__restrict__ q, con
             if (row >= 0)
                 for (int c = lane; c < rope; c += 64) p = fmaf(sq[nope + c], ld(rc + row * rope + c), p);
             p = wave_sum(p);
-            if (lane == 0) ss[e] = p * sm_scale;
+            const bool keep = !mask || ((mask[(t >> 5) * (int64_t)mask_stride + i] >> (t & 31)) & 1u);
+            if (lane == 0) ss[e] = keep ? p * sm_scale : -INFINITY;
         }
         __syncthreads();
         float x = tid < cnt ? ss[tid] : -INFINITY;
@@ -105,11 +108,12 @@ __global__ __launch_bounds__(256) void attn_generic(const T *__restrict__ q, con
         if (lane == 0) red[wave] = x;
         __syncthreads();
         const float nm = fmaxf(m, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-        const float scale = __expf(m - nm);
+        const float ns = nm == -INFINITY ? 0.f : nm;   // no attended key yet (a key mask): P = 0
+        const float scale = __expf(m - ns);
         __syncthreads();
         float pv = 0.f;
         if (tid < cnt) {
-            pv = __expf(ss[tid] - nm);
+            pv = __expf(ss[tid] - ns);
             ss[tid] = pv;
         }
         pv = wave_sum(pv);
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void attn_generic(const T *__restrict__ q, con
             }
         }
     }
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int j = tid + 256 * r;
@@ -144,7 +148,7 @@ size_t prefill_generic_ws(const mla_dims &d, int32_t, int64_t T)
 template <typename T>
 static mla_status run_prefill_generic(const void *q, const void *kv_b, const mla_dims &d, const KvView &kv, int32_t S,
                                       int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws,
-                                      hipStream_t s)
+                                      hipStream_t s, const uint32_t *mask, int mask_stride)
 {
     const int H = d.n_heads, nope = d.qk_nope, rope = d.qk_rope, v = d.v_head, L = d.kv_lora;
     const int64_t Tn = (int64_t)pos_base + S;
@@ -160,20 +164,20 @@ static mla_status run_prefill_generic(const void *q, const void *kv_b, const mla
     if (H > 65535) return fail(MLA_ERR_UNSUPPORTED, "prefill: too many heads");
     if (out_dt == MLA_FP32)
         hipLaunchKernelGGL((attn_generic<T, float>), dim3(S, H), dim3(256), shm, s, (const T *)q, kvw, kv, H, nope, rope,
-                           v, pos_base, sm_scale, (float *)out);
+                           v, pos_base, sm_scale, (float *)out, mask, mask_stride);
     else
         hipLaunchKernelGGL((attn_generic<T, bf16_t>), dim3(S, H), dim3(256), shm, s, (const T *)q, kvw, kv, H, nope,
-                           rope, v, pos_base, sm_scale, (bf16_t *)out);
+                           rope, v, pos_base, sm_scale, (bf16_t *)out, mask, mask_stride);
     return check_launch("attn_generic");
 }
 
 mla_status launch_prefill_generic(const void *q, const void *kv_b, mla_dtype dt, const mla_dims &d, const KvView &kv,
                                   int32_t S, int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws,
-                                  hipStream_t s)
+                                  hipStream_t s, const uint32_t *mask, int mask_stride)
 {
     if (dt == MLA_FP32)
-        return run_prefill_generic<float>(q, kv_b, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s);
-    return run_prefill_generic<bf16_t>(q, kv_b, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s);
+        return run_prefill_generic<float>(q, kv_b, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s, mask, mask_stride);
+    return run_prefill_generic<bf16_t>(q, kv_b, d, kv, S, pos_base, sm_scale, out, out_dt, ws, s, mask, mask_stride);
 }
 
 }  // namespace mla

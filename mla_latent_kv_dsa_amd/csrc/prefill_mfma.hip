@@ -170,6 +170,9 @@ constexpr int PA_BQ = 128, PA_BK = 64;
 constexpr int PA_KROW = 256;                              // bf16 per staged K or V row
 constexpr int PA_TILE = 2 * PA_BK * PA_KROW;              // bf16 per staged tile
 constexpr size_t PA_LDS = (size_t)2 * PA_TILE * 2;        // two tiles
+// With a key mask (a selection per query): per staged tile, the mask words of its two 32-key
+// groups for the block's 128 queries ([group][query], 1 KB), double-buffered behind the tiles.
+constexpr size_t PA_MASK_LDS = 2 * 2 * PA_BQ * 4;
 constexpr int PA_PF = 6;       // score operand reads in flight
 
 
@@ -180,9 +183,13 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 // MODE 0: Rc rows contiguous (row = position); 1: block table with block_size % 64 == 0 (a tile's
 // keys in one block, looked up once per tile with a scalar load); 2: any block table (one lookup
 // per key, a vector load whose wait also lands the copies in flight).
-template <int NOPE, typename OUT, int MODE>
+// MASK: keys are further restricted per query by a bitmap (bit t % 32 of word
+// mask[(t / 32) * mask_stride + i] set = key t attended by query i); wave 0 copies a tile's words into
+// LDS with its K rows, so the same waits cover them.
+template <int NOPE, typename OUT, int MODE, bool MASK>
 __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C, KvView kv,
-                                               int S, int pos_base, float scale_log2, OUT *__restrict__ out)
+                                               int S, int pos_base, float scale_log2, OUT *__restrict__ out,
+                                               const uint32_t *__restrict__ mask, int mask_stride)
 {
     extern __shared__ __attribute__((aligned(16))) char pa_smem[];
     bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 tiles][K rows, V rows][64][PA_KROW]
@@ -252,6 +259,10 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         bf16_t *dst = sT + (kt & 1) * PA_TILE;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
+            if (MASK && u == 8 && wave == 0) {   // the tile's mask words, after wave 0's K copies
+                const uint32_t *src = mask + (int64_t)(2 * kt + (lane >> 5)) * mask_stride + i0 + 4 * (lane & 31);
+                pf_dma16(src, pf_lds_addr(reinterpret_cast<const char *>(pa_smem) + PA_LDS + (kt & 1) * 1024));
+            }
             const int i = u & 7;
             const bool isv = u >= 8;
             const int r0 = 16 * wave + 2 * i, key = r0 + kh;   // this lane's key of the pair
@@ -326,6 +337,16 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
 #pragma unroll
             for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
+        if (MASK) {   // keys outside the query's selection
+            const uint32_t *mw = reinterpret_cast<const uint32_t *>(pa_smem + PA_LDS + (kt & 1) * 1024);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint32_t w = mw[PA_BQ * mt + 32 * wave + l32];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (!((w >> (8 * (r >> 2) + 4 * hi + (r & 3))) & 1u)) s[mt][r] = -INFINITY;
+            }
+        }
         // causal mask, only on tiles that reach past the wave's first query (positions < 2^31);
         // running maximum of the raw scores (lanes l and l ^ 32 hold the same query)
         const int qpos32 = (int)qpos;
@@ -356,6 +377,8 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         const bool move = mx > m_run + 8.f;
         const float m_new = move ? mx : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        // with a mask the reference stays -inf until the query's first attended key; its P are 0
+        const float m_sub = MASK && m_new == -INFINITY ? 0.f : m_new;
         // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt;
         // the sum is taken over the rounded values (two-element bf16 dot products with ones)
         uint2 pk[2][4];
@@ -368,7 +391,7 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
             for (int g = 0; g < 4; ++g) {
                 float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][4 * g + e], scale_log2, -m_new));
+                for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][4 * g + e], scale_log2, -m_sub));
                 pk[mt][g].x = pf_pack(p[0], p[1]);
                 pk[mt][g].y = pf_pack(p[2], p[3]);
                 psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].x), one2, psum, false);
@@ -451,34 +474,46 @@ size_t prefill_mfma_ws(const mla_dims &d, int64_t T)
     return 256 + (size_t)T * d.n_heads * (d.qk_nope + d.v_head) * 2;
 }
 
-template <int NOPE, typename OUT, int MODE>
+template <int NOPE, typename OUT, int MODE, bool MASK>
 static mla_status launch_attn_mode(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
-                                   float scale_log2, void *out, hipStream_t s)
+                                   float scale_log2, void *out, const uint32_t *mask, int mask_stride, hipStream_t s)
 {
+    constexpr size_t lds = PA_LDS + (MASK ? PA_MASK_LDS : 0);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT, MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)PA_LDS);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT, MODE, MASK>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         attr = true;
     }
     const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ * PF_H));
-    hipLaunchKernelGGL((pf_attn<NOPE, OUT, MODE>), g, dim3(256), PA_LDS, s, (const bf16_t *)q, C, kv, S, pos_base,
-                       scale_log2, (OUT *)out);
+    hipLaunchKernelGGL((pf_attn<NOPE, OUT, MODE, MASK>), g, dim3(256), lds, s, (const bf16_t *)q, C, kv, S, pos_base,
+                       scale_log2, (OUT *)out, mask, mask_stride);
     return check_launch("pf_attn");
 }
 
-template <int NOPE, typename OUT>
+template <int NOPE, typename OUT, bool MASK>
 static mla_status launch_attn(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
-                              float scale_log2, void *out, hipStream_t s)
+                              float scale_log2, void *out, const uint32_t *mask, int mask_stride, hipStream_t s)
 {
-    if (!kv.bt) return launch_attn_mode<NOPE, OUT, 0>(q, C, kv, S, pos_base, scale_log2, out, s);
-    if (kv.bs % PA_BK == 0) return launch_attn_mode<NOPE, OUT, 1>(q, C, kv, S, pos_base, scale_log2, out, s);
-    return launch_attn_mode<NOPE, OUT, 2>(q, C, kv, S, pos_base, scale_log2, out, s);
+    if (!kv.bt)
+        return launch_attn_mode<NOPE, OUT, 0, MASK>(q, C, kv, S, pos_base, scale_log2, out, mask, mask_stride, s);
+    if (kv.bs % PA_BK == 0)
+        return launch_attn_mode<NOPE, OUT, 1, MASK>(q, C, kv, S, pos_base, scale_log2, out, mask, mask_stride, s);
+    return launch_attn_mode<NOPE, OUT, 2, MASK>(q, C, kv, S, pos_base, scale_log2, out, mask, mask_stride, s);
+}
+
+template <int NOPE, typename OUT>
+static mla_status launch_attn_any(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
+                                  float scale_log2, void *out, const uint32_t *mask, int mask_stride, hipStream_t s)
+{
+    if (mask) return launch_attn<NOPE, OUT, true>(q, C, kv, S, pos_base, scale_log2, out, mask, mask_stride, s);
+    return launch_attn<NOPE, OUT, false>(q, C, kv, S, pos_base, scale_log2, out, nullptr, 0, s);
 }
 
 mla_status launch_prefill_mfma(const void *q, const void *kv_b, const mla_dims &d, const KvView &kv, int32_t S,
-                               int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws, hipStream_t s)
+                               int32_t pos_base, float sm_scale, void *out, mla_dtype out_dt, void *ws, hipStream_t s,
+                               const uint32_t *mask, int mask_stride)
 {
     const int64_t T = (int64_t)pos_base + S;
     const int N = d.n_heads * (d.qk_nope + d.v_head);
@@ -498,10 +533,10 @@ mla_status launch_prefill_mfma(const void *q, const void *kv_b, const mla_dims &
     if (st) return st;
     const float sl2 = sm_scale * 1.4426950408889634f;
     if (d.qk_nope == 192)
-        return out_dt == MLA_FP32 ? launch_attn<192, float>(q, C, kv, S, pos_base, sl2, out, s)
-                                  : launch_attn<192, bf16_t>(q, C, kv, S, pos_base, sl2, out, s);
-    return out_dt == MLA_FP32 ? launch_attn<128, float>(q, C, kv, S, pos_base, sl2, out, s)
-                              : launch_attn<128, bf16_t>(q, C, kv, S, pos_base, sl2, out, s);
+        return out_dt == MLA_FP32 ? launch_attn_any<192, float>(q, C, kv, S, pos_base, sl2, out, mask, mask_stride, s)
+                                  : launch_attn_any<192, bf16_t>(q, C, kv, S, pos_base, sl2, out, mask, mask_stride, s);
+    return out_dt == MLA_FP32 ? launch_attn_any<128, float>(q, C, kv, S, pos_base, sl2, out, mask, mask_stride, s)
+                              : launch_attn_any<128, bf16_t>(q, C, kv, S, pos_base, sl2, out, mask, mask_stride, s);
 }
 
 }  // namespace mla

@@ -354,3 +354,34 @@ def test_cache_write_and_shared_decode_validation(L):
     assert sh(theta=-1.0) == mla.MLA_ERR_ARG
     assert sh() == mla.MLA_ERR_WORKSPACE
     assert sh(ws=FAKE, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+
+
+def test_g_absorb_rule_and_attention_validation(L):
+    """colibri-analysis 06, sec. 2.3: g_absorb -1 absorbs when S <= 4, 0 never, 1 always."""
+    assert [L.mla_attention_absorbs(S, -1) for S in (1, 2, 3, 4, 5, 64, 4096)] == [1, 1, 1, 1, 0, 0, 0]
+    assert [L.mla_attention_absorbs(S, 0) for S in (1, 4, 4096)] == [0, 0, 0]
+    assert [L.mla_attention_absorbs(S, 1) for S in (1, 4, 4096)] == [1, 1, 1]
+    _no_gpu()
+    d = _dims()
+
+    def f(S=4, pb=100, g=-1, sel=None, nsel=None, stride=0, ws=None, wsb=0):
+        return L.mla_attention(FAKE, 1, FAKE, 1, ctypes.byref(d), ctypes.byref(_view(seq_len=None)), S, pb, sel, nsel,
+                               stride, 0.0625, g, FAKE, ws, wsb, None)
+    need = L.mla_attention_workspace_bytes(ctypes.byref(d), 4, 100, 0, -1)
+    assert need > 0
+    assert f() == mla.MLA_ERR_WORKSPACE
+    assert f(g=2) == mla.MLA_ERR_ARG
+    assert f(S=-1) == mla.MLA_ERR_ARG
+    assert f(sel=FAKE, nsel=None, stride=8) == mla.MLA_ERR_ARG
+    assert f(S=4000, pb=200) == mla.MLA_ERR_ARG          # rows beyond the 4096-row pool
+    assert f(S=0) == mla.MLA_OK
+    assert L.mla_attention_workspace_bytes(ctypes.byref(d), 4096, 0, 2048, 0) > \
+        L.mla_attention_workspace_bytes(ctypes.byref(d), 4096, 0, 0, 0)      # the key bitmap
+
+    def ps(S=8, pb=100, k=16, n_ih=32, ws=None, wsb=0):
+        return L.dsa_prefill_select(FAKE, FAKE, n_ih, ctypes.byref(_view(seq_len=None)), S, pb, k, FAKE, FAKE, FAKE,
+                                    ws, wsb, None)
+    assert ps() == mla.MLA_ERR_WORKSPACE
+    assert ps(k=0) == mla.MLA_ERR_ARG
+    assert ps(n_ih=65) == mla.MLA_ERR_UNSUPPORTED
+    assert ps(S=0) == mla.MLA_OK
