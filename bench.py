@@ -266,6 +266,7 @@ def bench_dsa_decode(args):
         extra["batched_paged_B32"] = bench_batched_paged(args)
         extra["dense_decode_T4096"] = bench_dense_decode(args)
         extra["prefill_S4096"] = measure_prefill(args, cpu=not args.no_cpu)
+        extra.update(bench_new_rows(args))
 
     line = {
         "metric": METRIC, "value": value, "unit": "keys·heads/s", "n_gpus": 1, "steps": args.steps,
@@ -441,6 +442,145 @@ def _oracle_timed(fn, reps, threads):
     finally:
         oracle.set_num_threads(keep)
     return statistics.median(times)
+
+
+def _time_fn(torch, fn, warmup, steps):
+    """Mean ms per call of fn() from events on the current stream (eager launches)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_new_rows(args):
+    """The cache-write side, the DSA-shared layer, multi-query absorbed decode (S = 4 draft queries at
+    T = 131072 with their own top-2048) and DSA in prefill (S = T = 4096, top-2048 per query), each with
+    its algorithmic bytes or flops against the HBM or bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_dsa_amd as mla
+    from mla_latent_kv_dsa_amd import synth
+
+    dev = torch.device("cuda:0")
+    H, NOPE, ROPE, V, L = synth.H, synth.QK_NOPE, synth.QK_ROPE, synth.V_HEAD, synth.KV_LORA
+    N_IH, HD, K = synth.N_IH, synth.INDEX_HD, synth.TOPK
+    sm = 1.0 / math.sqrt(NOPE + ROPE)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1009)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, generator=g, device=dev) * std
+    res = {}
+
+    # cache write: 4096 new tokens (a prefill's append) into 64-token paged pools, tiled indexer keys
+    n, bs = 4096, 64
+    nb = 2 * n // bs
+    pools = dict(lc=torch.zeros(nb * bs, L, dtype=torch.bfloat16, device=dev),
+                 rc=torch.zeros(nb * bs, ROPE, dtype=torch.bfloat16, device=dev),
+                 ic=torch.zeros(nb * bs, HD, dtype=torch.float32, device=dev))
+    bt = torch.randperm(nb, generator=g, device=dev).to(torch.int32)[None]
+    kv = mla.KvCache(pools["lc"], pools["rc"], pools["ic"], max_seq_len=nb * bs, block_table=bt, block_size=bs,
+                     ic_layout=mla.MLA_IC_TILE64)
+    comp, ik = rn(n, L + ROPE).bfloat16(), rn(n, HD).bfloat16()
+    seq = torch.zeros(n, dtype=torch.int32, device=dev)
+    pos = torch.arange(n, dtype=torch.int32, device=dev) + 1000
+    ms = _time_fn(torch, lambda: mla.mla_cache_write(comp, seq, pos, kv, 1, ik=ik, ix_rope_off=HD - ROPE,
+                                                     ix_rope_dim=ROPE), 3, 50)
+    nbytes = n * ((L + ROPE) * 2 + HD * 2 + 8 + L * 2 + ROPE * 2 + HD * 4)
+    res["cache_write_4096_tokens"] = {
+        "ms": ms, "bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "work": "4096 tokens: read comp (576 bf16) + ik (128 bf16) + seq/pos, write Lc/Rc (bf16) + Ic (fp32, tile64)"}
+
+    # one 131072-token sequence, its DSA selection (as the full layer of the step computes it)
+    T = 131072
+    lc, rc = rn(T, L).bfloat16(), rn(T, ROPE).bfloat16()
+    ic = rn(T, HD)
+    sl = torch.full((1,), T, dtype=torch.int32, device=dev)
+    kvT = mla.KvCache(lc, rc, synth.tile_index_keys(ic), seq_len=sl, max_seq_len=T, seq_stride=T,
+                      ic_layout=mla.MLA_IC_TILE64)
+    qi, wi = rn(1, N_IH, HD), rn(1, N_IH)
+    qn, qr, kvb = rn(1, H, NOPE).bfloat16(), rn(1, H, ROPE).bfloat16(), rn(H * (NOPE + V), L, std=0.02).bfloat16()
+    _, _, sel, nsel = mla.mla_dsa_decode(qn, qr, qi, wi, kvb, kvT, T, K, sm)
+    ws = torch.empty(mla.mla_decode_workspace_bytes(H, NOPE, ROPE, V, L, 1, K) + (1 << 20), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty(1, H, V, dtype=torch.float32, device=dev)
+    ms = _graph_time(torch, lambda: mla.mla_dsa_decode_shared(qn, qr, kvb, kvT, sel, nsel, sm, out=out, ws=ws),
+                     3, 50)
+    sel_bytes = K * (L + ROPE) * 2
+    kvb_bytes = H * (NOPE + V) * L * 2
+    res["shared_layer_T131072"] = {
+        "ms": ms, "keys_heads_per_s": T * H / (ms * 1e-3),
+        "bytes": sel_bytes + kvb_bytes, "GBs": (sel_bytes + kvb_bytes) / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "frac": (sel_bytes + kvb_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "work": "reuses the full layer's top-2048: RoPE, absorb (W_UK), attention over 2048 rows, W_UV"}
+
+    # multi-query absorbed decode: 4 draft queries at positions T-4 .. T-1, each with its own top-2048
+    S = 4
+    q4 = rn(S, H, NOPE + ROPE).bfloat16()
+    qi4, wi4 = rn(S, N_IH, HD), rn(S, N_IH)
+    kv4 = mla.KvCache(lc, rc, synth.tile_index_keys(ic), max_seq_len=T, seq_stride=T, ic_layout=mla.MLA_IC_TILE64)
+    sc4 = torch.empty(S, T, dtype=torch.float32, device=dev)
+    sel4 = torch.empty(S, K, dtype=torch.int32, device=dev)
+    nsel4 = torch.empty(S, dtype=torch.int32, device=dev)
+    ws_s = torch.empty(mla.lib().dsa_prefill_select_workspace_bytes(S, T - S, K), dtype=torch.uint8, device=dev)
+    out4 = torch.empty(S, H, V, dtype=torch.float32, device=dev)
+    d4 = mla._dims(H, NOPE, ROPE, V, L)
+    import ctypes
+    ws_a = torch.empty(mla.lib().mla_attention_workspace_bytes(ctypes.byref(d4), S, T - S, K, -1), dtype=torch.uint8,
+                       device=dev)
+
+    def mq_step():
+        mla.dsa_prefill_select(qi4, wi4, kv4, T - S, K, scores=sc4, sel=sel4, nsel=nsel4, ws=ws_s)
+        mla.mla_attention(q4, kvb, kv4, NOPE, T - S, sm, g_absorb=-1, sel=sel4, nsel=nsel4, out=out4, ws=ws_a)
+    ms = _graph_time(torch, mq_step, 3, 30)
+    ms_attn = _graph_time(torch, lambda: mla.mla_attention(q4, kvb, kv4, NOPE, T - S, sm, g_absorb=-1, sel=sel4,
+                                                           nsel=nsel4, out=out4, ws=ws_a), 3, 30)
+    kh = sum(T - S + i + 1 for i in range(S)) * H
+    stream = S * T * HD * 4 + S * sel_bytes
+    res["multi_query_decode_S4_T131072"] = {
+        "ms": ms, "keys_heads_per_s": kh / (ms * 1e-3), "ms_attention_only": ms_attn,
+        "stream_bytes": stream, "roofline": {"bound": "hbm", "frac": stream / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "work": "4 queries, each: indexer over its causal keys + top-2048 (dsa_prefill_select), absorbed attention "
+                "over its selection (mla_attention, g_absorb auto); the indexer streams Ic once per query"}
+
+    # DSA in prefill: S = T = 4096, top-2048 per query
+    S = T4 = 4096
+    p_lc, p_rc = rn(T4, L).bfloat16(), rn(T4, ROPE).bfloat16()
+    p_ic = rn(T4, HD)
+    kvp = mla.KvCache(p_lc, p_rc, synth.tile_index_keys(p_ic), max_seq_len=T4, seq_stride=T4,
+                      ic_layout=mla.MLA_IC_TILE64)
+    qp = rn(S, H, NOPE + ROPE).bfloat16()
+    qip, wip = rn(S, N_IH, HD), rn(S, N_IH)
+    scp = torch.empty(S, T4, dtype=torch.float32, device=dev)
+    selp = torch.empty(S, K, dtype=torch.int32, device=dev)
+    nselp = torch.empty(S, dtype=torch.int32, device=dev)
+    ws_p = torch.empty(mla.lib().dsa_prefill_select_workspace_bytes(S, 0, K), dtype=torch.uint8, device=dev)
+    outp = torch.empty(S, H, V, dtype=torch.float32, device=dev)
+    ms_sel = _time_fn(torch, lambda: mla.dsa_prefill_select(qip, wip, kvp, 0, K, scores=scp, sel=selp, nsel=nselp,
+                                                            ws=ws_p), 2, 5)
+    pairs = sum(min(i + 1, K) for i in range(S))
+    f_attn = 2 * H * pairs * (NOPE + ROPE + V)
+    f_kvb = 2 * T4 * H * (NOPE + V) * L
+    f_idx = 2 * N_IH * HD * (S * (S + 1) // 2)
+    dsa = {"ms_select": ms_sel, "indexer_flops_fp32": f_idx, "selected_pairs": pairs,
+           "work": "per query i: indexer over keys 0..i, top-2048, attention over its selection"}
+    for gab, name in ((0, "nonabsorbed"), (1, "absorbed")):
+        d_p = mla._dims(H, NOPE, ROPE, V, L)
+        ws_x = torch.empty(mla.lib().mla_attention_workspace_bytes(ctypes.byref(d_p), S, 0, K, gab), dtype=torch.uint8,
+                           device=dev)
+        ms = _time_fn(torch, lambda: mla.mla_attention(qp, kvb, kvp, NOPE, 0, sm, g_absorb=gab, sel=selp, nsel=nselp,
+                                                       out=outp, ws=ws_x), 2, 5)
+        fl = f_attn + (f_kvb if gab == 0 else 0)
+        dsa[name] = {"ms_attention": ms, "algorithmic_flops": fl, "TFLOPs": fl / (ms * 1e-3) / 1e12,
+                     "roofline": {"bound": "mfma", "frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
+    res["dsa_prefill_S4096"] = dsa
+    return res
 
 
 def cpu_baseline_decode(d, T, K, sm):
@@ -737,7 +877,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsa_decode", choices=["dsa_decode", "dsa_decode_paged_b32", "prefill", "copy"])
+    ap.add_argument("--workload", default="dsa_decode",
+                    choices=["dsa_decode", "dsa_decode_paged_b32", "prefill", "copy", "rows"])
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -783,6 +924,8 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "config": r}), flush=True)
     elif args.workload == "copy":
         bench_copy(args)
+    elif args.workload == "rows":   # the cache write, shared layer, multi-query decode and DSA prefill alone
+        print(json.dumps(bench_new_rows(args)), flush=True)
     else:
         bench_prefill(args)
 
