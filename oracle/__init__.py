@@ -64,6 +64,7 @@ def _load():
     lib.orc_prefill_rows.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f64, P, i32, P]
     lib.orc_tiny_layer.argtypes = [P, i32, i32, P, i32, P, P, i32, i32, i32, i32, f64, f64, P, P, P]
     lib.orc_o_proj.argtypes = [P, P, i32, i32, P]
+    lib.orc_dequant_rows.argtypes = [P, P, i32, i64, i32, P]
     lib.orc_cache_write.argtypes = [P, P, i64, P, P, i32, i32, i32, P, P, P, i32, i32, f64, f64, f64, P, i32, i32,
                                     i64, i64, P, P, P]
     _lib = lib
@@ -260,3 +261,26 @@ def cache_write(comp, ik, seq, pos, L: int, rope: int, *, rows: int, hd: int = 0
                             0 if bt is None else bt.shape[1], int(seq_stride), int(rows), _p(lc), _p(rc),
                             None if ic is None else _p(ic))
     return lc, rc, ic
+
+
+QFMT_FP8_E4M3, QFMT_INT8, QFMT_MXFP4 = 1, 2, 3
+
+
+def dequant_rows(codes, scales, fmt: int, cols: int) -> np.ndarray:
+    """Decode quantized kv_b rows to float64 (aiknowledge.cn Ch.7 sec. 03, sec. 3/5: int8, FP8 and
+    MXFP4 weight formats).  fmt 1: FP8 E4M3 codes [rows, cols] with an fp32 scale per row; fmt 2:
+    int8 codes with an fp32 scale per row; fmt 3: MXFP4, FP4 E2M1 codes two per byte (even element in
+    the low nibble) [rows, cols/2] with an E8M0 scale byte per 32 elements [rows, cols/32]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rows = codes.shape[0]
+    if fmt in (1, 2):
+        assert codes.shape == (rows, cols)
+        sc = _f32(scales)
+        assert sc.shape == (rows,)
+    else:
+        assert fmt == 3 and cols % 32 == 0 and codes.shape == (rows, cols // 2)
+        sc = np.ascontiguousarray(scales, dtype=np.uint8)
+        assert sc.shape == (rows, cols // 32)
+    out = np.empty((rows, cols), dtype=np.float64)
+    _load().orc_dequant_rows(_p(codes), _p(sc), int(fmt), rows, int(cols), _p(out))
+    return out

@@ -497,3 +497,55 @@ void orc_cache_write(const float *comp, const float *ik, int64_t n, const int32_
     free(u);
     free(y);
 }
+
+/* ------------------------------------------------------------------------------------
+ * Quantized kv_b rows  [P1 sec. 3 item 1 and sec. 5: int8 / FP8 / MXFP4 weight formats, each
+ * a bounded-loss representation of the same weights; P2 sec. 2.3: the absorbed path reads kv_b
+ * through qt_addrow / qt_matvec_rows over quantized rows]
+ * The pages name the formats, not their layout; the definitions used (readings):
+ *   fmt 1  FP8 E4M3 (OCP 8-bit floating point, "fn": no infinities, S.1111.111 is NaN):
+ *          code byte b: s = b>>7, e = (b>>3)&15, m = b&7; e == 0: (-1)^s m 2^-9;
+ *          else (-1)^s (1 + m/8) 2^(e-7).  One fp32 scale per row: w = scale[row] * value.
+ *   fmt 2  INT8: w = scale[row] * (signed byte).
+ *   fmt 3  MXFP4 (OCP Microscaling v1.0): blocks of 32 consecutive elements of a row share an
+ *          E8M0 scale byte x (2^(x-127); 255 is NaN); elements are FP4 E2M1, two per byte (the
+ *          even element in the low nibble): nibble n: s = n>>3, e = (n>>1)&3, m = n&1; e == 0:
+ *          (-1)^s m/2; else (-1)^s (1 + m/2) 2^(e-1).
+ * codes: fmt 1/2 [rows][cols] bytes, fmt 3 [rows][cols/2] bytes; scales: fmt 1/2 float [rows],
+ * fmt 3 bytes [rows][cols/32].  out: double [rows][cols].
+ * ----------------------------------------------------------------------------------*/
+static double orc_e4m3(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    if (e == 15 && m == 7) v = NAN;
+    return s ? -v : v;
+}
+
+static double orc_e2m1(unsigned n)
+{
+    int s = (n >> 3) & 1, e = (n >> 1) & 3, m = n & 1;
+    double v = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+    return s ? -v : v;
+}
+
+void orc_dequant_rows(const uint8_t *codes, const void *scales, int32_t fmt, int64_t rows, int32_t cols, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        double *o = out + r * cols;
+        if (fmt == 1 || fmt == 2) {
+            double sc = (double)((const float *)scales)[r];
+            const uint8_t *c = codes + r * cols;
+            for (int32_t j = 0; j < cols; ++j)
+                o[j] = sc * (fmt == 1 ? orc_e4m3(c[j]) : (double)(int8_t)c[j]);
+        } else {
+            const uint8_t *c = codes + r * (cols / 2);
+            const uint8_t *x = (const uint8_t *)scales + r * (cols / 32);
+            for (int32_t j = 0; j < cols; ++j) {
+                unsigned nib = (j & 1) ? (c[j / 2] >> 4) : (c[j / 2] & 15);
+                double sc = x[j / 32] == 255 ? NAN : ldexp(1.0, (int)x[j / 32] - 127);
+                o[j] = sc * orc_e2m1(nib);
+            }
+        }
+    }
+}

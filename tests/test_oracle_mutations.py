@@ -53,6 +53,18 @@ MUTATIONS = [
     ("cache write indexer rope slice at 0", "orc_rope_interleave(y, ic + row * hd, 1, 1, hd, ix_off, ix_rdim, pos + j, theta);",
      "orc_rope_interleave(y, ic + row * hd, 1, 1, hd, 0, ix_rdim, pos + j, theta);", 1),
     ("cache write beta dropped", "+ (beta ? (double)beta[c] : 0.0);", ";", 1),
+    ("e4m3 subnormal exponent", "ldexp((double)m, -9)", "ldexp((double)m, -10)", 1),
+    ("e4m3 exponent bias", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)", 1),
+    ("e4m3 mantissa weight", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 16.0, e - 7)", 1),
+    ("e2m1 subnormal value", "double v = e == 0 ? 0.5 * (double)m", "double v = e == 0 ? (double)m", 1),
+    ("mxfp4 nibble order", "unsigned nib = (j & 1) ? (c[j / 2] >> 4) : (c[j / 2] & 15);",
+     "unsigned nib = (j & 1) ? (c[j / 2] & 15) : (c[j / 2] >> 4);", 1),
+    ("e8m0 bias", "ldexp(1.0, (int)x[j / 32] - 127)", "ldexp(1.0, (int)x[j / 32] - 128)", 1),
+    ("mxfp4 block size", "const uint8_t *x = (const uint8_t *)scales + r * (cols / 32);",
+     "const uint8_t *x = (const uint8_t *)scales + r * (cols / 16);", 1),
+    ("int8 read unsigned", "(double)(int8_t)c[j]", "(double)c[j]", 1),
+    ("row scale of the wrong row", "double sc = (double)((const float *)scales)[r];",
+     "double sc = (double)((const float *)scales)[0];", 1),
 ]
 
 

@@ -492,3 +492,41 @@ def test_cache_write_paged_rows_worked_example(oracle):
     for j, r in written.items():
         c = seq[j] * 8 + pos[j]
         assert np.array_equal(lc[r], lc2[c]) and np.array_equal(rc[r], rc2[c]) and np.array_equal(ic[r], ic2[c])
+
+
+# ----------------------------------------------------------------------------- quantized kv_b rows
+def test_quant_formats_worked_values(oracle):
+    """FP8 E4M3, MXFP4 (E2M1 elements with E8M0 block scales) and INT8 rows decode to the values of
+    the published format definitions (tests/golden/quant_formats.json, worked by hand)."""
+    g = _golden("quant_formats.json")
+    codes = np.array([[int(c, 16) for c, _ in g["e4m3"]]], np.uint8)
+    got = oracle.dequant_rows(codes, np.array([1.0], np.float32), 1, codes.shape[1])[0]
+    assert np.array_equal(got, np.array([v for _, v in g["e4m3"]]))
+    assert np.isnan(oracle.dequant_rows(np.array([[0x7F, 0xFF]], np.uint8), np.ones(1, np.float32), 1, 2)).all()
+    # E2M1: 32 elements of one block, scale 2^0; element 2k in the low nibble of byte k
+    nib = np.array([n for n, _ in g["e2m1"]] + [0] * (32 - len(g["e2m1"])), np.uint8)
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)[None]
+    got = oracle.dequant_rows(packed, np.array([[127]], np.uint8), 3, 32)[0]
+    assert np.array_equal(got[: len(g["e2m1"])], np.array([v for _, v in g["e2m1"]]))
+    for x, v in g["e8m0"]:   # an all-ones-value block (code 2 = 1.0) shows the scale alone
+        got = oracle.dequant_rows(np.full((1, 16), 0x22, np.uint8), np.array([[x]], np.uint8), 3, 32)[0]
+        assert np.all(got == v), x
+    assert np.isnan(oracle.dequant_rows(np.full((1, 16), 0x22, np.uint8), np.array([[255]], np.uint8), 3, 32)).all()
+    got = oracle.dequant_rows(np.array([[0x80, 0x7F, 0xFF, 0x01]], np.uint8), np.array([0.25], np.float32), 2, 4)[0]
+    assert np.array_equal(got, [-32.0, 31.75, -0.25, 0.25])
+
+
+def test_quant_e4m3_is_monotone_and_scales_per_row(oracle):
+    """Every positive E4M3 code below NaN decodes to a strictly larger value than the one before it
+    (the format orders like its integer codes), negatives mirror them, and each row's scale
+    multiplies that row only; MXFP4 blocks of 32 take their own scale."""
+    pos = np.arange(127, dtype=np.uint8)[None]
+    v = oracle.dequant_rows(pos, np.ones(1, np.float32), 1, 127)[0]
+    assert np.all(np.diff(v) > 0) and v[0] == 0.0
+    neg = oracle.dequant_rows((pos | 0x80).astype(np.uint8), np.ones(1, np.float32), 1, 127)[0]
+    assert np.array_equal(neg, -v)
+    two = oracle.dequant_rows(np.vstack([pos, pos]), np.array([1.0, 3.0], np.float32), 1, 127)
+    assert np.array_equal(two[1], 3.0 * two[0])
+    blocks = oracle.dequant_rows(np.full((2, 32), 0x22, np.uint8), np.array([[127, 130], [125, 128]], np.uint8), 3, 64)
+    assert np.all(blocks[0, :32] == 1.0) and np.all(blocks[0, 32:] == 8.0)
+    assert np.all(blocks[1, :32] == 0.25) and np.all(blocks[1, 32:] == 2.0)
