@@ -363,6 +363,41 @@ mla_status dsa_prefill_select(const float *q_idx, const float *w_idx, int32_t n_
                               int32_t S, int32_t pos_base, int32_t k, float *scores, int32_t *sel,
                               int32_t *nsel, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Absorbed decode with a quantized kv_b.  [MLA] sec. 2.3: the absorbed path touches kv_b only in
+ * the per-head products qt_addrow (W_UK folded into the query) and qt_matvec_rows (W_UV applied to
+ * the latent), over quantized rows; [FDSA] sec. 3 and 5: int8 / FP8 / MXFP4 are bounded-loss forms
+ * of the same weights, each gated by a correctness check.  The result is mla_absorbed_decode's with
+ * kv_b replaced by the decoded weights (a row of kv_b = kv_lora columns, rows as in kv_b):
+ *   MLA_Q_FP8_E4M3  codes [N][kv_lora] bytes, OCP FP8 E4M3 (no infinities; the NaN codes 0x7F / 0xFF
+ *                   are outside the contract); scales fp32 [N]: w = scales[row] * e4m3(code)
+ *   MLA_Q_INT8      codes [N][kv_lora] signed bytes; scales fp32 [N]: w = scales[row] * code
+ *   MLA_Q_MXFP4     OCP Microscaling MXFP4: codes [N][kv_lora / 2] bytes, FP4 E2M1, column 2i in the
+ *                   low nibble of byte i; scales [N][kv_lora / 32] E8M0 bytes (255 = NaN, outside the
+ *                   contract): w = 2^(scale - 127) * e2m1(nibble)
+ * with N = n_heads * (qk_nope + v_head).  Products and sums run in fp32 (q_abs rounded to bf16 for
+ * the matrix cores, as on the bf16 path).  codes and scales are device pointers, 4-byte aligned.
+ * Supported: bf16 queries and cache, 64 heads, kv_lora 512, qk_rope 64, qk_nope a multiple of 8 up
+ * to 256, v_head a multiple of 32.  Other arguments and the workspace size as for
+ * mla_absorbed_decode (mla_decode_workspace_bytes).
+ * mla_dsa_decode_q is mla_dsa_decode with such a kv_b (the same scores, sel and nsel, bit for bit).
+ * --------------------------------------------------------------------------------- */
+typedef enum { MLA_Q_FP8_E4M3 = 1, MLA_Q_INT8 = 2, MLA_Q_MXFP4 = 3 } mla_qformat;
+typedef struct {
+    const void *codes;
+    const void *scales;
+    int32_t format;   /* mla_qformat */
+} mla_qweights;
+mla_status mla_absorbed_decode_q(const void *q_nope, const void *q_rope, mla_dtype q_dt, const mla_qweights *kv_b,
+                                 const mla_dims *d, int32_t B, const mla_kv_view *kv, const int32_t *sel,
+                                 const int32_t *nsel, int32_t sel_stride, float sm_scale, float *out, void *ws,
+                                 size_t ws_bytes, void *stream);
+mla_status mla_dsa_decode_q(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                            const float *q_idx, const float *w_idx, int32_t n_ih, const mla_qweights *kv_b,
+                            const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
+                            float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status, and the detail of the last failure on this thread. */
 const char *mla_status_string(mla_status s);
 const char *mla_last_error(void);

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libmla_dsa.so")
 MLA_OK, MLA_ERR_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_FP32, MLA_BF16 = 0, 1
 MLA_IC_ROWS, MLA_IC_TILE64 = 0, 1
+MLA_Q_FP8_E4M3, MLA_Q_INT8, MLA_Q_MXFP4 = 1, 2, 3
 
 EXPORTED = (
     "mla_rope_interleave", "mla_cache_write", "dsa_index_scores", "dsa_topk_workspace_bytes", "dsa_topk_select",
@@ -34,7 +35,7 @@ EXPORTED = (
     "mla_dsa_decode_workspace_bytes", "mla_dsa_decode", "mla_dsa_decode_noalloc",
     "mla_dsa_decode_shared_workspace_bytes", "mla_dsa_decode_shared",
     "mla_attention_absorbs", "mla_attention_workspace_bytes", "mla_attention",
-    "dsa_prefill_select_workspace_bytes", "dsa_prefill_select",
+    "dsa_prefill_select_workspace_bytes", "dsa_prefill_select", "mla_absorbed_decode_q", "mla_dsa_decode_q",
     "mla_prefill_workspace_bytes",
     "mla_prefill_nonabsorbed", "mla_status_string", "mla_last_error",
 )
@@ -134,6 +135,13 @@ def lib() -> ctypes.CDLL:
     L.dsa_prefill_select.argtypes = [P, P, i32, ctypes.POINTER(mla_kv_view), i32, i32, i32, P, P, P, P,
                                      ctypes.c_size_t, P]
     L.dsa_prefill_select.restype = st
+    L.mla_absorbed_decode_q.argtypes = [P, P, ctypes.c_int, ctypes.POINTER(mla_qweights), ctypes.POINTER(mla_dims), i32,
+                                        ctypes.POINTER(mla_kv_view), P, P, i32, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    L.mla_absorbed_decode_q.restype = st
+    L.mla_dsa_decode_q.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P, P, i32, ctypes.POINTER(mla_qweights),
+                                   ctypes.POINTER(mla_dims), i32, ctypes.POINTER(mla_kv_view), i64, i32, ctypes.c_float,
+                                   P, P, P, P, P, ctypes.c_size_t, P]
+    L.mla_dsa_decode_q.restype = st
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
@@ -181,6 +189,10 @@ def _contig(*ts):
     for t in ts:
         if t is not None and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+class mla_qweights(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("format", ctypes.c_int32)]
 
 
 class KvCache:
@@ -605,3 +617,83 @@ def dsa_prefill_select(q_idx: torch.Tensor, w_idx: torch.Tensor, kv: KvCache, po
     _check(lib().dsa_prefill_select(_ptr(q_idx), _ptr(w_idx), n_ih, ctypes.byref(kv.view), S, pos_base, k, _ptr(scores),
                                     _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return scores, sel, nsel
+
+
+def _qweights(codes: torch.Tensor, scales: torch.Tensor, fmt: int):
+    _dev(codes, scales)
+    _contig(codes, scales)
+    if codes.dtype != torch.uint8:
+        raise TypeError("codes must be uint8")
+    if fmt in (MLA_Q_FP8_E4M3, MLA_Q_INT8) and scales.dtype != torch.float32:
+        raise TypeError("FP8 / INT8 scales are float32, one per row")
+    if fmt == MLA_Q_MXFP4 and scales.dtype != torch.uint8:
+        raise TypeError("MXFP4 scales are E8M0 bytes")
+    w = mla_qweights()
+    w.codes, w.scales, w.format = codes.data_ptr(), scales.data_ptr(), int(fmt)
+    return w
+
+
+def mla_absorbed_decode_q(q_nope: torch.Tensor, q_rope: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                          fmt: int, kv: KvCache, sm_scale: float, sel: Optional[torch.Tensor] = None,
+                          nsel: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Absorbed decode with a quantized kv_b (codes uint8 [N, kv_lora] for FP8 / INT8 or [N, kv_lora/2] for
+    MXFP4; scales float32 [N] or E8M0 uint8 [N, kv_lora/32]; N = H * (qk_nope + v_head)).  Returns out
+    [B, H, v] float32."""
+    _dev(q_nope, q_rope, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, sel, nsel, out, ws)
+    B, H, nope = q_nope.shape
+    rope = q_rope.shape[2]
+    L = kv.lc.shape[1]
+    if q_rope.shape[:2] != (B, H) or codes.shape[0] % H or kv.rc.shape[1] != rope:
+        raise ValueError("shape mismatch between q_nope, q_rope, the cache and the codes")
+    v = codes.shape[0] // H - nope
+    stride = 0
+    if sel is not None:
+        if sel.dtype != torch.int32 or sel.dim() != 2 or sel.shape[0] != B or nsel is None \
+                or nsel.dtype != torch.int32 or nsel.shape != (B,):
+            raise ValueError("sel must be int32 [B, k] with nsel int32 [B]")
+        stride = sel.shape[1]
+    sel_p, nsel_p = _ptr(sel), _ptr(nsel)
+    w = _qweights(codes, scales, fmt)
+    d = _dims(H, nope, rope, v, L)
+    if out is None:
+        out = torch.empty((B, H, v), dtype=torch.float32, device=q_nope.device)
+    max_keys = stride if sel is not None else kv.view.max_seq_len
+    if ws is None:
+        need = int(lib().mla_decode_workspace_bytes(ctypes.byref(d), B, max_keys))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_absorbed_decode_q(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), ctypes.byref(w), ctypes.byref(d), B,
+                                       ctypes.byref(kv.view), sel_p, nsel_p, stride, float(sm_scale), _ptr(out),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(q_nope.device)))
+    return out
+
+
+def mla_dsa_decode_q(q_nope: torch.Tensor, q_rope: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
+                     codes: torch.Tensor, scales: torch.Tensor, fmt: int, kv: KvCache, t_max: int, k: int,
+                     sm_scale: float, theta: float = 10000.0, scores: Optional[torch.Tensor] = None,
+                     sel: Optional[torch.Tensor] = None, nsel: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """mla_dsa_decode with a quantized kv_b.  Returns (out, scores, sel, nsel)."""
+    _dev(q_nope, q_rope, q_idx, w_idx, scores, sel, nsel, out, ws)
+    _contig(q_nope, q_rope, q_idx, w_idx, scores, sel, nsel, out, ws)
+    B, H, nope = q_nope.shape
+    rope = q_rope.shape[2]
+    L = kv.lc.shape[1]
+    v = codes.shape[0] // H - nope
+    n_ih = q_idx.shape[1]
+    w = _qweights(codes, scales, fmt)
+    dev = q_nope.device
+    scores = torch.empty((B, t_max), dtype=torch.float32, device=dev) if scores is None else scores
+    sel = torch.empty((B, k), dtype=torch.int32, device=dev) if sel is None else sel
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev) if nsel is None else nsel
+    out = torch.empty((B, H, v), dtype=torch.float32, device=dev) if out is None else out
+    d = _dims(H, nope, rope, v, L)
+    if ws is None:
+        need = int(lib().mla_dsa_decode_workspace_bytes(ctypes.byref(d), B, t_max, k))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().mla_dsa_decode_q(_ptr(q_nope), _ptr(q_rope), _dt(q_nope), float(theta), _ptr(q_idx), _ptr(w_idx), n_ih,
+                                  ctypes.byref(w), ctypes.byref(d), B, ctypes.byref(kv.view), t_max, k,
+                                  float(sm_scale), _ptr(scores), _ptr(sel), _ptr(nsel), _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(dev)))
+    return out, scores, sel, nsel

@@ -393,6 +393,71 @@ mla_status mla_dsa_decode_noalloc(const void *q_nope, const void *q_rope, mla_dt
                           scores, sel, nsel, out, scratch, stream);
 }
 
+static mla_status check_qweights(const mla_qweights *w, const mla_dims *d)
+{
+    if (!w) return fail(MLA_ERR_ARG, "quantized kv_b: weights struct is NULL");
+    if (w->format != MLA_Q_FP8_E4M3 && w->format != MLA_Q_INT8 && w->format != MLA_Q_MXFP4)
+        return fail(MLA_ERR_ARG, "quantized kv_b: unknown format %d", (int)w->format);
+    if (!w->codes || !w->scales) return fail(MLA_ERR_ARG, "quantized kv_b: codes or scales is NULL");
+    if (((reinterpret_cast<uintptr_t>(w->codes) | reinterpret_cast<uintptr_t>(w->scales)) & 3u) != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "quantized kv_b: codes and scales must be 4-byte aligned");
+    if (!decode_quant_supported(*d, MLA_BF16))
+        return fail(MLA_ERR_UNSUPPORTED, "quantized kv_b: needs 64 heads, kv_lora 512, qk_rope 64, qk_nope a multiple "
+                    "of 8 up to 256, v_head a multiple of 32");
+    return MLA_OK;
+}
+
+static bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status mla_absorbed_decode_q(const void *q_nope, const void *q_rope, mla_dtype q_dt, const mla_qweights *kv_b,
+                                 const mla_dims *d, int32_t B, const mla_kv_view *kv, const int32_t *sel,
+                                 const int32_t *nsel, int32_t sel_stride, float sm_scale, float *out, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    mla_status st = check_decode_attend(d, B, q_dt, q_dt, kv, sel, nsel, sel_stride, sm_scale);
+    if (st) return st;
+    if (q_dt != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "quantized decode: bf16 queries and cache only");
+    st = check_qweights(kv_b, d);
+    if (st) return st;
+    if (B == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !out) return fail(MLA_ERR_ARG, "quantized decode: NULL tensor");
+    if (!al16(q_nope) || !al16(q_rope) || !al16(kv->lc) || !al16(kv->rc))
+        return fail(MLA_ERR_UNSUPPORTED, "quantized decode: q_nope, q_rope, Lc and Rc must be 16-byte aligned");
+    const int64_t max_keys = sel ? (int64_t)sel_stride : kv->max_seq_len;
+    st = check_ws("quantized decode", decode_workspace_bytes(*d, B, max_keys, q_dt), ws, ws_bytes);
+    if (st) return st;
+    return launch_decode_quant(q_nope, q_rope, (const uint8_t *)kv_b->codes, kv_b->scales, kv_b->format, *d, B,
+                               to_view(*kv), sel, nsel, sel ? sel_stride : 0, max_keys, sm_scale, out, ws,
+                               (hipStream_t)stream);
+}
+
+mla_status mla_dsa_decode_q(const void *q_nope, const void *q_rope, mla_dtype q_dt, double rope_theta,
+                            const float *q_idx, const float *w_idx, int32_t n_ih, const mla_qweights *kv_b,
+                            const mla_dims *d, int32_t B, const mla_kv_view *kv, int64_t t_max, int32_t k,
+                            float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                            size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    const void *codes = kv_b ? kv_b->codes : nullptr;
+    mla_status st = check_dsa_decode(q_nope, q_rope, q_dt, rope_theta, q_idx, w_idx, n_ih, codes, q_dt, d, B, kv,
+                                     t_max, k, sm_scale, scores, sel, nsel, out);
+    if (st || B == 0) return st;
+    if (q_dt != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "quantized decode: bf16 queries and cache only");
+    st = check_qweights(kv_b, d);
+    if (st) return st;
+    if (!al16(q_nope) || !al16(q_rope) || !al16(kv->lc) || !al16(kv->rc))
+        return fail(MLA_ERR_UNSUPPORTED, "quantized decode: q_nope, q_rope, Lc and Rc must be 16-byte aligned");
+    st = check_ws("quantized dsa decode", dsa_decode_workspace_bytes(*d, B, t_max, k, q_dt), ws, ws_bytes);
+    if (st) return st;
+    const KvView v = to_view(*kv);
+    KvView vs = v;
+    if (vs.max_seq_len > t_max) vs.max_seq_len = t_max;
+    return launch_dsa_decode_quant(q_nope, q_rope, rope_theta, q_idx, w_idx, n_ih, kv->index_hd,
+                                   (const uint8_t *)kv_b->codes, kv_b->scales, kv_b->format, *d, B, vs, v, t_max, k,
+                                   sm_scale, scores, sel, nsel, out, ws, (hipStream_t)stream);
+}
+
 int32_t mla_attention_absorbs(int32_t S, int32_t g_absorb) { return attention_absorbs(S, g_absorb) ? 1 : 0; }
 
 size_t mla_attention_workspace_bytes(const mla_dims *d, int32_t S, int32_t pos_base, int32_t sel_stride,

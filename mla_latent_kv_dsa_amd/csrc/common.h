@@ -283,6 +283,19 @@ mla_status launch_cache_write(const void *comp, const void *ik, mla_dtype in_dt,
                               int32_t ix_off, int32_t ix_rdim, float eps_kv, float eps_ix, double theta,
                               hipStream_t s);
 
+// absorbed decode with quantized kv_b rows (quant.hip); workspace as decode_workspace_bytes
+bool decode_quant_supported(const mla_dims &d, mla_dtype dt);
+mla_status launch_decode_quant(const void *q_nope, const void *q_rope, const uint8_t *codes, const void *scales,
+                               int32_t fmt, const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
+                               const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, float *out,
+                               void *ws, hipStream_t s);
+
+mla_status launch_dsa_decode_quant(const void *q_nope, const void *q_rope, double theta, const float *q_idx,
+                                   const float *w_idx, int32_t n_ih, int32_t hd, const uint8_t *codes,
+                                   const void *scales, int32_t fmt, const mla_dims &d, int32_t B, const KvView &kv_sel,
+                                   const KvView &kv, int64_t t_max, int32_t k, float sm_scale, float *scores,
+                                   int32_t *sel, int32_t *nsel, float *out, void *ws, hipStream_t s);
+
 // The library's static device scratch (noalloc.hip): its size, and its address on the calling
 // thread's current device (looked up once per device).
 constexpr size_t NOALLOC_SCRATCH_BYTES = MLA_NOALLOC_SCRATCH_BYTES;

@@ -174,4 +174,26 @@ mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype d
     return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
 }
 
+// The decode step with a quantized kv_b: RoPE of the query tails (out of place), indexer and top-k,
+// then the quantized absorbed decode over the selected keys.  Same workspace layout as the bf16 step.
+mla_status launch_dsa_decode_quant(const void *q_nope, const void *q_rope, double theta, const float *q_idx,
+                                   const float *w_idx, int32_t n_ih, int32_t hd, const uint8_t *codes,
+                                   const void *scales, int32_t fmt, const mla_dims &d, int32_t B, const KvView &kv_sel,
+                                   const KvView &kv, int64_t t_max, int32_t k, float sm_scale, float *scores,
+                                   int32_t *sel, int32_t *nsel, float *out, void *ws, hipStream_t s)
+{
+    char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    const size_t sel_bytes = index_select_workspace_bytes(B, t_max, k);
+    void *sel_ws = p;
+    p += al256(sel_bytes);
+    void *dec_ws = p;
+    p += al256(decode_workspace_bytes(d, B, k, MLA_BF16));
+    void *qr = p;
+    mla_status st = launch_rope_decode(q_rope, qr, MLA_BF16, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
+    if (st) return st;
+    st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s);
+    if (st) return st;
+    return launch_decode_quant(q_nope, qr, codes, scales, fmt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s);
+}
+
 }  // namespace mla

@@ -1108,4 +1108,38 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     return check_launch("combine_unabsorb");
 }
 
+// The attention part of the decode up to the combined latent rows, without W_UV (for weights the
+// matrix-core combine does not read, e.g. quantized ones): the key splits as above (no W_UV
+// read-ahead), then combine_reduce for every batch size.  q_abs must already sit in the workspace.
+mla_status launch_attend_mfma_clat(const void *q_rope, int32_t B, const KvView &kv, const int32_t *sel,
+                                   const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, void *ws,
+                                   hipStream_t s, bf16_t **clat)
+{
+    if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: B > 65535");
+    if (max_keys > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: too many keys");
+    const DecPlan p = dec_plan(B, max_keys);
+    const DecWs w = dec_ws(ws, B, p);
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+    mla_status st = enable_big_lds();
+    if (st) return st;
+    if (B >= MH_MIN_B)
+        hipLaunchKernelGGL(dec_core_mh, dim3(p.ns, B), dim3(256), MH_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv, sel,
+                           nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
+    else if (p.kps <= DC_SUP * DC_KC)
+        hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, (const bf16_t *)nullptr, 0, 0);
+    else
+        hipLaunchKernelGGL(dec_core<false>, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, (const bf16_t *)nullptr, 0, 0);
+    st = check_launch("dec_core");
+    if (st) return st;
+    const int npairs = B * DM_H;
+    hipLaunchKernelGGL(combine_reduce, dim3((npairs + CR_PAIRS - 1) / CR_PAIRS), dim3(256), 0, s, w.o_part, w.m_part,
+                       w.l_part, p.ns, npairs, w.clat);
+    *clat = w.clat;
+    return check_launch("combine_reduce");
+}
+
 }  // namespace mla

@@ -28,6 +28,9 @@ size_t decode_mfma_absorb_ws(int32_t B);
 mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_dims &d, int32_t B, void *ws,
                               hipStream_t s);
 bf16_t *decode_mfma_qabs(void *ws);   // where the absorb step leaves q_abs in a decode workspace
+mla_status launch_attend_mfma_clat(const void *q_rope, int32_t B, const KvView &kv, const int32_t *sel,
+                                   const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, void *ws,
+                                   hipStream_t s, bf16_t **clat);
 mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B, const KvView &kv,
                               const int32_t *sel, const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
                               float sm_scale, float *out, void *ws, hipStream_t s);

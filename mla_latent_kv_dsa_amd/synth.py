@@ -275,3 +275,37 @@ def paged_values_torch(pb: PagedBatch, seed: int, device, w_std=0.02) -> dict:
                 q_nope=rn(pb.B, pb.H, pb.nope, bf16=True), q_rope=rn(pb.B, pb.H, pb.rope, bf16=True),
                 kv_b=rn(pb.H * (pb.nope + pb.v), pb.L, std=w_std, bf16=True),
                 q_idx=rn(pb.B, pb.n_ih, pb.hd), w_idx=rn(pb.B, pb.n_ih))
+
+
+QFMT_FP8_E4M3, QFMT_INT8, QFMT_MXFP4 = 1, 2, 3
+
+
+def quantized_kv_b(seed: int, fmt: int, rows: int, cols: int):
+    """Random codes and scales of a quantized kv_b [rows, cols] (drawn directly in the format, with
+    magnitudes like N(0, 0.02^2) weights; no weight is quantized here):
+      FP8 E4M3: sign uniform, exponent field ~ round(N(7, 1.5)) clipped to [0, 15], mantissa uniform,
+                the NaN code (exponent 15, mantissa 7) redrawn as mantissa 6; scale per row
+                U(0.8, 1.2) * 0.02 / 1.5, float32
+      INT8:     round(N(0, 40^2)) clipped to [-127, 127]; scale per row U(0.8, 1.2) * 0.02 / 40
+      MXFP4:    nibbles uniform over the 16 E2M1 codes, two per byte; E8M0 scale per 32 columns
+                uniform over 127 - 9 .. 127 - 7
+    Returns (codes uint8, scales float32 [rows] or uint8 [rows, cols / 32])."""
+    rng = np.random.default_rng(seed)
+    if fmt == QFMT_FP8_E4M3:
+        s = rng.integers(0, 2, (rows, cols))
+        e = np.clip(np.rint(rng.normal(7.0, 1.5, (rows, cols))), 0, 15).astype(np.int64)
+        m = rng.integers(0, 8, (rows, cols))
+        m = np.where((e == 15) & (m == 7), 6, m)
+        codes = ((s << 7) | (e << 3) | m).astype(np.uint8)
+        scales = (rng.uniform(0.8, 1.2, rows) * 0.02 / 1.5).astype(np.float32)
+    elif fmt == QFMT_INT8:
+        codes = np.clip(np.rint(rng.normal(0.0, 40.0, (rows, cols))), -127, 127).astype(np.int8).view(np.uint8)
+        scales = (rng.uniform(0.8, 1.2, rows) * 0.02 / 40.0).astype(np.float32)
+    elif fmt == QFMT_MXFP4:
+        assert cols % 32 == 0
+        nib = rng.integers(0, 16, (rows, cols)).astype(np.uint8)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        scales = rng.integers(127 - 9, 127 - 6, (rows, cols // 32)).astype(np.uint8)
+    else:
+        raise ValueError(fmt)
+    return codes, scales

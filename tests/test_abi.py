@@ -385,3 +385,23 @@ def test_g_absorb_rule_and_attention_validation(L):
     assert ps(k=0) == mla.MLA_ERR_ARG
     assert ps(n_ih=65) == mla.MLA_ERR_UNSUPPORTED
     assert ps(S=0) == mla.MLA_OK
+
+
+def test_quantized_decode_validation(L):
+    _no_gpu()
+    d = _dims()
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 1, 4096)
+
+    def f(fmt=1, codes=FAKE, scales=FAKE, dd=None, q_dt=1, ws=FAKE, wsb=None):
+        w = mla.mla_qweights()
+        w.codes, w.scales, w.format = codes.value if codes else None, scales.value if scales else None, fmt
+        return L.mla_absorbed_decode_q(FAKE, FAKE, q_dt, ctypes.byref(w), ctypes.byref(dd or d), 1,
+                                       ctypes.byref(_view()), None, None, 0, 0.0625, FAKE, ws,
+                                       need if wsb is None else wsb, None)
+    assert f(fmt=0) == mla.MLA_ERR_ARG
+    assert f(fmt=4) == mla.MLA_ERR_ARG
+    assert f(codes=None) == mla.MLA_ERR_ARG
+    assert f(scales=ctypes.c_void_p(0x1002)) == mla.MLA_ERR_UNSUPPORTED     # 4-byte alignment
+    assert f(dd=_dims(kv_lora=256)) == mla.MLA_ERR_UNSUPPORTED              # not the matrix-core geometry
+    assert f(q_dt=0) == mla.MLA_ERR_UNSUPPORTED
+    assert f(wsb=need - 1) == mla.MLA_ERR_WORKSPACE
