@@ -580,6 +580,35 @@ def bench_new_rows(args):
         dsa[name] = {"ms_attention": ms, "algorithmic_flops": fl, "TFLOPs": fl / (ms * 1e-3) / 1e12,
                      "roofline": {"bound": "mfma", "frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}}
     res["dsa_prefill_S4096"] = dsa
+
+    # the decode step at T = 131072 with a quantized kv_b, per format; three input copies rotated
+    cps = []
+    for c in range(3):
+        kvc = mla.KvCache(rn(T, L).bfloat16(), rn(T, ROPE).bfloat16(), synth.tile_index_keys(rn(T, HD)), seq_len=sl,
+                          max_seq_len=T, seq_stride=T, ic_layout=mla.MLA_IC_TILE64)
+        cps.append(dict(kv=kvc, qn=rn(1, H, NOPE).bfloat16(), qr=rn(1, H, ROPE).bfloat16(), qi=rn(1, N_IH, HD),
+                        wi=rn(1, N_IH), sc=torch.empty(1, T, device=dev), sel=torch.empty(1, K, dtype=torch.int32,
+                                                                                            device=dev),
+                        nsel=torch.empty(1, dtype=torch.int32, device=dev), out=torch.empty(1, H, V, device=dev),
+                        ws=torch.empty(mla.mla_dsa_decode_workspace_bytes(H, NOPE, ROPE, V, L, 1, T, K),
+                                       dtype=torch.uint8, device=dev)))
+    N = H * (NOPE + V)
+    q_res = {}
+    for fmt, name in ((mla.MLA_Q_FP8_E4M3, "fp8_e4m3"), (mla.MLA_Q_INT8, "int8"), (mla.MLA_Q_MXFP4, "mxfp4")):
+        codes_np, scales_np = synth.quantized_kv_b(900 + fmt, fmt, N, L)
+        codes, scales = torch.from_numpy(codes_np).to(dev), torch.from_numpy(scales_np).to(dev)
+
+        def qstep():
+            for c in cps:
+                mla.mla_dsa_decode_q(c["qn"], c["qr"], c["qi"], c["wi"], codes, scales, fmt, c["kv"], T, K, sm,
+                                     scores=c["sc"], sel=c["sel"], nsel=c["nsel"], out=c["out"], ws=c["ws"])
+        ms = _graph_time(torch, qstep, 3, 20) / len(cps)
+        wbytes = codes.numel() + scales.numel() * scales.element_size()
+        step = T * HD * 4 + sel_bytes + wbytes
+        q_res[name] = {"ms_per_step": ms, "keys_heads_per_s": T * H / (ms * 1e-3), "weight_bytes": wbytes,
+                       "whole_step": {"bytes": step, "frac": step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                       "stream": {"frac": (T * HD * 4 + sel_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    res["dsa_decode_quantized_kv_b_T131072"] = q_res
     return res
 
 
