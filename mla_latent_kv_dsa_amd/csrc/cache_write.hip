@@ -23,6 +23,10 @@ __device__ __forceinline__ int64_t cw_row(const KvView &v, int b, int n_seq, int
     return r < v.rows ? r : -1;
 }
 
+// One wave per token.  Every load of the token (the kv_a row, the indexer key row, the gains) is
+// issued before the first reduction waits on any of them; lane l holds columns l, l + 64, .. .
+constexpr int CW_LC = 2048 / 64, CW_RP = 512 / 2 / 64, CW_IC = 256 / 64;   // per-lane capacities
+
 template <typename TIN, typename TKV>
 __global__ __launch_bounds__(64) void cache_write_kernel(const TIN *__restrict__ comp, const TIN *__restrict__ ik,
                                                          const int32_t *__restrict__ seq,
@@ -37,51 +41,82 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const TIN *__restrict__
     const int lane = threadIdx.x;
     const int b = seq[j];
     const int64_t p = pos[j];
+    const TIN *cj = comp + j * (int64_t)(L + rope);
+    const TIN *kj = ik ? ik + j * (int64_t)hd : nullptr;
+    const int half = rope >> 1;
+    // all loads first (clamped addresses, masked on use)
+    float xl[CW_LC], gl[CW_LC], ra[CW_RP], rb[CW_RP], xk[CW_IC], gk[CW_IC], bk[CW_IC];
+#pragma unroll
+    for (int u = 0; u < CW_LC; ++u) {
+        const int c = lane + 64 * u;
+        xl[u] = c < L ? ld(cj + c) : 0.f;
+        gl[u] = (c < L && kv_gain) ? kv_gain[c] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < CW_RP; ++u) {
+        const int q = lane + 64 * u;
+        ra[u] = q < half ? ld(cj + L + 2 * q) : 0.f;
+        rb[u] = q < half ? ld(cj + L + 2 * q + 1) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < CW_IC; ++u) {
+        const int c = lane + 64 * u;
+        xk[u] = (kj && c < hd) ? ld(kj + c) : 0.f;
+        gk[u] = (gamma && c < hd) ? gamma[c] : 1.f;
+        bk[u] = (beta && c < hd) ? beta[c] : 0.f;
+    }
     const int64_t row = cw_row(kv, b, n_seq, p);
     if (row < 0) return;   // wave-uniform
-    const TIN *cj = comp + j * (int64_t)(L + rope);
     // Lc = comp[0:L] / sqrt(mean(comp[0:L]^2) + eps) * gain
     float ss = 0.f;
-    for (int c = lane; c < L; c += 64) {
-        const float x = ld(cj + c);
-        ss = __builtin_fmaf(x, x, ss);
-    }
+#pragma unroll
+    for (int u = 0; u < CW_LC; ++u) ss = __builtin_fmaf(xl[u], xl[u], ss);
     ss = wave_sum(ss);
     const float inv = 1.0f / __builtin_sqrtf(ss / (float)L + eps_kv);
     TKV *lc = const_cast<TKV *>(reinterpret_cast<const TKV *>(kv.lc)) + row * L;
-    for (int c = lane; c < L; c += 64) {
-        const float g = kv_gain ? kv_gain[c] : 1.f;
-        st(lc + c, ld(cj + c) * inv * g);
+#pragma unroll
+    for (int u = 0; u < CW_LC; ++u) {
+        const int c = lane + 64 * u;
+        if (c < L) st(lc + c, xl[u] * inv * gl[u]);
     }
     // Rc = RoPE(comp[L:L+rope]) at the token's position
-    const int half = rope >> 1;
     TKV *rc = const_cast<TKV *>(reinterpret_cast<const TKV *>(kv.rc)) + row * rope;
-    for (int q = lane; q < half; q += 64) {
-        float lo, hi;
-        rope_pair(ld(cj + L + 2 * q), ld(cj + L + 2 * q + 1), q, rope, (double)p, theta, lo, hi);
-        st(rc + q, lo);
-        st(rc + half + q, hi);
+#pragma unroll
+    for (int u = 0; u < CW_RP; ++u) {
+        const int q = lane + 64 * u;
+        if (q < half) {
+            float lo, hi;
+            rope_pair(ra[u], rb[u], q, rope, (double)p, theta, lo, hi);
+            st(rc + q, lo);
+            st(rc + half + q, hi);
+        }
     }
-    if (!ik) return;
+    if (!kj) return;
     // Ic = RoPE over [ix_off, ix_off + ix_rdim) of LayerNorm(ik)
-    const TIN *kj = ik + j * (int64_t)hd;
     float s1 = 0.f;
-    for (int c = lane; c < hd; c += 64) s1 += ld(kj + c);
+#pragma unroll
+    for (int u = 0; u < CW_IC; ++u) s1 += xk[u];
     const float mean = wave_sum(s1) / (float)hd;
     float s2 = 0.f;
-    for (int c = lane; c < hd; c += 64) {
-        const float d = ld(kj + c) - mean;
-        s2 = __builtin_fmaf(d, d, s2);
+#pragma unroll
+    for (int u = 0; u < CW_IC; ++u) {
+        const int c = lane + 64 * u;
+        const float dlt = c < hd ? xk[u] - mean : 0.f;
+        s2 = __builtin_fmaf(dlt, dlt, s2);
     }
     const float is = 1.0f / __builtin_sqrtf(wave_sum(s2) / (float)hd + eps_ix);
-    for (int c = lane; c < hd; c += 64) {
-        const float y = (ld(kj + c) - mean) * is;
-        ys[c] = __builtin_fmaf(y, gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
+#pragma unroll
+    for (int u = 0; u < CW_IC; ++u) {
+        const int c = lane + 64 * u;
+        if (c < hd) ys[c] = __builtin_fmaf((xk[u] - mean) * is, gk[u], bk[u]);
     }
     __syncthreads();
     float *ic = const_cast<float *>(kv.ic);
     const int rh = ix_rdim >> 1;
-    for (int c = lane; c < hd; c += 64) {
+#pragma unroll
+    for (int u = 0; u < CW_IC; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= hd) continue;
         float o = ys[c];
         const int sidx = c - ix_off;
         if (sidx >= 0 && sidx < ix_rdim) {
