@@ -226,19 +226,10 @@ mla_status launch_rope_decode(const void *x, void *y, mla_dtype dt, int32_t B, i
 // hist_parts_max(B, t_max).
 struct HistOut {
     uint32_t *hl;     // [B][HL_CAP][parts_max]
-    uint32_t *hcnt;   // [B][parts_max] (candidate mode: the parts' headers)
+    uint32_t *hcnt;   // [B][parts_max]
     int parts_max;    // row stride in parts
     int parts;        // set by the launch
-    uint2 *cand;      // non-null: candidate mode (matrix-core indexer only), [B][parts_max][CAND_CAP]
 };
-// Candidate mode of the matrix-core indexer: each part keeps its keys at or above the bin of its
-// CAND_MIN-th largest key, at most CAND_CAP (dsa_index.hip); the selection is exact regardless.
-constexpr int CAND_MIN = 32, CAND_CAP = 64;
-// waves per workgroup of the matrix-core indexer: part p of a row holds the 64-key tiles t with
-// (t mod (parts * IX_WAVES_PER_PART)) / IX_WAVES_PER_PART == p
-constexpr int IX_WAVES_PER_PART = 4;
-// parts per row of the matrix-core indexer for this shape, or 0 when it does not serve it
-int index_mfma_parts(int32_t B, int64_t t_max, int32_t n_ih, int32_t hd, const KvView &kv, const float *q);
 int hist_parts_max(int32_t B, int64_t t_max);
 mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd,
                                const KvView &kv, int64_t t_max, float *scores, HistOut *hist, hipStream_t s);

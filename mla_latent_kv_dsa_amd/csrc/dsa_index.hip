@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void index_scores_generic(const float *__restr
 // block barrier does not wait on the key stream.
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-constexpr int IXM_WAVES = IX_WAVES_PER_PART;
+constexpr int IXM_WAVES = 4;
 constexpr int IXM_QROW = 128 + 4;    // floats per query row in LDS (pad against bank conflicts)
 
 // Pointer for the lane-private loads of key (tile * 64 + lane).  A key with no score (past the
@@ -204,32 +204,21 @@ __device__ __forceinline__ float ix_fold(const v32f &acc, const float *__restric
     return s;
 }
 
-// HM (what the workgroup records for the selection besides the scores), part blockIdx.x of row b:
-//   0  nothing
-//   1  the nonzero bins of an LDS histogram of the top 11 order-key bits of its keys t < n, as a
-//      list -- the first pass of the list-histogram selection
-//   2  its candidates: every key whose 11-bit bin lies at or above the bin bw that holds its
-//      CAND_MIN-th largest key (all its keys when it has at most CAND_CAP), at most CAND_CAP of
-//      them (keys of bin bw beyond the cap are left out), as (order key, position), and a header
-//      count | code << 16 where code = 1 + the highest bin with a key left out (0: none) -- the
-//      candidate selection (dsa_select.hip) checks the code against the row's threshold
+// HIST: also count the top 11 order-key bits of every score with t < n in an LDS histogram and
+// write its nonzero bins as this workgroup's list (part blockIdx.x of row b) -- the first pass of
+// the top-k selection.
 constexpr int IX_BINS = HIST_BINS;
-constexpr int IX_CT = 4;   // scores a wave keeps in LDS (tiles beyond re-read their own stores)
 
-template <int MODE, int HM, bool TILED>
+template <int MODE, bool HIST, bool TILED>
 __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float *__restrict__ q,
                                                                      const float *__restrict__ w, KvView kv,
                                                                      int64_t t_max, float *__restrict__ scores,
                                                                      uint32_t *__restrict__ hl,
-                                                                     uint32_t *__restrict__ hcnt, int parts_max,
-                                                                     uint2 *__restrict__ cand)
+                                                                     uint32_t *__restrict__ hcnt, int parts_max)
 {
-    constexpr bool HIST = HM != 0;
     __shared__ float sq[32 * IXM_QROW];
     __shared__ uint32_t hs[HIST ? IX_BINS : 1];
     __shared__ uint32_t sh_scan[IXM_WAVES];
-    __shared__ float ssc[HM == 2 ? IXM_WAVES * IX_CT * 64 : 1];
-    __shared__ uint32_t s_cut[5];   // bw, keys above bw, keys at or above bw, keys taken, bw keys taken
     const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile math stays scalar
     const int64_t n = seq_len_of(kv, b) < t_max ? seq_len_of(kv, b) : t_max;
@@ -272,7 +261,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     ix_load_slice<TILED>(KA, p, 0);
     __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
     ix_load_slice<TILED>(KB, p, 1);
-    for (int it = 0; tile < ntv; tile += waves_total, ++it) {
+    for (; tile < ntv; tile += waves_total) {
         // the next tile's first two slices are loaded unconditionally (from the query block
         // when there is no next tile) so every iteration leaves the same loads in flight
         const int64_t nxt = tile + waves_total;
@@ -294,69 +283,14 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
         const float sc = valid ? s : -INFINITY;
         if (t < t_max) out[t] = sc;
         if (HIST && t < n) atomicAdd(&hs[order_key(sc) >> 21], 1u);
-        if (HM == 2 && it < IX_CT) ssc[(wave * IX_CT + it) * 64 + lane] = sc;
         p = pn;
         valid = valid_n;
     }
     }
-    if (HM == 1) {
+    if (HIST) {
         __syncthreads();
         hist_write_list<64 * IXM_WAVES>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max,
                                         hcnt + (int64_t)b * parts_max + blockIdx.x, sh_scan);
-    }
-    if (HM == 2) {
-        __syncthreads();
-        // the cut bin bw: thread t owns bins 2047 - 8t .. 2040 - 8t (thread order = descending bins)
-        constexpr int PER = IX_BINS / (64 * IXM_WAVES);
-        const int top = IX_BINS - 1 - PER * tid;
-        uint32_t c[PER], local = 0u;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            c[j] = hs[top - j];
-            local += c[j];
-        }
-        uint32_t total;
-        const uint32_t before = block_excl_scan_dpp<IXM_WAVES>(local, sh_scan, &total);
-        if (before < (uint32_t)CAND_MIN && before + local >= (uint32_t)CAND_MIN) {
-            uint32_t cum = before;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                if (cum + c[j] >= (uint32_t)CAND_MIN) {
-                    s_cut[0] = (uint32_t)(top - j);
-                    s_cut[1] = cum;
-                    s_cut[2] = cum + c[j];
-                    break;
-                }
-                cum += c[j];
-            }
-        }
-        if (tid == 0) {
-            s_cut[3] = 0u;   // candidates taken
-            s_cut[4] = 0u;   // of them from bin bw, when bw does not fit whole
-            if (total < (uint32_t)CAND_MIN) s_cut[0] = 0u, s_cut[1] = 0u, s_cut[2] = total;
-        }
-        __syncthreads();
-        const bool all = total <= (uint32_t)CAND_CAP;
-        const uint32_t bw = all ? 0u : s_cut[0];
-        const bool full = all || s_cut[2] <= (uint32_t)CAND_CAP;
-        const uint32_t code = all ? 0u : (full ? bw : bw + 1u);
-        const uint32_t quota = (uint32_t)CAND_CAP - s_cut[1];   // bin bw's share when it does not fit whole
-        uint2 *cw = cand + ((int64_t)b * parts_max + blockIdx.x) * CAND_CAP;
-        int64_t tl = (int64_t)blockIdx.x * IXM_WAVES + wave;
-        for (int it = 0; tl < ntv; tl += waves_total, ++it) {
-            const int64_t t = tl * 64 + lane;
-            if (t >= n) continue;
-            const float sc = it < IX_CT ? ssc[(wave * IX_CT + it) * 64 + lane] : out[t];
-            const uint32_t key = order_key(sc), bin = key >> 21;
-            bool take = all || bin > bw || (bin == bw && full);
-            if (!take && bin == bw) take = atomicAdd(&s_cut[4], 1u) < quota;
-            if (take) {
-                const uint32_t at = atomicAdd(&s_cut[3], 1u);
-                cw[at] = make_uint2(key, (uint32_t)t);
-            }
-        }
-        __syncthreads();
-        if (tid == 0) hcnt[(int64_t)b * parts_max + blockIdx.x] = s_cut[3] | (code << 16);
     }
 }
 
@@ -379,13 +313,6 @@ static int64_t ixm_grid_x(int32_t B, int64_t t_max, bool tiled)
         if (bx > need) bx = need;
     }
     return bx < 1 ? 1 : bx;
-}
-
-int index_mfma_parts(int32_t B, int64_t t_max, int32_t n_ih, int32_t hd, const KvView &kv, const float *q)
-{
-    const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv.ic)) & 15u) == 0;
-    if (hd != 128 || n_ih != 32 || !aligned) return 0;
-    return (int)ixm_grid_x(B, t_max, kv.ic_tiled != 0);
 }
 
 int hist_parts_max(int32_t B, int64_t t_max)
@@ -417,19 +344,16 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
             hc = hist->hcnt;
             pm = hist->parts_max;
         }
-        uint2 *cd = hist ? hist->cand : nullptr;
         const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
 #define IX_LAUNCH(M, H, TL) \
-    hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, hl, hc, pm, cd)
-#define IX_LAUNCH3(M, TL) \
-    do { if (cd) IX_LAUNCH(M, 2, TL); else if (hist) IX_LAUNCH(M, 1, TL); else IX_LAUNCH(M, 0, TL); } while (0)
+    hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, hl, hc, pm)
+        const bool h = hist != nullptr;
         if (kv.ic_tiled) {
-            if (mode == 0) IX_LAUNCH3(0, true);
-            else IX_LAUNCH3(1, true);
-        } else if (mode == 0) IX_LAUNCH3(0, false);
-        else if (mode == 1) IX_LAUNCH3(1, false);
-        else IX_LAUNCH3(2, false);
-#undef IX_LAUNCH3
+            if (mode == 0) { if (h) IX_LAUNCH(0, true, true); else IX_LAUNCH(0, false, true); }
+            else { if (h) IX_LAUNCH(1, true, true); else IX_LAUNCH(1, false, true); }
+        } else if (mode == 0) { if (h) IX_LAUNCH(0, true, false); else IX_LAUNCH(0, false, false); }
+        else if (mode == 1) { if (h) IX_LAUNCH(1, true, false); else IX_LAUNCH(1, false, false); }
+        else { if (h) IX_LAUNCH(2, true, false); else IX_LAUNCH(2, false, false); }
 #undef IX_LAUNCH
         return check_launch("index_scores");
     } else if (hd == 128 && aligned)

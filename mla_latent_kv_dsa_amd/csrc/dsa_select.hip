@@ -466,9 +466,6 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
     resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
 }
 
-template <int NR>
-__device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbsorb &sa, int job, uint64_t *sr_dyn);
-
 // The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
 // work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
 // rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
@@ -488,16 +485,8 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
         resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
         return;
     }
-    side_absorb_job<NR>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
-}
-
-// Workgroup j (SR_NT threads) of the side work: two absorb jobs a = 2 j + half, (cb, h) = (a % 4,
-// a / 4); the cb == 0 job of head h also rotates that head's query tails.
-template <int NR>
-__device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbsorb &sa, int job, uint64_t *sr_dyn)
-{
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
-    const int a = 2 * job + half, cb = a & 3, h = a >> 2;
+    const int a = 2 * ((int)blockIdx.x - nres) + half, cb = a & 3, h = a >> 2;
     if (sa.B >= AB_MFMA_B) {
         absorb_block_mfma<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h,
                               reinterpret_cast<char *>(sr_dyn) + half * 16 * NR * AB_WROWB, jt);
@@ -519,240 +508,6 @@ __device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbso
     }
 }
 
-// ------------------------------------------------------------------------------ candidate selection
-// Behind the matrix-core indexer's candidate mode (dsa_index.hip): part p of a row listed its keys
-// at or above the bin of its CAND_MIN-th largest key (at most CAND_CAP), with a header count |
-// code << 16, code = 1 + the highest bin holding a key it left out (0: it left out none).  One
-// workgroup of SC_NT threads per row:
-//   1. loads every part's header and all 256 x CAND_CAP candidate slots at once (masked after);
-//   2. kth = the k-th largest order key among the candidates: three radix digits (bits 31..21,
-//      20..10, 9..0) on LDS histograms; `remaining` = how many keys equal to kth are kept;
-//   3. checks every part: a part that left out a key of a bin >= kth's bin may have left out a
-//      key of the true top-k.  Such parts are re-read whole from the scores (their keys in bins >=
-//      kth's bin replace their list).  Since the candidates are a subset of the row, the first kth
-//      is at most the row's true k-th key, so after this one re-read every key at or above the
-//      true k-th key is a candidate and step 2 once more gives the exact kth.  When the re-read
-//      keys exceed SC_AUG (massive ties), step 2 runs over the whole row from the scores instead;
-//   4. the kept positions: bits of keys > kth and the first `remaining` keys == kth in position
-//      order in LDS bitmasks, written out in ascending order (the same emission as the resolve).
-// The result is exactly that of the list-histogram selection and of dsa_topk_select.
-constexpr int SC_NT = SR_NT, SC_NW = SC_NT / 64;
-constexpr int SC_PARTS = 256;                              // parts per row read by the select
-constexpr int SC_SLOTS = SC_PARTS * CAND_CAP / SC_NT;     // candidate slots per thread
-constexpr int SC_AUG = 8192;                               // keys re-read from parts cut too high
-static_assert(SC_SLOTS <= 32, "slot mask is 32 bits");
-
-__device__ __forceinline__ void cand_select_row(int b, const KvView &kv, int k, int64_t t_max,
-                                                const float *__restrict__ scores, const uint2 *__restrict__ cand,
-                                                const uint32_t *__restrict__ chdr, int parts_max, int P,
-                                                int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
-                                                uint64_t *__restrict__ dyn, int wp)
-{
-    __shared__ uint32_t h[SEL_BINS];
-    __shared__ uint32_t sh[SC_NW];
-    __shared__ uint32_t s_hdr[SC_PARTS];
-    __shared__ uint32_t s_fail[SC_PARTS / 32];
-    __shared__ uint32_t s_bc[2], s_naug, s_over;
-    const int tid = threadIdx.x;
-    int64_t n = seq_len_of(kv, b);
-    if (n > t_max) n = t_max;
-    int32_t *out = sel + (int64_t)b * k;
-    if (n <= k) {   // every position is kept
-        for (int u = tid; u < k; u += SC_NT) out[u] = u < n ? u : -1;
-        if (tid == 0) nsel[b] = (int32_t)n;
-        return;
-    }
-    // 1. headers and every slot, issued before anything waits
-    const uint32_t hv = tid < P ? chdr[(int64_t)b * parts_max + tid] : 0u;
-    const uint2 *cb = cand + (int64_t)b * parts_max * CAND_CAP;
-    uint2 cv[SC_SLOTS];
-#pragma unroll
-    for (int j = 0; j < SC_SLOTS; ++j) {
-        const int i = tid + SC_NT * j, part = i / CAND_CAP;
-        cv[j] = cb[(int64_t)(part < P ? part : P - 1) * CAND_CAP + i % CAND_CAP];
-    }
-    if (tid < SC_PARTS) s_hdr[tid] = hv;
-    if (tid < SC_PARTS / 32) s_fail[tid] = 0u;
-    if (tid == 0) s_naug = 0u, s_over = 0u;
-    __syncthreads();
-    uint32_t vm = 0u, nv = 0u;   // valid slots (bit j)
-#pragma unroll
-    for (int j = 0; j < SC_SLOTS; ++j) {
-        const int i = tid + SC_NT * j, part = i / CAND_CAP;
-        if (part < P && (uint32_t)(i % CAND_CAP) < (s_hdr[part] & 0xFFFFu)) vm |= 1u << j, ++nv;
-    }
-    uint32_t total;
-    block_excl_scan_dpp<SC_NW>(nv, sh, &total);
-    uint64_t *keep = dyn, *eqm = dyn + wp;
-    uint2 *aug = reinterpret_cast<uint2 *>(dyn + 2 * wp);
-    const float *row = scores + (int64_t)b * t_max;
-    // src 0: the candidates (slots, then the re-read keys); src 1: every key of the row
-    auto for_each = [&](int src, auto f) {
-        if (src == 1) {
-            for (int64_t t = tid; t < n; t += SC_NT) f(order_key(row[t]), (uint32_t)t);
-            return;
-        }
-#pragma unroll
-        for (int j = 0; j < SC_SLOTS; ++j)
-            if ((vm >> j) & 1u) f(cv[j].x, cv[j].y);
-        const uint32_t na = s_naug < (uint32_t)SC_AUG ? s_naug : (uint32_t)SC_AUG;
-        for (uint32_t i = tid; i < na; i += SC_NT) f(aug[i].x, aug[i].y);
-    };
-    uint32_t kth = 0u, remaining = 0u;
-    auto kth_of = [&](int src) {
-        uint32_t prefix = 0u, mask = 0u, rem = (uint32_t)k;
-#pragma unroll 1
-        for (int p = 0; p < 3; ++p) {
-            const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
-            const int nb = p == 2 ? 1024 : 2048;
-            const uint32_t dm = (uint32_t)nb - 1u;
-#pragma unroll
-            for (int q = 0; q < SEL_BINS / SC_NT; ++q) h[tid + SC_NT * q] = 0u;
-            __syncthreads();
-            const uint32_t pf = prefix, mk = mask;
-            for_each(src, [&](uint32_t key, uint32_t) {
-                if ((key & mk) == pf) atomicAdd(&h[(key >> shift) & dm], 1u);
-            });
-            __syncthreads();
-            const int per = nb / SC_NT;   // 4 or 2 bins per thread, thread order = descending bins
-            const int top = nb - 1 - per * tid;
-            uint32_t hv4[4], local = 0u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                hv4[q] = q < per ? h[top - q] : 0u;
-                local += hv4[q];
-            }
-            const uint32_t before = block_excl_scan_dpp<SC_NW>(local, sh);
-            if (before < rem && before + local >= rem) {
-                uint32_t cum = before;
-                int bin = top;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (q < per && cum + hv4[q] >= rem) {
-                        bin = top - q;
-                        break;
-                    }
-                    cum += hv4[q];
-                }
-                s_bc[0] = rem - cum;
-                s_bc[1] = pf | ((uint32_t)bin << shift);
-            }
-            __syncthreads();
-            rem = s_bc[0];
-            prefix = s_bc[1];
-            mask |= dm << shift;
-        }
-        kth = prefix;
-        remaining = rem;
-    };
-    int src = total >= (uint32_t)k ? 0 : 1;
-    kth_of(src);
-    if (src == 0) {
-        // 3. parts that may have left out a key at or above the threshold
-        const uint32_t kb = kth >> 21;
-        const uint32_t code = s_hdr[tid < SC_PARTS ? tid : 0] >> 16;
-        const bool fail = tid < P && code != 0u && code - 1u >= kb;
-        if (fail) atomicOr(&s_fail[tid >> 5], 1u << (tid & 31));
-        if (__syncthreads_or(fail)) {
-#pragma unroll
-            for (int j = 0; j < SC_SLOTS; ++j) {
-                const int part = (tid + SC_NT * j) / CAND_CAP;
-                if (part < P && ((s_fail[part >> 5] >> (part & 31)) & 1u)) vm &= ~(1u << j);
-            }
-            const int64_t tiles_per_round = (int64_t)P * IX_WAVES_PER_PART;
-            for (int64_t t = tid; t < n; t += SC_NT) {
-                const int part = (int)(((t >> 6) % tiles_per_round) / IX_WAVES_PER_PART);
-                if (!((s_fail[part >> 5] >> (part & 31)) & 1u)) continue;
-                const uint32_t key = order_key(row[t]);
-                if ((key >> 21) < kb) continue;
-                const uint32_t at = atomicAdd(&s_naug, 1u);
-                if (at < (uint32_t)SC_AUG) aug[at] = make_uint2(key, (uint32_t)t);
-                else s_over = 1u;
-            }
-            __syncthreads();
-            if (s_over) src = 1;
-            kth_of(src);
-        }
-    }
-    // 4. the kept positions
-    for (int i = tid; i < wp; i += SC_NT) keep[i] = 0ull, eqm[i] = 0ull;
-    __syncthreads();
-    const uint32_t kt = kth;
-    for_each(src, [&](uint32_t key, uint32_t pos) {
-        if (key > kt) atomicOr(reinterpret_cast<unsigned long long *>(&keep[pos >> 6]), 1ull << (pos & 63));
-        else if (key == kt) atomicOr(reinterpret_cast<unsigned long long *>(&eqm[pos >> 6]), 1ull << (pos & 63));
-    });
-    __syncthreads();
-    const int wpt = wp / SC_NT;
-    uint64_t kw[SR_WPT], ew[SR_WPT];
-    uint32_t ec = 0u;
-#pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
-        kw[i] = i < wpt ? keep[tid * wpt + i] : 0ull;
-        ew[i] = i < wpt ? eqm[tid * wpt + i] : 0ull;
-        ec += (uint32_t)__popcll(ew[i]);
-    }
-    uint32_t erank = block_excl_scan_dpp<SC_NW>(ec, sh);   // equal keys before this run
-    uint32_t kc = 0u;
-#pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
-        uint64_t e = ew[i];
-        const uint32_t c = (uint32_t)__popcll(e);
-        if (erank >= remaining) e = 0ull;
-        else if (erank + c > remaining) {   // only the first remaining - erank of them
-            uint64_t take = 0ull;
-            for (uint32_t m = remaining - erank; m; --m) {
-                const uint64_t low = e & (~e + 1ull);
-                take |= low;
-                e ^= low;
-            }
-            e = take;
-        }
-        erank += c;
-        kw[i] |= e;
-        kc += (uint32_t)__popcll(kw[i]);
-    }
-    uint32_t o = block_excl_scan_dpp<SC_NW>(kc, sh);
-#pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
-        uint64_t x = kw[i];
-        const int base = 64 * (tid * wpt + i);
-        while (x) {
-            const int bit = __builtin_ctzll(x);
-            x &= x - 1ull;
-            if (o < (uint32_t)k) out[o] = base + bit;
-            ++o;
-        }
-    }
-    if (tid == 0) nsel[b] = k;
-}
-
-// grid (B [+ 2 * 64 side workgroups]), SC_NT threads, dynamic LDS 16 wp + 8 SC_AUG bytes
-__global__ __launch_bounds__(SC_NT) void sel_cand(KvView kv, int k, int64_t t_max, const float *__restrict__ scores,
-                                                  const uint2 *__restrict__ cand, const uint32_t *__restrict__ chdr,
-                                                  int parts_max, int P, int32_t *__restrict__ sel,
-                                                  int32_t *__restrict__ nsel, int wp)
-{
-    extern __shared__ uint64_t sr_dyn[];
-    cand_select_row(blockIdx.x, kv, k, t_max, scores, cand, chdr, parts_max, P, sel, nsel, sr_dyn, wp);
-}
-
-template <int NR>
-__global__ __launch_bounds__(SC_NT) void sel_cand_absorb(KvView kv, int k, int64_t t_max,
-                                                         const float *__restrict__ scores,
-                                                         const uint2 *__restrict__ cand,
-                                                         const uint32_t *__restrict__ chdr, int parts_max, int P,
-                                                         int32_t *__restrict__ sel, int32_t *__restrict__ nsel, int wp,
-                                                         int nres, SideAbsorb sa)
-{
-    extern __shared__ uint64_t sr_dyn[];
-    if ((int)blockIdx.x < nres) {
-        cand_select_row(blockIdx.x, kv, k, t_max, scores, cand, chdr, parts_max, P, sel, nsel, sr_dyn, wp);
-        return;
-    }
-    side_absorb_job<NR>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
-}
-
 // ------------------------------------------------------------------------------ host side
 struct SelWs {
     HistOut hist;
@@ -760,7 +515,6 @@ struct SelWs {
     SelRow *rows;
     uint64_t *keep;
     uint2 *cand;
-    uint2 *pcand;   // the indexer's candidate lists [B][parts_max][CAND_CAP]
     int64_t nch;
     int wp;
 };
@@ -787,8 +541,6 @@ static SelWs sel_ws(void *ws, int32_t B, int64_t t_max, size_t *bytes)
     w.rows = reinterpret_cast<SelRow *>(take((size_t)B * sizeof(SelRow)));
     w.keep = reinterpret_cast<uint64_t *>(take((size_t)B * w.wp * 8));
     w.cand = reinterpret_cast<uint2 *>(take((size_t)B * w.nch * SEL_CH * 8));
-    w.pcand = reinterpret_cast<uint2 *>(take((size_t)B * w.hist.parts_max * CAND_CAP * 8));
-    w.hist.cand = nullptr;
     if (bytes) *bytes = off;
     return w;
 }
@@ -805,15 +557,11 @@ static mla_status enable_sel_lds()
 {
     static bool done = false;
     if (!done) {
-        const void *f[8] = {reinterpret_cast<const void *>(&sel_resolve),
+        const void *f[4] = {reinterpret_cast<const void *>(&sel_resolve),
                             reinterpret_cast<const void *>(&sel_resolve_absorb<8>),
                             reinterpret_cast<const void *>(&sel_resolve_absorb<12>),
-                            reinterpret_cast<const void *>(&sel_resolve_absorb<16>),
-                            reinterpret_cast<const void *>(&sel_cand),
-                            reinterpret_cast<const void *>(&sel_cand_absorb<8>),
-                            reinterpret_cast<const void *>(&sel_cand_absorb<12>),
-                            reinterpret_cast<const void *>(&sel_cand_absorb<16>)};
-        for (int i = 0; i < 8; ++i) {
+                            reinterpret_cast<const void *>(&sel_resolve_absorb<16>)};
+        for (int i = 0; i < 4; ++i) {
             const hipError_t e = hipFuncSetAttribute(f[i], hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
             if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         }
@@ -838,38 +586,6 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     st = enable_sel_lds();
     if (st) return st;
     SelWs sw = sel_ws(ws, B, t_max, nullptr);
-    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
-                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
-    const size_t dyn_abs = !with_side ? 0
-                           : (B >= AB_MFMA_B ? 2 * (size_t)side->nope * AB_WROWB
-                                             : 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4);
-    // the candidate selection, when the matrix-core indexer's parts can cover k several times over
-    const int P = index_mfma_parts(B, t_max, n_ih, hd, kv, q);
-    if (t_max > 0 && P > 0 && P <= SC_PARTS && (int64_t)P * CAND_MIN >= 4 * (int64_t)k) {
-        sw.hist.cand = sw.pcand;
-        st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, &sw.hist, s);
-        if (st) return st;
-        const size_t dyn_c = (size_t)sw.wp * 16 + (size_t)SC_AUG * 8;
-        const size_t dyn = dyn_c > dyn_abs ? dyn_c : dyn_abs;
-        if (dyn > (size_t)SR_DYN_MAX) return fail(MLA_ERR_UNSUPPORTED, "select: candidate selection LDS");
-        if (!with_side) {
-            hipLaunchKernelGGL(sel_cand, dim3(B), dim3(SC_NT), dyn, s, kv, k, t_max, scores, sw.pcand, sw.hist.hcnt,
-                               sw.hist.parts_max, sw.hist.parts, sel, nsel, sw.wp);
-            return check_launch("sel_cand");
-        }
-        const dim3 g((unsigned)(B + 2 * AB_H));
-#define SCA_LAUNCH(NR)                                                                                               \
-    hipLaunchKernelGGL(sel_cand_absorb<NR>, g, dim3(SC_NT), dyn, s, kv, k, t_max, scores, sw.pcand, sw.hist.hcnt,  \
-                       sw.hist.parts_max, sw.hist.parts, sel, nsel, sw.wp, B, *side)
-        if (side->nope == 128) SCA_LAUNCH(8);
-        else if (side->nope == 192) SCA_LAUNCH(12);
-        else SCA_LAUNCH(16);
-#undef SCA_LAUNCH
-        st = check_launch("sel_cand_absorb");
-        if (st) return st;
-        if (side_done) *side_done = true;
-        return MLA_OK;
-    }
     if (t_max > 0) {
         st = launch_index_scores(q, w, B, n_ih, hd, kv, t_max, scores, &sw.hist, s);
         if (st) return st;
@@ -890,11 +606,15 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     // the bitmasks, then room for staged overflow candidates (at least 64 KB or what is left)
     const size_t dyn_masks = (size_t)sw.wp * 16;
     const size_t dyn_sel = dyn_masks + 65536 < (size_t)SR_DYN_MAX ? dyn_masks + 65536 : (size_t)SR_DYN_MAX;
+    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
+                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
     if (!with_side) {
         hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
                            sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
         return check_launch("sel_resolve");
     }
+    const size_t dyn_abs = B >= AB_MFMA_B ? 2 * (size_t)side->nope * AB_WROWB
+                                          : 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
     const dim3 g((unsigned)(B + 2 * AB_H));
 #define SRA_LAUNCH(NR)                                                                                              \

@@ -326,7 +326,7 @@ def test_index_select_deep_histogram_parts(tiled):
 
 
 def _cand_case(seed, B, T, window=None, repeat=1, equal=False):
-    """Tiled indexer pool at full context (the matrix-core indexer's candidate selection: 256 parts).
+    """Tiled indexer pool at full context (256 indexer workgroups per row).
     window: (start, length, factor) scales a block of key rows so the top keys crowd into a few
     parts; repeat: every row repeated so that equal scores come in groups; equal: all rows equal."""
     rng = np.random.default_rng(seed)
@@ -345,33 +345,32 @@ def _cand_case(seed, B, T, window=None, repeat=1, equal=False):
 
 
 @pytest.mark.parametrize("case", ["random", "window", "wide_window", "repeats", "all_equal"])
-def test_index_select_candidate_path(case):
-    """The candidate selection behind the tiled matrix-core indexer at T = 131072 (k = 2048), on every
-    branch: random scores (each part's list covers it), the top keys crowded into a 4096- or
-    12288-key window (the parts holding it are cut above the threshold and re-read), every score
-    repeated 16 times (equal keys at the threshold), and all scores equal (the re-read overflows:
-    the whole row is selected from the scores).  Bit-exact against the stand-alone top-k and the
-    oracle's sort."""
+def test_index_select_score_patterns(case):
+    """The selection behind the tiled matrix-core indexer at T = 131072 (k = 2048) on score patterns
+    that load its passes differently: random scores, the top keys crowded into a 4096- or 12288-key
+    window (a few indexer workgroups hold them all), every score repeated 16 times (equal keys at
+    the threshold) and all scores equal.  Bit-exact against the stand-alone top-k and the oracle's
+    sort."""
     B, T, k = 1, 131072, 2048
     kw = {"random": {}, "window": dict(window=(40000, 4096, 3.0)), "wide_window": dict(window=(70000, 12288, 2.0)),
           "repeats": dict(repeat=16), "all_equal": dict(equal=True)}[case]
     q, w, ic = _cand_case(300 + len(case), B, T, **kw)
     z = np.zeros((B * T, 8), np.uint16)
-    log(f"index+select candidate path: {case}")
+    log(f"index+select score pattern: {case}")
     kv = _kv(z, z, ic, [T], T, seq_stride=T, tiled=True)
     sel, nsel = _select_check(q, w, kv, T, k, [T])
     if case == "all_equal":
         assert np.array_equal(sel[0], np.arange(k))
 
 
-def test_index_select_candidate_path_batched():
-    """Three rows of different lengths on the candidate selection (parts past a row's end list
-    nothing; a row just over k and one under it)."""
+def test_index_select_batched_full_context_window():
+    """Three rows of different lengths at full context (workgroups past a row's end write empty
+    lists; a row just over k and one under it), the top keys crowded into a window."""
     B, T, k = 3, 131072, 2048
     q, w, ic = _cand_case(330, B, T, window=(100000, 2048, 2.5))
     seq = [T, 2100, 1500]
     z = np.zeros((B * T, 8), np.uint16)
-    log("index+select candidate path batched")
+    log("index+select batched full context")
     kv = _kv(z, z, ic, seq, T, seq_stride=T, tiled=True)
     _select_check(q, w, kv, T, k, seq)
 
