@@ -250,6 +250,9 @@ struct SideAbsorb {
     int B, nope, v, rope;
     double theta;
 };
+// The side work as a launch of its own (when no selection runs beside it)
+bool side_absorb_ok(const SideAbsorb &sa);
+mla_status launch_absorb_rope(const SideAbsorb &sa, const KvView &kv, hipStream_t s);
 mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
                                int64_t t_max, int32_t k, float *scores, int32_t *sel, int32_t *nsel, void *ws,
                                size_t ws_bytes, hipStream_t s,

@@ -169,7 +169,28 @@ mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype d
     char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
     void *dec_ws = p;
     void *qr = p + al256(decode_workspace_bytes(d, B, k, dt));
-    mla_status st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv, theta, s);
+    mla_status st;
+    if (use_mfma(d, dt)) {
+        st = need_aligned("shared decode", {q_nope, q_rope, kv_b, kv.lc, kv.rc});
+        if (st) return st;
+        SideAbsorb sa;   // the absorption and the query rotation in one launch
+        sa.q_nope = (const bf16_t *)q_nope;
+        sa.kv_b = (const bf16_t *)kv_b;
+        sa.q_abs = decode_mfma_qabs(dec_ws);
+        sa.q_rope = (const bf16_t *)q_rope;
+        sa.q_rope_out = (bf16_t *)qr;
+        sa.B = B;
+        sa.nope = d.qk_nope;
+        sa.v = d.v_head;
+        sa.rope = d.qk_rope;
+        sa.theta = theta;
+        if (side_absorb_ok(sa)) {
+            st = launch_absorb_rope(sa, kv, s);
+            if (st) return st;
+            return launch_attend_mfma(qr, kv_b, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s);
+        }
+    }
+    st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv, theta, s);
     if (st) return st;
     return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
 }

@@ -466,27 +466,14 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
     resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
 }
 
-// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
-// work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
-// rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
-// grid (nres + 2 * 64): workgroups nres.. run two absorb jobs a = 2 (blockIdx - nres) + half,
-// (cb, h) = (a % 4, a / 4), one per 256 threads; the cb == 0 job of head h also rotates that
-// head's query tails.
+// Side job j (SR_NT threads): two absorb jobs a = 2 j + half, (cb, h) = (a % 4, a / 4), one per 256
+// threads; the cb == 0 job of head h also rotates that head's query tails at each row's query
+// position seq_len - 1 (into a separate buffer).
 template <int NR>
-__global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
-                                                            const uint32_t *__restrict__ fcnt, int nch,
-                                                            const uint64_t *__restrict__ gkeep, int wp,
-                                                            const SelRow *__restrict__ rows,
-                                                            int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
-                                                            int nres, SideAbsorb sa, int ov_cap)
+__device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbsorb &sa, int job, uint64_t *sr_dyn)
 {
-    extern __shared__ uint64_t sr_dyn[];
-    if ((int)blockIdx.x < nres) {
-        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
-        return;
-    }
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
-    const int a = 2 * ((int)blockIdx.x - nres) + half, cb = a & 3, h = a >> 2;
+    const int a = 2 * job + half, cb = a & 3, h = a >> 2;
     if (sa.B >= AB_MFMA_B) {
         absorb_block_mfma<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h,
                               reinterpret_cast<char *>(sr_dyn) + half * 16 * NR * AB_WROWB, jt);
@@ -506,6 +493,68 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
         y[j] = f2bf(lo);
         y[hr + j] = f2bf(hi);
     }
+}
+
+// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
+// work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
+// rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
+// grid (nres + 2 * 64): workgroups nres.. run two absorb jobs a = 2 (blockIdx - nres) + half,
+// (cb, h) = (a % 4, a / 4), one per 256 threads; the cb == 0 job of head h also rotates that
+// head's query tails.
+template <int NR>
+__global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
+                                                            const uint32_t *__restrict__ fcnt, int nch,
+                                                            const uint64_t *__restrict__ gkeep, int wp,
+                                                            const SelRow *__restrict__ rows,
+                                                            int32_t *__restrict__ sel, int32_t *__restrict__ nsel,
+                                                            int nres, SideAbsorb sa, int ov_cap)
+{
+    extern __shared__ uint64_t sr_dyn[];
+    if ((int)blockIdx.x < nres) {
+        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
+        return;
+    }
+    side_absorb_job<NR>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
+}
+
+// The same side work as a launch of its own (2 * 64 workgroups of SR_NT threads), for decode steps
+// whose selection is given: the shared layer.
+template <int NR>
+__global__ __launch_bounds__(SR_NT) void absorb_rope(KvView kv, SideAbsorb sa)
+{
+    extern __shared__ uint64_t sr_dyn[];
+    side_absorb_job<NR>(kv, sa, blockIdx.x, sr_dyn);
+}
+
+static size_t side_lds(const SideAbsorb &sa)
+{
+    return sa.B >= AB_MFMA_B ? 2 * (size_t)sa.nope * AB_WROWB : 2 * ((size_t)sa.B * sa.nope + 4 * AB_QB * 128) * 4;
+}
+
+bool side_absorb_ok(const SideAbsorb &sa)
+{
+    return sa.B <= SIDE_MAXB && (sa.nope == 128 || sa.nope == 192 || sa.nope == 256);
+}
+
+mla_status launch_absorb_rope(const SideAbsorb &sa, const KvView &kv, hipStream_t s)
+{
+    static bool attr = false;
+    if (!attr) {
+        const void *f[3] = {reinterpret_cast<const void *>(&absorb_rope<8>),
+                            reinterpret_cast<const void *>(&absorb_rope<12>),
+                            reinterpret_cast<const void *>(&absorb_rope<16>)};
+        for (int i = 0; i < 3; ++i) {
+            const hipError_t e = hipFuncSetAttribute(f[i], hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+            if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+        }
+        attr = true;
+    }
+    const size_t dyn = side_lds(sa);
+    const dim3 g(2 * AB_H);
+    if (sa.nope == 128) hipLaunchKernelGGL(absorb_rope<8>, g, dim3(SR_NT), dyn, s, kv, sa);
+    else if (sa.nope == 192) hipLaunchKernelGGL(absorb_rope<12>, g, dim3(SR_NT), dyn, s, kv, sa);
+    else hipLaunchKernelGGL(absorb_rope<16>, g, dim3(SR_NT), dyn, s, kv, sa);
+    return check_launch("absorb_rope");
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -606,15 +655,13 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     // the bitmasks, then room for staged overflow candidates (at least 64 KB or what is left)
     const size_t dyn_masks = (size_t)sw.wp * 16;
     const size_t dyn_sel = dyn_masks + 65536 < (size_t)SR_DYN_MAX ? dyn_masks + 65536 : (size_t)SR_DYN_MAX;
-    const bool with_side = side && side->B == B && B <= SIDE_MAXB &&
-                           (side->nope == 128 || side->nope == 192 || side->nope == 256);
+    const bool with_side = side && side->B == B && side_absorb_ok(*side);
     if (!with_side) {
         hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
                            sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
         return check_launch("sel_resolve");
     }
-    const size_t dyn_abs = B >= AB_MFMA_B ? 2 * (size_t)side->nope * AB_WROWB
-                                          : 2 * ((size_t)B * side->nope + 4 * AB_QB * 128) * 4;
+    const size_t dyn_abs = side_lds(*side);
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
     const dim3 g((unsigned)(B + 2 * AB_H));
 #define SRA_LAUNCH(NR)                                                                                              \
