@@ -141,7 +141,8 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 // ONE: every split fits in one staged chunk (kps <= DC_SUP * DC_KC); the chunk's selection entries
 // are then requested before the query operands, so resolving them into cache rows waits for
 // nothing else (loads complete in issue order).
-template <bool ONE>
+// PB16: the split outputs are stored as bf16 (for combine_one), else fp32.
+template <bool ONE, bool PB16 = false>
 __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs, const bf16_t *__restrict__ q_rope,
                                                 KvView kv, const int32_t *__restrict__ sel,
                                                 const int32_t *__restrict__ nsel, int sel_stride, float scale_log2,
@@ -303,11 +304,20 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
         __syncthreads();   // the staged rows are no longer read
         if (ONE) break;
     }
-    float *po = o_part + (((int64_t)b * NS + s) * DM_H + h0 + 4 * quad) * DM_L + 128 * wave + jj;
+    const int64_t po0 = (((int64_t)b * NS + s) * DM_H + h0 + 4 * quad) * DM_L + 128 * wave + jj;
+    if (PB16) {
+        bf16_t *po = reinterpret_cast<bf16_t *>(o_part) + po0;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = acc[ct][r];
+            for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = f2bf(acc[ct][r]);
+    } else {
+        float *po = o_part + po0;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) po[(int64_t)r * DM_L + 16 * ct] = acc[ct][r];
+    }
     if (wave == 0 && quad == 0) {
         m_part[((int64_t)b * NS + s) * DM_H + h] = m_run;
         l_part[((int64_t)b * NS + s) * DM_H + h] = l_run;
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(256) void unabsorb(const bf16_t *__restrict__ clat,
 constexpr int C1_ROWS = 128;
 constexpr size_t C1_LDS = (size_t)(C1_ROWS * CU_WROW + 16 * CU_ROW) * 2 + (size_t)CU_MAXNS * 4;
 
-template <int SB>   // splits held per thread, NS <= SB
+template <int SB, bool PB16 = false>   // splits held per thread, NS <= SB; PB16: bf16 split outputs
 __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_part, const float *__restrict__ m_part,
                                                    const float *__restrict__ l_part, int NS,
                                                    const bf16_t *__restrict__ kv_b, int nope, int v,
@@ -862,7 +872,13 @@ __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_p
 #pragma unroll
         for (int u = 0; u < SB; ++u) {   // unconditional loads, the split clamped into range
             const int uc = u < NS ? u : NS - 1;
-            x[u] = *reinterpret_cast<const float2 *>(o_part + ((int64_t)uc * DM_H + h) * DM_L + 2 * tid);
+            if (PB16) {
+                const uint32_t pv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const bf16_t *>(o_part) +
+                                                                         ((int64_t)uc * DM_H + h) * DM_L + 2 * tid);
+                x[u] = make_float2(__uint_as_float(pv << 16), __uint_as_float(pv & 0xffff0000u));
+            } else {
+                x[u] = *reinterpret_cast<const float2 *>(o_part + ((int64_t)uc * DM_H + h) * DM_L + 2 * tid);
+            }
         }
         if (wave == 0) {
             const float mm = lane < NS ? m : -INFINITY;
@@ -937,6 +953,12 @@ static mla_status enable_big_lds()
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<true>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
         if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<true, true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<false, true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
+        if (e == hipSuccess)
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dec_core<false>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DC_LDS);
         if (e == hipSuccess)
@@ -953,10 +975,13 @@ static mla_status enable_big_lds()
                              reinterpret_cast<const void *>(&combine_unabsorb<4, 16>)};
         for (int i = 0; i < 4 && e == hipSuccess; ++i)
             e = hipFuncSetAttribute(cu[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)CU_LDS);
-        const void *c1[3] = {reinterpret_cast<const void *>(&combine_one<16>),
+        const void *c1[6] = {reinterpret_cast<const void *>(&combine_one<16>),
                              reinterpret_cast<const void *>(&combine_one<32>),
-                             reinterpret_cast<const void *>(&combine_one<64>)};
-        for (int i = 0; i < 3 && e == hipSuccess; ++i)
+                             reinterpret_cast<const void *>(&combine_one<64>),
+                             reinterpret_cast<const void *>(&combine_one<16, true>),
+                             reinterpret_cast<const void *>(&combine_one<32, true>),
+                             reinterpret_cast<const void *>(&combine_one<64, true>)};
+        for (int i = 0; i < 6 && e == hipSuccess; ++i)
             e = hipFuncSetAttribute(c1[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)C1_LDS);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
@@ -1057,10 +1082,20 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     if (st) return st;
     // the W_UV slice when the decode leaves at least as many CUs idle
     const int pf = (int64_t)B * p.ns * (DM_H / 16) <= 128 ? 1 : 0;
+    // one query: the split outputs go to combine_one as bf16 (half the bytes each way)
+    const bool one_b16 = B == 1 && d.v_head % C1_ROWS == 0;
     const bf16_t *wuv = (const bf16_t *)kv_b + (int64_t)d.qk_nope * DM_L;
     if (B >= MH_MIN_B)
         hipLaunchKernelGGL(dec_core_mh, dim3(p.ns, B), dim3(256), MH_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv, sel,
                            nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
+    else if (one_b16 && p.kps <= DC_SUP * DC_KC)
+        hipLaunchKernelGGL((dec_core<true, true>), dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+    else if (one_b16)
+        hipLaunchKernelGGL((dec_core<false, true>), dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
+                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
+                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
     else if (p.kps <= DC_SUP * DC_KC)
         hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
@@ -1085,14 +1120,14 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     if (B == 1 && d.v_head % C1_ROWS == 0) {
         const dim3 g1(d.v_head / C1_ROWS, DM_H);
         if (p.ns <= 16)
-            hipLaunchKernelGGL(combine_one<16>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
-                               d.qk_nope, d.v_head, out);
+            hipLaunchKernelGGL((combine_one<16, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                               kb, d.qk_nope, d.v_head, out);
         else if (p.ns <= 32)
-            hipLaunchKernelGGL(combine_one<32>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
-                               d.qk_nope, d.v_head, out);
+            hipLaunchKernelGGL((combine_one<32, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                               kb, d.qk_nope, d.v_head, out);
         else
-            hipLaunchKernelGGL(combine_one<64>, g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, kb,
-                               d.qk_nope, d.v_head, out);
+            hipLaunchKernelGGL((combine_one<64, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
+                               kb, d.qk_nope, d.v_head, out);
     } else if (B == 1 && p.ns <= 16)
         hipLaunchKernelGGL((combine_unabsorb<1, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
                            kb, B, d.qk_nope, d.v_head, out);
