@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MLA+DSA decode keys·heads/sec at T=128k; achieved HBM GB/s vs peak"
+IDX_KERNEL = "index_scores_mfma<0, false"   # the stand-alone indexer (no selection histogram)
 
 
 def _src_hash(path):
@@ -37,23 +38,39 @@ def _src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel_key: str, src: str, per_launch_algo_bytes: float):
-    """HBM traffic per launch from the committed counter summary, if it was taken on the
-    current source of the kernel; otherwise None."""
-    p = os.path.join(ROOT, "profiles", f"{kernel_key}.counters.txt")
+def _traffic(counters_name: str, kernel: str):
+    """HBM bytes per launch of one kernel (read + write, calibrated) from the committed counter
+    summary, if the summary was taken on the current source of the kernel's file; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"{counters_name}.counters.txt")
     if not os.path.exists(p):
         return None
-    kv = {}
+    sec, kv = None, {}
     for line in open(p):
-        m = re.match(r"^(\w+)\s*=\s*(\S+)", line.strip())
-        if m:
+        line = line.strip()
+        if line.startswith("[") and line.endswith("]"):
+            sec = line[1:-1]
+            continue
+        m = re.match(r"^(\w+)\s*=\s*(\S+)", line)
+        if m and sec == kernel:
             kv[m.group(1)] = m.group(2)
-    if kv.get("source_sha256_16") != _src_hash(src):
+    src = kv.get("source")
+    if not src or kv.get("source_sha256_16") != _src_hash(os.path.join(ROOT, src)):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_read_bytes_per_launch"]) + float(kv["hbm_write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _kernel_source(kernel: str):
+    """The library source file that defines a kernel (name up to its template arguments)."""
+    base = kernel.split("<")[0].split("(")[0].strip()
+    csrc = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith(".hip") and re.search(r"void\s+" + re.escape(base) + r"\s*\(",
+                                            open(os.path.join(csrc, f)).read()):
+            return os.path.join("mla_latent_kv_dsa_amd", "csrc", f)
+    return None
 
 
 def _events(torch, n):
@@ -255,8 +272,7 @@ def bench_dsa_decode(args):
     step_bytes = ic_bytes + sel_kv_bytes + kvb_bytes + score_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
     stream_bytes = ic_bytes + sel_kv_bytes
     stream_us = ms_step * 1e3   # the fused step: indexer, selection and attention (RoPE and absorb hidden)
-    src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", "dsa_index.hip")
-    traffic = _traffic("dsa_index_scores_T131072", src, idx_bytes)
+    traffic = _traffic("dsa_decode_T131072_B1", IDX_KERNEL)
 
     cpu = None
     if not args.no_cpu:
@@ -277,11 +293,15 @@ def bench_dsa_decode(args):
                    "topk": K, "kv_dtype": "bf16", "index_dtype": "fp32", "index_layout": "tile64",
                    "input_copies": args.copies,
                    "hip_graphs": bool(graphs), "steps_per_graph_replay": len(copies) if graphs else 0},
-        "roofline": {"kernel": "index_scores_mfma (dsa_index_scores; the step runs the same kernel with the "
-                               "selection histogram added, inside dsa_index_select)",
+        "roofline": {"kernel": IDX_KERNEL + " (dsa_index_scores; the step runs the same kernel with the "
+                               "selection histogram added)",
                      "bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": idx_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": idx_bytes, "avg_us": us["index"]},
+                     "algorithmic_bytes": idx_bytes, "avg_us": us["index"],
+                     # the whole step against the same peak: the bytes that must stream (Ic and the
+                     # selected latent rows) over the fused step's time
+                     "stream_over_step": {"bytes": stream_bytes, "us": stream_us,
+                                          "frac": stream_bytes / (stream_us * 1e-6) / 1e9 / HBM_PEAK_GBS}},
         "cpu_baseline": cpu,
         "breakdown_us": us,
         "stream": {"bytes": stream_bytes, "us_step": stream_us,
@@ -690,12 +710,18 @@ def measure_prefill(args, cpu=True):
            "TFLOPs": tf,
            "roofline": {"kernel": "pf_kvb + pf_attn (the whole mla_prefill_nonabsorbed call)", "bound": "mfma",
                         "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
-                        "traffic": None, "algorithmic_flops": flops, "flops_kv_b_gemm": f_kvb,
+                        "traffic": _prefill_traffic(), "algorithmic_flops": flops, "flops_kv_b_gemm": f_kvb,
                         "flops_attention": f_attn},
            "data": "synthetic: numpy seed 4"}
     if cpu:
         res["cpu_baseline"] = cpu_baseline_prefill(p, sm)
     return res
+
+
+def _prefill_traffic():
+    """HBM bytes of one prefill call (kv_b GEMM + attention) from the committed counters."""
+    t = [_traffic("prefill_S4096", k) for k in ("pf_kvb", "pf_attn")]
+    return None if None in t else sum(t)
 
 
 def cpu_baseline_prefill(p, sm):
@@ -763,53 +789,6 @@ def bench_copy(args):
         ms = e0.elapsed_time(e1) / args.steps
         res[name] = {"ms": ms, "GBs": 2 * n * 4 / (ms * 1e-3) / 1e9}
     print(json.dumps({"workload": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "kernels": res}), flush=True)
-
-
-def _counter_means(csv_path, kernel_substr):
-    """Mean value per dispatch of every counter in a rocprofv3 counter_collection.csv, over
-    the dispatches whose kernel name contains kernel_substr."""
-    import csv
-    from collections import defaultdict
-
-    acc = defaultdict(lambda: defaultdict(float))
-    for r in csv.DictReader(open(csv_path)):
-        if kernel_substr in r["Kernel_Name"]:
-            acc[r["Counter_Name"]][r.get("Dispatch_Id") or r.get("Correlation_Id")] += float(r["Counter_Value"])
-    return {k: (statistics.mean(v.values()), len(v)) for k, v in acc.items()}
-
-
-def summarize_counters(args):
-    """Write profiles/<name>.counters.txt from four rocprofv3 --pmc runs (FETCH_SIZE and
-    WRITE_SIZE, each for the kernel's workload and for the calibration copy)."""
-    d = args.counters_dir
-    find = lambda sub: next(os.path.join(r, f) for r, _, fs in os.walk(os.path.join(d, sub)) for f in fs
-                            if f.endswith("counter_collection.csv"))
-    copy_bytes = COPY_MIB * 2**20
-    cf, _ = _counter_means(find("copy_fetch"), "copyBuffer")["FETCH_SIZE"]
-    cw, _ = _counter_means(find("copy_write"), "copyBuffer")["WRITE_SIZE"]
-    ef, _ = _counter_means(find("copy_fetch"), "elementwise")["FETCH_SIZE"]
-    ew, _ = _counter_means(find("copy_write"), "elementwise")["WRITE_SIZE"]
-    kf, nf = _counter_means(find("kernel_fetch"), args.kernel)["FETCH_SIZE"]
-    kw, nw = _counter_means(find("kernel_write"), args.kernel)["WRITE_SIZE"]
-    f_fetch, f_write = copy_bytes / cf, copy_bytes / cw          # bytes per counter unit
-    hbm = kf * f_fetch + kw * f_write
-    src = os.path.join(ROOT, "mla_latent_kv_dsa_amd", "csrc", args.kernel_src)
-    out = os.path.join(ROOT, "profiles", f"{args.counters_name}.counters.txt")
-    with open(out, "w") as fo:
-        fo.write(f"# HBM traffic of {args.kernel} per launch, from rocprofv3 --pmc counters\n")
-        fo.write(f"# kernel runs : rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                 f"python3 bench.py {args.counters_cmd}\n")
-        fo.write(f"# calibration : rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                 f"python3 bench.py --workload copy --steps 5 --warmup 1   ({COPY_MIB} MiB read + written)\n")
-        fo.write(f"copy_FETCH_SIZE_per_dispatch = {cf:.1f}\ncopy_WRITE_SIZE_per_dispatch = {cw:.1f}\n")
-        fo.write(f"# cross-check, elementwise kernel over the same buffers: FETCH_SIZE {ef:.1f}, WRITE_SIZE {ew:.1f}\n")
-        fo.write(f"fetch_bytes_per_unit = {f_fetch:.4f}\nwrite_bytes_per_unit = {f_write:.4f}\n")
-        fo.write(f"kernel_dispatches = {nf}/{nw}\n")
-        fo.write(f"kernel_FETCH_SIZE_per_dispatch = {kf:.1f}\nkernel_WRITE_SIZE_per_dispatch = {kw:.1f}\n")
-        fo.write(f"fetch_bytes_per_launch = {kf * f_fetch:.0f}\nwrite_bytes_per_launch = {kw * f_write:.0f}\n")
-        fo.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
-        fo.write(f"source = {os.path.relpath(src, ROOT)}\nsource_sha256_16 = {_src_hash(src)}\n")
-    print(open(out).read())
 
 
 def _pmc_rows(csv_path):
@@ -881,6 +860,9 @@ def summarize_pmc(args):
                 fo.write(f"hbm_read_bytes_per_launch = {f[0] * fetch_unit:.0f}\n")
             if w and write_unit:
                 fo.write(f"hbm_write_bytes_per_launch = {w[0] * write_unit:.0f}\n")
+            src = _kernel_source(k)
+            if src:
+                fo.write(f"source = {src}\nsource_sha256_16 = {_src_hash(os.path.join(ROOT, src))}\n")
     print(open(out).read())
 
 
@@ -913,10 +895,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batched paged and dense decode configurations (profiling runs of the headline step)")
-    ap.add_argument("--counters-dir", help="summarize rocprofv3 --pmc runs found in this directory and exit")
-    ap.add_argument("--kernel", default="index_scores_mfma")
-    ap.add_argument("--kernel-src", default="dsa_index.hip")
-    ap.add_argument("--counters-name", default="dsa_index_scores_T131072")
+    ap.add_argument("--counters-name", default="dsa_decode_T131072_B1")
     ap.add_argument("--counters-cmd", default="--steps 5 --warmup 1 --no-cpu --no-extra")
     ap.add_argument("--pmc-dirs", help="summarize rocprofv3 --pmc passes (comma-separated directories) and exit")
     ap.add_argument("--pmc-kernels", default="index_scores_mfma", help="'|'-separated kernel name substrings")
@@ -929,9 +908,6 @@ def main():
     args = ap.parse_args()
     if args.stats_csv:
         summarize_trace(args)
-        return
-    if args.counters_dir:
-        summarize_counters(args)
         return
     if args.pmc_dirs:
         summarize_pmc(args)
