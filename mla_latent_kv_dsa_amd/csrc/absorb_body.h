@@ -14,24 +14,27 @@
 // wave, then across the four waves through LDS in a fixed order (fp32 FMA, bf16 out).
 #pragma once
 #include "common.h"
+#include "qformat.h"
 
 namespace mla {
 
 constexpr int AB_L = 512, AB_H = 64;
 constexpr int AB_QB = 8;
 
-template <int NR>   // qk_nope / 16
-__device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, const bf16_t *__restrict__ kv_b,
-                                             int B, int v, bf16_t *__restrict__ q_abs, int cb, int h,
-                                             float *__restrict__ sh_abs, int tid)
+// FMT: 0 for the bf16 kv_b, else its quantized format (qformat.h; kv_b then holds the codes and
+// scales their scales).
+template <int NR, int FMT = 0>   // qk_nope / 16
+__device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, const void *__restrict__ kv_b,
+                                             const void *__restrict__ scales, int B, int v, bf16_t *__restrict__ q_abs,
+                                             int cb, int h, float *__restrict__ sh_abs, int tid)
 {
     constexpr int nope = 16 * NR;
     const int rg = tid >> 4, cg = tid & 15, lane = tid & 63, wave = tid >> 6;
     const int cbase = cb * 128;
-    const bf16_t *W = kv_b + ((int64_t)h * (nope + v) + rg) * AB_L + cbase + cg * 8;
-    uint4 w[NR];
+    const int64_t row0 = (int64_t)h * (nope + v) + rg;
+    QRaw8<FMT> raw[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) w[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)k * 16 * AB_L);
+    for (int k = 0; k < NR; ++k) raw[k] = q_raw8<FMT>(kv_b, scales, row0 + 16 * k, AB_L, cbase + cg * 8);
     float *sq = sh_abs;
     float *red = sh_abs + B * nope;
     for (int i = tid; i < B * nope; i += 256) {
@@ -39,6 +42,12 @@ __device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, 
         sq[i] = bf2f(q_nope[((int64_t)b * AB_H + h) * nope + r]);
     }
     __syncthreads();
+    // the weights as exact bf16 values and a factor per row (the row scale of the byte formats,
+    // applied to the query element instead of every weight)
+    uint4 w[NR];
+    float wsc[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) q_bf16x8<FMT>(raw[k], w[k], wsc[k]);
     for (int b0 = 0; b0 < B; b0 += AB_QB) {
         const int nb = B - b0 < AB_QB ? B - b0 : AB_QB;
         float acc[AB_QB][8];
@@ -56,7 +65,9 @@ __device__ __forceinline__ void absorb_block(const bf16_t *__restrict__ q_nope, 
 #pragma unroll
             for (int q = 0; q < AB_QB; ++q) {
                 if (q < nb) {
-                    const float qv = sq[(b0 + q) * nope + rg + 16 * k];
+                    const float qv = (FMT == MLA_Q_FP8_E4M3 || FMT == MLA_Q_INT8)
+                                         ? sq[(b0 + q) * nope + rg + 16 * k] * wsc[k]
+                                         : sq[(b0 + q) * nope + rg + 16 * k];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(qv, wf[e], acc[q][e]);
                 }

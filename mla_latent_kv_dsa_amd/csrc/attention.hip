@@ -48,21 +48,55 @@ __global__ __launch_bounds__(256) void split_q_kernel(const E *__restrict__ q, E
     else qr[u * rope + (c - nope)] = q[e];
 }
 
-// Key bitmap of the selections: column i (query i), word g holds keys 32 g .. 32 g + 31.  One
-// workgroup per column clears it, then sets the bits of the query's kept positions in [0, T).
-__global__ __launch_bounds__(256) void sel_mask_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ nsel,
-                                                       int sel_stride, int S, int64_t T, int64_t groups, int64_t cols,
-                                                       uint32_t *__restrict__ mask)
+// Key bitmap of the selections: column i (query i), word g holds keys 32 g .. 32 g + 31.  Workgroup
+// (c, r) builds the words g in [MASK_GCH r, MASK_GCH (r + 1)) of the MASK_QB columns c MASK_QB ..
+// in LDS, then writes them out row by row, MASK_QB consecutive words at a time, so every word of the
+// mask is written.  The selection rows of its MASK_QB queries are one contiguous range of sel; the
+// workgroup reads it flat, MASK_LD entries per thread in flight, and sets the bits of the kept
+// positions in its key range with LDS atomics.
+constexpr int MASK_QB = 32, MASK_GCH = 256, MASK_NT = 512, MASK_LD = 8;
+
+__global__ __launch_bounds__(MASK_NT) void sel_mask_kernel(const int32_t *__restrict__ sel,
+                                                           const int32_t *__restrict__ nsel, int sel_stride, int S,
+                                                           int64_t T, int64_t groups, int64_t cols,
+                                                           uint32_t *__restrict__ mask)
 {
-    const int i = blockIdx.x, tid = threadIdx.x;
-    for (int64_t g = tid; g < groups; g += 256) mask[g * cols + i] = 0u;
+    __shared__ uint32_t m[MASK_GCH * MASK_QB];
+    __shared__ int ns[MASK_QB];
+    const int tid = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * MASK_QB, g0 = (int64_t)blockIdx.y * MASK_GCH;
+    const int64_t ng = groups - g0 < MASK_GCH ? groups - g0 : MASK_GCH;
+    for (int e = tid; e < MASK_GCH * MASK_QB; e += MASK_NT) m[e] = 0u;
+    if (tid < MASK_QB) {
+        int n = c0 + tid < S ? nsel[c0 + tid] : 0;
+        ns[tid] = n < 0 ? 0 : (n > sel_stride ? sel_stride : n);
+    }
     __syncthreads();
-    if (i >= S) return;
-    int n = nsel[i];
-    n = n < 0 ? 0 : (n > sel_stride ? sel_stride : n);
-    for (int j = tid; j < n; j += 256) {
-        const int32_t t = sel[(int64_t)i * sel_stride + j];
-        if (t >= 0 && t < T) atomicOr(&mask[(int64_t)(t >> 5) * cols + i], 1u << (t & 31));
+    const int64_t t_lo = 32 * g0, t_hi = (32 * (g0 + ng) < T) ? 32 * (g0 + ng) : T;
+    const int64_t qn = S - c0 < MASK_QB ? S - c0 : MASK_QB;
+    const int64_t total = qn * sel_stride;          // entries of the workgroup's rows of sel
+    const int32_t *base = sel + c0 * sel_stride;
+    for (int64_t f0 = 0; f0 < total; f0 += (int64_t)MASK_NT * MASK_LD) {
+        int32_t v[MASK_LD];
+#pragma unroll
+        for (int u = 0; u < MASK_LD; ++u) {
+            const int64_t f = f0 + (int64_t)u * MASK_NT + tid;
+            v[u] = f < total ? base[f] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < MASK_LD; ++u) {
+            const int64_t f = f0 + (int64_t)u * MASK_NT + tid;
+            if (f >= total) continue;
+            const int q = (int)(f / sel_stride), j = (int)(f - (int64_t)q * sel_stride);
+            const int32_t t = v[u];
+            if (j < ns[q] && t >= t_lo && t < t_hi)
+                atomicOr(&m[(int)((t >> 5) - g0) * MASK_QB + q], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < ng * MASK_QB; e += MASK_NT) {
+        const int g = e / MASK_QB, q = e % MASK_QB;
+        mask[(g0 + g) * cols + c0 + q] = m[e];
     }
 }
 
@@ -102,8 +136,10 @@ mla_status launch_attention(const void *q, mla_dtype dt, const void *kv_b, const
     if (sel) {
         mask = reinterpret_cast<uint32_t *>(p);
         p += al256((size_t)mask_groups(T) * cols * 4);
-        hipLaunchKernelGGL(sel_mask_kernel, dim3((unsigned)cols), dim3(256), 0, s, sel, nsel, sel_stride, S, T,
-                           mask_groups(T), cols, mask);
+        const int64_t gy = (mask_groups(T) + MASK_GCH - 1) / MASK_GCH;
+        if (gy > 65535) return fail(MLA_ERR_UNSUPPORTED, "attention: key range too long for the selection mask");
+        hipLaunchKernelGGL(sel_mask_kernel, dim3((unsigned)(cols / MASK_QB), (unsigned)gy), dim3(MASK_NT), 0, s, sel,
+                           nsel, sel_stride, S, T, mask_groups(T), cols, mask);
         mla_status st = check_launch("sel_mask_kernel");
         if (st) return st;
     }

@@ -243,10 +243,12 @@ size_t index_select_workspace_bytes(int32_t B, int64_t t_max, int32_t k);
 constexpr int SIDE_MAXB = 32;
 struct SideAbsorb {
     const bf16_t *q_nope;   // [B][64][nope]
-    const bf16_t *kv_b;     // [64 (nope + v)][512]
+    const void *kv_b;       // [64 (nope + v)][512]: bf16, or the codes of a quantized kv_b
+    const void *scales;     // the scales of a quantized kv_b (qformat.h)
+    int fmt;                // 0 for bf16, else an mla_qformat
     bf16_t *q_abs;          // [B][64][512]
     const bf16_t *q_rope;   // [B][64][rope], before rotation
-    bf16_t *q_rope_out;     // [B][64][rope]
+    bf16_t *q_rope_out;     // [B][64][rope]; nullptr: no rotation
     int B, nope, v, rope;
     double theta;
 };

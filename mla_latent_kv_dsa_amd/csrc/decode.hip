@@ -101,11 +101,33 @@ size_t dsa_decode_workspace_bytes(const mla_dims &d, int32_t B, int64_t t_max, i
            al256((size_t)B * d.n_heads * d.qk_rope * esz);
 }
 
-mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const float *q_idx,
-                             const float *w_idx, int32_t n_ih, int32_t hd, const void *kv_b, const mla_dims &d,
-                             int32_t B, const KvView &kv_sel, const KvView &kv, int64_t t_max, int32_t k,
-                             float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
-                             hipStream_t s)
+// The side work of a matrix-core decode step (absorption, and the rotation of the query tails into
+// qr_out unless it is nullptr).  fmt != 0: w holds the codes of a quantized kv_b.
+static SideAbsorb side_of(const void *q_nope, const void *q_rope, const void *w, const void *scales, int fmt,
+                          void *qr_out, void *dec_ws, int32_t B, const mla_dims &d, double theta)
+{
+    SideAbsorb sa{};
+    sa.q_nope = (const bf16_t *)q_nope;
+    sa.kv_b = w;
+    sa.scales = scales;
+    sa.fmt = fmt;
+    sa.q_abs = decode_mfma_qabs(dec_ws);
+    sa.q_rope = (const bf16_t *)q_rope;
+    sa.q_rope_out = (bf16_t *)qr_out;
+    sa.B = B;
+    sa.nope = d.qk_nope;
+    sa.v = d.v_head;
+    sa.rope = d.qk_rope;
+    sa.theta = theta;
+    return sa;
+}
+
+// fmt != 0: kv_b holds the codes of a quantized kv_b (matrix-core geometry only)
+static mla_status dsa_decode_step(const void *q_nope, const void *q_rope, mla_dtype dt, double theta,
+                                  const float *q_idx, const float *w_idx, int32_t n_ih, int32_t hd, const void *kv_b,
+                                  const void *scales, int fmt, const mla_dims &d, int32_t B, const KvView &kv_sel,
+                                  const KvView &kv, int64_t t_max, int32_t k, float sm_scale, float *scores,
+                                  int32_t *sel, int32_t *nsel, float *out, void *ws, hipStream_t s)
 {
     char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
     const size_t sel_bytes = index_select_workspace_bytes(B, t_max, k);
@@ -115,41 +137,44 @@ mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype d
     p += al256(decode_workspace_bytes(d, B, k, dt));
     void *qr = p;
     mla_status st;
-    if (use_mfma(d, dt)) {
+    const bool mfma = use_mfma(d, dt);
+    if (fmt != 0 && !mfma) return fail(MLA_ERR_UNSUPPORTED, "dsa decode: quantized kv_b needs the matrix-core geometry");
+    if (mfma) {
         st = need_aligned("dsa decode", {q_nope, q_rope, kv_b, kv.lc, kv.rc});
         if (st) return st;
     }
-    if (use_mfma(d, dt) && B <= SIDE_MAXB) {
+    if (mfma && B <= SIDE_MAXB) {
         // the query absorption and the rotation run as extra workgroups of the selection's
         // resolve step, which occupies only B workgroups
-        SideAbsorb sa;
-        sa.q_nope = (const bf16_t *)q_nope;
-        sa.kv_b = (const bf16_t *)kv_b;
-        sa.q_abs = decode_mfma_qabs(dec_ws);
-        sa.q_rope = (const bf16_t *)q_rope;
-        sa.q_rope_out = (bf16_t *)qr;
-        sa.B = B;
-        sa.nope = d.qk_nope;
-        sa.v = d.v_head;
-        sa.rope = d.qk_rope;
-        sa.theta = theta;
+        const SideAbsorb sa = side_of(q_nope, q_rope, kv_b, scales, fmt, qr, dec_ws, B, d, theta);
         bool done = false;
         st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s,
                                  &sa, &done);
         if (st) return st;
         if (!done) {
-            st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
-            if (st) return st;
-            st = launch_absorb_mfma(q_nope, kv_b, d, B, dec_ws, s);
+            st = launch_absorb_rope(sa, kv_sel, s);
             if (st) return st;
         }
-        return launch_attend_mfma(qr, kv_b, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s);
+        return launch_attend_mfma(qr, kv_b, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s, scales, fmt);
     }
     st = launch_rope_decode(q_rope, qr, dt, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
     if (st) return st;
     st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s);
     if (st) return st;
+    if (fmt != 0)
+        return launch_decode_quant(q_nope, qr, (const uint8_t *)kv_b, scales, fmt, d, B, kv, sel, nsel, k, k, sm_scale,
+                                   out, dec_ws, s);
     return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
+}
+
+mla_status launch_dsa_decode(const void *q_nope, const void *q_rope, mla_dtype dt, double theta, const float *q_idx,
+                             const float *w_idx, int32_t n_ih, int32_t hd, const void *kv_b, const mla_dims &d,
+                             int32_t B, const KvView &kv_sel, const KvView &kv, int64_t t_max, int32_t k,
+                             float sm_scale, float *scores, int32_t *sel, int32_t *nsel, float *out, void *ws,
+                             hipStream_t s)
+{
+    return dsa_decode_step(q_nope, q_rope, dt, theta, q_idx, w_idx, n_ih, hd, kv_b, nullptr, 0, d, B, kv_sel, kv, t_max,
+                           k, sm_scale, scores, sel, nsel, out, ws, s);
 }
 
 // ------------------------------------------------------------------------------ shared layer
@@ -173,17 +198,8 @@ mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype d
     if (use_mfma(d, dt)) {
         st = need_aligned("shared decode", {q_nope, q_rope, kv_b, kv.lc, kv.rc});
         if (st) return st;
-        SideAbsorb sa;   // the absorption and the query rotation in one launch
-        sa.q_nope = (const bf16_t *)q_nope;
-        sa.kv_b = (const bf16_t *)kv_b;
-        sa.q_abs = decode_mfma_qabs(dec_ws);
-        sa.q_rope = (const bf16_t *)q_rope;
-        sa.q_rope_out = (bf16_t *)qr;
-        sa.B = B;
-        sa.nope = d.qk_nope;
-        sa.v = d.v_head;
-        sa.rope = d.qk_rope;
-        sa.theta = theta;
+        // the absorption and the query rotation in one launch
+        const SideAbsorb sa = side_of(q_nope, q_rope, kv_b, nullptr, 0, qr, dec_ws, B, d, theta);
         if (side_absorb_ok(sa)) {
             st = launch_absorb_rope(sa, kv, s);
             if (st) return st;
@@ -195,26 +211,16 @@ mla_status launch_dsa_shared(const void *q_nope, const void *q_rope, mla_dtype d
     return launch_decode(q_nope, qr, kv_b, dt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, 0, s);
 }
 
-// The decode step with a quantized kv_b: RoPE of the query tails (out of place), indexer and top-k,
-// then the quantized absorbed decode over the selected keys.  Same workspace layout as the bf16 step.
+// The decode step with a quantized kv_b: the same launches as the bf16 step, the absorption and
+// W_UV reading the codes.  Same workspace layout as the bf16 step.
 mla_status launch_dsa_decode_quant(const void *q_nope, const void *q_rope, double theta, const float *q_idx,
                                    const float *w_idx, int32_t n_ih, int32_t hd, const uint8_t *codes,
                                    const void *scales, int32_t fmt, const mla_dims &d, int32_t B, const KvView &kv_sel,
                                    const KvView &kv, int64_t t_max, int32_t k, float sm_scale, float *scores,
                                    int32_t *sel, int32_t *nsel, float *out, void *ws, hipStream_t s)
 {
-    char *p = reinterpret_cast<char *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
-    const size_t sel_bytes = index_select_workspace_bytes(B, t_max, k);
-    void *sel_ws = p;
-    p += al256(sel_bytes);
-    void *dec_ws = p;
-    p += al256(decode_workspace_bytes(d, B, k, MLA_BF16));
-    void *qr = p;
-    mla_status st = launch_rope_decode(q_rope, qr, MLA_BF16, B, d.n_heads, d.qk_rope, kv_sel, theta, s);
-    if (st) return st;
-    st = launch_index_select(q_idx, w_idx, B, n_ih, hd, kv_sel, t_max, k, scores, sel, nsel, sel_ws, sel_bytes, s);
-    if (st) return st;
-    return launch_decode_quant(q_nope, qr, codes, scales, fmt, d, B, kv, sel, nsel, k, k, sm_scale, out, dec_ws, s);
+    return dsa_decode_step(q_nope, q_rope, MLA_BF16, theta, q_idx, w_idx, n_ih, hd, codes, scales, fmt, d, B, kv_sel,
+                           kv, t_max, k, sm_scale, scores, sel, nsel, out, ws, s);
 }
 
 }  // namespace mla

@@ -26,6 +26,7 @@
 #include "common.h"
 #include "decode_plan.h"
 #include "absorb_body.h"
+#include "qformat.h"
 
 namespace mla {
 
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void absorb_q(const bf16_t *__restrict__ q_nop
                                                 int B, int v, bf16_t *__restrict__ q_abs)
 {
     extern __shared__ float sh_abs[];   // q [B][nope] fp32, then partials [4][AB_QB][128]
-    absorb_block<NR>(q_nope, kv_b, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs, threadIdx.x);
+    absorb_block<NR>(q_nope, kv_b, nullptr, B, v, q_abs, blockIdx.x, blockIdx.y, sh_abs, threadIdx.x);
 }
 
 // grid (DM_L / 128, H): the matrix-core job for batches (absorb_block_mfma).
@@ -841,11 +842,46 @@ __global__ __launch_bounds__(256) void unabsorb(const bf16_t *__restrict__ clat,
 constexpr int C1_ROWS = 128;
 constexpr size_t C1_LDS = (size_t)(C1_ROWS * CU_WROW + 16 * CU_ROW) * 2 + (size_t)CU_MAXNS * 4;
 
-template <int SB, bool PB16 = false>   // splits held per thread, NS <= SB; PB16: bf16 split outputs
+//
+// FMT != 0: kv_b holds the codes of a quantized kv_b (qformat.h).  Waves 4..7 then load the codes
+// of their W_UV rows into registers and write them to LDS as bf16 in the same layout: the byte
+// codes without their row scale, which multiplies the row's product at the end, and MXFP4 weights
+// with their block scale; all of these are exact in bf16.
+template <int FMT>
+__device__ __forceinline__ void c1_stage_quant(const uint8_t *__restrict__ codes, const void *__restrict__ scales,
+                                               int64_t row0, bf16_t *__restrict__ sW, int t)
+{
+    // 128 rows x 32 pieces of 16 columns; piece p = t + 256 i: row p / 32, columns 16 (p % 32) ..
+    uint4 c[16];
+    float sc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int p = t + 256 * i, r = p >> 5, c16 = p & 31;
+        if constexpr (FMT == MLA_Q_MXFP4) {
+            const uint2 x = *reinterpret_cast<const uint2 *>(codes + (row0 + r) * (DM_L / 2) + 8 * c16);
+            c[i] = make_uint4(x.x, x.y, 0u, 0u);
+            sc[i] = q_scale_e8m0(reinterpret_cast<const uint8_t *>(scales)[(row0 + r) * (DM_L / 32) + (c16 >> 1)]);
+        } else {
+            c[i] = *reinterpret_cast<const uint4 *>(codes + (row0 + r) * DM_L + 16 * c16);
+            sc[i] = 1.f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int p = t + 256 * i, r = p >> 5, c16 = p & 31;
+        uint4 lo, hi;
+        q_bf16x16<FMT>(c[i], sc[i], lo, hi);
+        uint4 *d = reinterpret_cast<uint4 *>(sW + r * CU_WROW + 16 * c16);
+        d[0] = lo;
+        d[1] = hi;
+    }
+}
+
+template <int SB, bool PB16 = false, int FMT = 0>   // splits held per thread, NS <= SB; PB16: bf16 split outputs
 __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_part, const float *__restrict__ m_part,
                                                    const float *__restrict__ l_part, int NS,
-                                                   const bf16_t *__restrict__ kv_b, int nope, int v,
-                                                   float *__restrict__ out)
+                                                   const void *__restrict__ kv_b, const void *__restrict__ scales,
+                                                   int nope, int v, float *__restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) char c1_smem[];
     bf16_t *sW = reinterpret_cast<bf16_t *>(c1_smem);
@@ -853,12 +889,17 @@ __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_p
     float *sF = reinterpret_cast<float *>(sC + 16 * CU_ROW);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = blockIdx.y, jb = C1_ROWS * blockIdx.x;
+    const int64_t row0 = (int64_t)h * (nope + v) + nope + jb;   // first W_UV row of the workgroup
     if (wave >= 4) {
-        const int w4 = wave - 4;
-        const bf16_t *wsrc = kv_b + ((int64_t)h * (nope + v) + nope + jb + 32 * w4) * DM_L + 8 * lane;
+        if constexpr (FMT == 0) {
+            const int w4 = wave - 4;
+            const bf16_t *wsrc = reinterpret_cast<const bf16_t *>(kv_b) + (row0 + 32 * w4) * DM_L + 8 * lane;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) lds_dma16(wsrc + (int64_t)i * DM_L, lds_addr(sW + (32 * w4 + i) * CU_WROW));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies have landed
+            for (int i = 0; i < 32; ++i) lds_dma16(wsrc + (int64_t)i * DM_L, lds_addr(sW + (32 * w4 + i) * CU_WROW));
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies have landed
+        } else {
+            c1_stage_quant<FMT>(reinterpret_cast<const uint8_t *>(kv_b), scales, row0, sW, tid - 256);
+        }
         __syncthreads();
         __syncthreads();
     } else {
@@ -900,6 +941,8 @@ __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_p
         __syncthreads();
     }
     const int r16 = lane & 15, q4 = lane >> 4;
+    float rs = 1.f;   // the row scale of the byte formats
+    if (FMT == MLA_Q_FP8_E4M3 || FMT == MLA_Q_INT8) rs = reinterpret_cast<const float *>(scales)[row0 + 16 * wave + r16];
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     const bf16_t *wl = sW + (16 * wave + r16) * CU_WROW + 8 * q4;
 #pragma unroll
@@ -908,7 +951,7 @@ __global__ __launch_bounds__(512) void combine_one(const float *__restrict__ o_p
         const uint4 wq = *reinterpret_cast<const uint4 *>(wl + 32 * ks);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wq), d, 0, 0, 0);
     }
-    if (q4 == 0) out[(int64_t)h * v + jb + 16 * wave + r16] = d[0];
+    if (q4 == 0) out[(int64_t)h * v + jb + 16 * wave + r16] = (FMT == MLA_Q_FP8_E4M3 || FMT == MLA_Q_INT8) ? d[0] * rs : d[0];
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -945,6 +988,17 @@ static DecPlan dec_plan(int32_t B, int64_t max_keys)
     return p;
 }
 
+template <int FMT> static hipError_t c1_attrs()
+{
+    const void *c1[3] = {reinterpret_cast<const void *>(&combine_one<16, true, FMT>),
+                         reinterpret_cast<const void *>(&combine_one<32, true, FMT>),
+                         reinterpret_cast<const void *>(&combine_one<64, true, FMT>)};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 3 && e == hipSuccess; ++i)
+        e = hipFuncSetAttribute(c1[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)C1_LDS);
+    return e;
+}
+
 // dec_core stages 128 latent rows (134 KB), combine_unabsorb 64 rows of W_UV (65 KB)
 static mla_status enable_big_lds()
 {
@@ -975,14 +1029,10 @@ static mla_status enable_big_lds()
                              reinterpret_cast<const void *>(&combine_unabsorb<4, 16>)};
         for (int i = 0; i < 4 && e == hipSuccess; ++i)
             e = hipFuncSetAttribute(cu[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)CU_LDS);
-        const void *c1[6] = {reinterpret_cast<const void *>(&combine_one<16>),
-                             reinterpret_cast<const void *>(&combine_one<32>),
-                             reinterpret_cast<const void *>(&combine_one<64>),
-                             reinterpret_cast<const void *>(&combine_one<16, true>),
-                             reinterpret_cast<const void *>(&combine_one<32, true>),
-                             reinterpret_cast<const void *>(&combine_one<64, true>)};
-        for (int i = 0; i < 6 && e == hipSuccess; ++i)
-            e = hipFuncSetAttribute(c1[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)C1_LDS);
+        if (e == hipSuccess) e = c1_attrs<0>();
+        if (e == hipSuccess) e = c1_attrs<MLA_Q_FP8_E4M3>();
+        if (e == hipSuccess) e = c1_attrs<MLA_Q_INT8>();
+        if (e == hipSuccess) e = c1_attrs<MLA_Q_MXFP4>();
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
     }
@@ -1071,10 +1121,11 @@ mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_di
 
 mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B, const KvView &kv,
                               const int32_t *sel, const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
-                              float sm_scale, float *out, void *ws, hipStream_t s)
+                              float sm_scale, float *out, void *ws, hipStream_t s, const void *scales, int fmt)
 {
     if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: B > 65535");
     if (max_keys > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: too many keys");
+    if (fmt < 0 || fmt > MLA_Q_MXFP4) return fail(MLA_ERR_ARG, "decode: unknown weight format %d", fmt);
     const DecPlan p = dec_plan(B, max_keys);
     const DecWs w = dec_ws(ws, B, p);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
@@ -1084,51 +1135,66 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
     const int pf = (int64_t)B * p.ns * (DM_H / 16) <= 128 ? 1 : 0;
     // one query: the split outputs go to combine_one as bf16 (half the bytes each way)
     const bool one_b16 = B == 1 && d.v_head % C1_ROWS == 0;
-    const bf16_t *wuv = (const bf16_t *)kv_b + (int64_t)d.qk_nope * DM_L;
+    // W_UV in 1 KB units for the read-ahead slice: a bf16 row, two byte-code rows, or four MXFP4 rows
+    const int upr = fmt == 0 ? 1 : fmt == MLA_Q_MXFP4 ? 4 : 2;
+    const int64_t w_row_bytes = fmt == 0 ? 2 * DM_L : fmt == MLA_Q_MXFP4 ? DM_L / 2 : DM_L;
+    const bf16_t *wuv = reinterpret_cast<const bf16_t *>(reinterpret_cast<const char *>(kv_b) +
+                                                         (int64_t)d.qk_nope * w_row_bytes);
+    const int rph = (d.qk_nope + d.v_head) / upr, vpf = d.v_head / upr;
     if (B >= MH_MIN_B)
         hipLaunchKernelGGL(dec_core_mh, dim3(p.ns, B), dim3(256), MH_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv, sel,
                            nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
     else if (one_b16 && p.kps <= DC_SUP * DC_KC)
         hipLaunchKernelGGL((dec_core<true, true>), dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+                           w.l_part, B, wuv, rph, vpf);
     else if (one_b16)
         hipLaunchKernelGGL((dec_core<false, true>), dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+                           w.l_part, B, wuv, rph, vpf);
     else if (p.kps <= DC_SUP * DC_KC)
         hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+                           w.l_part, B, wuv, rph, vpf);
     else
         hipLaunchKernelGGL(dec_core<false>, dim3(p.ns, DM_H / 16, B + pf), dim3(256), DC_LDS, s, w.q_abs,
                            (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, wuv, d.qk_nope + d.v_head, d.v_head);
+                           w.l_part, B, wuv, rph, vpf);
     st = check_launch("dec_core");
     if (st) return st;
     const dim3 gc(d.v_head / 64, DM_H, (B + 15) / 16);
     const bf16_t *kb = (const bf16_t *)kv_b;
-    if (B >= MH_MIN_B) {
+    if (B >= MH_MIN_B || (fmt != 0 && !one_b16)) {
         const int npairs = B * DM_H;
         hipLaunchKernelGGL(combine_reduce, dim3((npairs + CR_PAIRS - 1) / CR_PAIRS), dim3(256), 0, s, w.o_part, w.m_part,
                            w.l_part, p.ns, npairs, w.clat);
         st = check_launch("combine_reduce");
         if (st) return st;
+        if (fmt != 0)
+            return launch_unabsorb_quant(w.clat, (const uint8_t *)kv_b, scales, fmt, d, B, out, s);
         hipLaunchKernelGGL(unabsorb, dim3(d.v_head / 64, DM_H), dim3(256), 0, s, w.clat, kb, B, d.qk_nope, d.v_head, out);
         return check_launch("unabsorb");
     }
-    if (B == 1 && d.v_head % C1_ROWS == 0) {
+    if (one_b16) {
         const dim3 g1(d.v_head / C1_ROWS, DM_H);
-        if (p.ns <= 16)
-            hipLaunchKernelGGL((combine_one<16, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
-                               kb, d.qk_nope, d.v_head, out);
-        else if (p.ns <= 32)
-            hipLaunchKernelGGL((combine_one<32, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
-                               kb, d.qk_nope, d.v_head, out);
-        else
-            hipLaunchKernelGGL((combine_one<64, true>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
-                               kb, d.qk_nope, d.v_head, out);
-    } else if (B == 1 && p.ns <= 16)
+#define C1_LAUNCH(SB, FMT)                                                                                       \
+    hipLaunchKernelGGL((combine_one<SB, true, FMT>), g1, dim3(512), C1_LDS, s, w.o_part, w.m_part, w.l_part, p.ns, \
+                       kv_b, scales, d.qk_nope, d.v_head, out)
+#define C1_FMT(SB)                                                  \
+    do {                                                            \
+        if (fmt == MLA_Q_FP8_E4M3) C1_LAUNCH(SB, MLA_Q_FP8_E4M3);   \
+        else if (fmt == MLA_Q_INT8) C1_LAUNCH(SB, MLA_Q_INT8);      \
+        else if (fmt == MLA_Q_MXFP4) C1_LAUNCH(SB, MLA_Q_MXFP4);    \
+        else C1_LAUNCH(SB, 0);                                      \
+    } while (0)
+        if (p.ns <= 16) C1_FMT(16);
+        else if (p.ns <= 32) C1_FMT(32);
+        else C1_FMT(64);
+#undef C1_FMT
+#undef C1_LAUNCH
+        return check_launch("combine_one");
+    }
+    if (B == 1 && p.ns <= 16)
         hipLaunchKernelGGL((combine_unabsorb<1, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
                            kb, B, d.qk_nope, d.v_head, out);
     else if (B == 1 && p.ns <= 32)
@@ -1141,40 +1207,6 @@ mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_di
         hipLaunchKernelGGL((combine_unabsorb<4, 16>), gc, dim3(256), CU_LDS, s, w.o_part, w.m_part, w.l_part, p.ns,
                            kb, B, d.qk_nope, d.v_head, out);
     return check_launch("combine_unabsorb");
-}
-
-// The attention part of the decode up to the combined latent rows, without W_UV (for weights the
-// matrix-core combine does not read, e.g. quantized ones): the key splits as above (no W_UV
-// read-ahead), then combine_reduce for every batch size.  q_abs must already sit in the workspace.
-mla_status launch_attend_mfma_clat(const void *q_rope, int32_t B, const KvView &kv, const int32_t *sel,
-                                   const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, void *ws,
-                                   hipStream_t s, bf16_t **clat)
-{
-    if (B > 65535) return fail(MLA_ERR_UNSUPPORTED, "decode: B > 65535");
-    if (max_keys > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "decode: too many keys");
-    const DecPlan p = dec_plan(B, max_keys);
-    const DecWs w = dec_ws(ws, B, p);
-    const float scale_log2 = sm_scale * 1.4426950408889634f;
-    mla_status st = enable_big_lds();
-    if (st) return st;
-    if (B >= MH_MIN_B)
-        hipLaunchKernelGGL(dec_core_mh, dim3(p.ns, B), dim3(256), MH_LDS, s, w.q_abs, (const bf16_t *)q_rope, kv, sel,
-                           nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part, w.l_part);
-    else if (p.kps <= DC_SUP * DC_KC)
-        hipLaunchKernelGGL(dec_core<true>, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs,
-                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, (const bf16_t *)nullptr, 0, 0);
-    else
-        hipLaunchKernelGGL(dec_core<false>, dim3(p.ns, DM_H / 16, B), dim3(256), DC_LDS, s, w.q_abs,
-                           (const bf16_t *)q_rope, kv, sel, nsel, sel_stride, scale_log2, (int)p.kps, w.o_part, w.m_part,
-                           w.l_part, B, (const bf16_t *)nullptr, 0, 0);
-    st = check_launch("dec_core");
-    if (st) return st;
-    const int npairs = B * DM_H;
-    hipLaunchKernelGGL(combine_reduce, dim3((npairs + CR_PAIRS - 1) / CR_PAIRS), dim3(256), 0, s, w.o_part, w.m_part,
-                       w.l_part, p.ns, npairs, w.clat);
-    *clat = w.clat;
-    return check_launch("combine_reduce");
 }
 
 }  // namespace mla

@@ -28,11 +28,13 @@ size_t decode_mfma_absorb_ws(int32_t B);
 mla_status launch_absorb_mfma(const void *q_nope, const void *kv_b, const mla_dims &d, int32_t B, void *ws,
                               hipStream_t s);
 bf16_t *decode_mfma_qabs(void *ws);   // where the absorb step leaves q_abs in a decode workspace
-mla_status launch_attend_mfma_clat(const void *q_rope, int32_t B, const KvView &kv, const int32_t *sel,
-                                   const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, void *ws,
-                                   hipStream_t s, bf16_t **clat);
+// fmt != 0: kv_b holds the codes of a quantized kv_b with the given scales (qformat.h)
 mla_status launch_attend_mfma(const void *q_rope, const void *kv_b, const mla_dims &d, int32_t B, const KvView &kv,
                               const int32_t *sel, const int32_t *nsel, int32_t sel_stride, int64_t max_keys,
-                              float sm_scale, float *out, void *ws, hipStream_t s);
+                              float sm_scale, float *out, void *ws, hipStream_t s, const void *scales = nullptr,
+                              int fmt = 0);
+// out[b][h][:] = W_UV[h] clat[b][h] over a quantized kv_b (bf16 clat [B][64][512])
+mla_status launch_unabsorb_quant(const bf16_t *clat, const uint8_t *codes, const void *scales, int32_t fmt,
+                                 const mla_dims &d, int32_t B, float *out, hipStream_t s);
 
 }  // namespace mla

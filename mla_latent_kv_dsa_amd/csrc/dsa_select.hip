@@ -468,20 +468,22 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
 
 // Side job j (SR_NT threads): two absorb jobs a = 2 j + half, (cb, h) = (a % 4, a / 4), one per 256
 // threads; the cb == 0 job of head h also rotates that head's query tails at each row's query
-// position seq_len - 1 (into a separate buffer).
-template <int NR>
+// position seq_len - 1 (into a separate buffer; no rotation when there is none).  FMT: 0 for the
+// bf16 kv_b, else its quantized format (always the vector-ALU absorption: the fp32 row scales are
+// not exact in the bf16 operands of the matrix-core one).
+template <int NR, int FMT>
 __device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbsorb &sa, int job, uint64_t *sr_dyn)
 {
     const int half = threadIdx.x >> 8, jt = threadIdx.x & 255;
     const int a = 2 * job + half, cb = a & 3, h = a >> 2;
-    if (sa.B >= AB_MFMA_B) {
-        absorb_block_mfma<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h,
+    if (FMT == 0 && sa.B >= AB_MFMA_B) {
+        absorb_block_mfma<NR>(sa.q_nope, reinterpret_cast<const bf16_t *>(sa.kv_b), sa.B, sa.v, sa.q_abs, cb, h,
                               reinterpret_cast<char *>(sr_dyn) + half * 16 * NR * AB_WROWB, jt);
     } else {
         float *shj = reinterpret_cast<float *>(sr_dyn) + half * (sa.B * 16 * NR + 4 * AB_QB * 128);
-        absorb_block<NR>(sa.q_nope, sa.kv_b, sa.B, sa.v, sa.q_abs, cb, h, shj, jt);
+        absorb_block<NR, FMT>(sa.q_nope, sa.kv_b, sa.scales, sa.B, sa.v, sa.q_abs, cb, h, shj, jt);
     }
-    if (cb != 0) return;
+    if (cb != 0 || !sa.q_rope_out) return;
     const int hr = sa.rope / 2;
     for (int p = jt; p < sa.B * hr; p += 256) {
         const int b = p / hr, j = p - b * hr;
@@ -501,7 +503,7 @@ __device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbso
 // grid (nres + 2 * 64): workgroups nres.. run two absorb jobs a = 2 (blockIdx - nres) + half,
 // (cb, h) = (a % 4, a / 4), one per 256 threads; the cb == 0 job of head h also rotates that
 // head's query tails.
-template <int NR>
+template <int NR, int FMT>
 __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
                                                             const uint32_t *__restrict__ fcnt, int nch,
                                                             const uint64_t *__restrict__ gkeep, int wp,
@@ -514,46 +516,84 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
         resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
         return;
     }
-    side_absorb_job<NR>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
+    side_absorb_job<NR, FMT>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
 }
 
 // The same side work as a launch of its own (2 * 64 workgroups of SR_NT threads), for decode steps
-// whose selection is given: the shared layer.
-template <int NR>
+// whose selection is given (the shared layer) or that run no selection.
+template <int NR, int FMT>
 __global__ __launch_bounds__(SR_NT) void absorb_rope(KvView kv, SideAbsorb sa)
 {
     extern __shared__ uint64_t sr_dyn[];
-    side_absorb_job<NR>(kv, sa, blockIdx.x, sr_dyn);
+    side_absorb_job<NR, FMT>(kv, sa, blockIdx.x, sr_dyn);
 }
 
 static size_t side_lds(const SideAbsorb &sa)
 {
-    return sa.B >= AB_MFMA_B ? 2 * (size_t)sa.nope * AB_WROWB : 2 * ((size_t)sa.B * sa.nope + 4 * AB_QB * 128) * 4;
+    return sa.fmt == 0 && sa.B >= AB_MFMA_B ? 2 * (size_t)sa.nope * AB_WROWB
+                                            : 2 * ((size_t)sa.B * sa.nope + 4 * AB_QB * 128) * 4;
 }
 
 bool side_absorb_ok(const SideAbsorb &sa)
 {
-    return sa.B <= SIDE_MAXB && (sa.nope == 128 || sa.nope == 192 || sa.nope == 256);
+    return sa.B <= SIDE_MAXB && (sa.nope == 128 || sa.nope == 192 || sa.nope == 256) && sa.fmt >= 0 &&
+           sa.fmt <= MLA_Q_MXFP4;
+}
+
+// f(NR, FMT) for the side job's template arguments
+#define SIDE_DISPATCH(sa, f)                                              \
+    do {                                                                  \
+        if ((sa).nope == 128) SIDE_DISPATCH_F((sa), f, 8);                \
+        else if ((sa).nope == 192) SIDE_DISPATCH_F((sa), f, 12);          \
+        else SIDE_DISPATCH_F((sa), f, 16);                                \
+    } while (0)
+#define SIDE_DISPATCH_F(sa, f, NR)                                        \
+    do {                                                                  \
+        if ((sa).fmt == MLA_Q_FP8_E4M3) f(NR, MLA_Q_FP8_E4M3);            \
+        else if ((sa).fmt == MLA_Q_INT8) f(NR, MLA_Q_INT8);               \
+        else if ((sa).fmt == MLA_Q_MXFP4) f(NR, MLA_Q_MXFP4);             \
+        else f(NR, 0);                                                    \
+    } while (0)
+
+template <int NR, int FMT> static hipError_t side_attr()
+{
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&absorb_rope<NR, FMT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve_absorb<NR, FMT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+    return e;
+}
+
+static mla_status enable_side_lds()
+{
+    static bool done = false;
+    if (!done) {
+        hipError_t e = hipSuccess;
+        for (int nope : {128, 192, 256})
+            for (int fmt = 0; fmt <= MLA_Q_MXFP4; ++fmt) {
+                SideAbsorb t{};
+                t.nope = nope;
+                t.fmt = fmt;
+#define SIDE_ATTR(NR, FMT) e = e == hipSuccess ? side_attr<NR, FMT>() : e
+                SIDE_DISPATCH(t, SIDE_ATTR);
+#undef SIDE_ATTR
+            }
+        if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+        done = true;
+    }
+    return MLA_OK;
 }
 
 mla_status launch_absorb_rope(const SideAbsorb &sa, const KvView &kv, hipStream_t s)
 {
-    static bool attr = false;
-    if (!attr) {
-        const void *f[3] = {reinterpret_cast<const void *>(&absorb_rope<8>),
-                            reinterpret_cast<const void *>(&absorb_rope<12>),
-                            reinterpret_cast<const void *>(&absorb_rope<16>)};
-        for (int i = 0; i < 3; ++i) {
-            const hipError_t e = hipFuncSetAttribute(f[i], hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
-            if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-        }
-        attr = true;
-    }
+    mla_status st = enable_side_lds();
+    if (st) return st;
     const size_t dyn = side_lds(sa);
     const dim3 g(2 * AB_H);
-    if (sa.nope == 128) hipLaunchKernelGGL(absorb_rope<8>, g, dim3(SR_NT), dyn, s, kv, sa);
-    else if (sa.nope == 192) hipLaunchKernelGGL(absorb_rope<12>, g, dim3(SR_NT), dyn, s, kv, sa);
-    else hipLaunchKernelGGL(absorb_rope<16>, g, dim3(SR_NT), dyn, s, kv, sa);
+#define AR_LAUNCH(NR, FMT) hipLaunchKernelGGL((absorb_rope<NR, FMT>), g, dim3(SR_NT), dyn, s, kv, sa)
+    SIDE_DISPATCH(sa, AR_LAUNCH);
+#undef AR_LAUNCH
     return check_launch("absorb_rope");
 }
 
@@ -606,17 +646,12 @@ static mla_status enable_sel_lds()
 {
     static bool done = false;
     if (!done) {
-        const void *f[4] = {reinterpret_cast<const void *>(&sel_resolve),
-                            reinterpret_cast<const void *>(&sel_resolve_absorb<8>),
-                            reinterpret_cast<const void *>(&sel_resolve_absorb<12>),
-                            reinterpret_cast<const void *>(&sel_resolve_absorb<16>)};
-        for (int i = 0; i < 4; ++i) {
-            const hipError_t e = hipFuncSetAttribute(f[i], hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
-            if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-        }
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+        if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
     }
-    return MLA_OK;
+    return enable_side_lds();
 }
 
 mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_t n_ih, int32_t hd, const KvView &kv,
@@ -664,12 +699,10 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     const size_t dyn_abs = side_lds(*side);
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
     const dim3 g((unsigned)(B + 2 * AB_H));
-#define SRA_LAUNCH(NR)                                                                                              \
-    hipLaunchKernelGGL(sel_resolve_absorb<NR>, g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, sw.wp, \
-                       sw.rows, sel, nsel, B, *side, (int)((dyn - dyn_masks) / 8))
-    if (side->nope == 128) SRA_LAUNCH(8);
-    else if (side->nope == 192) SRA_LAUNCH(12);
-    else SRA_LAUNCH(16);
+#define SRA_LAUNCH(NR, FMT)                                                                                     \
+    hipLaunchKernelGGL((sel_resolve_absorb<NR, FMT>), g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, \
+                       sw.wp, sw.rows, sel, nsel, B, *side, (int)((dyn - dyn_masks) / 8))
+    SIDE_DISPATCH(*side, SRA_LAUNCH);
 #undef SRA_LAUNCH
     st = check_launch("sel_resolve_absorb");
     if (st) return st;

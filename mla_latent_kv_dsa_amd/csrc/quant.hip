@@ -11,55 +11,20 @@
 //   MLA_Q_INT8      one signed byte per weight, one fp32 scale per row
 //   MLA_Q_MXFP4     OCP MX: FP4 E2M1, two per byte (even column in the low nibble), an E8M0
 //                   scale byte per 32 columns
-// The codes are decoded on the vector ALU by building the fp32 bit pattern; every product and sum is
-// fp32, so the only loss against the bf16 path is the weights' own.
-//   absorb_q_quant    q_abs[b][h][:] = W_UK[h]^T q_nope[b][h]          (bf16 out, as the bf16 path)
-//   (attention)       the matrix-core key splits and the split reduction into clat (decode_mfma)
+// The codes are decoded by the chip's scaled conversion instructions (qformat.h); every product and
+// sum is fp32, so the only loss against the bf16 path is the weights' own.
+//   absorption        q_abs[b][h][:] = W_UK[h]^T q_nope[b][h] (bf16 out, as the bf16 path): the
+//                     decode step's side job over the codes (absorb_body.h), or absorb_q_quant for
+//                     batches beyond it
+//   attention         the matrix-core key splits; at batch 1 combine_one decodes W_UV into LDS and
+//                     contracts it on the matrix cores (decode_mfma), otherwise the split
+//                     reduction into clat and unabsorb_quant
 //   unabsorb_quant    out[b][h][j] = W_UV[h][j] . clat[b][h]
 #include "common.h"
 #include "decode_plan.h"
+#include "qformat.h"
 
 namespace mla {
-
-// FP8 E4M3: s.eeee.mmm; e == 0: m 2^-9, else (1 + m/8) 2^(e-7)
-__device__ __forceinline__ float q_e4m3(uint32_t b)
-{
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float mag = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
-}
-
-// FP4 E2M1: s.ee.m; e == 0: m / 2, else (1 + m/2) 2^(e-1)
-__device__ __forceinline__ float q_e2m1(uint32_t n)
-{
-    const uint32_t e = (n >> 1) & 3u, m = n & 1u;
-    const float mag = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
-    return __uint_as_float(__float_as_uint(mag) | ((n & 8u) << 28));
-}
-
-// E8M0 scale 2^(x - 127) (x = 0 is the subnormal 2^-127)
-__device__ __forceinline__ float q_e8m0(uint32_t x) { return x ? __uint_as_float(x << 23) : __uint_as_float(0x00400000u); }
-
-// Weights row, columns c .. c + 3 (c a multiple of 4) of a quantized [rows][L] matrix.
-template <int FMT>
-__device__ __forceinline__ void q_load4(const uint8_t *__restrict__ codes, const void *__restrict__ scales, int64_t row,
-                                        int L, int c, float (&w)[4])
-{
-    if (FMT == MLA_Q_MXFP4) {
-        const uint32_t v = *reinterpret_cast<const uint16_t *>(codes + row * (L / 2) + c / 2);
-        const float sc = q_e8m0(reinterpret_cast<const uint8_t *>(scales)[row * (L / 32) + c / 32]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = sc * q_e2m1((v >> (4 * k)) & 15u);
-    } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(codes + row * L + c);
-        const float sc = reinterpret_cast<const float *>(scales)[row];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t b = (v >> (8 * k)) & 255u;
-            w[k] = sc * (FMT == MLA_Q_FP8_E4M3 ? q_e4m3(b) : (float)(int8_t)b);
-        }
-    }
-}
 
 constexpr int QA_QB = 8;   // queries per pass
 
@@ -153,6 +118,22 @@ bool decode_quant_supported(const mla_dims &d, mla_dtype dt)
     return decode_mfma_supported(d, dt) && d.qk_nope % 8 == 0 && d.qk_nope <= 256 && d.v_head % 32 == 0;
 }
 
+mla_status launch_unabsorb_quant(const bf16_t *clat, const uint8_t *codes, const void *scales, int32_t fmt,
+                                 const mla_dims &d, int32_t B, float *out, hipStream_t s)
+{
+    const int L = d.kv_lora, H = d.n_heads;
+#define MLA_UQ(F) hipLaunchKernelGGL(unabsorb_quant<F>, dim3(d.v_head / 32, H), dim3(256), 0, s, clat, codes, scales, \
+                                     B, d.qk_nope, d.v_head, L, out)
+    if (fmt == MLA_Q_FP8_E4M3) MLA_UQ(MLA_Q_FP8_E4M3);
+    else if (fmt == MLA_Q_INT8) MLA_UQ(MLA_Q_INT8);
+    else MLA_UQ(MLA_Q_MXFP4);
+#undef MLA_UQ
+    return check_launch("unabsorb_quant");
+}
+
+// The absorption over the quantized W_UK (the side job of the decode step as a launch of its own,
+// up to SIDE_MAXB queries; absorb_q_quant beyond), then the matrix-core attention with the
+// quantized W_UV (decode_mfma).
 mla_status launch_decode_quant(const void *q_nope, const void *q_rope, const uint8_t *codes, const void *scales,
                                int32_t fmt, const mla_dims &d, int32_t B, const KvView &kv, const int32_t *sel,
                                const int32_t *nsel, int32_t sel_stride, int64_t max_keys, float sm_scale, float *out,
@@ -161,24 +142,33 @@ mla_status launch_decode_quant(const void *q_nope, const void *q_rope, const uin
     const int L = d.kv_lora, H = d.n_heads;
     bf16_t *qa = decode_mfma_qabs(ws);
     const bf16_t *qn = (const bf16_t *)q_nope;
+    SideAbsorb sa{};
+    sa.q_nope = qn;
+    sa.kv_b = codes;
+    sa.scales = scales;
+    sa.fmt = fmt;
+    sa.q_abs = qa;
+    sa.q_rope = (const bf16_t *)q_rope;
+    sa.q_rope_out = nullptr;   // the query tails come rotated
+    sa.B = B;
+    sa.nope = d.qk_nope;
+    sa.v = d.v_head;
+    sa.rope = d.qk_rope;
+    mla_status st;
+    if (side_absorb_ok(sa)) {
+        st = launch_absorb_rope(sa, kv, s);
+    } else {
 #define MLA_QA(F) hipLaunchKernelGGL(absorb_q_quant<F>, dim3(L / 128, H), dim3(256), 0, s, qn, codes, scales, B, \
                                      d.qk_nope, d.v_head, L, qa)
-    if (fmt == MLA_Q_FP8_E4M3) MLA_QA(MLA_Q_FP8_E4M3);
-    else if (fmt == MLA_Q_INT8) MLA_QA(MLA_Q_INT8);
-    else MLA_QA(MLA_Q_MXFP4);
+        if (fmt == MLA_Q_FP8_E4M3) MLA_QA(MLA_Q_FP8_E4M3);
+        else if (fmt == MLA_Q_INT8) MLA_QA(MLA_Q_INT8);
+        else MLA_QA(MLA_Q_MXFP4);
 #undef MLA_QA
-    mla_status st = check_launch("absorb_q_quant");
+        st = check_launch("absorb_q_quant");
+    }
     if (st) return st;
-    bf16_t *clat = nullptr;
-    st = launch_attend_mfma_clat(q_rope, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, ws, s, &clat);
-    if (st) return st;
-#define MLA_UQ(F) hipLaunchKernelGGL(unabsorb_quant<F>, dim3(d.v_head / 32, H), dim3(256), 0, s, clat, codes, scales, \
-                                     B, d.qk_nope, d.v_head, L, out)
-    if (fmt == MLA_Q_FP8_E4M3) MLA_UQ(MLA_Q_FP8_E4M3);
-    else if (fmt == MLA_Q_INT8) MLA_UQ(MLA_Q_INT8);
-    else MLA_UQ(MLA_Q_MXFP4);
-#undef MLA_UQ
-    return check_launch("unabsorb_quant");
+    return launch_attend_mfma(q_rope, codes, d, B, kv, sel, nsel, sel_stride, max_keys, sm_scale, out, ws, s, scales,
+                              fmt);
 }
 
 }  // namespace mla

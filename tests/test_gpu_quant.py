@@ -35,15 +35,17 @@ def _ref(d, b, keys, kvb, sm, T):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("B", [1, 2, 5])
+@pytest.mark.parametrize("B", [1, 2, 5, 33])
 def test_quantized_decode_dense_and_selected(fmt, B):
+    """B = 1: the absorption job and combine_one decoding W_UV into LDS; B = 2: the split reduction
+    and unabsorb_quant; B = 5: the all-heads decode core; B = 33: the stand-alone absorb_q_quant."""
     T = 1500
     d = synth.decode(800 + B, T, B=B)
     N = d.H * (d.nope + d.v)
     codes, scales = synth.quantized_kv_b(810 + fmt, fmt, N, d.L)
     kvb = oracle.dequant_rows(codes, scales, fmt, d.L).astype(np.float32)
     sm = 1.0 / math.sqrt(d.nope + d.rope)
-    seq_len = [T - 211 * b for b in range(B)]
+    seq_len = [T - (211 * b) % 1400 for b in range(B)]
     kv = mla.KvCache(dev_bf16(d.lc), dev_bf16(d.rc), seq_len=dev(np.asarray(seq_len, np.int32)), max_seq_len=T,
                      seq_stride=T)
     qn, qr, c_d, s_d = dev_bf16(d.q_nope), dev_bf16(d.q_rope), dev(codes), dev(scales)
@@ -86,3 +88,29 @@ def test_quantized_dsa_step_full_context(fmt):
     q_rot = oracle.rope_interleave(cv(d.q_rope[0])[None], np.array([T - 1]), 0, d.rope)[0]
     ref = oracle.absorbed_decode(cv(d.q_nope[0]), q_rot, kvb, cv(d.lc), cv(d.rc), sel[0, : nsel[0]], d.v, sm)
     assert rel_err(out[0], ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantized_dsa_step_batch(fmt):
+    """The quantized step over three sequences of different lengths (the absorption runs beside the
+    selection's resolve workgroups for every row): selection equal to the bf16 step's, output against
+    the oracle per row."""
+    B, T, k = 3, 6000, 2048
+    d = synth.decode(31, T, B=B, dsa=True)
+    N = d.H * (d.nope + d.v)
+    codes, scales = synth.quantized_kv_b(840 + fmt, fmt, N, d.L)
+    kvb = oracle.dequant_rows(codes, scales, fmt, d.L).astype(np.float32)
+    sm = 1.0 / math.sqrt(d.nope + d.rope)
+    seq_len = np.array([T, 2500, 1300], np.int32)
+    kv = mla.KvCache(dev_bf16(d.lc), dev_bf16(d.rc), dev(d.ic), seq_len=dev(seq_len), max_seq_len=T, seq_stride=T)
+    args = (dev_bf16(d.q_nope), dev_bf16(d.q_rope), dev(d.q_idx), dev(d.w_idx))
+    log(f"quantized DSA step B=3 fmt={fmt}")
+    out, sc, sel, nsel = (host(x) for x in mla.mla_dsa_decode_q(*args, dev(codes), dev(scales), fmt, kv, T, k, sm))
+    _, sc_b, sel_b, nsel_b = (host(x) for x in mla.mla_dsa_decode(*args, dev_bf16(d.kv_b), kv, T, k, sm))
+    assert np.array_equal(sel, sel_b) and np.array_equal(nsel, nsel_b)
+    for b in range(B):
+        L = int(seq_len[b])
+        q_rot = oracle.rope_interleave(cv(d.q_rope[b])[None], np.array([L - 1]), 0, d.rope)[0]
+        ref = oracle.absorbed_decode(cv(d.q_nope[b]), q_rot, kvb, cv(d.lc[b * T:(b + 1) * T]),
+                                     cv(d.rc[b * T:(b + 1) * T]), sel[b, : nsel[b]], d.v, sm)
+        assert rel_err(out[b], ref) <= TOL_BF16, b
