@@ -294,6 +294,139 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     }
 }
 
+// The same for launch rows that are queries of one sequence (KvView.qps > 1): a workgroup scores
+// the QB consecutive queries r0 .. r0 + nb - 1 of one sequence against each key tile it loads, so
+// a key row is read once for all of them; each query keeps its own accumulators and its own
+// causal length (t < n of that row), and the products of each query are the same chain as above.
+// grid.y = sequences x nbps blocks of QB queries (the last block of a sequence may hold fewer).
+// Queries per workgroup of the multi-query indexer.  Two (50 KB of LDS, three workgroups per CU)
+// beat four (100 KB, one per CU): 0.81-0.84 against 0.83-0.85 ms for the selection of 4096
+// prefill queries, 65.5 against 69 us for 4 queries at 131072 keys (one query per workgroup:
+// 1.11 ms and 73 us).
+constexpr int IX_QB = 2;
+
+template <int MODE, bool HIST, bool TILED, int QB>
+__global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma_mq(const float *__restrict__ q,
+                                                                     const float *__restrict__ w, KvView kv,
+                                                                     int64_t t_max, float *__restrict__ scores,
+                                                                     uint32_t *__restrict__ hl,
+                                                                     uint32_t *__restrict__ hcnt, int parts_max,
+                                                                     int nbps)
+{
+    __shared__ float sq[QB * 32 * IXM_QROW];
+    __shared__ uint32_t hs[HIST ? QB * IX_BINS : 1];
+    __shared__ uint32_t sh_scan[IXM_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile math stays scalar
+    const int by = gridDim.y - 1 - blockIdx.y;   // the longest query blocks start first
+    const int sqn = by / nbps, jb = by - sqn * nbps;
+    const int r0 = sqn * kv.qps + jb * QB;
+    const int nb = kv.qps - jb * QB < QB ? kv.qps - jb * QB : QB;
+    int64_t nq[QB];
+    int64_t n = 0;   // the longest causal range of the block
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) {
+        const int64_t l = qi < nb ? seq_len_of(kv, r0 + qi) : 0;
+        nq[qi] = l < t_max ? l : t_max;
+        n = nq[qi] > n ? nq[qi] : n;
+    }
+    const int64_t ntv = (n + 63) / 64;   // tiles holding at least one scored key
+    const int64_t waves_total = (int64_t)gridDim.x * IXM_WAVES;
+
+    // whole tiles past the last scored key
+    for (int qi = 0; qi < nb; ++qi) {
+        float *out = scores + (int64_t)(r0 + qi) * t_max;
+        for (int64_t t = ntv * 64 + (int64_t)blockIdx.x * 64 * IXM_WAVES + tid; t < t_max; t += waves_total * 64)
+            out[t] = -INFINITY;
+    }
+    if ((int64_t)blockIdx.x * IXM_WAVES >= ntv) {   // no tile of a shorter row: an empty list, no query staging
+        if (HIST && tid < nb) hcnt[(int64_t)(r0 + tid) * parts_max + blockIdx.x] = 0u;
+        return;
+    }
+
+    if (HIST)
+        for (int i = tid; i < QB * IX_BINS; i += 64 * IXM_WAVES) hs[i] = 0u;
+    // queries to LDS: all loads in flight before the first store (rows past nb repeat the last)
+    constexpr int QL = 32 * 32 / (64 * IXM_WAVES);
+    float4 qv[QB * QL];
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) {
+        const float4 *qb = reinterpret_cast<const float4 *>(q + (int64_t)(r0 + (qi < nb ? qi : nb - 1)) * 32 * 128);
+#pragma unroll
+        for (int k = 0; k < QL; ++k) qv[qi * QL + k] = qb[tid + k * 64 * IXM_WAVES];
+    }
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi)
+#pragma unroll
+        for (int k = 0; k < QL; ++k) {
+            const int i = tid + k * 64 * IXM_WAVES;
+            *reinterpret_cast<float4 *>(&sq[(qi * 32 + (i >> 5)) * IXM_QROW + (i & 31) * 4]) = qv[qi * QL + k];
+        }
+    __syncthreads();
+
+    int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
+    if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
+    const float *qrow = &sq[(lane & 31) * IXM_QROW];
+
+    // stand-in for keys without a row: the query block (512 B rows), or the pool's first tile
+    const float *qraw = TILED ? kv.ic + 4 * lane : q + (int64_t)r0 * 32 * 128;
+    bool valid, valid_n = false;
+    const float *p = ix_key_ptr<MODE, TILED>(kv, r0, tile, lane, n, qraw, valid);
+    v32f KA, KB, acc[QB];
+    ix_load_slice<TILED>(KA, p, 0);
+    __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
+    ix_load_slice<TILED>(KB, p, 1);
+    for (; tile < ntv; tile += waves_total) {
+        // the next tile's first two slices are loaded unconditionally (from the query block
+        // when there is no next tile) so every iteration leaves the same loads in flight
+        const int64_t nxt = tile + waves_total;
+        const float *pn = qraw;
+        valid_n = false;
+        if (nxt < ntv) pn = ix_key_ptr<MODE, TILED>(kv, r0, nxt, lane, n, qraw, valid_n);
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+#pragma unroll
+            for (int r = 0; r < 32; ++r) acc[qi][r] = 0.f;
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+            if (qi < nb) ix_slice(acc[qi], KA, qrow + qi * 32 * IXM_QROW, 0);
+        ix_load_slice<TILED>(KA, p, 2);
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+            if (qi < nb) ix_slice(acc[qi], KB, qrow + qi * 32 * IXM_QROW, 1);
+        ix_load_slice<TILED>(KB, p, 3);
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+            if (qi < nb) ix_slice(acc[qi], KA, qrow + qi * 32 * IXM_QROW, 2);
+        ix_load_slice<TILED>(KA, pn, 0);
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+            if (qi < nb) ix_slice(acc[qi], KB, qrow + qi * 32 * IXM_QROW, 3);
+        ix_load_slice<TILED>(KB, pn, 1);
+        const int64_t t = tile * 64 + lane;
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi) {
+            if (qi < nb) {
+                const float s = ix_fold(acc[qi], w + (int64_t)(r0 + qi) * 32);
+                const bool in = t < nq[qi];
+                const float sc = valid && in ? s : -INFINITY;
+                if (t < t_max) scores[(int64_t)(r0 + qi) * t_max + t] = sc;
+                if (HIST && in) atomicAdd(&hs[qi * IX_BINS + (order_key(sc) >> 21)], 1u);
+            }
+        }
+        p = pn;
+        valid = valid_n;
+    }
+    }
+    if (HIST) {
+        __syncthreads();
+        for (int qi = 0; qi < nb; ++qi)
+            hist_write_list<64 * IXM_WAVES>(hs + qi * IX_BINS,
+                                            hl + (int64_t)(r0 + qi) * HL_CAP * parts_max + blockIdx.x, parts_max,
+                                            hcnt + (int64_t)(r0 + qi) * parts_max + blockIdx.x, sh_scan);
+    }
+}
+
 // workgroups per row of index_scores_mfma (the histogram parts of a row)
 static int64_t ixm_grid_x(int32_t B, int64_t t_max, bool tiled)
 {
@@ -334,19 +467,38 @@ mla_status launch_index_scores(const float *q, const float *w, int32_t B, int32_
     if (hd == 128 && n_ih == 32 && aligned) {
         const int mode = !kv.bt ? 0 : (kv.bs % 64 == 0 ? 1 : 2);
         if (kv.ic_tiled && mode == 2) return fail(MLA_ERR_UNSUPPORTED, "index: tiled keys need block_size % 64 == 0");
-        const int64_t bx = ixm_grid_x(B, t_max, kv.ic_tiled != 0);
+        // queries of one sequence (qps > 1) share their key tiles, IX_QB per workgroup
+        const bool multi = kv.qps > 1 && B % kv.qps == 0;
+        const int nbps = multi ? (kv.qps + IX_QB - 1) / IX_QB : 1;
+        const int64_t gy = multi ? (int64_t)(B / kv.qps) * nbps : B;
+        int64_t bx = ixm_grid_x(multi ? (int32_t)gy : B, t_max, kv.ic_tiled != 0);
+        if (multi) {
+            // about four workgroups per CU over the launch (query blocks of a prefill differ in length
+            // by up to the whole range, so many short workgroups even out the tail), at least one
+            // tile per wave
+            const int64_t want = (1024 + gy - 1) / gy, most = ((t_max + 63) / 64 + IXM_WAVES - 1) / IXM_WAVES;
+            bx = want < most ? want : most;
+            if (bx < 1) bx = 1;
+        }
         uint32_t *hl = nullptr, *hc = nullptr;
         int pm = 0;
         if (hist) {
+            if (multi && bx > hist->parts_max) bx = hist->parts_max;
             if (bx > hist->parts_max) return fail(MLA_ERR_UNSUPPORTED, "index: histogram parts exceed the workspace");
             hist->parts = (int)bx;
             hl = hist->hl;
             hc = hist->hcnt;
             pm = hist->parts_max;
         }
-        const dim3 g((unsigned)bx, (unsigned)B), blk(64 * IXM_WAVES);
-#define IX_LAUNCH(M, H, TL) \
-    hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, hl, hc, pm)
+        const dim3 g((unsigned)bx, (unsigned)gy), blk(64 * IXM_WAVES);
+#define IX_LAUNCH(M, H, TL)                                                                                         \
+    do {                                                                                                            \
+        if (multi)                                                                                                  \
+            hipLaunchKernelGGL((index_scores_mfma_mq<M, H, TL, IX_QB>), g, blk, 0, s, q, w, kv, t_max, scores, hl,  \
+                               hc, pm, nbps);                                                                       \
+        else                                                                                                        \
+            hipLaunchKernelGGL((index_scores_mfma<M, H, TL>), g, blk, 0, s, q, w, kv, t_max, scores, hl, hc, pm);   \
+    } while (0)
         const bool h = hist != nullptr;
         if (kv.ic_tiled) {
             if (mode == 0) { if (h) IX_LAUNCH(0, true, true); else IX_LAUNCH(0, false, true); }

@@ -178,6 +178,46 @@ def test_prefill_select_per_query(S, pb, k, tiled):
         assert int(nsel[i]) == rn and np.array_equal(sel[i], rs), i
 
 
+@pytest.mark.parametrize("layout", ["rows", "tiled", "paged64", "paged16", "paged64_tiled"])
+def test_prefill_select_every_row_all_layouts(layout):
+    """The multi-query indexer (queries of the sequence in groups of two per workgroup, a ragged last
+    group of one) in every addressing mode: every row's scores bit for bit against the oracle over its
+    causal keys (-inf after), and every row's selection."""
+    S, pb, k = 67, 130, 64
+    T = pb + S
+    rng = np.random.default_rng(790 + len(layout))
+    tiled = layout.endswith("tiled")
+    if layout.startswith("paged"):
+        bs = 64 if layout.startswith("paged64") else 16
+        nblk = (T + bs - 1) // bs + 2
+        perm = rng.permutation(nblk).astype(np.int32)
+        bt = perm[None, : (T + bs - 1) // bs].copy()
+        ic_pool = rng.standard_normal((nblk * bs, 128)).astype(np.float32)
+        t = np.arange(T)
+        ic = ic_pool[bt[0, t // bs].astype(np.int64) * bs + t % bs]
+        pool = synth.tile_index_keys(ic_pool) if tiled else ic_pool
+        z = np.zeros((nblk * bs, 8), np.uint16)
+        kv = mla.KvCache(dev_bf16(z), dev_bf16(z), dev(pool), max_seq_len=T, block_table=dev(bt), block_size=bs,
+                         ic_layout=mla.MLA_IC_TILE64 if tiled else mla.MLA_IC_ROWS)
+    else:
+        Tp = (T + 63) // 64 * 64
+        ic = rng.standard_normal((Tp, 128)).astype(np.float32)
+        z = np.zeros((Tp, 8), np.uint16)
+        kv = mla.KvCache(dev_bf16(z), dev_bf16(z), dev(synth.tile_index_keys(ic) if tiled else ic), max_seq_len=T,
+                         seq_stride=Tp, ic_layout=mla.MLA_IC_TILE64 if tiled else mla.MLA_IC_ROWS)
+    qi = rng.standard_normal((S, 32, 128)).astype(np.float32)
+    wi = rng.standard_normal((S, 32)).astype(np.float32)
+    log(f"prefill select every row layout={layout}")
+    sc, sel, nsel = (host(x) for x in mla.dsa_prefill_select(dev(qi), dev(wi), kv, pb, k))
+    for i in range(S):
+        n = pb + i + 1
+        ref = oracle.index_scores(qi[i], wi[i], ic[:n])
+        assert np.array_equal(sc[i, :n].view(np.uint32), ref.view(np.uint32)), i
+        assert np.all(np.isneginf(sc[i, n:])), i
+        rs, rn = oracle.topk(ref, n, k)
+        assert int(nsel[i]) == rn and np.array_equal(sel[i], rs), i
+
+
 def test_dsa_prefill_full_4096():
     """DSA in prefill at S = T = 4096, k = 2048: per-query selection, then sparse attention on both
     paths; 64 evenly spaced rows on all heads against the oracle over each row's selected keys."""
