@@ -23,22 +23,29 @@ __device__ __forceinline__ int64_t cw_row(const KvView &v, int b, int n_seq, int
     return r < v.rows ? r : -1;
 }
 
-// One wave per token.  Every load of the token (the kv_a row, the indexer key row, the gains) is
+// One wave per token, CW_TPW tokens per workgroup.  Every load of the token (the kv_a row, the indexer key row, the gains) is
 // issued before the first reduction waits on any of them; lane l holds columns l, l + 64, .. .
 constexpr int CW_LC = 2048 / 64, CW_RP = 512 / 2 / 64, CW_IC = 256 / 64;   // per-lane capacities
 
+constexpr int CW_TPW = 4;   // tokens (waves) per workgroup
+
 template <typename TIN, typename TKV>
-__global__ __launch_bounds__(64) void cache_write_kernel(const TIN *__restrict__ comp, const TIN *__restrict__ ik,
-                                                         const int32_t *__restrict__ seq,
-                                                         const int32_t *__restrict__ pos, int n_seq, KvView kv,
-                                                         int L, int rope, int hd, const float *__restrict__ kv_gain,
-                                                         const float *__restrict__ gamma,
-                                                         const float *__restrict__ beta, int ix_off, int ix_rdim,
-                                                         float eps_kv, float eps_ix, double theta)
+__global__ __launch_bounds__(64 * CW_TPW) void cache_write_kernel(const TIN *__restrict__ comp,
+                                                                  const TIN *__restrict__ ik,
+                                                                  const int32_t *__restrict__ seq,
+                                                                  const int32_t *__restrict__ pos, int64_t n_tok,
+                                                                  int n_seq, KvView kv, int L, int rope, int hd,
+                                                                  const float *__restrict__ kv_gain,
+                                                                  const float *__restrict__ gamma,
+                                                                  const float *__restrict__ beta, int ix_off,
+                                                                  int ix_rdim, float eps_kv, float eps_ix, double theta)
 {
-    __shared__ float ys[256];
-    const int64_t j = blockIdx.x;
-    const int lane = threadIdx.x;
+    __shared__ float ys_all[CW_TPW][256];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float *ys = ys_all[wave];
+    const int64_t jt = (int64_t)blockIdx.x * CW_TPW + wave;
+    const bool live = jt < n_tok;              // waves past the last token only pass the barrier
+    const int64_t j = live ? jt : n_tok - 1;
     const int b = seq[j];
     const int64_t p = pos[j];
     const TIN *cj = comp + j * (int64_t)(L + rope);
@@ -65,8 +72,8 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const TIN *__restrict__
         gk[u] = (gamma && c < hd) ? gamma[c] : 1.f;
         bk[u] = (beta && c < hd) ? beta[c] : 0.f;
     }
-    const int64_t row = cw_row(kv, b, n_seq, p);
-    if (row < 0) return;   // wave-uniform
+    const int64_t row = live ? cw_row(kv, b, n_seq, p) : -1;
+    const bool ok = row >= 0;   // wave-uniform; a wave without a row writes nothing
     // Lc = comp[0:L] / sqrt(mean(comp[0:L]^2) + eps) * gain
     float ss = 0.f;
 #pragma unroll
@@ -77,57 +84,69 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const TIN *__restrict__
 #pragma unroll
     for (int u = 0; u < CW_LC; ++u) {
         const int c = lane + 64 * u;
-        if (c < L) st(lc + c, xl[u] * inv * gl[u]);
+        if (ok && c < L) st(lc + c, xl[u] * inv * gl[u]);
     }
-    // Rc = RoPE(comp[L:L+rope]) at the token's position
     TKV *rc = const_cast<TKV *>(reinterpret_cast<const TKV *>(kv.rc)) + row * rope;
+    // Ic = RoPE over [ix_off, ix_off + ix_rdim) of LayerNorm(ik)
+    float *ic = const_cast<float *>(kv.ic);
+    const int rh = kj ? ix_rdim >> 1 : 0;
+    auto ic_at = [&](int c) {
+        return kv.ic_tiled ? ic + ((row >> 6) * (hd >> 2) + (c >> 2)) * 256 + (row & 63) * 4 + (c & 3)
+                           : ic + row * hd + c;
+    };
+    if (kj) {
+        float s1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < CW_RP; ++u) {
-        const int q = lane + 64 * u;
-        if (q < half) {
-            float lo, hi;
-            rope_pair(ra[u], rb[u], q, rope, (double)p, theta, lo, hi);
+        for (int u = 0; u < CW_IC; ++u) s1 += xk[u];
+        const float mean = wave_sum(s1) / (float)hd;
+        float s2 = 0.f;
+#pragma unroll
+        for (int u = 0; u < CW_IC; ++u) {
+            const int c = lane + 64 * u;
+            const float dlt = c < hd ? xk[u] - mean : 0.f;
+            s2 = __builtin_fmaf(dlt, dlt, s2);
+        }
+        const float is = 1.0f / __builtin_sqrtf(wave_sum(s2) / (float)hd + eps_ix);
+#pragma unroll
+        for (int u = 0; u < CW_IC; ++u) {
+            const int c = lane + 64 * u;
+            if (c < hd) {
+                const float y = __builtin_fmaf((xk[u] - mean) * is, gk[u], bk[u]);
+                ys[c] = y;
+                if (ok && (c < ix_off || c >= ix_off + ix_rdim)) *ic_at(c) = y;   // dims outside the rotated slice
+            }
+        }
+        __syncthreads();
+    }
+    // the rotations: pair job i < half is pair i of the Rc tail (comp[L:L+rope], held in ra/rb by
+    // lane i % 64), job half + q pair q of the Ic slice; every lane takes jobs lane, lane + 64, .. so
+    // each pair's angle (fp64) is formed once
+    for (int u = 0; ok && u * 64 < half + rh; ++u) {
+        const int pi = lane + 64 * u;
+        if (pi >= half + rh) break;
+        const bool is_rc = pi < half;
+        const int q = is_rc ? pi : pi - half;
+        float a = 0.f, bb = 0.f;
+        if (is_rc) {
+#pragma unroll
+            for (int v = 0; v < CW_RP; ++v)
+                if (v == u) {
+                    a = ra[v];
+                    bb = rb[v];
+                }
+        } else {
+            a = ys[ix_off + 2 * q];
+            bb = ys[ix_off + 2 * q + 1];
+        }
+        float lo, hi;
+        rope_pair(a, bb, q, is_rc ? rope : ix_rdim, (double)p, theta, lo, hi);
+        if (is_rc) {
             st(rc + q, lo);
             st(rc + half + q, hi);
+        } else {
+            *ic_at(ix_off + q) = lo;
+            *ic_at(ix_off + rh + q) = hi;
         }
-    }
-    if (!kj) return;
-    // Ic = RoPE over [ix_off, ix_off + ix_rdim) of LayerNorm(ik)
-    float s1 = 0.f;
-#pragma unroll
-    for (int u = 0; u < CW_IC; ++u) s1 += xk[u];
-    const float mean = wave_sum(s1) / (float)hd;
-    float s2 = 0.f;
-#pragma unroll
-    for (int u = 0; u < CW_IC; ++u) {
-        const int c = lane + 64 * u;
-        const float dlt = c < hd ? xk[u] - mean : 0.f;
-        s2 = __builtin_fmaf(dlt, dlt, s2);
-    }
-    const float is = 1.0f / __builtin_sqrtf(wave_sum(s2) / (float)hd + eps_ix);
-#pragma unroll
-    for (int u = 0; u < CW_IC; ++u) {
-        const int c = lane + 64 * u;
-        if (c < hd) ys[c] = __builtin_fmaf((xk[u] - mean) * is, gk[u], bk[u]);
-    }
-    __syncthreads();
-    float *ic = const_cast<float *>(kv.ic);
-    const int rh = ix_rdim >> 1;
-#pragma unroll
-    for (int u = 0; u < CW_IC; ++u) {
-        const int c = lane + 64 * u;
-        if (c >= hd) continue;
-        float o = ys[c];
-        const int sidx = c - ix_off;
-        if (sidx >= 0 && sidx < ix_rdim) {
-            const int q = sidx < rh ? sidx : sidx - rh;
-            float lo, hi;
-            rope_pair(ys[ix_off + 2 * q], ys[ix_off + 2 * q + 1], q, ix_rdim, (double)p, theta, lo, hi);
-            o = sidx < rh ? lo : hi;
-        }
-        float *dst = kv.ic_tiled ? ic + ((row >> 6) * (hd >> 2) + (c >> 2)) * 256 + (row & 63) * 4 + (c & 3)
-                                 : ic + row * hd + c;
-        *dst = o;
     }
 }
 
@@ -139,10 +158,10 @@ mla_status launch_cache_write(const void *comp, const void *ik, mla_dtype in_dt,
 {
     if (n == 0) return MLA_OK;
     if (n > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "cache write: too many tokens");
-    const dim3 g((unsigned)n), blk(64);
+    const dim3 g((unsigned)((n + CW_TPW - 1) / CW_TPW)), blk(64 * CW_TPW);
 #define MLA_CW(TI, TK)                                                                                            \
-    hipLaunchKernelGGL((cache_write_kernel<TI, TK>), g, blk, 0, s, (const TI *)comp, (const TI *)ik, seq, pos, n_seq, \
-                       kv, L, rope, hd, kv_gain, gamma, beta, ix_off, ix_rdim, eps_kv, eps_ix, theta)
+    hipLaunchKernelGGL((cache_write_kernel<TI, TK>), g, blk, 0, s, (const TI *)comp, (const TI *)ik, seq, pos, n, \
+                       n_seq, kv, L, rope, hd, kv_gain, gamma, beta, ix_off, ix_rdim, eps_kv, eps_ix, theta)
     if (in_dt == MLA_FP32 && kv_dt == MLA_FP32) MLA_CW(float, float);
     else if (in_dt == MLA_FP32) MLA_CW(float, bf16_t);
     else if (kv_dt == MLA_FP32) MLA_CW(bf16_t, float);

@@ -36,10 +36,12 @@ def _in_vals(a, bf16):
     return synth.bf16_bits_to_f32(synth.to_bf16_bits(a)) if bf16 else np.asarray(a, np.float32)
 
 
-@pytest.mark.parametrize("in_bf16,kv_bf16,tiled", [(False, False, False), (False, True, True), (True, True, False),
-                                                   (True, False, True)])
-def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled):
-    rng = np.random.default_rng(600 + 2 * in_bf16 + kv_bf16)
+@pytest.mark.parametrize("in_bf16,kv_bf16,tiled,per", [(False, False, False, 100), (False, True, True, 100),
+                                                       (True, True, False, 100), (True, False, True, 100),
+                                                       (True, True, True, 97)])
+def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled, per):
+    """per: tokens per sequence (97: a token count that leaves the last workgroup part-filled)."""
+    rng = np.random.default_rng(600 + 2 * in_bf16 + kv_bf16 + per)
     B, L, rope, hd = 3, 512, 64, 128
     bs = 64 if tiled else 16                        # a tiled indexer pool holds whole 64-row tiles per block
     max_blocks = 512 // bs
@@ -48,10 +50,10 @@ def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled):
     perm = rng.permutation(n_blocks).astype(np.int32)
     bt = perm.reshape(B, max_blocks).copy()
     bt[1, 5] = -1                                   # a hole: tokens there are not written
-    seq = np.repeat(np.arange(B, dtype=np.int32), 100)
+    seq = np.repeat(np.arange(B, dtype=np.int32), per)
     allowed = [np.arange(max_blocks * bs)] * B
     allowed[1] = np.setdiff1d(allowed[1], np.arange(5 * bs, 6 * bs))
-    pos = np.concatenate([np.sort(rng.choice(a, 100, replace=False)) for a in allowed]).astype(np.int32)
+    pos = np.concatenate([np.sort(rng.choice(a, per, replace=False)) for a in allowed]).astype(np.int32)
     pos[150] = 5 * bs + 3                          # lands in the hole of sequence 1
     n = seq.size
     comp = (rng.standard_normal((n, L + rope)) * 2.0 + 0.3).astype(np.float32)
@@ -66,7 +68,7 @@ def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled):
     ic = torch.full((rows, hd), 7.0, dtype=torch.float32, device="cuda")
     kv = mla.KvCache(lc, rc, ic, max_seq_len=max_blocks * bs, block_table=dev(bt), block_size=bs,
                      ic_layout=mla.MLA_IC_TILE64 if tiled else mla.MLA_IC_ROWS)
-    log(f"cache write in_bf16={in_bf16} kv_bf16={kv_bf16} tiled={tiled}")
+    log(f"cache write in_bf16={in_bf16} kv_bf16={kv_bf16} tiled={tiled} per={per}")
     mla.mla_cache_write(_to_dev(comp, in_bf16), dev(seq), dev(pos), kv, B, ik=_to_dev(ik, in_bf16), kv_gain=dev(gain),
                         ix_gamma=dev(gm), ix_beta=dev(bt_), ix_rope_off=ix_off, ix_rope_dim=ix_rd)
     r_lc, r_rc, r_ic = oracle.cache_write(_in_vals(comp, in_bf16), _in_vals(ik, in_bf16), seq, pos, L, rope, rows=rows,
