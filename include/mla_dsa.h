@@ -334,7 +334,8 @@ mla_status mla_prefill_nonabsorbed(const void *q, mla_dtype q_dt, const void *kv
  *   q      device [S][H][qk_nope + qk_rope] (tail already rotated), q_dt
  *   kv     host struct for sequence 0 (seq_len is not read; rows 0 .. pos_base + S - 1 used, every
  *          one mapped to a pool row)
- *   sel    device int32 [S][sel_stride] or NULL; nsel device int32 [S]
+ *   sel    device int32 [S][sel_stride] or NULL; nsel device int32 [S]; on the non-absorbed path
+ *          sel_stride must stay below 2^19 (MLA_ERR_UNSUPPORTED otherwise)
  *   out    device fp32 [S][H][v_head]
  *   ws     at least mla_attention_workspace_bytes(d, S, pos_base, sel ? sel_stride : 0, g_absorb)
  * mla_attention_absorbs(S, g_absorb) returns 1 when the call takes the absorbed path.

@@ -74,20 +74,30 @@ __global__ __launch_bounds__(MASK_NT) void sel_mask_kernel(const int32_t *__rest
     __syncthreads();
     const int64_t t_lo = 32 * g0, t_hi = (32 * (g0 + ng) < T) ? 32 * (g0 + ng) : T;
     const int64_t qn = S - c0 < MASK_QB ? S - c0 : MASK_QB;
-    const int64_t total = qn * sel_stride;          // entries of the workgroup's rows of sel
+    // entries of the workgroup's rows of sel: at most MASK_QB * 65536 = 2^21, so 32-bit indices,
+    // and the row of entry f from an fp32 reciprocal (exact below 2^24) corrected by one step
+    const int total = qn > 0 ? (int)qn * sel_stride : 0;
+    const float rcp = 1.0f / (float)sel_stride;
     const int32_t *base = sel + c0 * sel_stride;
-    for (int64_t f0 = 0; f0 < total; f0 += (int64_t)MASK_NT * MASK_LD) {
+    for (int f0 = 0; f0 < total; f0 += MASK_NT * MASK_LD) {
         int32_t v[MASK_LD];
 #pragma unroll
         for (int u = 0; u < MASK_LD; ++u) {
-            const int64_t f = f0 + (int64_t)u * MASK_NT + tid;
+            const int f = f0 + u * MASK_NT + tid;
             v[u] = f < total ? base[f] : -1;
         }
 #pragma unroll
         for (int u = 0; u < MASK_LD; ++u) {
-            const int64_t f = f0 + (int64_t)u * MASK_NT + tid;
+            const int f = f0 + u * MASK_NT + tid;
             if (f >= total) continue;
-            const int q = (int)(f / sel_stride), j = (int)(f - (int64_t)q * sel_stride);
+            int q = (int)((float)f * rcp), j = f - q * sel_stride;
+            if (j < 0) {
+                --q;
+                j += sel_stride;
+            } else if (j >= sel_stride) {
+                ++q;
+                j -= sel_stride;
+            }
             const int32_t t = v[u];
             if (j < ns[q] && t >= t_lo && t < t_hi)
                 atomicOr(&m[(int)((t >> 5) - g0) * MASK_QB + q], 1u << (t & 31));
@@ -138,6 +148,8 @@ mla_status launch_attention(const void *q, mla_dtype dt, const void *kv_b, const
         p += al256((size_t)mask_groups(T) * cols * 4);
         const int64_t gy = (mask_groups(T) + MASK_GCH - 1) / MASK_GCH;
         if (gy > 65535) return fail(MLA_ERR_UNSUPPORTED, "attention: key range too long for the selection mask");
+        if ((int64_t)MASK_QB * sel_stride >= ((int64_t)1 << 24))
+            return fail(MLA_ERR_UNSUPPORTED, "attention: sel_stride >= 2^19 on the non-absorbed path");
         hipLaunchKernelGGL(sel_mask_kernel, dim3((unsigned)(cols / MASK_QB), (unsigned)gy), dim3(MASK_NT), 0, s, sel,
                            nsel, sel_stride, S, T, mask_groups(T), cols, mask);
         mla_status st = check_launch("sel_mask_kernel");
