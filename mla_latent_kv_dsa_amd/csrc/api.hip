@@ -494,9 +494,11 @@ mla_status mla_attention(const void *q, mla_dtype q_dt, const void *kv_b, mla_dt
     if (q_dt != w_dt || q_dt != kv->kv_dtype) return fail(MLA_ERR_UNSUPPORTED, "attention: q, kv_b and cache dtypes must match");
     if (!isfinite(sm_scale)) return fail(MLA_ERR_ARG, "attention: sm_scale not finite");
     if (sel && (!nsel || sel_stride <= 0)) return fail(MLA_ERR_ARG, "attention: sel needs nsel and sel_stride > 0");
+    const bool ab = attention_absorbs(S, g_absorb);
+    if (sel && !ab && sel_stride >= (1 << 19))
+        return fail(MLA_ERR_UNSUPPORTED, "attention: sel_stride >= 2^19 on the non-absorbed path");
     if (S == 0) return MLA_OK;
     if (!q || !kv_b || !out) return fail(MLA_ERR_ARG, "attention: NULL tensor");
-    const bool ab = attention_absorbs(S, g_absorb);
     st = check_ws("attention", attention_workspace_bytes(*d, S, T, sel ? sel_stride : 0, ab, q_dt), ws, ws_bytes);
     if (st) return st;
     return launch_attention(q, q_dt, kv_b, *d, to_view(v1), S, pos_base, sel, nsel, sel ? sel_stride : 0, sm_scale, ab,

@@ -74,8 +74,9 @@ __global__ __launch_bounds__(MASK_NT) void sel_mask_kernel(const int32_t *__rest
     __syncthreads();
     const int64_t t_lo = 32 * g0, t_hi = (32 * (g0 + ng) < T) ? 32 * (g0 + ng) : T;
     const int64_t qn = S - c0 < MASK_QB ? S - c0 : MASK_QB;
-    // entries of the workgroup's rows of sel: at most MASK_QB * 65536 = 2^21, so 32-bit indices,
-    // and the row of entry f from an fp32 reciprocal (exact below 2^24) corrected by one step
+    // entries of the workgroup's rows of sel: below MASK_QB * 2^19 = 2^24 (the entry point bounds
+    // sel_stride), so 32-bit indices, and the row of entry f from an fp32 reciprocal (exact below
+    // 2^24) corrected by one step
     const int total = qn > 0 ? (int)qn * sel_stride : 0;
     const float rcp = 1.0f / (float)sel_stride;
     const int32_t *base = sel + c0 * sel_stride;
@@ -148,8 +149,6 @@ mla_status launch_attention(const void *q, mla_dtype dt, const void *kv_b, const
         p += al256((size_t)mask_groups(T) * cols * 4);
         const int64_t gy = (mask_groups(T) + MASK_GCH - 1) / MASK_GCH;
         if (gy > 65535) return fail(MLA_ERR_UNSUPPORTED, "attention: key range too long for the selection mask");
-        if ((int64_t)MASK_QB * sel_stride >= ((int64_t)1 << 24))
-            return fail(MLA_ERR_UNSUPPORTED, "attention: sel_stride >= 2^19 on the non-absorbed path");
         hipLaunchKernelGGL(sel_mask_kernel, dim3((unsigned)(cols / MASK_QB), (unsigned)gy), dim3(MASK_NT), 0, s, sel,
                            nsel, sel_stride, S, T, mask_groups(T), cols, mask);
         mla_status st = check_launch("sel_mask_kernel");

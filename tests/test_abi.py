@@ -373,6 +373,7 @@ def test_g_absorb_rule_and_attention_validation(L):
     assert f(g=2) == mla.MLA_ERR_ARG
     assert f(S=-1) == mla.MLA_ERR_ARG
     assert f(sel=FAKE, nsel=None, stride=8) == mla.MLA_ERR_ARG
+    assert f(S=8, g=0, sel=FAKE, nsel=FAKE, stride=1 << 19) == mla.MLA_ERR_UNSUPPORTED   # the key bitmap's limit
     assert f(S=4000, pb=200) == mla.MLA_ERR_ARG          # rows beyond the 4096-row pool
     assert f(S=0) == mla.MLA_OK
     assert L.mla_attention_workspace_bytes(ctypes.byref(d), 4096, 0, 2048, 0) > \
