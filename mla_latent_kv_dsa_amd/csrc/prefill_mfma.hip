@@ -6,19 +6,17 @@
 //
 //   pf_kvb    C[t][n] = sum_l kv_b[n][l] Lc(t)[l], bf16 out ([T][H (nope + v)], head h's k_nope
 //             then v in columns h (nope + v) ..).  Computed as C^T = kv_b . Lc^T in 256 x 256
-//             tiles (wave: 128 x 128) on v_mfma_f32_32x32x16_bf16, K = 512 in steps of 32 staged
-//             in LDS (rows padded to 80 B: conflict-free operand reads), the next step's global
-//             loads in flight during the current step's products.  With n as the row index of
-//             the product every lane holds four consecutive n of one token: 8-byte stores.
-//   pf_attn   per (128-query block, head), 4 waves x 32 queries, 64-key tiles of K (k_nope and
-//             Rc, 256 dims) and V (256 dims) staged in LDS:
-//               S^T = K Q^T      A = K rows from LDS, B = the wave's queries held in registers
-//               online softmax   lane l owns query l % 32 together with lane l ^ 32 (one
-//                                exchange per tile for the maximum and the sum)
-//               O^T += V^T P^T   A = V^T by transposed LDS reads, B = P^T straight from the
-//                                score registers after one v_permlane32_swap per register pair
-//             so all softmax bookkeeping is lane-local; blocks of late queries (the most keys)
-//             are dispatched first.
+//             tiles (wave: 128 x 128) on v_mfma_f32_32x32x16_bf16, K = 512 in steps of 64 copied
+//             straight into LDS through a two-slot ring (16-byte chunks XOR-swizzled: conflict-free
+//             operand reads); one v_permlane32_swap per register pair gives every lane eight
+//             consecutive columns of one token: 16-byte stores.
+//   pf_attn   per (128-query block, head), 64-key tiles of K (k_nope and Rc, 256 dims) and V (256
+//             dims) staged in LDS, two waves per SIMD with split roles:
+//               S-wave  S^T = K Q^T (A = K rows from LDS, B = its 32 queries held in registers),
+//                       masks, online softmax (lane l owns query l % 32 with lane l ^ 32), P to LDS
+//               O-wave  O^T += V^T P^T one tile later (A = V^T by transposed LDS reads, B = P^T
+//                       from LDS), the output at the end
+//             blocks of late queries (the most keys) are dispatched first.
 //
 // MFMA operand layouts (gfx950): v_mfma_f32_32x32x16_bf16 lane l supplies A[l%32][8(l/32)+e]
 // and B[8(l/32)+e][l%32], e = 0..7; result register r of lane l is D[8(r/4)+4(l/32)+r%4][l%32].
@@ -176,7 +174,7 @@ constexpr size_t PA_MASK_LDS = 2 * 2 * PA_BQ * 4;
 constexpr int PA_PF = 6;       // score operand reads in flight
 
 
-// grid (ceil(S / 128) * H), 256 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
+// grid (ceil(S / 128) * H), 512 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
 // Workgroups go to the 8 XCDs round-robin (id % 8); XCD x runs heads x, x + 8, .. one after the
 // other, each as all of its query blocks at once (late ones first), so the head's K and V (4 MB
 // at 4096 tokens) are fetched into that XCD's L2 once and shared by its 32 CUs.
@@ -184,64 +182,64 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 // keys in one block, looked up once per tile with a scalar load); 2: any block table (one lookup
 // per key, a vector load whose wait also lands the copies in flight).
 // MASK: keys are further restricted per query by a bitmap (bit t % 32 of word
-// mask[(t / 32) * mask_stride + i] set = key t attended by query i); wave 0 copies a tile's words into
-// LDS with its K rows, so the same waits cover them.
+// mask[(t / 32) * mask_stride + i] set = key t attended by query i); wave 0 copies a tile's words
+// into LDS with its K rows, so the same waits cover them.
+//
+// The work of a tile is split between two waves per SIMD: wave w < 4 (an S-wave) and wave w + 4
+// (its O-wave) share SIMD w and the queries 32 w .. 32 w + 31 of the block.  The S-wave forms S^T = K Q^T of a tile, masks it and runs the online softmax; it hands P
+// (bf16, [query][key]) and the tile's rescale factor to its O-wave through LDS, and the O-wave forms
+// O^T += V^T P^T one tile later, so that one wave's value products run while the other computes the
+// next tile's scores.  Two barriers per iteration it = 0 .. ntile:
+//   B_it   K(it), its mask words, and V(it - 1) have landed
+//          S-wave: scores and softmax of tile it (P kept in registers)
+//          O-wave: reads P(it - 1) and its factors, rescales, value products of tile it - 1
+//   B'_it  every P(it - 1) read is done, K(it) and V(it - 1) are consumed
+//          all waves: copies of K(it + 2) (into K(it)'s buffer) and V(it + 1) (into V(it - 1)'s)
+//          S-wave: writes P(it) and its factors
+// so a tile's copies have one and a half iterations to land.  Each wave copies keys 8 w .. 8 w + 7
+// of a tile (K or V halves of two keys per copy, chunk placement as pf_attn).
+constexpr int PW_PROW = 72;                                      // bf16 per P row (64 keys + pad)
+constexpr size_t PW_P_LDS = (size_t)4 * 32 * PW_PROW * 2;         // P of the four wave pairs
+constexpr size_t PW_LDS = PA_LDS + PW_P_LDS + 2 * PA_BQ * 4;      // + rescale factors and final sums
+
 template <int NOPE, typename OUT, int MODE, bool MASK>
-__global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C, KvView kv,
-                                               int S, int pos_base, float scale_log2, OUT *__restrict__ out,
-                                               const uint32_t *__restrict__ mask, int mask_stride)
+__global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C,
+                                                  KvView kv, int S, int pos_base, float scale_log2,
+                                                  OUT *__restrict__ out, const uint32_t *__restrict__ mask,
+                                                  int mask_stride)
 {
     extern __shared__ __attribute__((aligned(16))) char pa_smem[];
-    bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 tiles][K rows, V rows][64][PA_KROW]
-    constexpr int QD = NOPE + PF_R;            // query / key width (256 for nope 192)
-    constexpr int KS = QD / 16;                // K steps of the score product
-    constexpr int N = PF_H * (NOPE + PF_V);    // row length of C
+    bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 buffers][K rows, V rows][64][PA_KROW]
+    bf16_t *sP = reinterpret_cast<bf16_t *>(pa_smem + PA_LDS);           // [4 pairs][32 queries][PW_PROW]
+    float *sAl = reinterpret_cast<float *>(pa_smem + PA_LDS + PW_P_LDS);   // [128] rescale factor of P
+    float *sL = sAl + PA_BQ;                                               // [128] final sums
+    char *sMask = pa_smem + PW_LDS;                                        // [2][2 groups][128 queries]
+    constexpr int QD = NOPE + PF_R;
+    constexpr int KS = QD / 16;
+    constexpr int N = PF_H * (NOPE + PF_V);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pw = wave & 3;                   // the wave pair (SIMD) and its 32 queries
     const int l32 = lane & 31, hi = lane >> 5;
     const int nqb = (S + PA_BQ - 1) / PA_BQ;
     const int xcd = (int)blockIdx.x & 7, idx = (int)blockIdx.x >> 3;
     const int h = xcd + 8 * (idx / nqb);
     const int qb = nqb - 1 - idx % nqb;        // late query blocks (most keys) first
     const int i0 = qb * PA_BQ;
-    const int iq = i0 + 32 * wave + l32;       // this lane's query
+    const int iq = i0 + 32 * pw + l32;         // this lane's query
     const bf16_t *rc = reinterpret_cast<const bf16_t *>(kv.rc);
-
-    // the wave's queries as the B operand of S^T (query l32, dims 16 ks + 8 hi ..)
-    uint4 bq[KS];
-    {
-        const bf16_t *qr = q + ((int64_t)(iq < S ? iq : S - 1) * PF_H + h) * QD + 8 * hi;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
-    }
-    const int64_t qpos = (int64_t)pos_base + iq;                       // keys t <= qpos
     const int i_last = i0 + PA_BQ - 1 < S - 1 ? i0 + PA_BQ - 1 : S - 1;
-    const int64_t kend = (int64_t)pos_base + i_last + 1;               // keys of the block
+    const int64_t kend = (int64_t)pos_base + i_last + 1;
     const int ntile = (int)((kend + PA_BK - 1) / PA_BK);
-    float m_run = -INFINITY, l_run = 0.f;
-    pf32x16 o[PF_V / 32];
-#pragma unroll
-    for (int dt = 0; dt < PF_V / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-
-    // staging: wave w copies keys 16 w .. 16 w + 15 of a tile in pairs, one DMA for the K rows and
-    // one for the V rows of a pair (lanes 0..31 the first key, 32..63 the second): position p =
-    // lane % 32 of a K row takes chunk p ^ (key % 32) (k_nope from C, then Rc; chunks past the key
-    // width take chunk 0, never read), of a V row chunk p ^ 4 (key % 4).
     const int pp = lane & 31, kh = lane >> 5;
-    // Rc rows of the wave's 16 keys of tile kt: lane i < 16 resolves key 64 kt + 16 wave + i (the
-    // other lanes repeat them).  Resolved before the tile's copies are issued and complete before
-    // the first one: a block-table load consumed between the copies would make the compiler wait
-    // for every copy in flight (it does not see them).
+
+    // Rc rows of the wave's 8 keys of tile kt: lane i < 8 resolves key 64 kt + 8 wave + i
     auto rows_of = [&](int kt) -> int64_t {
-        const int64_t t0 = (int64_t)kt * PA_BK + 16 * wave + (lane & 15);
+        const int64_t t0 = (int64_t)kt * PA_BK + 8 * wave + (lane & 7);
         const int64_t t = t0 < kend ? t0 : kend - 1;
         int64_t row;
         if (MODE == 0) {
-            row = t < kv.rows ? t : -1;   // sequence 0 of a contiguous view: row = position
+            row = t < kv.rows ? t : -1;
         } else if (MODE == 1) {
-            // the tile's block (uniform address): a scalar load, whose wait counts LDS and
-            // scalar traffic only
             const int32_t *pb = kv.bt + (int)((int64_t)kt * PA_BK / kv.bs);
             int32_t blk;
             asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(pb) : "memory");
@@ -253,19 +251,16 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
         return row >= 0 ? row : 0;
     };
     auto settle = [](int64_t x) { asm volatile("" ::"v"((uint32_t)x), "v"((uint32_t)(x >> 32))); };
-    // the eight K copies of the wave go out first, then the eight V copies: the score product of
-    // a tile waits for its K rows only (vmcnt(8)), the value product for the V rows
-    auto stage = [&](int kt, int64_t rrow) {
+    // K rows (k_nope from C, then Rc) of tile kt, and wave 0's copy of its mask words first
+    auto stage_k = [&](int kt, int64_t rrow) {
         bf16_t *dst = sT + (kt & 1) * PA_TILE;
+        if (MASK && wave == 0) {
+            const uint32_t *src = mask + (int64_t)(2 * kt + (lane >> 5)) * mask_stride + i0 + 4 * (lane & 31);
+            pf_dma16(src, pf_lds_addr(sMask + (kt & 1) * 1024));
+        }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            if (MASK && u == 8 && wave == 0) {   // the tile's mask words, after wave 0's K copies
-                const uint32_t *src = mask + (int64_t)(2 * kt + (lane >> 5)) * mask_stride + i0 + 4 * (lane & 31);
-                pf_dma16(src, pf_lds_addr(reinterpret_cast<const char *>(pa_smem) + PA_LDS + (kt & 1) * 1024));
-            }
-            const int i = u & 7;
-            const bool isv = u >= 8;
-            const int r0 = 16 * wave + 2 * i, key = r0 + kh;   // this lane's key of the pair
+        for (int i = 0; i < 4; ++i) {
+            const int r0 = 8 * wave + 2 * i, key = r0 + kh;
             const int64_t t0 = (int64_t)kt * PA_BK + key;
             const int64_t t = t0 < kend ? t0 : kend - 1;
             const int64_t ra = ((int64_t)__builtin_amdgcn_readlane((int)(rrow >> 32), 2 * i) << 32) |
@@ -274,192 +269,241 @@ __global__ __launch_bounds__(256) void pf_attn(const bf16_t *__restrict__ q, con
                                (uint32_t)__builtin_amdgcn_readlane((int)rrow, 2 * i + 1);
             const int64_t rrc = kh ? rb : ra;
             const bf16_t *crow = C + t * (int64_t)N + h * (NOPE + PF_V);
-            const int ck = pp ^ (key & 31), cv = pp ^ (4 * (key & 3));
+            const int ck = pp ^ (key & 31);
             const bf16_t *sk = ck < NOPE / 8 ? crow + 8 * ck : (ck < QD / 8 ? rc + rrc * PF_R + 8 * ck - NOPE : crow);
-            if (!isv) pf_dma16(sk, pf_lds_addr(dst + r0 * PA_KROW));
-            else pf_dma16(crow + NOPE + 8 * cv, pf_lds_addr(dst + (PA_BK + r0) * PA_KROW));
+            pf_dma16(sk, pf_lds_addr(dst + r0 * PA_KROW));
         }
     };
-    const int G = lane >> 4, j16 = lane & 15;   // transposed-read address inside a 16-key step
-    const int r3 = j16 >> 2;                    // row % 4 of this lane's transposed reads
-    const int tr_off = PA_BK * PA_KROW + (8 * (G >> 1) + r3) * PA_KROW + 8 * (2 * (G & 1) + ((j16 & 3) >> 1)) +
-                       4 * (j16 & 1);
-    {
-        const int64_t rr = rows_of(0);
-        settle(rr);
-        // the query operands too are complete before the first copy (same reason)
+    // V rows of tile kt
+    auto stage_v = [&](int kt) {
+        bf16_t *dst = sT + (kt & 1) * PA_TILE;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bq[ks].x), "v"(bq[ks].y), "v"(bq[ks].z), "v"(bq[ks].w));
-        stage(0, rr);
-    }
-    for (int kt = 0; kt < ntile; ++kt) {
-        const int64_t k0 = (int64_t)kt * PA_BK;
-        // tile kt has landed in every wave's share, and every wave is done with tile kt - 1, whose
-        // buffer the next copies fill: one barrier per tile
-        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");   // the K rows of tile kt
-        if (kt + 1 < ntile) {
-            const int64_t rr = rows_of(kt + 1);
+        for (int i = 0; i < 4; ++i) {
+            const int r0 = 8 * wave + 2 * i, key = r0 + kh;
+            const int64_t t0 = (int64_t)kt * PA_BK + key;
+            const int64_t t = t0 < kend ? t0 : kend - 1;
+            const bf16_t *crow = C + t * (int64_t)N + h * (NOPE + PF_V);
+            const int cv = pp ^ (4 * (key & 3));
+            pf_dma16(crow + NOPE + 8 * cv, pf_lds_addr(dst + (PA_BK + r0) * PA_KROW));
+        }
+    };
+    // K(it + 2) and V(it + 1) after B'_it (it = -1: the prologue's second half)
+    auto stage_point = [&](int it) {
+        if (it + 2 < ntile) {
+            const int64_t rr = rows_of(it + 2);
             settle(rr);
-            stage(kt + 1, rr);
+            stage_k(it + 2, rr);
         }
-        const bf16_t *tk = sT + (kt & 1) * PA_TILE;
-        // S^T: two 32-key tiles; register r of s[mt] is key k0 + 32 mt + 8 (r/4) + 4 hi + r%4
-        // Step i of 2 KS takes key tile i % 2 and slice i / 2; the LDS operand reads run PA_PF steps
-        // ahead of their products (a ring of registers), so their latency hides behind the
-        // matrix cores instead of stalling each product.
-        pf32x16 s[2];
+        if (it + 1 < ntile) stage_v(it + 1);
+    };
+    // B_it: K(it) (with its mask words) and V(it - 1) landed; younger than them are the copies of
+    // stage point it - 1 (wave 0's mask copy among them only makes it wait longer)
+    auto top_wait = [&](int it) {
+        const int young = (it + 1 < ntile ? 4 : 0) + (it < ntile ? 4 : 0);
+        if (young == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+        else if (young == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    if (wave < 4) {
+        // ---------------------------------------------------------------- S-wave
+        uint4 bq[KS];
         {
+            const bf16_t *qr = q + ((int64_t)(iq < S ? iq : S - 1) * PF_H + h) * QD + 8 * hi;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-            // K row 32 mt + l32, dims 16 ks + 8 hi ..: chunk 2 ks + hi at position (2 ks + hi) ^ l32
-            const bf16_t *ka = tk + l32 * PA_KROW;
-            auto a_op = [&](int i) {
-                return *reinterpret_cast<const uint4 *>(ka + (i & 1) * 32 * PA_KROW + 8 * ((2 * (i >> 1) + hi) ^ l32));
-            };
-            uint4 ring[PA_PF];
-#pragma unroll
-            for (int i = 0; i < PA_PF; ++i) ring[i] = a_op(i);
-#pragma unroll
-            for (int i = 0; i < 2 * KS; ++i) {
-                const uint4 a = ring[i % PA_PF];
-                if (i + PA_PF < 2 * KS) ring[i % PA_PF] = a_op(i + PA_PF);
-                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(a), pf_bf16x8(bq[i >> 1]), s[i & 1], 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS reads
-#pragma unroll
-            for (int i = 0; i < 2 * KS - PA_PF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
         }
-        if (MASK) {   // keys outside the query's selection
-            const uint32_t *mw = reinterpret_cast<const uint32_t *>(pa_smem + PA_LDS + (kt & 1) * 1024);
+        const int64_t qpos = (int64_t)pos_base + iq;
+        float m_run = -INFINITY, l_run = 0.f;
+        {
+            const int64_t rr = rows_of(0);
+            settle(rr);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint32_t w = mw[PA_BQ * mt + 32 * wave + l32];
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (!((w >> (8 * (r >> 2) + 4 * hi + (r & 3))) & 1u)) s[mt][r] = -INFINITY;
-            }
+            for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(bq[ks].x), "v"(bq[ks].y), "v"(bq[ks].z), "v"(bq[ks].w));
+            stage_k(0, rr);
+            stage_point(-1);
         }
-        // causal mask, only on tiles that reach past the wave's first query (positions < 2^31);
-        // running maximum of the raw scores (lanes l and l ^ 32 hold the same query)
-        const int qpos32 = (int)qpos;
-        if (k0 + PA_BK - 1 > (int64_t)pos_base + i0 + 32 * wave) {
+        bf16_t *prow = sP + (pw * 32 + l32) * PW_PROW;
+        for (int it = 0; it <= ntile; ++it) {
+            top_wait(it);
+            uint2 pk[2][4];
+            float alpha = 1.f;
+            if (it < ntile) {
+                const int64_t k0 = (int64_t)it * PA_BK;
+                const bf16_t *tk = sT + (it & 1) * PA_TILE;
+                pf32x16 s[2];
+                {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = (int)k0 + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (t > qpos32) s[mt][r] = -INFINITY;
+                        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+                    const bf16_t *ka = tk + l32 * PA_KROW;
+                    auto a_op = [&](int i) {
+                        return *reinterpret_cast<const uint4 *>(ka + (i & 1) * 32 * PA_KROW +
+                                                                8 * ((2 * (i >> 1) + hi) ^ l32));
+                    };
+                    uint4 ring[PA_PF];
+#pragma unroll
+                    for (int i = 0; i < PA_PF; ++i) ring[i] = a_op(i);
+#pragma unroll
+                    for (int i = 0; i < 2 * KS; ++i) {
+                        const uint4 a = ring[i % PA_PF];
+                        if (i + PA_PF < 2 * KS) ring[i % PA_PF] = a_op(i + PA_PF);
+                        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf_bf16x8(a), pf_bf16x8(bq[i >> 1]), s[i & 1],
+                                                                           0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                    for (int i = 0; i < 2 * KS - PA_PF; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < PA_PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
+                if (MASK) {
+                    const uint32_t *mw = reinterpret_cast<const uint32_t *>(sMask + (it & 1) * 1024);
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const uint32_t w = mw[PA_BQ * mt + 32 * pw + l32];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (!((w >> (8 * (r >> 2) + 4 * hi + (r & 3))) & 1u)) s[mt][r] = -INFINITY;
+                    }
+                }
+                const int qpos32 = (int)qpos;
+                if (k0 + PA_BK - 1 > (int64_t)pos_base + i0 + 32 * pw) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int t = (int)k0 + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            if (t > qpos32) s[mt][r] = -INFINITY;
+                        }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+                }
+                // lazy reference, as pf_attn
+                const bool move = mx > m_run + 8.f;
+                const float m_new = move ? mx : m_run;
+                alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                const float m_sub = MASK && m_new == -INFINITY ? 0.f : m_new;
+                float psum = 0.f;
+                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                const bf2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float pv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][4 * g + e], scale_log2, -m_sub));
+                        pk[mt][g].x = pf_pack(pv[0], pv[1]);
+                        pk[mt][g].y = pf_pack(pv[2], pv[3]);
+                        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].x), one2, psum, false);
+                        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].y), one2, psum, false);
+                    }
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+                    psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                }
+                l_run = l_run * alpha + psum;
+                m_run = m_new;
+            }
+            asm volatile("s_barrier" ::: "memory");   // B'_it: the O-waves hold P(it - 1)
+            stage_point(it);
+            if (it < ntile) {
+                // P(it): lane (l32, hi) holds keys 32 mt + 8 g + 4 hi .. + 3 of query l32
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<uint2 *>(prow + 32 * mt + 8 * g + 4 * hi) = pk[mt][g];
+                if (hi == 0) sAl[32 * pw + l32] = alpha;
+                if (it == ntile - 1 && hi == 0) sL[32 * pw + l32] = l_run;
+            }
         }
-        float mx = -INFINITY;
+    } else {
+        // ---------------------------------------------------------------- O-wave
+        pf32x16 o[PF_V / 32];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int dt = 0; dt < PF_V / 32; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+            for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
         {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+            const int64_t rr = rows_of(0);
+            settle(rr);
+            stage_k(0, rr);
+            stage_point(-1);
         }
-        // the reference maximum moves only when the tile's maximum exceeds it by more than 8
-        // (log2 units): until then P = exp2(s - m_run) stays below 2^8, which bf16 P and the
-        // fp32 sums hold exactly as well, and the accumulators need no rescaling (the final
-        // normalization divides by the sum taken against the same reference).  Key 0 is in tile
-        // 0 and precedes every query, so the reference is finite from the first tile on and a
-        // masked score (-inf) gives P = exp2(-inf) = 0.
-        const bool move = mx > m_run + 8.f;
-        const float m_new = move ? mx : m_run;
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        // with a mask the reference stays -inf until the query's first attended key; its P are 0
-        const float m_sub = MASK && m_new == -INFINITY ? 0.f : m_new;
-        // P (bf16) packed per group of four keys: pk[mt][g] = keys 8g + 4 hi + 0..3 of tile mt;
-        // the sum is taken over the rounded values (two-element bf16 dot products with ones)
-        uint2 pk[2][4];
-        float psum = 0.f;
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-        const bf2 one2 = {(__bf16)1.f, (__bf16)1.f};
+        const int G = lane >> 4, j16 = lane & 15;
+        const int r3 = j16 >> 2;
+        const int tr_off = PA_BK * PA_KROW + (8 * (G >> 1) + r3) * PA_KROW + 8 * (2 * (G & 1) + ((j16 & 3) >> 1)) +
+                           4 * (j16 & 1);
+        const bf16_t *prow = sP + (pw * 32 + l32) * PW_PROW + 8 * hi;
+        for (int it = 0; it <= ntile; ++it) {
+            top_wait(it);
+            if (it >= 1) {
+                const int kt = it - 1;
+                uint4 pb[PA_BK / 16];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+                for (int kb = 0; kb < PA_BK / 16; ++kb) pb[kb] = *reinterpret_cast<const uint4 *>(prow + 16 * kb);
+                const float alpha = sAl[32 * pw + l32];
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                    for (int dt = 0; dt < PF_V / 32; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                }
+                const bf16_t *tk = sT + (kt & 1) * PA_TILE;
+#pragma unroll
+                for (int kb = 0; kb < PA_BK / 16; ++kb) {
+                    const bf16_t *vb = tk + 16 * kb * PA_KROW + tr_off;
+#pragma unroll
+                    for (int dt = 0; dt < PF_V / 32; ++dt) {
+                        const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) pv4s *)(vb + 32 * (dt ^ r3)));
+                        const pv4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_KROW + 32 * (dt ^ r3)));
+                        const pv8s vt = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt),
+                                                                        pf_bf16x8(pb[kb]), o[dt], 0, 0, 0);
+                    }
+                }
+            }
+            asm volatile("s_barrier" ::: "memory");   // B'_it
+            stage_point(it);
+        }
+        if (iq >= S) return;
+        const float l = sL[32 * pw + l32];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        OUT *orow = out + ((int64_t)iq * PF_H + h) * PF_V;
+#pragma unroll
+        for (int dt = 0; dt < PF_V / 32; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][4 * g + e], scale_log2, -m_sub));
-                pk[mt][g].x = pf_pack(p[0], p[1]);
-                pk[mt][g].y = pf_pack(p[2], p[3]);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].x), one2, psum, false);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, pk[mt][g].y), one2, psum, false);
+                const int dim = 32 * dt + 8 * g + 4 * hi;
+                const float a = o[dt][4 * g] * inv, b = o[dt][4 * g + 1] * inv, c = o[dt][4 * g + 2] * inv,
+                            d = o[dt][4 * g + 3] * inv;
+                if constexpr (sizeof(OUT) == 4) {
+                    *reinterpret_cast<float4 *>(orow + dim) = make_float4(a, b, c, d);
+                } else {
+                    uint2 v;
+                    v.x = pf_pack(a, b);
+                    v.y = pf_pack(c, d);
+                    *reinterpret_cast<uint2 *>(orow + dim) = v;
+                }
             }
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
-            psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(move)) {   // wave-uniform: lanes that keep theirs scale by 1
-#pragma unroll
-            for (int dt = 0; dt < PF_V / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        }
-        // the V rows of tile kt (the next tile's sixteen copies, if any, were issued after them)
-        if (kt + 1 < ntile) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        // O^T += V^T P^T over four 16-key steps: step kb covers keys 16 kb .. +15 (tile kb/2,
-        // groups g = 2 (kb%2), +1).  Lane l needs keys 8 hi .. 8 hi + 7 of the step for query l32;
-        // it holds keys 4 hi + 0..3 (group g) and 8 + 4 hi + 0..3 (group g + 1): one swap of the
-        // upper half's first group with the lower half's second group gives the operand.
-#pragma unroll
-        for (int kb = 0; kb < PA_BK / 16; ++kb) {
-            const int mt = kb >> 1, g = 2 * (kb & 1);
-            const auto x0 = __builtin_amdgcn_permlane32_swap(pk[mt][g].x, pk[mt][g + 1].x, false, false);
-            const auto x1 = __builtin_amdgcn_permlane32_swap(pk[mt][g].y, pk[mt][g + 1].y, false, false);
-            uint4 pb;
-            pb.x = x0[0];
-            pb.y = x1[0];
-            pb.z = x0[1];
-            pb.w = x1[1];
-            const bf16_t *vb = tk + 16 * kb * PA_KROW + tr_off;
-#pragma unroll
-            for (int dt = 0; dt < PF_V / 32; ++dt) {
-                // V chunk 4 dt + .. of rows with row % 4 == r3 sits at 4 (dt ^ r3) + ..
-                const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) pv4s *)(vb + 32 * (dt ^ r3)));
-                const pv4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_KROW + 32 * (dt ^ r3)));
-                const pv8s vt = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt), pf_bf16x8(pb), o[dt],
-                                                                0, 0, 0);
-            }
-        }
     }
-    if (iq >= S) return;
-    // register r of o[dt]: dim 32 dt + 8 (r/4) + 4 hi + r%4 of query iq
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    OUT *orow = out + ((int64_t)iq * PF_H + h) * PF_V;
-#pragma unroll
-    for (int dt = 0; dt < PF_V / 32; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int dim = 32 * dt + 8 * g + 4 * hi;
-            const float a = o[dt][4 * g] * inv, b = o[dt][4 * g + 1] * inv, c = o[dt][4 * g + 2] * inv,
-                        d = o[dt][4 * g + 3] * inv;
-            if constexpr (sizeof(OUT) == 4) {
-                *reinterpret_cast<float4 *>(orow + dim) = make_float4(a, b, c, d);
-            } else {
-                uint2 v;
-                v.x = pf_pack(a, b);
-                v.y = pf_pack(c, d);
-                *reinterpret_cast<uint2 *>(orow + dim) = v;
-            }
-        }
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -478,7 +522,7 @@ template <int NOPE, typename OUT, int MODE, bool MASK>
 static mla_status launch_attn_mode(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
                                    float scale_log2, void *out, const uint32_t *mask, int mask_stride, hipStream_t s)
 {
-    constexpr size_t lds = PA_LDS + (MASK ? PA_MASK_LDS : 0);
+    constexpr size_t lds = PW_LDS + (MASK ? PA_MASK_LDS : 0);
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT, MODE, MASK>),
@@ -487,7 +531,7 @@ static mla_status launch_attn_mode(const void *q, const bf16_t *C, const KvView 
         attr = true;
     }
     const dim3 g((unsigned)((S + PA_BQ - 1) / PA_BQ * PF_H));
-    hipLaunchKernelGGL((pf_attn<NOPE, OUT, MODE, MASK>), g, dim3(256), lds, s, (const bf16_t *)q, C, kv, S, pos_base,
+    hipLaunchKernelGGL((pf_attn<NOPE, OUT, MODE, MASK>), g, dim3(512), lds, s, (const bf16_t *)q, C, kv, S, pos_base,
                        scale_log2, (OUT *)out, mask, mask_stride);
     return check_launch("pf_attn");
 }
