@@ -201,6 +201,7 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 constexpr int PW_PROW = 72;                                      // bf16 per P row (64 keys + pad)
 constexpr size_t PW_P_LDS = (size_t)4 * 32 * PW_PROW * 2;         // P of the four wave pairs
 constexpr size_t PW_LDS = PA_LDS + PW_P_LDS + 2 * PA_BQ * 4;      // + rescale factors and final sums
+constexpr int PW_PV = 8;   // value-operand reads in flight (4: +1%, none: +2% prefill time, same box)
 
 template <int NOPE, typename OUT, int MODE, bool MASK>
 __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C,
@@ -465,20 +466,34 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
                         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
                 }
                 const bf16_t *tk = sT + (kt & 1) * PA_TILE;
+                // step i = 8 kb + dt: the two transposed V reads run PW_PV steps ahead of the product
+                auto v_op = [&](int i) {
+                    const bf16_t *vb = tk + 16 * (i >> 3) * PA_KROW + tr_off + 32 * ((i & 7) ^ r3);
+                    const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pv4s *)vb);
+                    const pv4s hi4 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_KROW));
+                    return __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
+                constexpr int NSTEP = (PA_BK / 16) * (PF_V / 32);
+                pv8s vring[PW_PV];
 #pragma unroll
-                for (int kb = 0; kb < PA_BK / 16; ++kb) {
-                    const bf16_t *vb = tk + 16 * kb * PA_KROW + tr_off;
+                for (int i = 0; i < PW_PV; ++i) vring[i] = v_op(i);
 #pragma unroll
-                    for (int dt = 0; dt < PF_V / 32; ++dt) {
-                        const pv4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) pv4s *)(vb + 32 * (dt ^ r3)));
-                        const pv4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) pv4s *)(vb + 4 * PA_KROW + 32 * (dt ^ r3)));
-                        const pv8s vt = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt),
-                                                                        pf_bf16x8(pb[kb]), o[dt], 0, 0, 0);
-                    }
+                for (int i = 0; i < NSTEP; ++i) {
+                    const pv8s vt = vring[i % PW_PV];
+                    if (i + PW_PV < NSTEP) vring[i % PW_PV] = v_op(i + PW_PV);
+                    o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pbf16x8, vt),
+                                                                       pf_bf16x8(pb[i >> 3]), o[i & 7], 0, 0, 0);
                 }
+#pragma unroll
+                for (int i = 0; i < 2 * PW_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < NSTEP - PW_PV; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < PW_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
             asm volatile("s_barrier" ::: "memory");   // B'_it
             stage_point(it);
