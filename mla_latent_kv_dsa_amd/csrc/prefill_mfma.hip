@@ -169,10 +169,9 @@ constexpr int PA_KROW = 256;                              // bf16 per staged K o
 constexpr int PA_TILE = 2 * PA_BK * PA_KROW;              // bf16 per staged tile
 constexpr size_t PA_LDS = (size_t)2 * PA_TILE * 2;        // two tiles
 // With a key mask (a selection per query): per staged tile, the mask words of its two 32-key
-// groups for the block's 128 queries ([group][query], 1 KB), double-buffered behind the tiles.
+// groups for the block's 128 queries ([group][query], 1 KB), double-buffered behind the rest.
 constexpr size_t PA_MASK_LDS = 2 * 2 * PA_BQ * 4;
 constexpr int PA_PF = 6;       // score operand reads in flight
-
 
 // grid (ceil(S / 128) * H), 512 threads.  NOPE: qk_nope (128 or 192).  OUT: float or bf16_t.
 // Workgroups go to the 8 XCDs round-robin (id % 8); XCD x runs heads x, x + 8, .. one after the
@@ -186,10 +185,11 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 // into LDS with its K rows, so the same waits cover them.
 //
 // The work of a tile is split between two waves per SIMD: wave w < 4 (an S-wave) and wave w + 4
-// (its O-wave) share SIMD w and the queries 32 w .. 32 w + 31 of the block.  The S-wave forms S^T = K Q^T of a tile, masks it and runs the online softmax; it hands P
-// (bf16, [query][key]) and the tile's rescale factor to its O-wave through LDS, and the O-wave forms
-// O^T += V^T P^T one tile later, so that one wave's value products run while the other computes the
-// next tile's scores.  Two barriers per iteration it = 0 .. ntile:
+// (its O-wave) share SIMD w and the queries 32 w .. 32 w + 31 of the block.  The S-wave forms
+// S^T = K Q^T of a tile, masks it and runs the online softmax; it hands P (bf16, [query][key]) and
+// the tile's rescale factor to its O-wave through LDS, and the O-wave forms O^T += V^T P^T one
+// tile later, so that one wave's value products run while the other computes the next tile's
+// scores.  Two barriers per iteration it = 0 .. ntile:
 //   B_it   K(it), its mask words, and V(it - 1) have landed
 //          S-wave: scores and softmax of tile it (P kept in registers)
 //          O-wave: reads P(it - 1) and its factors, rescales, value products of tile it - 1
@@ -197,7 +197,7 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 //          all waves: copies of K(it + 2) (into K(it)'s buffer) and V(it + 1) (into V(it - 1)'s)
 //          S-wave: writes P(it) and its factors
 // so a tile's copies have one and a half iterations to land.  Each wave copies keys 8 w .. 8 w + 7
-// of a tile (K or V halves of two keys per copy, chunk placement as pf_attn).
+// of a tile (K or V halves of two keys per copy, chunks placed as above).
 constexpr int PW_PROW = 72;                                      // bf16 per P row (64 keys + pad)
 constexpr size_t PW_P_LDS = (size_t)4 * 32 * PW_PROW * 2;         // P of the four wave pairs
 constexpr size_t PW_LDS = PA_LDS + PW_P_LDS + 2 * PA_BQ * 4;      // + rescale factors and final sums
@@ -205,9 +205,9 @@ constexpr int PW_PV = 8;   // value-operand reads in flight (4: +1%, none: +2% p
 
 template <int NOPE, typename OUT, int MODE, bool MASK>
 __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, const bf16_t *__restrict__ C,
-                                                  KvView kv, int S, int pos_base, float scale_log2,
-                                                  OUT *__restrict__ out, const uint32_t *__restrict__ mask,
-                                                  int mask_stride)
+                                               KvView kv, int S, int pos_base, float scale_log2,
+                                               OUT *__restrict__ out, const uint32_t *__restrict__ mask,
+                                               int mask_stride)
 {
     extern __shared__ __attribute__((aligned(16))) char pa_smem[];
     bf16_t *sT = reinterpret_cast<bf16_t *>(pa_smem);   // [2 buffers][K rows, V rows][64][PA_KROW]
@@ -392,7 +392,10 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
                     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                     mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
                 }
-                // lazy reference, as pf_attn
+                // lazy reference: it moves only when the tile's maximum exceeds it by more than 8
+                // (log2 units), so P = exp2(s - m_run) < 2^8 and the accumulators are rescaled only
+                // on the tiles where it moves; key 0 precedes every query, so the reference is finite
+                // from the first tile on and a masked score (-inf) gives P = 0
                 const bool move = mx > m_run + 8.f;
                 const float m_new = move ? mx : m_run;
                 alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
