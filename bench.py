@@ -35,8 +35,14 @@ IDX_KERNEL = "index_scores_mfma<0, false"   # the stand-alone indexer (no select
 
 
 def _src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 (16 hex digits) of a source file's code: line comments and blank lines left out, so
+    that a comment edit does not mark counters taken on the same code as stale."""
+    code = []
+    for line in open(path, encoding="utf-8"):
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def _traffic(counters_name: str, kernel: str):
