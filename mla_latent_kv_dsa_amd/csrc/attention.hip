@@ -51,10 +51,12 @@ __global__ __launch_bounds__(256) void split_q_kernel(const E *__restrict__ q, E
 // Key bitmap of the selections: column i (query i), word g holds keys 32 g .. 32 g + 31.  Workgroup
 // (c, r) builds the words g in [MASK_GCH r, MASK_GCH (r + 1)) of the MASK_QB columns c MASK_QB ..
 // in LDS, then writes them out row by row, MASK_QB consecutive words at a time, so every word of the
-// mask is written.  The selection rows of its MASK_QB queries are one contiguous range of sel; the
-// workgroup reads it flat, MASK_LD entries per thread in flight, and sets the bits of the kept
-// positions in its key range with LDS atomics.
-constexpr int MASK_QB = 32, MASK_GCH = 256, MASK_NT = 512, MASK_LD = 8;
+// mask is written.  A thread takes runs of MASK_RUN consecutive entries of one query's selection
+// (run r of row q: entries MASK_RUN r ..); the bits of consecutive entries in the same word are
+// merged in a register and set with one LDS atomic per change of word.  A selection in position
+// order (as the DSA selection is) then gives each lane of a wave its own words, entries 16 apart,
+// instead of 64 lanes setting bits of the same word; any order stays correct.
+constexpr int MASK_QB = 32, MASK_GCH = 256, MASK_NT = 512, MASK_RUN = 16;
 
 __global__ __launch_bounds__(MASK_NT) void sel_mask_kernel(const int32_t *__restrict__ sel,
                                                            const int32_t *__restrict__ nsel, int sel_stride, int S,
@@ -73,36 +75,45 @@ __global__ __launch_bounds__(MASK_NT) void sel_mask_kernel(const int32_t *__rest
     }
     __syncthreads();
     const int64_t t_lo = 32 * g0, t_hi = (32 * (g0 + ng) < T) ? 32 * (g0 + ng) : T;
-    const int64_t qn = S - c0 < MASK_QB ? S - c0 : MASK_QB;
-    // entries of the workgroup's rows of sel: below MASK_QB * 2^19 = 2^24 (the entry point bounds
-    // sel_stride), so 32-bit indices, and the row of entry f from an fp32 reciprocal (exact below
-    // 2^24) corrected by one step
-    const int total = qn > 0 ? (int)qn * sel_stride : 0;
-    const float rcp = 1.0f / (float)sel_stride;
+    const int qn = S - c0 < MASK_QB ? (int)(S - c0) : MASK_QB;
+    const int rpr = (sel_stride + MASK_RUN - 1) / MASK_RUN;   // runs per row (sel_stride < 2^19)
+    const int nruns = qn > 0 ? qn * rpr : 0;
     const int32_t *base = sel + c0 * sel_stride;
-    for (int f0 = 0; f0 < total; f0 += MASK_NT * MASK_LD) {
-        int32_t v[MASK_LD];
+    const bool vec = sel_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
+    for (int rr = tid; rr < nruns; rr += MASK_NT) {
+        const int q = rr / rpr, j0 = (rr - q * rpr) * MASK_RUN;
+        const int n = ns[q];
+        if (j0 >= n) continue;
+        const int32_t *src = base + (int64_t)q * sel_stride + j0;
+        int32_t v[MASK_RUN];
+        if (vec && j0 + MASK_RUN <= sel_stride) {
 #pragma unroll
-        for (int u = 0; u < MASK_LD; ++u) {
-            const int f = f0 + u * MASK_NT + tid;
-            v[u] = f < total ? base[f] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < MASK_LD; ++u) {
-            const int f = f0 + u * MASK_NT + tid;
-            if (f >= total) continue;
-            int q = (int)((float)f * rcp), j = f - q * sel_stride;
-            if (j < 0) {
-                --q;
-                j += sel_stride;
-            } else if (j >= sel_stride) {
-                ++q;
-                j -= sel_stride;
+            for (int k = 0; k < MASK_RUN / 4; ++k) {
+                const int4 x = reinterpret_cast<const int4 *>(src)[k];
+                v[4 * k] = x.x;
+                v[4 * k + 1] = x.y;
+                v[4 * k + 2] = x.z;
+                v[4 * k + 3] = x.w;
             }
-            const int32_t t = v[u];
-            if (j < ns[q] && t >= t_lo && t < t_hi)
-                atomicOr(&m[(int)((t >> 5) - g0) * MASK_QB + q], 1u << (t & 31));
+        } else {
+#pragma unroll
+            for (int k = 0; k < MASK_RUN; ++k) v[k] = j0 + k < sel_stride ? src[k] : -1;
         }
+        int wcur = -1;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int k = 0; k < MASK_RUN; ++k) {
+            const int32_t t = v[k];
+            const bool ok = j0 + k < n && t >= t_lo && t < t_hi;
+            const int w = ok ? (int)((t >> 5) - g0) : -1;
+            if (w != wcur) {
+                if (wcur >= 0) atomicOr(&m[wcur * MASK_QB + q], bits);
+                wcur = w;
+                bits = 0u;
+            }
+            if (ok) bits |= 1u << (t & 31);
+        }
+        if (wcur >= 0) atomicOr(&m[wcur * MASK_QB + q], bits);
     }
     __syncthreads();
     for (int e = tid; e < ng * MASK_QB; e += MASK_NT) {
