@@ -99,7 +99,8 @@ __global__ __launch_bounds__(256) void attn_generic(const T *__restrict__ q, con
             if (row >= 0)
                 for (int c = lane; c < rope; c += 64) p = fmaf(sq[nope + c], ld(rc + row * rope + c), p);
             p = wave_sum(p);
-            const bool keep = !mask || ((mask[(t >> 5) * (int64_t)mask_stride + i] >> (t & 31)) & 1u);
+            // a key without a pool row (a block-table hole) is not attended, as in the decode
+            const bool keep = row >= 0 && (!mask || ((mask[(t >> 5) * (int64_t)mask_stride + i] >> (t & 31)) & 1u));
             if (lane == 0) ss[e] = keep ? p * sm_scale : -INFINITY;
         }
         __syncthreads();

@@ -201,6 +201,7 @@ constexpr int PA_PF = 6;       // score operand reads in flight
 constexpr int PW_PROW = 72;                                      // bf16 per P row (64 keys + pad)
 constexpr size_t PW_P_LDS = (size_t)4 * 32 * PW_PROW * 2;         // P of the four wave pairs
 constexpr size_t PW_LDS = PA_LDS + PW_P_LDS + 2 * PA_BQ * 4;      // + rescale factors and final sums
+constexpr size_t PW_VALID = 16;                                   // + key validity words of the two tiles
 constexpr int PW_PV = 8;   // value-operand reads in flight (4: +1%, none: +2% prefill time, same box)
 
 template <int NOPE, typename OUT, int MODE, bool MASK>
@@ -214,7 +215,9 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
     bf16_t *sP = reinterpret_cast<bf16_t *>(pa_smem + PA_LDS);           // [4 pairs][32 queries][PW_PROW]
     float *sAl = reinterpret_cast<float *>(pa_smem + PA_LDS + PW_P_LDS);   // [128] rescale factor of P
     float *sL = sAl + PA_BQ;                                               // [128] final sums
-    char *sMask = pa_smem + PW_LDS;                                        // [2][2 groups][128 queries]
+    uint8_t *sValid = reinterpret_cast<uint8_t *>(pa_smem + PW_LDS);     // [2 tiles][8 waves]: bit i of byte w =
+                                                                           // key 8 w + i of the tile has a pool row
+    char *sMask = pa_smem + PW_LDS + PW_VALID;                             // [2][2 groups][128 queries]
     constexpr int QD = NOPE + PF_R;
     constexpr int KS = QD / 16;
     constexpr int N = PF_H * (NOPE + PF_V);
@@ -233,7 +236,10 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
     const int ntile = (int)((kend + PA_BK - 1) / PA_BK);
     const int pp = lane & 31, kh = lane >> 5;
 
-    // Rc rows of the wave's 8 keys of tile kt: lane i < 8 resolves key 64 kt + 8 wave + i
+    // Rc rows of the wave's 8 keys of tile kt: lane i < 8 resolves key 64 kt + 8 wave + i.  In a paged
+    // view, whether each has a pool row (none: a block-table hole) goes into the wave's byte of the
+    // tile's validity word, and a key without one scores -inf, as in the decode (a contiguous view
+    // has a row for every key: the view's checks require (B - 1) seq_stride + max_seq_len <= rows).
     auto rows_of = [&](int kt) -> int64_t {
         const int64_t t0 = (int64_t)kt * PA_BK + 8 * wave + (lane & 7);
         const int64_t t = t0 < kend ? t0 : kend - 1;
@@ -248,6 +254,10 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
             if (row >= kv.rows) row = -1;
         } else {
             row = kv_row(kv, 0, t);
+        }
+        if (MODE != 0) {
+            const uint32_t vb = (uint32_t)__builtin_amdgcn_ballot_w64(row >= 0) & 0xffu;
+            if (lane == 0) sValid[(kt & 1) * 8 + wave] = (uint8_t)vb;
         }
         return row >= 0 ? row : 0;
     };
@@ -373,6 +383,17 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
                             if (!((w >> (8 * (r >> 2) + 4 * hi + (r & 3))) & 1u)) s[mt][r] = -INFINITY;
                     }
                 }
+                if (MODE != 0) {   // keys without a pool row (the word is the same for the whole wave)
+                    const uint64_t vw = *reinterpret_cast<const uint64_t *>(sValid + (it & 1) * 8);
+                    if (__builtin_amdgcn_readfirstlane((uint32_t)vw) != 0xffffffffu ||
+                        __builtin_amdgcn_readfirstlane((uint32_t)(vw >> 32)) != 0xffffffffu) {
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                if (!((vw >> (32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3))) & 1ull)) s[mt][r] = -INFINITY;
+                    }
+                }
                 const int qpos32 = (int)qpos;
                 if (k0 + PA_BK - 1 > (int64_t)pos_base + i0 + 32 * pw) {
 #pragma unroll
@@ -394,12 +415,13 @@ __global__ __launch_bounds__(512) void pf_attn(const bf16_t *__restrict__ q, con
                 }
                 // lazy reference: it moves only when the tile's maximum exceeds it by more than 8
                 // (log2 units), so P = exp2(s - m_run) < 2^8 and the accumulators are rescaled only
-                // on the tiles where it moves; key 0 precedes every query, so the reference is finite
-                // from the first tile on and a masked score (-inf) gives P = 0
+                // on the tiles where it moves; a masked score (-inf) gives P = 0, and until the
+                // query's first attended key (key 0 unless it is masked or has no row) the reference
+                // stays -inf and its P are 0
                 const bool move = mx > m_run + 8.f;
                 const float m_new = move ? mx : m_run;
                 alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                const float m_sub = MASK && m_new == -INFINITY ? 0.f : m_new;
+                const float m_sub = m_new == -INFINITY ? 0.f : m_new;
                 float psum = 0.f;
                 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
                 const bf2 one2 = {(__bf16)1.f, (__bf16)1.f};
@@ -540,7 +562,7 @@ template <int NOPE, typename OUT, int MODE, bool MASK>
 static mla_status launch_attn_mode(const void *q, const bf16_t *C, const KvView &kv, int32_t S, int32_t pos_base,
                                    float scale_log2, void *out, const uint32_t *mask, int mask_stride, hipStream_t s)
 {
-    constexpr size_t lds = PW_LDS + (MASK ? PA_MASK_LDS : 0);
+    constexpr size_t lds = PW_LDS + PW_VALID + (MASK ? PA_MASK_LDS : 0);
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_attn<NOPE, OUT, MODE, MASK>),

@@ -677,6 +677,44 @@ def test_prefill_single_query_equals_absorbed_decode(T):
     assert rel_err(out, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("H_,S,pos_base,bs,holes", [(64, 200, 56, 64, (0, 2)), (64, 150, 106, 16, (0, 5, 6)),
+                                                    (4, 90, 38, 16, (0, 3))])
+def test_prefill_paged_hole(H_, S, pos_base, bs, holes):
+    """Keys in a block-table hole (entry -1) have no row and are not attended, as in the decode: on
+    the matrix-core kernels (64 heads; block size 64 looks a tile up once, 16 once per key) and on
+    the generic ones (4 heads).  Block 0 is a hole, so the first queries start with no attended
+    key (their output is 0 while they see holes only).  Reference: the oracle's non-absorbed
+    attention over the keys that have a row."""
+    T = pos_base + S
+    assert T % bs == 0
+    p = synth.prefill(190 + S + bs, S, pos_base, H_=H_)
+    sm = 1.0 / math.sqrt(p.nope + p.rope)
+    lc_p, bt = _paged_copy([p.lc], bs, np.random.default_rng(191 + S))
+    rc_p, _ = _paged_copy([p.rc], bs, np.random.default_rng(191 + S))
+    bt = bt.copy()
+    bt[0, list(holes)] = -1
+    log(f"prefill paged hole H={H_} S={S} pos_base={pos_base} bs={bs} holes={holes}")
+    kv = _kv(lc_p, rc_p, None, None, T, block_table=bt, block_size=bs)
+    out = host(mla.mla_prefill_nonabsorbed(dev_bf16(p.q), dev_bf16(p.kv_b), kv, p.nope, pos_base, sm))
+    assert np.isfinite(out).all()
+    valid = np.ones(T, bool)
+    for j in holes:
+        valid[j * bs:(j + 1) * bs] = False
+    cv = synth.bf16_bits_to_f32
+    q, lc, rc, kvb = cv(p.q), cv(p.lc), cv(p.rc), cv(p.kv_b)
+    rows = np.unique(np.r_[0, 1, S - 1, np.linspace(0, S - 1, 8).astype(int)])
+    empty = 0
+    for i in rows:
+        keys = np.nonzero(valid[: pos_base + i + 1])[0]
+        if keys.size == 0:
+            assert np.all(out[i] == 0), i
+            empty += 1
+            continue
+        ref = oracle.nonabsorbed_decode(q[i][:, : p.nope], q[i][:, p.nope:], kvb, lc, rc, keys, p.v, sm)
+        assert rel_err(out[i], ref) <= TOL_BF16, i
+    assert empty == (1 if pos_base < bs else 0) * int(np.sum(rows + pos_base < bs))
+
+
 # ------------------------------------------------------------------------------ end to end
 def test_dsa_decode_step_end_to_end_small():
     """index -> top-k -> absorbed decode over the selected keys, at a size with T > k."""
