@@ -966,8 +966,11 @@ struct DecPlan {
     int64_t kps;   // keys per split (multiple of 64)
 };
 
-// Batches of at least MH_MIN_B queries run dec_core_mh (all heads per workgroup).
-constexpr int MH_MIN_B = 4;
+// Batches of at least MH_MIN_B queries run dec_core_mh (all heads per workgroup).  Four queries
+// over 2048 selected keys each: 27-30 us on dec_core (16 splits x 4 head groups) + combine_unabsorb
+// against 36-39 us on dec_core_mh, whose 32 splits write 16 MB of fp32 partials; from five queries
+// on dec_core_mh is the faster (B = 6: 38 against 46 us, B = 16: 43 against 60 us).
+constexpr int MH_MIN_B = 5;
 
 // Splits: at most 256 keys per split, enough splits for ~256 workgroups (dec_core: 4 head groups
 // each), at least 64 keys per split and at most CU_MAXNS splits.
