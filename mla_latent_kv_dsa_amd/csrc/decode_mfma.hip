@@ -973,12 +973,14 @@ struct DecPlan {
 constexpr int MH_MIN_B = 5;
 
 // Splits: at most 256 keys per split, enough splits for ~256 workgroups (dec_core: 4 head groups
-// each), at least 64 keys per split and at most CU_MAXNS splits.
+// each; dec_core_mh: ~128, since each of its splits writes 64 heads' fp32 partials -- 2048 keys per
+// query, same box: B = 8 35.5 against 40.9 us with ~256, B = 12 40.4 against 44.9, B = 24 48.2
+// against 61.7, B = 5 39.9 against 37.2), at least 64 keys per split and at most CU_MAXNS splits.
 static DecPlan dec_plan(int32_t B, int64_t max_keys)
 {
     DecPlan p;
     const int64_t by_len = (max_keys + 255) / 256;
-    const int64_t by_fill = ((B >= MH_MIN_B ? 256 : 64) + B - 1) / (int64_t)B;
+    const int64_t by_fill = ((B >= MH_MIN_B ? 128 : 64) + B - 1) / (int64_t)B;
     const int64_t most = (max_keys + DC_KC - 1) / DC_KC;
     int64_t ns = by_len > by_fill ? by_len : by_fill;
     if (ns > most) ns = most;
