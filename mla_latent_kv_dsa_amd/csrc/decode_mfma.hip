@@ -983,6 +983,14 @@ static DecPlan dec_plan(int32_t B, int64_t max_keys)
     const int64_t by_fill = ((B >= MH_MIN_B ? 128 : 64) + B - 1) / (int64_t)B;
     const int64_t most = (max_keys + DC_KC - 1) / DC_KC;
     int64_t ns = by_len > by_fill ? by_len : by_fill;
+    if (B >= MH_MIN_B) {
+        // at most ~256 workgroups' worth of length splits: a large batch fills the chip by itself,
+        // and every split adds 64 heads' fp32 partials (2048 keys per query, same box: B = 64 95.9
+        // -> 79.7 us, B = 256 368 -> 264 us, 4096 queries 5.0 -> 3.4 ms; B = 32 keeps 8 splits)
+        const int64_t cap = (256 + B - 1) / B;
+        const int64_t l = by_len < cap ? by_len : cap;
+        ns = l > by_fill ? l : by_fill;
+    }
     // two to four queries: the fewest splits whose keys fit one staged set (DC_SUP chunks), so
     // that every split takes dec_core<true> (2048 keys: 16 splits; same box, B = 2 / 3: 27.0 /
     // 29.5 us against 31.4 / 35.3 with 32 / 22 splits)
