@@ -323,8 +323,10 @@ def bench_dsa_decode(args):
     print(json.dumps(line), flush=True)
 
 
-def _graph_time(torch, fn, warmup, steps):
-    """Mean ms per call of fn captured in a HIP graph (one call per replay), events on the stream."""
+def _graph_time(torch, fn, warmup, steps, per=8):
+    """Mean ms per call of fn captured in a HIP graph, `per` calls back to back per replay (so the
+    gap between replays is spread over them, as between the calls of a decode loop), events on
+    the stream."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -333,7 +335,8 @@ def _graph_time(torch, fn, warmup, steps):
     torch.cuda.synchronize()
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr):
-        fn()
+        for _ in range(per):
+            fn()
     for _ in range(warmup):
         gr.replay()
     torch.cuda.synchronize()
@@ -343,7 +346,7 @@ def _graph_time(torch, fn, warmup, steps):
         gr.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / (steps * per)
 
 
 def bench_batched_paged(args):
@@ -383,8 +386,8 @@ def bench_batched_paged(args):
     def index():
         mla.dsa_index_scores(qi, wi, kv, T, scores=scores)
 
-    ms = _graph_time(torch, step, 3, 20)
-    ms_idx = _graph_time(torch, index, 3, 20)
+    ms = _graph_time(torch, step, 3, 20, per=1)
+    ms_idx = _graph_time(torch, index, 3, 20, per=1)
     sum_t = int(pb.seq_len.sum())
     keys_heads = sum_t * H
     ic_bytes = sum_t * HD * 4
@@ -434,7 +437,7 @@ def bench_dense_decode(args):
         for c in cps:
             mla.mla_absorbed_decode(c["qn"], c["qr"], c["kvb"], c["kv"], sm, out=c["out"], ws=c["ws"])
 
-    ms = _graph_time(torch, step_all, 3, 10) / NC
+    ms = _graph_time(torch, step_all, 3, 10, per=1) / NC
     kv_bytes = T * (L + ROPE) * 2
     kvb_bytes = H * (NOPE + V) * L * 2
     whole = kv_bytes + kvb_bytes + B * H * (NOPE + ROPE) * 2 + B * H * V * 4
