@@ -901,20 +901,47 @@ def test_decode_generic_and_matrix_core_paths_agree():
         assert rel_err(slow[b], ref) <= TOL_F32
 
 
-def test_decode_batched_long_splits_and_growing_scores():
-    """A batch on the all-heads kernel with more than 256 keys per split (dense, 20000 keys:
-    64 splits of 320) and scores that grow along the sequence (latent rows scaled up with the
-    position), so later chunks keep raising the running maximum."""
-    B, T = 4, 20000
+@pytest.mark.parametrize("B", [4, 5])
+def test_decode_batched_long_splits_and_growing_scores(B):
+    """More than 256 keys per split (dense, 20000 keys) on both batch paths -- four queries on the
+    per-head-group kernel (64 splits of 320 keys), five on the all-heads kernel (52 splits of 448)
+    -- and scores that grow along the sequence (latent rows scaled up with the position), so later
+    chunks keep raising the running maximum."""
+    T = 20000
     d = synth.decode(83, T, B=B)
     lc = synth.bf16_bits_to_f32(d.lc).reshape(B, T, -1)
     lc *= (1.0 + np.arange(T, dtype=np.float32) / 2000.0)[None, :, None]
     d.lc = synth.to_bf16_bits(lc.reshape(B * T, -1))
-    seq_len = [T, 19999, 16385, 300]
-    log("decode batched long splits")
+    seq_len = [T, 19999, 16385, 300, 12345][:B]
+    log(f"decode batched long splits B={B}")
     out, sm = _run_decode(d, seq_len)
-    for b in (0, 2, 3):
+    for b in (0, 2, 3, B - 1):
         assert rel_err(out[b], _decode_ref(d, b, np.arange(seq_len[b]), sm)) <= TOL_BF16, b
+
+
+@pytest.mark.parametrize("B", [64, 300])
+def test_decode_large_batch_shared_pool(B):
+    """Batches large enough that the all-heads kernel splits the keys little or not at all (B = 64:
+    four splits of 512 keys; B = 300: one split of 2048, so each query's partial is its whole
+    attention), every sequence reading the same 2048 pool rows through its block table; sampled
+    rows against the oracle."""
+    T, bs = 2048, 64
+    pool = synth.decode(86, T)
+    qs = synth.decode(87 + B, 1, B=B)
+    rng = np.random.default_rng(88 + B)
+    seq_len = rng.integers(1, T + 1, B).astype(np.int32)
+    seq_len[:3] = [T, T - 1, 65]
+    bt = np.tile(np.arange(T // bs, dtype=np.int32), (B, 1))
+    kv = _kv(pool.lc, pool.rc, None, seq_len, T, block_table=bt, block_size=bs)
+    sm = 1.0 / math.sqrt(pool.nope + pool.rope)
+    log(f"decode large batch B={B} over one shared pool")
+    out = host(mla.mla_absorbed_decode(dev_bf16(qs.q_nope), dev_bf16(qs.q_rope), dev_bf16(pool.kv_b), kv, sm))
+    cv = synth.bf16_bits_to_f32
+    lc, rc, kvb = cv(pool.lc), cv(pool.rc), cv(pool.kv_b)
+    for b in sorted({0, 1, 2, B // 2, B - 1}):
+        ref = oracle.absorbed_decode(cv(qs.q_nope[b]), cv(qs.q_rope[b]), kvb, lc, rc, np.arange(seq_len[b]),
+                                     pool.v, sm)
+        assert rel_err(out[b], ref) <= TOL_BF16, b
 
 
 @pytest.mark.parametrize("nope,v", [(128, 128), (256, 192)])
