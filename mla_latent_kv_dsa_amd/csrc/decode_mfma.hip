@@ -995,6 +995,10 @@ static DecPlan dec_plan(int32_t B, int64_t max_keys)
     // that every split takes dec_core<true> (2048 keys: 16 splits; same box, B = 2 / 3: 27.0 /
     // 29.5 us against 31.4 / 35.3 with 32 / 22 splits)
     if (B > 1 && B < MH_MIN_B) ns = (max_keys + DC_SUP * DC_KC - 1) / (DC_SUP * DC_KC);
+    // one query over more than 2048 keys: likewise one staged set per split, up to CU_MAXNS splits
+    // (dense T = 4096: 32 splits of 128, 20.7 against 22.7 us with 64 of 64; 2048 keys keep 32
+    // splits of 64, faster than 16 of 128; from 8192 keys on CU_MAXNS decides)
+    if (B == 1 && max_keys > 2048) ns = (max_keys + DC_SUP * DC_KC - 1) / (DC_SUP * DC_KC);
     if (ns > most) ns = most;
     if (ns > CU_MAXNS) ns = CU_MAXNS;
     if (ns < 1) ns = 1;
