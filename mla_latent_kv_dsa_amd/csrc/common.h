@@ -128,12 +128,20 @@ __device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim,
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0.0 maps like +0.0.
 // Histogram of the top 11 order-key bits used by the key selection, written without atomics:
 // every workgroup p of a producing kernel (the indexer, or the histogram kernel) writes the
-// nonzero bins of its own keys as a list: entry i of part p is hl[b][i][p] = (bin << 21) | count,
-// i < hcnt[b][p], in descending bin order (entry-major, so that entry i of consecutive parts is
-// contiguous for the reader).  The row histogram is the sum of its parts' lists.
+// nonzero bins of its own keys as a list: entry i of part p, i < hcnt[b][p], in descending bin
+// order, is hl[b][hl_row(i, p)][p] = (bin << 21) | count (entry-major, so that one row of
+// consecutive parts is contiguous for the reader).  The first HL_TOP entries of part p sit in rows
+// rotated by p: the lists of different parts are much alike (entry i of every part is a bin near
+// the top of the row's range, often the same one), and a reader that loads one row for 64
+// consecutive parts then holds 16 different depths across its lanes, so its LDS histogram atomics
+// spread over many bins instead of piling onto one.  The row histogram is the sum of its parts'
+// lists.
 constexpr int HIST_BINS = 2048;
 constexpr int HL_CAP = HIST_BINS;          // entries per part (every bin nonzero at most)
+constexpr int HL_TOP = 16;                 // rotated head of every list (the entries a reader takes first)
+static_assert((HL_TOP & (HL_TOP - 1)) == 0, "list heads rotate modulo HL_TOP");
 __device__ __forceinline__ uint32_t hl_entry(uint32_t bin, uint32_t count) { return (bin << 21) | count; }
+__device__ __forceinline__ int hl_row(int i, int part) { return i < HL_TOP ? ((i + part) & (HL_TOP - 1)) : i; }
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -192,11 +200,11 @@ __device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *sh
 }
 
 // Writes the nonzero bins of the complete LDS histogram hs (HIST_BINS, every thread of an NT-thread
-// block calls it) as a list (descending bins; entry i at list[i * stride]) and its length `count`;
-// sh: NT / 64 words.
+// block calls it) as the list of part `part` (descending bins; entry i at list[hl_row(i, part) *
+// stride]) and its length `count`; sh: NT / 64 words.
 template <int NT>
 __device__ __forceinline__ void hist_write_list(const uint32_t *hs, uint32_t *__restrict__ list, int64_t stride,
-                                                uint32_t *__restrict__ count, uint32_t *sh)
+                                                int part, uint32_t *__restrict__ count, uint32_t *sh)
 {
     constexpr int PER = HIST_BINS / NT;   // bins per thread, thread order = descending bins
     const int top = HIST_BINS - 1 - PER * (int)threadIdx.x;
@@ -210,7 +218,7 @@ __device__ __forceinline__ void hist_write_list(const uint32_t *hs, uint32_t *__
     uint32_t off = block_excl_scan_dpp<NT / 64>(nz, sh, &total);
 #pragma unroll
     for (int q = 0; q < PER; ++q)
-        if (c[q]) list[(int64_t)(off++) * stride] = hl_entry((uint32_t)(top - q), c[q]);
+        if (c[q]) list[(int64_t)hl_row((int)(off++), part) * stride] = hl_entry((uint32_t)(top - q), c[q]);
     if (threadIdx.x == 0) *count = total;
 }
 

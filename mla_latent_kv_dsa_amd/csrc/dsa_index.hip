@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     if (HIST) {
         __syncthreads();
         hist_write_list<64 * IXM_WAVES>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max,
-                                        hcnt + (int64_t)b * parts_max + blockIdx.x, sh_scan);
+                                        (int)blockIdx.x, hcnt + (int64_t)b * parts_max + blockIdx.x, sh_scan);
     }
 }
 
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma_mq(const flo
         for (int qi = 0; qi < nb; ++qi)
             hist_write_list<64 * IXM_WAVES>(hs + qi * IX_BINS,
                                             hl + (int64_t)(r0 + qi) * HL_CAP * parts_max + blockIdx.x, parts_max,
-                                            hcnt + (int64_t)(r0 + qi) * parts_max + blockIdx.x, sh_scan);
+                                            (int)blockIdx.x, hcnt + (int64_t)(r0 + qi) * parts_max + blockIdx.x, sh_scan);
     }
 }
 

@@ -24,7 +24,6 @@ namespace mla {
 constexpr int SEL_BINS = HIST_BINS;        // top 11 key bits
 constexpr int SEL_CH = 1024;               // positions per filter workgroup (one candidate slot)
 constexpr int SEL_TMAX = 262144;           // longest row whose bitmasks the resolve step holds in LDS
-constexpr int HL_TOP = 16;                 // list entries per part the filter reads first
 
 // ------------------------------------------------------------------------------ 1'. histogram
 // For indexer kernels without a built-in histogram: grid (ceil(t_max/1024), B), one list part per
@@ -54,7 +53,7 @@ __global__ __launch_bounds__(256) void sel_hist(const float *__restrict__ scores
         }
     }
     __syncthreads();
-    hist_write_list<256>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max,
+    hist_write_list<256>(hs, hl + (int64_t)b * HL_CAP * parts_max + blockIdx.x, parts_max, (int)blockIdx.x,
                          hcnt + (int64_t)b * parts_max + blockIdx.x, sh);
 }
 
@@ -124,14 +123,18 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         sv[j] = row[t < n ? t : n - 1];
     }
+    // Row i of the list heads: register i of the thread of part p holds entry (i - p) % HL_TOP of
+    // that part (the heads are stored rotated, common.h), so the lanes of one LDS atomic below add
+    // bins of 16 different depths.
     const uint32_t *hlb = hl + (int64_t)b * HL_CAP * parts_max;
-    uint32_t pc[PPT], pe[PPT][HL_TOP];
+    uint32_t pc[PPT], pe[PPT][HL_TOP], pl[PPT];
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {   // clamped to the last part; parts past the end are skipped
         const int p = tid + 256 * r < parts ? tid + 256 * r : parts - 1;
         pc[r] = hcnt[(int64_t)b * parts_max + p];
 #pragma unroll
         for (int i = 0; i < HL_TOP; ++i) pe[r][i] = hlb[(int64_t)i * parts_max + p];
+        pl[r] = hlb[(int64_t)hl_row(HL_TOP - 1, p) * parts_max + p];   // entry HL_TOP - 1: a truncated part's floor
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -147,15 +150,23 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
         const int64_t t = (int64_t)c * SEL_CH + 256 * j + tid;
         key[j] = t < n ? order_key(sv[j]) : 0u;
     }
+    uint32_t fl = 0u;   // this thread's highest floor bin over its truncated parts
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
         if (tid + 256 * r >= parts) break;
         const uint32_t ne = pc[r] < HL_TOP ? pc[r] : HL_TOP;
 #pragma unroll
         for (int i = 0; i < HL_TOP; ++i)
-            if ((uint32_t)i < ne) atomicAdd(&hs[pe[r][i] >> 21], pe[r][i] & 0x1FFFFFu);
-        if (pc[r] > HL_TOP) atomicMax(&s_floor, pe[r][HL_TOP - 1] >> 21);
+            if ((uint32_t)((i - tid - 256 * r) & (HL_TOP - 1)) < ne) atomicAdd(&hs[pe[r][i] >> 21], pe[r][i] & 0x1FFFFFu);
+        if (pc[r] > HL_TOP && (pl[r] >> 21) > fl) fl = pl[r] >> 21;
     }
+    // one LDS atomic per wave for the floor (all lanes on one address would serialize)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t x = (uint32_t)__shfl_xor((int)fl, o);
+        fl = x > fl ? x : fl;
+    }
+    if (lane == 0 && fl > 0u) atomicMax(&s_floor, fl);
     __syncthreads();
     // threshold bin: thread t owns the 8 bins [2040-8t, 2048-8t) (thread order = descending bins)
     for (int pass = 0; pass < 2; ++pass) {
