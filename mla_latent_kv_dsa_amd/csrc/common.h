@@ -199,6 +199,53 @@ __device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t *sh
     return before + inc - v;
 }
 
+// The same without the closing barrier, for a caller that gives every call its own sh (NW words)
+// within one pass of the block, so that no later write can meet a slower thread's read.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan_once(uint32_t v, uint32_t *sh, uint32_t *total = nullptr)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_scan_dpp(v);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t t = sh[w];
+        before += w < wave ? t : 0u;
+        all += t;
+    }
+    if (total) *total = all;
+    return before + inc - v;
+}
+
+// Two exclusive scans behind one barrier (sh: 2 NW words, used once as above); ta, tb: totals.
+template <int NW>
+__device__ __forceinline__ void block_excl_scan2_once(uint32_t a, uint32_t b, uint32_t *sh, uint32_t &ea, uint32_t &eb,
+                                                      uint32_t *ta = nullptr, uint32_t *tb = nullptr)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t ia = wave_incl_scan_dpp(a), ib = wave_incl_scan_dpp(b);
+    if (lane == 63) {
+        sh[wave] = ia;
+        sh[NW + wave] = ib;
+    }
+    __syncthreads();
+    uint32_t ba = 0u, bb = 0u, sa = 0u, sb = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t x = sh[w], y = sh[NW + w];
+        ba += w < wave ? x : 0u;
+        bb += w < wave ? y : 0u;
+        sa += x;
+        sb += y;
+    }
+    ea = ba + ia - a;
+    eb = bb + ib - b;
+    if (ta) *ta = sa;
+    if (tb) *tb = sb;
+}
+
 // Writes the nonzero bins of the complete LDS histogram hs (HIST_BINS, every thread of an NT-thread
 // block calls it) as the list of part `part` (descending bins; entry i at list[hl_row(i, part) *
 // stride]) and its length `count`; sh: NT / 64 words.

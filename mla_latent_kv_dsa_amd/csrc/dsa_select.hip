@@ -82,7 +82,7 @@ mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, cons
 constexpr int SEL_CPT = 8;                     // candidates per thread held in registers (resolve)
 constexpr int SR_NT = 512, SR_NW = SR_NT / 64; // threads / waves of the resolve workgroup
 constexpr int SR_WPT = 8;                      // bitmask words per resolve thread (SEL_TMAX)
-constexpr int SR_STATIC = SEL_BINS * 4 + 2048; // static LDS of the resolve workgroup (bytes)
+constexpr int SR_STATIC = SEL_BINS * 6 + 2048; // static LDS of the resolve workgroup (bytes)
 constexpr int SR_DYN_MAX = 160 * 1024 - SR_STATIC;
 
 struct SelRow {           // per-row results of the filter (uint32 words)
@@ -260,19 +260,23 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
 //   - candidates above it set their bit in the row bitmask (held in LDS), candidates equal to it
 //     their bit in an eq bitmask
 //   - thread t owns the bitmask words [t wpt, (t+1) wpt), a run of positions: the first
-//     `remaining` eq bits in position order join the kept bits (block scan of eq popcounts), a
-//     block scan of the kept popcounts gives every thread its output offset, and the set bits are
-//     written out as positions -- ascending across the row.
-// dyn: keep[wp], eq[wp] (uint64).
+//     `remaining` eq bits in position order join the kept bits, and the set bits are written out
+//     as positions -- ascending across the row.  One pair of block scans gives both the eq keys
+//     before a thread's run (erank) and the kept keys above the threshold before it; its output
+//     offset is the latter plus min(remaining, erank), the eq keys taken before it.
+// Every histogram and scan has LDS of its own, cleared or written once, so a phase needs only the
+// barrier that publishes its inputs (9 barriers instead of 18).  (Compacting the positions in LDS
+// for 16-byte stores was slower than the scattered 4-byte stores.)
+// dyn: keep[wp], eq[wp] (uint64), then staged overflow candidates.
 __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k, const uint2 *__restrict__ cand,
                                                  const uint32_t *__restrict__ fcnt, int nch,
                                                  const uint64_t *__restrict__ gkeep, int wp,
                                                  const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
                                                  int32_t *__restrict__ nsel, uint64_t *__restrict__ dyn, int ov_cap)
 {
-    __shared__ uint32_t h[SEL_BINS];
-    __shared__ uint32_t sh[SR_NW];
-    __shared__ uint32_t s_bc[2];
+    __shared__ uint32_t h[SEL_BINS], h2[SEL_BINS / 2];   // radix histograms, bits 20..10 and 9..0
+    __shared__ uint32_t sh[5 * SR_NW];
+    __shared__ uint32_t s_bc[4];
     __shared__ uint32_t s_ov[SEL_TMAX / SEL_CH + 1];   // overflow prefix over the slots
     const int tid = threadIdx.x;
     const int64_t n = seq_len_of(kv, b);
@@ -309,13 +313,22 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         cr[2 * i + 1] = make_uint2(v.z, v.w);
     }
     uint64_t *keep = dyn, *eqm = dyn + wp;
+    // cleared or filled before the first barrier: eq bits, the filter's words of keys above the
+    // threshold bin, both radix histograms
     for (int i = tid; i < wp; i += SR_NT) eqm[i] = 0ull;
+#pragma unroll
+    for (int i = 0; i < SR_WPT; ++i)
+        if (i < wpt) keep[tid * wpt + i] = tid * wpt + i < nw ? kw[i] : 0ull;
+#pragma unroll
+    for (int q = 0; q < SEL_BINS / SR_NT; ++q) h[tid + SR_NT * q] = 0u;
+#pragma unroll
+    for (int q = 0; q < SEL_BINS / 2 / SR_NT; ++q) h2[tid + SR_NT * q] = 0u;
     const uint32_t tb = rin.tb, above_total = rin.above;
     // entries past the first D of each slot: prefix over the slots (thread t < nch: slot t)
     const uint32_t D = (uint32_t)tps * SEL_CPT;
     const uint32_t ov_t = tid < nch && cnt_t > D ? cnt_t - D : 0u;
     uint32_t OV = 0u;
-    const uint32_t ov_pre = block_excl_scan_dpp<SR_NW>(ov_t, sh, &OV);
+    const uint32_t ov_pre = block_excl_scan_once<SR_NW>(ov_t, sh, &OV);   // (publishes the clears)
     if (tid < nch) s_ov[tid] = ov_pre;
     if (tid == 0) s_ov[nch] = OV;
     // the overflow entries (item i: slot c with s_ov[c] <= i < s_ov[c+1]) are read from memory
@@ -331,20 +344,23 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         }
         return cb[(int64_t)lo * SEL_CH + D + (ic - s_ov[lo])];
     };
-    if (OV > 0u && ov_lds) {
+    if (OV > 0u) {
         __syncthreads();   // s_ov
-        for (uint32_t base = 0u; base < OV; base += 8u * SR_NT) {
-            uint2 t[8];
+        if (ov_lds) {
+            for (uint32_t base = 0u; base < OV; base += 8u * SR_NT) {
+                uint2 t[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t it = base + tid + (uint32_t)SR_NT * i;
-                t[i] = ov_item(it < OV ? it : OV - 1u);
-            }
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t it = base + tid + (uint32_t)SR_NT * i;
+                    t[i] = ov_item(it < OV ? it : OV - 1u);
+                }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t it = base + tid + (uint32_t)SR_NT * i;
-                if (it < OV) ovs[it] = t[i];
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t it = base + tid + (uint32_t)SR_NT * i;
+                    if (it < OV) ovs[it] = t[i];
+                }
             }
+            __syncthreads();   // ovs
         }
     }
     // every candidate once: those held in registers, then the overflow entries (from LDS, or in
@@ -374,14 +390,12 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int shift = p == 0 ? 10 : 0;
-        const int nb = p == 0 ? 2048 : 1024;
+        const int nb = p == 0 ? SEL_BINS : SEL_BINS / 2;
         const uint32_t dm = (uint32_t)nb - 1u;
-#pragma unroll
-        for (int q = 0; q < SEL_BINS / SR_NT; ++q) h[tid + SR_NT * q] = 0u;
-        __syncthreads();
+        uint32_t *hp = p == 0 ? h : h2;
         const uint32_t pf = prefix, mk = mask;
         for_each([&](uint2 c) {
-            if ((c.x & mk) == pf) atomicAdd(&h[(c.x >> shift) & dm], 1u);
+            if ((c.x & mk) == pf) atomicAdd(&hp[(c.x >> shift) & dm], 1u);
         });
         __syncthreads();
         const int per = nb / SR_NT;   // 4 or 2 bins per thread, thread order = descending bins
@@ -389,10 +403,10 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         uint32_t hv[4], local = 0u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            hv[q] = q < per ? h[top - q] : 0u;
+            hv[q] = q < per ? hp[top - q] : 0u;
             local += hv[q];
         }
-        const uint32_t before = block_excl_scan_dpp<SR_NW>(local, sh);
+        const uint32_t before = block_excl_scan_once<SR_NW>(local, sh + (1 + p) * SR_NW);
         if (before < remaining && before + local >= remaining) {
             uint32_t cum = before;
             int bin = top;
@@ -404,35 +418,33 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
                 }
                 cum += hv[q];
             }
-            s_bc[0] = remaining - cum;
-            s_bc[1] = prefix | ((uint32_t)bin << shift);
+            s_bc[2 * p] = remaining - cum;
+            s_bc[2 * p + 1] = prefix | ((uint32_t)bin << shift);
         }
         __syncthreads();
-        remaining = s_bc[0];
-        prefix = s_bc[1];
+        remaining = s_bc[2 * p];
+        prefix = s_bc[2 * p + 1];
         mask |= dm << shift;
     }
     const uint32_t kth = prefix;
-    // the filter's bitmask of keys above the threshold bin, then the candidates' bits
-#pragma unroll
-    for (int i = 0; i < SR_WPT; ++i)
-        if (i < wpt) keep[tid * wpt + i] = tid * wpt + i < nw ? kw[i] : 0ull;
-    __syncthreads();
+    // the candidates' bits: above the k-th key into the kept bitmask, equal to it into eq
     for_each([&](uint2 c) {
         if (c.x > kth) atomicOr(reinterpret_cast<unsigned long long *>(&keep[c.y >> 6]), 1ull << (c.y & 63));
         else if (c.x == kth) atomicOr(reinterpret_cast<unsigned long long *>(&eqm[c.y >> 6]), 1ull << (c.y & 63));
     });
     __syncthreads();
     uint64_t ew[SR_WPT];
-    uint32_t ec = 0u;
+    uint32_t ec = 0u, kc = 0u;
 #pragma unroll
     for (int i = 0; i < SR_WPT; ++i) {
         kw[i] = i < wpt ? keep[tid * wpt + i] : 0ull;
         ew[i] = i < wpt ? eqm[tid * wpt + i] : 0ull;
         ec += (uint32_t)__popcll(ew[i]);
+        kc += (uint32_t)__popcll(kw[i]);
     }
-    uint32_t erank = block_excl_scan_dpp<SR_NW>(ec, sh);   // equal keys before this run
-    uint32_t kc = 0u;
+    uint32_t erank, o;   // equal keys before this run; kept keys above the k-th before it
+    block_excl_scan2_once<SR_NW>(ec, kc, sh + 3 * SR_NW, erank, o);
+    o += erank < remaining ? erank : remaining;
 #pragma unroll
     for (int i = 0; i < SR_WPT; ++i) {
         uint64_t e = ew[i];
@@ -449,9 +461,7 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         }
         erank += c;
         kw[i] |= e;
-        kc += (uint32_t)__popcll(kw[i]);
     }
-    uint32_t o = block_excl_scan_dpp<SR_NW>(kc, sh);
 #pragma unroll
     for (int i = 0; i < SR_WPT; ++i) {
         uint64_t x = kw[i];

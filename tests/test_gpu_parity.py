@@ -325,6 +325,33 @@ def test_index_select_deep_histogram_parts(tiled):
     _select_check(q, w, kv, T, k, seq)
 
 
+def test_index_select_ties_across_filter_workgroups():
+    """T = 131072, k = 2048, scores spread over 64 octaves, with the k-th score given to 61 keys
+    spread over the row (one per filter workgroup): the first 29 of them in position order are
+    kept."""
+    rng = np.random.default_rng(340)
+    T, k = 131072, 2048
+    vals = np.exp2(np.arange(T) * (64.0 / T) - 20.0).astype(np.float32)
+    vals = vals[rng.permutation(T)]
+    order = np.argsort(-vals, kind="stable")
+    v = vals[order[2019]]                                  # 2019 keys above it
+    low = np.nonzero(vals < v)[0]
+    spread = low[np.linspace(0, low.size - 1, 60).astype(np.int64)]
+    vals[spread] = v                                       # 61 keys equal to the k-th
+    ic = rng.standard_normal((T, 128)).astype(np.float32)
+    ic[:, 0] = vals
+    q = np.zeros((1, 32, 128), np.float32)
+    q[0, 0, 0] = 1.0                                       # head 0 scores Ic[t, 0] exactly
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 1.0
+    z = np.zeros((T, 8), np.uint16)
+    log("index+select ties across filter workgroups")
+    kv = _kv(z, z, ic, [T], T, seq_stride=T, tiled=True)
+    sel, nsel = _select_check(q, w, kv, T, k, [T])
+    eq = np.sort(np.nonzero(vals == v)[0])
+    assert np.isin(eq[:29], sel[0]).all() and not np.isin(eq[29:], sel[0]).any()
+
+
 def _cand_case(seed, B, T, window=None, repeat=1, equal=False):
     """Tiled indexer pool at full context (256 indexer workgroups per row).
     window: (start, length, factor) scales a block of key rows so the top keys crowd into a few
