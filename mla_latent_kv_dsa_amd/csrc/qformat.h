@@ -88,7 +88,10 @@ __device__ __forceinline__ QRaw8<FMT> q_raw8(const void *__restrict__ w, const v
 {
     QRaw8<FMT> r;
     if constexpr (FMT == 0) {
-        r.v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const bf16_t *>(w) + row * L + c);
+        // read once per call: nontemporal (decode step 42.2 -> 42.0 us, three alternating pairs)
+        typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+        const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(reinterpret_cast<const bf16_t *>(w) + row * L + c));
+        r.v = make_uint4(x.x, x.y, x.z, x.w);
     } else if constexpr (FMT == MLA_Q_MXFP4) {
         r.v = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(w) + row * (L / 2) + c / 2);
         r.s = reinterpret_cast<const uint8_t *>(scales)[row * (L / 32) + c / 32];
