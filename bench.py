@@ -774,6 +774,56 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_vendor(args):
+    """Context for the prefill numbers: torch's own kernels on the same shapes (bf16, 64 heads,
+    S = T = 4096), timed beside mla_prefill_nonabsorbed.  torch.mm is the library GEMM
+    (hipBLASLt) for the kv_b rebuild C[T][H (nope + v)] = Lc kv_b^T (kv_b^T made contiguous);
+    scaled_dot_product_attention is held to its flash backend (it raises rather than falling back
+    to the math path), causal, with 256-wide queries, keys and values, the widths of the
+    non-absorbed attention here (192 + 64 and 256).  Same algorithmic flops as the prefill line."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    dev = torch.device("cuda:0")
+    S, H, L, R = 4096, 64, 512, 192 + 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(1011)
+
+    def timed(f, n):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    lc = torch.randn(S, L, device=dev, dtype=torch.bfloat16, generator=g)
+    kvbT = torch.randn(L, H * R, device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+    c = torch.empty(S, H * R, device=dev, dtype=torch.bfloat16)
+    ms_mm = timed(lambda: torch.mm(lc, kvbT, out=c), 20)
+    f_kvb = 2 * S * H * R * L
+    res = {"workload": "vendor_prefill_S4096", "gemm_torch_mm": {"ms": ms_mm, "TFLOPs": f_kvb / ms_mm / 1e9}}
+    del lc, kvbT, c
+    q = torch.randn(1, H, S, 256, device=dev, dtype=torch.bfloat16, generator=g)
+    k = torch.randn(1, H, S, 256, device=dev, dtype=torch.bfloat16, generator=g)
+    v = torch.randn(1, H, S, 256, device=dev, dtype=torch.bfloat16, generator=g)
+    f_attn = 2 * H * (S * (S + 1) // 2) * (256 + 256)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms_fa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True), 5)
+        res["attention_torch_sdpa_flash"] = {"ms": ms_fa, "TFLOPs": f_attn / ms_fa / 1e9}
+    except RuntimeError as ex:   # no flash backend in this torch build
+        res["attention_torch_sdpa_flash"] = {"unavailable": str(ex)[:200]}
+    del q, k, v
+    ours = measure_prefill(args, cpu=False)
+    res["mla_prefill_nonabsorbed"] = {"ms": ours["ms_per_step"], "TFLOPs": ours["TFLOPs"]}
+    print(json.dumps(res), flush=True)
+
+
 # ----------------------------------------------------------------------------- counters
 COPY_MIB = 256
 
@@ -906,7 +956,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsa_decode",
-                    choices=["dsa_decode", "dsa_decode_paged_b32", "prefill", "copy", "rows"])
+                    choices=["dsa_decode", "dsa_decode_paged_b32", "prefill", "copy", "rows", "vendor"])
     ap.add_argument("--copies", type=int, default=6, help="input copies rotated to defeat the Infinity Cache")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -946,6 +996,8 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "config": r}), flush=True)
     elif args.workload == "copy":
         bench_copy(args)
+    elif args.workload == "vendor":   # torch's GEMM and flash attention on the prefill shapes, for context
+        bench_vendor(args)
     elif args.workload == "rows":   # the cache write, shared layer, multi-query decode and DSA prefill alone
         print(json.dumps(bench_new_rows(args)), flush=True)
     else:

@@ -138,7 +138,11 @@ __device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int6
         row = (int64_t)kv_seq(kv, b) * kv.seq_stride + t;
     } else if (MODE == 1) {
         const int64_t t0 = tile * 64;
-        const int64_t blk = kv.bt[(int64_t)kv_seq(kv, b) * kv.max_blocks + t0 / kv.bs];
+        // read through the constant address space, so that the uniform entry is a scalar load: a
+        // vector load here is counted with the key slices in flight, and waiting for it drains them
+        typedef const __attribute__((address_space(4))) int32_t cbt_t;
+        cbt_t *bt = (cbt_t *)kv.bt;
+        const int64_t blk = bt[(int64_t)kv_seq(kv, b) * kv.max_blocks + t0 / kv.bs];
         row = blk < 0 ? -1 : blk * kv.bs + t0 % kv.bs + lane;
     } else {
         row = t < n ? kv_row(kv, b, t) : -1;
@@ -243,30 +247,39 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
 
     if (HIST)
         for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) hs[i] = 0u;
-    // query to LDS: all four loads in flight before the first store
-    const float4 *qb = reinterpret_cast<const float4 *>(q + (int64_t)b * 32 * 128);
-    float4 qv[32 * 32 / (64 * IXM_WAVES)];
-#pragma unroll
-    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) qv[k] = qb[tid + k * 64 * IXM_WAVES];
-#pragma unroll
-    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) {
-        const int i = tid + k * 64 * IXM_WAVES;
-        *reinterpret_cast<float4 *>(&sq[(i >> 5) * IXM_QROW + (i & 31) * 4]) = qv[k];
-    }
-    __syncthreads();
-
+    // The query's loads go out first and the wave's first key slices right behind them; the query
+    // is then staged in LDS while the key data is still on its way (loads return in issue order,
+    // so the stores wait for the query only), and the barrier waits for LDS alone.  The key
+    // pointer is formed before the query's loads (its branches would otherwise let the compiler
+    // sink them behind the key slices), and the slices are loaded unconditionally, from the
+    // stand-in for a wave without a tile.
     int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
-    if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
-
     // stand-in for keys without a row: the query block (512 B rows), or the pool's first tile
     const float *qraw = TILED ? kv.ic + 4 * lane : q + (int64_t)b * 32 * 128;
-    bool valid, valid_n = false;
-    const float *p = ix_key_ptr<MODE, TILED>(kv, b, tile, lane, n, qraw, valid);
+    bool valid = false, valid_n = false;
+    const float *p = qraw;
+    if (tile < ntv) p = ix_key_ptr<MODE, TILED>(kv, b, tile, lane, n, qraw, valid);
+    // (native vectors: a struct copy from memory to LDS would become one memcpy at the store)
+    const ix_f4 *qb = reinterpret_cast<const ix_f4 *>(q + (int64_t)b * 32 * 128);
+    ix_f4 qv[32 * 32 / (64 * IXM_WAVES)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) qv[k] = qb[tid + k * 64 * IXM_WAVES];
+    __builtin_amdgcn_sched_barrier(0);
     v32f KA, KB, acc;
     ix_load_slice<TILED>(KA, p, 0);
     __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
     ix_load_slice<TILED>(KB, p, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) {
+        const int i = tid + k * 64 * IXM_WAVES;
+        *reinterpret_cast<ix_f4 *>(&sq[(i >> 5) * IXM_QROW + (i & 31) * 4]) = qv[k];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the query and the cleared histogram
+
+    if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
     for (; tile < ntv; tile += waves_total) {
         // the next tile's first two slices are loaded unconditionally (from the query block
         // when there is no next tile) so every iteration leaves the same loads in flight
