@@ -12,9 +12,10 @@
 //   2. sel_filter   grid (t_max / 1024, B): sums the lists into the row histogram (only as deep
 //                   as the threshold needs), finds the threshold bin, writes the row bitmask words
 //                   of its keys above the bin and its keys inside the bin into its own slot
-//   3. sel_resolve  grid (B): the exact k-th key (two radix passes over the candidates'
+//   3. sel_resolve  grid (B x SR_PARTS): the exact k-th key (two radix passes over the candidates'
 //                   remaining 21 bits), the kept candidates' bits, ties resolved in position
 //                   order, and the kept positions written out of the bitmask in ascending order
+//                   (each of a row's SR_PARTS workgroups writes those of one part of the bitmask)
 // Rows longer than SEL_TMAX positions take the general top-k (three launches, any length).
 #include "common.h"
 #include "absorb_body.h"
@@ -82,6 +83,15 @@ mla_status launch_score_hist(const float *scores, int32_t B, int64_t t_max, cons
 constexpr int SEL_CPT = 8;                     // candidates per thread held in registers (resolve)
 constexpr int SR_NT = 512, SR_NW = SR_NT / 64; // threads / waves of the resolve workgroup
 constexpr int SR_WPT = 8;                      // bitmask words per resolve thread (SEL_TMAX)
+// The resolve code is compiled for at most WPT words per thread, WPT = 4 (rows up to 131072
+// positions) or SR_WPT: its per-word steps are unrolled straight-line code, so that rows of
+// 128k keys do not run the instructions of eight words per thread (~400 per wave after the scans).
+constexpr int sr_wpt_of(int wp) { return wp / 512 <= 4 ? 4 : SR_WPT; }
+// Workgroups per row of the resolve step.  Each finds the k-th key and the output offsets on its
+// own (the same loads, passes and scans) and then writes the positions of one part of the row's
+// bitmask words: the bit loop that turns words into positions costs ~2 us of one workgroup's ALU
+// time at k = 2048, and split this way each thread handles one word instead of four.
+constexpr int SR_PARTS = 4;
 constexpr int SR_STATIC = SEL_BINS * 6 + 2048; // static LDS of the resolve workgroup (bytes)
 constexpr int SR_DYN_MAX = 160 * 1024 - SR_STATIC;
 
@@ -250,7 +260,8 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
 }
 
 // ------------------------------------------------------------------------------ 3. resolve + emit
-// One workgroup of SR_NT threads per row b:
+// SR_PARTS workgroups of SR_NT threads per row b, each doing all of the following but writing only
+// the positions of its part of the bitmask words:
 //   - the candidates sit in nch slots (one per filter workgroup, fcnt[c] each).  The tps = SR_NT /
 //     nch consecutive threads t of slot c = t / tps take its entries in pairs: thread r = t % tps
 //     the pairs r + tps i, i < SEL_CPT / 2 (the first D = SEL_CPT tps entries, loaded before
@@ -260,15 +271,18 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
 //   - candidates above it set their bit in the row bitmask (held in LDS), candidates equal to it
 //     their bit in an eq bitmask
 //   - thread t owns the bitmask words [t wpt, (t+1) wpt), a run of positions: the first
-//     `remaining` eq bits in position order join the kept bits, and the set bits are written out
-//     as positions -- ascending across the row.  One pair of block scans gives both the eq keys
-//     before a thread's run (erank) and the kept keys above the threshold before it; its output
-//     offset is the latter plus min(remaining, erank), the eq keys taken before it.
+//     `remaining` eq bits in position order join the kept bits.  One pair of block scans gives both
+//     the eq keys before a thread's run (erank) and the kept keys above the threshold before it; its
+//     output offset is the latter plus min(remaining, erank), the eq keys taken before it.  The
+//     final words and each word's output offset go to LDS, and the set bits of the part's words are
+//     written out as positions -- ascending across the row.
 // Every histogram and scan has LDS of its own, cleared or written once, so a phase needs only the
 // barrier that publishes its inputs (9 barriers instead of 18).  (Compacting the positions in LDS
 // for 16-byte stores was slower than the scattered 4-byte stores.)
 // dyn: keep[wp], eq[wp] (uint64), then staged overflow candidates.
-__device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k, const uint2 *__restrict__ cand,
+template <int WPT>
+__device__ __forceinline__ void resolve_emit_row(int b, int part, const KvView &kv, int k,
+                                                 const uint2 *__restrict__ cand,
                                                  const uint32_t *__restrict__ fcnt, int nch,
                                                  const uint64_t *__restrict__ gkeep, int wp,
                                                  const SelRow *__restrict__ rows, int32_t *__restrict__ sel,
@@ -282,8 +296,8 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     const int64_t n = seq_len_of(kv, b);
     int32_t *out = sel + (int64_t)b * k;
     if (n <= k) {   // every position is kept
-        for (int u = tid; u < k; u += SR_NT) out[u] = u < n ? u : -1;
-        if (tid == 0) nsel[b] = (int32_t)n;
+        for (int u = part * SR_NT + tid; u < k; u += SR_PARTS * SR_NT) out[u] = u < n ? u : -1;
+        if (part == 0 && tid == 0) nsel[b] = (int32_t)n;
         return;
     }
     // issued before anything waits: the row's threshold, the slot counts, bitmask words and the
@@ -299,9 +313,9 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     const int wpt = wp / SR_NT;
     const int nw = (int)((n + 63) / 64);   // words that hold positions < n
     const uint64_t *gk = gkeep + (int64_t)b * wp + tid * wpt;
-    uint64_t kw[SR_WPT];
+    uint64_t kw[WPT];
 #pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) kw[i] = gk[i < wpt ? i : 0];
+    for (int i = 0; i < WPT; ++i) kw[i] = gk[i < wpt ? i : 0];
     const uint2 *cb = cand + (int64_t)b * nch * SEL_CH;
     const uint4 *cmine = reinterpret_cast<const uint4 *>(cb + (int64_t)my_c * SEL_CH);
     uint2 cr[SEL_CPT];
@@ -317,7 +331,7 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     // threshold bin, both radix histograms
     for (int i = tid; i < wp; i += SR_NT) eqm[i] = 0ull;
 #pragma unroll
-    for (int i = 0; i < SR_WPT; ++i)
+    for (int i = 0; i < WPT; ++i)
         if (i < wpt) keep[tid * wpt + i] = tid * wpt + i < nw ? kw[i] : 0ull;
 #pragma unroll
     for (int q = 0; q < SEL_BINS / SR_NT; ++q) h[tid + SR_NT * q] = 0u;
@@ -433,10 +447,10 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         else if (c.x == kth) atomicOr(reinterpret_cast<unsigned long long *>(&eqm[c.y >> 6]), 1ull << (c.y & 63));
     });
     __syncthreads();
-    uint64_t ew[SR_WPT];
+    uint64_t ew[WPT];
     uint32_t ec = 0u, kc = 0u;
 #pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
+    for (int i = 0; i < WPT; ++i) {
         kw[i] = i < wpt ? keep[tid * wpt + i] : 0ull;
         ew[i] = i < wpt ? eqm[tid * wpt + i] : 0ull;
         ec += (uint32_t)__popcll(ew[i]);
@@ -446,7 +460,7 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
     block_excl_scan2_once<SR_NW>(ec, kc, sh + 3 * SR_NW, erank, o);
     o += erank < remaining ? erank : remaining;
 #pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
+    for (int i = 0; i < WPT; ++i) {
         uint64_t e = ew[i];
         const uint32_t c = (uint32_t)__popcll(e);
         if (erank >= remaining) e = 0ull;
@@ -462,21 +476,35 @@ __device__ __forceinline__ void resolve_emit_row(int b, const KvView &kv, int k,
         erank += c;
         kw[i] |= e;
     }
+    // the final words and the output offset of each word go to LDS (over the bitmasks: every
+    // thread read its own words before the scans' barriers), then this part's words are emitted,
+    // one word per thread and pass, in ascending positions
+    uint32_t *woff = reinterpret_cast<uint32_t *>(eqm);
 #pragma unroll
-    for (int i = 0; i < SR_WPT; ++i) {
-        uint64_t x = kw[i];
-        const int base = 64 * (tid * wpt + i);
+    for (int i = 0; i < WPT; ++i) {
+        if (i < wpt) {
+            keep[tid * wpt + i] = kw[i];
+            woff[tid * wpt + i] = o;
+            o += (uint32_t)__popcll(kw[i]);
+        }
+    }
+    __syncthreads();
+    const int wpp = wp / SR_PARTS;   // (wp is a multiple of SR_NT)
+    for (int w = part * wpp + tid; w < (part + 1) * wpp; w += SR_NT) {
+        uint64_t x = keep[w];
+        uint32_t ow = woff[w];
         while (x) {
             const int bit = __builtin_ctzll(x);
             x &= x - 1ull;
-            if (o < (uint32_t)k) out[o] = base + bit;
-            ++o;
+            if (ow < (uint32_t)k) out[ow] = 64 * w + bit;
+            ++ow;
         }
     }
-    if (tid == 0) nsel[b] = k;
+    if (part == 0 && tid == 0) nsel[b] = k;
 }
 
-// grid (B), SR_NT threads, dynamic LDS 16 wp bytes
+// grid (B SR_PARTS), SR_NT threads, dynamic LDS 16 wp bytes + overflow room
+template <int WPT>
 __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uint2 *__restrict__ cand,
                                                      const uint32_t *__restrict__ fcnt, int nch,
                                                      const uint64_t *__restrict__ gkeep, int wp,
@@ -484,7 +512,9 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve(KvView kv, int k, const uin
                                                      int32_t *__restrict__ nsel, int ov_cap)
 {
     extern __shared__ uint64_t sr_dyn[];
-    resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
+    resolve_emit_row<WPT>((int)blockIdx.x / SR_PARTS, (int)blockIdx.x % SR_PARTS, kv, k, cand, fcnt, nch, gkeep, wp,
+                          rows,
+                     sel, nsel, sr_dyn, ov_cap);
 }
 
 // Side job j (SR_NT threads): two absorb jobs a = 2 j + half, (cb, h) = (a % 4, a / 4), one per 256
@@ -518,13 +548,13 @@ __device__ __forceinline__ void side_absorb_job(const KvView &kv, const SideAbso
     }
 }
 
-// The resolve step leaves all but B workgroups of the chip idle; the decode step fills them with
+// The resolve step leaves all but B SR_PARTS workgroups of the chip idle; the decode step fills them with
 // work that does not depend on the selection: the query absorption (absorb_body.h) and the RoPE
 // rotation of the query tails at each row's query position seq_len - 1 (into a separate buffer).
 // grid (nres + 2 * 64): workgroups nres.. run two absorb jobs a = 2 (blockIdx - nres) + half,
 // (cb, h) = (a % 4, a / 4), one per 256 threads; the cb == 0 job of head h also rotates that
 // head's query tails.
-template <int NR, int FMT>
+template <int NR, int FMT, int WPT>
 __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, const uint2 *__restrict__ cand,
                                                             const uint32_t *__restrict__ fcnt, int nch,
                                                             const uint64_t *__restrict__ gkeep, int wp,
@@ -534,7 +564,8 @@ __global__ __launch_bounds__(SR_NT) void sel_resolve_absorb(KvView kv, int k, co
 {
     extern __shared__ uint64_t sr_dyn[];
     if ((int)blockIdx.x < nres) {
-        resolve_emit_row(blockIdx.x, kv, k, cand, fcnt, nch, gkeep, wp, rows, sel, nsel, sr_dyn, ov_cap);
+        resolve_emit_row<WPT>((int)blockIdx.x / SR_PARTS, (int)blockIdx.x % SR_PARTS, kv, k, cand, fcnt, nch, gkeep,
+                              wp, rows, sel, nsel, sr_dyn, ov_cap);
         return;
     }
     side_absorb_job<NR, FMT>(kv, sa, (int)blockIdx.x - nres, sr_dyn);
@@ -581,7 +612,10 @@ template <int NR, int FMT> static hipError_t side_attr()
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&absorb_rope<NR, FMT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve_absorb<NR, FMT>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve_absorb<NR, FMT, 4>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve_absorb<NR, FMT, SR_WPT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
     return e;
 }
@@ -667,8 +701,11 @@ static mla_status enable_sel_lds()
 {
     static bool done = false;
     if (!done) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve<4>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sel_resolve<SR_WPT>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, SR_DYN_MAX);
         if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
         done = true;
     }
@@ -713,17 +750,26 @@ mla_status launch_index_select(const float *q, const float *w, int32_t B, int32_
     const size_t dyn_sel = dyn_masks + 65536 < (size_t)SR_DYN_MAX ? dyn_masks + 65536 : (size_t)SR_DYN_MAX;
     const bool with_side = side && side->B == B && side_absorb_ok(*side);
     if (!with_side) {
-        hipLaunchKernelGGL(sel_resolve, dim3(B), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
-                           sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
+        if (sr_wpt_of(sw.wp) == 4)
+            hipLaunchKernelGGL((sel_resolve<4>), dim3(B * SR_PARTS), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
+                               sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
+        else
+            hipLaunchKernelGGL((sel_resolve<SR_WPT>), dim3(B * SR_PARTS), dim3(SR_NT), dyn_sel, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep,
+                               sw.wp, sw.rows, sel, nsel, (int)((dyn_sel - dyn_masks) / 8));
         return check_launch("sel_resolve");
     }
     const size_t dyn_abs = side_lds(*side);
     const size_t dyn = dyn_sel > dyn_abs ? dyn_sel : dyn_abs;
-    const dim3 g((unsigned)(B + 2 * AB_H));
-#define SRA_LAUNCH(NR, FMT)                                                                                     \
-    hipLaunchKernelGGL((sel_resolve_absorb<NR, FMT>), g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, \
-                       sw.wp, sw.rows, sel, nsel, B, *side, (int)((dyn - dyn_masks) / 8))
-    SIDE_DISPATCH(*side, SRA_LAUNCH);
+    const dim3 g((unsigned)(B * SR_PARTS + 2 * AB_H));
+#define SRA_LAUNCH(NR, FMT, W)                                                                                  \
+    hipLaunchKernelGGL((sel_resolve_absorb<NR, FMT, W>), g, dim3(SR_NT), dyn, s, kv, k, sw.cand, sw.fcnt, nch, sw.keep, \
+                       sw.wp, sw.rows, sel, nsel, B * SR_PARTS, *side, (int)((dyn - dyn_masks) / 8))
+#define SRA_LAUNCH4(NR, FMT) SRA_LAUNCH(NR, FMT, 4)
+#define SRA_LAUNCH8(NR, FMT) SRA_LAUNCH(NR, FMT, SR_WPT)
+    if (sr_wpt_of(sw.wp) == 4) SIDE_DISPATCH(*side, SRA_LAUNCH4);
+    else SIDE_DISPATCH(*side, SRA_LAUNCH8);
+#undef SRA_LAUNCH8
+#undef SRA_LAUNCH4
 #undef SRA_LAUNCH
     st = check_launch("sel_resolve_absorb");
     if (st) return st;
