@@ -98,6 +98,44 @@ def test_cache_write_paged_rows_against_oracle(in_bf16, kv_bf16, tiled, per):
         assert np.array_equal(a.view(np.uint32) if not kv_bf16 else a, b.view(np.uint32) if not kv_bf16 else b)
 
 
+@pytest.mark.parametrize("ix_off,ix_rd,with_ik,in_bf16", [(0, 64, True, True), (0, 128, True, False),
+                                                           (32, 96, True, True), (0, 0, False, True)])
+def test_cache_write_rotated_slice_placements(ix_off, ix_rd, with_ik, in_bf16):
+    """The 512/64/128 geometry with the indexer's rotated slice in the lower half of the key (its
+    pairs then share lanes with the Rc pairs), over the whole key, straddling the middle, and
+    without an indexer key; contiguous pools, bf16 latent and rope rows, fp32 indexer rows."""
+    rng = np.random.default_rng(640 + ix_off + ix_rd + with_ik)
+    L, rope, hd, rows = 512, 64, 128, 300
+    n = 257
+    seq = np.zeros(n, np.int32)
+    pos = np.sort(rng.choice(rows, n, replace=False)).astype(np.int32)
+    comp = (rng.standard_normal((n, L + rope)) * 1.5 - 0.2).astype(np.float32)
+    ik = (rng.standard_normal((n, hd)) * 0.8 + 0.4).astype(np.float32) if with_ik else None
+    gain = rng.uniform(0.5, 1.5, L).astype(np.float32)
+    lc = torch.full((rows, L), 7.0, dtype=torch.bfloat16, device="cuda")
+    rc = torch.full((rows, rope), 7.0, dtype=torch.bfloat16, device="cuda")
+    ic = torch.full((rows, hd), 7.0, dtype=torch.float32, device="cuda") if with_ik else None
+    kv = mla.KvCache(lc, rc, ic, max_seq_len=rows, seq_stride=rows)
+    log(f"cache write slice off={ix_off} dim={ix_rd} ik={with_ik} in_bf16={in_bf16}")
+    mla.mla_cache_write(_to_dev(comp, in_bf16), dev(seq), dev(pos), kv, 1,
+                        ik=_to_dev(ik, in_bf16) if with_ik else None, kv_gain=dev(gain), ix_rope_off=ix_off,
+                        ix_rope_dim=ix_rd, theta=500000.0)
+    r_lc, r_rc, r_ic = oracle.cache_write(_in_vals(comp, in_bf16), _in_vals(ik, in_bf16) if with_ik else None, seq,
+                                          pos, L, rope, rows=rows, kv_gain=gain, ix_off=ix_off, ix_rdim=ix_rd,
+                                          theta=500000.0, seq_stride=rows)
+    written = np.zeros(rows, bool)
+    written[pos] = True
+    g_lc, g_rc = host(lc), host(rc)
+    assert np.all(g_lc[~written] == 7.0) and np.all(g_rc[~written] == 7.0)
+    for g, r in ((g_lc, r_lc), (g_rc, r_rc)):
+        g, r = g[written], r[written]
+        assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 2e-6 * np.abs(r).max())
+    if with_ik:
+        g_ic = host(ic)
+        assert np.all(g_ic[~written] == 7.0)
+        assert np.abs(g_ic[written] - r_ic[written]).max() <= 2e-5 * np.abs(r_ic[written]).max()
+
+
 def test_tiny_layer_cache_written_on_gpu():
     """The tiny fp32 layer end to end with the GPU filling the cache: the kv_a outputs (plain float64
     matmuls rounded to fp32) go through mla_cache_write (RMSNorm eps 1e-6, unit gain, RoPE at

@@ -402,6 +402,30 @@ def test_index_select_batched_full_context_window():
     _select_check(q, w, kv, T, k, seq)
 
 
+def test_index_select_row_past_131072_keys():
+    """A row of 200,000 keys (past 131072, so the resolve holds eight bitmask words per thread)
+    and a second, shorter row in the same call: scores and selection bit-exact against the oracle."""
+    T, k = 200000, 2048
+    rng = np.random.default_rng(77)
+    ic = rng.standard_normal((2 * T, 128), dtype=np.float32)
+    qi = rng.standard_normal((2, 32, 128), dtype=np.float32)
+    wi = rng.standard_normal((2, 32), dtype=np.float32)
+    seq_len = [T, 150001]
+    log("index+select T=200000 k=2048 (eight words per resolve thread)")
+    lc = torch.empty((2 * T, 512), dtype=torch.bfloat16, device="cuda")   # not read by the selection
+    rc = torch.empty((2 * T, 64), dtype=torch.bfloat16, device="cuda")
+    kv = mla.KvCache(lc, rc, dev(ic), seq_len=dev(np.asarray(seq_len, np.int32)), max_seq_len=T, seq_stride=T)
+    sc, sel, nsel = mla.dsa_index_select(dev(qi), dev(wi), kv, T, k)
+    sc, sel, nsel = host(sc), host(sel), host(nsel)
+    for b in range(2):
+        n = seq_len[b]
+        ref_s = oracle.index_scores(qi[b], wi[b], ic[b * T:b * T + n])
+        assert np.array_equal(sc[b, :n].view(np.uint32), ref_s.view(np.uint32)), b
+        assert np.all(np.isneginf(sc[b, n:])), b
+        ref_sel, ref_n = oracle.topk(ref_s, n, k)
+        assert int(nsel[b]) == ref_n == k and np.array_equal(sel[b], ref_sel), b
+
+
 def test_index_select_long_row_general_path():
     T, k = 300000, 2048
     rng = np.random.default_rng(291)
