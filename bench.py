@@ -527,6 +527,17 @@ def bench_new_rows(args):
         "roofline": {"bound": "hbm", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "work": "4096 tokens: read comp (576 bf16) + ik (128 bf16) + seq/pos, write Lc/Rc (bf16) + Ic (fp32, tile64)"}
 
+    # RoPE of a prefill's queries: the qk_rope tails of 4096 tokens x 64 heads, in place
+    qp = rn(n, H, NOPE + ROPE).bfloat16()
+    posq = torch.arange(n, dtype=torch.int32, device=dev) + 1000
+    ms = _time_fn(torch, lambda: mla.mla_rope_interleave(qp, posq, NOPE, ROPE), 3, 50)
+    nbytes = 2 * n * H * ROPE * 2 + 4 * n   # the tails read and written, the positions
+    res["rope_prefill_queries_4096_tokens"] = {
+        "ms": ms, "bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "work": "4096 tokens x 64 heads: the 64-wide tail of each 256-wide bf16 query rotated in place"}
+    del qp
+
     # one 131072-token sequence, its DSA selection (as the full layer of the step computes it)
     T = 131072
     lc, rc = rn(T, L).bfloat16(), rn(T, ROPE).bfloat16()

@@ -113,15 +113,28 @@ __device__ __forceinline__ int64_t seq_len_of(const KvView &v, int b)
 // Pair j of a rope_dim-wide interleaved tail at position pos: (a, b) -> (a cos - b sin,
 // b cos + a sin) with angle pos * theta^(-2j/rope_dim) formed in double.  The rotation uses
 // explicit fused multiply-adds so that every kernel that rotates produces the same bits.
-__device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim, double pos, double theta,
-                                          float &lo, float &hi)
+// cos and sin of pair j's angle at pos, formed in double and rounded to float
+__device__ __forceinline__ void rope_cs(int j, int rope_dim, double pos, double theta, float &c, float &sn)
 {
     const double inv = pow(theta, -2.0 * (double)j / (double)rope_dim);
     double sd, cd;
     sincos(pos * inv, &sd, &cd);
-    const float c = (float)cd, sn = (float)sd;
+    c = (float)cd;
+    sn = (float)sd;
+}
+
+__device__ __forceinline__ void rope_apply(float a, float b, float c, float sn, float &lo, float &hi)
+{
     lo = __builtin_fmaf(a, c, -(b * sn));
     hi = __builtin_fmaf(b, c, a * sn);
+}
+
+__device__ __forceinline__ void rope_pair(float a, float b, int j, int rope_dim, double pos, double theta,
+                                          float &lo, float &hi)
+{
+    float c, sn;
+    rope_cs(j, rope_dim, pos, theta, c, sn);
+    rope_apply(a, b, c, sn, lo, hi);
 }
 
 // ------------------------------------------------------------------ selection keys
