@@ -105,7 +105,9 @@ constexpr int DC_ROWB = 1024;                    // bytes per staged latent row 
 // 12-15, two chunks, per pass of 32 lanes) then hit distinct banks.
 __device__ __forceinline__ int dc_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1); }
 constexpr int DC_PROW = 72;                      // bf16 per P row (64 keys + pad: 144 B)
-constexpr size_t DC_LDS = (size_t)DC_SUP * DC_KC * DC_ROWB + 16 * DC_PROW * 2 + (64 + 64 + 16) * 4;
+constexpr size_t DC_QOFF = (size_t)DC_SUP * DC_KC * DC_ROWB + 16 * DC_PROW * 2 + (64 + 64 + 16) * 4;
+// + q_abs of the workgroup's 16 heads (16 rows of 1 KB, chunks placed by dc_swz like the latent rows)
+constexpr size_t DC_LDS = DC_QOFF + 16 * DC_ROWB;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -175,7 +177,6 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
     const int s = blockIdx.x, NS = gridDim.x, h0 = 16 * blockIdx.y, b = blockIdx.z;
     const int jj = lane & 15, quad = lane >> 4;
     const int h = h0 + jj;
-    const bf16_t *qa = q_abs + ((int64_t)b * DM_H + h) * DM_L + 8 * quad;
     const bf16_t *qr = q_rope + ((int64_t)b * DM_H + h) * DM_R + 8 * quad;
     const bf16_t *dummy = q_abs + ((int64_t)b * DM_H + h0) * DM_L + 8 * lane;   // any readable 1 KB
     const int64_t k0 = (int64_t)s * kps;
@@ -187,9 +188,12 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
             t_first[u] = sel ? sel[(int64_t)b * sel_stride + (j < sel_stride ? j : sel_stride - 1)] : (int32_t)j;
         }
     }
+    // The score product's B operand: q_abs of the 16 heads is copied into LDS once per workgroup
+    // (below, behind the first chunk's rows) and read from there; loaded by every wave into
+    // registers it was 64 KB of requests per workgroup queued ahead of the rows.  The rope part
+    // (2 KB per wave) is loaded straight into registers.
+    char *sQ = dc_smem + DC_QOFF;
     uint4 Bq[18];
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) Bq[ks] = *reinterpret_cast<const uint4 *>(qa + 32 * ks);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) Bq[16 + ks] = *reinterpret_cast<const uint4 *>(qr + 32 * ks);
     const int64_t sl = seq_len_of(kv, b);
@@ -230,7 +234,21 @@ __global__ __launch_bounds__(256) void dec_core(const bf16_t *__restrict__ q_abs
                 lds_dma16(src, lds_addr(sL + (64 * u + 16 * wave + i) * DC_ROWB));
             }
         }
+        if (c0 == k0) {   // q_abs rows of heads h0 + 4 wave .. + 3
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hr = 4 * wave + i;
+                lds_dma16(q_abs + ((int64_t)b * DM_H + h0 + hr) * DM_L + 8 * (lane ^ dc_swz(hr)),
+                          lds_addr(sQ + hr * DC_ROWB));
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (c0 == k0) {
+            const int fq = dc_swz(jj);
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+                Bq[ks] = *reinterpret_cast<const uint4 *>(sQ + jj * DC_ROWB + 16 * ((4 * ks + quad) ^ fq));
+        }
 #pragma unroll
         for (int u = 0; u < DC_SUP; ++u) {
             if (c0 + 64 * u >= k1) break;

@@ -39,11 +39,13 @@ __global__ __launch_bounds__(256) void rope_kernel(T *__restrict__ x, int64_t n_
 }
 
 // Tokens with several heads: every head of a token rotates by the same angles, so a block takes one
-// token, forms its half (cos, sin) pairs once (threads j < half) and then rotates the pairs of all
-// its heads in chunks of whole tails (half divides 256): each thread reads its pair, the block
-// syncs (the in-place hazard of one tail), then writes.  The same rope_cs / rope_apply arithmetic as
-// rope_pair, so the values equal the per-pair kernel's bit for bit; the double-precision angles
-// are formed half times per token instead of n_heads * half times.
+// token (grid.x) and a run of its heads (grid.y: all of them when there are many tokens, else one
+// chunk of 256 / half heads per block so that a few tokens still spread over the chip), forms the
+// half (cos, sin) pairs once (threads j < half) and rotates its heads in chunks of whole tails (half
+// divides 256): each thread reads its pair, the block syncs (the in-place hazard of one tail), then
+// writes.  The same rope_cs / rope_apply arithmetic as rope_pair, so the values equal the per-pair
+// kernel's bit for bit; the double-precision angles are formed half times per block instead of once
+// per pair.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_token_kernel(T *__restrict__ x, int32_t n_heads, int64_t tok_stride,
                                                          int64_t head_stride, int32_t rope_off, int32_t half,
@@ -55,16 +57,18 @@ __global__ __launch_bounds__(256) void rope_token_kernel(T *__restrict__ x, int3
     if (tid < half) rope_cs(tid, 2 * half, (double)pos[n], theta, s_c[tid], s_s[tid]);
     __syncthreads();
     T *tok = x + n * tok_stride + rope_off;
-    const int items = n_heads * half, upc = 256 / half;   // pairs of the token, tails per chunk
+    const int upc = 256 / half;                                        // tails per chunk
+    const int hpb = (n_heads + (int)gridDim.y - 1) / (int)gridDim.y;   // heads of this block's run
+    const int hb = (int)blockIdx.y * hpb, he = hb + hpb < n_heads ? hb + hpb : n_heads;
     const int j = tid % half, hl = tid / half;
     const float c = s_c[j], sn = s_s[j];
-    for (int h0 = 0; h0 * half < items; h0 += upc) {
+    for (int h0 = hb; h0 < he; h0 += upc) {
         const int h = h0 + hl;
         T *tail = tok + (int64_t)h * head_stride;
         float lo = 0.f, hi = 0.f;
-        if (h < n_heads) rope_apply(ld(tail + 2 * j), ld(tail + 2 * j + 1), c, sn, lo, hi);
+        if (h < he) rope_apply(ld(tail + 2 * j), ld(tail + 2 * j + 1), c, sn, lo, hi);
         __syncthreads();
-        if (h < n_heads) {
+        if (h < he) {
             st(tail + j, lo);
             st(tail + half + j, hi);
         }
@@ -78,12 +82,16 @@ mla_status launch_rope(void *x, mla_dtype dt, int64_t n_tok, int32_t n_heads, in
     const int32_t half = rope_dim / 2;
     if (n_heads > 1 && half > 0 && 256 % half == 0 && n_tok <= 0x7fffffff) {
         if (n_tok == 0) return MLA_OK;
+        // a block per token when the tokens fill the chip, else a block per chunk of heads
+        const int upc = 256 / half, nchunk = (n_heads + upc - 1) / upc;
+        const int gy = n_tok >= 512 || nchunk > 65535 ? 1 : nchunk;
+        const dim3 g((unsigned)n_tok, (unsigned)gy);
         if (dt == MLA_FP32)
-            hipLaunchKernelGGL(rope_token_kernel<float>, dim3((unsigned)n_tok), dim3(256), 0, s, (float *)x, n_heads,
-                               tok_stride, head_stride, rope_off, half, pos, theta);
+            hipLaunchKernelGGL(rope_token_kernel<float>, g, dim3(256), 0, s, (float *)x, n_heads, tok_stride,
+                               head_stride, rope_off, half, pos, theta);
         else
-            hipLaunchKernelGGL(rope_token_kernel<bf16_t>, dim3((unsigned)n_tok), dim3(256), 0, s, (bf16_t *)x,
-                               n_heads, tok_stride, head_stride, rope_off, half, pos, theta);
+            hipLaunchKernelGGL(rope_token_kernel<bf16_t>, g, dim3(256), 0, s, (bf16_t *)x, n_heads, tok_stride,
+                               head_stride, rope_off, half, pos, theta);
         return check_launch("rope_token_kernel");
     }
     const int32_t upb = 256 / half;
