@@ -277,9 +277,11 @@ __global__ __launch_bounds__(256) void sel_filter(const float *__restrict__ scor
 //     final words and each word's output offset go to LDS, and the set bits of the part's words are
 //     written out as positions -- ascending across the row.
 // Every histogram and scan has LDS of its own, cleared or written once, so a phase needs only the
-// barrier that publishes its inputs (9 barriers instead of 18).  (Compacting the positions in LDS
-// for 16-byte stores was slower than the scattered 4-byte stores.)
-// dyn: keep[wp], eq[wp] (uint64), then staged overflow candidates.
+// barrier that publishes its inputs (10 barriers with the one that publishes the final words).
+// (Writing the positions through LDS as one contiguous run instead of the scattered 4-byte stores
+// changed nothing.)
+// dyn: keep[wp], eq[wp] (uint64; the final words and their output offsets at the end), then staged
+// overflow candidates.
 template <int WPT>
 __device__ __forceinline__ void resolve_emit_row(int b, int part, const KvView &kv, int k,
                                                  const uint2 *__restrict__ cand,
