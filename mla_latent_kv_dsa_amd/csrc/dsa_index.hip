@@ -108,8 +108,9 @@ __global__ __launch_bounds__(256) void index_scores_generic(const float *__restr
 //   0..31 of the tile, block 1 keys 32..63.  Accumulator register r (0..15) of lane L holds
 //   block 0, key L % 32, head 8*(r/4) + 4*(L/32) + r%4; registers 16..31 hold block 1.
 // A wave owns 64-key tiles.  Lane L loads key L's row straight into registers, 32 dims
-// (one slice, 8 x 16 B) at a time, through a ring of two slices: while slice s feeds the
-// 32 MFMAs of one step, slice s + 2 is already in flight.  No LDS staging is needed because
+// (one slice, 8 x 16 B) at a time, through a ring of one slice refilled group by group (the
+// single-query kernel) or of two slices (the multi-query kernel): while slice s feeds its
+// MFMAs, the next slice is already in flight.  No LDS staging is needed because
 // the B operand of this MFMA is exactly "key L's value at dim d" in lane L.  The query
 // (32 x 128) is staged in LDS once per block, before any key load is issued, so that the
 // block barrier does not wait on the key stream.
@@ -187,6 +188,35 @@ __device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The same products over a ring of one slice, refilled group by group: once the four MFMAs of
+// dims 4j .. 4j+3 are issued, those four registers of K are reloaded with the same group of the
+// next slice (slice nsl at pn).  A wave then keeps one slice in flight all the time, and its
+// products run as the groups arrive.  The query group is read from LDS one group ahead: qq holds
+// group 0 of slice sl on entry and group 0 of slice (sl + 1) % 4 on exit (the query rows are the
+// same for every tile).
+template <bool TILED>
+__device__ __forceinline__ void ix_slice_refill(v32f &acc, v32f &K, const float *qrow, int sl, float4 &qq,
+                                                const float *pn, int nsl)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int nq = j < 7 ? sl * 32 + 4 * (j + 1) : ((sl + 1) & 3) * 32;
+        const float4 qn = *reinterpret_cast<const float4 *>(&qrow[nq]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, K[4 * j + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, K[4 * j + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, K[4 * j + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, K[4 * j + 3], acc, 0, 0, 0);
+        const ix_f4 x = __builtin_nontemporal_load(
+            reinterpret_cast<const ix_f4 *>(TILED ? pn + (nsl * 8 + j) * 256 : pn + nsl * 32 + 4 * j));
+        K[4 * j + 0] = x.x;
+        K[4 * j + 1] = x.y;
+        K[4 * j + 2] = x.z;
+        K[4 * j + 3] = x.w;
+        qq = qn;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Score of key L in lane L from the accumulator: lanes L and L^32 hold complementary head
 // groups of the same two keys, so one v_permlane32_swap per register pair leaves every lane
 // with heads 8g..8g+3 of its key in lo[] and heads 8g+4..8g+7 in hi[]; the heads are then folded
@@ -247,12 +277,14 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
 
     if (HIST)
         for (int i = tid; i < IX_BINS; i += 64 * IXM_WAVES) hs[i] = 0u;
-    // The query's loads go out first and the wave's first key slices right behind them; the query
+    // The query's loads go out first and the wave's first key slice right behind them; the query
     // is then staged in LDS while the key data is still on its way (loads return in issue order,
     // so the stores wait for the query only), and the barrier waits for LDS alone.  The key
     // pointer is formed before the query's loads (its branches would otherwise let the compiler
-    // sink them behind the key slices), and the slices are loaded unconditionally, from the
-    // stand-in for a wave without a tile.
+    // sink them behind the key slice), and the slices are loaded unconditionally, from the
+    // stand-in for a wave without a tile.  One slice in flight per wave, kept full by the
+    // group-by-group refill, streams faster than two (a wave then folds a slice in while the
+    // next arrives, and the chip holds 8 MB of requests in flight instead of up to 16 MB).
     int64_t tile = (int64_t)blockIdx.x * IXM_WAVES + wave;
     const float *qrow = &sq[(lane & 31) * IXM_QROW];
     // stand-in for keys without a row: the query block (512 B rows), or the pool's first tile
@@ -267,10 +299,8 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
 #pragma unroll
     for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) qv[k] = qb[tid + k * 64 * IXM_WAVES];
     __builtin_amdgcn_sched_barrier(0);
-    v32f KA, KB, acc;
-    ix_load_slice<TILED>(KA, p, 0);
-    __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
-    ix_load_slice<TILED>(KB, p, 1);
+    v32f K, acc;
+    ix_load_slice<TILED>(K, p, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) {
@@ -280,23 +310,20 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the query and the cleared histogram
 
     if (tile < ntv) {   // (no early return: the histogram flush below needs every wave at the barrier)
+    float4 qq = *reinterpret_cast<const float4 *>(&qrow[0]);
     for (; tile < ntv; tile += waves_total) {
-        // the next tile's first two slices are loaded unconditionally (from the query block
-        // when there is no next tile) so every iteration leaves the same loads in flight
+        // the next tile's first slice is loaded unconditionally (from the stand-in when there
+        // is no next tile) so every iteration leaves the same loads in flight
         const int64_t nxt = tile + waves_total;
         const float *pn = qraw;
         valid_n = false;
         if (nxt < ntv) pn = ix_key_ptr<MODE, TILED>(kv, b, nxt, lane, n, qraw, valid_n);
 #pragma unroll
         for (int r = 0; r < 32; ++r) acc[r] = 0.f;
-        ix_slice(acc, KA, qrow, 0);
-        ix_load_slice<TILED>(KA, p, 2);
-        ix_slice(acc, KB, qrow, 1);
-        ix_load_slice<TILED>(KB, p, 3);
-        ix_slice(acc, KA, qrow, 2);
-        ix_load_slice<TILED>(KA, pn, 0);
-        ix_slice(acc, KB, qrow, 3);
-        ix_load_slice<TILED>(KB, pn, 1);
+        ix_slice_refill<TILED>(acc, K, qrow, 0, qq, p, 1);
+        ix_slice_refill<TILED>(acc, K, qrow, 1, qq, p, 2);
+        ix_slice_refill<TILED>(acc, K, qrow, 2, qq, p, 3);
+        ix_slice_refill<TILED>(acc, K, qrow, 3, qq, pn, 0);
         const float s = ix_fold(acc, wb);
         const int64_t t = tile * 64 + lane;
         const float sc = valid ? s : -INFINITY;
