@@ -188,30 +188,50 @@ __device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The same products over a ring of one slice, refilled group by group: once the four MFMAs of
-// dims 4j .. 4j+3 are issued, those four registers of K are reloaded with the same group of the
-// next slice (slice nsl at pn).  A wave then keeps one slice in flight all the time, and its
-// products run as the groups arrive.  The query group is read from LDS one group ahead: qq holds
-// group 0 of slice sl on entry and group 0 of slice (sl + 1) % 4 on exit (the query rows are the
-// same for every tile).
+// A tile's 128 products per output over a ring of IX_LAG four-dim groups, refilled group by
+// group: once the four MFMAs of group g (dims 4g .. 4g+3) are issued, its ring slot is reloaded
+// with group g + IX_LAG (of this tile at p, or of the next tile at pn), so a wave keeps IX_LAG
+// groups in flight all the time and its products run as the groups arrive.  The query group is
+// read from LDS one group ahead: qq holds group 0 on entry and on exit (the query rows are the
+// same for every tile).  Eight groups (one slice, 8 KB per wave) stream best: four took the
+// T = 131072 indexer from 13.7-13.9 to 14.2-14.3 us and two to 17.9 us (same box, alternating).
+constexpr int IX_LAG = 8;
+typedef float ixk_t __attribute__((ext_vector_type(4 * IX_LAG)));
+static_assert(32 % IX_LAG == 0, "a tile's groups must fill whole rings");
+
 template <bool TILED>
-__device__ __forceinline__ void ix_slice_refill(v32f &acc, v32f &K, const float *qrow, int sl, float4 &qq,
-                                                const float *pn, int nsl)
+__device__ __forceinline__ void ix_load_ring(ixk_t &K, const float *p)
 {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int nq = j < 7 ? sl * 32 + 4 * (j + 1) : ((sl + 1) & 3) * 32;
-        const float4 qn = *reinterpret_cast<const float4 *>(&qrow[nq]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, K[4 * j + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, K[4 * j + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, K[4 * j + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, K[4 * j + 3], acc, 0, 0, 0);
-        const ix_f4 x = __builtin_nontemporal_load(
-            reinterpret_cast<const ix_f4 *>(TILED ? pn + (nsl * 8 + j) * 256 : pn + nsl * 32 + 4 * j));
-        K[4 * j + 0] = x.x;
-        K[4 * j + 1] = x.y;
-        K[4 * j + 2] = x.z;
-        K[4 * j + 3] = x.w;
+    for (int g = 0; g < IX_LAG; ++g) {
+        const ix_f4 x = __builtin_nontemporal_load(reinterpret_cast<const ix_f4 *>(TILED ? p + g * 256 : p + 4 * g));
+        K[4 * g + 0] = x.x;
+        K[4 * g + 1] = x.y;
+        K[4 * g + 2] = x.z;
+        K[4 * g + 3] = x.w;
+    }
+}
+
+template <bool TILED>
+__device__ __forceinline__ void ix_tile_refill(v32f &acc, ixk_t &K, const float *qrow, float4 &qq, const float *p,
+                                               const float *pn)
+{
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+        const int sl = 4 * (g % IX_LAG);
+        const float4 qn = *reinterpret_cast<const float4 *>(&qrow[4 * ((g + 1) & 31)]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, K[sl + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, K[sl + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, K[sl + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, K[sl + 3], acc, 0, 0, 0);
+        const int gl = (g + IX_LAG) & 31;
+        const float *src = g + IX_LAG < 32 ? p : pn;
+        const ix_f4 x =
+            __builtin_nontemporal_load(reinterpret_cast<const ix_f4 *>(TILED ? src + gl * 256 : src + 4 * gl));
+        K[sl + 0] = x.x;
+        K[sl + 1] = x.y;
+        K[sl + 2] = x.z;
+        K[sl + 3] = x.w;
         qq = qn;
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -299,8 +319,9 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
 #pragma unroll
     for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) qv[k] = qb[tid + k * 64 * IXM_WAVES];
     __builtin_amdgcn_sched_barrier(0);
-    v32f K, acc;
-    ix_load_slice<TILED>(K, p, 0);
+    ixk_t K;
+    v32f acc;
+    ix_load_ring<TILED>(K, p);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 32 * 32 / (64 * IXM_WAVES); ++k) {
@@ -320,10 +341,7 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma(const float 
         if (nxt < ntv) pn = ix_key_ptr<MODE, TILED>(kv, b, nxt, lane, n, qraw, valid_n);
 #pragma unroll
         for (int r = 0; r < 32; ++r) acc[r] = 0.f;
-        ix_slice_refill<TILED>(acc, K, qrow, 0, qq, p, 1);
-        ix_slice_refill<TILED>(acc, K, qrow, 1, qq, p, 2);
-        ix_slice_refill<TILED>(acc, K, qrow, 2, qq, p, 3);
-        ix_slice_refill<TILED>(acc, K, qrow, 3, qq, pn, 0);
+        ix_tile_refill<TILED>(acc, K, qrow, qq, p, pn);
         const float s = ix_fold(acc, wb);
         const int64_t t = tile * 64 + lane;
         const float sc = valid ? s : -INFINITY;
