@@ -158,36 +158,8 @@ __device__ __forceinline__ const float *ix_key_ptr(const KvView &kv, int b, int6
 // weights), and stream faster themselves (alone 17.1 -> 15.7 us, decode step 47.0 -> 43.7 us,
 // same box, alternating).
 typedef float ix_f4 __attribute__((ext_vector_type(4)));
-template <bool TILED>
-__device__ __forceinline__ void ix_load_slice(v32f &dst, const float *p, int sl)
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const ix_f4 x = __builtin_nontemporal_load(
-            reinterpret_cast<const ix_f4 *>(TILED ? p + (sl * 8 + i) * 256 : p + sl * 32 + 4 * i));
-        dst[4 * i + 0] = x.x;
-        dst[4 * i + 1] = x.y;
-        dst[4 * i + 2] = x.z;
-        dst[4 * i + 3] = x.w;
-    }
-}
 
-// acc += q[:, 32 sl .. 32 sl + 31] x K[:, same dims]^T, one MFMA per dim, d ascending.
-__device__ __forceinline__ void ix_slice(v32f &acc, const v32f &K, const float *qrow, int sl)
-{
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        // keeps the LDS reads of q next to their MFMAs instead of all hoisted (VGPR pressure)
-        if ((j & 1) == 0) __builtin_amdgcn_sched_barrier(0);
-        const float4 qq = *reinterpret_cast<const float4 *>(&qrow[sl * 32 + 4 * j]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.x, K[4 * j + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.y, K[4 * j + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.z, K[4 * j + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(qq.w, K[4 * j + 3], acc, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
+// acc += q x K^T over one 64-key tile, one MFMA per dim, d ascending.
 // A tile's 128 products per output over a ring of IX_LAG four-dim groups, refilled group by
 // group: once the four MFMAs of group g (dims 4g .. 4g+3) are issued, its ring slot is reloaded
 // with group g + IX_LAG (of this tile at p, or of the next tile at pn), so a wave keeps IX_LAG
@@ -233,6 +205,41 @@ __device__ __forceinline__ void ix_tile_refill(v32f &acc, ixk_t &K, const float 
         K[sl + 2] = x.z;
         K[sl + 3] = x.w;
         qq = qn;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same for QB queries against each key group (the multi-query kernel): each group's products
+// of every query are issued before its ring slot is refilled; qq[qi] holds group 0 of query qi's
+// rows on entry and on exit.
+template <bool TILED, int QB>
+__device__ __forceinline__ void ix_tile_refill_mq(v32f (&acc)[QB], ixk_t &K, const float *qrow, float4 (&qq)[QB],
+                                                  const float *p, const float *pn)
+{
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+        const int sl = 4 * (g % IX_LAG);
+        float4 qn[QB];
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi)
+            qn[qi] = *reinterpret_cast<const float4 *>(&qrow[qi * 32 * IXM_QROW + 4 * ((g + 1) & 31)]);
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi) {
+            acc[qi] = __builtin_amdgcn_mfma_f32_32x32x1f32(qq[qi].x, K[sl + 0], acc[qi], 0, 0, 0);
+            acc[qi] = __builtin_amdgcn_mfma_f32_32x32x1f32(qq[qi].y, K[sl + 1], acc[qi], 0, 0, 0);
+            acc[qi] = __builtin_amdgcn_mfma_f32_32x32x1f32(qq[qi].z, K[sl + 2], acc[qi], 0, 0, 0);
+            acc[qi] = __builtin_amdgcn_mfma_f32_32x32x1f32(qq[qi].w, K[sl + 3], acc[qi], 0, 0, 0);
+        }
+        const int gl = (g + IX_LAG) & 31;
+        const float *src = g + IX_LAG < 32 ? p : pn;
+        const ix_f4 x =
+            __builtin_nontemporal_load(reinterpret_cast<const ix_f4 *>(TILED ? src + gl * 256 : src + 4 * gl));
+        K[sl + 0] = x.x;
+        K[sl + 1] = x.y;
+        K[sl + 2] = x.z;
+        K[sl + 3] = x.w;
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi) qq[qi] = qn[qi];
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -436,13 +443,15 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma_mq(const flo
     const float *qraw = TILED ? kv.ic + 4 * lane : q + (int64_t)r0 * 32 * 128;
     bool valid, valid_n = false;
     const float *p = ix_key_ptr<MODE, TILED>(kv, r0, tile, lane, n, qraw, valid);
-    v32f KA, KB, acc[QB];
-    ix_load_slice<TILED>(KA, p, 0);
-    __builtin_amdgcn_sched_barrier(0);   // issue order KA then KB: the waits below count on it
-    ix_load_slice<TILED>(KB, p, 1);
+    ixk_t K;
+    v32f acc[QB];
+    ix_load_ring<TILED>(K, p);
+    float4 qq[QB];
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) qq[qi] = *reinterpret_cast<const float4 *>(&qrow[qi * 32 * IXM_QROW]);
     for (; tile < ntv; tile += waves_total) {
-        // the next tile's first two slices are loaded unconditionally (from the query block
-        // when there is no next tile) so every iteration leaves the same loads in flight
+        // the next tile's first slice is loaded unconditionally (from the stand-in when there is
+        // no next tile) so every iteration leaves the same loads in flight
         const int64_t nxt = tile + waves_total;
         const float *pn = qraw;
         valid_n = false;
@@ -451,22 +460,9 @@ __global__ __launch_bounds__(64 * IXM_WAVES) void index_scores_mfma_mq(const flo
         for (int qi = 0; qi < QB; ++qi)
 #pragma unroll
             for (int r = 0; r < 32; ++r) acc[qi][r] = 0.f;
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi)
-            if (qi < nb) ix_slice(acc[qi], KA, qrow + qi * 32 * IXM_QROW, 0);
-        ix_load_slice<TILED>(KA, p, 2);
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi)
-            if (qi < nb) ix_slice(acc[qi], KB, qrow + qi * 32 * IXM_QROW, 1);
-        ix_load_slice<TILED>(KB, p, 3);
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi)
-            if (qi < nb) ix_slice(acc[qi], KA, qrow + qi * 32 * IXM_QROW, 2);
-        ix_load_slice<TILED>(KA, pn, 0);
-#pragma unroll
-        for (int qi = 0; qi < QB; ++qi)
-            if (qi < nb) ix_slice(acc[qi], KB, qrow + qi * 32 * IXM_QROW, 3);
-        ix_load_slice<TILED>(KB, pn, 1);
+        // (a block with nb < QB queries repeats its last query's rows: the spare products are
+        // discarded, and the group loop stays free of branches)
+        ix_tile_refill_mq<TILED, QB>(acc, K, qrow, qq, p, pn);
         const int64_t t = tile * 64 + lane;
 #pragma unroll
         for (int qi = 0; qi < QB; ++qi) {
